@@ -1,0 +1,153 @@
+"""Pins for the GPTQ oracle (page export_gptq_cpu.py: pack_int32, quantize_sym,
+quantize_asym, and the uint4b8 convention of its module docstring)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.gptq as gq
+from _exact import F, rint_even, rn32, rnf16, same
+from golden.golden import floats, load
+from group_wise_bit_amd import workloads
+
+G = load("gptq_worked_group8.txt")
+
+
+def _hexwords(s):
+    return np.array([int(t, 16) for t in s.split()], np.uint32).view(np.int32)
+
+
+def _worked_weight():
+    w = np.zeros((8, 8), np.float32)
+    w[0] = floats(G["row0_f32"])
+    return w
+
+
+def test_pack_int32_examples():
+    c = np.arange(8, dtype=np.uint8)[:, None]
+    assert gq.pack_int32(c, 0).view(np.uint32)[0, 0] == int(G["pack_0_to_7_hex"], 16)
+    assert gq.pack_int32(c.T, 1).view(np.uint32)[0, 0] == int(G["pack_0_to_7_hex"], 16)
+    assert gq.pack_int32(np.full((8, 3), 15, np.uint8), 0).tolist() == [[-1, -1, -1]]
+
+
+@pytest.mark.parametrize("dim", [0, 1])
+def test_pack_roundtrip(dim):
+    rng = np.random.default_rng(21)
+    c = rng.integers(0, 16, (64, 48)).astype(np.uint8)
+    assert np.array_equal(gq.unpack_int32(gq.pack_int32(c, dim), dim), c)
+
+
+def test_worked_example_sym():
+    q = gq.quantize_sym(_worked_weight(), group=8)
+    assert np.array_equal(q["qweight"][0], _hexwords(G["sym_qweight_hex"]))
+    assert np.array_equal(q["qzeros"].ravel(), _hexwords(G["sym_qzeros_hex"]))
+    assert [int(b) for b in q["scales"].view(np.uint16)[0]] == [int(t, 16) for t in G["sym_scales_f16_hex"].split()]
+    d = gq.dequantize(q["qweight"], q["scales"], q["qzeros"], 8, sym=True)
+    assert d[0].tolist() == floats(G["sym_dequant_row0"])
+
+
+def test_worked_example_asym():
+    q = gq.quantize_asym(_worked_weight(), group=8)
+    assert np.array_equal(q["qweight"][0], _hexwords(G["asym_qweight_hex"]))
+    assert np.array_equal(q["qzeros"].ravel(), _hexwords(G["asym_qzeros_hex"]))
+    assert int(q["scales"].view(np.uint16)[0, 0]) == int(G["asym_scales_f16_hex0"], 16)
+
+
+def test_bits_per_weight():
+    assert gq.bits_per_weight(128) == float(G["bits_per_weight_g128"])
+
+
+def _inputs():
+    return [workloads.gptq_sym_weight(16, 256, seed=22).numpy(),
+            workloads.gptq_asym_weight(16, 256, seed=23).float().numpy(),
+            workloads.adversarial_weight(16, 256, seed=24, dtype=torch.float32).numpy(),
+            workloads.adversarial_weight(16, 256, seed=25, dtype=torch.bfloat16).float().numpy()]
+
+
+@pytest.mark.parametrize("group", [128, 32])
+def test_sym_bruteforce_exact(group):
+    eps = F(np.float32(1e-9))
+    for w in _inputs():
+        q = gq.quantize_sym(w, group)
+        n, k = w.shape
+        for col in range(0, n, 3):
+            for g in range(k // group):
+                xs = w[col, g * group:(g + 1) * group]
+                amax = max(abs(F(v)) for v in xs)
+                s = max(rn32(amax / 8), eps)
+                assert F(q["scale_f32"][g, col]) == s
+                assert same(q["scales"][g, col], rnf16(s))   # fp16 overflow -> inf
+                for i, v in enumerate(xs):
+                    t = rn32(F(v) / s)
+                    # nearest of the 16 codes to t + 8, ties to even (rint then clamp)
+                    dist = [abs(t + 8 - c) for c in range(16)]
+                    best = min(dist)
+                    cands = [c for c in range(16) if dist[c] == best]
+                    want = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
+                    assert q["codes"][g * group + i, col] == want
+
+
+def test_sym_invariants():
+    w = workloads.gptq_sym_weight(64, 512, seed=26).numpy()
+    q = gq.quantize_sym(w, 128)
+    assert np.all(q["qzeros"].view(np.uint32) == 0x77777777)
+    wt = w.T.reshape(4, 128, 64)
+    codes = q["codes"].reshape(4, 128, 64)
+    amax = np.abs(wt).max(1)
+    hit_pos = wt == amax[:, None, :]
+    hit_neg = wt == -amax[:, None, :]
+    assert np.all(codes[hit_pos] == 15) and np.all(codes[hit_neg] == 0)
+    assert np.all(q["scale_f32"] * 8 == amax)
+    z = w.copy()
+    z[:, :5] = 0
+    assert np.all(gq.quantize_sym(z, 128)["codes"][:5] == 8)
+
+
+@pytest.mark.parametrize("group", [128, 64])
+def test_asym_bruteforce_exact(group):
+    eps = F(np.float32(1e-9))
+    for w in _inputs():
+        q = gq.quantize_asym(w, group)
+        n, k = w.shape
+        for col in range(1, n, 3):
+            for g in range(k // group):
+                xs = w[col, g * group:(g + 1) * group]
+                mx, mn = max(F(v) for v in xs), min(F(v) for v in xs)
+                s = rn32(max(rn32(mx - mn), eps) / 15)
+                assert F(q["scale_f32"][g, col]) == s
+                zp = min(max(rint_even(rn32(-mn / s)), 0), 15)
+                assert q["zp"][g, col] == zp
+                for i, v in enumerate(xs):
+                    t = rn32(F(v) / s)
+                    # nearest integer code c to t + zp over the 16 codes, ties even in (c - zp)
+                    dist = [abs(t + zp - c) for c in range(16)]
+                    best = min(dist)
+                    cands = [c for c in range(16) if dist[c] == best]
+                    want = cands[0] if len(cands) == 1 else [c for c in cands if (c - zp) % 2 == 0][0]
+                    assert q["codes"][g * group + i, col] == want
+
+
+def test_asym_invariants():
+    w = workloads.gptq_asym_weight(64, 512, seed=27).float().numpy()
+    q = gq.quantize_asym(w, 128)
+    wt = w.T.reshape(4, 128, 64)
+    codes = q["codes"].reshape(4, 128, 64)
+    mn, mx = wt.min(1), wt.max(1)
+    assert np.all(mn <= 0) and np.all(mx >= 0)       # N(0, .02) groups straddle 0
+    assert np.all(codes[wt == mn[:, None, :]] == 0)
+    assert set(np.unique(codes[wt == mx[:, None, :]])) <= {14, 15}
+    assert np.array_equal(gq.unpack_int32(q["qzeros"], 1), q["zp"])
+
+
+@pytest.mark.parametrize("sym", [True, False])
+def test_dequant_from_stored_exact(sym):
+    w = workloads.adversarial_weight(16, 256, seed=28, dtype=torch.float32).numpy()
+    q = (gq.quantize_sym if sym else gq.quantize_asym)(w, 128)
+    d = gq.dequantize(q["qweight"], q["scales"], q["qzeros"], 128, sym)
+    zp = np.full((2, 16), 8) if sym else q["zp"]
+    for col in range(16):
+        for k in range(0, 256, 7):
+            c = int(q["codes"][k, col])
+            if not np.isfinite(q["scales"][k // 128, col]):
+                continue                       # fp16 scale overflowed (huge weights)
+            want = rn32((c - int(zp[k // 128, col])) * F(q["scales"][k // 128, col]))
+            assert F(d[col, k]) == want

@@ -1,0 +1,101 @@
+"""Planted mistakes in the oracle (CPU only, via monkeypatch) must each fail a pin.
+Shows the pins are sharp enough to catch a wrong tie rule, exponent offset, nibble or
+shard order, a dropped bfloat16 rounding, a wrong weighting and a wrong sign."""
+import numpy as np
+import pytest
+
+import oracle.awq as awq
+import oracle.gptq as gq
+import oracle.mxfp4 as mx
+import oracle.snr as snr
+import oracle.uintx as ux
+import test_oracle_gptq as tg
+import test_oracle_mxfp4 as tm
+import test_oracle_snr_awq as ts
+import test_oracle_uintx as tu
+
+
+def _fails(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_mxfp4_page_literal_ties_caught(monkeypatch):
+    orig = mx.nearest_index
+    monkeypatch.setattr(mx, "nearest_index", lambda m, ties="even": orig(m, "page_literal"))
+    _fails(tm.test_ties_go_to_even_code)
+
+
+def test_mxfp4_exponent_offset_caught(monkeypatch):
+    orig = mx.block_exponent
+    monkeypatch.setattr(mx, "block_exponent", lambda a: np.clip(orig(a) + 1, -127, 127))
+    _fails(tm.test_worked_example_block)
+    _fails(tm.test_invariants_block_max_lands_at_top)
+
+
+def test_mxfp4_nibble_order_caught(monkeypatch):
+    orig = mx.unpack_codes
+    def swapped(p):
+        c = orig(p)
+        out = c.copy()
+        out[:, 0::2], out[:, 1::2] = c[:, 1::2], c[:, 0::2]
+        return out
+    monkeypatch.setattr(mx, "unpack_codes", swapped)
+    _fails(tm.test_bruteforce_exact_random_and_adversarial, __import__("torch").float32)
+
+
+def test_gptq_pack_order_caught(monkeypatch):
+    orig = gq.pack_int32
+    def high_first(c, dim):
+        c = np.asarray(c)
+        c = c[::-1] if dim == 0 else c[:, ::-1]
+        return orig(np.ascontiguousarray(c), dim)
+    monkeypatch.setattr(gq, "pack_int32", high_first)
+    _fails(tg.test_pack_int32_examples)
+
+
+def test_gptq_sym_offset_caught(monkeypatch):
+    orig = gq.quantize_sym
+    def off7(w, group=128):
+        q = orig(w, group)
+        q["codes"] = np.clip(q["codes"].astype(int) - 1, 0, 15).astype(np.uint8)
+        q["qweight"] = gq.pack_int32(q["codes"], 0)
+        return q
+    monkeypatch.setattr(gq, "quantize_sym", off7)
+    _fails(tg.test_worked_example_sym)
+    _fails(tg.test_sym_bruteforce_exact, 128)
+
+
+def test_gptq_asym_zero_minus_one_caught(monkeypatch):
+    orig = gq.quantize_asym
+    def zm1(w, group=128):
+        q = orig(w, group)
+        q["qzeros"] = gq.pack_int32(np.clip(q["zp"].astype(int) - 1, 0, 15).astype(np.uint8), 1)
+        return q
+    monkeypatch.setattr(gq, "quantize_asym", zm1)
+    _fails(tg.test_worked_example_asym)
+
+
+def test_uintx_shard_order_caught(monkeypatch):
+    monkeypatch.setattr(ux, "SHARD_WIDTHS", (1, 2, 4, 8))
+    _fails(tu.test_pack_worked_examples)
+
+
+def test_uintx_dropped_bf16_rounding_caught(monkeypatch):
+    monkeypatch.setattr(ux, "bf", lambda x: np.asarray(x, np.float32))
+    _fails(tu.test_quantize_bruteforce_exact, 5)
+
+
+def test_awq_wrong_weighting_caught(monkeypatch):
+    orig = awq.clamp_stat
+    monkeypatch.setattr(awq, "clamp_stat", lambda a: (orig(a) / orig(a).mean()).astype(np.float32))
+    _fails(ts.test_weighted_error_bruteforce_exact)
+
+
+def test_snr_wrong_sign_caught(monkeypatch):
+    def plus(w, d):
+        w = np.asarray(w, np.float32); d = np.asarray(d, np.float32)
+        e = (w + d).astype(np.float64)
+        return float(np.sum(w.astype(np.float64) ** 2)), float(np.sum(e * e))
+    monkeypatch.setattr(snr, "sums", plus)
+    _fails(ts.test_snr_closed_form_relative_perturbation)
