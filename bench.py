@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Throughput of group-wise low-bit weight quantization on one MI355X.
+
+One step = the whole hot path over the gate_up-shaped bf16 weight [34816, 5120]:
+for each of MXFP4 (block 32), GPTQ symmetric and asymmetric (group 128) and affine
+uintx 2..7 bits (group 64): quantize+pack, unpack+dequantize to bf16, fused
+reconstruction SNR; then the AWQ alpha search (11 alphas) on the 2048-row strided
+subsample. Inputs are resident in HBM before timing starts.
+
+value = weight GB/s = (2 bytes * N * K) * (quantize + dequantize passes) / step time.
+The roofline object is for the kernel with the largest share of the step: its
+algorithmic bytes per launch / its average HIP-event duration, against 8 TB/s.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+N, K = 34816, 5120
+PEAK_HBM_GBPS = 8000.0
+FORMATS = [("mxfp4", 4, 32), ("gptq_sym", 4, 128), ("gptq_asym", 4, 128)] + \
+          [("uintx", b, 64) for b in range(2, 8)]
+ALPHAS = tuple(i / 10 for i in range(11))
+AWQ_ROWS = 2048
+
+
+def label(fmt, nbits):
+    return f"uintx{nbits}" if fmt == "uintx" else fmt
+
+
+def algo_bytes(op: str, fmt: str, nbits: int, n: int, k: int) -> float:
+    """Bytes the method must move per launch (intermediates stay on chip)."""
+    nk = n * k
+    if fmt == "mxfp4":
+        packed = nk / 2 + nk / 32                      # codes + e8m0
+    elif fmt.startswith("gptq"):
+        packed = nk / 2 + nk / 128 * 2                 # qweight + fp16 scales
+        if fmt == "gptq_asym" or op == "quant":
+            packed += nk / 128 / 2                     # qzeros (sym dequant ignores them)
+    else:
+        packed = nk * nbits / 8 + nk / 64 * 3          # shards + bf16 scale + uint8 zp
+    if op == "quant":
+        return 2 * nk + packed
+    if op == "dequant":
+        return packed + 2 * nk
+    if op == "snr":
+        return 2 * nk + packed
+    raise ValueError(op)
+
+
+def source_digest(name: str) -> str:
+    with open(os.path.join(ROOT, "group_wise_bit_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was taken on
+    the current source of that kernel; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_digest(rec["source"]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(W_cpu: torch.Tensor, a_cpu: torch.Tensor, rows: int, awq_rows: int):
+    """The oracle, as it stands, on the first `rows` rows (all formats: quantize,
+    dequantize, SNR) plus the AWQ search on `awq_rows` rows of the subsample."""
+    import oracle.awq as oawq
+    import oracle.gptq as ogq
+    import oracle.mxfp4 as omx
+    import oracle.snr as osnr
+    import oracle.uintx as oux
+
+    w = W_cpu[:rows].float().numpy()
+    wa = W_cpu[0:AWQ_ROWS * (N // AWQ_ROWS):N // AWQ_ROWS][:awq_rows].float().numpy()
+    t0 = time.perf_counter()
+    passes = 0
+    for fmt, nbits, g in FORMATS:
+        if fmt == "mxfp4":
+            p, e = omx.quantize(w)
+            d = omx.dequantize(p, e, K)
+        elif fmt.startswith("gptq"):
+            o = (ogq.quantize_sym if fmt == "gptq_sym" else ogq.quantize_asym)(w, g)
+            d = ogq.dequantize(o["qweight"], o["scales"], o["qzeros"], g, fmt == "gptq_sym")
+        else:
+            o = oux.quantize(w, nbits, g)
+            d = oux.dequantize(o["packed"], o["scale_bytes"], o["zero_point"], nbits, rows, K, g)
+        osnr.snr_db(w, d)
+        passes += 2
+    oawq.search(wa, a_cpu.numpy(), ALPHAS, max_rows=awq_rows)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(2.0 * rows * K * passes / dt / 1e9, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {rows} rows of the 34816x5120 weight through all 9 format variants "
+                  f"(quantize, dequantize, SNR) + AWQ search on {awq_rows} of the 2048 strided rows; "
+                  f"{dt:.1f} s single-threaded numpy; value uses the same weight-bytes formula as the GPU",
+        "seconds": round(dt, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=2176)          # 17 x 128: the step's 17:1 ratio
+    ap.add_argument("--cpu-awq-rows", type=int, default=128)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the quantization of "
+              "one weight is sharded by rows only in design; see the sharding notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    from group_wise_bit_amd import binding as gwb, workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    W_cpu = workloads.mxfp4_weight(N, K, seed=3)
+    a_cpu = workloads.awq_activation_stat(K, seed=5)
+    Wd = W_cpu.to(dev)
+    ad = a_cpu.to(dev)
+
+    # every buffer allocated up front: nothing is allocated in the timed region
+    qs = {label(f, b): gwb.quantize(Wd, f, nbits=b, group=g) for f, b, g in FORMATS}
+    deq = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(q.sizes["workspace"] for q in qs.values()) + 16, dtype=torch.uint8, device=dev)
+    snr_out = {k: torch.empty(3, dtype=torch.float64, device=dev) for k in qs}
+    awq_ws = torch.empty(gwb.awq_workspace_bytes(N, K, len(ALPHAS), AWQ_ROWS), dtype=torch.uint8, device=dev)
+    s_table = torch.empty(len(ALPHAS), K, dtype=torch.float32, device=dev)
+
+    ops = []   # (name, kernel key, algorithmic bytes, weight bytes, fn)
+    for f, b, g in FORMATS:
+        key = label(f, b)
+        q = qs[key]
+        ops.append((f"{key}.quant", f"{f}.quant", algo_bytes("quant", f, b, N, K), 2 * N * K,
+                    lambda f=f, b=b, g=g, q=q: gwb.quantize(Wd, f, nbits=b, group=g, out=q, workspace=ws)))
+        ops.append((f"{key}.dequant", f"{f}.dequant", algo_bytes("dequant", f, b, N, K), 2 * N * K,
+                    lambda q=q: gwb.dequantize(q, out=deq)))
+        ops.append((f"{key}.snr", f"{f}.snr", algo_bytes("snr", f, b, N, K), 0,
+                    lambda q=q, key=key: gwb.snr(Wd, q, workspace=ws, out=snr_out[key])))
+    awq_bytes = AWQ_ROWS * K * 2 + len(ALPHAS) * K * 4 + K * 4
+    ops.append(("awq.search", "awq", awq_bytes, 0,
+                lambda: gwb.awq_search(Wd, ad, ALPHAS, AWQ_ROWS, s_table=s_table, workspace=awq_ws)))
+
+    # same-run bandwidth ceiling: 1 GiB device-to-device with the library's copy kernel
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        gwb.stream_copy(dst, src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        gwb.stream_copy(dst, src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    # one event pair per op per step, created before the timed region
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
+           for _ in range(args.steps)]
+
+    def step(pairs):
+        for i, op in enumerate(ops):
+            if pairs is not None:
+                pairs[i][0].record()
+            op[4]()
+            if pairs is not None:
+                pairs[i][1].record()
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    durs = np.array([[e0.elapsed_time(e1) for e0, e1 in pairs] for pairs in evs])   # ms
+    avg = durs.mean(axis=0)
+    breakdown = []
+    for i, (name, key, abytes, wbytes, _) in enumerate(ops):
+        breakdown.append({
+            "op": name, "us": round(avg[i] * 1e3, 2),
+            "hbm_GBps": round(abytes / (avg[i] * 1e-3) / 1e9, 1),
+            "frac_hbm_peak": round(abytes / (avg[i] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "weight_GBps": round(wbytes / (avg[i] * 1e-3) / 1e9, 1) if wbytes else None,
+        })
+    dom = int(np.argmax(avg))
+    dname, dkey, dbytes = ops[dom][0], ops[dom][1], ops[dom][2]
+    achieved = dbytes / (avg[dom] * 1e-3) / 1e9
+    traffic = measured_traffic(dname)
+    weight_bytes_step = sum(op[3] for op in ops)
+    value = weight_bytes_step / (ms_per_step * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(W_cpu, a_cpu, args.cpu_rows, args.cpu_awq_rows)
+
+    line = {
+        "metric": "weight GB/s quantize+pack and unpack+dequant; % of HBM peak (34816x5120)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "bf16 [34816, 5120] (N(0, 0.015) x row gain lognormal(0, 0.5), seed 3): "
+                        "mxfp4 b32, gptq_sym g128, gptq_asym g128, uintx2..7 g64 -> quantize+pack, "
+                        "unpack+dequant to bf16, fused SNR; AWQ alpha search (11 alphas) on the 2048 "
+                        "strided rows with a[5120] lognormal(0, 1) seed 5",
+            "N": N, "K": K, "passes_per_step": sum(1 for op in ops if op[3]),
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": dname,
+            "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": int(dbytes), "avg_launch_us": round(avg[dom] * 1e3, 2),
+        },
+        "cpu_baseline": cpu,
+        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "breakdown": breakdown,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

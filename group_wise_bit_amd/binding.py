@@ -1,0 +1,242 @@
+"""Python binding of libgwb.so — group-wise low-bit weight quantization on MI355X.
+
+Thin Python binding of libgwb.so (C ABI in include/gwb.h). This module only
+marshals arguments: torch tensors provide device memory and the current HIP stream,
+every step of the method runs in the library's HIP kernels. There is no fallback: if
+the library is missing, importing this package raises.
+
+Formats ("fmt"): "gptq_sym", "gptq_asym", "mxfp4", "uintx".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional, Sequence
+
+import torch  # must come first: libgwb then binds to the HIP runtime torch loaded
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgwb.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m group_wise_bit_amd._build` "
+                      "(or __graft_entry__.build()) first")
+lib = ctypes.CDLL(LIB_PATH)
+
+OK, E_ARG, E_SHAPE, E_UNSUPPORTED, E_SIZE, E_HIP = 0, -1, -2, -3, -4, -5
+FORMATS = {"gptq_sym": 1, "gptq_asym": 2, "mxfp4": 3, "uintx": 4}
+DEFAULT_GROUP = {"gptq_sym": 128, "gptq_asym": 128, "mxfp4": 32, "uintx": 64}
+F32, BF16 = 0, 1
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+class QSpec(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("nbits", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("w_dtype", ctypes.c_int32)]
+
+
+class QTensors(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("g_idx", ctypes.c_void_p)]
+
+
+class Sizes(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_size_t), ("scales", ctypes.c_size_t), ("zeros", ctypes.c_size_t),
+                ("g_idx", ctypes.c_size_t), ("workspace", ctypes.c_size_t)]
+
+
+_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_SIGS = {
+    "gwb_query_sizes": [ctypes.POINTER(QSpec), _I64, _I64, ctypes.POINTER(Sizes)],
+    "gwb_quantize": [ctypes.POINTER(QSpec), _P, _I64, _I64, _I64, ctypes.POINTER(QTensors), _P, _SZ, _P],
+    "gwb_dequantize": [ctypes.POINTER(QSpec), ctypes.POINTER(QTensors), _I64, _I64, _P, _I32, _I64, _P, _SZ, _P],
+    "gwb_snr": [ctypes.POINTER(QSpec), _P, _I64, _I64, _I64, ctypes.POINTER(QTensors), _P, _P, _SZ, _P],
+    "gwb_awq_workspace": [_I64, _I64, _I32, _I64, ctypes.POINTER(_SZ)],
+    "gwb_awq_search_mxfp4": [_P, _I32, _I64, _I64, _I64, _P, _P, _I32, _I64, _P, _P, _P, _P, _SZ, _P],
+    "gwb_stream_copy": [_P, _P, _SZ, _P],
+}
+for _name, _args in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.argtypes = _args
+    _f.restype = ctypes.c_int
+lib.gwb_last_error.argtypes = []
+lib.gwb_last_error.restype = ctypes.c_char_p
+
+EXPORTS = tuple(_SIGS) + ("gwb_last_error",)
+
+
+class GwbError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"gwb error {code}: {msg}")
+        self.code = code
+
+
+def _check(rc: int) -> None:
+    if rc != OK:
+        raise GwbError(rc, lib.gwb_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_spec(fmt: str, nbits: int = 4, group: Optional[int] = None, w_dtype=torch.bfloat16) -> QSpec:
+    if fmt not in FORMATS:
+        raise ValueError(f"unknown format {fmt!r}")
+    return QSpec(FORMATS[fmt], nbits, DEFAULT_GROUP[fmt] if group is None else group,
+                 _DT.get(w_dtype, -1) if isinstance(w_dtype, torch.dtype) else int(w_dtype))
+
+
+def query_sizes(fmt: str, N: int, K: int, nbits: int = 4, group: Optional[int] = None,
+                w_dtype=torch.bfloat16) -> Dict[str, int]:
+    sp = make_spec(fmt, nbits, group, w_dtype)
+    s = Sizes()
+    _check(lib.gwb_query_sizes(ctypes.byref(sp), N, K, ctypes.byref(s)))
+    return {f: getattr(s, f) for f, _ in Sizes._fields_}
+
+
+def _alloc(nbytes: int, device) -> torch.Tensor:
+    # 256-byte aligned by the caching allocator; at least 16 bytes so the pointer is real
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def _views(fmt: str, N: int, K: int, group: int, sz, codes, scales, zeros, gidx):
+    """Typed views of the raw byte buffers (the layouts of gwb_qtensors)."""
+    out = {}
+    if fmt.startswith("gptq"):
+        out["qweight"] = codes[:sz["codes"]].view(torch.int32).view(K // 8, N)
+        out["scales"] = scales[:sz["scales"]].view(torch.float16).view(K // group, N)
+        out["qzeros"] = zeros[:sz["zeros"]].view(torch.int32).view(K // group, N // 8)
+        if gidx is not None:
+            out["g_idx"] = gidx[:sz["g_idx"]].view(torch.int32)
+    elif fmt == "mxfp4":
+        out["packed"] = codes[:sz["codes"]].view(N, K // 2)
+        out["e8m0"] = scales[:sz["scales"]].view(N, K // 32)
+    else:
+        out["packed"] = codes[:sz["codes"]]
+        out["scale_bytes"] = scales[:sz["scales"]].view(N, 2 * (K // group))
+        out["zero_point"] = zeros[:sz["zeros"]].view(N, K // group)
+    return out
+
+
+class Quantized:
+    """Raw buffers of one quantized weight plus typed views; pass it back to
+    dequantize() and snr()."""
+
+    def __init__(self, fmt, nbits, group, w_dtype, N, K, codes, scales, zeros, gidx, sizes):
+        self.fmt, self.nbits, self.group, self.w_dtype, self.N, self.K = fmt, nbits, group, w_dtype, N, K
+        self.codes, self.scales, self.zeros, self.gidx, self.sizes = codes, scales, zeros, gidx, sizes
+        self.views = _views(fmt, N, K, group, sizes, codes, scales, zeros, gidx)
+
+    def spec(self) -> QSpec:
+        return make_spec(self.fmt, self.nbits, self.group, self.w_dtype)
+
+    def qtensors(self) -> QTensors:
+        return QTensors(_ptr(self.codes), _ptr(self.scales), _ptr(self.zeros), _ptr(self.gidx))
+
+    def __getitem__(self, k):
+        return self.views[k]
+
+
+def _weight_args(W: torch.Tensor):
+    if W.dim() != 2 or W.dtype not in _DT or not W.is_cuda:
+        raise ValueError("W must be a 2-D float32 or bfloat16 CUDA tensor")
+    if W.stride(1) != 1:
+        raise ValueError("W must have unit stride along K")
+    return W.shape[0], W.shape[1], W.stride(0)
+
+
+def quantize(W: torch.Tensor, fmt: str, nbits: int = 4, group: Optional[int] = None,
+             with_g_idx: bool = True, out: Optional[Quantized] = None,
+             workspace: Optional[torch.Tensor] = None) -> Quantized:
+    """Quantize+pack W [N, K] into a new (or the given) Quantized."""
+    N, K, ldw = _weight_args(W)
+    group = DEFAULT_GROUP[fmt] if group is None else group
+    sp = make_spec(fmt, nbits, group, W.dtype)
+    sz = query_sizes(fmt, N, K, nbits, group, W.dtype)
+    if out is None:
+        dev = W.device
+        gidx = _alloc(sz["g_idx"], dev) if (fmt.startswith("gptq") and with_g_idx) else None
+        out = Quantized(fmt, nbits, group, W.dtype, N, K, _alloc(sz["codes"], dev), _alloc(sz["scales"], dev),
+                        _alloc(sz["zeros"], dev) if sz["zeros"] else None, gidx, sz)
+    if workspace is None and sz["workspace"]:
+        workspace = _alloc(sz["workspace"], W.device)
+    ws_b = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    qt = out.qtensors()
+    _check(lib.gwb_quantize(ctypes.byref(sp), _ptr(W), N, K, ldw, ctypes.byref(qt), _ptr(workspace), ws_b,
+                            _stream()))
+    return out
+
+
+def dequantize(q: Quantized, out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Unpack+dequantize to [N, K] of out_dtype (bf16 or f32)."""
+    if out is None:
+        out = torch.empty(q.N, q.K, dtype=out_dtype, device=q.codes.device)
+    if out.dtype not in _DT or out.stride(1) != 1:
+        raise ValueError("out must be float32 or bfloat16 with unit stride along K")
+    sp, qt = q.spec(), q.qtensors()
+    _check(lib.gwb_dequantize(ctypes.byref(sp), ctypes.byref(qt), q.N, q.K, _ptr(out), _DT[out.dtype],
+                              out.stride(0), None, 0, _stream()))
+    return out
+
+
+def snr(W: torch.Tensor, q: Quantized, workspace: Optional[torch.Tensor] = None,
+        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fused dequant + squared error. Returns a device float64 tensor
+    [sum w^2, sum (w - d)^2, SNR dB]."""
+    N, K, ldw = _weight_args(W)
+    if out is None:
+        out = torch.empty(3, dtype=torch.float64, device=W.device)
+    if workspace is None:
+        workspace = _alloc(q.sizes["workspace"], W.device)
+    sp, qt = q.spec(), q.qtensors()
+    _check(lib.gwb_snr(ctypes.byref(sp), _ptr(W), N, K, ldw, ctypes.byref(qt), _ptr(out), _ptr(workspace),
+                       workspace.numel(), _stream()))
+    return out
+
+
+def awq_workspace_bytes(N: int, K: int, n_alpha: int, max_rows: int = 2048) -> int:
+    b = ctypes.c_size_t()
+    _check(lib.gwb_awq_workspace(N, K, n_alpha, max_rows, ctypes.byref(b)))
+    return b.value
+
+
+DEFAULT_ALPHAS = tuple(i / 10 for i in range(11))
+
+
+def awq_search(W: torch.Tensor, a: torch.Tensor, alphas: Optional[Sequence[float]] = DEFAULT_ALPHAS,
+               max_rows: int = 2048, s_table: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """AWQ alpha search on MXFP4. With alphas=None, s_table [n_alpha, K] float32 is an
+    input (the scalings to evaluate); otherwise it is computed (and returned).
+    Returns device tensors: err float64 [n_alpha], best int32 [1], s_table."""
+    N, K, ldw = _weight_args(W)
+    if a.dtype != torch.float32 or a.numel() != K or not a.is_cuda:
+        raise ValueError("a must be a float32 CUDA tensor of K elements")
+    if alphas is None:
+        if s_table is None:
+            raise ValueError("alphas=None needs s_table")
+        n_alpha = s_table.shape[0]
+        host_alphas = None
+    else:
+        n_alpha = len(alphas)
+        host_alphas = (ctypes.c_double * n_alpha)(*alphas)
+        if s_table is None:
+            s_table = torch.empty(n_alpha, K, dtype=torch.float32, device=W.device)
+    err = torch.empty(n_alpha, dtype=torch.float64, device=W.device)
+    best = torch.empty(1, dtype=torch.int32, device=W.device)
+    if workspace is None:
+        workspace = _alloc(awq_workspace_bytes(N, K, n_alpha, max_rows), W.device)
+    _check(lib.gwb_awq_search_mxfp4(_ptr(W), _DT[W.dtype], N, K, ldw, _ptr(a.contiguous()),
+                                    host_alphas, n_alpha, max_rows, _ptr(s_table), _ptr(err), _ptr(best),
+                                    _ptr(workspace), workspace.numel(), _stream()))
+    return {"err": err, "best": best, "s_table": s_table}
+
+
+def stream_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
+    n = src.numel() * src.element_size()
+    _check(lib.gwb_stream_copy(_ptr(dst), _ptr(src), n, _stream()))

@@ -1,0 +1,292 @@
+// C ABI of libgwb: argument validation, buffer sizes, launch selection. Declared in
+// include/gwb.h. Everything is validated before the first launch, so a non-zero return
+// means nothing was enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "gwb.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return GWB_OK;
+}
+
+int hip_check(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(GWB_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Kernels index elements with 32-bit unsigned integers.
+constexpr int64_t kMaxElems = (int64_t)1 << 31;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t elem_size(int32_t dt) { return dt == GWB_F32 ? 4 : 2; }
+
+int check_spec(const gwb_qspec* sp, int64_t N, int64_t K) {
+  if (!sp) return fail(GWB_E_ARG, "spec is NULL");
+  if (N < 0 || K < 0) return fail(GWB_E_ARG, "negative shape N=%lld K=%lld", (long long)N, (long long)K);
+  if (sp->w_dtype != GWB_F32 && sp->w_dtype != GWB_BF16)
+    return fail(GWB_E_ARG, "unknown w_dtype %d", sp->w_dtype);
+  if (N > 0 && K > 0 && (N >= kMaxElems || K >= kMaxElems || N * K >= kMaxElems))
+    return fail(GWB_E_UNSUPPORTED, "N*K = %lld exceeds 2^31 elements", (long long)(N * K));
+  switch (sp->format) {
+    case GWB_GPTQ_SYM:
+    case GWB_GPTQ_ASYM:
+      if (sp->nbits != 4) return fail(GWB_E_ARG, "GPTQ is 4-bit, got nbits=%d", sp->nbits);
+      if (sp->group <= 0) return fail(GWB_E_ARG, "group must be positive, got %d", sp->group);
+      if (sp->group != 32 && sp->group != 64 && sp->group != 128)
+        return fail(GWB_E_UNSUPPORTED, "GPTQ group %d not provided (32, 64, 128)", sp->group);
+      if (K % sp->group) return fail(GWB_E_SHAPE, "K=%lld not divisible by group %d", (long long)K, sp->group);
+      if (N % 8) return fail(GWB_E_SHAPE, "GPTQ qzeros pack 8 columns per int32: N=%lld not divisible by 8",
+                             (long long)N);
+      return GWB_OK;
+    case GWB_MXFP4:
+      if (sp->nbits != 4) return fail(GWB_E_ARG, "MXFP4 is 4-bit, got nbits=%d", sp->nbits);
+      if (sp->group != 32) return fail(GWB_E_UNSUPPORTED, "MXFP4 blocks are 32 weights, got group %d", sp->group);
+      if (K % 32) return fail(GWB_E_SHAPE, "K=%lld not divisible by 32", (long long)K);
+      return GWB_OK;
+    case GWB_UINTX:
+      if (sp->nbits == 8)
+        return fail(GWB_E_UNSUPPORTED, "uint8 is refused: it was always left unquantized");
+      if (sp->nbits < 2 || sp->nbits > 8) return fail(GWB_E_ARG, "uintx nbits must be 2..7, got %d", sp->nbits);
+      if (sp->group != 64) return fail(GWB_E_UNSUPPORTED, "uintx group %d not provided (64)", sp->group);
+      if (sp->w_dtype != GWB_BF16)
+        return fail(GWB_E_UNSUPPORTED, "uintx arithmetic is bfloat16; w_dtype must be GWB_BF16");
+      if (K % sp->group) return fail(GWB_E_SHAPE, "K=%lld not divisible by group %d", (long long)K, sp->group);
+      return GWB_OK;
+    default:
+      return fail(GWB_E_ARG, "unknown format %d", sp->format);
+  }
+}
+
+size_t uintx_packed_bytes(int nbits, int64_t numel) {
+  size_t b = 0;
+  if (nbits & 4) b += (size_t)((numel + 1) / 2);
+  if (nbits & 2) b += (size_t)((numel + 3) / 4);
+  if (nbits & 1) b += (size_t)((numel + 7) / 8);
+  return b;
+}
+
+unsigned err_blocks(const gwb_qspec* sp, int64_t N, int64_t K) {
+  switch (sp->format) {
+    case GWB_MXFP4: return gwb::mxfp4_err_blocks(N, K);
+    case GWB_UINTX: return gwb::uintx_err_blocks(N, K);
+    default: return gwb::gptq_err_blocks(sp->group, N, K);
+  }
+}
+
+gwb_sizes sizes_of(const gwb_qspec* sp, int64_t N, int64_t K) {
+  gwb_sizes s{};
+  const int64_t G = sp->group;
+  switch (sp->format) {
+    case GWB_GPTQ_SYM:
+    case GWB_GPTQ_ASYM:
+      s.codes = (size_t)(K / 8 * N * 4);
+      s.scales = (size_t)(K / G * N * 2);
+      s.zeros = (size_t)(K / G * (N / 8) * 4);
+      s.g_idx = (size_t)(K * 4);
+      break;
+    case GWB_MXFP4:
+      s.codes = (size_t)(N * K / 2);
+      s.scales = (size_t)(N * K / 32);
+      break;
+    default:
+      s.codes = uintx_packed_bytes(sp->nbits, N * K);
+      s.scales = (size_t)(N * (K / G) * 2);
+      s.zeros = (size_t)(N * (K / G));
+      break;
+  }
+  size_t ws = 0;
+  if (N > 0 && K > 0) {
+    ws = (size_t)err_blocks(sp, N, K) * 2 * sizeof(double);
+    if (sp->format == GWB_UINTX) {
+      size_t c = gwb::uintx_code_workspace(N, K);
+      ws = c > ws ? c : ws;
+    }
+  }
+  s.workspace = ws;
+  return s;
+}
+
+int check_weight(const gwb_qspec* sp, const void* W, int64_t K, int64_t ldw) {
+  if (!W) return fail(GWB_E_ARG, "W is NULL");
+  if (ldw < K) return fail(GWB_E_ARG, "ldw=%lld < K=%lld", (long long)ldw, (long long)K);
+  if (!aligned16(W) || ((size_t)ldw * elem_size(sp->w_dtype)) % 16)
+    return fail(GWB_E_UNSUPPORTED, "W and its row stride must be 16-byte aligned");
+  return GWB_OK;
+}
+
+int check_tensors(const gwb_qspec* sp, const gwb_qtensors* q) {
+  if (!q) return fail(GWB_E_ARG, "tensors struct is NULL");
+  if (!q->codes || !q->scales) return fail(GWB_E_ARG, "codes and scales are required");
+  if (sp->format != GWB_MXFP4 && !q->zeros) return fail(GWB_E_ARG, "zeros is required for this format");
+  if (!aligned16(q->codes) || !aligned16(q->scales) || (q->zeros && !aligned16(q->zeros)))
+    return fail(GWB_E_UNSUPPORTED, "quantized tensors must be 16-byte aligned");
+  return GWB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gwb_last_error(void) { return g_err.c_str(); }
+
+int gwb_query_sizes(const gwb_qspec* spec, int64_t N, int64_t K, gwb_sizes* out) {
+  if (int rc = check_spec(spec, N, K)) return rc;
+  if (!out) return fail(GWB_E_ARG, "out is NULL");
+  *out = sizes_of(spec, N, K);
+  return ok();
+}
+
+int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
+                 const gwb_qtensors* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = check_spec(spec, N, K)) return rc;
+  if (N == 0 || K == 0) return ok();          // empty: valid, nothing to enqueue
+  if (int rc = check_weight(spec, W, K, ldw)) return rc;
+  if (int rc = check_tensors(spec, out)) return rc;
+  if (spec->format == GWB_UINTX && gwb::uintx_code_workspace(N, K) > 0 &&
+      (!workspace || workspace_bytes < gwb::uintx_code_workspace(N, K)))
+    return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", gwb::uintx_code_workspace(N, K),
+                workspace_bytes);
+  hipStream_t st = (hipStream_t)stream;
+  switch (spec->format) {
+    case GWB_GPTQ_SYM:
+    case GWB_GPTQ_ASYM:
+      gwb::launch_gptq_quant(spec->format == GWB_GPTQ_SYM, spec->group, W, spec->w_dtype, N, K, ldw, out->codes,
+                             out->scales, out->zeros, out->g_idx, st);
+      break;
+    case GWB_MXFP4:
+      gwb::launch_mxfp4_quant(W, spec->w_dtype, N, K, ldw, out->codes, out->scales, st);
+      break;
+    default:
+      gwb::launch_uintx_quant(spec->nbits, W, N, K, ldw, out->codes, out->scales, out->zeros, workspace, st);
+  }
+  return hip_check("quantize launch");
+}
+
+int gwb_dequantize(const gwb_qspec* spec, const gwb_qtensors* in, int64_t N, int64_t K, void* out,
+                   int32_t out_dtype, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (int rc = check_spec(spec, N, K)) return rc;
+  if (out_dtype != GWB_F32 && out_dtype != GWB_BF16) return fail(GWB_E_ARG, "unknown out_dtype %d", out_dtype);
+  if (N == 0 || K == 0) return ok();          // empty: valid, nothing to enqueue
+  if (int rc = check_tensors(spec, in)) return rc;
+  if (!out) return fail(GWB_E_ARG, "out is NULL");
+  if (ldo < K) return fail(GWB_E_ARG, "ldo=%lld < K=%lld", (long long)ldo, (long long)K);
+  if (!aligned16(out) || ((size_t)ldo * elem_size(out_dtype)) % 16)
+    return fail(GWB_E_UNSUPPORTED, "out and its row stride must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  switch (spec->format) {
+    case GWB_GPTQ_SYM:
+    case GWB_GPTQ_ASYM:
+      gwb::launch_gptq_dequant(spec->format == GWB_GPTQ_SYM, spec->group, in->codes, in->scales, in->zeros, N, K,
+                               out, out_dtype, ldo, st);
+      break;
+    case GWB_MXFP4:
+      gwb::launch_mxfp4_dequant(in->codes, in->scales, N, K, out, out_dtype, ldo, st);
+      break;
+    default:
+      gwb::launch_uintx_dequant(spec->nbits, in->codes, in->scales, in->zeros, N, K, out, out_dtype, ldo, st);
+  }
+  return hip_check("dequantize launch");
+}
+
+int gwb_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw, const gwb_qtensors* in,
+            double* d_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = check_spec(spec, N, K)) return rc;
+  if (int rc = check_weight(spec, W, K, ldw)) return rc;
+  if (int rc = check_tensors(spec, in)) return rc;
+  if (!d_out) return fail(GWB_E_ARG, "d_out is NULL");
+  if (N == 0 || K == 0) return fail(GWB_E_SHAPE, "SNR of an empty matrix is undefined");
+  const unsigned nb = err_blocks(spec, N, K);
+  const size_t need = (size_t)nb * 2 * sizeof(double);
+  if (!workspace || workspace_bytes < need)
+    return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  double* part = (double*)workspace;
+  switch (spec->format) {
+    case GWB_GPTQ_SYM:
+    case GWB_GPTQ_ASYM:
+      gwb::launch_gptq_err(spec->format == GWB_GPTQ_SYM, spec->group, W, spec->w_dtype, N, K, ldw, in->codes,
+                           in->scales, in->zeros, part, st);
+      break;
+    case GWB_MXFP4:
+      gwb::launch_mxfp4_err(W, spec->w_dtype, N, K, ldw, in->codes, in->scales, part, st);
+      break;
+    default:
+      gwb::launch_uintx_err(spec->nbits, W, N, K, ldw, in->codes, in->scales, in->zeros, part, st);
+  }
+  gwb::launch_err_finalize(part, nb, d_out, st);
+  return hip_check("snr launch");
+}
+
+static int awq_rows(int64_t N, int64_t max_rows, int64_t* rows, int64_t* step) {
+  *step = N / max_rows > 1 ? N / max_rows : 1;
+  int64_t avail = (N + *step - 1) / *step;
+  *rows = avail < max_rows ? avail : max_rows;
+  return 0;
+}
+
+int gwb_awq_workspace(int64_t N, int64_t K, int32_t n_alpha, int64_t max_rows, size_t* bytes) {
+  if (!bytes) return fail(GWB_E_ARG, "bytes is NULL");
+  if (N <= 0 || K <= 0 || max_rows <= 0) return fail(GWB_E_ARG, "N, K and max_rows must be positive");
+  if (n_alpha < 1 || n_alpha > 16) return fail(GWB_E_ARG, "n_alpha must be 1..16, got %d", n_alpha);
+  int64_t rows, step;
+  awq_rows(N, max_rows, &rows, &step);
+  *bytes = (size_t)gwb::awq_blocks(rows, K) * (size_t)n_alpha * sizeof(double);
+  return ok();
+}
+
+int gwb_awq_search_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw, const float* d_a,
+                         const double* alphas, int32_t n_alpha, int64_t max_rows, float* d_s_table, double* d_err,
+                         int32_t* d_best, void* workspace, size_t workspace_bytes, void* stream) {
+  gwb_qspec sp{GWB_MXFP4, 4, 32, w_dtype};
+  if (N <= 0 || K <= 0) return fail(GWB_E_ARG, "N and K must be positive");
+  if (int rc = check_spec(&sp, N, K)) return rc;
+  if (int rc = check_weight(&sp, W, K, ldw)) return rc;
+  if (!d_a || !d_s_table || !d_err || !d_best) return fail(GWB_E_ARG, "a, s_table, err and best are required");
+  if (!aligned16(d_s_table) || !aligned16(d_a)) return fail(GWB_E_UNSUPPORTED, "a and s_table must be 16-byte aligned");
+  if (n_alpha < 1 || n_alpha > 16) return fail(GWB_E_ARG, "n_alpha must be 1..16, got %d", n_alpha);
+  if (max_rows <= 0) return fail(GWB_E_ARG, "max_rows must be positive");
+  int64_t rows, step;
+  awq_rows(N, max_rows, &rows, &step);
+  const size_t need = (size_t)gwb::awq_blocks(rows, K) * (size_t)n_alpha * sizeof(double);
+  if (!workspace || workspace_bytes < need)
+    return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  gwb::launch_awq(W, w_dtype, rows, step, K, ldw, d_a, alphas, n_alpha, d_s_table, d_err, d_best,
+                  (double*)workspace, nullptr, (hipStream_t)stream);
+  return hip_check("awq launch");
+}
+
+int gwb_stream_copy(void* d_dst, const void* d_src, size_t bytes, void* stream) {
+  if (!d_dst || !d_src) return fail(GWB_E_ARG, "NULL pointer");
+  if (bytes % 16 || !aligned16(d_dst) || !aligned16(d_src))
+    return fail(GWB_E_UNSUPPORTED, "copy needs 16-byte aligned pointers and a multiple of 16 bytes");
+  if (bytes == 0) return ok();
+  gwb::launch_stream_copy(d_dst, d_src, bytes, (hipStream_t)stream);
+  return hip_check("copy launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// Reduction of the fused error kernels' per-block partial sums, and the bandwidth
+// reference copy used by the benchmark.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace gwb {
+
+// part[2*i], part[2*i+1] for i < nblocks -> out[0] = sum w^2, out[1] = sum (w-d)^2,
+// out[2] = 10 log10(out[0] / max(out[1], 1e-24)) (page export_gptq_cpu.py's
+// 20 log10(||w|| / max(||w - deq||, 1e-12)), squared inside the log). One block,
+// fixed summation order.
+__global__ __launch_bounds__(256) void err_finalize_kernel(const double* __restrict__ part,
+                                                           unsigned nblocks, double* __restrict__ out) {
+  __shared__ double sa[256], sb[256];
+  double a = 0.0, b = 0.0;
+  for (unsigned i = threadIdx.x; i < nblocks; i += 256) {
+    a += part[2 * i];
+    b += part[2 * i + 1];
+  }
+  sa[threadIdx.x] = a;
+  sb[threadIdx.x] = b;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) {
+      sa[threadIdx.x] += sa[threadIdx.x + s];
+      sb[threadIdx.x] += sb[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    double w2 = sa[0], e2 = sb[0];
+    out[0] = w2;
+    out[1] = e2;
+    out[2] = w2 == 0.0 ? -__builtin_inf() : 10.0 * log10(w2 / fmax(e2, 1e-24));
+  }
+}
+
+void launch_err_finalize(const double* part, unsigned nblocks, double* out, hipStream_t st) {
+  hipLaunchKernelGGL(err_finalize_kernel, dim3(1), dim3(256), 0, st, part, nblocks, out);
+}
+
+__global__ __launch_bounds__(256) void stream_copy_kernel(U4* __restrict__ dst, const U4* __restrict__ src,
+                                                          uint64_t n16) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    dst[i] = src[i];
+}
+
+void launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t st) {
+  uint64_t n16 = bytes / 16;
+  uint64_t g = (n16 + 255) / 256;
+  unsigned grid = (unsigned)(g < kStreamGridCap ? (g ? g : 1) : kStreamGridCap);
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(grid), dim3(256), 0, st, (U4*)dst, (const U4*)src, n16);
+}
+
+}  // namespace gwb

@@ -1,0 +1,145 @@
+// Device helpers shared by the gfx950 kernels: DPP group reductions within a
+// 64-wide wavefront, bfloat16 bit conversions, 32-bit fast division and the
+// workspace reduction used by the fused error kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gwb {
+
+// ---------------------------------------------------------------- DPP controls
+// quad_perm(1,0,3,2): lane i reads lane i^1;  quad_perm(2,3,0,1): lane i reads i^2.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+// row_half_mirror: within each 8 lanes, lane i reads 7-i (after the quad steps every
+// quad is uniform, so this joins the two quads of an 8-lane half-row).
+constexpr int kDppHalfMirror = 0x141;
+// row_mirror: within each 16-lane row, lane i reads 15-i (joins the two half-rows).
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_read(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_read_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+
+// Max / min over LANES consecutive, aligned lanes (LANES in {1, 2, 4, 8, 16}); every
+// lane of the set ends with the result. All sources lie inside the set.
+template <int LANES>
+__device__ __forceinline__ float lanes_max(float x) {
+  if constexpr (LANES >= 2) x = fmaxf(x, dpp_read<kDppXor1>(x));
+  if constexpr (LANES >= 4) x = fmaxf(x, dpp_read<kDppXor2>(x));
+  if constexpr (LANES >= 8) x = fmaxf(x, dpp_read<kDppHalfMirror>(x));
+  if constexpr (LANES >= 16) x = fmaxf(x, dpp_read<kDppMirror>(x));
+  static_assert(LANES <= 16, "groups wider than a DPP row are not used");
+  return x;
+}
+template <int LANES>
+__device__ __forceinline__ float lanes_min(float x) {
+  if constexpr (LANES >= 2) x = fminf(x, dpp_read<kDppXor1>(x));
+  if constexpr (LANES >= 4) x = fminf(x, dpp_read<kDppXor2>(x));
+  if constexpr (LANES >= 8) x = fminf(x, dpp_read<kDppHalfMirror>(x));
+  if constexpr (LANES >= 16) x = fminf(x, dpp_read<kDppMirror>(x));
+  return x;
+}
+
+// ---------------------------------------------------------------- bfloat16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// float32 -> bfloat16 bits, round to nearest, ties to even (finite and inf inputs;
+// subnormals round like any other value since bfloat16 shares float32's exponent).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (b >> 16) | 0x40u;  // NaN stays NaN
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+// float32 rounded to the nearest bfloat16 value, kept as a float32.
+__device__ __forceinline__ float round_bf16(float f) {
+  return __uint_as_float(f32_to_bf16_rne(f) << 16);
+}
+
+// ---------------------------------------------------------------- fast division
+// q = n / d for 0 <= n < 2^31 via q = (umulhi(n, m) + n) >> s (Granlund-Montgomery).
+struct FastDiv {
+  uint32_t d, m, s;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f{d, 0u, 0u};
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  f.s = s;
+  f.m = (uint32_t)((((1ull << s) - d) << 32) / d + 1);
+  return f;
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (uint32_t)(((uint64_t)__umulhi(n, f.m) + n) >> f.s);
+}
+
+// ---------------------------------------------------------------- loads
+struct alignas(16) U4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ U4 ld16(const void* p) {
+  return *reinterpret_cast<const U4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, U4 v) { *reinterpret_cast<U4*>(p) = v; }
+
+// Load 8 consecutive weights (16-byte aligned start) as float32.
+__device__ __forceinline__ void load8(const uint16_t* p, float* x) {
+  U4 v = ld16(p);
+  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+__device__ __forceinline__ void load8(const float* p, float* x) {
+  U4 a = ld16(p), b = ld16(p + 4);
+  x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
+  x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
+  x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
+  x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
+}
+
+// Store 8 float32 values as bf16 (RNE) or as float32.
+__device__ __forceinline__ void store8(uint16_t* p, const float* d) {
+  U4 v;
+  v.x = f32_to_bf16_rne(d[0]) | (f32_to_bf16_rne(d[1]) << 16);
+  v.y = f32_to_bf16_rne(d[2]) | (f32_to_bf16_rne(d[3]) << 16);
+  v.z = f32_to_bf16_rne(d[4]) | (f32_to_bf16_rne(d[5]) << 16);
+  v.w = f32_to_bf16_rne(d[6]) | (f32_to_bf16_rne(d[7]) << 16);
+  st16(p, v);
+}
+__device__ __forceinline__ void store8(float* p, const float* d) {
+  U4 a{__float_as_uint(d[0]), __float_as_uint(d[1]), __float_as_uint(d[2]), __float_as_uint(d[3])};
+  U4 b{__float_as_uint(d[4]), __float_as_uint(d[5]), __float_as_uint(d[6]), __float_as_uint(d[7])};
+  st16(p, a);
+  st16(p + 4, b);
+}
+
+// ---------------------------------------------------------------- error sums
+// Block-wide sum of two doubles; thread 0 writes them to part[2*blockIdx.x].
+// Fixed tree order, so the result is deterministic for a given launch shape.
+template <int THREADS>
+__device__ __forceinline__ void block_sum2_store(double a, double b, double* part) {
+  __shared__ double sa[THREADS], sb[THREADS];
+  sa[threadIdx.x] = a;
+  sb[threadIdx.x] = b;
+  __syncthreads();
+#pragma unroll
+  for (int s = THREADS / 2; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) {
+      sa[threadIdx.x] += sa[threadIdx.x + s];
+      sb[threadIdx.x] += sb[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    part[2 * blockIdx.x] = sa[0];
+    part[2 * blockIdx.x + 1] = sb[0];
+  }
+}
+
+}  // namespace gwb

@@ -1,0 +1,66 @@
+// Internal launchers of libgwb (host side). Arguments have been validated by the
+// C ABI layer (api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gwb {
+
+constexpr int kF32 = 0;   // gwb_dtype values
+constexpr int kBF16 = 1;
+constexpr int kStore = 0;  // dequant sinks
+constexpr int kErr = 1;
+
+// Grid caps: streaming kernels loop over their units grid-stride. The error kernels
+// keep their block count (and so their partial-sum layout) bounded.
+constexpr unsigned kStreamGridCap = 1u << 20;
+constexpr unsigned kErrGridCap = 4096;
+
+// ---- MXFP4 (mxfp4.hip)
+void launch_mxfp4_quant(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
+                        void* packed, void* e8m0, hipStream_t st);
+void launch_mxfp4_dequant(const void* packed, const void* e8m0, int64_t N, int64_t K, void* out,
+                          int32_t out_dtype, int64_t ldo, hipStream_t st);
+unsigned mxfp4_err_blocks(int64_t N, int64_t K);
+void launch_mxfp4_err(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
+                      const void* packed, const void* e8m0, double* part, hipStream_t st);
+
+// ---- GPTQ (gptq.hip); sym selects uint4b8, otherwise asymmetric with stored zp
+void launch_gptq_quant(bool sym, int group, const void* W, int32_t w_dtype, int64_t N, int64_t K,
+                       int64_t ldw, void* qweight, void* scales, void* qzeros, void* g_idx,
+                       hipStream_t st);
+void launch_gptq_dequant(bool sym, int group, const void* qweight, const void* scales,
+                         const void* qzeros, int64_t N, int64_t K, void* out, int32_t out_dtype,
+                         int64_t ldo, hipStream_t st);
+unsigned gptq_err_blocks(int group, int64_t N, int64_t K);
+void launch_gptq_err(bool sym, int group, const void* W, int32_t w_dtype, int64_t N, int64_t K,
+                     int64_t ldw, const void* qweight, const void* scales, const void* qzeros,
+                     double* part, hipStream_t st);
+
+// ---- UINTX (uintx.hip)
+bool uintx_tiled(int64_t N, int64_t K);   // shard lengths nest: N*K % 512 == 0
+size_t uintx_code_workspace(int64_t N, int64_t K);
+void launch_uintx_quant(int nbits, const void* W, int64_t N, int64_t K, int64_t ldw, void* packed,
+                        void* scales, void* zeros, void* workspace, hipStream_t st);
+void launch_uintx_dequant(int nbits, const void* packed, const void* scales, const void* zeros,
+                          int64_t N, int64_t K, void* out, int32_t out_dtype, int64_t ldo,
+                          hipStream_t st);
+unsigned uintx_err_blocks(int64_t N, int64_t K);
+void launch_uintx_err(int nbits, const void* W, int64_t N, int64_t K, int64_t ldw, const void* packed,
+                      const void* scales, const void* zeros, double* part, hipStream_t st);
+
+// ---- error finalize (common.hip): part[2*nblocks] -> out[3] = {sum w^2, sum e^2, dB}
+void launch_err_finalize(const double* part, unsigned nblocks, double* out, hipStream_t st);
+
+// ---- AWQ (awq.hip)
+unsigned awq_blocks(int64_t rows, int64_t K);
+void launch_awq(const void* W, int32_t w_dtype, int64_t rows, int64_t row_step, int64_t K,
+                int64_t ldw, const float* a, const double* alphas, int n_alpha, float* s_table,
+                double* err, int32_t* best, double* part, double* stat, hipStream_t st);
+
+// ---- measurement copy (common.hip)
+void launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
+
+}  // namespace gwb

@@ -1,0 +1,170 @@
+/*
+ * gwb.h — group-wise low-bit weight quantization on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libgwb.so. A linear layer's weight W is [N, K] (N output rows, K input
+ * channels, K contiguous within a row, row stride ldw elements). Groups run along K.
+ * Three formats, as the source pages define them:
+ *
+ *   GWB_GPTQ_SYM   page export_gptq_cpu.py, quantize_sym and the module docstring's
+ *                  uint4b8 convention: w = (code - 8) * scale, code in [0, 15].
+ *   GWB_GPTQ_ASYM  same page, quantize_asym: w = (code - zp) * scale, zp stored as is.
+ *   GWB_MXFP4      page quantize_dflash_mxfp4.py, quantize_mxfp4 / dequantize_mxfp4:
+ *                  e2m1 codes (round half to even), an E8M0 exponent per 32 weights.
+ *   GWB_UINTX      page uintx_quant.py, UIntXQuantizer: affine uint2..uint7 with
+ *                  preserve_zero, arithmetic in bfloat16, planar power-of-two shards.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named d_* and every tensor pointer are DEVICE pointers owned by the
+ *     caller (for example torch tensors). The library never allocates or frees device
+ *     memory; buffers it needs beyond inputs and outputs come in as `workspace`.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued
+ *     asynchronously; nothing synchronizes except where stated.
+ *   - Arguments are validated before anything is enqueued. On a non-zero return no
+ *     kernel was launched and no output was written; gwb_last_error() describes why.
+ *   - Empty shapes (N == 0 or K == 0) are valid and enqueue nothing.
+ */
+#ifndef GWB_H
+#define GWB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GWB_OK = 0,
+  GWB_E_ARG = -1,          /* NULL where a pointer is required, unknown enum, negative size */
+  GWB_E_SHAPE = -2,        /* shape not divisible as the format requires */
+  GWB_E_UNSUPPORTED = -3,  /* refused, as the pages refuse it (uintx nbits 8) or not provided */
+  GWB_E_SIZE = -4,         /* a caller-declared buffer size is too small */
+  GWB_E_HIP = -5           /* a HIP launch failed; gwb_last_error() names it */
+} gwb_status;
+
+typedef enum { GWB_GPTQ_SYM = 1, GWB_GPTQ_ASYM = 2, GWB_MXFP4 = 3, GWB_UINTX = 4 } gwb_format;
+typedef enum { GWB_F32 = 0, GWB_BF16 = 1 } gwb_dtype;
+
+/* What to quantize to.
+ *   format  gwb_format
+ *   nbits   4 for GPTQ and MXFP4; 2..7 for UINTX (8 is refused with GWB_E_UNSUPPORTED:
+ *           page uintx_quant.py, can_quantize, always left uint8 layers unquantized)
+ *   group   GPTQ: 32, 64 or 128 (page export_gptq_cpu.py, --group, default 128);
+ *           MXFP4: 32 (the page's GROUP); UINTX: 64 (UIntXQuantizer's group_size)
+ *   w_dtype gwb_dtype of W. UINTX requires GWB_BF16 (its arithmetic is bfloat16).   */
+typedef struct {
+  int32_t format;
+  int32_t nbits;
+  int32_t group;
+  int32_t w_dtype;
+} gwb_qspec;
+
+/* The quantized tensors (device pointers), per format:
+ *   GPTQ   codes  int32 qweight [K/8, N]: nibble i of word (r, n) = code(k = 8r+i, n)
+ *          scales fp16 [K/G, N]: the float32 group scale rounded to fp16 (RNE)
+ *          zeros  int32 qzeros [K/G, N/8]: nibble i of word (g, q) = zero point of
+ *                 column 8q+i; symmetric: every nibble 7; asymmetric: zp itself
+ *          g_idx  int32 [K] = k / G; optional on output (NULL skips), unused on input
+ *   MXFP4  codes  uint8 [N, K/2]: byte = code(2i) | code(2i+1) << 4, code = e2m1
+ *                 magnitude index | sign << 3
+ *          scales uint8 e8m0 [N, K/32] = exponent + 127;  zeros, g_idx unused (NULL)
+ *   UINTX  codes  uint8 flat: one planar shard per power of two present in nbits, in
+ *                 the order 4, 2, 1 (bits [off, off+k) of a code in the k-bit shard,
+ *                 off counted from 0); shard k has ceil(N*K / (8/k)) bytes; byte i of
+ *                 shard k = OR_j field(code[j*L + i]) << (j*k), L = that byte count,
+ *                 codes taken in row-major order, zero-padded
+ *          scales bfloat16 [N, K/G] (the bytes of the bf16 values, little-endian)
+ *          zeros  uint8 [N, K/G] zero points in [0, 2**nbits - 1]; g_idx unused     */
+typedef struct {
+  void* codes;
+  void* scales;
+  void* zeros;
+  void* g_idx;
+} gwb_qtensors;
+
+/* Byte sizes of the quantized tensors and of the workspace that gwb_quantize,
+ * gwb_dequantize and gwb_snr need for (spec, N, K). */
+typedef struct {
+  size_t codes;
+  size_t scales;
+  size_t zeros;
+  size_t g_idx;
+  size_t workspace;
+} gwb_sizes;
+
+/* Validate (spec, N, K) and report buffer sizes. Host only, launches nothing.
+ * Returns GWB_E_ARG / GWB_E_SHAPE / GWB_E_UNSUPPORTED as the format requires:
+ *   GPTQ: K % group == 0, N % 8 == 0 (qzeros pack 8 columns per word);
+ *   MXFP4: K % 32 == 0 (page quantize_mxfp4 asserts it);
+ *   UINTX: K % group == 0 (can_quantize refuses otherwise).                      */
+int gwb_query_sizes(const gwb_qspec* spec, int64_t N, int64_t K, gwb_sizes* out);
+
+/* Quantize and pack W [N, K] (row stride ldw >= K elements, of spec->w_dtype).
+ * Steps: per-group reduction (GPTQ sym amax, asym min/max, MXFP4 amax, UINTX
+ * min/max extended to 0), scale and zero-point selection, round-and-clamp to codes,
+ * bit packing; page export_gptq_cpu.py quantize_sym / quantize_asym / pack_int32,
+ * page quantize_dflash_mxfp4.py quantize_mxfp4, page uintx_quant.py _quantize_impl /
+ * pack_uintx. Every code, zero point, E8M0 byte and stored scale is bit-exact with
+ * the step list of those passages (round half to even everywhere).
+ * workspace/workspace_bytes: at least gwb_sizes.workspace bytes (may be NULL if 0). */
+int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
+                 const gwb_qtensors* out, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/* Unpack and dequantize into out [N, K] (row stride ldo >= K) of out_dtype, in the
+ * weight's own [N, K] layout for every format (the GPTQ transpose is undone).
+ * GPTQ: (code - 8) * scale or (code - zp) * scale with the fp16 scale widened;
+ * MXFP4: +-E2M1[code & 7] * 2**(e8m0 - 127); UINTX: bf16(bf16(q - zp) * scale);
+ * page export_gptq_cpu.py (module docstring), page quantize_dflash_mxfp4.py
+ * dequantize_mxfp4, page uintx_quant.py _dequantize_native. Each value is the
+ * correctly rounded result of an exact product, so bf16 and f32 outputs are exact
+ * roundings. workspace as for gwb_quantize. */
+int gwb_dequantize(const gwb_qspec* spec, const gwb_qtensors* in, int64_t N, int64_t K,
+                   void* out, int32_t out_dtype, int64_t ldo, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Reconstruction SNR of stored tensors against W, fused (the dequantized matrix is
+ * never written). d_out (device, 3 doubles) receives
+ *   d_out[0] = sum w**2, d_out[1] = sum (w - d)**2 (w - d a float32 subtraction, sums
+ *   in float64), d_out[2] = 10 log10(d_out[0] / max(d_out[1], 1e-24)) dB,
+ * which is page export_gptq_cpu.py's 20 log10(||w|| / max(||w - deq||, 1e-12)) and
+ * gives page quantize_dflash_mxfp4.py's relative error 10**(-dB/20).
+ * w is W as float32; d is the dequantized value in float32 (UINTX: the bf16 result).
+ * workspace: at least gwb_sizes.workspace bytes. Deterministic for a given shape.  */
+int gwb_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
+            const gwb_qtensors* in, double* d_out, void* workspace, size_t workspace_bytes,
+            void* stream);
+
+/* Workspace bytes for gwb_awq_search_mxfp4 on an [N, K] weight. Host only. */
+int gwb_awq_workspace(int64_t N, int64_t K, int32_t n_alpha, int64_t max_rows, size_t* bytes);
+
+/* AWQ-style alpha search on MXFP4, page quantize_dflash_mxfp4.py, search_scale, with
+ * the diagonal surrogate objective of its module docstring.
+ *   W        [N, K] of w_dtype, row stride ldw; rows W[::max(1, N / max_rows)][:max_rows]
+ *            are used (max_rows > 0; the page uses 2048)
+ *   d_a      float32 [K] per-input-channel mean |x| (device)
+ *   alphas   HOST array of n_alpha doubles (1 <= n_alpha <= 32), e.g. 0, 0.1, ..., 1
+ * Steps: a' = max(a, 1e-8); an = a' / mean(a'); per alpha s = clamp(an**alpha, 1e-2,
+ * 1e2) / geomean (float64, rounded once to float32, written to d_s_table [n_alpha, K]);
+ * X = W * s; D = dequant(quant_mxfp4(X)); err = sum(((D / s - W) * a')**2) with float32
+ * elementwise ops and a float64 sum -> d_err [n_alpha] (device doubles);
+ * d_best[0] = the first index with the strictly smallest error (device int32).
+ * K % 32 == 0 is required.                                                          */
+int gwb_awq_search_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
+                         const float* d_a, const double* alphas, int32_t n_alpha,
+                         int64_t max_rows, float* d_s_table, double* d_err, int32_t* d_best,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Measurement helper, not part of the method: copy `bytes` (a multiple of 16, both
+ * pointers 16-byte aligned) from d_src to d_dst with the same 128-bit load/store
+ * idiom the quantization kernels use; a same-run bandwidth ceiling. */
+int gwb_stream_copy(void* d_dst, const void* d_src, size_t bytes, void* stream);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char* gwb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GWB_H */

@@ -1,0 +1,143 @@
+"""C ABI boundary checks that need no GPU: libgwb.so loads, exports every entry point
+include/gwb.h declares, reports the documented sizes, and rejects bad arguments with the
+documented codes before anything is enqueued (so no HIP call is reached here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gwb.h")
+
+gwb = pytest.importorskip("group_wise_bit_amd.binding", reason="libgwb.so not built")
+lib = gwb.lib
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(gwb_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_declares_what_binding_exports():
+    declared = _declared()
+    assert declared, "no declarations found"
+    assert set(declared) == set(gwb.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def _sizes(fmt, N, K, nbits=4, group=None, dt=gwb.BF16):
+    sp = gwb.make_spec(fmt, nbits, group, dt)
+    s = gwb.Sizes()
+    rc = lib.gwb_query_sizes(ctypes.byref(sp), N, K, ctypes.byref(s))
+    return rc, s
+
+
+def test_sizes_match_layouts():
+    rc, s = _sizes("mxfp4", 34816, 5120)
+    assert rc == 0 and s.codes == 34816 * 2560 and s.scales == 34816 * 160 and s.zeros == 0
+    rc, s = _sizes("gptq_sym", 256, 1024, dt=gwb.F32)
+    assert rc == 0 and (s.codes, s.scales, s.zeros, s.g_idx) == (128 * 256 * 4, 8 * 256 * 2, 8 * 32 * 4, 1024 * 4)
+    rc, s = _sizes("gptq_asym", 4096, 4096)
+    assert rc == 0 and (s.codes, s.scales, s.zeros) == (512 * 4096 * 4, 32 * 4096 * 2, 32 * 512 * 4)
+    for nbits, want in [(2, 9437184), (3, 14155776), (4, 18874368), (5, 23592960), (6, 28311552), (7, 33030144)]:
+        rc, s = _sizes("uintx", 3072, 12288, nbits=nbits)
+        assert rc == 0 and s.codes == want and s.scales == 1179648 and s.zeros == 589824
+    # ragged uintx: shards padded independently, workspace for the two-pass path
+    rc, s = _sizes("uintx", 1, 64, nbits=5)
+    assert rc == 0 and s.codes == 32 + 8 and s.workspace >= 64
+
+
+def test_bits_per_weight_from_sizes():
+    # page export_gptq_cpu.py main: 4 + (16 + 4) / group bits per weight
+    rc, s = _sizes("gptq_asym", 4096, 4096)
+    bpw = 8 * (s.codes + s.scales + s.zeros) / (4096 * 4096)
+    assert bpw == 4 + 20 / 128
+
+
+@pytest.mark.parametrize("fmt,N,K,nbits,group,dt,code", [
+    ("mxfp4", 4, 48, 4, 32, gwb.BF16, gwb.E_SHAPE),
+    ("mxfp4", 4, 64, 4, 16, gwb.BF16, gwb.E_UNSUPPORTED),
+    ("mxfp4", 4, 64, 3, 32, gwb.BF16, gwb.E_ARG),
+    ("gptq_sym", 4, 128, 4, 128, gwb.F32, gwb.E_SHAPE),       # N % 8
+    ("gptq_sym", 8, 192, 4, 128, gwb.F32, gwb.E_SHAPE),       # K % group
+    ("gptq_asym", 8, 128, 4, 256, gwb.BF16, gwb.E_UNSUPPORTED),
+    ("gptq_asym", 8, 128, 4, 0, gwb.BF16, gwb.E_ARG),
+    ("gptq_asym", 8, 128, 3, 128, gwb.BF16, gwb.E_ARG),
+    ("uintx", 8, 128, 8, 64, gwb.BF16, gwb.E_UNSUPPORTED),    # uint8 refused
+    ("uintx", 8, 128, 1, 64, gwb.BF16, gwb.E_ARG),
+    ("uintx", 8, 100, 4, 64, gwb.BF16, gwb.E_SHAPE),
+    ("uintx", 8, 128, 4, 64, gwb.F32, gwb.E_UNSUPPORTED),
+    ("uintx", -1, 128, 4, 64, gwb.BF16, gwb.E_ARG),
+    ("mxfp4", 1 << 16, 1 << 16, 4, 32, gwb.BF16, gwb.E_UNSUPPORTED),   # beyond 2^31 elements
+])
+def test_query_rejects(fmt, N, K, nbits, group, dt, code):
+    rc, _ = _sizes(fmt, N, K, nbits, group, dt)
+    assert rc == code
+    assert lib.gwb_last_error().decode()
+
+
+def test_unknown_format_and_dtype():
+    s = gwb.Sizes()
+    assert lib.gwb_query_sizes(ctypes.byref(gwb.QSpec(9, 4, 32, 1)), 8, 64, ctypes.byref(s)) == gwb.E_ARG
+    assert lib.gwb_query_sizes(ctypes.byref(gwb.QSpec(3, 4, 32, 7)), 8, 64, ctypes.byref(s)) == gwb.E_ARG
+    assert lib.gwb_query_sizes(None, 8, 64, ctypes.byref(s)) == gwb.E_ARG
+
+
+def test_quantize_validates_before_launch():
+    sp = gwb.make_spec("mxfp4", 4, 32, gwb.BF16)
+    fake = 1 << 20          # never dereferenced: every call below fails validation first
+    qt = gwb.QTensors(fake, fake, None, None)
+    assert lib.gwb_quantize(ctypes.byref(sp), None, 8, 64, 64, ctypes.byref(qt), None, 0, None) == gwb.E_ARG
+    assert lib.gwb_quantize(ctypes.byref(sp), fake, 8, 64, 32, ctypes.byref(qt), None, 0, None) == gwb.E_ARG
+    assert lib.gwb_quantize(ctypes.byref(sp), fake + 2, 8, 64, 64, ctypes.byref(qt), None, 0, None) == gwb.E_UNSUPPORTED
+    assert lib.gwb_quantize(ctypes.byref(sp), fake, 8, 64, 68, ctypes.byref(qt), None, 0, None) == gwb.E_UNSUPPORTED
+    bad = gwb.QTensors(None, fake, None, None)
+    assert lib.gwb_quantize(ctypes.byref(sp), fake, 8, 64, 64, ctypes.byref(bad), None, 0, None) == gwb.E_ARG
+    # uintx two-pass path needs its workspace
+    su = gwb.make_spec("uintx", 3, 64, gwb.BF16)
+    qu = gwb.QTensors(fake, fake, fake, None)
+    assert lib.gwb_quantize(ctypes.byref(su), fake, 1, 64, 64, ctypes.byref(qu), None, 0, None) == gwb.E_SIZE
+    # GPTQ needs zeros
+    sg = gwb.make_spec("gptq_sym", 4, 128, gwb.F32)
+    assert lib.gwb_quantize(ctypes.byref(sg), fake, 8, 128, 128, ctypes.byref(qt), None, 0, None) == gwb.E_ARG
+    # empty shapes are valid and enqueue nothing
+    assert lib.gwb_quantize(ctypes.byref(sp), fake, 0, 64, 64, ctypes.byref(qt), None, 0, None) == gwb.OK
+    assert lib.gwb_quantize(ctypes.byref(sp), fake, 8, 0, 0, ctypes.byref(qt), None, 0, None) == gwb.OK
+
+
+def test_dequantize_snr_awq_validate():
+    fake = 1 << 20
+    sp = gwb.make_spec("mxfp4", 4, 32, gwb.BF16)
+    qt = gwb.QTensors(fake, fake, None, None)
+    assert lib.gwb_dequantize(ctypes.byref(sp), ctypes.byref(qt), 8, 64, fake, 5, 64, None, 0, None) == gwb.E_ARG
+    assert lib.gwb_dequantize(ctypes.byref(sp), ctypes.byref(qt), 8, 64, fake, gwb.BF16, 32, None, 0, None) == gwb.E_ARG
+    assert lib.gwb_dequantize(ctypes.byref(sp), ctypes.byref(qt), 8, 64, None, gwb.BF16, 64, None, 0, None) == gwb.E_ARG
+    assert lib.gwb_snr(ctypes.byref(sp), fake, 8, 64, 64, ctypes.byref(qt), fake, None, 0, None) == gwb.E_SIZE
+    assert lib.gwb_snr(ctypes.byref(sp), fake, 0, 64, 64, ctypes.byref(qt), fake, fake, 1 << 20, None) == gwb.E_SHAPE
+    al = (ctypes.c_double * 11)(*[i / 10 for i in range(11)])
+    args = dict(W=fake, dt=gwb.BF16, N=64, K=64, ldw=64, a=fake, al=al, na=11, mr=2048, s=fake, e=fake, b=fake)
+    def awq(**kw):
+        a = dict(args, **kw)
+        return lib.gwb_awq_search_mxfp4(a["W"], a["dt"], a["N"], a["K"], a["ldw"], a["a"], a["al"], a["na"], a["mr"],
+                                        a["s"], a["e"], a["b"], None, 0, None)
+    assert awq() == gwb.E_SIZE
+    assert awq(K=48) == gwb.E_SHAPE
+    assert awq(na=17) == gwb.E_ARG
+    assert awq(na=0) == gwb.E_ARG
+    assert awq(mr=0) == gwb.E_ARG
+    assert awq(a=None) == gwb.E_ARG
+    b = ctypes.c_size_t()
+    assert lib.gwb_awq_workspace(34816, 5120, 11, 2048, ctypes.byref(b)) == 0 and b.value > 0
+    assert lib.gwb_stream_copy(fake, fake, 24, None) == gwb.E_UNSUPPORTED
+
+
+def test_error_message_is_thread_local_and_cleared():
+    _sizes("uintx", 8, 128, nbits=8)
+    assert "uint8" in lib.gwb_last_error().decode()
+    rc, _ = _sizes("mxfp4", 8, 64)
+    assert rc == 0 and lib.gwb_last_error().decode() == ""
