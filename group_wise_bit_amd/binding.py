@@ -161,8 +161,9 @@ def quantize(W: torch.Tensor, fmt: str, nbits: int = 4, group: Optional[int] = N
     if out is None:
         dev = W.device
         gidx = _alloc(sz["g_idx"], dev) if (fmt.startswith("gptq") and with_g_idx) else None
+        zeros = _alloc(sz["zeros"], dev) if fmt != "mxfp4" else None      # GPTQ and uintx carry zeros
         out = Quantized(fmt, nbits, group, W.dtype, N, K, _alloc(sz["codes"], dev), _alloc(sz["scales"], dev),
-                        _alloc(sz["zeros"], dev) if sz["zeros"] else None, gidx, sz)
+                        zeros, gidx, sz)
     if workspace is None and sz["workspace"]:
         workspace = _alloc(sz["workspace"], W.device)
     ws_b = 0 if workspace is None else workspace.numel() * workspace.element_size()

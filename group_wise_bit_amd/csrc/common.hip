@@ -1,9 +1,40 @@
 // Reduction of the fused error kernels' per-block partial sums, and the bandwidth
 // reference copy used by the benchmark.
+#include <atomic>
+#include <cstdlib>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace gwb {
+
+static int compute_units_of_current_device() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+static int blocks_per_cu() {
+  static const int v = [] {
+    const char* s = std::getenv("GWB_BLOCKS_PER_CU");
+    int x = s ? std::atoi(s) : 0;
+    return x > 0 && x <= 64 ? x : 8;
+  }();
+  return v;
+}
+
+unsigned stream_blocks(uint64_t units) {
+  uint64_t need = (units + 255) / 256;
+  if (need == 0) need = 1;
+  const uint64_t cap = (uint64_t)compute_units_of_current_device() * (uint64_t)blocks_per_cu();
+  return (unsigned)(need < cap ? need : cap);
+}
 
 // part[2*i], part[2*i+1] for i < nblocks -> out[0] = sum w^2, out[1] = sum (w-d)^2,
 // out[2] = 10 log10(out[0] / max(out[1], 1e-24)) (page export_gptq_cpu.py's

@@ -89,6 +89,35 @@ __device__ __forceinline__ U4 ld16(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, U4 v) { *reinterpret_cast<U4*>(p) = v; }
 
+// Non-temporal (streaming) variants: data read or written exactly once.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ U4 ld16_nt(const void* p) {
+  u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return U4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ void st16_nt(void* p, U4 v) {
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ uint32_t ld4_nt(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st4_nt(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+
+// Raw weights of one 8-element unit: one 16-byte load of bf16, two of float32.
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> { U4 v; };
+template <> struct Raw8<float> { U4 a, b; };
+__device__ __forceinline__ Raw8<uint16_t> load_raw8(const uint16_t* p) { return Raw8<uint16_t>{ld16_nt(p)}; }
+__device__ __forceinline__ Raw8<float> load_raw8(const float* p) { return Raw8<float>{ld16_nt(p), ld16_nt(p + 4)}; }
+__device__ __forceinline__ void to_f32(const Raw8<uint16_t>& r, float* x) {
+  x[0] = __uint_as_float(r.v.x << 16); x[1] = __uint_as_float(r.v.x & 0xFFFF0000u);
+  x[2] = __uint_as_float(r.v.y << 16); x[3] = __uint_as_float(r.v.y & 0xFFFF0000u);
+  x[4] = __uint_as_float(r.v.z << 16); x[5] = __uint_as_float(r.v.z & 0xFFFF0000u);
+  x[6] = __uint_as_float(r.v.w << 16); x[7] = __uint_as_float(r.v.w & 0xFFFF0000u);
+}
+__device__ __forceinline__ void to_f32(const Raw8<float>& r, float* x) {
+  x[0] = __uint_as_float(r.a.x); x[1] = __uint_as_float(r.a.y); x[2] = __uint_as_float(r.a.z); x[3] = __uint_as_float(r.a.w);
+  x[4] = __uint_as_float(r.b.x); x[5] = __uint_as_float(r.b.y); x[6] = __uint_as_float(r.b.z); x[7] = __uint_as_float(r.b.w);
+}
+
 // Load 8 consecutive weights (16-byte aligned start) as float32.
 __device__ __forceinline__ void load8(const uint16_t* p, float* x) {
   U4 v = ld16(p);
@@ -117,6 +146,18 @@ __device__ __forceinline__ void store8(float* p, const float* d) {
   U4 b{__float_as_uint(d[4]), __float_as_uint(d[5]), __float_as_uint(d[6]), __float_as_uint(d[7])};
   st16(p, a);
   st16(p + 4, b);
+}
+
+// Accumulate sum w^2 and sum (w - d)^2 of 8 elements (w - d a float32 subtraction,
+// squares and sums in float64, where the squares are exact).
+__device__ __forceinline__ void acc_err8(const float* x, const float* d, double& sw, double& se) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const double xd = (double)x[i];
+    const double ed = (double)(x[i] - d[i]);
+    sw = fma(xd, xd, sw);
+    se = fma(ed, ed, se);
+  }
 }
 
 // ---------------------------------------------------------------- error sums

@@ -248,7 +248,7 @@ void launch_gptq_dequant(bool sym, int group, const void* qweight, const void* s
 
 unsigned gptq_err_blocks(int group, int64_t N, int64_t K) {
   unsigned t = tiles_of(group, N, K);
-  return t < kErrGridCap ? (t ? t : 1) : kErrGridCap;
+  return t < kErrGridCap ? (t ? t : 1) : kErrGridCap;   // tiles, capped: fixed by the shape
 }
 
 void launch_gptq_err(bool sym, int group, const void* W, int32_t w_dtype, int64_t N, int64_t K,

@@ -14,9 +14,19 @@ constexpr int kStore = 0;  // dequant sinks
 constexpr int kErr = 1;
 
 // Grid caps: streaming kernels loop over their units grid-stride. The error kernels
-// keep their block count (and so their partial-sum layout) bounded.
+// keep their block count (and so their partial-sum layout and workspace) fixed by the
+// shape alone, independent of the device.
 constexpr unsigned kStreamGridCap = 1u << 20;
-constexpr unsigned kErrGridCap = 4096;
+constexpr unsigned kErrGridCap = 1024;
+
+// Blocks of 256 threads for a grid-stride streaming kernel over `units` thread-units:
+// one unit per thread at most, and at most GWB_BLOCKS_PER_CU (default 8) blocks per
+// compute unit of the current device. Launch time only (queries the device).
+unsigned stream_blocks(uint64_t units);
+inline unsigned err_blocks_for(uint64_t units) {
+  uint64_t g = (units + 255) / 256;
+  return (unsigned)(g < kErrGridCap ? (g ? g : 1) : kErrGridCap);
+}
 
 // ---- MXFP4 (mxfp4.hip)
 void launch_mxfp4_quant(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,

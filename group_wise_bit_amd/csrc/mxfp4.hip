@@ -2,43 +2,91 @@
 // Page quantize_dflash_mxfp4.py: the E2M1 table, quantize_mxfp4, dequantize_mxfp4.
 //
 // Work unit: 8 consecutive weights of one row (one 128-bit bf16 load). Four
-// consecutive lanes hold one 32-weight block, so the block amax is two DPP steps.
-// A unit's 8 codes are one 32-bit word of the packed output (byte j of the word =
-// code(2j) | code(2j+1) << 4), so a wavefront stores 256 contiguous bytes.
+// consecutive lanes hold one 32-weight block, so the block amax is two DPP steps. A
+// unit's 8 codes are one 32-bit word of the packed output (byte j of the word =
+// code(2j) | code(2j+1) << 4), so a wavefront stores 256 contiguous bytes. Each lane
+// keeps four units' loads in flight before converting them (grid-stride, a few blocks
+// per compute unit), which is what the HBM3E stream needs to stay busy.
 #include "kernels.hpp"
 #include "mxfp4_math.hpp"
 
 namespace gwb {
 
+__device__ __forceinline__ uint32_t absmax_bits(const Raw8<uint16_t>& r) { return absmax8_bits(r.v); }
+__device__ __forceinline__ uint32_t absmax_bits(const Raw8<float>& r) {
+  float x[8];
+  to_f32(r, x);
+  return absmax8_bits(x);
+}
+__device__ __forceinline__ uint32_t pack_unit(const Raw8<uint16_t>& r, float sc) { return mx_pack8(r.v, sc); }
+__device__ __forceinline__ uint32_t pack_unit(const Raw8<float>& r, float sc) {
+  float x[8];
+  to_f32(r, x);
+  return mx_pack8(x, sc);
+}
+
+// Address of unit u: rows of K/8 units, row stride ld elements. With contiguous rows
+// (ld == K) the unit index is the element offset / 8 and no division is needed.
+template <bool CONTIG, typename T>
+__device__ __forceinline__ T* unit_ptr(T* base, int64_t ld, uint32_t u, FastDiv upr) {
+  if constexpr (CONTIG) return base + (int64_t)u * 8;
+  const uint32_t n = fdiv(u, upr);
+  return base + (int64_t)n * ld + 8 * (u - n * upr.d);
+}
+
 template <typename TIn>
+__device__ __forceinline__ void quant_unit(const Raw8<TIn>& r, uint32_t u, uint32_t* __restrict__ packed,
+                                           uint8_t* __restrict__ e8m0) {
+  const uint32_t e8 = mx_e8m0_bits(quad_max_u(absmax_bits(r)));
+  packed[u] = pack_unit(r, mx_scale_operand(e8));
+  if ((u & 3u) == 0) e8m0[u >> 2] = (uint8_t)e8;
+}
+
+// units = N*K/8 is a multiple of 4 and every stride is too, so the four lanes of a
+// block always take the same branch of each loop (the DPP step needs all four).
+template <bool CONTIG, typename TIn>
 __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const TIn* __restrict__ W, int64_t ldw,
                                                           uint32_t units, FastDiv upr,
                                                           uint32_t* __restrict__ packed,
                                                           uint8_t* __restrict__ e8m0) {
   const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
-    uint32_t n = fdiv(u, upr);
-    uint32_t kc = u - n * upr.d;
-    float x[8];
-    load8(W + (int64_t)n * ldw + 8 * kc, x);
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-    amax = lanes_max<4>(amax);
-    uint32_t e8 = mx_e8m0(amax);
-    float inv = mx_inv_scale(e8);
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) word |= e2m1_code(x[i], inv) << (4 * i);
-    packed[u] = word;
-    if ((u & 3u) == 0) e8m0[u >> 2] = (uint8_t)e8;
+  uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
+  for (; u + 3 * stride < units; u += 4 * stride) {
+    const Raw8<TIn> r0 = load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr));
+    const Raw8<TIn> r1 = load_raw8(unit_ptr<CONTIG>(W, ldw, u + stride, upr));
+    const Raw8<TIn> r2 = load_raw8(unit_ptr<CONTIG>(W, ldw, u + 2 * stride, upr));
+    const Raw8<TIn> r3 = load_raw8(unit_ptr<CONTIG>(W, ldw, u + 3 * stride, upr));
+    quant_unit(r0, u, packed, e8m0);
+    quant_unit(r1, u + stride, packed, e8m0);
+    quant_unit(r2, u + 2 * stride, packed, e8m0);
+    quant_unit(r3, u + 3 * stride, packed, e8m0);
   }
+  for (; u < units; u += stride) quant_unit(load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr)), u, packed, e8m0);
 }
 
 // Unpack + dequantize. SINK == kStore writes out[n, k]; SINK == kErr reads W at the
-// same place and accumulates sum w^2 and sum (w - d)^2 (float32 subtraction, float64
-// sums) into per-block partials.
-template <int SINK, typename TOut, typename TW>
+// same place and accumulates sum w^2 and sum (w - d)^2 into per-block partials.
+template <int SINK, bool CONTIG, typename TOut, typename TW>
+__device__ __forceinline__ void dequant_unit(uint32_t word, uint32_t e8, uint32_t u, FastDiv upr,
+                                             TOut* __restrict__ out, int64_t ldo, const TW* __restrict__ W,
+                                             int64_t ldw, double& sw, double& se) {
+  if constexpr (SINK == kStore) {
+    if constexpr (sizeof(TOut) == 2) {
+      st16(unit_ptr<CONTIG>(out, ldo, u, upr), mx_unpack8_bf16(word, e8));
+    } else {
+      float d[8];
+      mx_unpack8(word, e8, d);
+      store8(unit_ptr<CONTIG>(out, ldo, u, upr), d);
+    }
+  } else {
+    float d[8], x[8];
+    mx_unpack8(word, e8, d);
+    to_f32(load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr)), x);
+    acc_err8(x, d, sw, se);
+  }
+}
+
+template <int SINK, bool CONTIG, typename TOut, typename TW>
 __global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint32_t* __restrict__ packed,
                                                             const uint8_t* __restrict__ e8m0,
                                                             uint32_t units, FastDiv upr,
@@ -47,80 +95,70 @@ __global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint32_t* __re
                                                             double* __restrict__ part) {
   const uint32_t stride = gridDim.x * blockDim.x;
   double sw = 0.0, se = 0.0;
-  for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
-    uint32_t n = fdiv(u, upr);
-    uint32_t kc = u - n * upr.d;
-    uint32_t word = packed[u];
-    float sc = mx_scale(e8m0[u >> 2]);
-    float d[8];
+  uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
+  for (; u + 3 * stride < units; u += 4 * stride) {
+    uint32_t w[4], e[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) d[i] = e2m1_value((word >> (4 * i)) & 0xFu, sc);
-    if constexpr (SINK == kStore) {
-      store8(out + (int64_t)n * ldo + 8 * kc, d);
-    } else {
-      float x[8];
-      load8(W + (int64_t)n * ldw + 8 * kc, x);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        double xd = (double)x[i];
-        double ed = (double)(x[i] - d[i]);
-        sw = fma(xd, xd, sw);
-        se = fma(ed, ed, se);
-      }
+    for (int i = 0; i < 4; ++i) {
+      w[i] = ld4_nt(packed + u + i * stride);
+      e[i] = e8m0[(u + i * stride) >> 2];
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dequant_unit<SINK, CONTIG>(w[i], e[i], u + i * stride, upr, out, ldo, W, ldw, sw, se);
   }
+  for (; u < units; u += stride)
+    dequant_unit<SINK, CONTIG>(ld4_nt(packed + u), (uint32_t)e8m0[u >> 2], u, upr, out, ldo, W, ldw, sw, se);
   if constexpr (SINK == kErr) block_sum2_store<256>(sw, se, part);
 }
 
 // ------------------------------------------------------------------ launchers
-static unsigned grid_for(uint64_t units, unsigned cap) {
-  uint64_t g = (units + 255) / 256;
-  return (unsigned)(g < cap ? (g ? g : 1) : cap);
-}
-
 void launch_mxfp4_quant(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
                         void* packed, void* e8m0, hipStream_t st) {
-  uint32_t units = (uint32_t)(N * K / 8);
-  FastDiv upr = make_fastdiv((uint32_t)(K / 8));
-  unsigned grid = grid_for(units, kStreamGridCap);
+  const uint32_t units = (uint32_t)(N * K / 8);
+  const FastDiv upr = make_fastdiv((uint32_t)(K / 8));
+  const unsigned grid = stream_blocks(units);
+  const bool contig = ldw == K;
   if (w_dtype == kBF16)
-    hipLaunchKernelGGL(mxfp4_quant_kernel<uint16_t>, dim3(grid), dim3(256), 0, st,
-                       (const uint16_t*)W, ldw, units, upr, (uint32_t*)packed, (uint8_t*)e8m0);
+    hipLaunchKernelGGL((contig ? mxfp4_quant_kernel<true, uint16_t> : mxfp4_quant_kernel<false, uint16_t>),
+                       dim3(grid), dim3(256), 0, st, (const uint16_t*)W, ldw, units, upr, (uint32_t*)packed,
+                       (uint8_t*)e8m0);
   else
-    hipLaunchKernelGGL(mxfp4_quant_kernel<float>, dim3(grid), dim3(256), 0, st,
-                       (const float*)W, ldw, units, upr, (uint32_t*)packed, (uint8_t*)e8m0);
+    hipLaunchKernelGGL((contig ? mxfp4_quant_kernel<true, float> : mxfp4_quant_kernel<false, float>), dim3(grid),
+                       dim3(256), 0, st, (const float*)W, ldw, units, upr, (uint32_t*)packed, (uint8_t*)e8m0);
 }
 
 void launch_mxfp4_dequant(const void* packed, const void* e8m0, int64_t N, int64_t K, void* out,
                           int32_t out_dtype, int64_t ldo, hipStream_t st) {
-  uint32_t units = (uint32_t)(N * K / 8);
-  FastDiv upr = make_fastdiv((uint32_t)(K / 8));
-  unsigned grid = grid_for(units, kStreamGridCap);
+  const uint32_t units = (uint32_t)(N * K / 8);
+  const FastDiv upr = make_fastdiv((uint32_t)(K / 8));
+  const unsigned grid = stream_blocks(units);
+  const bool contig = ldo == K;
   if (out_dtype == kBF16)
-    hipLaunchKernelGGL((mxfp4_dequant_kernel<kStore, uint16_t, uint16_t>), dim3(grid), dim3(256), 0, st,
-                       (const uint32_t*)packed, (const uint8_t*)e8m0, units, upr, (uint16_t*)out, ldo,
-                       (const uint16_t*)nullptr, (int64_t)0, (double*)nullptr);
+    hipLaunchKernelGGL((contig ? mxfp4_dequant_kernel<kStore, true, uint16_t, uint16_t> : mxfp4_dequant_kernel<kStore, false, uint16_t, uint16_t>),
+                       dim3(grid), dim3(256), 0, st, (const uint32_t*)packed, (const uint8_t*)e8m0, units, upr,
+                       (uint16_t*)out, ldo, (const uint16_t*)nullptr, (int64_t)0, (double*)nullptr);
   else
-    hipLaunchKernelGGL((mxfp4_dequant_kernel<kStore, float, uint16_t>), dim3(grid), dim3(256), 0, st,
-                       (const uint32_t*)packed, (const uint8_t*)e8m0, units, upr, (float*)out, ldo,
-                       (const uint16_t*)nullptr, (int64_t)0, (double*)nullptr);
+    hipLaunchKernelGGL((contig ? mxfp4_dequant_kernel<kStore, true, float, uint16_t> : mxfp4_dequant_kernel<kStore, false, float, uint16_t>),
+                       dim3(grid), dim3(256), 0, st, (const uint32_t*)packed, (const uint8_t*)e8m0, units, upr,
+                       (float*)out, ldo, (const uint16_t*)nullptr, (int64_t)0, (double*)nullptr);
 }
 
-unsigned mxfp4_err_blocks(int64_t N, int64_t K) { return grid_for((uint64_t)(N * K / 8), kErrGridCap); }
+unsigned mxfp4_err_blocks(int64_t N, int64_t K) { return err_blocks_for((uint64_t)(N * K / 8)); }
 
 void launch_mxfp4_err(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
                       const void* packed, const void* e8m0, double* part, hipStream_t st) {
-  uint32_t units = (uint32_t)(N * K / 8);
-  FastDiv upr = make_fastdiv((uint32_t)(K / 8));
-  unsigned grid = mxfp4_err_blocks(N, K);
+  const uint32_t units = (uint32_t)(N * K / 8);
+  const FastDiv upr = make_fastdiv((uint32_t)(K / 8));
+  const unsigned grid = mxfp4_err_blocks(N, K);
+  const bool contig = ldw == K;
   if (w_dtype == kBF16)
-    hipLaunchKernelGGL((mxfp4_dequant_kernel<kErr, float, uint16_t>), dim3(grid), dim3(256), 0, st,
-                       (const uint32_t*)packed, (const uint8_t*)e8m0, units, upr, (float*)nullptr,
-                       (int64_t)0, (const uint16_t*)W, ldw, part);
+    hipLaunchKernelGGL((contig ? mxfp4_dequant_kernel<kErr, true, float, uint16_t> : mxfp4_dequant_kernel<kErr, false, float, uint16_t>),
+                       dim3(grid), dim3(256), 0, st, (const uint32_t*)packed, (const uint8_t*)e8m0, units, upr,
+                       (float*)nullptr, (int64_t)0, (const uint16_t*)W, ldw, part);
   else
-    hipLaunchKernelGGL((mxfp4_dequant_kernel<kErr, float, float>), dim3(grid), dim3(256), 0, st,
-                       (const uint32_t*)packed, (const uint8_t*)e8m0, units, upr, (float*)nullptr,
-                       (int64_t)0, (const float*)W, ldw, part);
+    hipLaunchKernelGGL((contig ? mxfp4_dequant_kernel<kErr, true, float, float> : mxfp4_dequant_kernel<kErr, false, float, float>),
+                       dim3(grid), dim3(256), 0, st, (const uint32_t*)packed, (const uint8_t*)e8m0, units, upr,
+                       (float*)nullptr, (int64_t)0, (const float*)W, ldw, part);
 }
 
 }  // namespace gwb
