@@ -21,6 +21,10 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgwb.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.hip", "common.hip", "mxfp4.hip", "gptq.hip", "uintx.hip", "awq.hip"]
+# uintx's arithmetic never produces a NaN from finite bf16 weights, and non-finite
+# weights are outside the method; without NaN semantics the compiler drops the
+# canonicalization it otherwise inserts around every float min/max.
+EXTRA = {"uintx.hip": ["-fno-honor-nans"]}
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     "-ffp-contract=off",
@@ -43,7 +47,7 @@ def build(verbose: bool = True) -> str:
 
     def compile_one(src):
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        rc, out = _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        rc, out = _run([HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         return src, obj, rc, out
 
     jobs = min(len(SOURCES), max(1, os.cpu_count() or 1), 8)

@@ -241,3 +241,53 @@ def awq_search(W: torch.Tensor, a: torch.Tensor, alphas: Optional[Sequence[float
 def stream_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
     n = src.numel() * src.element_size()
     _check(lib.gwb_stream_copy(_ptr(dst), _ptr(src), n, _stream()))
+
+
+class Prepared:
+    """One library call with its arguments marshalled once, for repeated launches
+    (timing loops, serving): calling it makes exactly one C call, on the stream that
+    was current when it was prepared. The tensors it refers to must stay alive."""
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, tuple(args), keep
+
+    def __call__(self) -> None:
+        _check(self._fn(*self._args))
+
+
+def prepare_quantize(W: torch.Tensor, q: Quantized, workspace: Optional[torch.Tensor] = None) -> Prepared:
+    N, K, ldw = _weight_args(W)
+    if (N, K, W.dtype) != (q.N, q.K, q.w_dtype):
+        raise ValueError("W does not match the Quantized buffers")
+    if workspace is None and q.sizes["workspace"]:
+        workspace = _alloc(q.sizes["workspace"], W.device)
+    sp, qt = q.spec(), q.qtensors()
+    ws_b = 0 if workspace is None else workspace.numel()
+    return Prepared(lib.gwb_quantize, (ctypes.byref(sp), _ptr(W), N, K, ldw, ctypes.byref(qt), _ptr(workspace),
+                                       ws_b, _stream()), (sp, qt, W, q, workspace))
+
+
+def prepare_dequantize(q: Quantized, out: torch.Tensor) -> Prepared:
+    if out.dtype not in _DT or out.stride(1) != 1 or tuple(out.shape) != (q.N, q.K):
+        raise ValueError("out must be [N, K] float32 or bfloat16 with unit stride along K")
+    sp, qt = q.spec(), q.qtensors()
+    return Prepared(lib.gwb_dequantize, (ctypes.byref(sp), ctypes.byref(qt), q.N, q.K, _ptr(out), _DT[out.dtype],
+                                         out.stride(0), None, 0, _stream()), (sp, qt, q, out))
+
+
+def prepare_snr(W: torch.Tensor, q: Quantized, out: torch.Tensor, workspace: torch.Tensor) -> Prepared:
+    N, K, ldw = _weight_args(W)
+    sp, qt = q.spec(), q.qtensors()
+    return Prepared(lib.gwb_snr, (ctypes.byref(sp), _ptr(W), N, K, ldw, ctypes.byref(qt), _ptr(out), _ptr(workspace),
+                                  workspace.numel(), _stream()), (sp, qt, W, q, out, workspace))
+
+
+def prepare_awq_search(W: torch.Tensor, a: torch.Tensor, alphas: Sequence[float], max_rows: int,
+                       s_table: torch.Tensor, err: torch.Tensor, best: torch.Tensor,
+                       workspace: torch.Tensor) -> Prepared:
+    N, K, ldw = _weight_args(W)
+    host_alphas = (ctypes.c_double * len(alphas))(*alphas)
+    return Prepared(lib.gwb_awq_search_mxfp4, (_ptr(W), _DT[W.dtype], N, K, ldw, _ptr(a), host_alphas, len(alphas),
+                                               max_rows, _ptr(s_table), _ptr(err), _ptr(best), _ptr(workspace),
+                                               workspace.numel(), _stream()),
+                    (W, a, host_alphas, s_table, err, best, workspace))

@@ -132,14 +132,17 @@ __device__ __forceinline__ void load8(const float* p, float* x) {
   x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
 }
 
+// Two float32 -> packed bf16 pair (a in the low half), round to nearest even: the
+// hardware pair conversion (v_cvt_pk_bf16_f32; float32 denormals are kept).
+typedef __bf16 dc_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float dc_f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(dc_f32x2_t{a, b}, dc_bf16x2_t));
+}
+
 // Store 8 float32 values as bf16 (RNE) or as float32.
 __device__ __forceinline__ void store8(uint16_t* p, const float* d) {
-  U4 v;
-  v.x = f32_to_bf16_rne(d[0]) | (f32_to_bf16_rne(d[1]) << 16);
-  v.y = f32_to_bf16_rne(d[2]) | (f32_to_bf16_rne(d[3]) << 16);
-  v.z = f32_to_bf16_rne(d[4]) | (f32_to_bf16_rne(d[5]) << 16);
-  v.w = f32_to_bf16_rne(d[6]) | (f32_to_bf16_rne(d[7]) << 16);
-  st16(p, v);
+  st16(p, U4{pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]), pack_bf16x2(d[4], d[5]), pack_bf16x2(d[6], d[7])});
 }
 __device__ __forceinline__ void store8(float* p, const float* d) {
   U4 a{__float_as_uint(d[0]), __float_as_uint(d[1]), __float_as_uint(d[2]), __float_as_uint(d[3])};

@@ -5,36 +5,41 @@
 //
 // Planar shards: byte i of the k-bit shard holds codes i, i+L, i+2L, ... (L = that
 // shard's byte count), which lie far apart in the matrix. With numel % 512 == 0 the
-// shard lengths nest (L_1 = numel/8, L_2 = 2 L_1, L_4 = 4 L_1), so a block that takes
-// the 8 segments [b0 + j*L_1, b0 + j*L_1 + T), j = 0..7, owns complete bytes of every
-// shard: [b0, b0+T) of the 1-bit shard, [b0 + m*L_1, +T) for m < 2 of the 2-bit
-// shard and for m < 4 of the 4-bit shard. Segments start on group boundaries, so
-// qparams stay local. Codes meet in LDS, where bytes are assembled four at a time.
+// shard lengths nest (L_1 = numel/8, L_2 = 2 L_1, L_4 = 4 L_1): the codes at position
+// p of the 8 segments j*L_1 + p (j = 0..7) fill byte p of the 1-bit shard, bytes
+// p and L_1 + p of the 2-bit shard and bytes m*L_1 + p (m < 4) of the 4-bit shard, and
+// nothing else. So a lane that loads the same 8 positions of all 8 segments owns
+// complete output bytes and assembles them in registers. Segments start on group
+// boundaries, so each group's qparams stay within the 8 lanes that hold it.
 // Other sizes take a two-pass path: codes to workspace, then one thread per byte.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace gwb {
 
-constexpr int kT = 256;          // elements per segment per block
-constexpr int kCS = kT + 16;     // LDS row stride of the code tile (bytes)
+// Tiled path geometry: a lane takes 8 consecutive positions p of all 8 segments
+// (elements j*L1 + p), a wavefront 512 positions, a block of 4 wavefronts 2048.
+constexpr int kLanePos = 8;
+constexpr int kWavePos = 64 * kLanePos;
+constexpr int kBlockPos = 4 * kWavePos;
 
-struct Shards {                  // byte offsets and bit offsets of the present shards
+struct Shards {                  // byte offsets of the present shards in the packed buffer
   int64_t base4, base2, base1;
-  int off2, off1;
-  bool has4, has2, has1;
 };
 static Shards shards_of(int nbits, int64_t numel) {
   Shards s{};
-  s.has4 = nbits & 4; s.has2 = nbits & 2; s.has1 = nbits & 1;
   int64_t L4 = (numel + 1) / 2, L2 = (numel + 3) / 4;
   s.base4 = 0;
-  s.base2 = s.has4 ? L4 : 0;
-  s.base1 = s.base2 + (s.has2 ? L2 : 0);
-  s.off2 = s.has4 ? 4 : 0;
-  s.off1 = (s.has4 ? 4 : 0) + (s.has2 ? 2 : 0);
+  s.base2 = (nbits & 4) ? L4 : 0;
+  s.base1 = s.base2 + ((nbits & 2) ? L2 : 0);
   return s;
 }
+// bit offsets of the 2-bit and 1-bit shards' fields within a code (pack order 4, 2, 1)
+template <int NB> struct ShardBits {
+  static constexpr bool has4 = NB & 4, has2 = NB & 2, has1 = NB & 1;
+  static constexpr int off2 = has4 ? 4 : 0;
+  static constexpr int off1 = (has4 ? 4 : 0) + (has2 ? 2 : 0);
+};
 
 // Group qparams from the group's min and max (every op a float32 op rounded to bf16):
 // mn = min(min, 0), mx = max(max, 0); scale = bf(bf(mx - mn) / qmax), at least 2^-23;
@@ -60,145 +65,214 @@ __device__ __forceinline__ float uintx_value(uint32_t c, float zp, float s) {
   return round_bf16(((float)c - zp) * s);
 }
 
-// Load 8 consecutive bf16 of flat element e (row-major [N, K], row stride ldw).
-__device__ __forceinline__ void load8_at(const uint16_t* W, int64_t ldw, uint32_t e, FastDiv kdiv, float* x) {
-  uint32_t n = fdiv(e, kdiv);
-  uint32_t k = e - n * kdiv.d;
-  load8(W + (int64_t)n * ldw + k, x);
+typedef __bf16 ux_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float ux_f32x2_t __attribute__((ext_vector_type(2)));
+// Two float32 rounded to bf16 (RNE, the hardware pair conversion), back as float32.
+__device__ __forceinline__ void round_bf16_pair(float& a, float& b) {
+  const uint32_t r = __builtin_bit_cast(uint32_t, __builtin_convertvector(ux_f32x2_t{a, b}, ux_bf16x2_t));
+  a = __uint_as_float(r << 16);
+  b = __uint_as_float(r & 0xFFFF0000u);
 }
 
+// Codes of 8 bf16 weights (one 16-byte load) as bytes: lo = positions 0..3, hi = 4..7.
+__device__ __forceinline__ void codes8(U4 v, float inv, float zp, float qmax, uint32_t& lo, uint32_t& hi) {
+  float x[8];
+  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] *= inv;                      // exact: 8-bit x 8-bit significands
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) round_bf16_pair(x[i], x[i + 1]);
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float c = __builtin_amdgcn_fmed3f(rintf(x[i]) + zp, 0.0f, qmax);
+    w[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(c, i & 3, w[i >> 2]);
+  }
+  lo = w[0];
+  hi = w[1];
+}
+
+template <bool CONTIG, typename T>
+__device__ __forceinline__ T* elem_ptr(T* base, int64_t ld, uint32_t e, FastDiv kdiv) {
+  if constexpr (CONTIG) return base + e;
+  const uint32_t n = fdiv(e, kdiv);
+  return base + (int64_t)n * ld + (e - n * kdiv.d);
+}
+
+__device__ __forceinline__ void st8(uint8_t* p, uint32_t lo, uint32_t hi) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+__device__ __forceinline__ uint2 ld8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
+
 // ------------------------------------------------------------- tiled quantize
-__global__ __launch_bounds__(256) void uintx_quant_tiled(const uint16_t* __restrict__ W, int64_t ldw,
-                                                         FastDiv kdiv, uint32_t L1, int nbits, Shards sh,
-                                                         uint8_t* __restrict__ packed,
+// One block per 2048 positions. Per lane: 8 loads (one per segment) in flight; per
+// segment a DPP min/max over the 8 lanes that share each 64-weight group; each of
+// those lanes then computes the qparams of one segment's group (lane & 7) and they
+// exchange (1/scale, zp) through LDS; codes are assembled into shard bytes in registers.
+template <int NB, bool CONTIG>
+__global__ __launch_bounds__(256) void uintx_quant_tiled(const uint16_t* __restrict__ W, int64_t ldw, FastDiv kdiv,
+                                                         uint32_t L1, Shards sh, uint8_t* __restrict__ packed,
                                                          uint16_t* __restrict__ scales,
                                                          uint8_t* __restrict__ zeros) {
-  __shared__ uint8_t ctile[8 * kCS];
-  const int t = threadIdx.x;
-  const uint32_t b0 = blockIdx.x * kT;
-  const uint32_t Tb = min((uint32_t)kT, L1 - b0);      // a multiple of 64
-  const float qmax = (float)((1 << nbits) - 1);
-  {
-    const int j = t / 32, tl = t % 32;
-    if ((uint32_t)tl * 8 < Tb) {
-      const uint32_t e = j * L1 + b0 + tl * 8;
-      float x[8];
-      load8_at(W, ldw, e, kdiv, x);
-      float mn = x[0], mx = x[0];
+  using SB = ShardBits<NB>;
+  __shared__ uint32_t qp_lds[256];
+  const float qmax = (float)((1 << NB) - 1);
+  const int lane = threadIdx.x & 63;
+  const uint32_t p = blockIdx.x * kBlockPos + (threadIdx.x >> 6) * kWavePos + lane * kLanePos;
+  const bool active = p < L1;                // whole groups of 8 lanes: L1 % 64 == 0
+  U4 raw[8];
+  if (active) {
 #pragma unroll
-      for (int i = 1; i < 8; ++i) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
-      mn = lanes_min<8>(mn);
-      mx = lanes_max<8>(mx);
-      QP q = uintx_qparams(mn, mx, qmax);
-      uint32_t lo = 0, hi = 0;
+    for (int j = 0; j < 8; ++j) raw[j] = ld16_nt(elem_ptr<CONTIG>(W, ldw, j * L1 + p, kdiv));
+    float mn[8], mx[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= uintx_code(x[i], q, qmax) << (8 * i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= uintx_code(x[i + 4], q, qmax) << (8 * i);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(&ctile[j * kCS + tl * 8]);
-      dst[0] = lo;
-      dst[1] = hi;
-      if ((tl & 7) == 0) {
-        const uint32_t gi = e / 64;
-        scales[gi] = (uint16_t)(__float_as_uint(q.s) >> 16);
-        zeros[gi] = (uint8_t)q.zp;
-      }
+    for (int j = 0; j < 8; ++j) {
+      const U4 v = raw[j];
+      const float a0 = bf16_lo(v.x), a1 = bf16_hi(v.x), a2 = bf16_lo(v.y), a3 = bf16_hi(v.y);
+      const float a4 = bf16_lo(v.z), a5 = bf16_hi(v.z), a6 = bf16_lo(v.w), a7 = bf16_hi(v.w);
+      mn[j] = fminf(fminf(fminf(a0, a1), fminf(a2, a3)), fminf(fminf(a4, a5), fminf(a6, a7)));
+      mx[j] = fmaxf(fmaxf(fmaxf(a0, a1), fmaxf(a2, a3)), fmaxf(fmaxf(a4, a5), fmaxf(a6, a7)));
+      mn[j] = lanes_min<8>(mn[j]);
+      mx[j] = lanes_max<8>(mx[j]);
     }
+    const int i = lane & 7;                  // this lane's segment for the qparams
+    float mni = mn[0], mxi = mx[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+      mni = i == j ? mn[j] : mni;
+      mxi = i == j ? mx[j] : mxi;
+    }
+    const QP q = uintx_qparams(mni, mxi, qmax);
+    const uint32_t g = (i * L1 + (p - i * kLanePos)) / 64;
+    scales[g] = (uint16_t)(__float_as_uint(q.s) >> 16);
+    zeros[g] = (uint8_t)q.zp;
+    qp_lds[threadIdx.x] = (__float_as_uint(q.inv) & 0xFFFF0000u) | (uint32_t)q.zp;
   }
   __syncthreads();
-  const int rho = t / 64;
-  const uint32_t p4 = (t % 64) * 4;
-  if (p4 >= Tb) return;
-  uint32_t C[8];
+  if (!active) return;
+  const uint32_t* qpo = &qp_lds[threadIdx.x & ~7u];
+  uint32_t clo[8], chi[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) C[j] = *reinterpret_cast<const uint32_t*>(&ctile[j * kCS + p4]);
-  if (sh.has4) {
-    const int m = rho;
-    uint32_t v = (C[m] & 0x0F0F0F0Fu) | ((C[m + 4] & 0x0F0F0F0Fu) << 4);
-    *reinterpret_cast<uint32_t*>(packed + sh.base4 + (int64_t)m * L1 + b0 + p4) = v;
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t w = qpo[j];
+    codes8(raw[j], __uint_as_float(w & 0xFFFF0000u), (float)(w & 0xFFu), qmax, clo[j], chi[j]);
   }
-  if (sh.has2 && rho < 2) {
-    const int m = rho;
-    uint32_t v = 0;
+  if constexpr (SB::has4) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) v |= ((C[m + 2 * jj] >> sh.off2) & 0x03030303u) << (2 * jj);
-    *reinterpret_cast<uint32_t*>(packed + sh.base2 + (int64_t)m * L1 + b0 + p4) = v;
+    for (int m = 0; m < 4; ++m)
+      st8(packed + sh.base4 + (int64_t)m * L1 + p, (clo[m] & 0x0F0F0F0Fu) | ((clo[m + 4] & 0x0F0F0F0Fu) << 4),
+          (chi[m] & 0x0F0F0F0Fu) | ((chi[m + 4] & 0x0F0F0F0Fu) << 4));
   }
-  if (sh.has1 && rho == 0) {
-    uint32_t v = 0;
+  if constexpr (SB::has2) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v |= ((C[j] >> sh.off1) & 0x01010101u) << j;
-    *reinterpret_cast<uint32_t*>(packed + sh.base1 + b0 + p4) = v;
+    for (int m = 0; m < 2; ++m) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        lo |= ((clo[m + 2 * jj] >> SB::off2) & 0x03030303u) << (2 * jj);
+        hi |= ((chi[m + 2 * jj] >> SB::off2) & 0x03030303u) << (2 * jj);
+      }
+      st8(packed + sh.base2 + (int64_t)m * L1 + p, lo, hi);
+    }
+  }
+  if constexpr (SB::has1) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      lo |= ((clo[j] >> SB::off1) & 0x01010101u) << j;
+      hi |= ((chi[j] >> SB::off1) & 0x01010101u) << j;
+    }
+    st8(packed + sh.base1 + p, lo, hi);
   }
 }
 
 // ------------------------------------------------------------- tiled dequantize
-template <int SINK, typename TOut>
+template <int NB, int SINK, bool CONTIG, typename TOut>
 __global__ __launch_bounds__(256) void uintx_dequant_tiled(const uint8_t* __restrict__ packed,
                                                            const uint16_t* __restrict__ scales,
-                                                           const uint8_t* __restrict__ zeros,
-                                                           FastDiv kdiv, uint32_t L1, int nbits, Shards sh,
-                                                           TOut* __restrict__ out, int64_t ldo,
-                                                           const uint16_t* __restrict__ W, int64_t ldw,
+                                                           const uint8_t* __restrict__ zeros, FastDiv kdiv,
+                                                           uint32_t L1, Shards sh, TOut* __restrict__ out,
+                                                           int64_t ldo, const uint16_t* __restrict__ W, int64_t ldw,
                                                            double* __restrict__ part) {
-  __shared__ uint8_t s4[4 * kCS], s2[2 * kCS], s1[kCS];
-  const int t = threadIdx.x;
-  const int rho = t / 64;
-  const uint32_t p4 = (t % 64) * 4;
-  const int j = t / 32, tl = t % 32;
-  double sw = 0.0, se = 0.0;
-  const uint32_t ntiles = (L1 + kT - 1) / kT;
-  for (uint32_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const uint32_t b0 = tile * kT;
-    const uint32_t Tb = min((uint32_t)kT, L1 - b0);
-    if (p4 < Tb) {
-      if (sh.has4)
-        *reinterpret_cast<uint32_t*>(&s4[rho * kCS + p4]) =
-            *reinterpret_cast<const uint32_t*>(packed + sh.base4 + (int64_t)rho * L1 + b0 + p4);
-      if (sh.has2 && rho < 2)
-        *reinterpret_cast<uint32_t*>(&s2[rho * kCS + p4]) =
-            *reinterpret_cast<const uint32_t*>(packed + sh.base2 + (int64_t)rho * L1 + b0 + p4);
-      if (sh.has1 && rho == 0)
-        *reinterpret_cast<uint32_t*>(&s1[p4]) = *reinterpret_cast<const uint32_t*>(packed + sh.base1 + b0 + p4);
+  using SB = ShardBits<NB>;
+  __shared__ uint32_t qp_lds[256];
+  const int lane = threadIdx.x & 63;
+  const uint32_t p = blockIdx.x * kBlockPos + (threadIdx.x >> 6) * kWavePos + lane * kLanePos;
+  const bool active = p < L1;
+  uint2 s4[4], s2[2], s1;
+  if (active) {
+    if constexpr (SB::has4) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) s4[m] = ld8(packed + sh.base4 + (int64_t)m * L1 + p);
     }
-    __syncthreads();
-    if ((uint32_t)tl * 8 < Tb) {
-      const uint32_t e = j * L1 + b0 + tl * 8;
-      const uint32_t gi = e / 64;
-      const float s = bf16_to_f32(scales[gi]);
-      const float zp = (float)zeros[gi];
+    if constexpr (SB::has2) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) s2[m] = ld8(packed + sh.base2 + (int64_t)m * L1 + p);
+    }
+    if constexpr (SB::has1) s1 = ld8(packed + sh.base1 + p);
+    const int i = lane & 7;
+    const uint32_t g = (i * L1 + (p - i * kLanePos)) / 64;
+    qp_lds[threadIdx.x] = ((uint32_t)scales[g] << 16) | (uint32_t)zeros[g];
+  }
+  __syncthreads();
+  double sw = 0.0, se = 0.0;
+  if (active) {
+    const uint32_t* qpo = &qp_lds[threadIdx.x & ~7u];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w = qpo[j];
+      const float s = __uint_as_float(w & 0xFFFF0000u), zp = (float)(w & 0xFFu);
+      uint32_t c[2] = {0u, 0u};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (SB::has4) c[h] |= ((h ? s4[j & 3].y : s4[j & 3].x) >> (4 * (j >> 2))) & 0x0F0F0F0Fu;
+        if constexpr (SB::has2) c[h] |= (((h ? s2[j & 1].y : s2[j & 1].x) >> (2 * (j >> 1))) & 0x03030303u) << SB::off2;
+        if constexpr (SB::has1) c[h] |= (((h ? s1.y : s1.x) >> j) & 0x01010101u) << SB::off1;
+      }
       float d[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int p = tl * 8 + i;
-        uint32_t c = 0;
-        if (sh.has4) c |= (s4[(j & 3) * kCS + p] >> (4 * (j >> 2))) & 0xFu;
-        if (sh.has2) c |= ((s2[(j & 1) * kCS + p] >> (2 * (j >> 1))) & 0x3u) << sh.off2;
-        if (sh.has1) c |= ((s1[p] >> j) & 0x1u) << sh.off1;
-        d[i] = uintx_value(c, zp, s);
+      for (int b = 0; b < 8; ++b) d[b] = ((float)((c[b >> 2] >> (8 * (b & 3))) & 0xFFu) - zp) * s;   // exact
+      const uint32_t e = j * L1 + p;
+      if constexpr (SINK == kStore && sizeof(TOut) == 2) {
+        U4 v;
+        v.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(ux_f32x2_t{d[0], d[1]}, ux_bf16x2_t));
+        v.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(ux_f32x2_t{d[2], d[3]}, ux_bf16x2_t));
+        v.z = __builtin_bit_cast(uint32_t, __builtin_convertvector(ux_f32x2_t{d[4], d[5]}, ux_bf16x2_t));
+        v.w = __builtin_bit_cast(uint32_t, __builtin_convertvector(ux_f32x2_t{d[6], d[7]}, ux_bf16x2_t));
+        st16(elem_ptr<CONTIG>(out, ldo, e, kdiv), v);
+        continue;
       }
-      const uint32_t n = fdiv(e, kdiv);
-      const uint32_t k = e - n * kdiv.d;
+#pragma unroll
+      for (int b = 0; b < 8; b += 2) round_bf16_pair(d[b], d[b + 1]);
       if constexpr (SINK == kStore) {
-        store8(out + (int64_t)n * ldo + k, d);
+        store8(elem_ptr<CONTIG>(out, ldo, e, kdiv), d);
       } else {
         float x[8];
-        load8(W + (int64_t)n * ldw + k, x);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          double xd = (double)x[i];
-          double ed = (double)(x[i] - d[i]);
-          sw = fma(xd, xd, sw);
-          se = fma(ed, ed, se);
-        }
+        to_f32(load_raw8(elem_ptr<CONTIG>(W, ldw, e, kdiv)), x);
+        acc_err8(x, d, sw, se);
       }
     }
-    __syncthreads();
   }
   if constexpr (SINK == kErr) block_sum2_store<256>(sw, se, part);
 }
 
 // ------------------------------------------------------------- ragged sizes
+struct RaggedShards {
+  int64_t base4, base2, base1;
+  int off2, off1;
+  bool has4, has2, has1;
+};
+static RaggedShards ragged_shards(int nbits, int64_t numel) {
+  const Shards b = shards_of(nbits, numel);
+  RaggedShards r{b.base4, b.base2, b.base1, (nbits & 4) ? 4 : 0, ((nbits & 4) ? 4 : 0) + ((nbits & 2) ? 2 : 0),
+                 (nbits & 4) != 0, (nbits & 2) != 0, (nbits & 1) != 0};
+  return r;
+}
+__device__ __forceinline__ void load8_at(const uint16_t* W, int64_t ldw, uint32_t e, FastDiv kdiv, float* x) {
+  const uint32_t n = fdiv(e, kdiv);
+  load8(W + (int64_t)n * ldw + (e - n * kdiv.d), x);
+}
 // Pass 1: codes of 8 consecutive elements per lane (8 lanes per group) to workspace.
 __global__ __launch_bounds__(256) void uintx_codes_flat(const uint16_t* __restrict__ W, int64_t ldw,
                                                         FastDiv kdiv, uint32_t units, int nbits,
@@ -241,7 +315,7 @@ __global__ __launch_bounds__(256) void uintx_pack_shard(const uint8_t* __restric
   }
 }
 
-__device__ __forceinline__ uint32_t uintx_gather(const uint8_t* packed, const Shards& sh, uint32_t numel,
+__device__ __forceinline__ uint32_t uintx_gather(const uint8_t* packed, const RaggedShards& sh, uint32_t numel,
                                                  uint32_t idx) {
   uint32_t c = 0;
   if (sh.has4) {
@@ -264,7 +338,7 @@ __global__ __launch_bounds__(256) void uintx_dequant_flat(const uint8_t* __restr
                                                           const uint16_t* __restrict__ scales,
                                                           const uint8_t* __restrict__ zeros,
                                                           FastDiv kdiv, uint32_t units, uint32_t numel,
-                                                          Shards sh, TOut* __restrict__ out, int64_t ldo,
+                                                          RaggedShards sh, TOut* __restrict__ out, int64_t ldo,
                                                           const uint16_t* __restrict__ W, int64_t ldw,
                                                           double* __restrict__ part) {
   const uint32_t stride = gridDim.x * blockDim.x;
@@ -302,18 +376,35 @@ size_t uintx_code_workspace(int64_t N, int64_t K) { return uintx_tiled(N, K) ? 0
 static unsigned capped(uint64_t blocks, unsigned cap) {
   return (unsigned)(blocks < cap ? (blocks ? blocks : 1) : cap);
 }
+static unsigned tiles_of(int64_t N, int64_t K) { return (unsigned)(((uint64_t)(N * K) / 8 + kBlockPos - 1) / kBlockPos); }
+
+template <int NB>
+static void quant_tiled(const void* W, int64_t N, int64_t K, int64_t ldw, void* packed, void* scales, void* zeros,
+                        hipStream_t st) {
+  const uint32_t numel = (uint32_t)(N * K);
+  const Shards sh = shards_of(NB, numel);
+  const FastDiv kdiv = make_fastdiv((uint32_t)K);
+  hipLaunchKernelGGL((ldw == K ? uintx_quant_tiled<NB, true> : uintx_quant_tiled<NB, false>), dim3(tiles_of(N, K)),
+                     dim3(256), 0, st, (const uint16_t*)W, ldw, kdiv, numel / 8, sh, (uint8_t*)packed,
+                     (uint16_t*)scales, (uint8_t*)zeros);
+}
 
 void launch_uintx_quant(int nbits, const void* W, int64_t N, int64_t K, int64_t ldw, void* packed,
                         void* scales, void* zeros, void* workspace, hipStream_t st) {
-  const uint32_t numel = (uint32_t)(N * K);
-  const Shards sh = shards_of(nbits, numel);
-  const FastDiv kdiv = make_fastdiv((uint32_t)K);
   if (uintx_tiled(N, K)) {
-    const uint32_t L1 = numel / 8;
-    hipLaunchKernelGGL(uintx_quant_tiled, dim3((L1 + kT - 1) / kT), dim3(256), 0, st, (const uint16_t*)W, ldw,
-                       kdiv, L1, nbits, sh, (uint8_t*)packed, (uint16_t*)scales, (uint8_t*)zeros);
+    switch (nbits) {
+      case 2: quant_tiled<2>(W, N, K, ldw, packed, scales, zeros, st); break;
+      case 3: quant_tiled<3>(W, N, K, ldw, packed, scales, zeros, st); break;
+      case 4: quant_tiled<4>(W, N, K, ldw, packed, scales, zeros, st); break;
+      case 5: quant_tiled<5>(W, N, K, ldw, packed, scales, zeros, st); break;
+      case 6: quant_tiled<6>(W, N, K, ldw, packed, scales, zeros, st); break;
+      default: quant_tiled<7>(W, N, K, ldw, packed, scales, zeros, st); break;
+    }
     return;
   }
+  const uint32_t numel = (uint32_t)(N * K);
+  const RaggedShards sh = ragged_shards(nbits, numel);
+  const FastDiv kdiv = make_fastdiv((uint32_t)K);
   uint8_t* codes = (uint8_t*)workspace;
   const uint32_t units = numel / 8;
   hipLaunchKernelGGL(uintx_codes_flat, dim3(capped((units + 255) / 256, kStreamGridCap)), dim3(256), 0, st,
@@ -329,43 +420,60 @@ void launch_uintx_quant(int nbits, const void* W, int64_t N, int64_t K, int64_t 
   }
 }
 
-template <int SINK, typename TOut>
-static void deq(unsigned grid, int nbits, const void* packed, const void* scales, const void* zeros, int64_t N,
-                int64_t K, void* out, int64_t ldo, const void* W, int64_t ldw, double* part, hipStream_t st) {
+template <int NB, int SINK, typename TOut>
+static void deq_tiled(const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K, void* out,
+                      int64_t ldo, const void* W, int64_t ldw, double* part, hipStream_t st) {
   const uint32_t numel = (uint32_t)(N * K);
-  const Shards sh = shards_of(nbits, numel);
+  const Shards sh = shards_of(NB, numel);
   const FastDiv kdiv = make_fastdiv((uint32_t)K);
-  if (uintx_tiled(N, K)) {
-    hipLaunchKernelGGL((uintx_dequant_tiled<SINK, TOut>), dim3(grid), dim3(256), 0, st, (const uint8_t*)packed,
-                       (const uint16_t*)scales, (const uint8_t*)zeros, kdiv, numel / 8, nbits, sh, (TOut*)out,
-                       ldo, (const uint16_t*)W, ldw, part);
-  } else {
-    hipLaunchKernelGGL((uintx_dequant_flat<SINK, TOut>), dim3(grid), dim3(256), 0, st, (const uint8_t*)packed,
-                       (const uint16_t*)scales, (const uint8_t*)zeros, kdiv, numel / 8, numel, sh, (TOut*)out,
-                       ldo, (const uint16_t*)W, ldw, part);
-  }
+  const bool contig = SINK == kStore ? ldo == K : ldw == K;
+  hipLaunchKernelGGL((contig ? uintx_dequant_tiled<NB, SINK, true, TOut> : uintx_dequant_tiled<NB, SINK, false, TOut>),
+                     dim3(tiles_of(N, K)), dim3(256), 0, st, (const uint8_t*)packed, (const uint16_t*)scales,
+                     (const uint8_t*)zeros, kdiv, numel / 8, sh, (TOut*)out, ldo, (const uint16_t*)W, ldw, part);
 }
 
-static uint64_t uintx_blocks(int64_t N, int64_t K) {
-  uint64_t numel = (uint64_t)(N * K);
-  return uintx_tiled(N, K) ? (numel / 8 + kT - 1) / kT : (numel / 8 + 255) / 256;
+template <int SINK, typename TOut>
+static void deq(int nbits, const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K,
+                void* out, int64_t ldo, const void* W, int64_t ldw, double* part, hipStream_t st) {
+  if (uintx_tiled(N, K)) {
+    switch (nbits) {
+      case 2: deq_tiled<2, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
+      case 3: deq_tiled<3, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
+      case 4: deq_tiled<4, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
+      case 5: deq_tiled<5, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
+      case 6: deq_tiled<6, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
+      default: deq_tiled<7, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
+    }
+    return;
+  }
+  const uint32_t numel = (uint32_t)(N * K);
+  const RaggedShards sh = ragged_shards(nbits, numel);
+  const FastDiv kdiv = make_fastdiv((uint32_t)K);
+  const unsigned grid = SINK == kErr ? uintx_err_blocks(N, K) : capped((numel / 8 + 255) / 256, kStreamGridCap);
+  hipLaunchKernelGGL((uintx_dequant_flat<SINK, TOut>), dim3(grid), dim3(256), 0, st, (const uint8_t*)packed,
+                     (const uint16_t*)scales, (const uint8_t*)zeros, kdiv, numel / 8, numel, sh, (TOut*)out, ldo,
+                     (const uint16_t*)W, ldw, part);
 }
 
 void launch_uintx_dequant(int nbits, const void* packed, const void* scales, const void* zeros,
                           int64_t N, int64_t K, void* out, int32_t out_dtype, int64_t ldo,
                           hipStream_t st) {
-  unsigned grid = capped(uintx_blocks(N, K), kStreamGridCap);
   if (out_dtype == kBF16)
-    deq<kStore, uint16_t>(grid, nbits, packed, scales, zeros, N, K, out, ldo, nullptr, 0, nullptr, st);
+    deq<kStore, uint16_t>(nbits, packed, scales, zeros, N, K, out, ldo, nullptr, 0, nullptr, st);
   else
-    deq<kStore, float>(grid, nbits, packed, scales, zeros, N, K, out, ldo, nullptr, 0, nullptr, st);
+    deq<kStore, float>(nbits, packed, scales, zeros, N, K, out, ldo, nullptr, 0, nullptr, st);
 }
 
-unsigned uintx_err_blocks(int64_t N, int64_t K) { return capped(uintx_blocks(N, K), kErrGridCap); }
+// The tiled error kernel runs one block per tile (its partials follow the tiles); the
+// ragged one is grid-stride with a capped grid. Both depend on the shape only.
+unsigned uintx_err_blocks(int64_t N, int64_t K) {
+  if (uintx_tiled(N, K)) return tiles_of(N, K);
+  return capped(((uint64_t)(N * K) / 8 + 255) / 256, kErrGridCap);
+}
 
 void launch_uintx_err(int nbits, const void* W, int64_t N, int64_t K, int64_t ldw, const void* packed,
                       const void* scales, const void* zeros, double* part, hipStream_t st) {
-  deq<kErr, float>(uintx_err_blocks(N, K), nbits, packed, scales, zeros, N, K, nullptr, 0, W, ldw, part, st);
+  deq<kErr, float>(nbits, packed, scales, zeros, N, K, nullptr, 0, W, ldw, part, st);
 }
 
 }  // namespace gwb

@@ -349,3 +349,22 @@ def test_empty_shapes(fmt):
         q = gwb.quantize(W, fmt)
         d = gwb.dequantize(q)
         assert tuple(d.shape) == shape
+
+
+def test_prepared_calls_match_direct_calls():
+    W = workloads.mxfp4_weight(128, 512, seed=81)
+    Wd = W.to(DEV)
+    for fmt, nb, g in [("mxfp4", 4, 32), ("gptq_asym", 4, 128), ("uintx", 5, 64)]:
+        q1 = gwb.quantize(Wd, fmt, nbits=nb, group=g)
+        q2 = gwb.quantize(torch.zeros_like(Wd), fmt, nbits=nb, group=g)
+        gwb.prepare_quantize(Wd, q2)()
+        assert torch.equal(q1.codes, q2.codes) and torch.equal(q1.scales, q2.scales)
+        d1 = gwb.dequantize(q1)
+        d2 = torch.empty_like(d1)
+        gwb.prepare_dequantize(q2, d2)()
+        assert torch.equal(d1.view(torch.int16), d2.view(torch.int16))
+        s1 = gwb.snr(Wd, q1)
+        s2 = torch.empty(3, dtype=torch.float64, device=DEV)
+        ws = torch.empty(q2.sizes["workspace"] + 16, dtype=torch.uint8, device=DEV)
+        gwb.prepare_snr(Wd, q2, s2, ws)()
+        assert torch.equal(s1, s2)
