@@ -60,22 +60,39 @@ def algo_bytes(op: str, fmt: str, nbits: int, n: int, k: int) -> float:
     raise ValueError(op)
 
 
-def source_digest(name: str) -> str:
-    with open(os.path.join(ROOT, "group_wise_bit_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+KERNEL_SOURCES = {   # what each op's kernel is compiled from (for the traffic record's digest)
+    "mxfp4": ["mxfp4.hip", "mxfp4_math.hpp", "device_common.hpp", "kernels.hpp"],
+    "gptq": ["gptq.hip", "device_common.hpp", "kernels.hpp"],
+    "uintx": ["uintx.hip", "device_common.hpp", "kernels.hpp"],
+    "awq": ["awq.hip", "mxfp4_math.hpp", "device_common.hpp", "kernels.hpp"],
+}
 
 
-def measured_traffic(kernel_key: str):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was taken on
-    the current source of that kernel; else None."""
+def source_digest(family: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[family]:
+        with open(os.path.join(ROOT, "group_wise_bit_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def family_of(op: str) -> str:
+    head = op.split(".")[0]
+    return "gptq" if head.startswith("gptq") else ("uintx" if head.startswith("uintx") else head)
+
+
+def measured_traffic(op: str):
+    """HBM bytes per launch of op's main kernel from the committed rocprofv3 --pmc
+    summary (profiles/traffic.json), if it was taken on the current kernel source;
+    else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(kernel_key)
-    except (OSError, ValueError):
+        rec = json.load(open(path))["ops"].get(op)
+    except (OSError, ValueError, KeyError):
         return None
-    if not rec or rec.get("source_sha") != source_digest(rec["source"]):
+    if not rec or rec.get("source_sha") != source_digest(family_of(op)):
         return None
     return rec.get("bytes_per_launch")
 
@@ -125,8 +142,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2176)          # 17 x 128: the step's 17:1 ratio
-    ap.add_argument("--cpu-awq-rows", type=int, default=128)
+    ap.add_argument("--cpu-rows", type=int, default=6528)          # 17 x 384: the step's 17:1 ratio
+    ap.add_argument("--cpu-awq-rows", type=int, default=384)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the quantization of "

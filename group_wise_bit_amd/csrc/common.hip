@@ -38,20 +38,32 @@ unsigned stream_blocks(uint64_t units) {
 
 // part[2*i], part[2*i+1] for i < nblocks -> out[0] = sum w^2, out[1] = sum (w-d)^2,
 // out[2] = 10 log10(out[0] / max(out[1], 1e-24)) (page export_gptq_cpu.py's
-// 20 log10(||w|| / max(||w - deq||, 1e-12)), squared inside the log). One block,
-// fixed summation order.
-__global__ __launch_bounds__(256) void err_finalize_kernel(const double* __restrict__ part,
-                                                           unsigned nblocks, double* __restrict__ out) {
-  __shared__ double sa[256], sb[256];
-  double a = 0.0, b = 0.0;
-  for (unsigned i = threadIdx.x; i < nblocks; i += 256) {
-    a += part[2 * i];
-    b += part[2 * i + 1];
+// 20 log10(||w|| / max(||w - deq||, 1e-12)), squared inside the log). One block of
+// 1024 threads; each thread sums a fixed strided subset with four independent chains,
+// then a fixed tree: deterministic for a given partial count.
+constexpr int kFinThreads = 1024;
+__global__ __launch_bounds__(kFinThreads) void err_finalize_kernel(const double2* __restrict__ part,
+                                                                   unsigned nblocks, double* __restrict__ out) {
+  __shared__ double sa[kFinThreads], sb[kFinThreads];
+  double a[4] = {0.0, 0.0, 0.0, 0.0}, b[4] = {0.0, 0.0, 0.0, 0.0};
+  unsigned i = threadIdx.x;
+  for (; i + 3 * kFinThreads < nblocks; i += 4 * kFinThreads) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double2 v = part[i + j * kFinThreads];
+      a[j] += v.x;
+      b[j] += v.y;
+    }
   }
-  sa[threadIdx.x] = a;
-  sb[threadIdx.x] = b;
+  for (; i < nblocks; i += kFinThreads) {
+    const double2 v = part[i];
+    a[0] += v.x;
+    b[0] += v.y;
+  }
+  sa[threadIdx.x] = (a[0] + a[1]) + (a[2] + a[3]);
+  sb[threadIdx.x] = (b[0] + b[1]) + (b[2] + b[3]);
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
+  for (int s = kFinThreads / 2; s > 0; s >>= 1) {
     if ((int)threadIdx.x < s) {
       sa[threadIdx.x] += sa[threadIdx.x + s];
       sb[threadIdx.x] += sb[threadIdx.x + s];
@@ -59,7 +71,7 @@ __global__ __launch_bounds__(256) void err_finalize_kernel(const double* __restr
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    double w2 = sa[0], e2 = sb[0];
+    const double w2 = sa[0], e2 = sb[0];
     out[0] = w2;
     out[1] = e2;
     out[2] = w2 == 0.0 ? -__builtin_inf() : 10.0 * log10(w2 / fmax(e2, 1e-24));
@@ -67,7 +79,7 @@ __global__ __launch_bounds__(256) void err_finalize_kernel(const double* __restr
 }
 
 void launch_err_finalize(const double* part, unsigned nblocks, double* out, hipStream_t st) {
-  hipLaunchKernelGGL(err_finalize_kernel, dim3(1), dim3(256), 0, st, part, nblocks, out);
+  hipLaunchKernelGGL(err_finalize_kernel, dim3(1), dim3(kFinThreads), 0, st, (const double2*)part, nblocks, out);
 }
 
 __global__ __launch_bounds__(256) void stream_copy_kernel(U4* __restrict__ dst, const U4* __restrict__ src,
