@@ -17,6 +17,8 @@ constexpr int kDppXor2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
 // row_mirror: within each 16-lane row, lane i reads 15-i (joins the two half-rows).
 constexpr int kDppMirror = 0x140;
+// row_ror:8: within each 16-lane row, lane i reads lane (i + 8) % 16.
+constexpr int kDppRor8 = 0x128;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_read(float x) {

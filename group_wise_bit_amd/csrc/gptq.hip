@@ -4,125 +4,73 @@
 //
 // A tile is 32 weight rows (output channels n) x 512 along K. Each lane takes 8
 // consecutive k of one row (one 128-bit bf16 load), so a group of G is G/8 adjacent
-// lanes and its amax (or min/max) is a DPP reduction within a 16-lane row, while each
-// load instruction of a wavefront reads 1 KB of one row (long DRAM runs). A lane's 8
-// codes are one qweight word (r, n); words go through LDS so that the [K/8, N] int32
-// output leaves as 128-byte runs along n.
-//
-// Codes need rint(fl(x / s)) with IEEE division. Per element the kernel forms
-// q = x * y with y the hardware reciprocal of s (within 1 ulp of 1/s), so
-// |q - x/s| <= |x/s| * 1.5 * 2^-23, and fl(x/s) is within |x/s| * 2^-24 of x/s: when
-// rint(q) is further than |q| * 2^-19 from a half-integer, both round to the same
-// integer. Otherwise (about one element in 10^4) the kernel divides exactly. |q| > 64
-// clamps either way.
+// lanes while each load instruction of a wavefront reads 1 KB of one row (long DRAM
+// runs). A group's extremes are reduced for all 8 rows of a wave at once, transposed
+// over the group's lanes, so each (row, group) scale and zero point is computed by one
+// lane (with IEEE division) and shared through LDS. A lane's 8 codes are one qweight
+// word (r, n); words go through LDS so that the [K/8, N] int32 output leaves as 128-byte
+// runs along n.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace gwb {
 
-typedef short s16x2_t __attribute__((ext_vector_type(2)));
-typedef unsigned short gq_u16x2_t __attribute__((ext_vector_type(2)));
+// ------------------------------------------------------------- group extremes
+// Order-preserving float keys of a lane's 8 weights. A 32-bit word holding two bf16
+// weights, read as a float32, orders like its upper weight: the lower weight only adds
+// mantissa bits below the upper one's last place, so words whose upper weights differ
+// never swap. The word rotated by 16 bits orders like its lower weight. Clearing the
+// low 16 bits of the extreme key gives that weight exactly. float32 weights are their
+// own keys.
+template <typename TIn> struct GqKeys;
+template <> struct GqKeys<uint16_t> {
+  static __device__ __forceinline__ void get(const Raw8<uint16_t>& r, float* o) {
+    const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[i] = __uint_as_float(w[i]);
+      o[i + 4] = __uint_as_float((w[i] >> 16) | (w[i] << 16));
+    }
+  }
+  static __device__ __forceinline__ float value(float k) { return __uint_as_float(__float_as_uint(k) & 0xFFFF0000u); }
+};
+template <> struct GqKeys<float> {
+  static __device__ __forceinline__ void get(const Raw8<float>& r, float* o) { to_f32(r, o); }
+  static __device__ __forceinline__ float value(float k) { return k; }
+};
 
-// ------------------------------------------------------------- group reductions
-// amax of 8 weights as float32 bits (|x| orders like its bits).
-__device__ __forceinline__ uint32_t gq_absmax_bits(const Raw8<uint16_t>& r) {
-  const uint32_t m = 0x7FFF7FFFu;
-  gq_u16x2_t a = __builtin_bit_cast(gq_u16x2_t, r.v.x & m), b = __builtin_bit_cast(gq_u16x2_t, r.v.y & m);
-  gq_u16x2_t c = __builtin_bit_cast(gq_u16x2_t, r.v.z & m), d = __builtin_bit_cast(gq_u16x2_t, r.v.w & m);
-  gq_u16x2_t e = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
-  const uint32_t lo = e[0], hi = e[1];
-  return (lo > hi ? lo : hi) << 16;
-}
-__device__ __forceinline__ uint32_t gq_absmax_bits(const Raw8<float>& r) {
-  const uint32_t m = 0x7FFFFFFFu;
-  uint32_t a = max(max(r.a.x & m, r.a.y & m), max(r.a.z & m, r.a.w & m));
-  uint32_t b = max(max(r.b.x & m, r.b.y & m), max(r.b.z & m, r.b.w & m));
-  return max(a, b);
-}
-template <int LANES>
-__device__ __forceinline__ uint32_t lanes_max_u(uint32_t x) {
-  if constexpr (LANES >= 2) x = max(x, dpp_read_u<kDppXor1>(x));
-  if constexpr (LANES >= 4) x = max(x, dpp_read_u<kDppXor2>(x));
-  if constexpr (LANES >= 8) x = max(x, dpp_read_u<kDppHalfMirror>(x));
-  if constexpr (LANES >= 16) x = max(x, dpp_read_u<kDppMirror>(x));
-  return x;
-}
-template <int LANES>
-__device__ __forceinline__ int lanes_min_i(int x) {
-  if constexpr (LANES >= 2) x = min(x, (int)dpp_read_u<kDppXor1>((uint32_t)x));
-  if constexpr (LANES >= 4) x = min(x, (int)dpp_read_u<kDppXor2>((uint32_t)x));
-  if constexpr (LANES >= 8) x = min(x, (int)dpp_read_u<kDppHalfMirror>((uint32_t)x));
-  if constexpr (LANES >= 16) x = min(x, (int)dpp_read_u<kDppMirror>((uint32_t)x));
-  return x;
-}
-template <int LANES>
-__device__ __forceinline__ int lanes_max_i(int x) {
-  if constexpr (LANES >= 2) x = max(x, (int)dpp_read_u<kDppXor1>((uint32_t)x));
-  if constexpr (LANES >= 4) x = max(x, (int)dpp_read_u<kDppXor2>((uint32_t)x));
-  if constexpr (LANES >= 8) x = max(x, (int)dpp_read_u<kDppHalfMirror>((uint32_t)x));
-  if constexpr (LANES >= 16) x = max(x, (int)dpp_read_u<kDppMirror>((uint32_t)x));
-  return x;
+// One butterfly step over the first NV values: lanes with `up` set keep the upper half
+// and send the lower, their partner (which has `up` clear) does the opposite.
+template <int CTRL, int NV, bool MAX>
+__device__ __forceinline__ void xstep(float (&v)[8], bool up) {
+#pragma unroll
+  for (int i = 0; i < NV / 2; ++i) {
+    const float keep = up ? v[i + NV / 2] : v[i], send = up ? v[i] : v[i + NV / 2];
+    const float other = dpp_read<CTRL>(send);
+    v[i] = MAX ? fmaxf(keep, other) : fminf(keep, other);
+  }
 }
 
-// Signed-order keys: key(h) = h ^ ((h >> 15) & 0x7FFF) as int16 orders bf16 bit
-// patterns h like their values (-0 just below +0); the map is its own inverse.
-__device__ __forceinline__ s16x2_t bf16_keys(uint32_t w) {
-  const s16x2_t h = __builtin_bit_cast(s16x2_t, w);
-  return h ^ ((h >> (short)15) & (short)0x7FFF);
-}
-__device__ __forceinline__ float key_to_f32(int k) {
-  const int h = k ^ ((k >> 15) & 0x7FFF);
-  return __uint_as_float((uint32_t)h << 16);
-}
-template <int LANES>
-__device__ __forceinline__ void gq_minmax(const Raw8<uint16_t>& r, float& mn, float& mx) {
-  const s16x2_t a = bf16_keys(r.v.x), b = bf16_keys(r.v.y), c = bf16_keys(r.v.z), d = bf16_keys(r.v.w);
-  const s16x2_t lo = __builtin_elementwise_min(__builtin_elementwise_min(a, b), __builtin_elementwise_min(c, d));
-  const s16x2_t hi = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
-  const int kmin = lanes_min_i<LANES>(min((int)lo[0], (int)lo[1]));
-  const int kmax = lanes_max_i<LANES>(max((int)hi[0], (int)hi[1]));
-  mn = key_to_f32(kmin);
-  mx = key_to_f32(kmax);
-}
-template <int LANES>
-__device__ __forceinline__ void gq_minmax(const Raw8<float>& r, float& mn, float& mx) {
-  float x[8];
-  to_f32(r, x);
-  mn = x[0];
-  mx = x[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    mn = fminf(mn, x[i]);
-    mx = fmaxf(mx, x[i]);
+// Reduce 8 rows' values over the L lanes of a group, transposed: with LL = min(L, 8)
+// and R = 8 / LL, lane l ends holding rows (l % LL) * R + j, j < R, in v[j]. The
+// half-mirror partner of lane i is 7 - i, which differs in bit 2 (and in bits 0-1, which
+// no earlier step has used); the quad steps pair lanes differing in bit 1, then bit 0;
+// for 16 lanes a rotation by 8 joins the two half-rows, which hold the same rows.
+template <int L, bool MAX>
+__device__ __forceinline__ void xreduce(float (&v)[8], int lane) {
+  static_assert(L == 4 || L == 8 || L == 16, "groups of 32, 64 or 128");
+  if constexpr (L >= 8) {
+    xstep<kDppHalfMirror, 8, MAX>(v, lane & 4);
+    xstep<kDppXor2, 4, MAX>(v, lane & 2);
+    xstep<kDppXor1, 2, MAX>(v, lane & 1);
+    if constexpr (L == 16) {
+      const float other = dpp_read<kDppRor8>(v[0]);
+      v[0] = MAX ? fmaxf(v[0], other) : fminf(v[0], other);
+    }
+  } else {
+    xstep<kDppXor2, 8, MAX>(v, lane & 2);
+    xstep<kDppXor1, 4, MAX>(v, lane & 1);
   }
-  mn = lanes_min<LANES>(mn);
-  mx = lanes_max<LANES>(mx);
-}
-
-// ------------------------------------------------------------- codes
-// 8 codes clamp(rint(fl(x / s)) + zp, 0, 15) packed into one word (code i in bits 4i..).
-// A |q| so large that the margin test fails (only in degenerate groups) takes the exact
-// path too.
-__device__ __forceinline__ uint32_t gq_word(const float* x, float s, float zp) {
-  const float y = __builtin_amdgcn_rcpf(s);
-  float n[8];
-  bool ok = true;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float q = x[i] * y;
-    n[i] = rintf(q);
-    // fmaf only bounds a margin: its rounding cannot pass an unsafe case, the margin
-    // being 8x the worst-case distance
-    ok &= __builtin_fmaf(fabsf(q), 0x1p-19f, fabsf(q - n[i])) < 0.5f;
-  }
-  if (!ok) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) n[i] = rintf(x[i] / s);
-  }
-  uint32_t w = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) w |= (uint32_t)__builtin_amdgcn_fmed3f(n[i] + zp, 0.0f, 15.0f) << (4 * i);
-  return w;
 }
 
 // Tile: 32 rows x 512 k. Wave w holds rows 8w..8w+7; lane l holds k = k0 + 8l..8l+7 of
@@ -138,6 +86,13 @@ struct TileG {
   static constexpr int NG = kTK / G;                // groups per tile row
 };
 
+// Codes: with y the hardware reciprocal of s (within 1 ulp of 1/s) and t = x / s,
+// u = fma(x, y, zp) is within (|t| + 8) * 1.5 * 2^-23 of t + zp, and fl(x / s) within
+// |t| * 2^-24 of t. When every |u - rint(u)| of a lane's 8 weights stays below
+// 0.5 - (A / s + 16) * 2^-19 (A the group's largest magnitude, so |t| <= A / s), t + zp
+// and fl(x / s) + zp lie strictly inside the same unit interval around rint(u), so
+// rint(u) = rint(fl(x / s)) + zp. Otherwise (about one weight in 10^4, or every weight
+// of a group whose A / s reaches 2^18) the lane divides exactly.
 template <bool SYM, int G, typename TIn>
 __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__ W, int64_t ldw,
                                                          int N, int K, int ntk,
@@ -146,43 +101,88 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
                                                          uint32_t* __restrict__ qzeros,
                                                          int32_t* __restrict__ g_idx) {
   using T = TileG<G>;
+  constexpr int L = T::L, LL = L < 8 ? L : 8, R = 8 / LL;
   __shared__ uint32_t qtile[kTR * kQS];
-  __shared__ float stile[T::NG * kTN];
-  __shared__ uint8_t ztile[T::NG * kTN];
+  __shared__ float4 qp[kTN][T::NG];                 // per tile row and group: {1/s, zp, margin, s}
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
   const int nt = blockIdx.x / ntk, kt = blockIdx.x - nt * ntk;
   const int n0 = nt * kTN, k0 = kt * kTK;
-  const int k = k0 + lane * 8;
-  const bool kok = k < K;                           // whole groups: K % G == 0
+  // Lanes past K read a valid place instead: K % G == 0, so their groups lie wholly past
+  // K and every reduction below stays within one group. Rows past N repeat row N - 1.
+  // Nothing of either reaches memory.
+  const int kc = min(k0 + lane * 8, K - 8);
   Raw8<TIn> raw[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int n = n0 + wave * 8 + i;
-    if (kok && n < N) raw[i] = load_raw8(W + (int64_t)n * ldw + k);
-  }
+  for (int i = 0; i < 8; ++i) raw[i] = load_raw8(W + (int64_t)min(n0 + wave * 8 + i, N - 1) * ldw + kc);
+
+  float lo[8], hi[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int rl = wave * 8 + i;
-    if (kok && n0 + rl < N) {
-      float x[8];
-      to_f32(raw[i], x);
-      float s, zp;
+    float key[8];
+    GqKeys<TIn>::get(raw[i], key);
+    if constexpr (SYM) {
+      float m = fabsf(key[0]);
+#pragma unroll
+      for (int j = 1; j < 8; ++j) m = fmaxf(m, fabsf(key[j]));
+      hi[i] = m;
+    } else {
+      float a = key[0], b = key[0];
+#pragma unroll
+      for (int j = 1; j < 8; ++j) {
+        a = fminf(a, key[j]);
+        b = fmaxf(b, key[j]);
+      }
+      lo[i] = a;
+      hi[i] = b;
+    }
+  }
+  if constexpr (!SYM) xreduce<L, false>(lo, lane);
+  xreduce<L, true>(hi, lane);
+  if (L < 16 || (lane & 8) == 0) {                  // for 16 lanes, lanes 8-15 repeat 0-7
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const int row = (lane % LL) * R + j;
+      float s, zp, a;
       if constexpr (SYM) {
-        const float amax = __uint_as_float(lanes_max_u<T::L>(gq_absmax_bits(raw[i])));
-        s = fmaxf(amax * 0.125f, 1e-9f);            // amax / 8: exact scaling by 2^-3
+        a = GqKeys<TIn>::value(hi[j]);
+        s = fmaxf(a * 0.125f, 1e-9f);               // amax / 8: exact scaling by 2^-3
         zp = 8.0f;
       } else {
-        float mn, mx;
-        gq_minmax<T::L>(raw[i], mn, mx);
+        const float mn = GqKeys<TIn>::value(lo[j]), mx = GqKeys<TIn>::value(hi[j]);
         s = fmaxf(mx - mn, 1e-9f) / 15.0f;
         zp = __builtin_amdgcn_fmed3f(rintf(-mn / s), 0.0f, 15.0f);
+        a = fmaxf(fabsf(mn), fabsf(mx));
       }
-      qtile[lane * kQS + rl] = gq_word(x, s, zp);
-      if ((lane % T::L) == 0) {
-        stile[(lane / T::L) * kTN + rl] = s;
-        ztile[(lane / T::L) * kTN + rl] = (uint8_t)zp;
-      }
+      const float y = __builtin_amdgcn_rcpf(s);
+      const float margin = 0.5f - __builtin_fmaf(a, y, 16.0f) * 0x1p-19f;
+      qp[wave * 8 + row][lane / L] = make_float4(y, zp, margin, s);
     }
+  }
+  __syncthreads();
+  const int gl = lane / L;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 p = qp[wave * 8 + i][gl];
+    float x[8], c[8], dev = 0.0f;
+    to_f32(raw[i], x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float u = __builtin_fmaf(x[j], p.x, p.y);
+      c[j] = rintf(u);
+      dev = fmaxf(dev, fabsf(u - c[j]));
+    }
+    // margin <= 0 flags a group whose quotients may overflow: dev is not used then
+    if (p.z <= 0.0f || dev >= p.z) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = rintf(x[j] / p.w) + p.y;
+    }
+    uint32_t ev = 0, od = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ev = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(c[2 * j], 0.0f, 15.0f), j, ev);
+      od = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(c[2 * j + 1], 0.0f, 15.0f), j, od);
+    }
+    qtile[lane * kQS + wave * 8 + i] = ev | (od << 4);
   }
   __syncthreads();
   {  // qweight [K/8, N]: 64 r-rows x 32 words, 8 words (32 bytes) per thread
@@ -195,20 +195,20 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
     }
   }
   for (int e = t; e < T::NG * kTN; e += 256) {   // scales [K/G, N]
-    const int gl = e / kTN, rl = e % kTN;
-    if (k0 + gl * G < K && n0 + rl < N) scales[(int64_t)(k0 / G + gl) * N + n0 + rl] = (_Float16)stile[e];
+    const int g = e / kTN, rl = e % kTN;
+    if (k0 + g * G < K && n0 + rl < N) scales[(int64_t)(k0 / G + g) * N + n0 + rl] = (_Float16)qp[rl][g].w;
   }
   static_assert(T::NG * (kTN / 8) <= 256, "one qzeros word per thread");
   if (t < T::NG * (kTN / 8)) {   // qzeros [K/G, N/8]
-    const int gl = t / (kTN / 8), q = t % (kTN / 8);
-    if (k0 + gl * G < K && n0 + 8 * q < N) {
+    const int g = t / (kTN / 8), q = t % (kTN / 8);
+    if (k0 + g * G < K && n0 + 8 * q < N) {
       uint32_t w = 0x77777777u;
       if constexpr (!SYM) {
         w = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) w |= (uint32_t)ztile[gl * kTN + 8 * q + i] << (4 * i);
+        for (int i = 0; i < 8; ++i) w |= (uint32_t)qp[8 * q + i][g].y << (4 * i);
       }
-      qzeros[(int64_t)(k0 / G + gl) * (N / 8) + n0 / 8 + q] = w;
+      qzeros[(int64_t)(k0 / G + g) * (N / 8) + n0 / 8 + q] = w;
     }
   }
   if (g_idx && nt == 0) {
