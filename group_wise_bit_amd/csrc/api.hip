@@ -255,7 +255,7 @@ int gwb_awq_workspace(int64_t N, int64_t K, int32_t n_alpha, int64_t max_rows, s
   if (n_alpha < 1 || n_alpha > 16) return fail(GWB_E_ARG, "n_alpha must be 1..16, got %d", n_alpha);
   int64_t rows, step;
   awq_rows(N, max_rows, &rows, &step);
-  *bytes = (size_t)gwb::awq_blocks(rows, K) * (size_t)n_alpha * sizeof(double);
+  *bytes = gwb::awq_workspace_bytes(rows, K, n_alpha);
   return ok();
 }
 
@@ -272,11 +272,12 @@ int gwb_awq_search_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, i
   if (max_rows <= 0) return fail(GWB_E_ARG, "max_rows must be positive");
   int64_t rows, step;
   awq_rows(N, max_rows, &rows, &step);
-  const size_t need = (size_t)gwb::awq_blocks(rows, K) * (size_t)n_alpha * sizeof(double);
+  const size_t need = gwb::awq_workspace_bytes(rows, K, n_alpha);
   if (!workspace || workspace_bytes < need)
     return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
   gwb::launch_awq(W, w_dtype, rows, step, K, ldw, d_a, alphas, n_alpha, d_s_table, d_err, d_best,
-                  (double*)workspace, nullptr, (hipStream_t)stream);
+                  workspace, (hipStream_t)stream);
   return hip_check("awq launch");
 }
 

@@ -65,10 +65,13 @@ void launch_uintx_err(int nbits, const void* W, int64_t N, int64_t K, int64_t ld
 void launch_err_finalize(const double* part, unsigned nblocks, double* out, hipStream_t st);
 
 // ---- AWQ (awq.hip)
-unsigned awq_blocks(int64_t rows, int64_t K);
+// Workspace bytes for a search over `rows` subsample rows of K columns (fixed by the
+// shape alone); launch_awq carves it into the scaling powers, their log sums, the
+// reciprocal tables and the per-block error partials.
+size_t awq_workspace_bytes(int64_t rows, int64_t K, int n_alpha);
 void launch_awq(const void* W, int32_t w_dtype, int64_t rows, int64_t row_step, int64_t K,
                 int64_t ldw, const float* a, const double* alphas, int n_alpha, float* s_table,
-                double* err, int32_t* best, double* part, double* stat, hipStream_t st);
+                double* err, int32_t* best, void* workspace, hipStream_t st);
 
 // ---- measurement copy (common.hip)
 void launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t st);

@@ -71,24 +71,27 @@ __device__ __forceinline__ uint32_t mx_pack8(const float* x, float sc) {
 // Dequantized value of one code with an E8M0 byte of 255, which the conversions do not
 // define: the page's float32 product +-E2M1[c & 7] * 2**128 (inf, or NaN for 0 * inf).
 __device__ __forceinline__ float mx_value_nan_scale(uint32_t c) {
-  float mag = (c & 7u) ? __builtin_inff() : __builtin_nanf("");
+  float mag = __uint_as_float((c & 7u) ? 0x7F800000u : 0x7FC00000u);
   return (c & 8u) ? -mag : mag;
 }
 
 // word of 8 codes -> 8 float32 / 8 bf16 (exact: e2m1 values times a power of two).
-__device__ __forceinline__ void mx_unpack8(uint32_t w, uint32_t e8, float* d) {
-  if (e8 == 255u) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) d[i] = mx_value_nan_scale((w >> (4 * i)) & 0xFu);
-    return;
-  }
-  const float sc = mx_scale_operand(e8);
+// mx_unpack8_cvt takes the scale operand of an E8M0 byte other than 255.
+__device__ __forceinline__ void mx_unpack8_cvt(uint32_t w, float sc, float* d) {
   f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
   f32x2_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
   f32x2_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
   f32x2_t e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
   d[0] = a[0]; d[1] = a[1]; d[2] = b[0]; d[3] = b[1];
   d[4] = c[0]; d[5] = c[1]; d[6] = e[0]; d[7] = e[1];
+}
+__device__ __forceinline__ void mx_unpack8(uint32_t w, uint32_t e8, float* d) {
+  if (e8 == 255u) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d[i] = mx_value_nan_scale((w >> (4 * i)) & 0xFu);
+    return;
+  }
+  mx_unpack8_cvt(w, mx_scale_operand(e8), d);
 }
 __device__ __forceinline__ U4 mx_unpack8_bf16(uint32_t w, uint32_t e8) {
   if (e8 == 255u) {

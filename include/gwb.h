@@ -143,13 +143,15 @@ int gwb_awq_workspace(int64_t N, int64_t K, int32_t n_alpha, int64_t max_rows, s
  *   W        [N, K] of w_dtype, row stride ldw; rows W[::max(1, N / max_rows)][:max_rows]
  *            are used (max_rows > 0; the page uses 2048)
  *   d_a      float32 [K] per-input-channel mean |x| (device)
- *   alphas   HOST array of n_alpha doubles (1 <= n_alpha <= 32), e.g. 0, 0.1, ..., 1
+ *   alphas   HOST array of n_alpha doubles (1 <= n_alpha <= 16), e.g. 0, 0.1, ..., 1;
+ *            NULL: d_s_table already holds the n_alpha scaling rows and is only read
  * Steps: a' = max(a, 1e-8); an = a' / mean(a'); per alpha s = clamp(an**alpha, 1e-2,
  * 1e2) / geomean (float64, rounded once to float32, written to d_s_table [n_alpha, K]);
  * X = W * s; D = dequant(quant_mxfp4(X)); err = sum(((D / s - W) * a')**2) with float32
  * elementwise ops and a float64 sum -> d_err [n_alpha] (device doubles);
  * d_best[0] = the first index with the strictly smallest error (device int32).
- * K % 32 == 0 is required.                                                          */
+ * K % 32 == 0 is required; d_a, d_s_table and workspace must be 16-byte aligned, with
+ * at least gwb_awq_workspace bytes of workspace. Deterministic for a given shape.    */
 int gwb_awq_search_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
                          const float* d_a, const double* alphas, int32_t n_alpha,
                          int64_t max_rows, float* d_s_table, double* d_err, int32_t* d_best,

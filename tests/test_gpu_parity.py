@@ -227,6 +227,35 @@ def test_awq_constant_stat_selects_alpha0():
     assert np.all(err == err[0]) and int(_np(r["best"])[0]) == 0
 
 
+def test_awq_exact_division_blocks_and_scalings():
+    """D / s is a product with a stored quotient only for blocks whose E8M0 byte lies in
+    [16, 238] and scalings in [2^-14, 2^14]; subnormal and tiny spans (E8M0 below 16)
+    and scalings at and beyond those edges take the exact division. Both paths must give
+    the oracle's errors (same scalings supplied: only the float64 sum order differs)."""
+    W = workloads.adversarial_weight(64, 512, seed=64).float()
+    W = torch.where(W.abs() > 1e3, W * 2.0 ** -100, W).to(torch.bfloat16)   # keep every square finite
+    a = workloads.awq_activation_stat(512, seed=65)
+    rng = np.random.default_rng(66)
+    base = np.exp(rng.uniform(-2, 2, 512)).astype(np.float32)
+    col = np.arange(512)
+    table = np.stack([
+        base,
+        np.full(512, 2.0 ** -14, np.float32),
+        np.full(512, 2.0 ** 14, np.float32),
+        np.where(col % 7 == 0, np.float32(2.0 ** -20), base).astype(np.float32),
+        np.where(col % 5 == 0, np.float32(3.0e5), base).astype(np.float32),
+        np.where(col % 3 == 0, np.float32(1.0e-30), base).astype(np.float32),
+    ])
+    Wn = W.float().numpy()
+    ref = np.array([oawq.weighted_error(Wn, a.numpy(), table[i]) for i in range(len(table))])
+    assert np.all(np.isfinite(ref))
+    r = gwb.awq_search(W.to(DEV), a.to(DEV), alphas=None, s_table=torch.from_numpy(table).to(DEV),
+                       max_rows=W.shape[0])
+    assert np.array_equal(_np(r["s_table"]), table)
+    assert np.allclose(_np(r["err"]), ref, rtol=1e-12, atol=0)
+    assert int(_np(r["best"])[0]) == int(np.argmin(ref))
+
+
 # ------------------------------------------------------------- full config sizes
 def _rows(n, count, seed):
     return np.sort(np.random.default_rng(seed).choice(n, count, replace=False))
