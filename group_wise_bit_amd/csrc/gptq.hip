@@ -91,8 +91,9 @@ struct TileG {
 // |t| * 2^-24 of t. When every |u - rint(u)| of a lane's 8 weights stays below
 // 0.5 - (A / s + 16) * 2^-19 (A the group's largest magnitude, so |t| <= A / s), t + zp
 // and fl(x / s) + zp lie strictly inside the same unit interval around rint(u), so
-// rint(u) = rint(fl(x / s)) + zp. Otherwise (about one weight in 10^4, or every weight
-// of a group whose A / s reaches 2^18) the lane divides exactly.
+// rint(u) = rint(fl(x / s)) + zp. Otherwise (the exact and near ties, a few weights in
+// a thousand for bf16 data, or every weight of a group whose A / s reaches 2^18) the
+// weight is divided exactly.
 template <bool SYM, int G, typename TIn>
 __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__ W, int64_t ldw,
                                                          int N, int K, int ntk,
@@ -153,8 +154,12 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
         zp = __builtin_amdgcn_fmed3f(rintf(-mn / s), 0.0f, 15.0f);
         a = fmaxf(fabsf(mn), fabsf(mx));
       }
-      const float y = __builtin_amdgcn_rcpf(s);
-      const float margin = 0.5f - __builtin_fmaf(a, y, 16.0f) * 0x1p-19f;
+      float y = __builtin_amdgcn_rcpf(s);
+      float margin = 0.5f - __builtin_fmaf(a, y, 16.0f) * 0x1p-19f;
+      if (!(margin > 0.0f)) {   // quotients up to 2^18 or beyond: every weight divides
+        y = 0.0f;               // (u = zp then, so no overflow reaches the margin test)
+        margin = -1.0f;
+      }
       qp[wave * 8 + row][lane / L] = make_float4(y, zp, margin, s);
     }
   }
@@ -163,18 +168,20 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float4 p = qp[wave * 8 + i][gl];
-    float x[8], c[8], dev = 0.0f;
+    float x[8], u[8], c[8], dev = 0.0f;
     to_f32(raw[i], x);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float u = __builtin_fmaf(x[j], p.x, p.y);
-      c[j] = rintf(u);
-      dev = fmaxf(dev, fabsf(u - c[j]));
+      u[j] = __builtin_fmaf(x[j], p.x, p.y);
+      c[j] = rintf(u[j]);
+      dev = fmaxf(dev, fabsf(u[j] - c[j]));
     }
-    // margin <= 0 flags a group whose quotients may overflow: dev is not used then
-    if (p.z <= 0.0f || dev >= p.z) {
+    // Bf16 weights make exact and near ties x / s = k + 1/2 common (a few per thousand):
+    // only the weights that fail the margin divide, each under its own mask.
+    if (dev >= p.z) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) c[j] = rintf(x[j] / p.w) + p.y;
+      for (int j = 0; j < 8; ++j)
+        if (fabsf(u[j] - c[j]) >= p.z) c[j] = rintf(x[j] / p.w) + p.y;
     }
     uint32_t ev = 0, od = 0;
 #pragma unroll
