@@ -238,31 +238,53 @@ __global__ __launch_bounds__(256) void gptq_dequant_kernel(const uint32_t* __res
                                                            double* __restrict__ part) {
   using T = TileG<G>;
   __shared__ uint32_t qtile[kTR * kQS];
-  __shared__ float stile[T::NG * kTN];
+  __shared__ uint16_t stile[T::NG * kTN];          // fp16 scale bits, widened on use
   __shared__ uint32_t ztile[T::NG * (kTN / 8)];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const uint16_t* scale_bits = reinterpret_cast<const uint16_t*>(scales);
   double sw = 0.0, se = 0.0;
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int nt = tile / ntk, kt = tile - nt * ntk;
     const int n0 = nt * kTN, k0 = kt * kTK;
-    {
-      const int r = t >> 2, c8 = (t & 3) * 8;
-      if (k0 / 8 + r < K / 8 && n0 + c8 < N) {
-        const uint32_t* src = qweight + (int64_t)(k0 / 8 + r) * N + n0 + c8;
-        const U4 a = ld16_nt(src), b = ld16_nt(src + 4);
-        uint32_t* dst = &qtile[r * kQS + c8];
-        dst[0] = a.x; dst[1] = a.y; dst[2] = a.z; dst[3] = a.w;
-        dst[4] = b.x; dst[5] = b.y; dst[6] = b.z; dst[7] = b.w;
-      }
+    // Staging loads first, then the error sink's weights: the LDS stores below wait only
+    // for the staging data, and the weights stay in flight across the barrier. (Rows
+    // past N or k past K read clamped in-bounds places; those values are not used.)
+    const int r = t >> 2, c8 = (t & 3) * 8;
+    const bool qok = k0 / 8 + r < K / 8 && n0 + c8 < N;
+    U4 qa{}, qb{};
+    if (qok) {
+      const uint32_t* src = qweight + (int64_t)(k0 / 8 + r) * N + n0 + c8;
+      qa = ld16_nt(src);
+      qb = ld16_nt(src + 4);
     }
-    for (int e = t; e < T::NG * kTN; e += 256) {
-      const int gl = e / kTN, rl = e % kTN;
-      if (k0 + gl * G < K && n0 + rl < N) stile[e] = (float)scales[(int64_t)(k0 / G + gl) * N + n0 + rl];
+    constexpr int kSPer = (T::NG * kTN + 255) / 256;   // scales per thread
+    uint16_t sv[kSPer];
+#pragma unroll
+    for (int q = 0; q < kSPer; ++q) {
+      const int e = t + 256 * q, gl = e / kTN, rl = e % kTN;
+      sv[q] = 0;
+      if (e < T::NG * kTN && k0 + gl * G < K && n0 + rl < N) sv[q] = scale_bits[(int64_t)(k0 / G + gl) * N + n0 + rl];
     }
+    uint32_t zv = 0;
     if (!SYM && t < T::NG * (kTN / 8)) {
       const int gl = t / (kTN / 8), q = t % (kTN / 8);
-      if (k0 + gl * G < K && n0 + 8 * q < N) ztile[t] = qzeros[(int64_t)(k0 / G + gl) * (N / 8) + n0 / 8 + q];
+      if (k0 + gl * G < K && n0 + 8 * q < N) zv = qzeros[(int64_t)(k0 / G + gl) * (N / 8) + n0 / 8 + q];
     }
+    Raw8<TW> wr[8];
+    if constexpr (SINK == kErr) {
+      const int kc = min(k0 + lane * 8, K - 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) wr[i] = load_raw8(W + (int64_t)min(n0 + wave * 8 + i, N - 1) * ldw + kc);
+    }
+    if (qok) {
+      uint32_t* dst = &qtile[r * kQS + c8];
+      dst[0] = qa.x; dst[1] = qa.y; dst[2] = qa.z; dst[3] = qa.w;
+      dst[4] = qb.x; dst[5] = qb.y; dst[6] = qb.z; dst[7] = qb.w;
+    }
+#pragma unroll
+    for (int q = 0; q < kSPer; ++q)
+      if (t + 256 * q < T::NG * kTN) stile[t + 256 * q] = sv[q];
+    if (!SYM && t < T::NG * (kTN / 8)) ztile[t] = zv;
     __syncthreads();
     const int k = k0 + lane * 8;
     if (k < K) {
@@ -273,7 +295,7 @@ __global__ __launch_bounds__(256) void gptq_dequant_kernel(const uint32_t* __res
         const int n = n0 + rl;
         if (n < N) {
           const uint32_t word = qtile[lane * kQS + rl];
-          const float s = stile[gl * kTN + rl];
+          const float s = (float)__builtin_bit_cast(_Float16, stile[gl * kTN + rl]);
           float z = 8.0f;
           if constexpr (!SYM) z = (float)((ztile[gl * (kTN / 8) + rl / 8] >> (4 * (rl % 8))) & 0xFu);
           const uint32_t ev = word & 0x0F0F0F0Fu, od = (word >> 4) & 0x0F0F0F0Fu;
@@ -297,7 +319,7 @@ __global__ __launch_bounds__(256) void gptq_dequant_kernel(const uint32_t* __res
             store8(out + (int64_t)n * ldo + k, d);
           } else {
             float x[8];
-            to_f32(load_raw8(W + (int64_t)n * ldw + k), x);
+            to_f32(wr[i], x);
             acc_err8(x, d, sw, se);
           }
         }

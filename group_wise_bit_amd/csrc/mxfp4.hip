@@ -64,15 +64,16 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const TIn* __restrict_
   for (; u < units; u += stride) quant_unit(load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr)), u, packed, e8m0);
 }
 
-// Unpack + dequantize. SINK == kStore writes out[n, k]; SINK == kErr reads W at the
-// same place and accumulates sum w^2 and sum (w - d)^2 into per-block partials.
+// Unpack + dequantize. SINK == kStore writes out[n, k]; SINK == kErr takes W at the
+// same place (loaded by the caller with the packed word) and accumulates sum w^2 and
+// sum (w - d)^2 into per-block partials.
 template <int SINK, bool CONTIG, typename TOut, typename TW>
 __device__ __forceinline__ void dequant_unit(uint32_t word, uint32_t e8, uint32_t u, FastDiv upr,
-                                             TOut* __restrict__ out, int64_t ldo, const TW* __restrict__ W,
-                                             int64_t ldw, double& sw, double& se) {
+                                             TOut* __restrict__ out, int64_t ldo, const Raw8<TW>& wraw,
+                                             double& sw, double& se) {
   if constexpr (SINK == kStore) {
     if constexpr (sizeof(TOut) == 2) {
-      st16(unit_ptr<CONTIG>(out, ldo, u, upr), mx_unpack8_bf16(word, e8));
+      st16_nt(unit_ptr<CONTIG>(out, ldo, u, upr), mx_unpack8_bf16(word, e8));
     } else {
       float d[8];
       mx_unpack8(word, e8, d);
@@ -81,7 +82,7 @@ __device__ __forceinline__ void dequant_unit(uint32_t word, uint32_t e8, uint32_
   } else {
     float d[8], x[8];
     mx_unpack8(word, e8, d);
-    to_f32(load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr)), x);
+    to_f32(wraw, x);
     acc_err8(x, d, sw, se);
   }
 }
@@ -96,18 +97,22 @@ __global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint32_t* __re
   const uint32_t stride = gridDim.x * blockDim.x;
   double sw = 0.0, se = 0.0;
   uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
+  Raw8<TW> x[4] = {};
   for (; u + 3 * stride < units; u += 4 * stride) {
     uint32_t w[4], e[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       w[i] = ld4_nt(packed + u + i * stride);
       e[i] = e8m0[(u + i * stride) >> 2];
+      if constexpr (SINK == kErr) x[i] = load_raw8(unit_ptr<CONTIG>(W, ldw, u + i * stride, upr));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dequant_unit<SINK, CONTIG>(w[i], e[i], u + i * stride, upr, out, ldo, W, ldw, sw, se);
+    for (int i = 0; i < 4; ++i) dequant_unit<SINK, CONTIG>(w[i], e[i], u + i * stride, upr, out, ldo, x[i], sw, se);
   }
-  for (; u < units; u += stride)
-    dequant_unit<SINK, CONTIG>(ld4_nt(packed + u), (uint32_t)e8m0[u >> 2], u, upr, out, ldo, W, ldw, sw, se);
+  for (; u < units; u += stride) {
+    if constexpr (SINK == kErr) x[0] = load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr));
+    dequant_unit<SINK, CONTIG>(ld4_nt(packed + u), (uint32_t)e8m0[u >> 2], u, upr, out, ldo, x[0], sw, se);
+  }
   if constexpr (SINK == kErr) block_sum2_store<256>(sw, se, part);
 }
 

@@ -201,7 +201,13 @@ __global__ __launch_bounds__(256) void uintx_dequant_tiled(const uint8_t* __rest
   const uint32_t p = blockIdx.x * kBlockPos + (threadIdx.x >> 6) * kWavePos + lane * kLanePos;
   const bool active = p < L1;
   uint2 s4[4], s2[2], s1;
+  U4 wr[8];                                  // the error sink's weights
   if (active) {
+    // The group's scale and zero point go first: the LDS exchange waits only for them,
+    // while the shard bytes and the weights stay in flight across the barrier.
+    const int i = lane & 7;
+    const uint32_t g = (i * L1 + (p - i * kLanePos)) / 64;
+    const uint32_t sc = scales[g], zz = zeros[g];
     if constexpr (SB::has4) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) s4[m] = ld8(packed + sh.base4 + (int64_t)m * L1 + p);
@@ -211,9 +217,11 @@ __global__ __launch_bounds__(256) void uintx_dequant_tiled(const uint8_t* __rest
       for (int m = 0; m < 2; ++m) s2[m] = ld8(packed + sh.base2 + (int64_t)m * L1 + p);
     }
     if constexpr (SB::has1) s1 = ld8(packed + sh.base1 + p);
-    const int i = lane & 7;
-    const uint32_t g = (i * L1 + (p - i * kLanePos)) / 64;
-    qp_lds[threadIdx.x] = ((uint32_t)scales[g] << 16) | (uint32_t)zeros[g];
+    if constexpr (SINK == kErr) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wr[j] = ld16_nt(elem_ptr<CONTIG>(W, ldw, j * L1 + p, kdiv));
+    }
+    qp_lds[threadIdx.x] = (sc << 16) | zz;
   }
   __syncthreads();
   double sw = 0.0, se = 0.0;
@@ -240,7 +248,7 @@ __global__ __launch_bounds__(256) void uintx_dequant_tiled(const uint8_t* __rest
         v.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(ux_f32x2_t{d[2], d[3]}, ux_bf16x2_t));
         v.z = __builtin_bit_cast(uint32_t, __builtin_convertvector(ux_f32x2_t{d[4], d[5]}, ux_bf16x2_t));
         v.w = __builtin_bit_cast(uint32_t, __builtin_convertvector(ux_f32x2_t{d[6], d[7]}, ux_bf16x2_t));
-        st16(elem_ptr<CONTIG>(out, ldo, e, kdiv), v);
+        st16_nt(elem_ptr<CONTIG>(out, ldo, e, kdiv), v);
         continue;
       }
 #pragma unroll
@@ -249,7 +257,7 @@ __global__ __launch_bounds__(256) void uintx_dequant_tiled(const uint8_t* __rest
         store8(elem_ptr<CONTIG>(out, ldo, e, kdiv), d);
       } else {
         float x[8];
-        to_f32(load_raw8(elem_ptr<CONTIG>(W, ldw, e, kdiv)), x);
+        to_f32(Raw8<uint16_t>{wr[j]}, x);
         acc_err8(x, d, sw, se);
       }
     }
