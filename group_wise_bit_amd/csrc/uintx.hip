@@ -125,16 +125,28 @@ __global__ __launch_bounds__(256) void uintx_quant_tiled(const uint16_t* __restr
   if (active) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) raw[j] = ld16_nt(elem_ptr<CONTIG>(W, ldw, j * L1 + p, kdiv));
+    // Extremes on order-preserving keys: a word of two bf16 read as a float32 orders
+    // like its upper weight (the lower one only extends the mantissa), the word rotated
+    // by 16 bits like its lower weight; clearing the low 16 bits of the extreme key
+    // gives that weight exactly.
     float mn[8], mx[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const U4 v = raw[j];
-      const float a0 = bf16_lo(v.x), a1 = bf16_hi(v.x), a2 = bf16_lo(v.y), a3 = bf16_hi(v.y);
-      const float a4 = bf16_lo(v.z), a5 = bf16_hi(v.z), a6 = bf16_lo(v.w), a7 = bf16_hi(v.w);
-      mn[j] = fminf(fminf(fminf(a0, a1), fminf(a2, a3)), fminf(fminf(a4, a5), fminf(a6, a7)));
-      mx[j] = fmaxf(fmaxf(fmaxf(a0, a1), fmaxf(a2, a3)), fmaxf(fmaxf(a4, a5), fmaxf(a6, a7)));
-      mn[j] = lanes_min<8>(mn[j]);
-      mx[j] = lanes_max<8>(mx[j]);
+      const uint32_t w4[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+      float k[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        k[q] = __uint_as_float(w4[q]);
+        k[q + 4] = __uint_as_float((w4[q] >> 16) | (w4[q] << 16));
+      }
+      float a = k[0], b = k[0];
+#pragma unroll
+      for (int q = 1; q < 8; ++q) {
+        a = fminf(a, k[q]);
+        b = fmaxf(b, k[q]);
+      }
+      mn[j] = lanes_min<8>(a);
+      mx[j] = lanes_max<8>(b);
     }
     const int i = lane & 7;                  // this lane's segment for the qparams
     float mni = mn[0], mxi = mx[0];
@@ -143,7 +155,8 @@ __global__ __launch_bounds__(256) void uintx_quant_tiled(const uint16_t* __restr
       mni = i == j ? mn[j] : mni;
       mxi = i == j ? mx[j] : mxi;
     }
-    const QP q = uintx_qparams(mni, mxi, qmax);
+    const QP q = uintx_qparams(__uint_as_float(__float_as_uint(mni) & 0xFFFF0000u),
+                               __uint_as_float(__float_as_uint(mxi) & 0xFFFF0000u), qmax);
     const uint32_t g = (i * L1 + (p - i * kLanePos)) / 64;
     scales[g] = (uint16_t)(__float_as_uint(q.s) >> 16);
     zeros[g] = (uint8_t)q.zp;
