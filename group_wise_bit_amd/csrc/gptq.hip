@@ -254,8 +254,8 @@ __global__ __launch_bounds__(256) void gptq_dequant_kernel(const uint32_t* __res
     U4 qa{}, qb{};
     if (qok) {
       const uint32_t* src = qweight + (int64_t)(k0 / 8 + r) * N + n0 + c8;
-      qa = ld16_nt(src);
-      qb = ld16_nt(src + 4);
+      qa = ld16(src);
+      qb = ld16(src + 4);
     }
     constexpr int kSPer = (T::NG * kTN + 255) / 256;   // scales per thread
     uint16_t sv[kSPer];

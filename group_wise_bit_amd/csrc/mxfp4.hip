@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint32_t* __re
     uint32_t w[4], e[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      w[i] = ld4_nt(packed + u + i * stride);
+      w[i] = packed[u + i * stride];
       e[i] = e8m0[(u + i * stride) >> 2];
       if constexpr (SINK == kErr) x[i] = load_raw8(unit_ptr<CONTIG>(W, ldw, u + i * stride, upr));
     }
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint32_t* __re
   }
   for (; u < units; u += stride) {
     if constexpr (SINK == kErr) x[0] = load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr));
-    dequant_unit<SINK, CONTIG>(ld4_nt(packed + u), (uint32_t)e8m0[u >> 2], u, upr, out, ldo, x[0], sw, se);
+    dequant_unit<SINK, CONTIG>(packed[u], (uint32_t)e8m0[u >> 2], u, upr, out, ldo, x[0], sw, se);
   }
   if constexpr (SINK == kErr) block_sum2_store<256>(sw, se, part);
 }
