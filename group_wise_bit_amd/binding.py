@@ -54,6 +54,7 @@ _SIGS = {
     "gwb_awq_workspace": [_I64, _I64, _I32, _I64, ctypes.POINTER(_SZ)],
     "gwb_awq_search_mxfp4": [_P, _I32, _I64, _I64, _I64, _P, _P, _I32, _I64, _P, _P, _P, _P, _SZ, _P],
     "gwb_stream_copy": [_P, _P, _SZ, _P],
+    "gwb_awq_scales_host": [_P, _I64, _P, _I32, _P],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(lib, _name)
@@ -200,13 +201,24 @@ def snr(W: torch.Tensor, q: Quantized, workspace: Optional[torch.Tensor] = None,
     return out
 
 
+DEFAULT_ALPHAS = tuple(i / 10 for i in range(11))
+
+
+def awq_scales_host(a: torch.Tensor, alphas: Sequence[float] = DEFAULT_ALPHAS) -> torch.Tensor:
+    """The AWQ scaling table [n_alpha, K] float32, computed on the host."""
+    a = a.detach().to("cpu", torch.float32).contiguous()
+    al = (ctypes.c_double * len(alphas))(*[float(x) for x in alphas])
+    out = torch.empty(len(alphas), a.numel(), dtype=torch.float32)
+    _check(lib.gwb_awq_scales_host(a.data_ptr(), a.numel(), ctypes.cast(al, _P), len(alphas), out.data_ptr()))
+    return out
+
+
 def awq_workspace_bytes(N: int, K: int, n_alpha: int, max_rows: int = 2048) -> int:
     b = ctypes.c_size_t()
     _check(lib.gwb_awq_workspace(N, K, n_alpha, max_rows, ctypes.byref(b)))
     return b.value
 
 
-DEFAULT_ALPHAS = tuple(i / 10 for i in range(11))
 
 
 def awq_search(W: torch.Tensor, a: torch.Tensor, alphas: Optional[Sequence[float]] = DEFAULT_ALPHAS,

@@ -6,6 +6,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
+#include <cmath>
 
 #include "gwb.h"
 #include "kernels.hpp"
@@ -279,6 +281,37 @@ int gwb_awq_search_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, i
   gwb::launch_awq(W, w_dtype, rows, step, K, ldw, d_a, alphas, n_alpha, d_s_table, d_err, d_best,
                   workspace, (hipStream_t)stream);
   return hip_check("awq launch");
+}
+
+// Host computation of the AWQ scaling table, the same steps and precision as the device
+// table kernels: a' = max(a, 1e-8) in float32, then float64 for an = a' / mean(a'),
+// p = clamp(an**alpha, 1e-2, 1e2) (exact 1, an and sqrt(an) for alpha 0, 1 and 0.5) and
+// s = p / exp(mean(log p)), rounded once to float32.
+int gwb_awq_scales_host(const float* a, int64_t K, const double* alphas, int32_t n_alpha, float* s_out) {
+  if (!a || !alphas || !s_out) return fail(GWB_E_ARG, "a, alphas and s_out are required");
+  if (K <= 0) return fail(GWB_E_ARG, "K must be positive, got %lld", (long long)K);
+  if (n_alpha < 1 || n_alpha > 16) return fail(GWB_E_ARG, "n_alpha must be 1..16, got %d", n_alpha);
+  std::vector<double> ap((size_t)K), p((size_t)K);
+  double sum = 0.0;
+  for (int64_t k = 0; k < K; ++k) {
+    ap[k] = (double)std::fmax(a[k], 1e-8f);
+    sum += ap[k];
+  }
+  const double mean = sum / (double)K;
+  for (int32_t i = 0; i < n_alpha; ++i) {
+    const double alpha = alphas[i];
+    double lg = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      const double an = ap[k] / mean;
+      double v = alpha == 0.0 ? 1.0 : (alpha == 1.0 ? an : (alpha == 0.5 ? std::sqrt(an) : std::pow(an, alpha)));
+      v = std::fmin(std::fmax(v, 1e-2), 1e2);
+      p[k] = v;
+      lg += std::log(v);
+    }
+    const double g = std::exp(lg / (double)K);
+    for (int64_t k = 0; k < K; ++k) s_out[(int64_t)i * K + k] = (float)(p[k] / g);
+  }
+  return ok();
 }
 
 int gwb_stream_copy(void* d_dst, const void* d_src, size_t bytes, void* stream) {

@@ -157,6 +157,13 @@ int gwb_awq_search_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, i
                          int64_t max_rows, float* d_s_table, double* d_err, int32_t* d_best,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* The AWQ scaling table on the host (page quantize_dflash_mxfp4.py, search_scale: the
+ * per-alpha s of the search). a: HOST float32 [K] per-channel mean |x|; alphas: HOST
+ * array of n_alpha doubles (1..16); s_out: HOST float32 [n_alpha, K]. Steps as in
+ * gwb_awq_search_mxfp4 (float64, one rounding to float32); the device table agrees to
+ * within one float32 ulp (float64 summation order). Touches no device memory.      */
+int gwb_awq_scales_host(const float* a, int64_t K, const double* alphas, int32_t n_alpha, float* s_out);
+
 /* Measurement helper, not part of the method: copy `bytes` (a multiple of 16, both
  * pointers 16-byte aligned) from d_src to d_dst with the same 128-bit load/store
  * idiom the quantization kernels use; a same-run bandwidth ceiling. */

@@ -141,3 +141,36 @@ def test_error_message_is_thread_local_and_cleared():
     assert "uint8" in lib.gwb_last_error().decode()
     rc, _ = _sizes("mxfp4", 8, 64)
     assert rc == 0 and lib.gwb_last_error().decode() == ""
+
+
+def test_awq_scales_host_matches_oracle_table():
+    """Host scaling table (no device memory touched) against the oracle's: float64
+    steps rounded once to float32, so at most one float32 ulp apart (summation order)."""
+    import numpy as np
+    import torch
+    import oracle.awq as oawq
+    from group_wise_bit_amd import workloads
+    for K, seed in ((5120, 5), (96, 71), (1, 72)):
+        a = workloads.awq_activation_stat(K, seed=seed)
+        got = gwb.awq_scales_host(a).numpy()
+        want = oawq.scale_table(a.numpy())
+        ulps = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+        assert ulps.max() <= 1, (K, ulps.max())
+        assert np.all(got[0] == 1.0)                       # alpha = 0: s is exactly 1
+    flat = gwb.awq_scales_host(torch.full((64,), 0.3))    # constant a: every alpha gives s = 1
+    assert torch.all(flat == 1.0)
+
+
+def test_awq_scales_host_rejects():
+    out = (ctypes.c_float * 64)()
+    a = (ctypes.c_float * 8)(*([1.0] * 8))
+    al = (ctypes.c_double * 17)(*([0.5] * 17))
+    f = lib.gwb_awq_scales_host
+    assert f(None, 8, ctypes.cast(al, ctypes.c_void_p), 1, ctypes.cast(out, ctypes.c_void_p)) == gwb.E_ARG
+    assert f(ctypes.cast(a, ctypes.c_void_p), 0, ctypes.cast(al, ctypes.c_void_p), 1,
+             ctypes.cast(out, ctypes.c_void_p)) == gwb.E_ARG
+    assert f(ctypes.cast(a, ctypes.c_void_p), 8, ctypes.cast(al, ctypes.c_void_p), 17,
+             ctypes.cast(out, ctypes.c_void_p)) == gwb.E_ARG
+    assert f(ctypes.cast(a, ctypes.c_void_p), 8, ctypes.cast(al, ctypes.c_void_p), 0,
+             ctypes.cast(out, ctypes.c_void_p)) == gwb.E_ARG
+    assert b"n_alpha" in lib.gwb_last_error()

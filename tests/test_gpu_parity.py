@@ -207,6 +207,7 @@ def test_awq_parity_small():
     o = oawq.search(W.float().numpy(), a.numpy(), max_rows=64)
     st = _np(r["s_table"])
     assert _ulps(st, o["s_table"]).max() <= 1
+    assert _ulps(st, gwb.awq_scales_host(a).numpy()).max() <= 1    # device and host tables
     assert np.all(st[0] == 1.0)
     err = _np(r["err"])
     assert np.allclose(err, o["errors"], rtol=1e-6, atol=0)
