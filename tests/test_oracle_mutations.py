@@ -99,3 +99,23 @@ def test_snr_wrong_sign_caught(monkeypatch):
         return float(np.sum(w.astype(np.float64) ** 2)), float(np.sum(e * e))
     monkeypatch.setattr(snr, "sums", plus)
     _fails(ts.test_snr_closed_form_relative_perturbation)
+
+
+def test_fold_dropped_rounding_caught(monkeypatch):
+    import oracle.fold as fd
+    import test_oracle_fold as tf
+    monkeypatch.setattr(fd, "_apply", lambda x, v, op: x if op == "none" or v is None else (x * v if op == "mul" else x / v))
+    _fails(tf.test_each_step_is_one_rounding_of_the_exact_result)
+
+
+def test_fold_transposed_row_vector_caught(monkeypatch):
+    import oracle.fold as fd
+    import test_oracle_fold as tf
+    orig = fd.fold
+    def swapped(w, col=None, col_op="none", row=None, row_op="none"):
+        x = orig(w, col, col_op)
+        if row_op == "none":
+            return x
+        return fd._apply(x, np.resize(np.asarray(row, np.float32), x.shape[1])[None, :], row_op)
+    monkeypatch.setattr(fd, "fold", swapped)
+    _fails(tf.test_orientation_and_order)
