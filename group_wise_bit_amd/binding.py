@@ -40,6 +40,14 @@ class QTensors(ctypes.Structure):
                 ("zeros", ctypes.c_void_p), ("g_idx", ctypes.c_void_p)]
 
 
+class Fold(ctypes.Structure):
+    _fields_ = [("col", ctypes.c_void_p), ("row", ctypes.c_void_p), ("col_op", ctypes.c_int32),
+                ("row_op", ctypes.c_int32)]
+
+
+FOLD_OPS = {"none": 0, "mul": 1, "div": 2}
+
+
 class Sizes(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_size_t), ("scales", ctypes.c_size_t), ("zeros", ctypes.c_size_t),
                 ("g_idx", ctypes.c_size_t), ("workspace", ctypes.c_size_t)]
@@ -55,6 +63,7 @@ _SIGS = {
     "gwb_awq_search_mxfp4": [_P, _I32, _I64, _I64, _I64, _P, _P, _I32, _I64, _P, _P, _P, _P, _SZ, _P],
     "gwb_stream_copy": [_P, _P, _SZ, _P],
     "gwb_awq_scales_host": [_P, _I64, _P, _I32, _P],
+    "gwb_fold_mxfp4": [_P, _I32, _I64, _I64, _I64, ctypes.POINTER(Fold), _P, _I64, ctypes.POINTER(QTensors), _P],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(lib, _name)
@@ -248,6 +257,46 @@ def awq_search(W: torch.Tensor, a: torch.Tensor, alphas: Optional[Sequence[float
                                     host_alphas, n_alpha, max_rows, _ptr(s_table), _ptr(err), _ptr(best),
                                     _ptr(workspace), workspace.numel(), _stream()))
     return {"err": err, "best": best, "s_table": s_table}
+
+
+def _fold_args(W, col, col_op, row, row_op, folded, mx):
+    N, K, ldw = _weight_args(W)
+    if W.dtype != torch.bfloat16:
+        raise ValueError("the fold takes bf16 weights")
+    for v, n, what in ((col, K, "col"), (row, N, "row")):
+        if v is not None and (v.dtype != torch.float32 or v.numel() != n or not v.is_cuda or not v.is_contiguous()):
+            raise ValueError(f"{what} must be a contiguous float32 CUDA tensor of {n} elements")
+    f = Fold(_ptr(col), _ptr(row), FOLD_OPS[col_op], FOLD_OPS[row_op])
+    qt = None if mx is None else QTensors(_ptr(mx.codes), _ptr(mx.scales), None, None)
+    ldo = 0 if folded is None else folded.stride(0)
+    return (_ptr(W), BF16, N, K, ldw, ctypes.byref(f), _ptr(folded), ldo,
+            None if qt is None else ctypes.byref(qt), _stream()), (f, qt)
+
+
+def fold_mxfp4(W: torch.Tensor, col: Optional[torch.Tensor] = None, col_op: str = "none",
+               row: Optional[torch.Tensor] = None, row_op: str = "none", want_folded: bool = True,
+               want_mxfp4: bool = True, folded: Optional[torch.Tensor] = None,
+               mx: Optional[Quantized] = None) -> Dict[str, object]:
+    """Fold per-column / per-row AWQ scales into a bf16 W [N, K] (column step, then row
+    step, each rounded to bf16) and/or quantize the folded weight to MXFP4, in one pass.
+    Returns {"folded": bf16 [N, K] or None, "mxfp4": Quantized or None}."""
+    N, K, _ = _weight_args(W)
+    if want_folded and folded is None:
+        folded = torch.empty(N, K, dtype=torch.bfloat16, device=W.device)
+    if want_mxfp4 and mx is None:
+        sz = query_sizes("mxfp4", N, K, 4, 32, W.dtype)
+        mx = Quantized("mxfp4", 4, 32, W.dtype, N, K, _alloc(sz["codes"], W.device), _alloc(sz["scales"], W.device),
+                       None, None, sz)
+    args, keep = _fold_args(W, col, col_op, row, row_op, folded if want_folded else None,
+                            mx if want_mxfp4 else None)
+    _check(lib.gwb_fold_mxfp4(*args))
+    return {"folded": folded if want_folded else None, "mxfp4": mx if want_mxfp4 else None}
+
+
+def prepare_fold_mxfp4(W: torch.Tensor, col, col_op: str, row, row_op: str, folded: Optional[torch.Tensor],
+                       mx: Optional[Quantized]) -> Prepared:
+    args, keep = _fold_args(W, col, col_op, row, row_op, folded, mx)
+    return Prepared(lib.gwb_fold_mxfp4, args, (keep, W, col, row, folded, mx))
 
 
 def stream_copy(dst: torch.Tensor, src: torch.Tensor) -> None:

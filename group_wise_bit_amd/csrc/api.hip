@@ -283,6 +283,35 @@ int gwb_awq_search_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, i
   return hip_check("awq launch");
 }
 
+int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw, const gwb_fold* fold,
+                   void* out_bf16, int64_t ldo, const gwb_qtensors* mx, void* stream) {
+  if (w_dtype != GWB_BF16) return fail(GWB_E_UNSUPPORTED, "the fold takes bf16 weights (the pages' dtype)");
+  if (N < 0 || K < 0) return fail(GWB_E_ARG, "negative shape N=%lld K=%lld", (long long)N, (long long)K);
+  if (N > 0 && K > 0 && (N >= kMaxElems || K >= kMaxElems || N * K >= kMaxElems))
+    return fail(GWB_E_UNSUPPORTED, "N*K = %lld exceeds 2^31 elements", (long long)(N * K));
+  const gwb_fold none{nullptr, nullptr, GWB_FOLD_NONE, GWB_FOLD_NONE};
+  const gwb_fold* f = fold ? fold : &none;
+  for (int32_t op : {f->col_op, f->row_op})
+    if (op != GWB_FOLD_NONE && op != GWB_FOLD_MUL && op != GWB_FOLD_DIV) return fail(GWB_E_ARG, "unknown fold op %d", op);
+  const bool want_mx = mx && mx->codes;
+  if (!out_bf16 && !want_mx) return fail(GWB_E_ARG, "nothing to write: out_bf16 and mx are both NULL");
+  if (K % (want_mx ? 32 : 8)) return fail(GWB_E_SHAPE, "K=%lld must be a multiple of %d", (long long)K, want_mx ? 32 : 8);
+  if (N == 0 || K == 0) return ok();
+  if (!W) return fail(GWB_E_ARG, "W is NULL");
+  if (ldw < K) return fail(GWB_E_ARG, "ldw=%lld < K=%lld", (long long)ldw, (long long)K);
+  if (!aligned16(W) || ldw % 8) return fail(GWB_E_UNSUPPORTED, "W and its row stride must be 16-byte aligned");
+  if (f->col_op != GWB_FOLD_NONE && (!f->col || !aligned16(f->col)))
+    return fail(GWB_E_ARG, "the column step needs a 16-byte aligned col vector");
+  if (f->row_op != GWB_FOLD_NONE && !f->row) return fail(GWB_E_ARG, "the row step needs a row vector");
+  if (out_bf16 && (ldo < K || !aligned16(out_bf16) || ldo % 8))
+    return fail(GWB_E_UNSUPPORTED, "out_bf16 needs ldo >= K and a 16-byte aligned start and row stride");
+  if (want_mx && (!mx->scales || !aligned16(mx->codes)))
+    return fail(GWB_E_ARG, "MXFP4 output needs 16-byte aligned codes and an e8m0 buffer");
+  gwb::launch_fold(f->col_op, f->row_op, W, N, K, ldw, f->col, f->row, out_bf16, ldo, want_mx ? mx->codes : nullptr,
+                   want_mx ? mx->scales : nullptr, (hipStream_t)stream);
+  return hip_check("fold launch");
+}
+
 // Host computation of the AWQ scaling table, the same steps and precision as the device
 // table kernels: a' = max(a, 1e-8) in float32, then float64 for an = a' / mean(a'),
 // p = clamp(an**alpha, 1e-2, 1e2) (exact 1, an and sqrt(an) for alpha 0, 1 and 0.5) and

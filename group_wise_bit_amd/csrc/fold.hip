@@ -1,0 +1,122 @@
+// Folding AWQ scales into weights, then requantizing to MXFP4, in one pass.
+// Page quantize_dflash_mxfp4.py, main and its module docstring: after the alpha search
+// the page divides the norm weights by s, multiplies the columns of the projections
+// that read the normed input (and the conv's kernel projection) by s, divides up's
+// rows by down's s, rounding each result to bfloat16, and then quantizes the folded
+// weights with quantize_mxfp4.
+//
+// A fold here is an optional column step (multiply or divide by col[k]) followed by an
+// optional row step (by row[n]), each one float32 operation rounded to bfloat16 (the
+// hardware pair conversion, RNE); divisions are IEEE. The folded words can be stored
+// (bf16, non-temporal) and/or quantized to MXFP4 exactly as mxfp4.hip does, so a
+// folded linear that is served quantized never exists in HBM as bf16.
+#include "kernels.hpp"
+#include "mxfp4_math.hpp"
+
+namespace gwb {
+
+typedef __bf16 fd_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float fd_f32x2_t __attribute__((ext_vector_type(2)));
+
+template <int OP>
+__device__ __forceinline__ float fold_op(float x, float v) {
+  if constexpr (OP == kFoldMul) return x * v;
+  else return x / v;
+}
+__device__ __forceinline__ uint32_t bf16_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(fd_f32x2_t{a, b}, fd_bf16x2_t));
+}
+
+// One unit: 8 consecutive bf16 weights of row n from k0. Returns the folded bf16 words.
+template <int COP, int ROP>
+__device__ __forceinline__ U4 fold_unit(U4 w, const float* __restrict__ col, const float* __restrict__ row,
+                                        uint32_t n, uint32_t k0) {
+  if constexpr (COP != kFoldNone) {
+    float x[8], c[8];
+    to_f32(Raw8<uint16_t>{w}, x);
+    load8(col + k0, c);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = fold_op<COP>(x[j], c[j]);
+    w = U4{bf16_pair(x[0], x[1]), bf16_pair(x[2], x[3]), bf16_pair(x[4], x[5]), bf16_pair(x[6], x[7])};
+  }
+  if constexpr (ROP != kFoldNone) {
+    const float r = row[n];
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = bf16_pair(fold_op<ROP>(__uint_as_float(ws[q] << 16), r),
+                       fold_op<ROP>(__uint_as_float(ws[q] & 0xFFFF0000u), r));
+    w = U4{o[0], o[1], o[2], o[3]};
+  }
+  return w;
+}
+
+template <int COP, int ROP>
+__device__ __forceinline__ void fold_store(U4 raw, uint32_t u, FastDiv upr,
+                                           const float* __restrict__ col, const float* __restrict__ row,
+                                           uint16_t* __restrict__ out, int64_t ldo,
+                                           uint32_t* __restrict__ packed, uint8_t* __restrict__ e8m0) {
+  const uint32_t n = fdiv(u, upr), k0 = 8 * (u - n * upr.d);
+  const U4 w = fold_unit<COP, ROP>(raw, col, row, n, k0);
+  if (out) st16_nt(out + (int64_t)n * ldo + k0, w);
+  if (packed) {       // uniform per launch; the DPP step below has all four lanes
+    const uint32_t e8 = mx_e8m0_bits(quad_max_u(absmax8_bits(w)));
+    packed[u] = mx_pack8(w, mx_scale_operand(e8));
+    if ((u & 3u) == 0) e8m0[u >> 2] = (uint8_t)e8;
+  }
+}
+
+// Grid-stride over units of 8 weights, four loads in flight per lane. units = N*K/8 is
+// a multiple of 4 and so is every stride, so the four lanes of a 32-block stay together.
+template <int COP, int ROP>
+__global__ __launch_bounds__(256) void fold_kernel(const uint16_t* __restrict__ W, int64_t ldw, uint32_t units,
+                                                   FastDiv upr, const float* __restrict__ col,
+                                                   const float* __restrict__ row, uint16_t* __restrict__ out,
+                                                   int64_t ldo, uint32_t* __restrict__ packed,
+                                                   uint8_t* __restrict__ e8m0) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
+  auto at = [&](uint32_t v) {
+    const uint32_t n = fdiv(v, upr);
+    return W + (int64_t)n * ldw + 8 * (v - n * upr.d);
+  };
+  for (; u + 3 * stride < units; u += 4 * stride) {
+    const U4 r0 = ld16_nt(at(u)), r1 = ld16_nt(at(u + stride));
+    const U4 r2 = ld16_nt(at(u + 2 * stride)), r3 = ld16_nt(at(u + 3 * stride));
+    fold_store<COP, ROP>(r0, u, upr, col, row, out, ldo, packed, e8m0);
+    fold_store<COP, ROP>(r1, u + stride, upr, col, row, out, ldo, packed, e8m0);
+    fold_store<COP, ROP>(r2, u + 2 * stride, upr, col, row, out, ldo, packed, e8m0);
+    fold_store<COP, ROP>(r3, u + 3 * stride, upr, col, row, out, ldo, packed, e8m0);
+  }
+  for (; u < units; u += stride) fold_store<COP, ROP>(ld16_nt(at(u)), u, upr, col, row, out, ldo, packed, e8m0);
+}
+
+// ------------------------------------------------------------------ launchers
+template <int COP, int ROP>
+static void fold_launch_t(const void* W, int64_t N, int64_t K, int64_t ldw, const float* col, const float* row,
+                          void* out, int64_t ldo, void* packed, void* e8m0, hipStream_t st) {
+  const uint32_t units = (uint32_t)(N * K / 8);
+  const FastDiv upr = make_fastdiv((uint32_t)(K / 8));
+  hipLaunchKernelGGL((fold_kernel<COP, ROP>), dim3(stream_blocks(units)), dim3(256), 0, st, (const uint16_t*)W, ldw,
+                     units, upr, col, row, (uint16_t*)out, ldo, (uint32_t*)packed, (uint8_t*)e8m0);
+}
+
+template <int COP>
+static void fold_launch_c(int row_op, const void* W, int64_t N, int64_t K, int64_t ldw,
+                          const float* col, const float* row, void* out, int64_t ldo, void* packed, void* e8m0,
+                          hipStream_t st) {
+  if (row_op == kFoldMul) fold_launch_t<COP, kFoldMul>(W, N, K, ldw, col, row, out, ldo, packed, e8m0, st);
+  else if (row_op == kFoldDiv) fold_launch_t<COP, kFoldDiv>(W, N, K, ldw, col, row, out, ldo, packed, e8m0, st);
+  else fold_launch_t<COP, kFoldNone>(W, N, K, ldw, col, row, out, ldo, packed, e8m0, st);
+}
+
+void launch_fold(int col_op, int row_op, const void* W, int64_t N, int64_t K, int64_t ldw,
+                 const float* col, const float* row, void* out, int64_t ldo, void* packed, void* e8m0,
+                 hipStream_t st) {
+  if (col_op == kFoldMul) fold_launch_c<kFoldMul>(row_op, W, N, K, ldw, col, row, out, ldo, packed, e8m0, st);
+  else if (col_op == kFoldDiv) fold_launch_c<kFoldDiv>(row_op, W, N, K, ldw, col, row, out, ldo, packed, e8m0, st);
+  else fold_launch_c<kFoldNone>(row_op, W, N, K, ldw, col, row, out, ldo, packed, e8m0, st);
+}
+
+}  // namespace gwb

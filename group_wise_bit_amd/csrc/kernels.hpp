@@ -73,6 +73,13 @@ void launch_awq(const void* W, int32_t w_dtype, int64_t rows, int64_t row_step, 
                 int64_t ldw, const float* a, const double* alphas, int n_alpha, float* s_table,
                 double* err, int32_t* best, void* workspace, hipStream_t st);
 
+// ---- AWQ fold + MXFP4 requantize (fold.hip): column step, then row step, each
+// rounded to bf16; outputs optional (NULL pointer = not written).
+constexpr int kFoldNone = 0, kFoldMul = 1, kFoldDiv = 2;
+void launch_fold(int col_op, int row_op, const void* W, int64_t N, int64_t K, int64_t ldw,
+                 const float* col, const float* row, void* out, int64_t ldo, void* packed, void* e8m0,
+                 hipStream_t st);
+
 // ---- measurement copy (common.hip)
 void launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 

@@ -157,6 +157,29 @@ int gwb_awq_search_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, i
                          int64_t max_rows, float* d_s_table, double* d_err, int32_t* d_best,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Folding the AWQ scales into a bf16 weight, then requantizing it to MXFP4 (page
+ * quantize_dflash_mxfp4.py, main and its module docstring: norm weights / s, the
+ * columns of the projections that read the normed input * s, up's rows / down's s,
+ * each rounded to bfloat16, then quantize_mxfp4 of every served linear).
+ *   W        bf16 [N, K], row stride ldw (elements, multiple of 8), 16-byte aligned
+ *   fold     column step (col_op with col: device float32 [K], 16-byte aligned) then
+ *            row step (row_op with row: device float32 [N]); each op GWB_FOLD_NONE,
+ *            GWB_FOLD_MUL or GWB_FOLD_DIV (IEEE), each result rounded to bfloat16
+ *            (RNE); fold == NULL: no steps
+ *   out_bf16 device bf16 [N, K] with row stride ldo (multiple of 8), or NULL
+ *   mx       MXFP4 output as in gwb_quantize (codes = packed [N, K/2], scales =
+ *            e8m0 [N, K/32]), or NULL / codes NULL for no quantization
+ * At least one output is required. K % 32 == 0 with MXFP4 output, K % 8 == 0 without.
+ * Only bf16 weights (E_UNSUPPORTED otherwise). Asynchronous on `stream`.            */
+typedef enum { GWB_FOLD_NONE = 0, GWB_FOLD_MUL = 1, GWB_FOLD_DIV = 2 } gwb_fold_op;
+typedef struct {
+  const float* col;
+  const float* row;
+  int32_t col_op, row_op;
+} gwb_fold;
+int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw, const gwb_fold* fold,
+                   void* out_bf16, int64_t ldo, const gwb_qtensors* mx, void* stream);
+
 /* The AWQ scaling table on the host (page quantize_dflash_mxfp4.py, search_scale: the
  * per-alpha s of the search). a: HOST float32 [K] per-channel mean |x|; alphas: HOST
  * array of n_alpha doubles (1..16); s_out: HOST float32 [n_alpha, K]. Steps as in

@@ -174,3 +174,28 @@ def test_awq_scales_host_rejects():
     assert f(ctypes.cast(a, ctypes.c_void_p), 8, ctypes.cast(al, ctypes.c_void_p), 0,
              ctypes.cast(out, ctypes.c_void_p)) == gwb.E_ARG
     assert b"n_alpha" in lib.gwb_last_error()
+
+
+def test_fold_validates_before_launch():
+    """Every invalid call returns its code before anything is enqueued (dummy device
+    addresses are never touched)."""
+    P = ctypes.c_void_p
+    fake = P(1 << 20)                                  # 16-byte aligned, never dereferenced
+    mx = gwb.QTensors(fake.value, fake.value, None, None)
+    f = gwb.Fold(fake.value, fake.value, 1, 2)
+    call = lib.gwb_fold_mxfp4
+    def go(dt=gwb.BF16, N=8, K=64, ldw=64, fold=f, out=fake, ldo=64, q=mx):
+        return call(fake, dt, N, K, ldw, None if fold is None else ctypes.byref(fold), out, ldo,
+                    None if q is None else ctypes.byref(q), None)
+    assert go(dt=gwb.F32) == gwb.E_UNSUPPORTED
+    assert go(out=None, q=None) == gwb.E_ARG
+    assert go(K=40) == gwb.E_SHAPE                      # MXFP4 output needs K % 32 == 0
+    assert go(K=36, ldw=40, q=None, ldo=40) == gwb.E_SHAPE
+    assert go(fold=gwb.Fold(fake.value, fake.value, 3, 0)) == gwb.E_ARG
+    assert go(fold=gwb.Fold(None, fake.value, 1, 0)) == gwb.E_ARG
+    assert go(fold=gwb.Fold(fake.value, None, 0, 2)) == gwb.E_ARG
+    assert go(ldw=60) == gwb.E_ARG
+    assert go(ldw=68) == gwb.E_UNSUPPORTED
+    assert go(ldo=60) == gwb.E_UNSUPPORTED
+    assert go(N=0) == gwb.OK and go(K=0) == gwb.OK      # empty: nothing to do
+    assert go(N=1 << 20, K=1 << 12, ldw=1 << 12, ldo=1 << 12) == gwb.E_UNSUPPORTED

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle.awq as oawq
+import oracle.fold as ofold
 import oracle.gptq as ogq
 import oracle.mxfp4 as omx
 import oracle.snr as osnr
@@ -257,6 +258,52 @@ def test_awq_exact_division_blocks_and_scalings():
     assert int(_np(r["best"])[0]) == int(np.argmin(ref))
 
 
+# --------------------------------------------------------------- fold + requantize
+def _fold_vec(n, seed):
+    return np.exp(np.random.default_rng(seed).uniform(-2, 2, n)).astype(np.float32)
+
+
+@pytest.mark.parametrize("n,k,col_op,row_op,kind", [
+    (1, 5120, "div", "none", "normal"),        # a norm vector / s
+    (64, 512, "mul", "none", "normal"),        # q/k/v, gate/up, down columns * s
+    (72, 1024, "mul", "div", "normal"),        # up: columns * s, then rows / down's s
+    (40, 256, "div", "mul", "adv"),
+    (33, 96, "none", "div", "normal"),
+    (16, 128, "none", "none", "adv")])
+def test_fold_parity(n, k, col_op, row_op, kind):
+    W = _weight(kind, n, k, seed=400 + n, dtype=torch.bfloat16)
+    col, row = _fold_vec(k, 401 + n), _fold_vec(n, 402 + n)
+    r = gwb.fold_mxfp4(W.to(DEV), torch.from_numpy(col).to(DEV), col_op, torch.from_numpy(row).to(DEV), row_op)
+    x, packed, e8 = ofold.fold_quantize(W.float().numpy(), col, col_op, row, row_op)
+    assert np.array_equal(_gpu_bf16bits(r["folded"]), _ref_bf16bits(x))
+    assert np.array_equal(_np(r["mxfp4"]["packed"]), packed)
+    assert np.array_equal(_np(r["mxfp4"]["e8m0"]), e8)
+    # the folded, quantized weight dequantizes like any MXFP4 tensor
+    _check_dequant(r["mxfp4"], omx.dequantize(packed, e8, k))
+
+
+def test_fold_outputs_strides_and_ragged_k():
+    W = workloads.mxfp4_weight(24, 320, seed=403)
+    big = torch.zeros(24, 384, dtype=torch.bfloat16)
+    big[:, :320] = W
+    view = big.to(DEV)[:, :320]
+    col, row = _fold_vec(320, 404), _fold_vec(24, 405)
+    cd, rd = torch.from_numpy(col).to(DEV), torch.from_numpy(row).to(DEV)
+    x, packed, e8 = ofold.fold_quantize(W.float().numpy(), col, "mul", row, "div")
+    only_mx = gwb.fold_mxfp4(view, cd, "mul", rd, "div", want_folded=False)
+    assert only_mx["folded"] is None
+    assert np.array_equal(_np(only_mx["mxfp4"]["packed"]), packed)
+    out = torch.full((24, 336), 9.0, dtype=torch.bfloat16, device=DEV)
+    gwb.fold_mxfp4(view, cd, "mul", rd, "div", want_mxfp4=False, folded=out[:, :320])
+    assert np.array_equal(_gpu_bf16bits(out[:, :320]), _ref_bf16bits(x))
+    assert torch.all(out[:, 320:] == 9.0)
+    # K = 40: the bf16 fold alone needs only K % 8 == 0
+    W40 = workloads.mxfp4_weight(5, 40, seed=406)
+    c40 = _fold_vec(40, 407)
+    r40 = gwb.fold_mxfp4(W40.to(DEV), torch.from_numpy(c40).to(DEV), "div", want_mxfp4=False)
+    assert np.array_equal(_gpu_bf16bits(r40["folded"]), _ref_bf16bits(ofold.fold(W40.float().numpy(), c40, "div")))
+
+
 # ------------------------------------------------------------- full config sizes
 def _rows(n, count, seed):
     return np.sort(np.random.default_rng(seed).choice(n, count, replace=False))
@@ -369,6 +416,20 @@ def test_full_awq_2048_of_34816x5120():
     assert np.allclose(_np(rs["err"]), o["errors"], rtol=1e-6, atol=0)
     # the full search's scalings are the sampled search's (same a)
     assert np.array_equal(_np(r["s_table"]), _np(rs["s_table"]))
+
+
+def test_full_fold_34816x5120_sampled():
+    """The gate_up fold at its real shape: columns * s, straight to MXFP4, checked on
+    sampled rows."""
+    W = workloads.mxfp4_weight()
+    a = workloads.awq_activation_stat()
+    s = oawq.scale_table(a.numpy(), (0.5,))[0]
+    r = gwb.fold_mxfp4(W.to(DEV), torch.from_numpy(s).to(DEV), "mul")
+    rows = _rows(34816, 48, 408)
+    x, packed, e8 = ofold.fold_quantize(W[rows].float().numpy(), s, "mul")
+    assert np.array_equal(_gpu_bf16bits(r["folded"][rows]), _ref_bf16bits(x))
+    assert np.array_equal(_np(r["mxfp4"]["packed"][rows]), packed)
+    assert np.array_equal(_np(r["mxfp4"]["e8m0"][rows]), e8)
 
 
 # ------------------------------------------------------------------ empty shapes
