@@ -136,6 +136,42 @@ def cpu_baseline(W_cpu: torch.Tensor, a_cpu: torch.Tensor, rows: int, awq_rows: 
     }
 
 
+def _time_op(fn, reps: int = 20, warm: int = 3) -> float:
+    """Average microseconds of back-to-back launches of one prepared call."""
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def measure_extras(gwb, workloads, Wd, ad, dev):
+    """Paths next to the hot path, timed on their own after the step (not part of
+    value): the AWQ fold of the gate_up weight (columns * s) straight to MXFP4, and the
+    same fold also writing the folded bf16 weight."""
+    out = []
+    s = torch.from_numpy(gwb.awq_scales_host(ad.cpu(), (0.5,))[0].numpy()).to(dev)
+    mx = gwb.fold_mxfp4(Wd, s, "mul", want_folded=False)["mxfp4"]
+    folded = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+    nk = N * K
+    cases = [
+        ("fold_mxfp4.columns_to_mxfp4", 2 * nk + nk / 2 + nk / 32 + 4 * K,
+         gwb.prepare_fold_mxfp4(Wd, s, "mul", None, "none", None, mx)),
+        ("fold_mxfp4.columns_to_bf16_and_mxfp4", 4 * nk + nk / 2 + nk / 32 + 4 * K,
+         gwb.prepare_fold_mxfp4(Wd, s, "mul", None, "none", folded, mx)),
+    ]
+    for name, abytes, fn in cases:
+        us = _time_op(fn)
+        out.append({"op": name, "shape": [N, K], "us": round(us, 2),
+                    "hbm_GBps": round(abytes / (us * 1e-6) / 1e9, 1),
+                    "frac_hbm_peak": round(abytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +274,8 @@ def main():
     weight_bytes_step = sum(op[3] for op in ops)
     value = weight_bytes_step / (ms_per_step * 1e-3) / 1e9
 
+    extras = measure_extras(gwb, workloads, Wd, ad, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(W_cpu, a_cpu, args.cpu_rows, args.cpu_awq_rows)
@@ -272,6 +310,7 @@ def main():
         "cpu_baseline": cpu,
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "breakdown": breakdown,
+        "extras": extras,
     }
     print(json.dumps(line))
 
