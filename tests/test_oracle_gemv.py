@@ -1,0 +1,59 @@
+"""Pins for the decode-GEMV reference (y = x @ dequantize(W)^T; page
+export_gptq_cpu.py's W4A16 consumer, page uintx_quant.py's forward)."""
+from fractions import Fraction
+
+import numpy as np
+
+import oracle.gemv as og
+import oracle.gptq as gq
+import oracle.mxfp4 as mx
+from _exact import F
+from group_wise_bit_amd import workloads
+
+
+def _x(b, k, seed):
+    return workloads.normal_weight(b, k, std=1.0, seed=seed).float().numpy()
+
+
+def test_one_hot_activation_reads_one_weight_column():
+    W = workloads.mxfp4_weight(24, 128, seed=95).float().numpy()
+    packed, e8 = mx.quantize(W)
+    deq = og.dequantized("mxfp4", {"packed": packed, "e8m0": e8}, 24, 128)
+    for k in (0, 37, 127):
+        x = np.zeros((1, 128), np.float32)
+        x[0, k] = 1.0
+        assert np.array_equal(og.gemv(deq, x)[0], deq[:, k].astype(np.float64))
+
+
+def test_exact_rational_sums_on_tiny_inputs():
+    W = workloads.mxfp4_weight(8, 128, seed=96).float().numpy()
+    q = gq.quantize_asym(W, 32)
+    deq = og.dequantized("gptq_asym", q, 8, 128, group=32)
+    x = _x(3, 128, 97)
+    y = og.gemv(deq, x)
+    for b in range(3):
+        for n in range(8):
+            exact = sum(F(deq[n, k]) * F(x[b, k]) for k in range(128))
+            assert abs(Fraction(y[b, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 45) + Fraction(1, 2 ** 200)
+
+
+def test_orientation_and_linearity():
+    """Output n uses row n (a non-square shape catches a transpose); integer-valued
+    inputs make the float64 results exact, so linearity holds bit for bit."""
+    rng = np.random.default_rng(98)
+    deq = rng.integers(-8, 8, (5, 96)).astype(np.float32)
+    x1 = rng.integers(-4, 5, (2, 96)).astype(np.float32)
+    x2 = rng.integers(-4, 5, (2, 96)).astype(np.float32)
+    y = og.gemv(deq, x1)
+    assert y.shape == (2, 5)
+    assert y[1, 3] == float(np.dot(deq[3].astype(np.float64), x1[1]))
+    assert np.array_equal(og.gemv(deq, 3 * x1 + x2), 3 * y + og.gemv(deq, x2))
+    assert np.array_equal(og.gemv(deq, np.ones((1, 96), np.float32))[0], deq.sum(1).astype(np.float64))
+    assert np.array_equal(og.abs_gemv(deq, x1), np.abs(x1).astype(np.float64) @ np.abs(deq).T)
+
+
+def test_dequantized_matches_each_format_oracle():
+    W = workloads.mxfp4_weight(16, 256, seed=99).float().numpy()
+    q = gq.quantize_sym(W, 128)
+    assert np.array_equal(og.dequantized("gptq_sym", q, 16, 256),
+                          gq.dequantize(q["qweight"], q["scales"], q["qzeros"], 128, True))

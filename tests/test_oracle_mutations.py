@@ -119,3 +119,12 @@ def test_fold_transposed_row_vector_caught(monkeypatch):
         return fd._apply(x, np.resize(np.asarray(row, np.float32), x.shape[1])[None, :], row_op)
     monkeypatch.setattr(fd, "fold", swapped)
     _fails(tf.test_orientation_and_order)
+
+
+def test_gemv_transposed_weight_caught(monkeypatch):
+    import oracle.gemv as og
+    import test_oracle_gemv as tgv
+    monkeypatch.setattr(og, "gemv", lambda deq, x: np.asarray(x, np.float64).reshape(-1, np.shape(deq)[0])
+                        @ np.asarray(deq, np.float64) if np.shape(x)[-1] == np.shape(deq)[0]
+                        else np.zeros((np.atleast_2d(x).shape[0], np.shape(deq)[0])))
+    _fails(tgv.test_orientation_and_linearity)
