@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgwb.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "common.hip", "mxfp4.hip", "gptq.hip", "uintx.hip", "awq.hip", "fold.hip"]
+SOURCES = ["api.hip", "common.hip", "mxfp4.hip", "gptq.hip", "uintx.hip", "awq.hip", "fold.hip", "gemv.hip"]
 # The uintx, GPTQ and AWQ arithmetic never produces a NaN from finite weights and
 # scalings, and non-finite inputs are outside the method; without NaN semantics the
 # compiler drops the canonicalization it otherwise inserts around every float min/max.

@@ -64,6 +64,9 @@ _SIGS = {
     "gwb_stream_copy": [_P, _P, _SZ, _P],
     "gwb_awq_scales_host": [_P, _I64, _P, _I32, _P],
     "gwb_fold_mxfp4": [_P, _I32, _I64, _I64, _I64, ctypes.POINTER(Fold), _P, _I64, ctypes.POINTER(QTensors), _P],
+    "gwb_gemv_workspace": [ctypes.POINTER(QSpec), _I64, _I64, _I64, ctypes.POINTER(_SZ)],
+    "gwb_gemv": [ctypes.POINTER(QSpec), ctypes.POINTER(QTensors), _I64, _I64, _P, _I64, _I64, _P, _I32, _I64, _P,
+                 _SZ, _P],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(lib, _name)
@@ -297,6 +300,43 @@ def prepare_fold_mxfp4(W: torch.Tensor, col, col_op: str, row, row_op: str, fold
                        mx: Optional[Quantized]) -> Prepared:
     args, keep = _fold_args(W, col, col_op, row, row_op, folded, mx)
     return Prepared(lib.gwb_fold_mxfp4, args, (keep, W, col, row, folded, mx))
+
+
+def gemv_workspace_bytes(q: Quantized, B: int) -> int:
+    sp, b = q.spec(), ctypes.c_size_t()
+    _check(lib.gwb_gemv_workspace(ctypes.byref(sp), q.N, q.K, B, ctypes.byref(b)))
+    return b.value
+
+
+def _gemv_args(q, x, y, workspace):
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != q.K or x.stride(1) != 1 or not x.is_cuda:
+        raise ValueError("x must be a bf16 CUDA tensor [B, K] with unit stride along K")
+    B = x.shape[0]
+    if y.dtype not in _DT or tuple(y.shape) != (B, q.N) or y.stride(1) != 1:
+        raise ValueError("y must be float32 or bf16 [B, N] with unit stride along N")
+    sp, qt = q.spec(), q.qtensors()
+    ws_b = 0 if workspace is None else workspace.numel()
+    return (ctypes.byref(sp), ctypes.byref(qt), q.N, q.K, _ptr(x), B, x.stride(0), _ptr(y), _DT[y.dtype], y.stride(0),
+            _ptr(workspace), ws_b, _stream()), (sp, qt)
+
+
+def gemv(q: Quantized, x: torch.Tensor, y_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x @ dequantize(W)^T from the packed weight (GPTQ or MXFP4); x bf16 [B, K],
+    B <= 8; returns y [B, N] of y_dtype."""
+    if out is None:
+        out = torch.empty(x.shape[0], q.N, dtype=y_dtype, device=x.device)
+    if workspace is None:
+        nb = gemv_workspace_bytes(q, x.shape[0])
+        workspace = _alloc(nb, x.device) if nb else None
+    args, _keep = _gemv_args(q, x, out, workspace)
+    _check(lib.gwb_gemv(*args))
+    return out
+
+
+def prepare_gemv(q: Quantized, x: torch.Tensor, y: torch.Tensor, workspace: Optional[torch.Tensor]) -> Prepared:
+    args, keep = _gemv_args(q, x, y, workspace)
+    return Prepared(lib.gwb_gemv, args, (keep, q, x, y, workspace))
 
 
 def stream_copy(dst: torch.Tensor, src: torch.Tensor) -> None:

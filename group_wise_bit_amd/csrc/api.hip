@@ -312,6 +312,50 @@ int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t
   return hip_check("fold launch");
 }
 
+static size_t gemv_workspace(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
+  if (sp->format == GWB_GPTQ_SYM || sp->format == GWB_GPTQ_ASYM)
+    return (size_t)gwb::gptq_gemv_splits(K) * (size_t)B * (size_t)N * sizeof(float);
+  return 0;
+}
+
+static int check_gemv(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
+  if (int rc = check_spec(sp, N, K)) return rc;
+  if (sp->format == GWB_UINTX) return fail(GWB_E_UNSUPPORTED, "the GEMV takes GPTQ and MXFP4 weights");
+  if (B < 1 || B > 8) return fail(GWB_E_ARG, "B must be 1..8, got %lld", (long long)B);
+  return GWB_OK;
+}
+
+int gwb_gemv_workspace(const gwb_qspec* spec, int64_t N, int64_t K, int64_t B, size_t* bytes) {
+  if (!bytes) return fail(GWB_E_ARG, "bytes is NULL");
+  if (int rc = check_gemv(spec, N, K, B)) return rc;
+  *bytes = gemv_workspace(spec, N, K, B);
+  return ok();
+}
+
+int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K, const void* x, int64_t B,
+             int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  if (int rc = check_gemv(spec, N, K, B)) return rc;
+  if (y_dtype != GWB_F32 && y_dtype != GWB_BF16) return fail(GWB_E_ARG, "unknown y_dtype %d", y_dtype);
+  if (N == 0) return ok();
+  if (!x || !y) return fail(GWB_E_ARG, "x and y are required");
+  if (ldx < K || ldy < N) return fail(GWB_E_ARG, "ldx must be >= K and ldy >= N");
+  if (!aligned16(x) || ldx % 8) return fail(GWB_E_UNSUPPORTED, "x and its row stride must be 16-byte aligned");
+  if (K == 0) return fail(GWB_E_SHAPE, "K must be positive");
+  if (int rc = check_tensors(spec, w)) return rc;
+  const size_t need = gemv_workspace(spec, N, K, B);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (need && !aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  if (spec->format == GWB_MXFP4)
+    gwb::launch_mxfp4_gemv((int)B, w->codes, w->scales, N, K, x, ldx, y, y_dtype, ldy, st);
+  else
+    gwb::launch_gptq_gemv(spec->format == GWB_GPTQ_SYM, spec->group, (int)B, w->codes, w->scales, w->zeros, N, K, x,
+                          ldx, y, y_dtype, ldy, (float*)workspace, st);
+  return hip_check("gemv launch");
+}
+
 // Host computation of the AWQ scaling table, the same steps and precision as the device
 // table kernels: a' = max(a, 1e-8) in float32, then float64 for an = a' / mean(a'),
 // p = clamp(an**alpha, 1e-2, 1e2) (exact 1, an and sqrt(an) for alpha 0, 1 and 0.5) and

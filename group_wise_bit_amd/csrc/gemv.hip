@@ -1,0 +1,324 @@
+// Decode GEMV on quantized weights: y[b, n] = sum_k x[b, k] * dequant(W)[n, k], with the
+// weights read in their packed form (about a quarter of the bf16 bytes). Page
+// export_gptq_cpu.py: vLLM's W4A16 kernel consumes the GPTQ tensors directly, and the
+// 131072 x 2048 lm_head is the largest read of a decode step; page
+// quantize_dflash_mxfp4.py serves its linears as MXFP4.
+//
+// Activations are bf16 [B, K] (B <= 8), results float32 or bf16 [B, N]. Every product
+// of a dequantized value and an activation is exact in float32; sums accumulate in
+// float32 in a fixed order (deterministic for a given shape).
+//
+// GPTQ ([K/8, N] words, n contiguous): a lane owns 4 adjacent outputs (one 16-byte load
+// per qweight row r), a wavefront 256 outputs x 128 k (16 loads in flight), a block's
+// four wavefronts 512 k, combined through LDS. With (c - z) * s per group,
+// sum_k (c - z) s x = s (sum_k c x - z sum_k x): codes become floats with
+// v_cvt_f32_ubyte, the group sum of x is a wavefront reduction. Longer K is split
+// across blocks, whose partial sums a second kernel adds in order.
+//
+// MXFP4 ([N, K/2] bytes + E8M0 [N, K/32]): lanes run along K, one 32-block per lane
+// and step; the codes of a block become bf16 pairs with the scaled FP4 conversion at
+// scale 1 (exact), v_dot2c_f32_bf16 multiplies them with the activation pairs, and the
+// block sum is scaled by 2^(e8m0 - 127) (exact). A wavefront takes 8 rows at a time and
+// reduces each across its lanes.
+#include "kernels.hpp"
+#include "mxfp4_math.hpp"
+
+namespace gwb {
+
+typedef __bf16 gv_bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <typename TY>
+__device__ __forceinline__ void store_y(TY* p, float v) {
+  if constexpr (sizeof(TY) == 4) *p = v;
+  else *p = (uint16_t)f32_to_bf16_rne(v);
+}
+
+// Sum over the 64 lanes of a wavefront, fixed butterfly order; every lane gets it.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_read<kDppXor1>(v);
+  v += dpp_read<kDppXor2>(v);
+  v += dpp_read<kDppHalfMirror>(v);
+  v += dpp_read<kDppMirror>(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// ------------------------------------------------------------------ GPTQ
+constexpr int kGqLaneN = 4, kGqWaveN = 64 * kGqLaneN, kGqWaveK = 128, kGqBlockK = 4 * kGqWaveK;
+
+// B is the compiled width (1, 2, 4, 8); Bn <= B activation rows are real: the others
+// re-read row Bn - 1 and are not stored.
+template <bool SYM, int G, int B>
+__global__ __launch_bounds__(256) void gptq_gemv_kernel(const uint32_t* __restrict__ qweight,
+                                                        const uint16_t* __restrict__ scale_bits,
+                                                        const uint32_t* __restrict__ qzeros, int N, int K,
+                                                        const uint16_t* __restrict__ x, int64_t ldx, int Bn,
+                                                        float* __restrict__ part) {
+  static_assert(kGqWaveK % G == 0, "a wavefront covers whole groups");
+  __shared__ float red[4][B][kGqWaveN];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int n0 = blockIdx.x * kGqWaveN + lane * kGqLaneN;
+  const int nc = min(n0, N - kGqLaneN);                 // N % 8 == 0: lanes past N read a valid place
+  const int kw = blockIdx.y * kGqBlockK + wave * kGqWaveK;
+  float acc[B][kGqLaneN];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int j = 0; j < kGqLaneN; ++j) acc[b][j] = 0.0f;
+  if (kw < K) {                                         // wave-uniform; K % G == 0, so whole groups
+    const int nr = min(kGqWaveK, K - kw) / 8;           // qweight rows of this wavefront
+    U4 wv[kGqWaveK / 8];
+#pragma unroll
+    for (int r = 0; r < kGqWaveK / 8; ++r)
+      if (r < nr) wv[r] = ld16(qweight + (int64_t)(kw / 8 + r) * N + nc);
+#pragma unroll
+    for (int gi = 0; gi < kGqWaveK / G; ++gi) {
+      const int g0 = kw + gi * G;
+      if (g0 >= K) break;
+      const int g = g0 / G;
+      // group sum of each activation row: two activations per lane, then the wavefront
+      float xs[B];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        float v = 0.0f;
+        if (2 * lane < G) {
+          const uint32_t p = *reinterpret_cast<const uint32_t*>(x + (int64_t)min(b, Bn - 1) * ldx + g0 + 2 * lane);
+          v = bf16_lo(p) + bf16_hi(p);
+        }
+        xs[b] = wave_sum(v);
+      }
+      float cx[B][kGqLaneN];
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int j = 0; j < kGqLaneN; ++j) cx[b][j] = 0.0f;
+#pragma unroll
+      for (int rr = 0; rr < G / 8; ++rr) {
+        const int r = gi * (G / 8) + rr;
+        const uint32_t w4[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
+        float xk[B][8];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const U4 xv = *reinterpret_cast<const U4*>(x + (int64_t)min(b, Bn - 1) * ldx + kw + 8 * r);
+          xk[b][0] = bf16_lo(xv.x); xk[b][1] = bf16_hi(xv.x); xk[b][2] = bf16_lo(xv.y); xk[b][3] = bf16_hi(xv.y);
+          xk[b][4] = bf16_lo(xv.z); xk[b][5] = bf16_hi(xv.z); xk[b][6] = bf16_lo(xv.w); xk[b][7] = bf16_hi(xv.w);
+        }
+#pragma unroll
+        for (int j = 0; j < kGqLaneN; ++j) {
+          uint32_t ev = w4[j] & 0x0F0F0F0Fu, od = (w4[j] >> 4) & 0x0F0F0F0Fu;
+          // opaque to the combiner, so each code converts straight from its byte
+          // (v_cvt_f32_ubyte0..3) instead of a bit-field extract per code
+          asm volatile("" : "+v"(ev), "+v"(od));
+          const float c[8] = {(float)(ev & 0xFFu), (float)(od & 0xFFu), (float)((ev >> 8) & 0xFFu),
+                              (float)((od >> 8) & 0xFFu), (float)((ev >> 16) & 0xFFu), (float)((od >> 16) & 0xFFu),
+                              (float)(ev >> 24), (float)(od >> 24)};
+#pragma unroll
+          for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) cx[b][j] = __builtin_fmaf(c[i], xk[b][i], cx[b][j]);
+        }
+      }
+      // s * (sum c x - z * sum x) for this group
+      const uint2 sb = *reinterpret_cast<const uint2*>(scale_bits + (int64_t)g * N + nc);
+      const float s[4] = {(float)__builtin_bit_cast(_Float16, (uint16_t)(sb.x & 0xFFFFu)),
+                          (float)__builtin_bit_cast(_Float16, (uint16_t)(sb.x >> 16)),
+                          (float)__builtin_bit_cast(_Float16, (uint16_t)(sb.y & 0xFFFFu)),
+                          (float)__builtin_bit_cast(_Float16, (uint16_t)(sb.y >> 16))};
+      float z[4] = {8.0f, 8.0f, 8.0f, 8.0f};
+      if constexpr (!SYM) {
+        const uint32_t zw = qzeros[(int64_t)g * (N / 8) + nc / 8] >> (4 * (nc % 8));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z[j] = (float)((zw >> (4 * j)) & 0xFu);
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int j = 0; j < kGqLaneN; ++j) acc[b][j] = __builtin_fmaf(s[j], __builtin_fmaf(-z[j], xs[b], cx[b][j]), acc[b][j]);
+    }
+  }
+  // the four wavefronts' k-ranges, added in order
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int j = 0; j < kGqLaneN; ++j) red[wave][b][lane * kGqLaneN + j] = acc[b][j];
+  __syncthreads();
+  for (int e = t; e < B * kGqWaveN; e += 256) {
+    const int b = e / kGqWaveN, i = e % kGqWaveN, n = blockIdx.x * kGqWaveN + i;
+    if (n < N && b < Bn)
+      part[((int64_t)blockIdx.y * Bn + b) * N + n] = ((red[0][b][i] + red[1][b][i]) + red[2][b][i]) + red[3][b][i];
+  }
+}
+
+// y[b, n] = sum over the K splits of part[s][b][n], in order.
+template <typename TY>
+__global__ __launch_bounds__(256) void gemv_finalize_kernel(const float* __restrict__ part, int S, int B, int N,
+                                                            TY* __restrict__ y, int64_t ldy) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)B * N) return;
+  const int b = (int)(e / N), n = (int)(e % N);
+  float v = 0.0f;
+  for (int s = 0; s < S; ++s) v += part[((int64_t)s * B + b) * N + n];
+  store_y(y + (int64_t)b * ldy + n, v);
+}
+
+// ------------------------------------------------------------------ MXFP4
+template <int B> struct MxRows { static constexpr int R = B <= 2 ? 8 : (B <= 4 ? 4 : 2); };
+
+template <int B>
+__device__ __forceinline__ void load_x_block(const uint16_t* __restrict__ x, int64_t ldx, int blk, uint32_t (&xa)[B][16]) {
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    const U4* xp = reinterpret_cast<const U4*>(x + (int64_t)b * ldx + 32 * blk);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const U4 v = xp[q];
+      xa[b][4 * q] = v.x; xa[b][4 * q + 1] = v.y; xa[b][4 * q + 2] = v.z; xa[b][4 * q + 3] = v.w;
+    }
+  }
+}
+
+template <int B, typename TY>
+__global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restrict__ packed,
+                                                         const uint8_t* __restrict__ e8m0, int N, int K,
+                                                         const uint16_t* __restrict__ x, int64_t ldx,
+                                                         TY* __restrict__ y, int64_t ldy) {
+  constexpr int R = MxRows<B>::R;
+  const int lane = threadIdx.x & 63;
+  const int nblk = K / 32;                            // blocks per row
+  const int steps = (nblk + 63) / 64;                 // blocks per lane
+  const int waves = gridDim.x * 4;
+  const int wave = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const float one = mx_scale_operand(127u);
+  uint32_t xa[B][16];                                 // activation pairs of the lane's block
+  if (steps == 1) load_x_block<B>(x, ldx, min(lane, nblk - 1), xa);
+  for (int row0 = wave * R; row0 < N; row0 += waves * R) {     // wave-uniform
+    float acc[R][B];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int b = 0; b < B; ++b) acc[i][b] = 0.0f;
+    for (int st = 0; st < steps; ++st) {
+      const int blk = st * 64 + lane;
+      const bool ok = blk < nblk;
+      const int bc = ok ? blk : nblk - 1;
+      if (steps != 1) load_x_block<B>(x, ldx, bc, xa);
+      U4 pw[R];
+      uint32_t ev[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int n = min(row0 + i, N - 1);
+        pw[i] = ld16_nt(packed + (int64_t)n * (K / 2) + 16 * bc);
+        ev[i] = e8m0[(int64_t)n * nblk + bc];
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const uint32_t w[4] = {pw[i].x, pw[i].y, pw[i].z, pw[i].w};
+        float d[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) d[b] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          gv_bf16x2_t v[4];
+          v[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], one, 0);
+          v[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], one, 1);
+          v[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], one, 2);
+          v[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], one, 3);
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+              d[b] = __builtin_amdgcn_fdot2_f32_bf16(v[p], __builtin_bit_cast(gv_bf16x2_t, xa[b][4 * q + p]), d[b],
+                                                     false);
+        }
+        const int ex = (int)ev[i] - 127;
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[i][b] += ok ? ldexpf(d[b], ex) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const float v = wave_sum(acc[i][b]);
+        if (lane == 0 && row0 + i < N) store_y(y + (int64_t)b * ldy + row0 + i, v);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+int gptq_gemv_splits(int64_t K) { return (int)((K + kGqBlockK - 1) / kGqBlockK); }
+
+template <bool SYM, int G, int B>
+static void gptq_gemv_b(int Bn, const void* qw, const void* sc, const void* qz, int64_t N, int64_t K, const void* x,
+                        int64_t ldx, float* part, hipStream_t st) {
+  const dim3 grid((unsigned)((N + kGqWaveN - 1) / kGqWaveN), (unsigned)gptq_gemv_splits(K));
+  hipLaunchKernelGGL((gptq_gemv_kernel<SYM, G, B>), grid, dim3(256), 0, st, (const uint32_t*)qw,
+                     (const uint16_t*)sc, (const uint32_t*)qz, (int)N, (int)K, (const uint16_t*)x, ldx, Bn, part);
+}
+
+template <bool SYM, int G>
+static void gptq_gemv_g(int B, const void* qw, const void* sc, const void* qz, int64_t N, int64_t K, const void* x,
+                        int64_t ldx, float* part, hipStream_t st) {
+  if (B == 1) gptq_gemv_b<SYM, G, 1>(B, qw, sc, qz, N, K, x, ldx, part, st);
+  else if (B == 2) gptq_gemv_b<SYM, G, 2>(B, qw, sc, qz, N, K, x, ldx, part, st);
+  else if (B <= 4) gptq_gemv_b<SYM, G, 4>(B, qw, sc, qz, N, K, x, ldx, part, st);
+  else gptq_gemv_b<SYM, G, 8>(B, qw, sc, qz, N, K, x, ldx, part, st);
+}
+
+void launch_gptq_gemv(bool sym, int group, int B, const void* qweight, const void* scales, const void* qzeros,
+                      int64_t N, int64_t K, const void* x, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
+                      float* part, hipStream_t st) {
+  if (sym) {
+    if (group == 32) gptq_gemv_g<true, 32>(B, qweight, scales, qzeros, N, K, x, ldx, part, st);
+    else if (group == 64) gptq_gemv_g<true, 64>(B, qweight, scales, qzeros, N, K, x, ldx, part, st);
+    else gptq_gemv_g<true, 128>(B, qweight, scales, qzeros, N, K, x, ldx, part, st);
+  } else {
+    if (group == 32) gptq_gemv_g<false, 32>(B, qweight, scales, qzeros, N, K, x, ldx, part, st);
+    else if (group == 64) gptq_gemv_g<false, 64>(B, qweight, scales, qzeros, N, K, x, ldx, part, st);
+    else gptq_gemv_g<false, 128>(B, qweight, scales, qzeros, N, K, x, ldx, part, st);
+  }
+  const int S = gptq_gemv_splits(K);
+  const int64_t total = (int64_t)B * N;
+  const unsigned fgrid = (unsigned)((total + 255) / 256);
+  if (y_dtype == kBF16)
+    hipLaunchKernelGGL(gemv_finalize_kernel<uint16_t>, dim3(fgrid), dim3(256), 0, st, (const float*)part, S, B,
+                       (int)N, (uint16_t*)y, ldy);
+  else
+    hipLaunchKernelGGL(gemv_finalize_kernel<float>, dim3(fgrid), dim3(256), 0, st, (const float*)part, S, B,
+                       (int)N, (float*)y, ldy);
+}
+
+template <int B, typename TY>
+static void mxfp4_gemv_b(const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x, int64_t ldx,
+                         void* y, int64_t ldy, hipStream_t st) {
+  const int64_t passes = (N + MxRows<B>::R - 1) / MxRows<B>::R;       // wavefront passes
+  const unsigned grid = stream_blocks((uint64_t)passes * 64);          // one wavefront per pass, capped
+  hipLaunchKernelGGL((mxfp4_gemv_kernel<B, TY>), dim3(grid), dim3(256), 0, st, (const uint8_t*)packed,
+                     (const uint8_t*)e8m0, (int)N, (int)K, (const uint16_t*)x, ldx, (TY*)y, ldy);
+}
+
+template <typename TY>
+static void mxfp4_gemv_t(int B, const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x,
+                         int64_t ldx, void* y, int64_t ldy, hipStream_t st) {
+  switch (B) {
+    case 1: mxfp4_gemv_b<1, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
+    case 2: mxfp4_gemv_b<2, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
+    case 3: mxfp4_gemv_b<3, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
+    case 4: mxfp4_gemv_b<4, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
+    case 5: mxfp4_gemv_b<5, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
+    case 6: mxfp4_gemv_b<6, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
+    case 7: mxfp4_gemv_b<7, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
+    default: mxfp4_gemv_b<8, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
+  }
+}
+
+void launch_mxfp4_gemv(int B, const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x,
+                       int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, hipStream_t st) {
+  if (y_dtype == kBF16) mxfp4_gemv_t<uint16_t>(B, packed, e8m0, N, K, x, ldx, y, ldy, st);
+  else mxfp4_gemv_t<float>(B, packed, e8m0, N, K, x, ldx, y, ldy, st);
+}
+
+}  // namespace gwb

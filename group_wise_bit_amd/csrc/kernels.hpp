@@ -80,6 +80,14 @@ void launch_fold(int col_op, int row_op, const void* W, int64_t N, int64_t K, in
                  const float* col, const float* row, void* out, int64_t ldo, void* packed, void* e8m0,
                  hipStream_t st);
 
+// ---- decode GEMV on quantized weights (gemv.hip); B <= 8 activation rows (bf16)
+int gptq_gemv_splits(int64_t K);     // K splits; part holds splits * B * N floats
+void launch_gptq_gemv(bool sym, int group, int B, const void* qweight, const void* scales, const void* qzeros,
+                      int64_t N, int64_t K, const void* x, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
+                      float* part, hipStream_t st);
+void launch_mxfp4_gemv(int B, const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x,
+                       int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, hipStream_t st);
+
 // ---- measurement copy (common.hip)
 void launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
 

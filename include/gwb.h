@@ -180,6 +180,23 @@ typedef struct {
 int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw, const gwb_fold* fold,
                    void* out_bf16, int64_t ldo, const gwb_qtensors* mx, void* stream);
 
+/* Decode GEMV on quantized weights: y[b, n] = sum_k x[b, k] * dequant(W)[n, k], the
+ * weights read in their packed form. Page export_gptq_cpu.py: vLLM's W4A16 kernel
+ * consumes the GPTQ tensors as stored (its lm_head note: the 131072 x 2048 head is the
+ * largest read of a decode step); page quantize_dflash_mxfp4.py serves its linears as
+ * MXFP4.
+ *   spec, w  a GPTQ (sym or asym) or MXFP4 weight as gwb_quantize wrote it, [N, K]
+ *   x        device bf16 [B, K], row stride ldx (multiple of 8), 16-byte aligned; 1 <= B <= 8
+ *   y        device [B, N] of y_dtype (GWB_F32 or GWB_BF16, RNE), row stride ldy
+ *   workspace at least gwb_gemv_workspace bytes (GPTQ: K-split partial sums; MXFP4: 0)
+ * Products of dequantized values and activations are exact in float32; sums are float32
+ * in a fixed order (deterministic for a given shape; error bounded by the float32
+ * accumulation). uintx weights: GWB_E_UNSUPPORTED.                                  */
+int gwb_gemv_workspace(const gwb_qspec* spec, int64_t N, int64_t K, int64_t B, size_t* bytes);
+int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K, const void* x, int64_t B,
+             int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+             void* stream);
+
 /* The AWQ scaling table on the host (page quantize_dflash_mxfp4.py, search_scale: the
  * per-alpha s of the search). a: HOST float32 [K] per-channel mean |x|; alphas: HOST
  * array of n_alpha doubles (1..16); s_out: HOST float32 [n_alpha, K]. Steps as in

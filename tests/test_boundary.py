@@ -199,3 +199,30 @@ def test_fold_validates_before_launch():
     assert go(ldo=60) == gwb.E_UNSUPPORTED
     assert go(N=0) == gwb.OK and go(K=0) == gwb.OK      # empty: nothing to do
     assert go(N=1 << 20, K=1 << 12, ldw=1 << 12, ldo=1 << 12) == gwb.E_UNSUPPORTED
+
+
+def test_gemv_sizes_and_validation():
+    P = ctypes.c_void_p
+    fake = 1 << 20
+    qt = gwb.QTensors(fake, fake, fake, None)
+    def ws(fmt, N, K, B, group=None):
+        sp, b = gwb.make_spec(fmt, 4, group), ctypes.c_size_t()
+        rc = lib.gwb_gemv_workspace(ctypes.byref(sp), N, K, B, ctypes.byref(b))
+        return rc, b.value
+    assert ws("gptq_sym", 131072, 2048, 1) == (gwb.OK, 4 * 131072 * 4)      # 4 K-splits of 512
+    assert ws("gptq_asym", 256, 640, 3, 64) == (gwb.OK, 2 * 3 * 256 * 4)
+    assert ws("mxfp4", 4096, 2048, 8) == (gwb.OK, 0)
+    assert ws("gptq_sym", 256, 512, 0)[0] == gwb.E_ARG
+    assert ws("gptq_sym", 256, 512, 9)[0] == gwb.E_ARG
+    sp_u = gwb.make_spec("uintx", 4, 64)
+    assert lib.gwb_gemv_workspace(ctypes.byref(sp_u), 64, 128, 1, ctypes.byref(ctypes.c_size_t())) == gwb.E_UNSUPPORTED
+    sp = gwb.make_spec("gptq_sym", 4, 128)
+    def go(x=fake, B=1, ldx=512, y=fake, ydt=gwb.F32, ldy=256, w=0, wsb=0):
+        return lib.gwb_gemv(ctypes.byref(sp), ctypes.byref(qt), 256, 512, P(x), B, ldx, P(y), ydt, ldy, P(w), wsb, None)
+    assert go(ydt=7) == gwb.E_ARG
+    assert go(x=None) == gwb.E_ARG
+    assert go(ldx=500) == gwb.E_ARG
+    assert go(ldx=516) == gwb.E_UNSUPPORTED
+    assert go(x=fake + 4) == gwb.E_UNSUPPORTED
+    assert go() == gwb.E_SIZE                                                 # K-split partials needed
+    assert go(w=fake + 8, wsb=1 << 20) == gwb.E_UNSUPPORTED

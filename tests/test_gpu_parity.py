@@ -12,6 +12,7 @@ import torch
 
 import oracle.awq as oawq
 import oracle.fold as ofold
+import oracle.gemv as ogv
 import oracle.gptq as ogq
 import oracle.mxfp4 as omx
 import oracle.snr as osnr
@@ -304,6 +305,71 @@ def test_fold_outputs_strides_and_ragged_k():
     assert np.array_equal(_gpu_bf16bits(r40["folded"]), _ref_bf16bits(ofold.fold(W40.float().numpy(), c40, "div")))
 
 
+# --------------------------------------------------------------------- decode GEMV
+U32 = 2.0 ** -24
+
+
+def _gemv_check(y, ref, bound, ydt):
+    got = _np(y.float()).astype(np.float64)
+    err = np.abs(got - ref)
+    tol = bound + (np.abs(ref) * 2.0 ** -8 if ydt == torch.bfloat16 else 0.0)
+    assert np.all(err <= tol), float(np.max(err / np.maximum(tol, 1e-300)))
+
+
+def _gptq_bound(o, x, group, sym, K):
+    """float32 error bound of the kernel's evaluation order, s (sum c x - z sum x) per
+    group: u (G + K/G + 40) sum_k |s| (c + z) |x|."""
+    codes = o["codes"].astype(np.float64)                                  # [K, N]
+    s = np.abs(np.asarray(o["scales"], np.float16).astype(np.float64))       # [G, N]
+    z = np.full(s.shape, 8.0) if sym else o["zp"].astype(np.float64)
+    w = (codes.reshape(K // group, group, -1) + z[:, None, :]) * s[:, None, :]
+    return U32 * (group + K // group + 40) * (np.abs(x.astype(np.float64)) @ w.reshape(K, -1))
+
+
+@pytest.mark.parametrize("fmt", ["gptq_sym", "gptq_asym"])
+@pytest.mark.parametrize("group", [32, 64, 128])
+@pytest.mark.parametrize("n,k,B", [(256, 512, 1), (72, 384, 3), (520, 1664, 8), (264, 640, 2)])
+def test_gemv_gptq_parity(fmt, group, n, k, B):
+    W = workloads.mxfp4_weight(n, k, seed=500 + n + group)
+    x = workloads.normal_weight(B, k, std=1.0, seed=501 + B)
+    q = gwb.quantize(W.to(DEV), fmt, group=group)
+    o = (ogq.quantize_sym if fmt == "gptq_sym" else ogq.quantize_asym)(W.float().numpy(), group)
+    deq = ogv.dequantized(fmt, o, n, k, group=group)
+    ref = ogv.gemv(deq, x.float().numpy())
+    bound = _gptq_bound(o, x.float().numpy(), group, fmt == "gptq_sym", k)
+    for ydt in (torch.float32, torch.bfloat16):
+        _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ref, bound, ydt)
+
+
+@pytest.mark.parametrize("n,k,B", [(64, 512, 1), (33, 96, 3), (40, 4096, 2), (17, 2080, 8), (300, 2048, 5)])
+def test_gemv_mxfp4_parity(n, k, B):
+    W = workloads.mxfp4_weight(n, k, seed=510 + n)
+    x = workloads.normal_weight(B, k, std=1.0, seed=511 + B)
+    q = gwb.quantize(W.to(DEV), "mxfp4")
+    packed, e8 = omx.quantize(W.float().numpy())
+    deq = omx.dequantize(packed, e8, k)
+    xf = x.float().numpy()
+    ref = ogv.gemv(deq, xf)
+    bound = U32 * (32 + k // 2048 + 40) * ogv.abs_gemv(deq, xf)
+    for ydt in (torch.float32, torch.bfloat16):
+        _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ref, bound, ydt)
+
+
+def test_gemv_one_hot_reads_columns_exactly():
+    """A one-hot activation makes every sum a single exact product: the GEMV returns
+    dequantized weight columns bit for bit (float32 output)."""
+    W = workloads.mxfp4_weight(264, 512, seed=512)
+    for fmt, group in (("gptq_asym", 64), ("mxfp4", None)):
+        q = gwb.quantize(W.to(DEV), fmt, group=group)
+        d = _np(gwb.dequantize(q, torch.float32))
+        x = torch.zeros(3, 512, dtype=torch.bfloat16)
+        for b, kk in enumerate((0, 200, 511)):
+            x[b, kk] = 1.0
+        y = _np(gwb.gemv(q, x.to(DEV)))
+        for b, kk in enumerate((0, 200, 511)):
+            assert np.array_equal(y[b], d[:, kk]), (fmt, kk)
+
+
 # ------------------------------------------------------------- full config sizes
 def _rows(n, count, seed):
     return np.sort(np.random.default_rng(seed).choice(n, count, replace=False))
@@ -430,6 +496,28 @@ def test_full_fold_34816x5120_sampled():
     assert np.array_equal(_gpu_bf16bits(r["folded"][rows]), _ref_bf16bits(x))
     assert np.array_equal(_np(r["mxfp4"]["packed"][rows]), packed)
     assert np.array_equal(_np(r["mxfp4"]["e8m0"][rows]), e8)
+
+
+def test_full_gemv_lm_head_131072x2048_sampled():
+    """The page's lm_head decode read: GPTQ sym g128 and MXFP4 of a 131072 x 2048
+    weight, one activation row; checked on sampled output rows against the oracle."""
+    N_, K_ = 131072, 2048
+    W = workloads.normal_weight(N_, K_, seed=520)
+    x = workloads.normal_weight(1, K_, std=1.0, seed=521)
+    Wd, xd = W.to(DEV), x.to(DEV)
+    rows = np.sort(np.random.default_rng(522).choice(N_ // 8, 32, replace=False)) * 8
+    ns = (rows[:, None] + np.arange(8)[None, :]).reshape(-1)            # whole qzeros words
+    xf = x.float().numpy()
+    q = gwb.quantize(Wd, "gptq_sym", group=128)
+    y = _np(gwb.gemv(q, xd)).astype(np.float64)
+    o = ogq.quantize_sym(W[ns].float().numpy(), 128)
+    deq = ogv.dequantized("gptq_sym", o, len(ns), K_, group=128)
+    _gemv_check(torch.from_numpy(y[:, ns]), ogv.gemv(deq, xf), _gptq_bound(o, xf, 128, True, K_), torch.float32)
+    qm = gwb.quantize(Wd, "mxfp4")
+    ym = _np(gwb.gemv(qm, xd)).astype(np.float64)
+    packed, e8 = omx.quantize(W[ns].float().numpy())
+    dm = omx.dequantize(packed, e8, K_)
+    _gemv_check(torch.from_numpy(ym[:, ns]), ogv.gemv(dm, xf), U32 * 73 * ogv.abs_gemv(dm, xf), torch.float32)
 
 
 # ------------------------------------------------------------------ empty shapes
