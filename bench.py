@@ -136,7 +136,7 @@ def cpu_baseline(W_cpu: torch.Tensor, a_cpu: torch.Tensor, rows: int, awq_rows: 
     }
 
 
-def _time_op(fn, reps: int = 20, warm: int = 3) -> float:
+def _time_op(fn, reps: int = 21, warm: int = 3) -> float:
     """Average microseconds of back-to-back launches of one prepared call."""
     for _ in range(warm):
         fn()
@@ -151,8 +151,9 @@ def _time_op(fn, reps: int = 20, warm: int = 3) -> float:
 
 def measure_extras(gwb, workloads, Wd, ad, dev):
     """Paths next to the hot path, timed on their own after the step (not part of
-    value): the AWQ fold of the gate_up weight (columns * s) straight to MXFP4, and the
-    same fold also writing the folded bf16 weight."""
+    value): the AWQ fold of the gate_up weight (columns * s) straight to MXFP4, the same
+    fold also writing the folded bf16 weight, and the decode GEMV reading a packed
+    131072 x 2048 lm_head (GPTQ sym g128, MXFP4) for one activation row."""
     out = []
     s = torch.from_numpy(gwb.awq_scales_host(ad.cpu(), (0.5,))[0].numpy()).to(dev)
     mx = gwb.fold_mxfp4(Wd, s, "mul", want_folded=False)["mxfp4"]
@@ -164,9 +165,37 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
         ("fold_mxfp4.columns_to_bf16_and_mxfp4", 4 * nk + nk / 2 + nk / 32 + 4 * K,
          gwb.prepare_fold_mxfp4(Wd, s, "mul", None, "none", folded, mx)),
     ]
-    for name, abytes, fn in cases:
+    # decode GEMV on the 131072 x 2048 lm_head (one activation row), weights packed
+    HN, HK = 131072, 2048
+    head = workloads.normal_weight(HN, HK, seed=520).to(dev)
+    xh = workloads.normal_weight(1, HK, std=1.0, seed=521).to(dev)
+    yh = torch.empty(1, HN, dtype=torch.float32, device=dev)
+    # three copies of each packed head (> 256 MB together), cycled, so each launch
+    # streams its weight from HBM as a decode step would rather than from the
+    # Infinity Cache
+    qg = [gwb.quantize(head, "gptq_sym", group=128) for _ in range(3)]
+    qm = [gwb.quantize(head, "mxfp4") for _ in range(3)]
+    del head
+    wsg = torch.empty(gwb.gemv_workspace_bytes(qg[0], 1), dtype=torch.uint8, device=dev)
+    hk = HN * HK
+
+    def cycle(calls):
+        it = {"i": 0}
+
+        def fn():
+            calls[it["i"] % len(calls)]()
+            it["i"] += 1
+        return fn
+    gemv_cases = [
+        ("gemv.gptq_sym_g128.lm_head_b1", hk / 2 + hk / 128 * 2 + 2 * HK + 4 * HN,
+         cycle([gwb.prepare_gemv(q, xh, yh, wsg) for q in qg])),
+        ("gemv.mxfp4.lm_head_b1", hk / 2 + hk / 32 + 2 * HK + 4 * HN,
+         cycle([gwb.prepare_gemv(q, xh, yh, None) for q in qm])),
+    ]
+    for name, abytes, fn in cases + gemv_cases:
         us = _time_op(fn)
-        out.append({"op": name, "shape": [N, K], "us": round(us, 2),
+        shape = [HN, HK] if name.startswith("gemv") else [N, K]
+        out.append({"op": name, "shape": shape, "us": round(us, 2),
                     "hbm_GBps": round(abytes / (us * 1e-6) / 1e9, 1),
                     "frac_hbm_peak": round(abytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)})
     return out
