@@ -315,12 +315,15 @@ int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t
 static size_t gemv_workspace(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
   if (sp->format == GWB_GPTQ_SYM || sp->format == GWB_GPTQ_ASYM)
     return (size_t)gwb::gptq_gemv_splits(K) * (size_t)B * (size_t)N * sizeof(float);
+  if (sp->format == GWB_UINTX) return (size_t)(K / 512) * (size_t)B * (size_t)N * sizeof(float);
   return 0;
 }
 
 static int check_gemv(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
   if (int rc = check_spec(sp, N, K)) return rc;
-  if (sp->format == GWB_UINTX) return fail(GWB_E_UNSUPPORTED, "the GEMV takes GPTQ and MXFP4 weights");
+  if (sp->format == GWB_UINTX && !gwb::uintx_gemv_supported(N, K))
+    return fail(GWB_E_UNSUPPORTED, "the uintx GEMV needs N %% 8 == 0 and K %% 512 == 0, got N=%lld K=%lld",
+                (long long)N, (long long)K);
   if (B < 1 || B > 8) return fail(GWB_E_ARG, "B must be 1..8, got %lld", (long long)B);
   return GWB_OK;
 }
@@ -350,6 +353,9 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
   hipStream_t st = (hipStream_t)stream;
   if (spec->format == GWB_MXFP4)
     gwb::launch_mxfp4_gemv((int)B, w->codes, w->scales, N, K, x, ldx, y, y_dtype, ldy, st);
+  else if (spec->format == GWB_UINTX)
+    gwb::launch_uintx_gemv(spec->nbits, (int)B, w->codes, w->scales, w->zeros, N, K, x, ldx, y, y_dtype, ldy,
+                           (float*)workspace, st);
   else
     gwb::launch_gptq_gemv(spec->format == GWB_GPTQ_SYM, spec->group, (int)B, w->codes, w->scales, w->zeros, N, K, x,
                           ldx, y, y_dtype, ldy, (float*)workspace, st);

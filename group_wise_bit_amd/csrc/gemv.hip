@@ -280,15 +280,18 @@ void launch_gptq_gemv(bool sym, int group, int B, const void* qweight, const voi
     else if (group == 64) gptq_gemv_g<false, 64>(B, qweight, scales, qzeros, N, K, x, ldx, part, st);
     else gptq_gemv_g<false, 128>(B, qweight, scales, qzeros, N, K, x, ldx, part, st);
   }
-  const int S = gptq_gemv_splits(K);
+  launch_gemv_finalize(part, gptq_gemv_splits(K), B, N, y, y_dtype, ldy, st);
+}
+
+void launch_gemv_finalize(const float* part, int S, int B, int64_t N, void* y, int32_t y_dtype, int64_t ldy,
+                          hipStream_t st) {
   const int64_t total = (int64_t)B * N;
   const unsigned fgrid = (unsigned)((total + 255) / 256);
   if (y_dtype == kBF16)
-    hipLaunchKernelGGL(gemv_finalize_kernel<uint16_t>, dim3(fgrid), dim3(256), 0, st, (const float*)part, S, B,
-                       (int)N, (uint16_t*)y, ldy);
+    hipLaunchKernelGGL(gemv_finalize_kernel<uint16_t>, dim3(fgrid), dim3(256), 0, st, part, S, B, (int)N,
+                       (uint16_t*)y, ldy);
   else
-    hipLaunchKernelGGL(gemv_finalize_kernel<float>, dim3(fgrid), dim3(256), 0, st, (const float*)part, S, B,
-                       (int)N, (float*)y, ldy);
+    hipLaunchKernelGGL(gemv_finalize_kernel<float>, dim3(fgrid), dim3(256), 0, st, part, S, B, (int)N, (float*)y, ldy);
 }
 
 template <int B, typename TY>

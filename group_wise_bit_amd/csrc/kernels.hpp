@@ -87,6 +87,14 @@ void launch_gptq_gemv(bool sym, int group, int B, const void* qweight, const voi
                       float* part, hipStream_t st);
 void launch_mxfp4_gemv(int B, const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x,
                        int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, hipStream_t st);
+// uintx (uintx.hip): N % 8 == 0 and K % 512 == 0; part holds K/512 * B * N floats
+bool uintx_gemv_supported(int64_t N, int64_t K);
+void launch_uintx_gemv(int nbits, int B, const void* packed, const void* scales, const void* zeros, int64_t N,
+                       int64_t K, const void* x, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, float* part,
+                       hipStream_t st);
+// y[b, n] = sum over s < S of part[(s * B + b) * N + n], in order
+void launch_gemv_finalize(const float* part, int S, int B, int64_t N, void* y, int32_t y_dtype, int64_t ldy,
+                          hipStream_t st);
 
 // ---- measurement copy (common.hip)
 void launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t st);

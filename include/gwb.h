@@ -185,13 +185,16 @@ int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t
  * consumes the GPTQ tensors as stored (its lm_head note: the 131072 x 2048 head is the
  * largest read of a decode step); page quantize_dflash_mxfp4.py serves its linears as
  * MXFP4.
- *   spec, w  a GPTQ (sym or asym) or MXFP4 weight as gwb_quantize wrote it, [N, K]
+ *   spec, w  a GPTQ (sym or asym), MXFP4 or uintx weight as gwb_quantize wrote it, [N, K];
+ *            uintx (page uintx_quant.py, forward: the bf16 weight bf16((q - zp) * s)
+ *            times x) needs N % 8 == 0 and K % 512 == 0, else GWB_E_UNSUPPORTED
  *   x        device bf16 [B, K], row stride ldx (multiple of 8), 16-byte aligned; 1 <= B <= 8
  *   y        device [B, N] of y_dtype (GWB_F32 or GWB_BF16, RNE), row stride ldy
- *   workspace at least gwb_gemv_workspace bytes (GPTQ: K-split partial sums; MXFP4: 0)
+ *   workspace at least gwb_gemv_workspace bytes (GPTQ and uintx: K-split partial sums;
+ *            MXFP4: 0)
  * Products of dequantized values and activations are exact in float32; sums are float32
  * in a fixed order (deterministic for a given shape; error bounded by the float32
- * accumulation). uintx weights: GWB_E_UNSUPPORTED.                                  */
+ * accumulation).                                                                    */
 int gwb_gemv_workspace(const gwb_qspec* spec, int64_t N, int64_t K, int64_t B, size_t* bytes);
 int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K, const void* x, int64_t B,
              int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,

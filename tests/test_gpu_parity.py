@@ -355,12 +355,37 @@ def test_gemv_mxfp4_parity(n, k, B):
         _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ref, bound, ydt)
 
 
+@pytest.mark.parametrize("nbits", [2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("n,k,B", [(64, 512, 1), (16, 1024, 3), (8, 2048, 8), (136, 1536, 2)])
+def test_gemv_uintx_parity(nbits, n, k, B):
+    """The page's forward: x times the bf16 weight bf16((q - zp) * s)."""
+    W = workloads.uintx_weight(n, k, seed=530 + n + nbits, outlier_frac=0.01)
+    x = workloads.normal_weight(B, k, std=1.0, seed=531 + B)
+    q = gwb.quantize(W.to(DEV), "uintx", nbits=nbits)
+    o = oux.quantize(W.float().numpy(), nbits)
+    deq = ogv.dequantized("uintx", o, n, k, nbits=nbits)
+    xf = x.float().numpy()
+    bound = U32 * (k // 512 + 40) * ogv.abs_gemv(deq, xf)
+    for ydt in (torch.float32, torch.bfloat16):
+        _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ogv.gemv(deq, xf), bound, ydt)
+
+
+def test_gemv_uintx_config_3072x12288():
+    W = workloads.uintx_weight()
+    x = workloads.normal_weight(2, 12288, std=1.0, seed=532)
+    q = gwb.quantize(W.to(DEV), "uintx", nbits=3)
+    o = oux.quantize(W.float().numpy(), 3)
+    deq = ogv.dequantized("uintx", o, 3072, 12288, nbits=3)
+    xf = x.float().numpy()
+    _gemv_check(gwb.gemv(q, x.to(DEV)), ogv.gemv(deq, xf), U32 * (24 + 40) * ogv.abs_gemv(deq, xf), torch.float32)
+
+
 def test_gemv_one_hot_reads_columns_exactly():
     """A one-hot activation makes every sum a single exact product: the GEMV returns
     dequantized weight columns bit for bit (float32 output)."""
     W = workloads.mxfp4_weight(264, 512, seed=512)
-    for fmt, group in (("gptq_asym", 64), ("mxfp4", None)):
-        q = gwb.quantize(W.to(DEV), fmt, group=group)
+    for fmt, group, nb in (("gptq_asym", 64, 4), ("mxfp4", None, 4), ("uintx", 64, 5)):
+        q = gwb.quantize(W.to(DEV), fmt, nbits=nb, group=group)
         d = _np(gwb.dequantize(q, torch.float32))
         x = torch.zeros(3, 512, dtype=torch.bfloat16)
         for b, kk in enumerate((0, 200, 511)):
