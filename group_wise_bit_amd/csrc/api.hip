@@ -315,7 +315,7 @@ int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t
 static size_t gemv_workspace(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
   if (sp->format == GWB_GPTQ_SYM || sp->format == GWB_GPTQ_ASYM)
     return (size_t)gwb::gptq_gemv_splits(K) * (size_t)B * (size_t)N * sizeof(float);
-  if (sp->format == GWB_UINTX) return (size_t)(K / 512) * (size_t)B * (size_t)N * sizeof(float);
+  if (sp->format == GWB_UINTX) return (size_t)gwb::uintx_gemv_splits(K) * (size_t)B * (size_t)N * sizeof(float);
   return 0;
 }
 

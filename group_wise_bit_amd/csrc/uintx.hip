@@ -394,82 +394,114 @@ __global__ __launch_bounds__(256) void uintx_dequant_flat(const uint8_t* __restr
 // y[b, n] = sum_k x[b, k] * w[n, k] with w = bf16((q - zp) * s), the bf16 weight the
 // page's forward builds before its linear. With N % 8 == 0 and K % 512 == 0, position p
 // of segment j is row j * N/8 + p / K, column p % K: a lane's 8 positions of the 8
-// segments share 8 activation columns and feed 8 output rows, and a wavefront's 512
-// positions lie in one row of each segment. The weight pairs (the hardware bf16 pair
-// conversion of the exact products) meet the activation pairs in v_dot2c_f32_bf16;
-// each wavefront writes one partial per (row, 512-column chunk), added in order after.
-__device__ __forceinline__ float ux_wave_sum(float v) {
-  v += dpp_read<kDppXor1>(v);
-  v += dpp_read<kDppXor2>(v);
-  v += dpp_read<kDppHalfMirror>(v);
-  v += dpp_read<kDppMirror>(v);
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+// segments share 8 activation columns and feed 8 output rows. A wavefront takes CH
+// consecutive 512-position chunks of one row (CH = 4 when K % 2048 == 0), so each lane
+// sums 64 * CH weights per row before one transposed reduction leaves lane j with row
+// j's sum. The weight pairs (the hardware bf16 pair conversion of the exact products)
+// meet the activation pairs in v_dot2c_f32_bf16; each wavefront writes one partial per
+// row, added over the K / (512 CH) wavefronts of a row in order afterwards.
+template <int CTRL, int NV>
+__device__ __forceinline__ void ux_fold_half(float (&v)[8], bool up) {
+#pragma unroll
+  for (int i = 0; i < NV / 2; ++i) {
+    const float keep = up ? v[i + NV / 2] : v[i], send = up ? v[i] : v[i + NV / 2];
+    v[i] = keep + dpp_read<CTRL>(send);
+  }
+}
+// 8 values per lane -> lane l holds the wavefront sum of value (l & 7). The half-mirror
+// partner of lane i is 7 - i (differs in bit 2), the quad steps pair bits 1 and 0; then
+// the eight 8-lane groups, which hold the same value index, are added.
+__device__ __forceinline__ float ux_transposed_sum(float (&v)[8], int lane) {
+  ux_fold_half<kDppHalfMirror, 8>(v, lane & 4);
+  ux_fold_half<kDppXor2, 4>(v, lane & 2);
+  ux_fold_half<kDppXor1, 2>(v, lane & 1);
+  float r = v[0];
+  r += dpp_read<kDppRor8>(r);
+  r += __shfl_xor(r, 16);
+  r += __shfl_xor(r, 32);
+  return r;
 }
 
-template <int NB, int B>
+template <int NB, int B, int CH>
 __global__ __launch_bounds__(256) void uintx_gemv_tiled(const uint8_t* __restrict__ packed,
                                                         const uint16_t* __restrict__ scales,
                                                         const uint8_t* __restrict__ zeros, FastDiv kdiv, uint32_t L1,
                                                         Shards sh, int N, const uint16_t* __restrict__ x,
                                                         int64_t ldx, int Bn, float* __restrict__ part) {
   using SB = ShardBits<NB>;
-  __shared__ uint32_t qp_lds[256];
+  __shared__ uint32_t qp_lds[CH][256];
   const int lane = threadIdx.x & 63;
-  const uint32_t p = blockIdx.x * kBlockPos + (threadIdx.x >> 6) * kWavePos + lane * kLanePos;
-  const bool active = p < L1;                // whole wavefronts: L1 % 512 == 0
-  const uint32_t row = fdiv(p < L1 ? p : 0, kdiv), col = (p < L1 ? p : 0) - row * kdiv.d;
-  uint2 s4[4], s2[2], s1;
-  U4 xv[B];
+  const uint32_t p0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * (uint32_t)(kWavePos * CH) + lane * kLanePos;
+  const bool active = p0 < L1;               // whole wavefronts: L1 % (512 CH) == 0
+  const uint32_t pa = active ? p0 : 0;
+  const uint32_t row = fdiv(pa, kdiv), col0 = pa - row * kdiv.d;   // the CH chunks stay in this row
+  uint2 s4[CH][4], s2[CH][2], s1[CH];
+  U4 xv[CH][B];
   if (active) {
     const int i = lane & 7;
-    const uint32_t g = (i * L1 + (p - i * kLanePos)) / 64;
-    const uint32_t sc = scales[g], zz = zeros[g];
-    if constexpr (SB::has4) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) s4[m] = ld8(packed + sh.base4 + (int64_t)m * L1 + p);
+    for (int c = 0; c < CH; ++c) {
+      const uint32_t p = p0 + c * kWavePos;
+      const uint32_t g = (i * L1 + (p - i * kLanePos)) / 64;
+      const uint32_t sc = scales[g], zz = zeros[g];
+      if constexpr (SB::has4) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) s4[c][m] = ld8(packed + sh.base4 + (int64_t)m * L1 + p);
+      }
+      if constexpr (SB::has2) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) s2[c][m] = ld8(packed + sh.base2 + (int64_t)m * L1 + p);
+      }
+      if constexpr (SB::has1) s1[c] = ld8(packed + sh.base1 + p);
+#pragma unroll
+      for (int b = 0; b < B; ++b) xv[c][b] = ld16(x + (int64_t)min(b, Bn - 1) * ldx + col0 + c * kWavePos);
+      qp_lds[c][threadIdx.x] = (sc << 16) | zz;
     }
-    if constexpr (SB::has2) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m) s2[m] = ld8(packed + sh.base2 + (int64_t)m * L1 + p);
-    }
-    if constexpr (SB::has1) s1 = ld8(packed + sh.base1 + p);
-#pragma unroll
-    for (int b = 0; b < B; ++b) xv[b] = ld16(x + (int64_t)min(b, Bn - 1) * ldx + col);
-    qp_lds[threadIdx.x] = (sc << 16) | zz;
   }
   __syncthreads();
   if (!active) return;                       // wave-uniform, after the only barrier
-  const uint32_t* qpo = &qp_lds[threadIdx.x & ~7u];
+  float acc[B][8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t w = qpo[j];
-    const float s = __uint_as_float(w & 0xFFFF0000u), zp = (float)(w & 0xFFu);
-    uint32_t c[2] = {0u, 0u};
+  for (int b = 0; b < B; ++b)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if constexpr (SB::has4) c[h] |= ((h ? s4[j & 3].y : s4[j & 3].x) >> (4 * (j >> 2))) & 0x0F0F0F0Fu;
-      if constexpr (SB::has2) c[h] |= (((h ? s2[j & 1].y : s2[j & 1].x) >> (2 * (j >> 1))) & 0x03030303u) << SB::off2;
-      if constexpr (SB::has1) c[h] |= (((h ? s1.y : s1.x) >> j) & 0x01010101u) << SB::off1;
+    for (int j = 0; j < 8; ++j) acc[b][j] = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const uint32_t* qpo = &qp_lds[c][threadIdx.x & ~7u];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t w = qpo[j];
+      const float s = __uint_as_float(w & 0xFFFF0000u), zp = (float)(w & 0xFFu);
+      uint32_t cd[2] = {0u, 0u};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (SB::has4) cd[h] |= ((h ? s4[c][j & 3].y : s4[c][j & 3].x) >> (4 * (j >> 2))) & 0x0F0F0F0Fu;
+        if constexpr (SB::has2)
+          cd[h] |= (((h ? s2[c][j & 1].y : s2[c][j & 1].x) >> (2 * (j >> 1))) & 0x03030303u) << SB::off2;
+        if constexpr (SB::has1) cd[h] |= (((h ? s1[c].y : s1[c].x) >> j) & 0x01010101u) << SB::off1;
+      }
+      const float nzs = -(zp * s);
+      float d[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) d[q] = __builtin_fmaf((float)((cd[q >> 2] >> (8 * (q & 3))) & 0xFFu), s, nzs);  // exact
+      ux_bf16x2_t wp[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wp[q] = __builtin_convertvector(ux_f32x2_t{d[2 * q], d[2 * q + 1]}, ux_bf16x2_t);
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const uint32_t xw[4] = {xv[c][b].x, xv[c][b].y, xv[c][b].z, xv[c][b].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[b][j] = __builtin_amdgcn_fdot2_f32_bf16(wp[q], __builtin_bit_cast(ux_bf16x2_t, xw[q]), acc[b][j], false);
+      }
     }
-    const float nzs = -(zp * s);
-    float d[8];
+  }
+  const int j = lane & 7;
+  const uint32_t chunk = col0 / (kWavePos * CH);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) d[q] = __builtin_fmaf((float)((c[q >> 2] >> (8 * (q & 3))) & 0xFFu), s, nzs);   // exact
-    ux_bf16x2_t wp[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) wp[q] = __builtin_convertvector(ux_f32x2_t{d[2 * q], d[2 * q + 1]}, ux_bf16x2_t);
-    const uint32_t R = j * (uint32_t)(N / 8) + row;
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      const uint32_t xw[4] = {xv[b].x, xv[b].y, xv[b].z, xv[b].w};
-      float acc = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_fdot2_f32_bf16(wp[q], __builtin_bit_cast(ux_bf16x2_t, xw[q]), acc, false);
-      acc = ux_wave_sum(acc);
-      if (lane == 0 && b < Bn) part[((int64_t)(col / 512) * Bn + b) * N + R] = acc;
-    }
+  for (int b = 0; b < B; ++b) {
+    const float v = ux_transposed_sum(acc[b], lane);
+    if (lane < 8 && b < Bn) part[((int64_t)chunk * Bn + b) * N + j * (uint32_t)(N / 8) + row] = v;
   }
 }
 
@@ -584,23 +616,33 @@ void launch_uintx_err(int nbits, const void* W, int64_t N, int64_t K, int64_t ld
 
 namespace gwb {
 
-template <int NB, int B>
+template <int NB, int B, int CH>
 static void gemv_tiled(int Bn, const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K,
                        const void* x, int64_t ldx, float* part, hipStream_t st) {
   const uint32_t numel = (uint32_t)(N * K);
-  hipLaunchKernelGGL((uintx_gemv_tiled<NB, B>), dim3(tiles_of(N, K)), dim3(256), 0, st, (const uint8_t*)packed,
+  const unsigned blocks = (unsigned)(((uint64_t)numel / 8 / (kWavePos * CH) + 3) / 4);
+  hipLaunchKernelGGL((uintx_gemv_tiled<NB, B, CH>), dim3(blocks), dim3(256), 0, st, (const uint8_t*)packed,
                      (const uint16_t*)scales, (const uint8_t*)zeros, make_fastdiv((uint32_t)K), numel / 8,
                      shards_of(NB, numel), (int)N, (const uint16_t*)x, ldx, Bn, part);
+}
+
+template <int NB, int CH>
+static void gemv_ch(int B, const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K,
+                    const void* x, int64_t ldx, float* part, hipStream_t st) {
+  if (B == 1) gemv_tiled<NB, 1, CH>(B, packed, scales, zeros, N, K, x, ldx, part, st);
+  else if (B == 2) gemv_tiled<NB, 2, CH>(B, packed, scales, zeros, N, K, x, ldx, part, st);
+  else if (B <= 4) gemv_tiled<NB, 4, CH>(B, packed, scales, zeros, N, K, x, ldx, part, st);
+  else gemv_tiled<NB, 8, CH>(B, packed, scales, zeros, N, K, x, ldx, part, st);
 }
 
 template <int NB>
 static void gemv_nb(int B, const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K,
                     const void* x, int64_t ldx, float* part, hipStream_t st) {
-  if (B == 1) gemv_tiled<NB, 1>(B, packed, scales, zeros, N, K, x, ldx, part, st);
-  else if (B == 2) gemv_tiled<NB, 2>(B, packed, scales, zeros, N, K, x, ldx, part, st);
-  else if (B <= 4) gemv_tiled<NB, 4>(B, packed, scales, zeros, N, K, x, ldx, part, st);
-  else gemv_tiled<NB, 8>(B, packed, scales, zeros, N, K, x, ldx, part, st);
+  if (K % 2048 == 0) gemv_ch<NB, 4>(B, packed, scales, zeros, N, K, x, ldx, part, st);
+  else gemv_ch<NB, 1>(B, packed, scales, zeros, N, K, x, ldx, part, st);
 }
+
+int uintx_gemv_splits(int64_t K) { return (int)(K % 2048 == 0 ? K / 2048 : K / 512); }
 
 bool uintx_gemv_supported(int64_t N, int64_t K) { return N % 8 == 0 && K % 512 == 0; }
 
@@ -615,7 +657,7 @@ void launch_uintx_gemv(int nbits, int B, const void* packed, const void* scales,
     case 6: gemv_nb<6>(B, packed, scales, zeros, N, K, x, ldx, part, st); break;
     default: gemv_nb<7>(B, packed, scales, zeros, N, K, x, ldx, part, st); break;
   }
-  launch_gemv_finalize(part, (int)(K / 512), B, N, y, y_dtype, ldy, st);
+  launch_gemv_finalize(part, uintx_gemv_splits(K), B, N, y, y_dtype, ldy, st);
 }
 
 }  // namespace gwb

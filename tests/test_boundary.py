@@ -217,7 +217,8 @@ def test_gemv_sizes_and_validation():
     sp_u = gwb.make_spec("uintx", 4, 64)
     assert lib.gwb_gemv_workspace(ctypes.byref(sp_u), 64, 128, 1, ctypes.byref(ctypes.c_size_t())) == gwb.E_UNSUPPORTED
     assert lib.gwb_gemv_workspace(ctypes.byref(sp_u), 12, 512, 1, ctypes.byref(ctypes.c_size_t())) == gwb.E_UNSUPPORTED
-    assert ws("uintx", 3072, 12288, 2) == (gwb.OK, 24 * 2 * 3072 * 4)
+    assert ws("uintx", 3072, 12288, 2) == (gwb.OK, 6 * 2 * 3072 * 4)             # 2048-column splits
+    assert ws("uintx", 64, 1536, 1) == (gwb.OK, 3 * 64 * 4)                      # 512-column splits
     sp = gwb.make_spec("gptq_sym", 4, 128)
     def go(x=fake, B=1, ldx=512, y=fake, ydt=gwb.F32, ldy=256, w=0, wsb=0):
         return lib.gwb_gemv(ctypes.byref(sp), ctypes.byref(qt), 256, 512, P(x), B, ldx, P(y), ydt, ldy, P(w), wsb, None)
