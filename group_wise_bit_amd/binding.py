@@ -5,7 +5,8 @@ marshals arguments: torch tensors provide device memory and the current HIP stre
 every step of the method runs in the library's HIP kernels. There is no fallback: if
 the library is missing, importing this package raises.
 
-Formats ("fmt"): "gptq_sym", "gptq_asym", "mxfp4", "uintx".
+Formats ("fmt"): "gptq_sym", "gptq_asym", "mxfp4", "uintx", "mxfp4_page_ties" (MXFP4 with the
+page code's own tie rule; same stored layout).
 """
 from __future__ import annotations
 
@@ -24,8 +25,8 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 OK, E_ARG, E_SHAPE, E_UNSUPPORTED, E_SIZE, E_HIP = 0, -1, -2, -3, -4, -5
-FORMATS = {"gptq_sym": 1, "gptq_asym": 2, "mxfp4": 3, "uintx": 4}
-DEFAULT_GROUP = {"gptq_sym": 128, "gptq_asym": 128, "mxfp4": 32, "uintx": 64}
+FORMATS = {"gptq_sym": 1, "gptq_asym": 2, "mxfp4": 3, "uintx": 4, "mxfp4_page_ties": 5}
+DEFAULT_GROUP = {"gptq_sym": 128, "gptq_asym": 128, "mxfp4": 32, "uintx": 64, "mxfp4_page_ties": 32}
 F32, BF16 = 0, 1
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 
@@ -126,7 +127,7 @@ def _views(fmt: str, N: int, K: int, group: int, sz, codes, scales, zeros, gidx)
         out["qzeros"] = zeros[:sz["zeros"]].view(torch.int32).view(K // group, N // 8)
         if gidx is not None:
             out["g_idx"] = gidx[:sz["g_idx"]].view(torch.int32)
-    elif fmt == "mxfp4":
+    elif fmt.startswith("mxfp4"):
         out["packed"] = codes[:sz["codes"]].view(N, K // 2)
         out["e8m0"] = scales[:sz["scales"]].view(N, K // 32)
     else:
@@ -174,7 +175,7 @@ def quantize(W: torch.Tensor, fmt: str, nbits: int = 4, group: Optional[int] = N
     if out is None:
         dev = W.device
         gidx = _alloc(sz["g_idx"], dev) if (fmt.startswith("gptq") and with_g_idx) else None
-        zeros = _alloc(sz["zeros"], dev) if fmt != "mxfp4" else None      # GPTQ and uintx carry zeros
+        zeros = _alloc(sz["zeros"], dev) if not fmt.startswith("mxfp4") else None   # GPTQ and uintx carry zeros
         out = Quantized(fmt, nbits, group, W.dtype, N, K, _alloc(sz["codes"], dev), _alloc(sz["scales"], dev),
                         zeros, gidx, sz)
     if workspace is None and sz["workspace"]:

@@ -42,6 +42,9 @@ constexpr int64_t kMaxElems = (int64_t)1 << 31;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// the two MXFP4 formats share every stored layout; only quantization differs
+bool is_mxfp4(int32_t f) { return f == GWB_MXFP4 || f == GWB_MXFP4_PAGE_TIES; }
+
 size_t elem_size(int32_t dt) { return dt == GWB_F32 ? 4 : 2; }
 
 int check_spec(const gwb_qspec* sp, int64_t N, int64_t K) {
@@ -63,6 +66,7 @@ int check_spec(const gwb_qspec* sp, int64_t N, int64_t K) {
                              (long long)N);
       return GWB_OK;
     case GWB_MXFP4:
+    case GWB_MXFP4_PAGE_TIES:
       if (sp->nbits != 4) return fail(GWB_E_ARG, "MXFP4 is 4-bit, got nbits=%d", sp->nbits);
       if (sp->group != 32) return fail(GWB_E_UNSUPPORTED, "MXFP4 blocks are 32 weights, got group %d", sp->group);
       if (K % 32) return fail(GWB_E_SHAPE, "K=%lld not divisible by 32", (long long)K);
@@ -91,7 +95,8 @@ size_t uintx_packed_bytes(int nbits, int64_t numel) {
 
 unsigned err_blocks(const gwb_qspec* sp, int64_t N, int64_t K) {
   switch (sp->format) {
-    case GWB_MXFP4: return gwb::mxfp4_err_blocks(N, K);
+    case GWB_MXFP4:
+    case GWB_MXFP4_PAGE_TIES: return gwb::mxfp4_err_blocks(N, K);
     case GWB_UINTX: return gwb::uintx_err_blocks(N, K);
     default: return gwb::gptq_err_blocks(sp->group, N, K);
   }
@@ -109,6 +114,7 @@ gwb_sizes sizes_of(const gwb_qspec* sp, int64_t N, int64_t K) {
       s.g_idx = (size_t)(K * 4);
       break;
     case GWB_MXFP4:
+    case GWB_MXFP4_PAGE_TIES:
       s.codes = (size_t)(N * K / 2);
       s.scales = (size_t)(N * K / 32);
       break;
@@ -141,7 +147,7 @@ int check_weight(const gwb_qspec* sp, const void* W, int64_t K, int64_t ldw) {
 int check_tensors(const gwb_qspec* sp, const gwb_qtensors* q) {
   if (!q) return fail(GWB_E_ARG, "tensors struct is NULL");
   if (!q->codes || !q->scales) return fail(GWB_E_ARG, "codes and scales are required");
-  if (sp->format != GWB_MXFP4 && !q->zeros) return fail(GWB_E_ARG, "zeros is required for this format");
+  if (!is_mxfp4(sp->format) && !q->zeros) return fail(GWB_E_ARG, "zeros is required for this format");
   if (!aligned16(q->codes) || !aligned16(q->scales) || (q->zeros && !aligned16(q->zeros)))
     return fail(GWB_E_UNSUPPORTED, "quantized tensors must be 16-byte aligned");
   return GWB_OK;
@@ -178,7 +184,9 @@ int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int
                              out->scales, out->zeros, out->g_idx, st);
       break;
     case GWB_MXFP4:
-      gwb::launch_mxfp4_quant(W, spec->w_dtype, N, K, ldw, out->codes, out->scales, st);
+    case GWB_MXFP4_PAGE_TIES:
+      gwb::launch_mxfp4_quant(spec->format == GWB_MXFP4_PAGE_TIES, W, spec->w_dtype, N, K, ldw, out->codes,
+                              out->scales, st);
       break;
     default:
       gwb::launch_uintx_quant(spec->nbits, W, N, K, ldw, out->codes, out->scales, out->zeros, workspace, st);
@@ -206,6 +214,7 @@ int gwb_dequantize(const gwb_qspec* spec, const gwb_qtensors* in, int64_t N, int
                                out, out_dtype, ldo, st);
       break;
     case GWB_MXFP4:
+    case GWB_MXFP4_PAGE_TIES:
       gwb::launch_mxfp4_dequant(in->codes, in->scales, N, K, out, out_dtype, ldo, st);
       break;
     default:
@@ -235,6 +244,7 @@ int gwb_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t 
                            in->scales, in->zeros, part, st);
       break;
     case GWB_MXFP4:
+    case GWB_MXFP4_PAGE_TIES:
       gwb::launch_mxfp4_err(W, spec->w_dtype, N, K, ldw, in->codes, in->scales, part, st);
       break;
     default:
@@ -351,7 +361,7 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
     return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (need && !aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
-  if (spec->format == GWB_MXFP4)
+  if (is_mxfp4(spec->format))
     gwb::launch_mxfp4_gemv((int)B, w->codes, w->scales, N, K, x, ldx, y, y_dtype, ldy, st);
   else if (spec->format == GWB_UINTX)
     gwb::launch_uintx_gemv(spec->nbits, (int)B, w->codes, w->scales, w->zeros, N, K, x, ldx, y, y_dtype, ldy,

@@ -29,7 +29,7 @@ inline unsigned err_blocks_for(uint64_t units) {
 }
 
 // ---- MXFP4 (mxfp4.hip)
-void launch_mxfp4_quant(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
+void launch_mxfp4_quant(bool page_ties, const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
                         void* packed, void* e8m0, hipStream_t st);
 void launch_mxfp4_dequant(const void* packed, const void* e8m0, int64_t N, int64_t K, void* out,
                           int32_t out_dtype, int64_t ldo, hipStream_t st);

@@ -34,17 +34,39 @@ __device__ __forceinline__ T* unit_ptr(T* base, int64_t ld, uint32_t u, FastDiv 
   return base + (int64_t)n * ld + 8 * (u - n * upr.d);
 }
 
+// The page's own tie rule (its code takes the first tied index, then rounds that index
+// down to even) differs from round-half-to-even at three magnitudes only: |x| / 2^e =
+// 0.75, 1.75 and 3.5 go to codes 0, 2 and 4 instead of 2, 4 and 6. Returns what to
+// subtract from the word (2 in each such nibble; the magnitude bits never borrow from
+// the sign bit since the magnitude is at least 2).
 template <typename TIn>
+__device__ __forceinline__ uint32_t page_tie_fix(const Raw8<TIn>& r, uint32_t e8) {
+  float x[8];
+  to_f32(r, x);
+  const int e = (int)e8 - 127;
+  const float t1 = ldexpf(0.75f, e), t2 = ldexpf(1.75f, e), t3 = ldexpf(3.5f, e);
+  uint32_t corr = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float a = fabsf(x[i]);
+    if (a == t1 || a == t2 || a == t3) corr |= 2u << (4 * i);
+  }
+  return corr;
+}
+
+template <bool LIT, typename TIn>
 __device__ __forceinline__ void quant_unit(const Raw8<TIn>& r, uint32_t u, uint32_t* __restrict__ packed,
                                            uint8_t* __restrict__ e8m0) {
   const uint32_t e8 = mx_e8m0_bits(quad_max_u(absmax_bits(r)));
-  packed[u] = pack_unit(r, mx_scale_operand(e8));
+  uint32_t w = pack_unit(r, mx_scale_operand(e8));
+  if constexpr (LIT) w -= page_tie_fix(r, e8);
+  packed[u] = w;
   if ((u & 3u) == 0) e8m0[u >> 2] = (uint8_t)e8;
 }
 
 // units = N*K/8 is a multiple of 4 and every stride is too, so the four lanes of a
 // block always take the same branch of each loop (the DPP step needs all four).
-template <bool CONTIG, typename TIn>
+template <bool CONTIG, bool LIT, typename TIn>
 __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const TIn* __restrict__ W, int64_t ldw,
                                                           uint32_t units, FastDiv upr,
                                                           uint32_t* __restrict__ packed,
@@ -56,12 +78,12 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const TIn* __restrict_
     const Raw8<TIn> r1 = load_raw8(unit_ptr<CONTIG>(W, ldw, u + stride, upr));
     const Raw8<TIn> r2 = load_raw8(unit_ptr<CONTIG>(W, ldw, u + 2 * stride, upr));
     const Raw8<TIn> r3 = load_raw8(unit_ptr<CONTIG>(W, ldw, u + 3 * stride, upr));
-    quant_unit(r0, u, packed, e8m0);
-    quant_unit(r1, u + stride, packed, e8m0);
-    quant_unit(r2, u + 2 * stride, packed, e8m0);
-    quant_unit(r3, u + 3 * stride, packed, e8m0);
+    quant_unit<LIT>(r0, u, packed, e8m0);
+    quant_unit<LIT>(r1, u + stride, packed, e8m0);
+    quant_unit<LIT>(r2, u + 2 * stride, packed, e8m0);
+    quant_unit<LIT>(r3, u + 3 * stride, packed, e8m0);
   }
-  for (; u < units; u += stride) quant_unit(load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr)), u, packed, e8m0);
+  for (; u < units; u += stride) quant_unit<LIT>(load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr)), u, packed, e8m0);
 }
 
 // Unpack + dequantize. SINK == kStore writes out[n, k]; SINK == kErr takes W at the
@@ -117,19 +139,27 @@ __global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint32_t* __re
 }
 
 // ------------------------------------------------------------------ launchers
-void launch_mxfp4_quant(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
-                        void* packed, void* e8m0, hipStream_t st) {
+template <bool LIT>
+static void quant_lit(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw, void* packed, void* e8m0,
+                      hipStream_t st) {
   const uint32_t units = (uint32_t)(N * K / 8);
   const FastDiv upr = make_fastdiv((uint32_t)(K / 8));
   const unsigned grid = stream_blocks(units);
   const bool contig = ldw == K;
   if (w_dtype == kBF16)
-    hipLaunchKernelGGL((contig ? mxfp4_quant_kernel<true, uint16_t> : mxfp4_quant_kernel<false, uint16_t>),
+    hipLaunchKernelGGL((contig ? mxfp4_quant_kernel<true, LIT, uint16_t> : mxfp4_quant_kernel<false, LIT, uint16_t>),
                        dim3(grid), dim3(256), 0, st, (const uint16_t*)W, ldw, units, upr, (uint32_t*)packed,
                        (uint8_t*)e8m0);
   else
-    hipLaunchKernelGGL((contig ? mxfp4_quant_kernel<true, float> : mxfp4_quant_kernel<false, float>), dim3(grid),
-                       dim3(256), 0, st, (const float*)W, ldw, units, upr, (uint32_t*)packed, (uint8_t*)e8m0);
+    hipLaunchKernelGGL((contig ? mxfp4_quant_kernel<true, LIT, float> : mxfp4_quant_kernel<false, LIT, float>),
+                       dim3(grid), dim3(256), 0, st, (const float*)W, ldw, units, upr, (uint32_t*)packed,
+                       (uint8_t*)e8m0);
+}
+
+void launch_mxfp4_quant(bool page_ties, const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
+                        void* packed, void* e8m0, hipStream_t st) {
+  if (page_ties) quant_lit<true>(W, w_dtype, N, K, ldw, packed, e8m0, st);
+  else quant_lit<false>(W, w_dtype, N, K, ldw, packed, e8m0, st);
 }
 
 void launch_mxfp4_dequant(const void* packed, const void* e8m0, int64_t N, int64_t K, void* out,

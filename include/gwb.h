@@ -12,6 +12,10 @@
  *                  e2m1 codes (round half to even), an E8M0 exponent per 32 weights.
  *   GWB_UINTX      page uintx_quant.py, UIntXQuantizer: affine uint2..uint7 with
  *                  preserve_zero, arithmetic in bfloat16, planar power-of-two shards.
+ *   GWB_MXFP4_PAGE_TIES  MXFP4 with the tie rule of the page's code instead of its
+ *                  stated round-half-to-even: the first tied index, rounded down to even
+ *                  (|x| / 2^e = 0.75, 1.75, 3.5 give 0, 1, 2 rather than 1, 2, 4). Same
+ *                  stored layout; dequantization, SNR and the GEMV are MXFP4's.
  *
  * Conventions for every entry point:
  *   - Pointers named d_* and every tensor pointer are DEVICE pointers owned by the
@@ -42,7 +46,7 @@ typedef enum {
   GWB_E_HIP = -5           /* a HIP launch failed; gwb_last_error() names it */
 } gwb_status;
 
-typedef enum { GWB_GPTQ_SYM = 1, GWB_GPTQ_ASYM = 2, GWB_MXFP4 = 3, GWB_UINTX = 4 } gwb_format;
+typedef enum { GWB_GPTQ_SYM = 1, GWB_GPTQ_ASYM = 2, GWB_MXFP4 = 3, GWB_UINTX = 4, GWB_MXFP4_PAGE_TIES = 5 } gwb_format;
 typedef enum { GWB_F32 = 0, GWB_BF16 = 1 } gwb_dtype;
 
 /* What to quantize to.

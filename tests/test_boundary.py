@@ -229,3 +229,12 @@ def test_gemv_sizes_and_validation():
     assert go(x=fake + 4) == gwb.E_UNSUPPORTED
     assert go() == gwb.E_SIZE                                                 # K-split partials needed
     assert go(w=fake + 8, wsb=1 << 20) == gwb.E_UNSUPPORTED
+
+
+def test_page_ties_format_shares_mxfp4_sizes():
+    for N, K in ((34816, 5120), (3, 96)):
+        a = gwb.query_sizes("mxfp4", N, K, 4, 32)
+        b = gwb.query_sizes("mxfp4_page_ties", N, K, 4, 32)
+        assert a == b
+    sp = gwb.make_spec("mxfp4_page_ties", 4, 32)
+    assert lib.gwb_query_sizes(ctypes.byref(sp), 8, 48, ctypes.byref(gwb.Sizes())) == gwb.E_SHAPE

@@ -104,6 +104,24 @@ def test_mxfp4_parity(n, k, kind, dtype):
     _check_snr(W, Wd, q, ref)
 
 
+@pytest.mark.parametrize("n,k,kind", [(40, 256, "adv"), (96, 640, "adv"), (257, 1024, "normal")])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_mxfp4_page_ties_parity(n, k, kind, dtype):
+    """The page code's tie rule (first tied index, rounded down to even) as its own format:
+    codes against the oracle's page_literal rule; everything stored is MXFP4's layout."""
+    W = _weight(kind, n, k, seed=150 + n, dtype=dtype)
+    Wd = W.to(DEV)
+    q = gwb.quantize(Wd, "mxfp4_page_ties")
+    packed, e8 = omx.quantize(W.float().numpy(), ties="page_literal")
+    assert np.array_equal(_np(q["packed"]), packed)
+    assert np.array_equal(_np(q["e8m0"]), e8)
+    ref = omx.dequantize(packed, e8, k)
+    _check_dequant(q, ref)
+    _check_snr(W, Wd, q, ref)
+    if kind == "adv":      # the adversarial spans hold exact ties: the two rules must differ there
+        assert not np.array_equal(_np(q["packed"]), omx.quantize(W.float().numpy())[0])
+
+
 def test_mxfp4_strided_rows():
     W = workloads.mxfp4_weight(70, 320, seed=7)
     big = torch.zeros(70, 384, dtype=torch.bfloat16)
