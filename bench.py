@@ -153,7 +153,7 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
     """Paths next to the hot path, timed on their own after the step (not part of
     value): the AWQ fold of the gate_up weight (columns * s) straight to MXFP4, the same
     fold also writing the folded bf16 weight, and the decode GEMV reading a packed
-    131072 x 2048 lm_head (GPTQ sym g128, MXFP4) for one activation row."""
+    131072 x 2048 lm_head (GPTQ sym g128, MXFP4, uintx4 g64) for one activation row."""
     out = []
     s = torch.from_numpy(gwb.awq_scales_host(ad.cpu(), (0.5,))[0].numpy()).to(dev)
     mx = gwb.fold_mxfp4(Wd, s, "mul", want_folded=False)["mxfp4"]
@@ -175,7 +175,9 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
     # Infinity Cache
     qg = [gwb.quantize(head, "gptq_sym", group=128) for _ in range(3)]
     qm = [gwb.quantize(head, "mxfp4") for _ in range(3)]
+    qu = [gwb.quantize(head, "uintx", nbits=4) for _ in range(3)]
     del head
+    wsu = torch.empty(gwb.gemv_workspace_bytes(qu[0], 1), dtype=torch.uint8, device=dev)
     wsg = torch.empty(gwb.gemv_workspace_bytes(qg[0], 1), dtype=torch.uint8, device=dev)
     hk = HN * HK
 
@@ -191,6 +193,8 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
          cycle([gwb.prepare_gemv(q, xh, yh, wsg) for q in qg])),
         ("gemv.mxfp4.lm_head_b1", hk / 2 + hk / 32 + 2 * HK + 4 * HN,
          cycle([gwb.prepare_gemv(q, xh, yh, None) for q in qm])),
+        ("gemv.uintx4_g64.lm_head_b1", hk / 2 + hk / 64 * 3 + 2 * HK + 4 * HN,
+         cycle([gwb.prepare_gemv(q, xh, yh, wsu) for q in qu])),
     ]
     for name, abytes, fn in cases + gemv_cases:
         us = _time_op(fn)
