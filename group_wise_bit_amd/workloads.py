@@ -69,16 +69,16 @@ def mxfp4_weight(n: int = 34816, k: int = 5120, seed: int = 3,
 
 
 def uintx_weight(n: int = 3072, k: int = 12288, seed: int = 4,
-                 outlier_frac: float = 0.001) -> torch.Tensor:
-    """bf16 [n, k], N(0, 0.02) with round(outlier_frac * n * k) distinct entries
-    replaced by U(-0.5, 0.5)."""
+                 outlier_frac: float = 0.001, dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """[n, k] (bf16 by default), N(0, 0.02) with round(outlier_frac * n * k) distinct
+    entries replaced by U(-0.5, 0.5)."""
     rng = _rng(seed)
     x = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.02)
     m = int(round(outlier_frac * n * k))
     if m:
         idx = rng.choice(n * k, size=m, replace=False)
         x.reshape(-1)[idx] = rng.uniform(-0.5, 0.5, size=m).astype(np.float32)
-    return _finish(x, torch.bfloat16)
+    return _finish(x, dtype)
 
 
 def awq_activation_stat(k: int = 5120, seed: int = 5) -> torch.Tensor:
@@ -101,9 +101,13 @@ def adversarial_weight(n: int, k: int, seed: int = 6,
     whose magnitude maximum is an exact power of two, spans made of multiples of
     power-of-two half steps (exact ties for every rounding grid used here),
     bfloat16/float32 subnormals, maxima one float32 ulp below a power of two, very
-    large and very small magnitudes, a lone outlier, and all-negative spans."""
+    large and very small magnitudes, a lone outlier, and all-negative spans. For
+    float16 the very large, subnormal and very small kinds use float16's own range
+    (2**12 scale, multiples of 2**-24, 2**-24..2**-15), with the same random draws."""
     assert k % 128 == 0
     rng = _rng(seed)
+    half = dtype == torch.float16
+    huge_e, sub_e, tiny_lo, tiny_hi = (12, -24, -24, -14) if half else (100, -133, -126, -100)
     x = np.empty((n, k), dtype=np.float32)
     spans = x.reshape(n, k // 128, 128)
     kinds = rng.integers(0, len(_ADV_KINDS), size=(n, k // 128))
@@ -126,14 +130,14 @@ def adversarial_weight(n: int, k: int, seed: int = 6,
                 # integer multiples of 2**(e-4): many exact midpoints of coarse grids
                 v = (rng.integers(-96, 97, 128).astype(np.float32) * np.float32(2.0 ** (e - 4)))
             elif kind == "subnormal":
-                v = (rng.integers(-127, 128, 128).astype(np.float32) * np.float32(2.0 ** -133))
+                v = (rng.integers(-127, 128, 128).astype(np.float32) * np.float32(2.0 ** sub_e))
             elif kind == "below_pow2":
                 v = (rng.uniform(-1, 1, 128) * 2.0 ** e).astype(np.float32)
                 v[rng.integers(0, 128)] = np.nextafter(np.float32(2.0 ** e), np.float32(0))
             elif kind == "huge":
-                v = (rng.standard_normal(128) * 2.0 ** 100).astype(np.float32)
+                v = (rng.standard_normal(128) * 2.0 ** huge_e).astype(np.float32)
             elif kind == "tiny_mixed":
-                v = (rng.standard_normal(128) * 2.0 ** rng.integers(-126, -100, 128)).astype(np.float32)
+                v = (rng.standard_normal(128) * 2.0 ** rng.integers(tiny_lo, tiny_hi, 128)).astype(np.float32)
             elif kind == "sparse_outlier":
                 v = (rng.standard_normal(128) * 2.0 ** (e - 8)).astype(np.float32)
                 v[rng.integers(0, 128)] = np.float32(rng.choice([-1.0, 1.0]) * 2.0 ** e * 3.1)

@@ -2,10 +2,21 @@
 
 Follows page uintx_quant.py (module docstring; _pack_shard, _unpack_shard, pack_uintx,
 unpack_uintx; UIntXQuantizer.can_quantize, _quantize_impl, _dequantize_native).
-The weight is bfloat16 and every arithmetic op is a bfloat16 tensor op, i.e. one
-float32 op whose result is rounded to bfloat16 (bf16_round below).
+The arithmetic runs in the weight's own dtype (the page's docstring: usually
+bfloat16): every op is one float32 op whose result is rounded to that dtype — bfloat16
+or float16 (RNE, as torch's half ops compute in float32 and round) — or a plain float32
+op for float32 weights. The scale is stored as the bytes of that dtype.
+Reading for float32 weights: `scale / qmax` is the division the page writes (IEEE);
+torch's GPU path multiplies by the float32 reciprocal instead, which changes the last
+bit of about a third of the scales. For bfloat16 and float16 the two agree after the
+rounding for every value (exhaustive check in the pins).
+Reading for float16 weights: a group whose scale is below about 2**-16 has an infinite
+float16 reciprocal, so w * inv is +inf, -inf or (for a zero weight) NaN; the clamp sends
+the infinities to qmax and 0, and the NaN becomes code 0, which is what torch's float to
+uint8 conversion returns for it on the CPU.
 
-Step list per group of G (64) consecutive weights along K, qmax = 2**nbits - 1:
+Step list per group of G (64 by default; 32 and 128 too) consecutive weights along K,
+qmax = 2**nbits - 1, bf = rounding to the weight dtype:
   min, max over the group (exact)
   mn = min(min, 0), mx = max(max, 0)                    (preserve_zero)
   scale = bf(bf(mx - mn) / qmax); scale = max(scale, 2**-23)
@@ -21,7 +32,26 @@ import numpy as np
 
 from ._fp import bf16_round as bf, f32, is_bf16
 
-EPS = np.float32(np.finfo(np.float32).eps)   # 2**-23, exactly a bfloat16 too
+EPS = np.float32(np.finfo(np.float32).eps)   # 2**-23, exactly a bfloat16 and a float16 too
+DTYPES = ("bf16", "f16", "f32")
+SCALE_BYTES = {"bf16": 2, "f16": 2, "f32": 4}
+
+
+def f16(x) -> np.ndarray:
+    """Round float32 values to float16 (RNE, gradual underflow, overflow to inf), back
+    as float32."""
+    return np.asarray(x, np.float32).astype(np.float16).astype(np.float32)
+
+
+def rounder(dtype: str):
+    return {"bf16": bf, "f16": f16, "f32": lambda v: np.asarray(v, np.float32)}[dtype]
+
+
+def is_dtype(x, dtype: str) -> bool:
+    x = np.asarray(x, np.float32)
+    return bool(np.array_equal(rounder(dtype)(x), x) or np.isnan(x).any())
+
+
 SHARD_WIDTHS = (8, 4, 2, 1)                  # the page's shard order
 
 
@@ -102,13 +132,14 @@ def unpack(packed, nbits: int, numel: int) -> np.ndarray:
     return out
 
 
-def quantize(w, nbits: int, group: int = 64):
-    """bf16 [N, K] (as float32 values) -> dict(packed uint8 flat, scale bf16 as float32
-    [N, K/G], scale_bytes uint8 [N, 2K/G] little-endian, zero_point uint8 [N, K/G],
-    codes uint8 [N, K])."""
+def quantize(w, nbits: int, group: int = 64, dtype: str = "bf16"):
+    """[N, K] weights of `dtype` (as float32 values) -> dict(packed uint8 flat, scale as
+    float32 [N, K/G], scale_bytes uint8 [N, bytes * K/G] little-endian, zero_point uint8
+    [N, K/G], codes uint8 [N, K])."""
     x = f32(w)
+    rnd = rounder(dtype)
     assert can_quantize(nbits, x.shape, group), (nbits, x.shape, group)
-    assert is_bf16(x), "uintx arithmetic is specified for bfloat16 weights"
+    assert is_dtype(x, dtype), f"weights are not {dtype} values"
     qmin, qmax = 0, (1 << nbits) - 1
     n, k = x.shape
     wv = x.reshape(n, k // group, group)
@@ -116,39 +147,61 @@ def quantize(w, nbits: int, group: int = 64):
     mx = wv.max(axis=2)
     mn_neg = np.minimum(mn, np.float32(0.0))
     mx_pos = np.maximum(mx, np.float32(0.0))
-    scale = bf(bf(mx_pos - mn_neg) / np.float32(qmax - qmin))
-    scale = np.maximum(scale, EPS)
-    zp = bf(np.float32(qmin) - np.rint(bf(mn_neg / scale)))
-    zp = np.clip(zp, qmin, qmax).astype(np.int32)
-    inv = bf(np.float32(1.0) / scale)
-    t = bf(wv * inv[:, :, None])
-    q = bf(np.rint(t) + zp[:, :, None].astype(np.float32))
-    q = np.clip(q, qmin, qmax).astype(np.uint8).reshape(n, k)
-    sbits = (scale.view(np.uint32) >> 16).astype(np.uint16)
+    with np.errstate(over="ignore"):
+        scale = rnd(rnd(mx_pos - mn_neg) / np.float32(qmax - qmin))
+        scale = np.maximum(scale, EPS)
+        zp = rnd(np.float32(qmin) - np.rint(rnd(mn_neg / scale)))
+        zp = np.clip(zp, qmin, qmax).astype(np.int32)
+        inv = rnd(np.float32(1.0) / scale)
+    with np.errstate(invalid="ignore", over="ignore"):
+        t = rnd(wv * inv[:, :, None])
+        q = rnd(np.rint(t) + zp[:, :, None].astype(np.float32))
+        q = np.clip(q, qmin, qmax)
+    q = np.where(np.isnan(q), np.float32(0.0), q)     # 0 * inf (float16 only)
+    q = q.astype(np.uint8).reshape(n, k)
     return dict(
         packed=pack(q, nbits),
         scale=scale,
-        scale_bytes=np.ascontiguousarray(sbits.astype("<u2")).view(np.uint8).reshape(n, 2 * (k // group)),
+        scale_bytes=scale_to_bytes(scale, dtype),
         zero_point=zp.astype(np.uint8),
         codes=q,
     )
 
 
-def scale_from_bytes(scale_bytes, n: int, groups: int) -> np.ndarray:
-    u = np.ascontiguousarray(scale_bytes, np.uint8).view("<u2").reshape(n, groups)
-    return (u.astype(np.uint32) << 16).view(np.float32)
+def scale_to_bytes(scale, dtype: str = "bf16") -> np.ndarray:
+    scale = np.ascontiguousarray(scale, np.float32)
+    n = scale.shape[0]
+    if dtype == "bf16":
+        u = (scale.view(np.uint32) >> 16).astype("<u2")
+    elif dtype == "f16":
+        u = scale.astype("<f2")
+    else:
+        u = scale.astype("<f4")
+    return np.ascontiguousarray(u).view(np.uint8).reshape(n, -1)
 
 
-def dequantize(packed, scale_bytes, zero_point, nbits: int, n: int, k: int, group: int = 64) -> np.ndarray:
-    """-> bf16 values as float32 [N, K]: bf(bf(q - zp) * scale)."""
+def scale_from_bytes(scale_bytes, n: int, groups: int, dtype: str = "bf16") -> np.ndarray:
+    b = np.ascontiguousarray(scale_bytes, np.uint8)
+    if dtype == "bf16":
+        u = b.view("<u2").reshape(n, groups)
+        return (u.astype(np.uint32) << 16).view(np.float32)
+    if dtype == "f16":
+        return b.view("<f2").reshape(n, groups).astype(np.float32)
+    return b.view("<f4").reshape(n, groups).astype(np.float32)
+
+
+def dequantize(packed, scale_bytes, zero_point, nbits: int, n: int, k: int, group: int = 64,
+               dtype: str = "bf16") -> np.ndarray:
+    """-> values of `dtype` as float32 [N, K]: rnd(rnd(q - zp) * scale)."""
+    rnd = rounder(dtype)
     q = unpack(packed, nbits, n * k).reshape(n, k // group, group).astype(np.float32)
-    scale = scale_from_bytes(scale_bytes, n, k // group)
+    scale = scale_from_bytes(scale_bytes, n, k // group, dtype)
     zp = np.asarray(zero_point, np.uint8).reshape(n, k // group).astype(np.float32)
-    dq = bf(q - zp[:, :, None])
-    dq = bf(dq * scale[:, :, None])
+    dq = rnd(q - zp[:, :, None])
+    dq = rnd(dq * scale[:, :, None])
     return dq.reshape(n, k)
 
 
-def bits_per_weight(nbits: int, group: int = 64) -> float:
-    """nbits per code plus a 16-bit scale and an 8-bit zero point per group."""
-    return nbits + (16 + 8) / group
+def bits_per_weight(nbits: int, group: int = 64, dtype: str = "bf16") -> float:
+    """nbits per code plus a scale of the weight dtype and an 8-bit zero point per group."""
+    return nbits + (8 * SCALE_BYTES[dtype] + 8) / group

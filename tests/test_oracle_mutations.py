@@ -86,6 +86,17 @@ def test_uintx_dropped_bf16_rounding_caught(monkeypatch):
     _fails(tu.test_quantize_bruteforce_exact, 5)
 
 
+def test_uintx_float16_rounded_as_bf16_caught(monkeypatch):
+    monkeypatch.setattr(ux, "f16", ux.bf)
+    _fails(tu.test_quantize_bruteforce_exact_other_dtypes, "f16", 4, 64)
+
+
+def test_uintx_float32_rounded_as_bf16_caught(monkeypatch):
+    orig = ux.rounder
+    monkeypatch.setattr(ux, "rounder", lambda d: orig("bf16") if d == "f32" else orig(d))
+    _fails(tu.test_quantize_bruteforce_exact_other_dtypes, "f32", 2, 32)
+
+
 def test_awq_wrong_weighting_caught(monkeypatch):
     orig = awq.clamp_stat
     monkeypatch.setattr(awq, "clamp_stat", lambda a: (orig(a) / orig(a).mean()).astype(np.float32))
