@@ -27,8 +27,8 @@ lib = ctypes.CDLL(LIB_PATH)
 OK, E_ARG, E_SHAPE, E_UNSUPPORTED, E_SIZE, E_HIP = 0, -1, -2, -3, -4, -5
 FORMATS = {"gptq_sym": 1, "gptq_asym": 2, "mxfp4": 3, "uintx": 4, "mxfp4_page_ties": 5}
 DEFAULT_GROUP = {"gptq_sym": 128, "gptq_asym": 128, "mxfp4": 32, "uintx": 64, "mxfp4_page_ties": 32}
-F32, BF16 = 0, 1
-_DT = {torch.float32: F32, torch.bfloat16: BF16}
+F32, BF16, F16 = 0, 1, 2
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
 
 class QSpec(ctypes.Structure):
@@ -118,7 +118,7 @@ def _alloc(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
-def _views(fmt: str, N: int, K: int, group: int, sz, codes, scales, zeros, gidx):
+def _views(fmt: str, N: int, K: int, group: int, w_dtype, sz, codes, scales, zeros, gidx):
     """Typed views of the raw byte buffers (the layouts of gwb_qtensors)."""
     out = {}
     if fmt.startswith("gptq"):
@@ -132,7 +132,8 @@ def _views(fmt: str, N: int, K: int, group: int, sz, codes, scales, zeros, gidx)
         out["e8m0"] = scales[:sz["scales"]].view(N, K // 32)
     else:
         out["packed"] = codes[:sz["codes"]]
-        out["scale_bytes"] = scales[:sz["scales"]].view(N, 2 * (K // group))
+        esize = 4 if w_dtype == torch.float32 else 2            # the scale has the weight dtype
+        out["scale_bytes"] = scales[:sz["scales"]].view(N, esize * (K // group))
         out["zero_point"] = zeros[:sz["zeros"]].view(N, K // group)
     return out
 
@@ -144,7 +145,7 @@ class Quantized:
     def __init__(self, fmt, nbits, group, w_dtype, N, K, codes, scales, zeros, gidx, sizes):
         self.fmt, self.nbits, self.group, self.w_dtype, self.N, self.K = fmt, nbits, group, w_dtype, N, K
         self.codes, self.scales, self.zeros, self.gidx, self.sizes = codes, scales, zeros, gidx, sizes
-        self.views = _views(fmt, N, K, group, sizes, codes, scales, zeros, gidx)
+        self.views = _views(fmt, N, K, group, w_dtype, sizes, codes, scales, zeros, gidx)
 
     def spec(self) -> QSpec:
         return make_spec(self.fmt, self.nbits, self.group, self.w_dtype)
@@ -158,7 +159,7 @@ class Quantized:
 
 def _weight_args(W: torch.Tensor):
     if W.dim() != 2 or W.dtype not in _DT or not W.is_cuda:
-        raise ValueError("W must be a 2-D float32 or bfloat16 CUDA tensor")
+        raise ValueError("W must be a 2-D float32, bfloat16 or float16 CUDA tensor")
     if W.stride(1) != 1:
         raise ValueError("W must have unit stride along K")
     return W.shape[0], W.shape[1], W.stride(0)
@@ -187,12 +188,15 @@ def quantize(W: torch.Tensor, fmt: str, nbits: int = 4, group: Optional[int] = N
     return out
 
 
-def dequantize(q: Quantized, out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Unpack+dequantize to [N, K] of out_dtype (bf16 or f32)."""
+def dequantize(q: Quantized, out_dtype=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Unpack+dequantize to [N, K] of out_dtype: float32 or bfloat16; uintx: float32 or
+    the weight dtype. Default: bfloat16, uintx the weight dtype."""
+    if out_dtype is None:
+        out_dtype = q.w_dtype if q.fmt == "uintx" else torch.bfloat16
     if out is None:
         out = torch.empty(q.N, q.K, dtype=out_dtype, device=q.codes.device)
     if out.dtype not in _DT or out.stride(1) != 1:
-        raise ValueError("out must be float32 or bfloat16 with unit stride along K")
+        raise ValueError("out must be float32, bfloat16 or float16 with unit stride along K")
     sp, qt = q.spec(), q.qtensors()
     _check(lib.gwb_dequantize(ctypes.byref(sp), ctypes.byref(qt), q.N, q.K, _ptr(out), _DT[out.dtype],
                               out.stride(0), None, 0, _stream()))
@@ -371,7 +375,7 @@ def prepare_quantize(W: torch.Tensor, q: Quantized, workspace: Optional[torch.Te
 
 def prepare_dequantize(q: Quantized, out: torch.Tensor) -> Prepared:
     if out.dtype not in _DT or out.stride(1) != 1 or tuple(out.shape) != (q.N, q.K):
-        raise ValueError("out must be [N, K] float32 or bfloat16 with unit stride along K")
+        raise ValueError("out must be [N, K] float32, bfloat16 or float16 with unit stride along K")
     sp, qt = q.spec(), q.qtensors()
     return Prepared(lib.gwb_dequantize, (ctypes.byref(sp), ctypes.byref(qt), q.N, q.K, _ptr(out), _DT[out.dtype],
                                          out.stride(0), None, 0, _stream()), (sp, qt, q, out))

@@ -50,8 +50,10 @@ size_t elem_size(int32_t dt) { return dt == GWB_F32 ? 4 : 2; }
 int check_spec(const gwb_qspec* sp, int64_t N, int64_t K) {
   if (!sp) return fail(GWB_E_ARG, "spec is NULL");
   if (N < 0 || K < 0) return fail(GWB_E_ARG, "negative shape N=%lld K=%lld", (long long)N, (long long)K);
-  if (sp->w_dtype != GWB_F32 && sp->w_dtype != GWB_BF16)
+  if (sp->w_dtype != GWB_F32 && sp->w_dtype != GWB_BF16 && sp->w_dtype != GWB_F16)
     return fail(GWB_E_ARG, "unknown w_dtype %d", sp->w_dtype);
+  if (sp->w_dtype == GWB_F16 && sp->format != GWB_UINTX)
+    return fail(GWB_E_UNSUPPORTED, "float16 weights are provided for UINTX only");
   if (N > 0 && K > 0 && (N >= kMaxElems || K >= kMaxElems || N * K >= kMaxElems))
     return fail(GWB_E_UNSUPPORTED, "N*K = %lld exceeds 2^31 elements", (long long)(N * K));
   switch (sp->format) {
@@ -75,9 +77,9 @@ int check_spec(const gwb_qspec* sp, int64_t N, int64_t K) {
       if (sp->nbits == 8)
         return fail(GWB_E_UNSUPPORTED, "uint8 is refused: it was always left unquantized");
       if (sp->nbits < 2 || sp->nbits > 8) return fail(GWB_E_ARG, "uintx nbits must be 2..7, got %d", sp->nbits);
-      if (sp->group != 64) return fail(GWB_E_UNSUPPORTED, "uintx group %d not provided (64)", sp->group);
-      if (sp->w_dtype != GWB_BF16)
-        return fail(GWB_E_UNSUPPORTED, "uintx arithmetic is bfloat16; w_dtype must be GWB_BF16");
+      if (sp->group <= 0) return fail(GWB_E_ARG, "group must be positive, got %d", sp->group);
+      if (sp->group != 32 && sp->group != 64 && sp->group != 128)
+        return fail(GWB_E_UNSUPPORTED, "uintx group %d not provided (32, 64, 128)", sp->group);
       if (K % sp->group) return fail(GWB_E_SHAPE, "K=%lld not divisible by group %d", (long long)K, sp->group);
       return GWB_OK;
     default:
@@ -97,7 +99,7 @@ unsigned err_blocks(const gwb_qspec* sp, int64_t N, int64_t K) {
   switch (sp->format) {
     case GWB_MXFP4:
     case GWB_MXFP4_PAGE_TIES: return gwb::mxfp4_err_blocks(N, K);
-    case GWB_UINTX: return gwb::uintx_err_blocks(N, K);
+    case GWB_UINTX: return gwb::uintx_err_blocks(sp->w_dtype, sp->group, N, K);
     default: return gwb::gptq_err_blocks(sp->group, N, K);
   }
 }
@@ -120,7 +122,7 @@ gwb_sizes sizes_of(const gwb_qspec* sp, int64_t N, int64_t K) {
       break;
     default:
       s.codes = uintx_packed_bytes(sp->nbits, N * K);
-      s.scales = (size_t)(N * (K / G) * 2);
+      s.scales = (size_t)(N * (K / G)) * elem_size(sp->w_dtype);   // the weight dtype
       s.zeros = (size_t)(N * (K / G));
       break;
   }
@@ -128,7 +130,7 @@ gwb_sizes sizes_of(const gwb_qspec* sp, int64_t N, int64_t K) {
   if (N > 0 && K > 0) {
     ws = (size_t)err_blocks(sp, N, K) * 2 * sizeof(double);
     if (sp->format == GWB_UINTX) {
-      size_t c = gwb::uintx_code_workspace(N, K);
+      size_t c = gwb::uintx_code_workspace(sp->w_dtype, sp->group, N, K);
       ws = c > ws ? c : ws;
     }
   }
@@ -172,10 +174,12 @@ int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int
   if (N == 0 || K == 0) return ok();          // empty: valid, nothing to enqueue
   if (int rc = check_weight(spec, W, K, ldw)) return rc;
   if (int rc = check_tensors(spec, out)) return rc;
-  if (spec->format == GWB_UINTX && gwb::uintx_code_workspace(N, K) > 0 &&
-      (!workspace || workspace_bytes < gwb::uintx_code_workspace(N, K)))
-    return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", gwb::uintx_code_workspace(N, K),
-                workspace_bytes);
+  if (spec->format == GWB_UINTX) {
+    const size_t need = gwb::uintx_code_workspace(spec->w_dtype, spec->group, N, K);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+    if (need > 0 && !aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
+  }
   hipStream_t st = (hipStream_t)stream;
   switch (spec->format) {
     case GWB_GPTQ_SYM:
@@ -189,7 +193,8 @@ int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int
                               out->scales, st);
       break;
     default:
-      gwb::launch_uintx_quant(spec->nbits, W, N, K, ldw, out->codes, out->scales, out->zeros, workspace, st);
+      gwb::launch_uintx_quant(spec->nbits, spec->w_dtype, spec->group, W, N, K, ldw, out->codes, out->scales,
+                              out->zeros, workspace, st);
   }
   return hip_check("quantize launch");
 }
@@ -199,7 +204,12 @@ int gwb_dequantize(const gwb_qspec* spec, const gwb_qtensors* in, int64_t N, int
   (void)workspace;
   (void)workspace_bytes;
   if (int rc = check_spec(spec, N, K)) return rc;
-  if (out_dtype != GWB_F32 && out_dtype != GWB_BF16) return fail(GWB_E_ARG, "unknown out_dtype %d", out_dtype);
+  if (out_dtype != GWB_F32 && out_dtype != GWB_BF16 && out_dtype != GWB_F16)
+    return fail(GWB_E_ARG, "unknown out_dtype %d", out_dtype);
+  // UINTX values are of the weight dtype (float32 holds them exactly); the other
+  // formats' exact products are rounded once to bf16 or kept in float32.
+  if (spec->format == GWB_UINTX ? (out_dtype != GWB_F32 && out_dtype != spec->w_dtype) : out_dtype == GWB_F16)
+    return fail(GWB_E_UNSUPPORTED, "out_dtype %d not provided for this format and weight dtype", out_dtype);
   if (N == 0 || K == 0) return ok();          // empty: valid, nothing to enqueue
   if (int rc = check_tensors(spec, in)) return rc;
   if (!out) return fail(GWB_E_ARG, "out is NULL");
@@ -218,7 +228,8 @@ int gwb_dequantize(const gwb_qspec* spec, const gwb_qtensors* in, int64_t N, int
       gwb::launch_mxfp4_dequant(in->codes, in->scales, N, K, out, out_dtype, ldo, st);
       break;
     default:
-      gwb::launch_uintx_dequant(spec->nbits, in->codes, in->scales, in->zeros, N, K, out, out_dtype, ldo, st);
+      gwb::launch_uintx_dequant(spec->nbits, spec->w_dtype, spec->group, in->codes, in->scales, in->zeros, N, K,
+                                out, out_dtype, ldo, st);
   }
   return hip_check("dequantize launch");
 }
@@ -248,7 +259,8 @@ int gwb_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t 
       gwb::launch_mxfp4_err(W, spec->w_dtype, N, K, ldw, in->codes, in->scales, part, st);
       break;
     default:
-      gwb::launch_uintx_err(spec->nbits, W, N, K, ldw, in->codes, in->scales, in->zeros, part, st);
+      gwb::launch_uintx_err(spec->nbits, spec->w_dtype, spec->group, W, N, K, ldw, in->codes, in->scales,
+                            in->zeros, part, st);
   }
   gwb::launch_err_finalize(part, nb, d_out, st);
   return hip_check("snr launch");
@@ -331,6 +343,8 @@ static size_t gemv_workspace(const gwb_qspec* sp, int64_t N, int64_t K, int64_t 
 
 static int check_gemv(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
   if (int rc = check_spec(sp, N, K)) return rc;
+  if (sp->format == GWB_UINTX && (sp->w_dtype != GWB_BF16 || sp->group != 64))
+    return fail(GWB_E_UNSUPPORTED, "the uintx GEMV takes bf16 weights in groups of 64");
   if (sp->format == GWB_UINTX && !gwb::uintx_gemv_supported(N, K))
     return fail(GWB_E_UNSUPPORTED, "the uintx GEMV needs N %% 8 == 0 and K %% 512 == 0, got N=%lld K=%lld",
                 (long long)N, (long long)K);

@@ -10,6 +10,7 @@ namespace gwb {
 
 constexpr int kF32 = 0;   // gwb_dtype values
 constexpr int kBF16 = 1;
+constexpr int kF16 = 2;
 constexpr int kStore = 0;  // dequant sinks
 constexpr int kErr = 1;
 
@@ -49,17 +50,27 @@ void launch_gptq_err(bool sym, int group, const void* W, int32_t w_dtype, int64_
                      int64_t ldw, const void* qweight, const void* scales, const void* qzeros,
                      double* part, hipStream_t st);
 
-// ---- UINTX (uintx.hip)
-bool uintx_tiled(int64_t N, int64_t K);   // shard lengths nest: N*K % 512 == 0
-size_t uintx_code_workspace(int64_t N, int64_t K);
-void launch_uintx_quant(int nbits, const void* W, int64_t N, int64_t K, int64_t ldw, void* packed,
-                        void* scales, void* zeros, void* workspace, hipStream_t st);
-void launch_uintx_dequant(int nbits, const void* packed, const void* scales, const void* zeros,
-                          int64_t N, int64_t K, void* out, int32_t out_dtype, int64_t ldo,
+// ---- UINTX (uintx.hip: tiled bf16 group-64 kernels when N*K % 512 == 0, which nest
+// the shard lengths; uintx_flat.hip: every dtype, group and shape). dt is the weight
+// dtype (kBF16, kF16, kF32); group 32, 64 or 128.
+bool uintx_tiled(int32_t dt, int group, int64_t N, int64_t K);
+size_t uintx_code_workspace(int32_t dt, int group, int64_t N, int64_t K);
+void launch_uintx_quant(int nbits, int32_t dt, int group, const void* W, int64_t N, int64_t K, int64_t ldw,
+                        void* packed, void* scales, void* zeros, void* workspace, hipStream_t st);
+void launch_uintx_dequant(int nbits, int32_t dt, int group, const void* packed, const void* scales,
+                          const void* zeros, int64_t N, int64_t K, void* out, int32_t out_dtype, int64_t ldo,
                           hipStream_t st);
-unsigned uintx_err_blocks(int64_t N, int64_t K);
-void launch_uintx_err(int nbits, const void* W, int64_t N, int64_t K, int64_t ldw, const void* packed,
-                      const void* scales, const void* zeros, double* part, hipStream_t st);
+unsigned uintx_err_blocks(int32_t dt, int group, int64_t N, int64_t K);
+void launch_uintx_err(int nbits, int32_t dt, int group, const void* W, int64_t N, int64_t K, int64_t ldw,
+                      const void* packed, const void* scales, const void* zeros, double* part, hipStream_t st);
+void launch_uintx_quant_flat(int nbits, int32_t dt, int group, const void* W, int64_t N, int64_t K, int64_t ldw,
+                             void* packed, void* scales, void* zeros, void* workspace, hipStream_t st);
+void launch_uintx_dequant_flat(int nbits, int32_t dt, int group, const void* packed, const void* scales,
+                               const void* zeros, int64_t N, int64_t K, void* out, int32_t out_dtype, int64_t ldo,
+                               hipStream_t st);
+unsigned uintx_flat_err_blocks(int64_t N, int64_t K);
+void launch_uintx_err_flat(int nbits, int32_t dt, int group, const void* W, int64_t N, int64_t K, int64_t ldw,
+                           const void* packed, const void* scales, const void* zeros, double* part, hipStream_t st);
 
 // ---- error finalize (common.hip): part[2*nblocks] -> out[3] = {sum w^2, sum e^2, dB}
 void launch_err_finalize(const double* part, unsigned nblocks, double* out, hipStream_t st);

@@ -14,6 +14,7 @@
 // Other sizes take a two-pass path: codes to workspace, then one thread per byte.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "uintx_layout.hpp"
 
 namespace gwb {
 
@@ -22,24 +23,6 @@ namespace gwb {
 constexpr int kLanePos = 8;
 constexpr int kWavePos = 64 * kLanePos;
 constexpr int kBlockPos = 4 * kWavePos;
-
-struct Shards {                  // byte offsets of the present shards in the packed buffer
-  int64_t base4, base2, base1;
-};
-static Shards shards_of(int nbits, int64_t numel) {
-  Shards s{};
-  int64_t L4 = (numel + 1) / 2, L2 = (numel + 3) / 4;
-  s.base4 = 0;
-  s.base2 = (nbits & 4) ? L4 : 0;
-  s.base1 = s.base2 + ((nbits & 2) ? L2 : 0);
-  return s;
-}
-// bit offsets of the 2-bit and 1-bit shards' fields within a code (pack order 4, 2, 1)
-template <int NB> struct ShardBits {
-  static constexpr bool has4 = NB & 4, has2 = NB & 2, has1 = NB & 1;
-  static constexpr int off2 = has4 ? 4 : 0;
-  static constexpr int off1 = (has4 ? 4 : 0) + (has2 ? 2 : 0);
-};
 
 // Group qparams from the group's min and max (every op a float32 op rounded to bf16):
 // mn = min(min, 0), mx = max(max, 0); scale = bf(bf(mx - mn) / qmax), at least 2^-23;
@@ -278,118 +261,6 @@ __global__ __launch_bounds__(256) void uintx_dequant_tiled(const uint8_t* __rest
   if constexpr (SINK == kErr) block_sum2_store<256>(sw, se, part);
 }
 
-// ------------------------------------------------------------- ragged sizes
-struct RaggedShards {
-  int64_t base4, base2, base1;
-  int off2, off1;
-  bool has4, has2, has1;
-};
-static RaggedShards ragged_shards(int nbits, int64_t numel) {
-  const Shards b = shards_of(nbits, numel);
-  RaggedShards r{b.base4, b.base2, b.base1, (nbits & 4) ? 4 : 0, ((nbits & 4) ? 4 : 0) + ((nbits & 2) ? 2 : 0),
-                 (nbits & 4) != 0, (nbits & 2) != 0, (nbits & 1) != 0};
-  return r;
-}
-__device__ __forceinline__ void load8_at(const uint16_t* W, int64_t ldw, uint32_t e, FastDiv kdiv, float* x) {
-  const uint32_t n = fdiv(e, kdiv);
-  load8(W + (int64_t)n * ldw + (e - n * kdiv.d), x);
-}
-// Pass 1: codes of 8 consecutive elements per lane (8 lanes per group) to workspace.
-__global__ __launch_bounds__(256) void uintx_codes_flat(const uint16_t* __restrict__ W, int64_t ldw,
-                                                        FastDiv kdiv, uint32_t units, int nbits,
-                                                        uint8_t* __restrict__ codes,
-                                                        uint16_t* __restrict__ scales,
-                                                        uint8_t* __restrict__ zeros) {
-  const float qmax = (float)((1 << nbits) - 1);
-  const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
-    float x[8];
-    load8_at(W, ldw, u * 8, kdiv, x);
-    float mn = x[0], mx = x[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
-    mn = lanes_min<8>(mn);
-    mx = lanes_max<8>(mx);
-    QP q = uintx_qparams(mn, mx, qmax);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) codes[u * 8 + i] = (uint8_t)uintx_code(x[i], q, qmax);
-    if ((u & 7u) == 0) {
-      scales[u / 8] = (uint16_t)(__float_as_uint(q.s) >> 16);
-      zeros[u / 8] = (uint8_t)q.zp;
-    }
-  }
-}
-
-// Pass 2: one thread per byte of the k-bit shard (bits [off, off+k) of each code).
-__global__ __launch_bounds__(256) void uintx_pack_shard(const uint8_t* __restrict__ codes, uint32_t numel,
-                                                        int k, int off, uint8_t* __restrict__ shard) {
-  const int vpb = 8 / k;
-  const uint32_t L = (numel + vpb - 1) / vpb;
-  const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < L; i += stride) {
-    uint32_t v = 0;
-    for (int j = 0; j < vpb; ++j) {
-      uint32_t idx = j * L + i;
-      if (idx < numel) v |= ((codes[idx] >> off) & ((1u << k) - 1u)) << (j * k);
-    }
-    shard[i] = (uint8_t)v;
-  }
-}
-
-__device__ __forceinline__ uint32_t uintx_gather(const uint8_t* packed, const RaggedShards& sh, uint32_t numel,
-                                                 uint32_t idx) {
-  uint32_t c = 0;
-  if (sh.has4) {
-    uint32_t L = (numel + 1) / 2;
-    c |= (packed[sh.base4 + idx % L] >> (4 * (idx / L))) & 0xFu;
-  }
-  if (sh.has2) {
-    uint32_t L = (numel + 3) / 4;
-    c |= ((packed[sh.base2 + idx % L] >> (2 * (idx / L))) & 0x3u) << sh.off2;
-  }
-  if (sh.has1) {
-    uint32_t L = (numel + 7) / 8;
-    c |= ((packed[sh.base1 + idx % L] >> (idx / L)) & 0x1u) << sh.off1;
-  }
-  return c;
-}
-
-template <int SINK, typename TOut>
-__global__ __launch_bounds__(256) void uintx_dequant_flat(const uint8_t* __restrict__ packed,
-                                                          const uint16_t* __restrict__ scales,
-                                                          const uint8_t* __restrict__ zeros,
-                                                          FastDiv kdiv, uint32_t units, uint32_t numel,
-                                                          RaggedShards sh, TOut* __restrict__ out, int64_t ldo,
-                                                          const uint16_t* __restrict__ W, int64_t ldw,
-                                                          double* __restrict__ part) {
-  const uint32_t stride = gridDim.x * blockDim.x;
-  double sw = 0.0, se = 0.0;
-  for (uint32_t u = blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
-    const uint32_t e = u * 8;
-    const float s = bf16_to_f32(scales[e / 64]);
-    const float zp = (float)zeros[e / 64];
-    float d[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) d[i] = uintx_value(uintx_gather(packed, sh, numel, e + i), zp, s);
-    const uint32_t n = fdiv(e, kdiv);
-    const uint32_t k = e - n * kdiv.d;
-    if constexpr (SINK == kStore) {
-      store8(out + (int64_t)n * ldo + k, d);
-    } else {
-      float x[8];
-      load8(W + (int64_t)n * ldw + k, x);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        double xd = (double)x[i];
-        double ed = (double)(x[i] - d[i]);
-        sw = fma(xd, xd, sw);
-        se = fma(ed, ed, se);
-      }
-    }
-  }
-  if constexpr (SINK == kErr) block_sum2_store<256>(sw, se, part);
-}
-
 // ------------------------------------------------------------- decode GEMV
 // y[b, n] = sum_k x[b, k] * w[n, k] with w = bf16((q - zp) * s), the bf16 weight the
 // page's forward builds before its linear. With N % 8 == 0 and K % 512 == 0, position p
@@ -506,12 +377,13 @@ __global__ __launch_bounds__(256) void uintx_gemv_tiled(const uint8_t* __restric
 }
 
 // ------------------------------------------------------------------ launchers
-bool uintx_tiled(int64_t N, int64_t K) { return ((N * K) % 512) == 0; }
-size_t uintx_code_workspace(int64_t N, int64_t K) { return uintx_tiled(N, K) ? 0 : (size_t)(N * K); }
-
-static unsigned capped(uint64_t blocks, unsigned cap) {
-  return (unsigned)(blocks < cap ? (blocks ? blocks : 1) : cap);
+bool uintx_tiled(int32_t dt, int group, int64_t N, int64_t K) {
+  return dt == kBF16 && group == 64 && ((N * K) % 512) == 0;
 }
+size_t uintx_code_workspace(int32_t dt, int group, int64_t N, int64_t K) {
+  return uintx_tiled(dt, group, N, K) ? 0 : (size_t)(N * K);
+}
+
 static unsigned tiles_of(int64_t N, int64_t K) { return (unsigned)(((uint64_t)(N * K) / 8 + kBlockPos - 1) / kBlockPos); }
 
 template <int NB>
@@ -525,34 +397,19 @@ static void quant_tiled(const void* W, int64_t N, int64_t K, int64_t ldw, void* 
                      (uint16_t*)scales, (uint8_t*)zeros);
 }
 
-void launch_uintx_quant(int nbits, const void* W, int64_t N, int64_t K, int64_t ldw, void* packed,
-                        void* scales, void* zeros, void* workspace, hipStream_t st) {
-  if (uintx_tiled(N, K)) {
-    switch (nbits) {
-      case 2: quant_tiled<2>(W, N, K, ldw, packed, scales, zeros, st); break;
-      case 3: quant_tiled<3>(W, N, K, ldw, packed, scales, zeros, st); break;
-      case 4: quant_tiled<4>(W, N, K, ldw, packed, scales, zeros, st); break;
-      case 5: quant_tiled<5>(W, N, K, ldw, packed, scales, zeros, st); break;
-      case 6: quant_tiled<6>(W, N, K, ldw, packed, scales, zeros, st); break;
-      default: quant_tiled<7>(W, N, K, ldw, packed, scales, zeros, st); break;
-    }
+void launch_uintx_quant(int nbits, int32_t dt, int group, const void* W, int64_t N, int64_t K, int64_t ldw,
+                        void* packed, void* scales, void* zeros, void* workspace, hipStream_t st) {
+  if (!uintx_tiled(dt, group, N, K)) {
+    launch_uintx_quant_flat(nbits, dt, group, W, N, K, ldw, packed, scales, zeros, workspace, st);
     return;
   }
-  const uint32_t numel = (uint32_t)(N * K);
-  const RaggedShards sh = ragged_shards(nbits, numel);
-  const FastDiv kdiv = make_fastdiv((uint32_t)K);
-  uint8_t* codes = (uint8_t*)workspace;
-  const uint32_t units = numel / 8;
-  hipLaunchKernelGGL(uintx_codes_flat, dim3(capped((units + 255) / 256, kStreamGridCap)), dim3(256), 0, st,
-                     (const uint16_t*)W, ldw, kdiv, units, nbits, codes, (uint16_t*)scales, (uint8_t*)zeros);
-  int off = 0;
-  for (int k : {4, 2, 1}) {
-    if (!(nbits & k)) continue;
-    int64_t base = k == 4 ? sh.base4 : (k == 2 ? sh.base2 : sh.base1);
-    uint32_t L = (numel + (8 / k) - 1) / (8 / k);
-    hipLaunchKernelGGL(uintx_pack_shard, dim3(capped((L + 255) / 256, kStreamGridCap)), dim3(256), 0, st,
-                       (const uint8_t*)codes, numel, k, off, (uint8_t*)packed + base);
-    off += k;
+  switch (nbits) {
+    case 2: quant_tiled<2>(W, N, K, ldw, packed, scales, zeros, st); break;
+    case 3: quant_tiled<3>(W, N, K, ldw, packed, scales, zeros, st); break;
+    case 4: quant_tiled<4>(W, N, K, ldw, packed, scales, zeros, st); break;
+    case 5: quant_tiled<5>(W, N, K, ldw, packed, scales, zeros, st); break;
+    case 6: quant_tiled<6>(W, N, K, ldw, packed, scales, zeros, st); break;
+    default: quant_tiled<7>(W, N, K, ldw, packed, scales, zeros, st); break;
   }
 }
 
@@ -569,47 +426,41 @@ static void deq_tiled(const void* packed, const void* scales, const void* zeros,
 }
 
 template <int SINK, typename TOut>
-static void deq(int nbits, const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K,
-                void* out, int64_t ldo, const void* W, int64_t ldw, double* part, hipStream_t st) {
-  if (uintx_tiled(N, K)) {
-    switch (nbits) {
-      case 2: deq_tiled<2, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
-      case 3: deq_tiled<3, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
-      case 4: deq_tiled<4, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
-      case 5: deq_tiled<5, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
-      case 6: deq_tiled<6, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
-      default: deq_tiled<7, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
-    }
-    return;
+static void deq_tiled_nb(int nbits, const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K,
+                         void* out, int64_t ldo, const void* W, int64_t ldw, double* part, hipStream_t st) {
+  switch (nbits) {
+    case 2: deq_tiled<2, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
+    case 3: deq_tiled<3, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
+    case 4: deq_tiled<4, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
+    case 5: deq_tiled<5, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
+    case 6: deq_tiled<6, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
+    default: deq_tiled<7, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
   }
-  const uint32_t numel = (uint32_t)(N * K);
-  const RaggedShards sh = ragged_shards(nbits, numel);
-  const FastDiv kdiv = make_fastdiv((uint32_t)K);
-  const unsigned grid = SINK == kErr ? uintx_err_blocks(N, K) : capped((numel / 8 + 255) / 256, kStreamGridCap);
-  hipLaunchKernelGGL((uintx_dequant_flat<SINK, TOut>), dim3(grid), dim3(256), 0, st, (const uint8_t*)packed,
-                     (const uint16_t*)scales, (const uint8_t*)zeros, kdiv, numel / 8, numel, sh, (TOut*)out, ldo,
-                     (const uint16_t*)W, ldw, part);
 }
 
-void launch_uintx_dequant(int nbits, const void* packed, const void* scales, const void* zeros,
-                          int64_t N, int64_t K, void* out, int32_t out_dtype, int64_t ldo,
+void launch_uintx_dequant(int nbits, int32_t dt, int group, const void* packed, const void* scales,
+                          const void* zeros, int64_t N, int64_t K, void* out, int32_t out_dtype, int64_t ldo,
                           hipStream_t st) {
-  if (out_dtype == kBF16)
-    deq<kStore, uint16_t>(nbits, packed, scales, zeros, N, K, out, ldo, nullptr, 0, nullptr, st);
+  if (!uintx_tiled(dt, group, N, K))
+    launch_uintx_dequant_flat(nbits, dt, group, packed, scales, zeros, N, K, out, out_dtype, ldo, st);
+  else if (out_dtype == kBF16)
+    deq_tiled_nb<kStore, uint16_t>(nbits, packed, scales, zeros, N, K, out, ldo, nullptr, 0, nullptr, st);
   else
-    deq<kStore, float>(nbits, packed, scales, zeros, N, K, out, ldo, nullptr, 0, nullptr, st);
+    deq_tiled_nb<kStore, float>(nbits, packed, scales, zeros, N, K, out, ldo, nullptr, 0, nullptr, st);
 }
 
 // The tiled error kernel runs one block per tile (its partials follow the tiles); the
-// ragged one is grid-stride with a capped grid. Both depend on the shape only.
-unsigned uintx_err_blocks(int64_t N, int64_t K) {
-  if (uintx_tiled(N, K)) return tiles_of(N, K);
-  return capped(((uint64_t)(N * K) / 8 + 255) / 256, kErrGridCap);
+// flat one is grid-stride with a capped grid. Both depend on the shape only.
+unsigned uintx_err_blocks(int32_t dt, int group, int64_t N, int64_t K) {
+  return uintx_tiled(dt, group, N, K) ? tiles_of(N, K) : uintx_flat_err_blocks(N, K);
 }
 
-void launch_uintx_err(int nbits, const void* W, int64_t N, int64_t K, int64_t ldw, const void* packed,
-                      const void* scales, const void* zeros, double* part, hipStream_t st) {
-  deq<kErr, float>(nbits, packed, scales, zeros, N, K, nullptr, 0, W, ldw, part, st);
+void launch_uintx_err(int nbits, int32_t dt, int group, const void* W, int64_t N, int64_t K, int64_t ldw,
+                      const void* packed, const void* scales, const void* zeros, double* part, hipStream_t st) {
+  if (uintx_tiled(dt, group, N, K))
+    deq_tiled_nb<kErr, float>(nbits, packed, scales, zeros, N, K, nullptr, 0, W, ldw, part, st);
+  else
+    launch_uintx_err_flat(nbits, dt, group, W, N, K, ldw, packed, scales, zeros, part, st);
 }
 
 }  // namespace gwb

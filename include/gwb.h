@@ -11,7 +11,8 @@
  *   GWB_MXFP4      page quantize_dflash_mxfp4.py, quantize_mxfp4 / dequantize_mxfp4:
  *                  e2m1 codes (round half to even), an E8M0 exponent per 32 weights.
  *   GWB_UINTX      page uintx_quant.py, UIntXQuantizer: affine uint2..uint7 with
- *                  preserve_zero, arithmetic in bfloat16, planar power-of-two shards.
+ *                  preserve_zero, arithmetic in the weight's dtype (usually bfloat16),
+ *                  planar power-of-two shards.
  *   GWB_MXFP4_PAGE_TIES  MXFP4 with the tie rule of the page's code instead of its
  *                  stated round-half-to-even: the first tied index, rounded down to even
  *                  (|x| / 2^e = 0.75, 1.75, 3.5 give 0, 1, 2 rather than 1, 2, 4). Same
@@ -47,15 +48,21 @@ typedef enum {
 } gwb_status;
 
 typedef enum { GWB_GPTQ_SYM = 1, GWB_GPTQ_ASYM = 2, GWB_MXFP4 = 3, GWB_UINTX = 4, GWB_MXFP4_PAGE_TIES = 5 } gwb_format;
-typedef enum { GWB_F32 = 0, GWB_BF16 = 1 } gwb_dtype;
+typedef enum { GWB_F32 = 0, GWB_BF16 = 1, GWB_F16 = 2 } gwb_dtype;
 
 /* What to quantize to.
  *   format  gwb_format
  *   nbits   4 for GPTQ and MXFP4; 2..7 for UINTX (8 is refused with GWB_E_UNSUPPORTED:
  *           page uintx_quant.py, can_quantize, always left uint8 layers unquantized)
  *   group   GPTQ: 32, 64 or 128 (page export_gptq_cpu.py, --group, default 128);
- *           MXFP4: 32 (the page's GROUP); UINTX: 64 (UIntXQuantizer's group_size)
- *   w_dtype gwb_dtype of W. UINTX requires GWB_BF16 (its arithmetic is bfloat16).   */
+ *           MXFP4: 32 (the page's GROUP); UINTX: 32, 64 (UIntXQuantizer's default
+ *           group_size) or 128
+ *   w_dtype gwb_dtype of W. GPTQ and MXFP4: GWB_BF16 or GWB_F32 (the pages widen W to
+ *           float32). UINTX: GWB_BF16, GWB_F16 or GWB_F32; page uintx_quant.py runs the
+ *           arithmetic in the weight's dtype (every op one float32 op rounded to it,
+ *           float32 ops for GWB_F32) and stores the scale as that dtype. GWB_BF16 with
+ *           group 64 and N*K % 512 == 0 takes the tiled kernels, everything else a
+ *           two-pass path with a workspace.                                        */
 typedef struct {
   int32_t format;
   int32_t nbits;
@@ -77,7 +84,7 @@ typedef struct {
  *                 off counted from 0); shard k has ceil(N*K / (8/k)) bytes; byte i of
  *                 shard k = OR_j field(code[j*L + i]) << (j*k), L = that byte count,
  *                 codes taken in row-major order, zero-padded
- *          scales bfloat16 [N, K/G] (the bytes of the bf16 values, little-endian)
+ *          scales [N, K/G] of w_dtype (the bytes of its values, little-endian)
  *          zeros  uint8 [N, K/G] zero points in [0, 2**nbits - 1]; g_idx unused     */
 typedef struct {
   void* codes;
@@ -118,11 +125,14 @@ int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int
 /* Unpack and dequantize into out [N, K] (row stride ldo >= K) of out_dtype, in the
  * weight's own [N, K] layout for every format (the GPTQ transpose is undone).
  * GPTQ: (code - 8) * scale or (code - zp) * scale with the fp16 scale widened;
- * MXFP4: +-E2M1[code & 7] * 2**(e8m0 - 127); UINTX: bf16(bf16(q - zp) * scale);
+ * MXFP4: +-E2M1[code & 7] * 2**(e8m0 - 127); UINTX: r(r(q - zp) * scale), r the
+ * rounding to w_dtype;
  * page export_gptq_cpu.py (module docstring), page quantize_dflash_mxfp4.py
  * dequantize_mxfp4, page uintx_quant.py _dequantize_native. Each value is the
  * correctly rounded result of an exact product, so bf16 and f32 outputs are exact
- * roundings. workspace as for gwb_quantize. */
+ * roundings. out_dtype: GWB_F32 or GWB_BF16; UINTX: GWB_F32 or w_dtype (its values
+ * are of the weight dtype), anything else GWB_E_UNSUPPORTED. workspace as for
+ * gwb_quantize. */
 int gwb_dequantize(const gwb_qspec* spec, const gwb_qtensors* in, int64_t N, int64_t K,
                    void* out, int32_t out_dtype, int64_t ldo, void* workspace,
                    size_t workspace_bytes, void* stream);
@@ -133,7 +143,8 @@ int gwb_dequantize(const gwb_qspec* spec, const gwb_qtensors* in, int64_t N, int
  *   in float64), d_out[2] = 10 log10(d_out[0] / max(d_out[1], 1e-24)) dB,
  * which is page export_gptq_cpu.py's 20 log10(||w|| / max(||w - deq||, 1e-12)) and
  * gives page quantize_dflash_mxfp4.py's relative error 10**(-dB/20).
- * w is W as float32; d is the dequantized value in float32 (UINTX: the bf16 result).
+ * w is W as float32; d is the dequantized value in float32 (UINTX: the value of the
+ * weight dtype that gwb_dequantize returns).
  * workspace: at least gwb_sizes.workspace bytes. Deterministic for a given shape.  */
 int gwb_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
             const gwb_qtensors* in, double* d_out, void* workspace, size_t workspace_bytes,
@@ -191,7 +202,8 @@ int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t
  * MXFP4.
  *   spec, w  a GPTQ (sym or asym), MXFP4 or uintx weight as gwb_quantize wrote it, [N, K];
  *            uintx (page uintx_quant.py, forward: the bf16 weight bf16((q - zp) * s)
- *            times x) needs N % 8 == 0 and K % 512 == 0, else GWB_E_UNSUPPORTED
+ *            times x) needs bf16 weights, group 64, N % 8 == 0 and K % 512 == 0,
+ *            else GWB_E_UNSUPPORTED
  *   x        device bf16 [B, K], row stride ldx (multiple of 8), 16-byte aligned; 1 <= B <= 8
  *   y        device [B, N] of y_dtype (GWB_F32 or GWB_BF16, RNE), row stride ldy
  *   workspace at least gwb_gemv_workspace bytes (GPTQ and uintx: K-split partial sums;

@@ -50,6 +50,15 @@ def test_sizes_match_layouts():
     # ragged uintx: shards padded independently, workspace for the two-pass path
     rc, s = _sizes("uintx", 1, 64, nbits=5)
     assert rc == 0 and s.codes == 32 + 8 and s.workspace >= 64
+    # the uintx scale has the weight dtype; groups 32 and 128; non-bf16 / non-64 groups
+    # take the two-pass path (codes workspace of N*K bytes)
+    rc, s = _sizes("uintx", 64, 512, nbits=4, group=32, dt=gwb.F32)
+    assert rc == 0 and s.scales == 64 * 16 * 4 and s.zeros == 64 * 16 and s.workspace >= 64 * 512
+    rc, s = _sizes("uintx", 64, 512, nbits=3, group=128, dt=gwb.F16)
+    assert rc == 0 and s.scales == 64 * 4 * 2 and s.zeros == 64 * 4 and s.codes == 64 * 512 * 3 // 8
+    assert s.workspace >= 64 * 512
+    rc, s = _sizes("uintx", 64, 512, nbits=3, group=64, dt=gwb.BF16)
+    assert rc == 0 and s.workspace < 64 * 512                  # tiled: error partials only
 
 
 def test_bits_per_weight_from_sizes():
@@ -71,7 +80,12 @@ def test_bits_per_weight_from_sizes():
     ("uintx", 8, 128, 8, 64, gwb.BF16, gwb.E_UNSUPPORTED),    # uint8 refused
     ("uintx", 8, 128, 1, 64, gwb.BF16, gwb.E_ARG),
     ("uintx", 8, 100, 4, 64, gwb.BF16, gwb.E_SHAPE),
-    ("uintx", 8, 128, 4, 64, gwb.F32, gwb.E_UNSUPPORTED),
+    ("uintx", 8, 128, 4, 16, gwb.F16, gwb.E_UNSUPPORTED),     # groups 32, 64, 128
+    ("uintx", 8, 128, 4, 0, gwb.F32, gwb.E_ARG),
+    ("uintx", 8, 96, 4, 64, gwb.F16, gwb.E_SHAPE),
+    ("uintx", 8, 128, 4, 64, 3, gwb.E_ARG),                   # unknown dtype
+    ("mxfp4", 8, 128, 4, 32, gwb.F16, gwb.E_UNSUPPORTED),     # float16 weights: uintx only
+    ("gptq_sym", 8, 128, 4, 128, gwb.F16, gwb.E_UNSUPPORTED),
     ("uintx", -1, 128, 4, 64, gwb.BF16, gwb.E_ARG),
     ("mxfp4", 1 << 16, 1 << 16, 4, 32, gwb.BF16, gwb.E_UNSUPPORTED),   # beyond 2^31 elements
 ])
@@ -117,6 +131,14 @@ def test_dequantize_snr_awq_validate():
     assert lib.gwb_dequantize(ctypes.byref(sp), ctypes.byref(qt), 8, 64, fake, 5, 64, None, 0, None) == gwb.E_ARG
     assert lib.gwb_dequantize(ctypes.byref(sp), ctypes.byref(qt), 8, 64, fake, gwb.BF16, 32, None, 0, None) == gwb.E_ARG
     assert lib.gwb_dequantize(ctypes.byref(sp), ctypes.byref(qt), 8, 64, None, gwb.BF16, 64, None, 0, None) == gwb.E_ARG
+    assert lib.gwb_dequantize(ctypes.byref(sp), ctypes.byref(qt), 8, 64, fake, gwb.F16, 64, None, 0, None) \
+        == gwb.E_UNSUPPORTED                                   # float16 output: uintx only
+    # uintx values are of the weight dtype: float32 or that dtype out, nothing else
+    qu = gwb.QTensors(fake, fake, fake, None)
+    for wdt, odt in [(gwb.F16, gwb.BF16), (gwb.F32, gwb.BF16), (gwb.F32, gwb.F16), (gwb.BF16, gwb.F16)]:
+        su = gwb.make_spec("uintx", 4, 64, wdt)
+        assert lib.gwb_dequantize(ctypes.byref(su), ctypes.byref(qu), 8, 64, fake, odt, 64, None, 0, None) \
+            == gwb.E_UNSUPPORTED, (wdt, odt)
     assert lib.gwb_snr(ctypes.byref(sp), fake, 8, 64, 64, ctypes.byref(qt), fake, None, 0, None) == gwb.E_SIZE
     assert lib.gwb_snr(ctypes.byref(sp), fake, 0, 64, 64, ctypes.byref(qt), fake, fake, 1 << 20, None) == gwb.E_SHAPE
     al = (ctypes.c_double * 11)(*[i / 10 for i in range(11)])
@@ -219,6 +241,10 @@ def test_gemv_sizes_and_validation():
     assert lib.gwb_gemv_workspace(ctypes.byref(sp_u), 12, 512, 1, ctypes.byref(ctypes.c_size_t())) == gwb.E_UNSUPPORTED
     assert ws("uintx", 3072, 12288, 2) == (gwb.OK, 6 * 2 * 3072 * 4)             # 2048-column splits
     assert ws("uintx", 64, 1536, 1) == (gwb.OK, 3 * 64 * 4)                      # 512-column splits
+    for g, dt in [(32, gwb.BF16), (64, gwb.F16), (64, gwb.F32)]:                 # bf16 group 64 only
+        su = gwb.make_spec("uintx", 4, g, dt)
+        assert lib.gwb_gemv_workspace(ctypes.byref(su), 64, 1536, 1, ctypes.byref(ctypes.c_size_t())) \
+            == gwb.E_UNSUPPORTED
     sp = gwb.make_spec("gptq_sym", 4, 128)
     def go(x=fake, B=1, ldx=512, y=fake, ydt=gwb.F32, ldy=256, w=0, wsb=0):
         return lib.gwb_gemv(ctypes.byref(sp), ctypes.byref(qt), 256, 512, P(x), B, ldx, P(y), ydt, ldy, P(w), wsb, None)

@@ -212,6 +212,86 @@ def test_uintx_parity(nbits, n, k, kind):
     _check_snr(W, Wd, q, ref)
 
 
+_TDT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+
+
+def _gpu_bits(t: torch.Tensor) -> np.ndarray:
+    return _gpu_f32bits(t) if t.dtype == torch.float32 else _gpu_bf16bits(t)
+
+
+def _ref_bits(x, dt: str) -> np.ndarray:
+    if dt == "f32":
+        return _f32bits(x)
+    if dt == "f16":
+        return np.asarray(x, np.float32).astype(np.float16).view(np.uint16)
+    return _ref_bf16bits(x)
+
+
+def _uintx_case(W: torch.Tensor, dt: str, nbits: int, group: int, Wd=None):
+    """Quantize on the device and in the oracle; compare every stored byte, both
+    dequantized outputs (float32 and the weight dtype) and the SNR sums."""
+    n, k = W.shape
+    Wd = W.to(DEV) if Wd is None else Wd
+    q = gwb.quantize(Wd, "uintx", nbits=nbits, group=group)
+    o = oux.quantize(W.float().numpy(), nbits, group, dt)
+    assert np.array_equal(_np(q["packed"]), o["packed"])
+    assert np.array_equal(_np(q["scale_bytes"]), o["scale_bytes"])
+    assert np.array_equal(_np(q["zero_point"]), o["zero_point"])
+    ref = oux.dequantize(o["packed"], o["scale_bytes"], o["zero_point"], nbits, n, k, group, dt)
+    d32 = gwb.dequantize(q, torch.float32)
+    dn = gwb.dequantize(q, _TDT[dt])
+    torch.cuda.synchronize()
+    nan = np.isnan(ref)
+    assert _same_bits(_gpu_f32bits(d32), _f32bits(ref), nan)
+    assert _same_bits(_gpu_bits(dn), _ref_bits(ref, dt), nan)
+    _check_snr(W, Wd, q, ref)
+    return o
+
+
+@pytest.mark.parametrize("dt,group", [("f16", 64), ("f32", 64), ("f16", 32), ("f32", 128), ("bf16", 32),
+                                      ("bf16", 128), ("f16", 128), ("f32", 32)])
+@pytest.mark.parametrize("nbits", [2, 3, 4, 7])
+@pytest.mark.parametrize("n,k,kind", [(1, 128, "normal"), (3, 256, "adv"), (8, 384, "normal"),
+                                      (64, 512, "adv"), (72, 1536, "normal")])
+def test_uintx_dtype_group_parity(dt, group, nbits, n, k, kind):
+    """Page uintx_quant.py in the weight's own dtype: float16 and float32 weights, and
+    groups 32 and 128 (the general two-pass path), bit for bit with the oracle."""
+    seed = 500 + n + nbits + group
+    if kind == "adv":
+        W = workloads.adversarial_weight(n, k, seed=seed, dtype=_TDT[dt])
+    else:
+        W = workloads.uintx_weight(n, k, seed=seed, outlier_frac=0.01, dtype=_TDT[dt])
+    _uintx_case(W, dt, nbits, group)
+
+
+def test_uintx_f16_infinite_reciprocal_groups():
+    """float16 groups whose scale is below about 2^-16: the reciprocal is inf, positive
+    weights take qmax, negatives 0 and zeros (NaN from 0 * inf) code 0."""
+    rng = np.random.default_rng(510)
+    W = (rng.integers(-40, 41, (16, 256)) * 2.0 ** -24).astype(np.float32)     # float16 subnormals
+    W[0, :64] = 2.0 ** -20
+    W[0, 3], W[0, 5] = 0.0, -(2.0 ** -22)                                     # the hand-worked group
+    W[1] = 0.0
+    W[2, ::2] = -0.0
+    Wt = torch.from_numpy(W).to(torch.float16)
+    assert np.array_equal(Wt.float().numpy(), W)
+    o = _uintx_case(Wt, "f16", 4, 64)
+    assert o["codes"][0, :8].tolist() == [15, 15, 15, 0, 15, 0, 15, 15]
+    assert np.all(o["codes"][1] == 0)
+    assert np.mean(o["scale"] < 2.0 ** -16) > 0.5                             # most groups hit the case
+
+
+def test_uintx_other_dtypes_strided_and_larger():
+    """Row stride beyond K, and a size that spans many grid-stride passes."""
+    big = workloads.uintx_weight(48, 1024 + 64, seed=511, outlier_frac=0.01, dtype=torch.float16)
+    Wd = big.to(DEV)[:, :1024]
+    _uintx_case(big[:, :1024].contiguous(), "f16", 5, 128, Wd=Wd)
+    big32 = workloads.uintx_weight(40, 512 + 4, seed=512, dtype=torch.float32)
+    Wd32 = big32.to(DEV)[:, :512]
+    _uintx_case(big32[:, :512].contiguous(), "f32", 3, 32, Wd=Wd32)
+    _uintx_case(workloads.uintx_weight(512, 4096, seed=513, dtype=torch.float16), "f16", 4, 64)
+
+
 # -------------------------------------------------------------------------- AWQ
 def _ulps(a, b):
     ia = _f32bits(a).astype(np.int64)
