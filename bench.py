@@ -63,7 +63,7 @@ def algo_bytes(op: str, fmt: str, nbits: int, n: int, k: int) -> float:
 KERNEL_SOURCES = {   # what each op's kernel is compiled from (for the traffic record's digest)
     "mxfp4": ["mxfp4.hip", "mxfp4_math.hpp", "device_common.hpp", "kernels.hpp"],
     "gptq": ["gptq.hip", "device_common.hpp", "kernels.hpp"],
-    "uintx": ["uintx.hip", "device_common.hpp", "kernels.hpp"],
+    "uintx": ["uintx.hip", "uintx_layout.hpp", "device_common.hpp", "kernels.hpp"],
     "awq": ["awq.hip", "mxfp4_math.hpp", "device_common.hpp", "kernels.hpp"],
 }
 
@@ -153,7 +153,8 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
     """Paths next to the hot path, timed on their own after the step (not part of
     value): the AWQ fold of the gate_up weight (columns * s) straight to MXFP4, the same
     fold also writing the folded bf16 weight, and the decode GEMV reading a packed
-    131072 x 2048 lm_head (GPTQ sym g128, MXFP4, uintx4 g64) for one activation row."""
+    131072 x 2048 lm_head (GPTQ sym g128, MXFP4, uintx4 g64) for one activation row, and
+    the uintx variants (float16 / float32 weights, groups 32 / 128) at [3072, 12288]."""
     out = []
     s = torch.from_numpy(gwb.awq_scales_host(ad.cpu(), (0.5,))[0].numpy()).to(dev)
     mx = gwb.fold_mxfp4(Wd, s, "mul", want_folded=False)["mxfp4"]
@@ -196,9 +197,31 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
         ("gemv.uintx4_g64.lm_head_b1", hk / 2 + hk / 64 * 3 + 2 * HK + 4 * HN,
          cycle([gwb.prepare_gemv(q, xh, yh, wsu) for q in qu])),
     ]
-    for name, abytes, fn in cases + gemv_cases:
+    # uintx variants at the uintx workload shape [3072, 12288], 4 bits: float16 and
+    # float32 weights (group 64) and bf16 groups 32 and 128; enough copies cycled that
+    # the weights exceed the Infinity Cache
+    UN, UK = 3072, 12288
+    unk = UN * UK
+    var_cases = []
+    for dt, tdt, group in (("f16", torch.float16, 64), ("f32", torch.float32, 64),
+                           ("bf16", torch.bfloat16, 32), ("bf16", torch.bfloat16, 128)):
+        esz = torch.tensor([], dtype=tdt).element_size()
+        copies = -(-320 * 2 ** 20 // (esz * unk))
+        Ws = [workloads.uintx_weight(UN, UK, dtype=tdt).to(dev) for _ in range(copies)]
+        qs = [gwb.quantize(w, "uintx", nbits=4, group=group) for w in Ws]
+        ws = torch.empty(max(qs[0].sizes["workspace"], 16), dtype=torch.uint8, device=dev)
+        outs = [torch.empty(UN, UK, dtype=tdt, device=dev) for _ in range(copies)]
+        res = torch.empty(3, dtype=torch.float64, device=dev)
+        packed = unk / 2 + unk / group * (esz + 1)
+        tag = f"uintx4_{dt}_g{group}"
+        var_cases += [
+            (f"{tag}.quant", esz * unk + packed, cycle([gwb.prepare_quantize(w, q, ws) for w, q in zip(Ws, qs)])),
+            (f"{tag}.dequant", packed + esz * unk, cycle([gwb.prepare_dequantize(q, o) for q, o in zip(qs, outs)])),
+            (f"{tag}.snr", esz * unk + packed, cycle([gwb.prepare_snr(w, q, res, ws) for w, q in zip(Ws, qs)])),
+        ]
+    for name, abytes, fn in cases + gemv_cases + var_cases:
         us = _time_op(fn)
-        shape = [HN, HK] if name.startswith("gemv") else [N, K]
+        shape = [HN, HK] if name.startswith("gemv") else ([UN, UK] if name.startswith("uintx") else [N, K])
         out.append({"op": name, "shape": shape, "us": round(us, 2),
                     "hbm_GBps": round(abytes / (us * 1e-6) / 1e9, 1),
                     "frac_hbm_peak": round(abytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)})

@@ -20,13 +20,16 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgwb.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "common.hip", "mxfp4.hip", "gptq.hip", "uintx.hip", "uintx_flat.hip", "awq.hip", "fold.hip", "gemv.hip"]
-# The uintx, GPTQ and AWQ arithmetic never produces a NaN from finite weights and
-# scalings, and non-finite inputs are outside the method; without NaN semantics the
-# compiler drops the canonicalization it otherwise inserts around every float min/max.
-# (A NaN fp16 scale handed to GPTQ dequantization still yields NaN on either branch.)
-# uintx_flat.hip keeps NaN semantics: float16 weights can meet an infinite reciprocal.
-EXTRA = {name: ["-fno-honor-nans"] for name in ("uintx.hip", "gptq.hip", "awq.hip")}
+SOURCES = ["api.hip", "common.hip", "mxfp4.hip", "gptq.hip", "uintx.hip", "uintx_bf16.hip", "uintx_f16.hip", "uintx_f32.hip",
+           "uintx_flat.hip", "awq.hip", "fold.hip", "gemv.hip"]
+# The uintx, GPTQ and AWQ arithmetic feeds no NaN to a float op whose result is kept
+# (the one NaN uintx can make, a float16 zero weight times an infinite reciprocal, is
+# decided on the reciprocal's bits first), and non-finite inputs are outside the method;
+# without NaN semantics the compiler drops the canonicalization it otherwise inserts
+# around every float min/max. (A NaN fp16 scale handed to GPTQ dequantization still
+# yields NaN on either branch.)
+EXTRA = {name: ["-fno-honor-nans"] for name in ("uintx.hip", "uintx_bf16.hip", "uintx_f16.hip", "uintx_f32.hip",
+                                                "gptq.hip", "awq.hip")}
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     "-ffp-contract=off",

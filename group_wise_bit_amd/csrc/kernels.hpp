@@ -50,8 +50,9 @@ void launch_gptq_err(bool sym, int group, const void* W, int32_t w_dtype, int64_
                      int64_t ldw, const void* qweight, const void* scales, const void* qzeros,
                      double* part, hipStream_t st);
 
-// ---- UINTX (uintx.hip: tiled bf16 group-64 kernels when N*K % 512 == 0, which nest
-// the shard lengths; uintx_flat.hip: every dtype, group and shape). dt is the weight
+// ---- UINTX: tiled kernels (uintx_tiled.hpp) when N*K % (8 group) == 0, instantiated
+// for bf16 group 64 in uintx.hip and for the other (dtype, group) pairs in uintx_bf16.hip,
+// uintx_f16.hip, uintx_f32.hip; uintx_flat.hip for every other shape. dt is the weight
 // dtype (kBF16, kF16, kF32); group 32, 64 or 128.
 bool uintx_tiled(int32_t dt, int group, int64_t N, int64_t K);
 size_t uintx_code_workspace(int32_t dt, int group, int64_t N, int64_t K);
@@ -69,6 +70,17 @@ void launch_uintx_dequant_flat(int nbits, int32_t dt, int group, const void* pac
                                const void* zeros, int64_t N, int64_t K, void* out, int32_t out_dtype, int64_t ldo,
                                hipStream_t st);
 unsigned uintx_flat_err_blocks(int64_t N, int64_t K);
+#define GWB_UINTX_TILED_DT(SUF)                                                                                     \
+  void uintx_tiled_quant_##SUF(int nbits, int group, const void* W, int64_t N, int64_t K, int64_t ldw,              \
+                               void* packed, void* scales, void* zeros, hipStream_t st);                             \
+  void uintx_tiled_dequant_##SUF(int nbits, int group, const void* packed, const void* scales, const void* zeros,   \
+                                 int64_t N, int64_t K, void* out, int32_t out_dtype, int64_t ldo, hipStream_t st);  \
+  void uintx_tiled_err_##SUF(int nbits, int group, const void* W, int64_t N, int64_t K, int64_t ldw,                \
+                             const void* packed, const void* scales, const void* zeros, double* part, hipStream_t st);
+GWB_UINTX_TILED_DT(bf16)
+GWB_UINTX_TILED_DT(f16)
+GWB_UINTX_TILED_DT(f32)
+#undef GWB_UINTX_TILED_DT
 void launch_uintx_err_flat(int nbits, int32_t dt, int group, const void* W, int64_t N, int64_t K, int64_t ldw,
                            const void* packed, const void* scales, const void* zeros, double* part, hipStream_t st);
 

@@ -1,265 +1,16 @@
-// Affine uint2..uint7 (torchao-style, preserve_zero, bfloat16 arithmetic) quantize+
-// pack into planar power-of-two shards, unpack+dequantize, fused reconstruction error.
-// Page uintx_quant.py: _pack_shard, pack_uintx, unpack_uintx,
-// UIntXQuantizer._quantize_impl and _dequantize_native. Group 64 along K.
-//
-// Planar shards: byte i of the k-bit shard holds codes i, i+L, i+2L, ... (L = that
-// shard's byte count), which lie far apart in the matrix. With numel % 512 == 0 the
-// shard lengths nest (L_1 = numel/8, L_2 = 2 L_1, L_4 = 4 L_1): the codes at position
-// p of the 8 segments j*L_1 + p (j = 0..7) fill byte p of the 1-bit shard, bytes
-// p and L_1 + p of the 2-bit shard and bytes m*L_1 + p (m < 4) of the 4-bit shard, and
-// nothing else. So a lane that loads the same 8 positions of all 8 segments owns
-// complete output bytes and assembles them in registers. Segments start on group
-// boundaries, so each group's qparams stay within the 8 lanes that hold it.
-// Other sizes take a two-pass path: codes to workspace, then one thread per byte.
+// Affine uint2..uint7 (torchao-style, preserve_zero): the bfloat16 / group-64 tiled
+// kernels (page uintx_quant.py's defaults), the decode GEMV on packed uintx weights, and
+// the launch selection for every dtype and group. Page uintx_quant.py: pack_uintx,
+// unpack_uintx, UIntXQuantizer._quantize_impl, _dequantize_native and forward.
+// The tiled kernels (uintx_tiled.hpp) need numel % 8G == 0; their other instantiations
+// live in uintx_f16.hip, uintx_f32.hip and uintx_bf16.hip, and every other shape takes
+// the two-pass path of uintx_flat.hip.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "uintx_layout.hpp"
+#include "uintx_tiled.hpp"
 
 namespace gwb {
-
-// Tiled path geometry: a lane takes 8 consecutive positions p of all 8 segments
-// (elements j*L1 + p), a wavefront 512 positions, a block of 4 wavefronts 2048.
-constexpr int kLanePos = 8;
-constexpr int kWavePos = 64 * kLanePos;
-constexpr int kBlockPos = 4 * kWavePos;
-
-// Group qparams from the group's min and max (every op a float32 op rounded to bf16):
-// mn = min(min, 0), mx = max(max, 0); scale = bf(bf(mx - mn) / qmax), at least 2^-23;
-// zp = clamp(-rint(bf(mn / scale)), 0, qmax); inv = bf(1 / scale).
-struct QP { float s, inv, zp; };
-__device__ __forceinline__ QP uintx_qparams(float mn, float mx, float qmax) {
-  float mnn = fminf(mn, 0.0f), mxp = fmaxf(mx, 0.0f);
-  float s = round_bf16(round_bf16(mxp - mnn) / qmax);
-  s = fmaxf(s, 0x1p-23f);
-  float zp = fminf(fmaxf(-rintf(round_bf16(mnn / s)), 0.0f), qmax);
-  return QP{s, round_bf16(1.0f / s), zp};
-}
-// q = clamp(rint(bf(w * inv)) + zp, 0, qmax). The page rounds the sum to bf16 before
-// the clamp; rounding is monotonic and 0 and qmax are bf16 integers, so the clamped
-// result is the same.
-__device__ __forceinline__ uint32_t uintx_code(float x, const QP& q, float qmax) {
-  float t = round_bf16(x * q.inv);
-  return (uint32_t)fminf(fmaxf(rintf(t) + q.zp, 0.0f), qmax);
-}
-// bf(bf(q - zp) * scale): q - zp is an exact small integer, the product is exact in
-// float32, so this is one rounding.
-__device__ __forceinline__ float uintx_value(uint32_t c, float zp, float s) {
-  return round_bf16(((float)c - zp) * s);
-}
-
-typedef __bf16 ux_bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float ux_f32x2_t __attribute__((ext_vector_type(2)));
-// Two float32 rounded to bf16 (RNE, the hardware pair conversion), back as float32.
-__device__ __forceinline__ void round_bf16_pair(float& a, float& b) {
-  const uint32_t r = __builtin_bit_cast(uint32_t, __builtin_convertvector(ux_f32x2_t{a, b}, ux_bf16x2_t));
-  a = __uint_as_float(r << 16);
-  b = __uint_as_float(r & 0xFFFF0000u);
-}
-
-// Codes of 8 bf16 weights (one 16-byte load) as bytes: lo = positions 0..3, hi = 4..7.
-__device__ __forceinline__ void codes8(U4 v, float inv, float zp, float qmax, uint32_t& lo, uint32_t& hi) {
-  float x[8];
-  x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
-  x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] *= inv;                      // exact: 8-bit x 8-bit significands
-#pragma unroll
-  for (int i = 0; i < 8; i += 2) round_bf16_pair(x[i], x[i + 1]);
-  uint32_t w[2] = {0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float c = __builtin_amdgcn_fmed3f(rintf(x[i]) + zp, 0.0f, qmax);
-    w[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(c, i & 3, w[i >> 2]);
-  }
-  lo = w[0];
-  hi = w[1];
-}
-
-template <bool CONTIG, typename T>
-__device__ __forceinline__ T* elem_ptr(T* base, int64_t ld, uint32_t e, FastDiv kdiv) {
-  if constexpr (CONTIG) return base + e;
-  const uint32_t n = fdiv(e, kdiv);
-  return base + (int64_t)n * ld + (e - n * kdiv.d);
-}
-
-__device__ __forceinline__ void st8(uint8_t* p, uint32_t lo, uint32_t hi) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
-}
-__device__ __forceinline__ uint2 ld8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
-
-// ------------------------------------------------------------- tiled quantize
-// One block per 2048 positions. Per lane: 8 loads (one per segment) in flight; per
-// segment a DPP min/max over the 8 lanes that share each 64-weight group; each of
-// those lanes then computes the qparams of one segment's group (lane & 7) and they
-// exchange (1/scale, zp) through LDS; codes are assembled into shard bytes in registers.
-template <int NB, bool CONTIG>
-__global__ __launch_bounds__(256) void uintx_quant_tiled(const uint16_t* __restrict__ W, int64_t ldw, FastDiv kdiv,
-                                                         uint32_t L1, Shards sh, uint8_t* __restrict__ packed,
-                                                         uint16_t* __restrict__ scales,
-                                                         uint8_t* __restrict__ zeros) {
-  using SB = ShardBits<NB>;
-  __shared__ uint32_t qp_lds[256];
-  const float qmax = (float)((1 << NB) - 1);
-  const int lane = threadIdx.x & 63;
-  const uint32_t p = blockIdx.x * kBlockPos + (threadIdx.x >> 6) * kWavePos + lane * kLanePos;
-  const bool active = p < L1;                // whole groups of 8 lanes: L1 % 64 == 0
-  U4 raw[8];
-  if (active) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) raw[j] = ld16_nt(elem_ptr<CONTIG>(W, ldw, j * L1 + p, kdiv));
-    // Extremes on order-preserving keys: a word of two bf16 read as a float32 orders
-    // like its upper weight (the lower one only extends the mantissa), the word rotated
-    // by 16 bits like its lower weight; clearing the low 16 bits of the extreme key
-    // gives that weight exactly.
-    float mn[8], mx[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t w4[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
-      float k[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        k[q] = __uint_as_float(w4[q]);
-        k[q + 4] = __uint_as_float((w4[q] >> 16) | (w4[q] << 16));
-      }
-      float a = k[0], b = k[0];
-#pragma unroll
-      for (int q = 1; q < 8; ++q) {
-        a = fminf(a, k[q]);
-        b = fmaxf(b, k[q]);
-      }
-      mn[j] = lanes_min<8>(a);
-      mx[j] = lanes_max<8>(b);
-    }
-    const int i = lane & 7;                  // this lane's segment for the qparams
-    float mni = mn[0], mxi = mx[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) {
-      mni = i == j ? mn[j] : mni;
-      mxi = i == j ? mx[j] : mxi;
-    }
-    const QP q = uintx_qparams(__uint_as_float(__float_as_uint(mni) & 0xFFFF0000u),
-                               __uint_as_float(__float_as_uint(mxi) & 0xFFFF0000u), qmax);
-    const uint32_t g = (i * L1 + (p - i * kLanePos)) / 64;
-    scales[g] = (uint16_t)(__float_as_uint(q.s) >> 16);
-    zeros[g] = (uint8_t)q.zp;
-    qp_lds[threadIdx.x] = (__float_as_uint(q.inv) & 0xFFFF0000u) | (uint32_t)q.zp;
-  }
-  __syncthreads();
-  if (!active) return;
-  const uint32_t* qpo = &qp_lds[threadIdx.x & ~7u];
-  uint32_t clo[8], chi[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t w = qpo[j];
-    codes8(raw[j], __uint_as_float(w & 0xFFFF0000u), (float)(w & 0xFFu), qmax, clo[j], chi[j]);
-  }
-  if constexpr (SB::has4) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      st8(packed + sh.base4 + (int64_t)m * L1 + p, (clo[m] & 0x0F0F0F0Fu) | ((clo[m + 4] & 0x0F0F0F0Fu) << 4),
-          (chi[m] & 0x0F0F0F0Fu) | ((chi[m + 4] & 0x0F0F0F0Fu) << 4));
-  }
-  if constexpr (SB::has2) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        lo |= ((clo[m + 2 * jj] >> SB::off2) & 0x03030303u) << (2 * jj);
-        hi |= ((chi[m + 2 * jj] >> SB::off2) & 0x03030303u) << (2 * jj);
-      }
-      st8(packed + sh.base2 + (int64_t)m * L1 + p, lo, hi);
-    }
-  }
-  if constexpr (SB::has1) {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      lo |= ((clo[j] >> SB::off1) & 0x01010101u) << j;
-      hi |= ((chi[j] >> SB::off1) & 0x01010101u) << j;
-    }
-    st8(packed + sh.base1 + p, lo, hi);
-  }
-}
-
-// ------------------------------------------------------------- tiled dequantize
-template <int NB, int SINK, bool CONTIG, typename TOut>
-__global__ __launch_bounds__(256) void uintx_dequant_tiled(const uint8_t* __restrict__ packed,
-                                                           const uint16_t* __restrict__ scales,
-                                                           const uint8_t* __restrict__ zeros, FastDiv kdiv,
-                                                           uint32_t L1, Shards sh, TOut* __restrict__ out,
-                                                           int64_t ldo, const uint16_t* __restrict__ W, int64_t ldw,
-                                                           double* __restrict__ part) {
-  using SB = ShardBits<NB>;
-  __shared__ uint32_t qp_lds[256];
-  const int lane = threadIdx.x & 63;
-  const uint32_t p = blockIdx.x * kBlockPos + (threadIdx.x >> 6) * kWavePos + lane * kLanePos;
-  const bool active = p < L1;
-  uint2 s4[4], s2[2], s1;
-  U4 wr[8];                                  // the error sink's weights
-  if (active) {
-    // The group's scale and zero point go first: the LDS exchange waits only for them,
-    // while the shard bytes and the weights stay in flight across the barrier.
-    const int i = lane & 7;
-    const uint32_t g = (i * L1 + (p - i * kLanePos)) / 64;
-    const uint32_t sc = scales[g], zz = zeros[g];
-    if constexpr (SB::has4) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) s4[m] = ld8(packed + sh.base4 + (int64_t)m * L1 + p);
-    }
-    if constexpr (SB::has2) {
-#pragma unroll
-      for (int m = 0; m < 2; ++m) s2[m] = ld8(packed + sh.base2 + (int64_t)m * L1 + p);
-    }
-    if constexpr (SB::has1) s1 = ld8(packed + sh.base1 + p);
-    if constexpr (SINK == kErr) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) wr[j] = ld16_nt(elem_ptr<CONTIG>(W, ldw, j * L1 + p, kdiv));
-    }
-    qp_lds[threadIdx.x] = (sc << 16) | zz;
-  }
-  __syncthreads();
-  double sw = 0.0, se = 0.0;
-  if (active) {
-    const uint32_t* qpo = &qp_lds[threadIdx.x & ~7u];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t w = qpo[j];
-      const float s = __uint_as_float(w & 0xFFFF0000u), zp = (float)(w & 0xFFu);
-      uint32_t c[2] = {0u, 0u};
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if constexpr (SB::has4) c[h] |= ((h ? s4[j & 3].y : s4[j & 3].x) >> (4 * (j >> 2))) & 0x0F0F0F0Fu;
-        if constexpr (SB::has2) c[h] |= (((h ? s2[j & 1].y : s2[j & 1].x) >> (2 * (j >> 1))) & 0x03030303u) << SB::off2;
-        if constexpr (SB::has1) c[h] |= (((h ? s1.y : s1.x) >> j) & 0x01010101u) << SB::off1;
-      }
-      float d[8];
-#pragma unroll
-      for (int b = 0; b < 8; ++b) d[b] = ((float)((c[b >> 2] >> (8 * (b & 3))) & 0xFFu) - zp) * s;   // exact
-      const uint32_t e = j * L1 + p;
-      if constexpr (SINK == kStore && sizeof(TOut) == 2) {
-        U4 v;
-        v.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(ux_f32x2_t{d[0], d[1]}, ux_bf16x2_t));
-        v.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(ux_f32x2_t{d[2], d[3]}, ux_bf16x2_t));
-        v.z = __builtin_bit_cast(uint32_t, __builtin_convertvector(ux_f32x2_t{d[4], d[5]}, ux_bf16x2_t));
-        v.w = __builtin_bit_cast(uint32_t, __builtin_convertvector(ux_f32x2_t{d[6], d[7]}, ux_bf16x2_t));
-        st16_nt(elem_ptr<CONTIG>(out, ldo, e, kdiv), v);
-        continue;
-      }
-#pragma unroll
-      for (int b = 0; b < 8; b += 2) round_bf16_pair(d[b], d[b + 1]);
-      if constexpr (SINK == kStore) {
-        store8(elem_ptr<CONTIG>(out, ldo, e, kdiv), d);
-      } else {
-        float x[8];
-        to_f32(Raw8<uint16_t>{wr[j]}, x);
-        acc_err8(x, d, sw, se);
-      }
-    }
-  }
-  if constexpr (SINK == kErr) block_sum2_store<256>(sw, se, part);
-}
 
 // ------------------------------------------------------------- decode GEMV
 // y[b, n] = sum_k x[b, k] * w[n, k] with w = bf16((q - zp) * s), the bf16 weight the
@@ -378,64 +129,25 @@ __global__ __launch_bounds__(256) void uintx_gemv_tiled(const uint8_t* __restric
 
 // ------------------------------------------------------------------ launchers
 bool uintx_tiled(int32_t dt, int group, int64_t N, int64_t K) {
-  return dt == kBF16 && group == 64 && ((N * K) % 512) == 0;
+  (void)dt;
+  return uintx_tiles_fit(group, N * K);
 }
 size_t uintx_code_workspace(int32_t dt, int group, int64_t N, int64_t K) {
   return uintx_tiled(dt, group, N, K) ? 0 : (size_t)(N * K);
 }
 
-static unsigned tiles_of(int64_t N, int64_t K) { return (unsigned)(((uint64_t)(N * K) / 8 + kBlockPos - 1) / kBlockPos); }
-
-template <int NB>
-static void quant_tiled(const void* W, int64_t N, int64_t K, int64_t ldw, void* packed, void* scales, void* zeros,
-                        hipStream_t st) {
-  const uint32_t numel = (uint32_t)(N * K);
-  const Shards sh = shards_of(NB, numel);
-  const FastDiv kdiv = make_fastdiv((uint32_t)K);
-  hipLaunchKernelGGL((ldw == K ? uintx_quant_tiled<NB, true> : uintx_quant_tiled<NB, false>), dim3(tiles_of(N, K)),
-                     dim3(256), 0, st, (const uint16_t*)W, ldw, kdiv, numel / 8, sh, (uint8_t*)packed,
-                     (uint16_t*)scales, (uint8_t*)zeros);
-}
-
 void launch_uintx_quant(int nbits, int32_t dt, int group, const void* W, int64_t N, int64_t K, int64_t ldw,
                         void* packed, void* scales, void* zeros, void* workspace, hipStream_t st) {
-  if (!uintx_tiled(dt, group, N, K)) {
+  if (!uintx_tiled(dt, group, N, K))
     launch_uintx_quant_flat(nbits, dt, group, W, N, K, ldw, packed, scales, zeros, workspace, st);
-    return;
-  }
-  switch (nbits) {
-    case 2: quant_tiled<2>(W, N, K, ldw, packed, scales, zeros, st); break;
-    case 3: quant_tiled<3>(W, N, K, ldw, packed, scales, zeros, st); break;
-    case 4: quant_tiled<4>(W, N, K, ldw, packed, scales, zeros, st); break;
-    case 5: quant_tiled<5>(W, N, K, ldw, packed, scales, zeros, st); break;
-    case 6: quant_tiled<6>(W, N, K, ldw, packed, scales, zeros, st); break;
-    default: quant_tiled<7>(W, N, K, ldw, packed, scales, zeros, st); break;
-  }
-}
-
-template <int NB, int SINK, typename TOut>
-static void deq_tiled(const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K, void* out,
-                      int64_t ldo, const void* W, int64_t ldw, double* part, hipStream_t st) {
-  const uint32_t numel = (uint32_t)(N * K);
-  const Shards sh = shards_of(NB, numel);
-  const FastDiv kdiv = make_fastdiv((uint32_t)K);
-  const bool contig = SINK == kStore ? ldo == K : ldw == K;
-  hipLaunchKernelGGL((contig ? uintx_dequant_tiled<NB, SINK, true, TOut> : uintx_dequant_tiled<NB, SINK, false, TOut>),
-                     dim3(tiles_of(N, K)), dim3(256), 0, st, (const uint8_t*)packed, (const uint16_t*)scales,
-                     (const uint8_t*)zeros, kdiv, numel / 8, sh, (TOut*)out, ldo, (const uint16_t*)W, ldw, part);
-}
-
-template <int SINK, typename TOut>
-static void deq_tiled_nb(int nbits, const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K,
-                         void* out, int64_t ldo, const void* W, int64_t ldw, double* part, hipStream_t st) {
-  switch (nbits) {
-    case 2: deq_tiled<2, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
-    case 3: deq_tiled<3, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
-    case 4: deq_tiled<4, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
-    case 5: deq_tiled<5, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
-    case 6: deq_tiled<6, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
-    default: deq_tiled<7, SINK, TOut>(packed, scales, zeros, N, K, out, ldo, W, ldw, part, st); break;
-  }
+  else if (dt == kBF16 && group == 64)
+    ux_tiled_quant_entry<kBF16, 64>(nbits, W, N, K, ldw, packed, scales, zeros, st);
+  else if (dt == kBF16)
+    uintx_tiled_quant_bf16(nbits, group, W, N, K, ldw, packed, scales, zeros, st);
+  else if (dt == kF16)
+    uintx_tiled_quant_f16(nbits, group, W, N, K, ldw, packed, scales, zeros, st);
+  else
+    uintx_tiled_quant_f32(nbits, group, W, N, K, ldw, packed, scales, zeros, st);
 }
 
 void launch_uintx_dequant(int nbits, int32_t dt, int group, const void* packed, const void* scales,
@@ -443,24 +155,34 @@ void launch_uintx_dequant(int nbits, int32_t dt, int group, const void* packed, 
                           hipStream_t st) {
   if (!uintx_tiled(dt, group, N, K))
     launch_uintx_dequant_flat(nbits, dt, group, packed, scales, zeros, N, K, out, out_dtype, ldo, st);
-  else if (out_dtype == kBF16)
-    deq_tiled_nb<kStore, uint16_t>(nbits, packed, scales, zeros, N, K, out, ldo, nullptr, 0, nullptr, st);
+  else if (dt == kBF16 && group == 64)
+    ux_tiled_dequant_entry<kBF16, 64>(nbits, packed, scales, zeros, N, K, out, out_dtype, ldo, st);
+  else if (dt == kBF16)
+    uintx_tiled_dequant_bf16(nbits, group, packed, scales, zeros, N, K, out, out_dtype, ldo, st);
+  else if (dt == kF16)
+    uintx_tiled_dequant_f16(nbits, group, packed, scales, zeros, N, K, out, out_dtype, ldo, st);
   else
-    deq_tiled_nb<kStore, float>(nbits, packed, scales, zeros, N, K, out, ldo, nullptr, 0, nullptr, st);
+    uintx_tiled_dequant_f32(nbits, group, packed, scales, zeros, N, K, out, out_dtype, ldo, st);
 }
 
-// The tiled error kernel runs one block per tile (its partials follow the tiles); the
+// The tiled error kernels run one block per tile (their partials follow the tiles); the
 // flat one is grid-stride with a capped grid. Both depend on the shape only.
 unsigned uintx_err_blocks(int32_t dt, int group, int64_t N, int64_t K) {
-  return uintx_tiled(dt, group, N, K) ? tiles_of(N, K) : uintx_flat_err_blocks(N, K);
+  return uintx_tiled(dt, group, N, K) ? uintx_tiles(N * K) : uintx_flat_err_blocks(N, K);
 }
 
 void launch_uintx_err(int nbits, int32_t dt, int group, const void* W, int64_t N, int64_t K, int64_t ldw,
                       const void* packed, const void* scales, const void* zeros, double* part, hipStream_t st) {
-  if (uintx_tiled(dt, group, N, K))
-    deq_tiled_nb<kErr, float>(nbits, packed, scales, zeros, N, K, nullptr, 0, W, ldw, part, st);
-  else
+  if (!uintx_tiled(dt, group, N, K))
     launch_uintx_err_flat(nbits, dt, group, W, N, K, ldw, packed, scales, zeros, part, st);
+  else if (dt == kBF16 && group == 64)
+    ux_tiled_err_entry<kBF16, 64>(nbits, W, N, K, ldw, packed, scales, zeros, part, st);
+  else if (dt == kBF16)
+    uintx_tiled_err_bf16(nbits, group, W, N, K, ldw, packed, scales, zeros, part, st);
+  else if (dt == kF16)
+    uintx_tiled_err_f16(nbits, group, W, N, K, ldw, packed, scales, zeros, part, st);
+  else
+    uintx_tiled_err_f32(nbits, group, W, N, K, ldw, packed, scales, zeros, part, st);
 }
 
 }  // namespace gwb

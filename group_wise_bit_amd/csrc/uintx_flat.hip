@@ -8,38 +8,13 @@
 // Quantization takes two passes: codes of 8 consecutive weights per lane (G/8 lanes
 // per group, DPP min/max) to a workspace, then one thread per byte of each shard.
 // Dequantization and the fused error sink gather each code from its shards.
-//
-// This file keeps IEEE NaN semantics: for float16 a group whose scale is below about
-// 2^-16 has an infinite reciprocal, so a zero weight's w * inv is NaN, and the clamp
-// max(NaN, 0) = 0 (maxNum returns the number) gives it code 0, the value torch's float
-// to uint8 conversion gives that NaN; +inf and -inf clamp to qmax and 0.
+// The per-dtype arithmetic (uintx_math.hpp) is shared with the tiled kernels.
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "uintx_layout.hpp"
+#include "uintx_math.hpp"
 
 namespace gwb {
-
-// Per weight dtype: the storage word, rounding of a float32 result to the dtype, the
-// value of a stored scale word and the word of a value that is already of the dtype.
-template <int DT> struct UxDt;
-template <> struct UxDt<kBF16> {
-  using T = uint16_t;
-  static __device__ __forceinline__ float rnd(float x) { return round_bf16(x); }
-  static __device__ __forceinline__ float value(T h) { return __uint_as_float((uint32_t)h << 16); }
-  static __device__ __forceinline__ T word(float v) { return (T)(__float_as_uint(v) >> 16); }
-};
-template <> struct UxDt<kF16> {
-  using T = uint16_t;
-  static __device__ __forceinline__ float rnd(float x) { return (float)(_Float16)x; }   // RNE, v_cvt_f16_f32
-  static __device__ __forceinline__ float value(T h) { return (float)__builtin_bit_cast(_Float16, h); }
-  static __device__ __forceinline__ T word(float v) { return __builtin_bit_cast(T, (_Float16)v); }
-};
-template <> struct UxDt<kF32> {
-  using T = float;
-  static __device__ __forceinline__ float rnd(float x) { return x; }
-  static __device__ __forceinline__ float value(T h) { return h; }
-  static __device__ __forceinline__ T word(float v) { return v; }
-};
 
 // 8 consecutive weights (16-byte aligned) as float32.
 template <int DT>
@@ -51,8 +26,8 @@ __device__ __forceinline__ void load8_dt(const typename UxDt<DT>::T* p, float* x
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      x[2 * q] = UxDt<DT>::value((uint16_t)(w[q] & 0xFFFFu));
-      x[2 * q + 1] = UxDt<DT>::value((uint16_t)(w[q] >> 16));
+      x[2 * q] = UxDt<DT>::value(w[q] & 0xFFFFu);
+      x[2 * q + 1] = UxDt<DT>::value(w[q] >> 16);
     }
   }
 }
@@ -61,32 +36,6 @@ __device__ __forceinline__ void load8_at(const typename UxDt<DT>::T* W, int64_t 
                                          float* x) {
   const uint32_t n = fdiv(e, kdiv);
   load8_dt<DT>(W + (int64_t)n * ldw + (e - n * kdiv.d), x);
-}
-
-// Group qparams: mn = min(min, 0), mx = max(max, 0); scale = r(r(mx - mn) / qmax), at
-// least 2^-23; zp = clamp(-rint(r(mn / scale)), 0, qmax); inv = r(1 / scale).
-struct UxQP { float s, inv, zp; };
-template <int DT>
-__device__ __forceinline__ UxQP ux_qparams(float mn, float mx, float qmax) {
-  using D = UxDt<DT>;
-  const float mnn = fminf(mn, 0.0f), mxp = fmaxf(mx, 0.0f);
-  const float s = fmaxf(D::rnd(D::rnd(mxp - mnn) / qmax), 0x1p-23f);
-  const float zp = fminf(fmaxf(-rintf(D::rnd(mnn / s)), 0.0f), qmax);
-  return UxQP{s, D::rnd(1.0f / s), zp};
-}
-// q = clamp(rint(r(w * inv)) + zp, 0, qmax); the page rounds the sum to the dtype
-// before the clamp, which changes nothing: the sum is an integer below 2^11 or +-inf.
-template <int DT>
-__device__ __forceinline__ uint32_t ux_code(float x, const UxQP& q, float qmax) {
-  const float t = UxDt<DT>::rnd(x * q.inv);
-  return (uint32_t)fminf(fmaxf(rintf(t) + q.zp, 0.0f), qmax);
-}
-// r(r(q - zp) * scale): q - zp is an exact small integer; the product is exact in
-// float32 for the 2-byte dtypes (one rounding to the dtype) and one float32 rounding
-// for float32 weights.
-template <int DT>
-__device__ __forceinline__ float ux_value(uint32_t c, float zp, float s) {
-  return UxDt<DT>::rnd(((float)c - zp) * s);
 }
 
 // Pass 1: codes of 8 consecutive elements per lane to workspace, G/8 lanes per group.

@@ -50,15 +50,18 @@ def test_sizes_match_layouts():
     # ragged uintx: shards padded independently, workspace for the two-pass path
     rc, s = _sizes("uintx", 1, 64, nbits=5)
     assert rc == 0 and s.codes == 32 + 8 and s.workspace >= 64
-    # the uintx scale has the weight dtype; groups 32 and 128; non-bf16 / non-64 groups
-    # take the two-pass path (codes workspace of N*K bytes)
+    # the uintx scale has the weight dtype; groups 32 and 128. N*K % (8 group) == 0 takes
+    # the tiled kernels (error partials only), other shapes the two-pass path (a codes
+    # workspace of N*K bytes)
     rc, s = _sizes("uintx", 64, 512, nbits=4, group=32, dt=gwb.F32)
-    assert rc == 0 and s.scales == 64 * 16 * 4 and s.zeros == 64 * 16 and s.workspace >= 64 * 512
+    assert rc == 0 and s.scales == 64 * 16 * 4 and s.zeros == 64 * 16 and s.workspace < 64 * 512
     rc, s = _sizes("uintx", 64, 512, nbits=3, group=128, dt=gwb.F16)
     assert rc == 0 and s.scales == 64 * 4 * 2 and s.zeros == 64 * 4 and s.codes == 64 * 512 * 3 // 8
-    assert s.workspace >= 64 * 512
-    rc, s = _sizes("uintx", 64, 512, nbits=3, group=64, dt=gwb.BF16)
-    assert rc == 0 and s.workspace < 64 * 512                  # tiled: error partials only
+    assert s.workspace < 64 * 512
+    rc, s = _sizes("uintx", 3, 256, nbits=3, group=128, dt=gwb.F16)      # 768 % 1024 != 0
+    assert rc == 0 and s.workspace >= 3 * 256
+    rc, s = _sizes("uintx", 3, 256, nbits=3, group=32, dt=gwb.F16)       # 768 % 256 == 0
+    assert rc == 0 and s.workspace < 3 * 256
 
 
 def test_bits_per_weight_from_sizes():
