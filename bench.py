@@ -63,7 +63,8 @@ def algo_bytes(op: str, fmt: str, nbits: int, n: int, k: int) -> float:
 KERNEL_SOURCES = {   # what each op's kernel is compiled from (for the traffic record's digest)
     "mxfp4": ["mxfp4.hip", "mxfp4_math.hpp", "device_common.hpp", "kernels.hpp"],
     "gptq": ["gptq.hip", "device_common.hpp", "kernels.hpp"],
-    "uintx": ["uintx.hip", "uintx_layout.hpp", "device_common.hpp", "kernels.hpp"],
+    "uintx": ["uintx.hip", "uintx_tiled.hpp", "uintx_math.hpp", "uintx_layout.hpp", "device_common.hpp",
+              "kernels.hpp"],
     "awq": ["awq.hip", "mxfp4_math.hpp", "device_common.hpp", "kernels.hpp"],
 }
 
@@ -234,6 +235,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the paths timed beside the step (keeps a profile to the step's kernels)")
     ap.add_argument("--cpu-rows", type=int, default=6528)          # 17 x 384: the step's 17:1 ratio
     ap.add_argument("--cpu-awq-rows", type=int, default=384)
     args = ap.parse_args()
@@ -330,7 +333,7 @@ def main():
     weight_bytes_step = sum(op[3] for op in ops)
     value = weight_bytes_step / (ms_per_step * 1e-3) / 1e9
 
-    extras = measure_extras(gwb, workloads, Wd, ad, dev)
+    extras = None if args.no_extras else measure_extras(gwb, workloads, Wd, ad, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
