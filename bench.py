@@ -8,10 +8,14 @@ reconstruction SNR; then the AWQ alpha search (11 alphas) on the 2048-row stride
 subsample. Inputs are resident in HBM before timing starts.
 
 value = weight GB/s = (2 bytes * N * K) * (quantize + dequantize passes) / step time.
-The roofline object is for the kernel with the largest share of the step: its
-algorithmic bytes per launch / its average HIP-event duration, against 8 TB/s.
+The timed steps carry no per-op markers (an event pair around each of the 40 launches
+costs about 0.2 ms of the step): an untimed pass with an event pair per op gives the
+breakdown and names the op with the largest share, and in the timed steps one event
+pair brackets that op alone. The roofline object is for that kernel: its algorithmic
+bytes per launch / its average HIP-event duration in the timed steps, against 8 TB/s.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--breakdown-steps 10]
+                    [--no-cpu-baseline] [--no-extras]
 """
 from __future__ import annotations
 
@@ -234,6 +238,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--breakdown-steps", type=int, default=10,
+                    help="untimed steps with an event pair per op (the per-op breakdown)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the paths timed beside the step (keeps a profile to the step's kernels)")
@@ -294,30 +300,42 @@ def main():
     copy_gbps = 2 * (1 << 30) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del src, dst
 
-    # one event pair per op per step, created before the timed region
+    # event pairs created before anything is timed
+    bd_steps = max(args.breakdown_steps, 1)
     evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ops]
-           for _ in range(args.steps)]
+           for _ in range(bd_steps)]
+    dom_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
 
-    def step(pairs):
+    def step(pairs=None, mark=None, mark_pair=None):
         for i, op in enumerate(ops):
-            if pairs is not None:
-                pairs[i][0].record()
+            ev = pairs[i] if pairs is not None else (mark_pair if i == mark else None)
+            if ev is not None:
+                ev[0].record()
             op[4]()
-            if pairs is not None:
-                pairs[i][1].record()
+            if ev is not None:
+                ev[1].record()
 
     for _ in range(args.warmup):
-        step(None)
+        step()
+    # untimed breakdown pass: one event pair per op
+    for s in range(bd_steps):
+        step(pairs=evs[s])
+    torch.cuda.synchronize()
+    durs = np.array([[e0.elapsed_time(e1) for e0, e1 in pairs] for pairs in evs])   # ms
+    avg = durs.mean(axis=0)
+    dom = int(np.argmax(avg))
+
+    # timed region: the step as a caller runs it; one event pair around the dominant op
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(evs[s])
+        step(mark=dom, mark_pair=dom_evs[s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dom_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in dom_evs]))
 
-    durs = np.array([[e0.elapsed_time(e1) for e0, e1 in pairs] for pairs in evs])   # ms
-    avg = durs.mean(axis=0)
     breakdown = []
     for i, (name, key, abytes, wbytes, _) in enumerate(ops):
         breakdown.append({
@@ -326,9 +344,8 @@ def main():
             "frac_hbm_peak": round(abytes / (avg[i] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "weight_GBps": round(wbytes / (avg[i] * 1e-3) / 1e9, 1) if wbytes else None,
         })
-    dom = int(np.argmax(avg))
     dname, dkey, dbytes = ops[dom][0], ops[dom][1], ops[dom][2]
-    achieved = dbytes / (avg[dom] * 1e-3) / 1e9
+    achieved = dbytes / (dom_ms * 1e-3) / 1e9
     traffic = measured_traffic(dname)
     weight_bytes_step = sum(op[3] for op in ops)
     value = weight_bytes_step / (ms_per_step * 1e-3) / 1e9
@@ -364,10 +381,11 @@ def main():
             "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": int(dbytes), "avg_launch_us": round(avg[dom] * 1e3, 2),
+            "algorithmic_bytes_per_launch": int(dbytes), "avg_launch_us": round(dom_ms * 1e3, 2),
         },
         "cpu_baseline": cpu,
         "copy_ceiling_GBps": round(copy_gbps, 1),
+        "breakdown_steps": bd_steps,
         "breakdown": breakdown,
         "extras": extras,
     }
