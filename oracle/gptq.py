@@ -9,7 +9,15 @@ Layouts (GPTQ stores the transposed weight [K, N]):
   qzeros  int32 [K/G, N/8] nibble i of word (g, q) = zero point of (g, n = 8q + i);
                            symmetric: every nibble 7; asymmetric: the zero point
   scales  fp16  [K/G, N]   the float32 group scale rounded to fp16 (RNE)
-  g_idx   int32 [K]        k // G
+  g_idx   int32 [K]        k // G; act-order (quantize_act_order): the group of column k
+
+Act-order (the "desc_act" field the page writes into its quantization_config as False,
+and the g_idx tensor it stores): GPTQ checkpoints with desc_act true form the groups over
+the input channels taken in a given order (by decreasing activation statistic) rather
+than in index order, keep qweight in the original channel order, and record each
+channel's group in g_idx; a consumer dequantizes channel k with the scale and zero point
+of group g_idx[k]. Reading: the page's own per-group formulas (quantize_sym /
+quantize_asym) applied to those groups.
 """
 from __future__ import annotations
 
@@ -110,6 +118,24 @@ def quantize_asym(w, group: int = 128):
     )
 
 
+def quantize_act_order(w, group: int, sym: bool, perm):
+    """Act-order variant: group g = the columns perm[g*G : (g+1)*G] (perm a permutation of
+    0..K-1). Scales and zero points [K/G, N] per such group as quantize_sym /
+    quantize_asym compute them; codes and qweight in the original column order;
+    g_idx[k] = the group of column k."""
+    x = f32(w)
+    k = x.shape[1]
+    perm = np.asarray(perm, np.int64)
+    assert perm.shape == (k,) and np.array_equal(np.sort(perm), np.arange(k)), "perm must be a permutation"
+    q = (quantize_sym if sym else quantize_asym)(x[:, perm], group)   # groups over the permuted columns
+    codes = np.empty_like(q["codes"])                                 # [K, N]: back to column order
+    codes[perm] = q["codes"]
+    g_idx = np.empty(k, np.int32)
+    g_idx[perm] = (np.arange(k) // group).astype(np.int32)
+    q.update(qweight=pack_int32(codes, 0), codes=codes, g_idx=g_idx)
+    return q
+
+
 def _snr_page(wt, deq) -> float:
     """20 log10(||w|| / max(||w - deq||, 1e-12)) with float64 norms of float32 data."""
     num = np.sqrt(np.sum(wt.astype(np.float64) ** 2))
@@ -118,10 +144,11 @@ def _snr_page(wt, deq) -> float:
         return float(20.0 * np.log10(num / den))
 
 
-def dequantize(qweight, scales, qzeros, group: int, sym: bool) -> np.ndarray:
+def dequantize(qweight, scales, qzeros, group: int, sym: bool, g_idx=None) -> np.ndarray:
     """Stored tensors -> float32 [N, K] (the caller's layout). Symmetric:
     (code - 8) * scale, qzeros ignored; asymmetric: (code - zp) * scale, zp read from
-    qzeros. The scale is the stored fp16 value widened to float32."""
+    qzeros. The scale is the stored fp16 value widened to float32. Column k uses group
+    k // G, or g_idx[k] when g_idx is given (act-order)."""
     codes = unpack_int32(qweight, 0).astype(np.float32)            # [K, N]
     k, n = codes.shape
     s = np.asarray(scales, np.float16).astype(np.float32)           # [G, N]
@@ -129,8 +156,9 @@ def dequantize(qweight, scales, qzeros, group: int, sym: bool) -> np.ndarray:
         zp = np.full(s.shape, 8.0, np.float32)
     else:
         zp = unpack_int32(qzeros, 1).astype(np.float32)             # [G, N]
-    d = (codes.reshape(k // group, group, n) - zp[:, None, :]) * s[:, None, :]
-    return np.ascontiguousarray(d.reshape(k, n).T)
+    gi = np.arange(k) // group if g_idx is None else np.asarray(g_idx, np.int64)
+    d = (codes - zp[gi, :]) * s[gi, :]                              # row k uses group gi[k]
+    return np.ascontiguousarray(d.T)
 
 
 def bits_per_weight(group: int) -> float:

@@ -151,3 +151,86 @@ def test_dequant_from_stored_exact(sym):
                 continue                       # fp16 scale overflowed (huge weights)
             want = rn32((c - int(zp[k // 128, col])) * F(q["scales"][k // 128, col]))
             assert F(d[col, k]) == want
+
+
+# ---------------------------------------------------------------- act-order (g_idx)
+def _perm(k, seed):
+    return np.random.default_rng(seed).permutation(k)
+
+
+@pytest.mark.parametrize("sym", [True, False])
+def test_act_order_identity_is_plain(sym):
+    w = workloads.gptq_asym_weight(16, 256, seed=29).float().numpy()
+    a = gq.quantize_act_order(w, 64, sym, np.arange(256))
+    b = (gq.quantize_sym if sym else gq.quantize_asym)(w, 64)
+    for key in ("qweight", "qzeros", "scales", "g_idx"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("sym", [True, False])
+def test_act_order_bruteforce_exact(sym):
+    """Each group is the set of columns perm[gG:(g+1)G]; its scale, zero point and codes
+    are re-derived exactly from those columns, and g_idx names that group."""
+    group = 32
+    eps = F(np.float32(1e-9))
+    for w in _inputs()[1:3]:
+        n, k = w.shape
+        perm = _perm(k, 30)
+        q = gq.quantize_act_order(w, group, sym, perm)
+        for g in range(k // group):
+            cols = perm[g * group:(g + 1) * group]
+            assert np.all(q["g_idx"][cols] == g)
+            for row in range(0, n, 5):
+                xs = [w[row, c] for c in cols]
+                if sym:
+                    s = max(rn32(max(abs(F(v)) for v in xs) / 8), eps)
+                    zp = 8
+                else:
+                    mx, mn = max(F(v) for v in xs), min(F(v) for v in xs)
+                    s = rn32(max(rn32(mx - mn), eps) / 15)
+                    zp = min(max(rint_even(rn32(-mn / s)), 0), 15)
+                    assert q["zp"][g, row] == zp
+                assert F(q["scale_f32"][g, row]) == s
+                for c, v in zip(cols, xs):
+                    t = rn32(F(v) / s)
+                    dist = [abs(t + zp - cc) for cc in range(16)]
+                    best = min(dist)
+                    cands = [cc for cc in range(16) if dist[cc] == best]
+                    want = cands[0] if len(cands) == 1 else [cc for cc in cands if (cc - zp) % 2 == 0][0]
+                    assert q["codes"][c, row] == want
+
+
+def test_act_order_invariances():
+    w = workloads.gptq_asym_weight(16, 512, seed=31).float().numpy()
+    perm = _perm(512, 32)
+    q = gq.quantize_act_order(w, 128, False, perm)
+    # every group holds exactly G columns
+    assert np.array_equal(np.bincount(q["g_idx"], minlength=4), [128] * 4)
+    # reordering columns inside a group changes nothing
+    p2 = perm.copy()
+    p2[:128] = p2[:128][::-1]
+    q2 = gq.quantize_act_order(w, 128, False, p2)
+    for key in ("qweight", "qzeros", "scales", "g_idx"):
+        assert np.array_equal(q[key], q2[key]), key
+    # quantizing the permuted weight plainly gives the permuted codes, the same scales
+    qp = gq.quantize_asym(w[:, perm], 128)
+    assert np.array_equal(qp["codes"], q["codes"][perm])
+    assert np.array_equal(qp["scales"], q["scales"])
+
+
+@pytest.mark.parametrize("sym", [True, False])
+def test_dequant_g_idx_exact(sym):
+    """Column k dequantizes with the scale and zero point of group g_idx[k]."""
+    w = workloads.adversarial_weight(16, 256, seed=33, dtype=torch.float32).numpy()
+    w = np.where(np.abs(w) > 1e3, w * np.float32(2.0 ** -100), w).astype(np.float32)   # finite fp16 scales
+    perm = _perm(256, 34)
+    q = gq.quantize_act_order(w, 64, sym, perm)
+    d = gq.dequantize(q["qweight"], q["scales"], q["qzeros"], 64, sym, g_idx=q["g_idx"])
+    zp = np.full((4, 16), 8) if sym else q["zp"]
+    for col in range(16):
+        for k in range(256):
+            g = int(q["g_idx"][k])
+            want = rn32((int(q["codes"][k, col]) - int(zp[g, col])) * F(q["scales"][g, col]))
+            assert F(d[col, k]) == want
+    # without g_idx the same tensors would be read as contiguous groups: a different weight
+    assert not np.array_equal(d, gq.dequantize(q["qweight"], q["scales"], q["qzeros"], 64, sym))

@@ -86,6 +86,18 @@ def test_uintx_dropped_bf16_rounding_caught(monkeypatch):
     _fails(tu.test_quantize_bruteforce_exact, 5)
 
 
+def test_gptq_g_idx_ignored_caught(monkeypatch):
+    orig = gq.dequantize
+    monkeypatch.setattr(gq, "dequantize", lambda qw, s, qz, group, sym, g_idx=None: orig(qw, s, qz, group, sym))
+    _fails(tg.test_dequant_g_idx_exact, False)
+
+
+def test_gptq_act_order_groups_in_index_order_caught(monkeypatch):
+    orig = gq.quantize_act_order
+    monkeypatch.setattr(gq, "quantize_act_order", lambda w, group, sym, perm: orig(w, group, sym, np.sort(perm)))
+    _fails(tg.test_act_order_bruteforce_exact, True)
+
+
 def test_uintx_float16_rounded_as_bf16_caught(monkeypatch):
     monkeypatch.setattr(ux, "f16", ux.bf)
     _fails(tu.test_quantize_bruteforce_exact_other_dtypes, "f16", 4, 64)
