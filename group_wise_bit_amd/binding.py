@@ -6,7 +6,8 @@ every step of the method runs in the library's HIP kernels. There is no fallback
 the library is missing, importing this package raises.
 
 Formats ("fmt"): "gptq_sym", "gptq_asym", "mxfp4", "uintx", "mxfp4_page_ties" (MXFP4 with the
-page code's own tie rule; same stored layout).
+page code's own tie rule; same stored layout), "gptq_sym_act" / "gptq_asym_act" (GPTQ with
+act-order groups: quantize takes the channel order `perm`, g_idx names each channel's group).
 """
 from __future__ import annotations
 
@@ -25,8 +26,10 @@ if not os.path.exists(LIB_PATH):
 lib = ctypes.CDLL(LIB_PATH)
 
 OK, E_ARG, E_SHAPE, E_UNSUPPORTED, E_SIZE, E_HIP = 0, -1, -2, -3, -4, -5
-FORMATS = {"gptq_sym": 1, "gptq_asym": 2, "mxfp4": 3, "uintx": 4, "mxfp4_page_ties": 5}
-DEFAULT_GROUP = {"gptq_sym": 128, "gptq_asym": 128, "mxfp4": 32, "uintx": 64, "mxfp4_page_ties": 32}
+FORMATS = {"gptq_sym": 1, "gptq_asym": 2, "mxfp4": 3, "uintx": 4, "mxfp4_page_ties": 5,
+           "gptq_sym_act": 6, "gptq_asym_act": 7}
+DEFAULT_GROUP = {"gptq_sym": 128, "gptq_asym": 128, "mxfp4": 32, "uintx": 64, "mxfp4_page_ties": 32,
+                 "gptq_sym_act": 128, "gptq_asym_act": 128}
 F32, BF16, F16 = 0, 1, 2
 _DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
@@ -58,6 +61,8 @@ _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_
 _SIGS = {
     "gwb_query_sizes": [ctypes.POINTER(QSpec), _I64, _I64, ctypes.POINTER(Sizes)],
     "gwb_quantize": [ctypes.POINTER(QSpec), _P, _I64, _I64, _I64, ctypes.POINTER(QTensors), _P, _SZ, _P],
+    "gwb_quantize_act_order": [ctypes.POINTER(QSpec), _P, _I64, _I64, _I64, _P, ctypes.POINTER(QTensors), _P, _SZ,
+                               _P],
     "gwb_dequantize": [ctypes.POINTER(QSpec), ctypes.POINTER(QTensors), _I64, _I64, _P, _I32, _I64, _P, _SZ, _P],
     "gwb_snr": [ctypes.POINTER(QSpec), _P, _I64, _I64, _I64, ctypes.POINTER(QTensors), _P, _P, _SZ, _P],
     "gwb_awq_workspace": [_I64, _I64, _I32, _I64, ctypes.POINTER(_SZ)],
@@ -167,15 +172,19 @@ def _weight_args(W: torch.Tensor):
 
 def quantize(W: torch.Tensor, fmt: str, nbits: int = 4, group: Optional[int] = None,
              with_g_idx: bool = True, out: Optional[Quantized] = None,
-             workspace: Optional[torch.Tensor] = None) -> Quantized:
-    """Quantize+pack W [N, K] into a new (or the given) Quantized."""
+             workspace: Optional[torch.Tensor] = None, perm: Optional[torch.Tensor] = None) -> Quantized:
+    """Quantize+pack W [N, K] into a new (or the given) Quantized. The act-order GPTQ
+    formats take perm, the channel order (int32 [K] on the device)."""
     N, K, ldw = _weight_args(W)
     group = DEFAULT_GROUP[fmt] if group is None else group
+    act = fmt.endswith("_act")
+    if act and (perm is None or perm.dtype != torch.int32 or tuple(perm.shape) != (K,) or not perm.is_cuda):
+        raise ValueError("act-order formats need perm: an int32 CUDA tensor [K]")
     sp = make_spec(fmt, nbits, group, W.dtype)
     sz = query_sizes(fmt, N, K, nbits, group, W.dtype)
     if out is None:
         dev = W.device
-        gidx = _alloc(sz["g_idx"], dev) if (fmt.startswith("gptq") and with_g_idx) else None
+        gidx = _alloc(sz["g_idx"], dev) if (fmt.startswith("gptq") and (with_g_idx or act)) else None
         zeros = _alloc(sz["zeros"], dev) if not fmt.startswith("mxfp4") else None   # GPTQ and uintx carry zeros
         out = Quantized(fmt, nbits, group, W.dtype, N, K, _alloc(sz["codes"], dev), _alloc(sz["scales"], dev),
                         zeros, gidx, sz)
@@ -183,8 +192,12 @@ def quantize(W: torch.Tensor, fmt: str, nbits: int = 4, group: Optional[int] = N
         workspace = _alloc(sz["workspace"], W.device)
     ws_b = 0 if workspace is None else workspace.numel() * workspace.element_size()
     qt = out.qtensors()
-    _check(lib.gwb_quantize(ctypes.byref(sp), _ptr(W), N, K, ldw, ctypes.byref(qt), _ptr(workspace), ws_b,
-                            _stream()))
+    if act:
+        _check(lib.gwb_quantize_act_order(ctypes.byref(sp), _ptr(W), N, K, ldw, _ptr(perm.contiguous()),
+                                          ctypes.byref(qt), _ptr(workspace), ws_b, _stream()))
+    else:
+        _check(lib.gwb_quantize(ctypes.byref(sp), _ptr(W), N, K, ldw, ctypes.byref(qt), _ptr(workspace), ws_b,
+                                _stream()))
     return out
 
 

@@ -44,6 +44,9 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // the two MXFP4 formats share every stored layout; only quantization differs
 bool is_mxfp4(int32_t f) { return f == GWB_MXFP4 || f == GWB_MXFP4_PAGE_TIES; }
+// act-order GPTQ shares GPTQ's stored layout; its groups come from g_idx
+bool is_act(int32_t f) { return f == GWB_GPTQ_SYM_ACT || f == GWB_GPTQ_ASYM_ACT; }
+bool is_gptq_sym(int32_t f) { return f == GWB_GPTQ_SYM || f == GWB_GPTQ_SYM_ACT; }
 
 size_t elem_size(int32_t dt) { return dt == GWB_F32 ? 4 : 2; }
 
@@ -59,6 +62,8 @@ int check_spec(const gwb_qspec* sp, int64_t N, int64_t K) {
   switch (sp->format) {
     case GWB_GPTQ_SYM:
     case GWB_GPTQ_ASYM:
+    case GWB_GPTQ_SYM_ACT:
+    case GWB_GPTQ_ASYM_ACT:
       if (sp->nbits != 4) return fail(GWB_E_ARG, "GPTQ is 4-bit, got nbits=%d", sp->nbits);
       if (sp->group <= 0) return fail(GWB_E_ARG, "group must be positive, got %d", sp->group);
       if (sp->group != 32 && sp->group != 64 && sp->group != 128)
@@ -66,6 +71,9 @@ int check_spec(const gwb_qspec* sp, int64_t N, int64_t K) {
       if (K % sp->group) return fail(GWB_E_SHAPE, "K=%lld not divisible by group %d", (long long)K, sp->group);
       if (N % 8) return fail(GWB_E_SHAPE, "GPTQ qzeros pack 8 columns per int32: N=%lld not divisible by 8",
                              (long long)N);
+      if (is_act(sp->format) && K / sp->group > gwb::kActMaxGroups)
+        return fail(GWB_E_UNSUPPORTED, "act-order GPTQ holds at most %d groups per row, got K/G=%lld",
+                    gwb::kActMaxGroups, (long long)(K / sp->group));
       return GWB_OK;
     case GWB_MXFP4:
     case GWB_MXFP4_PAGE_TIES:
@@ -100,6 +108,8 @@ unsigned err_blocks(const gwb_qspec* sp, int64_t N, int64_t K) {
     case GWB_MXFP4:
     case GWB_MXFP4_PAGE_TIES: return gwb::mxfp4_err_blocks(N, K);
     case GWB_UINTX: return gwb::uintx_err_blocks(sp->w_dtype, sp->group, N, K);
+    case GWB_GPTQ_SYM_ACT:
+    case GWB_GPTQ_ASYM_ACT: return gwb::gptq_act_err_blocks(N, K);
     default: return gwb::gptq_err_blocks(sp->group, N, K);
   }
 }
@@ -110,6 +120,8 @@ gwb_sizes sizes_of(const gwb_qspec* sp, int64_t N, int64_t K) {
   switch (sp->format) {
     case GWB_GPTQ_SYM:
     case GWB_GPTQ_ASYM:
+    case GWB_GPTQ_SYM_ACT:
+    case GWB_GPTQ_ASYM_ACT:
       s.codes = (size_t)(K / 8 * N * 4);
       s.scales = (size_t)(K / G * N * 2);
       s.zeros = (size_t)(K / G * (N / 8) * 4);
@@ -133,6 +145,10 @@ gwb_sizes sizes_of(const gwb_qspec* sp, int64_t N, int64_t K) {
       size_t c = gwb::uintx_code_workspace(sp->w_dtype, sp->group, N, K);
       ws = c > ws ? c : ws;
     }
+    if (is_act(sp->format)) {     // the column-ordered copy, its codes and the inverse order
+      size_t c = gwb::gptq_act_workspace_bytes(sp->w_dtype, N, K);
+      ws = c > ws ? c : ws;
+    }
   }
   s.workspace = ws;
   return s;
@@ -150,7 +166,9 @@ int check_tensors(const gwb_qspec* sp, const gwb_qtensors* q) {
   if (!q) return fail(GWB_E_ARG, "tensors struct is NULL");
   if (!q->codes || !q->scales) return fail(GWB_E_ARG, "codes and scales are required");
   if (!is_mxfp4(sp->format) && !q->zeros) return fail(GWB_E_ARG, "zeros is required for this format");
-  if (!aligned16(q->codes) || !aligned16(q->scales) || (q->zeros && !aligned16(q->zeros)))
+  if (is_act(sp->format) && !q->g_idx) return fail(GWB_E_ARG, "act-order GPTQ needs g_idx");
+  if (!aligned16(q->codes) || !aligned16(q->scales) || (q->zeros && !aligned16(q->zeros)) ||
+      (is_act(sp->format) && !aligned16(q->g_idx)))
     return fail(GWB_E_UNSUPPORTED, "quantized tensors must be 16-byte aligned");
   return GWB_OK;
 }
@@ -171,6 +189,8 @@ int gwb_query_sizes(const gwb_qspec* spec, int64_t N, int64_t K, gwb_sizes* out)
 int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
                  const gwb_qtensors* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (int rc = check_spec(spec, N, K)) return rc;
+  if (is_act(spec->format))
+    return fail(GWB_E_ARG, "act-order GPTQ takes the channel order: use gwb_quantize_act_order");
   if (N == 0 || K == 0) return ok();          // empty: valid, nothing to enqueue
   if (int rc = check_weight(spec, W, K, ldw)) return rc;
   if (int rc = check_tensors(spec, out)) return rc;
@@ -223,6 +243,11 @@ int gwb_dequantize(const gwb_qspec* spec, const gwb_qtensors* in, int64_t N, int
       gwb::launch_gptq_dequant(spec->format == GWB_GPTQ_SYM, spec->group, in->codes, in->scales, in->zeros, N, K,
                                out, out_dtype, ldo, st);
       break;
+    case GWB_GPTQ_SYM_ACT:
+    case GWB_GPTQ_ASYM_ACT:
+      gwb::launch_gptq_act_dequant(is_gptq_sym(spec->format), spec->group, in->codes, in->scales, in->zeros,
+                                   (const int32_t*)in->g_idx, N, K, out, out_dtype, ldo, st);
+      break;
     case GWB_MXFP4:
     case GWB_MXFP4_PAGE_TIES:
       gwb::launch_mxfp4_dequant(in->codes, in->scales, N, K, out, out_dtype, ldo, st);
@@ -254,6 +279,11 @@ int gwb_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t 
       gwb::launch_gptq_err(spec->format == GWB_GPTQ_SYM, spec->group, W, spec->w_dtype, N, K, ldw, in->codes,
                            in->scales, in->zeros, part, st);
       break;
+    case GWB_GPTQ_SYM_ACT:
+    case GWB_GPTQ_ASYM_ACT:
+      gwb::launch_gptq_act_err(is_gptq_sym(spec->format), spec->group, W, spec->w_dtype, N, K, ldw, in->codes,
+                               in->scales, in->zeros, (const int32_t*)in->g_idx, part, st);
+      break;
     case GWB_MXFP4:
     case GWB_MXFP4_PAGE_TIES:
       gwb::launch_mxfp4_err(W, spec->w_dtype, N, K, ldw, in->codes, in->scales, part, st);
@@ -264,6 +294,24 @@ int gwb_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t 
   }
   gwb::launch_err_finalize(part, nb, d_out, st);
   return hip_check("snr launch");
+}
+
+int gwb_quantize_act_order(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
+                           const int32_t* perm, const gwb_qtensors* out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (int rc = check_spec(spec, N, K)) return rc;
+  if (!is_act(spec->format)) return fail(GWB_E_ARG, "format must be GWB_GPTQ_SYM_ACT or GWB_GPTQ_ASYM_ACT");
+  if (N == 0 || K == 0) return ok();          // empty: valid, nothing to enqueue
+  if (int rc = check_weight(spec, W, K, ldw)) return rc;
+  if (int rc = check_tensors(spec, out)) return rc;
+  if (!perm) return fail(GWB_E_ARG, "perm is NULL");
+  const size_t need = gwb::gptq_act_workspace_bytes(spec->w_dtype, N, K);
+  if (!workspace || workspace_bytes < need)
+    return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
+  gwb::launch_gptq_act_quant(is_gptq_sym(spec->format), spec->group, W, spec->w_dtype, N, K, ldw, perm, out->codes,
+                             out->scales, out->zeros, (int32_t*)out->g_idx, workspace, (hipStream_t)stream);
+  return hip_check("act-order quantize launch");
 }
 
 static int awq_rows(int64_t N, int64_t max_rows, int64_t* rows, int64_t* step) {
@@ -343,6 +391,8 @@ static size_t gemv_workspace(const gwb_qspec* sp, int64_t N, int64_t K, int64_t 
 
 static int check_gemv(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
   if (int rc = check_spec(sp, N, K)) return rc;
+  if (is_act(sp->format))
+    return fail(GWB_E_UNSUPPORTED, "the GEMV reads contiguous GPTQ groups; act-order weights are not provided");
   if (sp->format == GWB_UINTX && (sp->w_dtype != GWB_BF16 || sp->group != 64))
     return fail(GWB_E_UNSUPPORTED, "the uintx GEMV takes bf16 weights in groups of 64");
   if (sp->format == GWB_UINTX && !gwb::uintx_gemv_supported(N, K))

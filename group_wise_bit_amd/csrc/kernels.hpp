@@ -50,6 +50,21 @@ void launch_gptq_err(bool sym, int group, const void* W, int32_t w_dtype, int64_
                      int64_t ldw, const void* qweight, const void* scales, const void* qzeros,
                      double* part, hipStream_t st);
 
+// ---- GPTQ with act-order groups (gptq_act.hip): group of channel k = g_idx[k]; the
+// dequantize / error kernels hold every group of a 32-row band in LDS (K/G <= kActMaxGroups)
+constexpr int kActMaxGroups = 512;
+size_t gptq_act_workspace_bytes(int32_t w_dtype, int64_t N, int64_t K);
+void launch_gptq_act_quant(bool sym, int group, const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
+                           const int32_t* perm, void* qweight, void* scales, void* qzeros, int32_t* g_idx,
+                           void* workspace, hipStream_t st);
+void launch_gptq_act_dequant(bool sym, int group, const void* qweight, const void* scales, const void* qzeros,
+                             const int32_t* g_idx, int64_t N, int64_t K, void* out, int32_t out_dtype, int64_t ldo,
+                             hipStream_t st);
+unsigned gptq_act_err_blocks(int64_t N, int64_t K);
+void launch_gptq_act_err(bool sym, int group, const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
+                         const void* qweight, const void* scales, const void* qzeros, const int32_t* g_idx,
+                         double* part, hipStream_t st);
+
 // ---- UINTX: tiled kernels (uintx_tiled.hpp) when N*K % (8 group) == 0, instantiated
 // for bf16 group 64 in uintx.hip and for the other (dtype, group) pairs in uintx_bf16.hip,
 // uintx_f16.hip, uintx_f32.hip; uintx_flat.hip for every other shape. dt is the weight

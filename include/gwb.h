@@ -17,6 +17,12 @@
  *                  stated round-half-to-even: the first tied index, rounded down to even
  *                  (|x| / 2^e = 0.75, 1.75, 3.5 give 0, 1, 2 rather than 1, 2, 4). Same
  *                  stored layout; dequantization, SNR and the GEMV are MXFP4's.
+ *   GWB_GPTQ_SYM_ACT / GWB_GPTQ_ASYM_ACT  GPTQ with act-order groups (the page stores
+ *                  g_idx and writes desc_act into its checkpoint config): the groups are
+ *                  the input channels taken in a caller-given order, G at a time; qweight
+ *                  stays in channel order and g_idx[k] names channel k's group. Per-group
+ *                  formulas as GWB_GPTQ_SYM / _ASYM; stored layout as GPTQ plus g_idx,
+ *                  which gwb_quantize_act_order writes and dequantization and SNR read.
  *
  * Conventions for every entry point:
  *   - Pointers named d_* and every tensor pointer are DEVICE pointers owned by the
@@ -47,7 +53,10 @@ typedef enum {
   GWB_E_HIP = -5           /* a HIP launch failed; gwb_last_error() names it */
 } gwb_status;
 
-typedef enum { GWB_GPTQ_SYM = 1, GWB_GPTQ_ASYM = 2, GWB_MXFP4 = 3, GWB_UINTX = 4, GWB_MXFP4_PAGE_TIES = 5 } gwb_format;
+typedef enum {
+  GWB_GPTQ_SYM = 1, GWB_GPTQ_ASYM = 2, GWB_MXFP4 = 3, GWB_UINTX = 4, GWB_MXFP4_PAGE_TIES = 5,
+  GWB_GPTQ_SYM_ACT = 6, GWB_GPTQ_ASYM_ACT = 7
+} gwb_format;
 typedef enum { GWB_F32 = 0, GWB_BF16 = 1, GWB_F16 = 2 } gwb_dtype;
 
 /* What to quantize to.
@@ -75,7 +84,9 @@ typedef struct {
  *          scales fp16 [K/G, N]: the float32 group scale rounded to fp16 (RNE)
  *          zeros  int32 qzeros [K/G, N/8]: nibble i of word (g, q) = zero point of
  *                 column 8q+i; symmetric: every nibble 7; asymmetric: zp itself
- *          g_idx  int32 [K] = k / G; optional on output (NULL skips), unused on input
+ *          g_idx  int32 [K] = k / G; optional on output (NULL skips), unused on input;
+ *                 act-order GPTQ: the group of channel k, required (input to
+ *                 dequantization and SNR, output of gwb_quantize_act_order)
  *   MXFP4  codes  uint8 [N, K/2]: byte = code(2i) | code(2i+1) << 4, code = e2m1
  *                 magnitude index | sign << 3
  *          scales uint8 e8m0 [N, K/32] = exponent + 127;  zeros, g_idx unused (NULL)
@@ -105,7 +116,8 @@ typedef struct {
 
 /* Validate (spec, N, K) and report buffer sizes. Host only, launches nothing.
  * Returns GWB_E_ARG / GWB_E_SHAPE / GWB_E_UNSUPPORTED as the format requires:
- *   GPTQ: K % group == 0, N % 8 == 0 (qzeros pack 8 columns per word);
+ *   GPTQ: K % group == 0, N % 8 == 0 (qzeros pack 8 columns per word); act-order
+ *         GPTQ also K / group <= 512 (GWB_E_UNSUPPORTED);
  *   MXFP4: K % 32 == 0 (page quantize_mxfp4 asserts it);
  *   UINTX: K % group == 0 (can_quantize refuses otherwise).                      */
 int gwb_query_sizes(const gwb_qspec* spec, int64_t N, int64_t K, gwb_sizes* out);
@@ -121,6 +133,20 @@ int gwb_query_sizes(const gwb_qspec* spec, int64_t N, int64_t K, gwb_sizes* out)
 int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
                  const gwb_qtensors* out, void* workspace, size_t workspace_bytes,
                  void* stream);
+
+/* Act-order GPTQ quantize (spec->format GWB_GPTQ_SYM_ACT or GWB_GPTQ_ASYM_ACT): group g is
+ * the channels perm[g*G .. g*G + G - 1], quantized with page export_gptq_cpu.py's
+ * quantize_sym / quantize_asym formulas; out->codes (qweight, channel order), scales and
+ * zeros as for GPTQ, out->g_idx (required) int32 [K] with g_idx[perm[j]] = j / G.
+ *   perm      device int32 [K], a permutation of 0..K-1 (e.g. channels by decreasing
+ *             activation magnitude); other contents give unspecified results, never an
+ *             access outside the buffers
+ *   workspace at least gwb_sizes.workspace bytes, 16-byte aligned (the weight gathered
+ *             into perm order, its codes, the inverse order)
+ * gwb_quantize refuses these formats with GWB_E_ARG. */
+int gwb_quantize_act_order(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
+                           const int32_t* perm, const gwb_qtensors* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* Unpack and dequantize into out [N, K] (row stride ldo >= K) of out_dtype, in the
  * weight's own [N, K] layout for every format (the GPTQ transpose is undone).

@@ -267,3 +267,33 @@ def test_page_ties_format_shares_mxfp4_sizes():
         assert a == b
     sp = gwb.make_spec("mxfp4_page_ties", 4, 32)
     assert lib.gwb_query_sizes(ctypes.byref(sp), 8, 48, ctypes.byref(gwb.Sizes())) == gwb.E_SHAPE
+
+
+def test_act_order_gptq_validates():
+    fake = 1 << 20
+    P = ctypes.c_void_p
+    rc, s = _sizes("gptq_sym_act", 256, 1024, group=32)
+    rc2, s2 = _sizes("gptq_sym", 256, 1024, group=32)
+    assert rc == 0 and (s.codes, s.scales, s.zeros, s.g_idx) == (s2.codes, s2.scales, s2.zeros, s2.g_idx)
+    assert s.workspace >= 256 * 1024 * 2 + 1024 // 8 * 256 * 4 + 1024 * 4     # gathered copy, codes, inverse
+    assert _sizes("gptq_asym_act", 8, 32 * 513, group=32)[0] == gwb.E_UNSUPPORTED   # > 512 groups per row
+    assert _sizes("gptq_asym_act", 8, 32 * 512, group=32)[0] == gwb.OK
+    sp = gwb.make_spec("gptq_asym_act", 4, 128, gwb.BF16)
+    qt = gwb.QTensors(fake, fake, fake, fake)
+    qn = gwb.QTensors(fake, fake, fake, None)
+    # plain quantize refuses the act-order formats; the act-order entry refuses the others
+    assert lib.gwb_quantize(ctypes.byref(sp), fake, 8, 256, 256, ctypes.byref(qt), fake, 1 << 30, None) == gwb.E_ARG
+    def act(spec=sp, perm=fake, q=qt, ws=fake, wsb=1 << 30):
+        return lib.gwb_quantize_act_order(ctypes.byref(spec), P(fake), 8, 256, 256, P(perm), ctypes.byref(q), P(ws),
+                                          wsb, None)
+    assert act(spec=gwb.make_spec("gptq_asym", 4, 128, gwb.BF16)) == gwb.E_ARG
+    assert act(perm=None) == gwb.E_ARG
+    assert act(q=qn) == gwb.E_ARG                                   # g_idx is an output here
+    assert act(wsb=1024) == gwb.E_SIZE
+    assert act(ws=fake + 8) == gwb.E_UNSUPPORTED
+    # dequantization and SNR need g_idx; the GEMV does not take act-order weights
+    assert lib.gwb_dequantize(ctypes.byref(sp), ctypes.byref(qn), 8, 256, P(fake), gwb.F32, 256, None, 0, None) \
+        == gwb.E_ARG
+    assert lib.gwb_snr(ctypes.byref(sp), P(fake), 8, 256, 256, ctypes.byref(qn), P(fake), P(fake), 1 << 20, None) \
+        == gwb.E_ARG
+    assert lib.gwb_gemv_workspace(ctypes.byref(sp), 8, 256, 1, ctypes.byref(ctypes.c_size_t())) == gwb.E_UNSUPPORTED

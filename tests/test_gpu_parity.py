@@ -292,6 +292,47 @@ def test_uintx_other_dtypes_strided_and_larger():
     _uintx_case(workloads.uintx_weight(512, 4096, seed=513, dtype=torch.float16), "f16", 4, 64)
 
 
+# ------------------------------------------------------------- GPTQ act-order
+@pytest.mark.parametrize("sym", [True, False])
+@pytest.mark.parametrize("group", [32, 128])
+@pytest.mark.parametrize("n,k,kind", [(8, 256, "normal"), (64, 384, "adv"), (72, 1024, "normal"),
+                                      (40, 4096, "normal")])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_gptq_act_order_parity(sym, group, n, k, kind, dtype):
+    """Act-order groups (a random channel order): qweight, scales, qzeros and g_idx bit
+    for bit; g_idx-indexed dequantization element by element; SNR."""
+    if kind == "adv" and k % 128:
+        kind = "normal"
+    W = _weight(kind, n, k, seed=600 + n + group, dtype=dtype)
+    if kind == "adv":
+        W = torch.where(W.float().abs() > 1e3, W.float() * 2.0 ** -100, W.float()).to(dtype)   # finite fp16 scales
+    perm = np.random.default_rng(601 + k).permutation(k)
+    Wd = W.to(DEV)
+    fmt = "gptq_sym_act" if sym else "gptq_asym_act"
+    q = gwb.quantize(Wd, fmt, group=group, perm=torch.from_numpy(perm.astype(np.int32)).to(DEV))
+    o = ogq.quantize_act_order(W.float().numpy(), group, sym, perm)
+    assert np.array_equal(_np(q["qweight"]), o["qweight"])
+    assert np.array_equal(_np(q["scales"]).view(np.uint16), o["scales"].view(np.uint16))
+    assert np.array_equal(_np(q["g_idx"]), o["g_idx"])
+    if not sym:
+        assert np.array_equal(_np(q["qzeros"]), o["qzeros"])
+    ref = ogq.dequantize(o["qweight"], o["scales"], o["qzeros"], group, sym, g_idx=o["g_idx"])
+    _check_dequant(q, ref)
+    _check_snr(W, Wd, q, ref)
+
+
+def test_gptq_act_order_identity_matches_plain():
+    W = workloads.gptq_asym_weight(64, 1024, seed=602)
+    Wd = W.to(DEV)
+    ident = torch.arange(1024, dtype=torch.int32, device=DEV)
+    for sym in (True, False):
+        a = gwb.quantize(Wd, "gptq_sym_act" if sym else "gptq_asym_act", perm=ident)
+        b = gwb.quantize(Wd, "gptq_sym" if sym else "gptq_asym")
+        for key in ("qweight", "scales", "qzeros", "g_idx"):
+            assert torch.equal(a[key], b[key]), key
+        assert torch.equal(gwb.dequantize(a, torch.float32), gwb.dequantize(b, torch.float32))
+
+
 # -------------------------------------------------------------------------- AWQ
 def _ulps(a, b):
     ia = _f32bits(a).astype(np.int64)
