@@ -159,7 +159,8 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
     value): the AWQ fold of the gate_up weight (columns * s) straight to MXFP4, the same
     fold also writing the folded bf16 weight, and the decode GEMV reading a packed
     131072 x 2048 lm_head (GPTQ sym g128, MXFP4, uintx4 g64) for one activation row, and
-    the uintx variants (float16 / float32 weights, groups 32 / 128) at [3072, 12288]."""
+    the uintx variants (float16 / float32 weights, groups 32 / 128) at [3072, 12288], and
+    GPTQ with act-order groups on the gate_up weight."""
     out = []
     s = torch.from_numpy(gwb.awq_scales_host(ad.cpu(), (0.5,))[0].numpy()).to(dev)
     mx = gwb.fold_mxfp4(Wd, s, "mul", want_folded=False)["mxfp4"]
@@ -224,7 +225,22 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
             (f"{tag}.dequant", packed + esz * unk, cycle([gwb.prepare_dequantize(q, o) for q, o in zip(qs, outs)])),
             (f"{tag}.snr", esz * unk + packed, cycle([gwb.prepare_snr(w, q, res, ws) for w, q in zip(Ws, qs)])),
         ]
-    for name, abytes, fn in cases + gemv_cases + var_cases:
+    # GPTQ with act-order groups (sym and asym, g128) on the gate_up weight, channels in
+    # the order of decreasing activation statistic (the AWQ stat a)
+    perm = torch.argsort(ad, descending=True).to(torch.int32).contiguous()
+    act_cases = []
+    for fmt in ("gptq_sym_act", "gptq_asym_act"):
+        qa = gwb.quantize(Wd, fmt, group=128, perm=perm)
+        wsa = torch.empty(qa.sizes["workspace"], dtype=torch.uint8, device=dev)
+        res = torch.empty(3, dtype=torch.float64, device=dev)
+        packed = nk / 2 + nk / 128 * 2 + (nk / 128 / 2 if fmt == "gptq_asym_act" else 0) + 4 * K
+        act_cases += [
+            (f"{fmt}_g128.quant", 2 * nk + packed + nk / 128 / 2 * (fmt == "gptq_sym_act"),
+             gwb.prepare_quantize(Wd, qa, wsa, perm=perm)),
+            (f"{fmt}_g128.dequant", packed + 2 * nk, gwb.prepare_dequantize(qa, folded)),
+            (f"{fmt}_g128.snr", 2 * nk + packed, gwb.prepare_snr(Wd, qa, res, wsa)),
+        ]
+    for name, abytes, fn in cases + gemv_cases + var_cases + act_cases:
         us = _time_op(fn)
         shape = [HN, HK] if name.startswith("gemv") else ([UN, UK] if name.startswith("uintx") else [N, K])
         out.append({"op": name, "shape": shape, "us": round(us, 2),

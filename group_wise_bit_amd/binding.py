@@ -374,7 +374,8 @@ class Prepared:
         _check(self._fn(*self._args))
 
 
-def prepare_quantize(W: torch.Tensor, q: Quantized, workspace: Optional[torch.Tensor] = None) -> Prepared:
+def prepare_quantize(W: torch.Tensor, q: Quantized, workspace: Optional[torch.Tensor] = None,
+                     perm: Optional[torch.Tensor] = None) -> Prepared:
     N, K, ldw = _weight_args(W)
     if (N, K, W.dtype) != (q.N, q.K, q.w_dtype):
         raise ValueError("W does not match the Quantized buffers")
@@ -382,6 +383,12 @@ def prepare_quantize(W: torch.Tensor, q: Quantized, workspace: Optional[torch.Te
         workspace = _alloc(q.sizes["workspace"], W.device)
     sp, qt = q.spec(), q.qtensors()
     ws_b = 0 if workspace is None else workspace.numel()
+    if q.fmt.endswith("_act"):
+        if perm is None or perm.dtype != torch.int32 or not perm.is_contiguous():
+            raise ValueError("act-order formats need perm: a contiguous int32 CUDA tensor [K]")
+        return Prepared(lib.gwb_quantize_act_order, (ctypes.byref(sp), _ptr(W), N, K, ldw, _ptr(perm),
+                                                     ctypes.byref(qt), _ptr(workspace), ws_b, _stream()),
+                        (sp, qt, W, q, workspace, perm))
     return Prepared(lib.gwb_quantize, (ctypes.byref(sp), _ptr(W), N, K, ldw, ctypes.byref(qt), _ptr(workspace),
                                        ws_b, _stream()), (sp, qt, W, q, workspace))
 

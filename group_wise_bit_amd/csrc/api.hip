@@ -74,6 +74,9 @@ int check_spec(const gwb_qspec* sp, int64_t N, int64_t K) {
       if (is_act(sp->format) && K / sp->group > gwb::kActMaxGroups)
         return fail(GWB_E_UNSUPPORTED, "act-order GPTQ holds at most %d groups per row, got K/G=%lld",
                     gwb::kActMaxGroups, (long long)(K / sp->group));
+      if (is_act(sp->format) && K * (int64_t)elem_size(sp->w_dtype) > gwb::kActMaxRowBytes)
+        return fail(GWB_E_UNSUPPORTED, "act-order GPTQ holds a weight row of at most %lld bytes, got %lld",
+                    (long long)gwb::kActMaxRowBytes, (long long)(K * (int64_t)elem_size(sp->w_dtype)));
       return GWB_OK;
     case GWB_MXFP4:
     case GWB_MXFP4_PAGE_TIES:
@@ -145,8 +148,8 @@ gwb_sizes sizes_of(const gwb_qspec* sp, int64_t N, int64_t K) {
       size_t c = gwb::uintx_code_workspace(sp->w_dtype, sp->group, N, K);
       ws = c > ws ? c : ws;
     }
-    if (is_act(sp->format)) {     // the column-ordered copy, its codes and the inverse order
-      size_t c = gwb::gptq_act_workspace_bytes(sp->w_dtype, N, K);
+    if (is_act(sp->format)) {     // float32 scale and zero point of every (row, group)
+      size_t c = gwb::gptq_act_workspace_bytes(N, K, sp->group);
       ws = c > ws ? c : ws;
     }
   }
@@ -305,7 +308,8 @@ int gwb_quantize_act_order(const gwb_qspec* spec, const void* W, int64_t N, int6
   if (int rc = check_weight(spec, W, K, ldw)) return rc;
   if (int rc = check_tensors(spec, out)) return rc;
   if (!perm) return fail(GWB_E_ARG, "perm is NULL");
-  const size_t need = gwb::gptq_act_workspace_bytes(spec->w_dtype, N, K);
+  if (!aligned16(perm)) return fail(GWB_E_UNSUPPORTED, "perm must be 16-byte aligned");
+  const size_t need = gwb::gptq_act_workspace_bytes(N, K, spec->group);
   if (!workspace || workspace_bytes < need)
     return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (!aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");

@@ -50,10 +50,12 @@ void launch_gptq_err(bool sym, int group, const void* W, int32_t w_dtype, int64_
                      int64_t ldw, const void* qweight, const void* scales, const void* qzeros,
                      double* part, hipStream_t st);
 
-// ---- GPTQ with act-order groups (gptq_act.hip): group of channel k = g_idx[k]; the
-// dequantize / error kernels hold every group of a 32-row band in LDS (K/G <= kActMaxGroups)
-constexpr int kActMaxGroups = 512;
-size_t gptq_act_workspace_bytes(int32_t w_dtype, int64_t N, int64_t K);
+// ---- GPTQ with act-order groups (gptq_act.hip): group of channel k = g_idx[k]; the tile
+// kernels hold every group of a 32-row band in LDS (K/G <= kActMaxGroups) and quantization
+// holds one weight row in LDS (K * element size <= kActMaxRowBytes)
+constexpr int kActMaxGroups = 256;
+constexpr int64_t kActMaxRowBytes = 65536;
+size_t gptq_act_workspace_bytes(int64_t N, int64_t K, int group);
 void launch_gptq_act_quant(bool sym, int group, const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
                            const int32_t* perm, void* qweight, void* scales, void* qzeros, int32_t* g_idx,
                            void* workspace, hipStream_t st);

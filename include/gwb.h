@@ -117,7 +117,7 @@ typedef struct {
 /* Validate (spec, N, K) and report buffer sizes. Host only, launches nothing.
  * Returns GWB_E_ARG / GWB_E_SHAPE / GWB_E_UNSUPPORTED as the format requires:
  *   GPTQ: K % group == 0, N % 8 == 0 (qzeros pack 8 columns per word); act-order
- *         GPTQ also K / group <= 512 (GWB_E_UNSUPPORTED);
+ *         GPTQ also K / group <= 256 and K * element size <= 64 KB (GWB_E_UNSUPPORTED);
  *   MXFP4: K % 32 == 0 (page quantize_mxfp4 asserts it);
  *   UINTX: K % group == 0 (can_quantize refuses otherwise).                      */
 int gwb_query_sizes(const gwb_qspec* spec, int64_t N, int64_t K, gwb_sizes* out);
@@ -138,11 +138,11 @@ int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int
  * the channels perm[g*G .. g*G + G - 1], quantized with page export_gptq_cpu.py's
  * quantize_sym / quantize_asym formulas; out->codes (qweight, channel order), scales and
  * zeros as for GPTQ, out->g_idx (required) int32 [K] with g_idx[perm[j]] = j / G.
- *   perm      device int32 [K], a permutation of 0..K-1 (e.g. channels by decreasing
- *             activation magnitude); other contents give unspecified results, never an
- *             access outside the buffers
- *   workspace at least gwb_sizes.workspace bytes, 16-byte aligned (the weight gathered
- *             into perm order, its codes, the inverse order)
+ *   perm      device int32 [K], 16-byte aligned, a permutation of 0..K-1 (e.g. channels
+ *             by decreasing activation magnitude); other contents give unspecified
+ *             results, never an access outside the buffers
+ *   workspace at least gwb_sizes.workspace bytes, 16-byte aligned (the float32 scale and
+ *             zero point of every row and group)
  * gwb_quantize refuses these formats with GWB_E_ARG. */
 int gwb_quantize_act_order(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
                            const int32_t* perm, const gwb_qtensors* out, void* workspace, size_t workspace_bytes,

@@ -275,9 +275,11 @@ def test_act_order_gptq_validates():
     rc, s = _sizes("gptq_sym_act", 256, 1024, group=32)
     rc2, s2 = _sizes("gptq_sym", 256, 1024, group=32)
     assert rc == 0 and (s.codes, s.scales, s.zeros, s.g_idx) == (s2.codes, s2.scales, s2.zeros, s2.g_idx)
-    assert s.workspace >= 256 * 1024 * 2 + 1024 // 8 * 256 * 4 + 1024 * 4     # gathered copy, codes, inverse
-    assert _sizes("gptq_asym_act", 8, 32 * 513, group=32)[0] == gwb.E_UNSUPPORTED   # > 512 groups per row
-    assert _sizes("gptq_asym_act", 8, 32 * 512, group=32)[0] == gwb.OK
+    assert s.workspace >= 256 * 32 * 5                             # float32 scale + zero point per (row, group)
+    assert _sizes("gptq_asym_act", 8, 32 * 257, group=32)[0] == gwb.E_UNSUPPORTED   # > 256 groups per row
+    assert _sizes("gptq_asym_act", 8, 32 * 256, group=32)[0] == gwb.OK
+    assert _sizes("gptq_asym_act", 8, 32768, group=128)[0] == gwb.OK                 # a 64 KB bf16 row
+    assert _sizes("gptq_asym_act", 8, 32768, group=128, dt=gwb.F32)[0] == gwb.E_UNSUPPORTED
     sp = gwb.make_spec("gptq_asym_act", 4, 128, gwb.BF16)
     qt = gwb.QTensors(fake, fake, fake, fake)
     qn = gwb.QTensors(fake, fake, fake, None)
@@ -289,8 +291,9 @@ def test_act_order_gptq_validates():
     assert act(spec=gwb.make_spec("gptq_asym", 4, 128, gwb.BF16)) == gwb.E_ARG
     assert act(perm=None) == gwb.E_ARG
     assert act(q=qn) == gwb.E_ARG                                   # g_idx is an output here
-    assert act(wsb=1024) == gwb.E_SIZE
+    assert act(wsb=100) == gwb.E_SIZE
     assert act(ws=fake + 8) == gwb.E_UNSUPPORTED
+    assert act(perm=fake + 4) == gwb.E_UNSUPPORTED
     # dequantization and SNR need g_idx; the GEMV does not take act-order weights
     assert lib.gwb_dequantize(ctypes.byref(sp), ctypes.byref(qn), 8, 256, P(fake), gwb.F32, 256, None, 0, None) \
         == gwb.E_ARG
