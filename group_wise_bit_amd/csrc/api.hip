@@ -387,10 +387,11 @@ int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t
 }
 
 static size_t gemv_workspace(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
-  if (sp->format == GWB_GPTQ_SYM || sp->format == GWB_GPTQ_ASYM)
-    return (size_t)gwb::gptq_gemv_splits(K) * (size_t)B * (size_t)N * sizeof(float);
-  if (sp->format == GWB_UINTX) return (size_t)gwb::uintx_gemv_splits(K) * (size_t)B * (size_t)N * sizeof(float);
-  return 0;
+  // the K-split partial sums (none with a single split)
+  int S = 0;
+  if (sp->format == GWB_GPTQ_SYM || sp->format == GWB_GPTQ_ASYM) S = gwb::gptq_gemv_splits(N, K);
+  if (sp->format == GWB_UINTX) S = gwb::uintx_gemv_splits(K);
+  return S > 1 ? (size_t)S * (size_t)B * (size_t)N * sizeof(float) : 0;
 }
 
 static int check_gemv(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {

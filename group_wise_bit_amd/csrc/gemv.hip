@@ -9,11 +9,12 @@
 // float32 in a fixed order (deterministic for a given shape).
 //
 // GPTQ ([K/8, N] words, n contiguous): a lane owns 4 adjacent outputs (one 16-byte load
-// per qweight row r), a wavefront 256 outputs x 128 k (16 loads in flight), a block's
-// four wavefronts 512 k, combined through LDS. With (c - z) * s per group,
-// sum_k (c - z) s x = s (sum_k c x - z sum_k x): codes become floats with
-// v_cvt_f32_ubyte, the group sum of x is a wavefront reduction. Longer K is split
-// across blocks, whose partial sums a second kernel adds in order.
+// per qweight row r), a wavefront 256 outputs x 128 k per step (16 loads in flight); a
+// block's four wavefronts take the steps of its K range in turn and are combined through
+// LDS. With (c - z) * s per group, sum_k (c - z) s x = s (sum_k c x - z sum_k x): codes
+// become floats with v_cvt_f32_ubyte, the group sum of x is a wavefront reduction. When
+// N alone gives enough blocks, one block covers all of K and writes y; otherwise K is
+// split across blocks, whose partial sums a second kernel adds in order.
 //
 // MXFP4 ([N, K/2] bytes + E8M0 [N, K/32]): lanes run along K, one 32-block per lane
 // and step; the codes of a block become bf16 pairs with the scaled FP4 conversion at
@@ -48,26 +49,29 @@ __device__ __forceinline__ float wave_sum(float v) {
 constexpr int kGqLaneN = 4, kGqWaveN = 64 * kGqLaneN, kGqWaveK = 128, kGqBlockK = 4 * kGqWaveK;
 
 // B is the compiled width (1, 2, 4, 8); Bn <= B activation rows are real: the others
-// re-read row Bn - 1 and are not stored.
-template <bool SYM, int G, int B>
+// re-read row Bn - 1 and are not stored. kspan: the K range of one split (a multiple of
+// kGqBlockK); with one split the block writes y (TY), otherwise its partial sums.
+template <bool SYM, int G, int B, typename TY>
 __global__ __launch_bounds__(256) void gptq_gemv_kernel(const uint32_t* __restrict__ qweight,
                                                         const uint16_t* __restrict__ scale_bits,
                                                         const uint32_t* __restrict__ qzeros, int N, int K,
-                                                        const uint16_t* __restrict__ x, int64_t ldx, int Bn,
-                                                        float* __restrict__ part) {
+                                                        int kspan, const uint16_t* __restrict__ x, int64_t ldx,
+                                                        int Bn, float* __restrict__ part, TY* __restrict__ y,
+                                                        int64_t ldy) {
   static_assert(kGqWaveK % G == 0, "a wavefront covers whole groups");
   __shared__ float red[4][B][kGqWaveN];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int n0 = blockIdx.x * kGqWaveN + lane * kGqLaneN;
   const int nc = min(n0, N - kGqLaneN);                 // N % 8 == 0: lanes past N read a valid place
-  const int kw = blockIdx.y * kGqBlockK + wave * kGqWaveK;
+  const int kend = min(K, (int)(blockIdx.y + 1) * kspan);
   float acc[B][kGqLaneN];
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
     for (int j = 0; j < kGqLaneN; ++j) acc[b][j] = 0.0f;
-  if (kw < K) {                                         // wave-uniform; K % G == 0, so whole groups
+  // wave-uniform steps; K % G == 0, so every step holds whole groups
+  for (int kw = blockIdx.y * kspan + wave * kGqWaveK; kw < kend; kw += kGqBlockK) {
     const int nr = min(kGqWaveK, K - kw) / 8;           // qweight rows of this wavefront
     U4 wv[kGqWaveK / 8];
 #pragma unroll
@@ -146,8 +150,11 @@ __global__ __launch_bounds__(256) void gptq_gemv_kernel(const uint32_t* __restri
   __syncthreads();
   for (int e = t; e < B * kGqWaveN; e += 256) {
     const int b = e / kGqWaveN, i = e % kGqWaveN, n = blockIdx.x * kGqWaveN + i;
-    if (n < N && b < Bn)
-      part[((int64_t)blockIdx.y * Bn + b) * N + n] = ((red[0][b][i] + red[1][b][i]) + red[2][b][i]) + red[3][b][i];
+    if (n < N && b < Bn) {
+      const float v = ((red[0][b][i] + red[1][b][i]) + red[2][b][i]) + red[3][b][i];
+      if (gridDim.y == 1) store_y(y + (int64_t)b * ldy + n, v);
+      else part[((int64_t)blockIdx.y * Bn + b) * N + n] = v;
+    }
   }
 }
 
@@ -249,38 +256,56 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restri
 }
 
 // ------------------------------------------------------------------ launchers
-int gptq_gemv_splits(int64_t K) { return (int)((K + kGqBlockK - 1) / kGqBlockK); }
-
-template <bool SYM, int G, int B>
-static void gptq_gemv_b(int Bn, const void* qw, const void* sc, const void* qz, int64_t N, int64_t K, const void* x,
-                        int64_t ldx, float* part, hipStream_t st) {
-  const dim3 grid((unsigned)((N + kGqWaveN - 1) / kGqWaveN), (unsigned)gptq_gemv_splits(K));
-  hipLaunchKernelGGL((gptq_gemv_kernel<SYM, G, B>), grid, dim3(256), 0, st, (const uint32_t*)qw,
-                     (const uint16_t*)sc, (const uint32_t*)qz, (int)N, (int)K, (const uint16_t*)x, ldx, Bn, part);
+// K splits: one per kGqBlockK of K when N gives few blocks, fewer (down to one, which needs
+// no second pass) when N / 256 alone gives at least kGqMinBlocks.
+constexpr int kGqMinBlocks = 512;
+int gptq_gemv_splits(int64_t N, int64_t K) {
+  const int64_t tiles = (N + kGqWaveN - 1) / kGqWaveN, kb = (K + kGqBlockK - 1) / kGqBlockK;
+  const int64_t want = (kGqMinBlocks + tiles - 1) / tiles;
+  return (int)(want < 1 ? 1 : (want > kb ? kb : want));
 }
 
-template <bool SYM, int G>
+template <bool SYM, int G, int B, typename TY>
+static void gptq_gemv_b(int Bn, const void* qw, const void* sc, const void* qz, int64_t N, int64_t K, const void* x,
+                        int64_t ldx, float* part, void* y, int64_t ldy, hipStream_t st) {
+  const int S = gptq_gemv_splits(N, K);
+  const int64_t kb = (K + kGqBlockK - 1) / kGqBlockK;
+  const int kspan = (int)((kb + S - 1) / S) * kGqBlockK;
+  const dim3 grid((unsigned)((N + kGqWaveN - 1) / kGqWaveN), (unsigned)S);
+  hipLaunchKernelGGL((gptq_gemv_kernel<SYM, G, B, TY>), grid, dim3(256), 0, st, (const uint32_t*)qw,
+                     (const uint16_t*)sc, (const uint32_t*)qz, (int)N, (int)K, kspan, (const uint16_t*)x, ldx, Bn,
+                     part, (TY*)y, ldy);
+}
+
+template <bool SYM, int G, typename TY>
 static void gptq_gemv_g(int B, const void* qw, const void* sc, const void* qz, int64_t N, int64_t K, const void* x,
-                        int64_t ldx, float* part, hipStream_t st) {
-  if (B == 1) gptq_gemv_b<SYM, G, 1>(B, qw, sc, qz, N, K, x, ldx, part, st);
-  else if (B == 2) gptq_gemv_b<SYM, G, 2>(B, qw, sc, qz, N, K, x, ldx, part, st);
-  else if (B <= 4) gptq_gemv_b<SYM, G, 4>(B, qw, sc, qz, N, K, x, ldx, part, st);
-  else gptq_gemv_b<SYM, G, 8>(B, qw, sc, qz, N, K, x, ldx, part, st);
+                        int64_t ldx, float* part, void* y, int64_t ldy, hipStream_t st) {
+  if (B == 1) gptq_gemv_b<SYM, G, 1, TY>(B, qw, sc, qz, N, K, x, ldx, part, y, ldy, st);
+  else if (B == 2) gptq_gemv_b<SYM, G, 2, TY>(B, qw, sc, qz, N, K, x, ldx, part, y, ldy, st);
+  else if (B <= 4) gptq_gemv_b<SYM, G, 4, TY>(B, qw, sc, qz, N, K, x, ldx, part, y, ldy, st);
+  else gptq_gemv_b<SYM, G, 8, TY>(B, qw, sc, qz, N, K, x, ldx, part, y, ldy, st);
+}
+
+template <bool SYM, typename TY>
+static void gptq_gemv_s(int group, int B, const void* qw, const void* sc, const void* qz, int64_t N, int64_t K,
+                        const void* x, int64_t ldx, float* part, void* y, int64_t ldy, hipStream_t st) {
+  if (group == 32) gptq_gemv_g<SYM, 32, TY>(B, qw, sc, qz, N, K, x, ldx, part, y, ldy, st);
+  else if (group == 64) gptq_gemv_g<SYM, 64, TY>(B, qw, sc, qz, N, K, x, ldx, part, y, ldy, st);
+  else gptq_gemv_g<SYM, 128, TY>(B, qw, sc, qz, N, K, x, ldx, part, y, ldy, st);
 }
 
 void launch_gptq_gemv(bool sym, int group, int B, const void* qweight, const void* scales, const void* qzeros,
                       int64_t N, int64_t K, const void* x, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
                       float* part, hipStream_t st) {
-  if (sym) {
-    if (group == 32) gptq_gemv_g<true, 32>(B, qweight, scales, qzeros, N, K, x, ldx, part, st);
-    else if (group == 64) gptq_gemv_g<true, 64>(B, qweight, scales, qzeros, N, K, x, ldx, part, st);
-    else gptq_gemv_g<true, 128>(B, qweight, scales, qzeros, N, K, x, ldx, part, st);
+  if (y_dtype == kBF16) {
+    if (sym) gptq_gemv_s<true, uint16_t>(group, B, qweight, scales, qzeros, N, K, x, ldx, part, y, ldy, st);
+    else gptq_gemv_s<false, uint16_t>(group, B, qweight, scales, qzeros, N, K, x, ldx, part, y, ldy, st);
   } else {
-    if (group == 32) gptq_gemv_g<false, 32>(B, qweight, scales, qzeros, N, K, x, ldx, part, st);
-    else if (group == 64) gptq_gemv_g<false, 64>(B, qweight, scales, qzeros, N, K, x, ldx, part, st);
-    else gptq_gemv_g<false, 128>(B, qweight, scales, qzeros, N, K, x, ldx, part, st);
+    if (sym) gptq_gemv_s<true, float>(group, B, qweight, scales, qzeros, N, K, x, ldx, part, y, ldy, st);
+    else gptq_gemv_s<false, float>(group, B, qweight, scales, qzeros, N, K, x, ldx, part, y, ldy, st);
   }
-  launch_gemv_finalize(part, gptq_gemv_splits(K), B, N, y, y_dtype, ldy, st);
+  const int S = gptq_gemv_splits(N, K);
+  if (S > 1) launch_gemv_finalize(part, S, B, N, y, y_dtype, ldy, st);
 }
 
 void launch_gemv_finalize(const float* part, int S, int B, int64_t N, void* y, int32_t y_dtype, int64_t ldy,

@@ -121,13 +121,14 @@ void launch_fold(int col_op, int row_op, const void* W, int64_t N, int64_t K, in
                  hipStream_t st);
 
 // ---- decode GEMV on quantized weights (gemv.hip); B <= 8 activation rows (bf16)
-int gptq_gemv_splits(int64_t K);     // K splits; part holds splits * B * N floats
+int gptq_gemv_splits(int64_t N, int64_t K);   // K splits; with more than one, part holds splits * B * N floats
 void launch_gptq_gemv(bool sym, int group, int B, const void* qweight, const void* scales, const void* qzeros,
                       int64_t N, int64_t K, const void* x, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
                       float* part, hipStream_t st);
 void launch_mxfp4_gemv(int B, const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x,
                        int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, hipStream_t st);
-// uintx (uintx.hip): N % 8 == 0 and K % 512 == 0; part holds splits * B * N floats
+// uintx (uintx.hip): N % 8 == 0 and K % 512 == 0; with more than one split, part holds
+// splits * B * N floats
 bool uintx_gemv_supported(int64_t N, int64_t K);
 int uintx_gemv_splits(int64_t K);
 void launch_uintx_gemv(int nbits, int B, const void* packed, const void* scales, const void* zeros, int64_t N,

@@ -44,12 +44,21 @@ __device__ __forceinline__ float ux_transposed_sum(float (&v)[8], int lane) {
   return r;
 }
 
+// Where the GEMV's row sums go: K-split partials, or y itself (float32 or bf16, RNE).
+struct GemvOut {
+  enum { kPart = 0, kF32 = 1, kBF16 = 2 };
+  float* part;
+  void* y;
+  int64_t ldy;
+  int mode;
+};
+
 template <int NB, int B, int CH>
 __global__ __launch_bounds__(256) void uintx_gemv_tiled(const uint8_t* __restrict__ packed,
                                                         const uint16_t* __restrict__ scales,
                                                         const uint8_t* __restrict__ zeros, FastDiv kdiv, uint32_t L1,
                                                         Shards sh, int N, const uint16_t* __restrict__ x,
-                                                        int64_t ldx, int Bn, float* __restrict__ part) {
+                                                        int64_t ldx, int Bn, GemvOut out) {
   using SB = ShardBits<NB>;
   __shared__ uint32_t qp_lds[CH][256];
   const int lane = threadIdx.x & 63;
@@ -123,7 +132,12 @@ __global__ __launch_bounds__(256) void uintx_gemv_tiled(const uint8_t* __restric
 #pragma unroll
   for (int b = 0; b < B; ++b) {
     const float v = ux_transposed_sum(acc[b], lane);
-    if (lane < 8 && b < Bn) part[((int64_t)chunk * Bn + b) * N + j * (uint32_t)(N / 8) + row] = v;
+    if (lane < 8 && b < Bn) {
+      const int64_t n = (int64_t)j * (N / 8) + row;
+      if (out.mode == GemvOut::kPart) out.part[((int64_t)chunk * Bn + b) * N + n] = v;
+      else if (out.mode == GemvOut::kF32) static_cast<float*>(out.y)[b * out.ldy + n] = v;
+      else static_cast<uint16_t*>(out.y)[b * out.ldy + n] = (uint16_t)f32_to_bf16_rne(v);
+    }
   }
 }
 
@@ -191,28 +205,28 @@ namespace gwb {
 
 template <int NB, int B, int CH>
 static void gemv_tiled(int Bn, const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K,
-                       const void* x, int64_t ldx, float* part, hipStream_t st) {
+                       const void* x, int64_t ldx, GemvOut out, hipStream_t st) {
   const uint32_t numel = (uint32_t)(N * K);
   const unsigned blocks = (unsigned)(((uint64_t)numel / 8 / (kWavePos * CH) + 3) / 4);
   hipLaunchKernelGGL((uintx_gemv_tiled<NB, B, CH>), dim3(blocks), dim3(256), 0, st, (const uint8_t*)packed,
                      (const uint16_t*)scales, (const uint8_t*)zeros, make_fastdiv((uint32_t)K), numel / 8,
-                     shards_of(NB, numel), (int)N, (const uint16_t*)x, ldx, Bn, part);
+                     shards_of(NB, numel), (int)N, (const uint16_t*)x, ldx, Bn, out);
 }
 
 template <int NB, int CH>
 static void gemv_ch(int B, const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K,
-                    const void* x, int64_t ldx, float* part, hipStream_t st) {
-  if (B == 1) gemv_tiled<NB, 1, CH>(B, packed, scales, zeros, N, K, x, ldx, part, st);
-  else if (B == 2) gemv_tiled<NB, 2, CH>(B, packed, scales, zeros, N, K, x, ldx, part, st);
-  else if (B <= 4) gemv_tiled<NB, 4, CH>(B, packed, scales, zeros, N, K, x, ldx, part, st);
-  else gemv_tiled<NB, 8, CH>(B, packed, scales, zeros, N, K, x, ldx, part, st);
+                    const void* x, int64_t ldx, GemvOut out, hipStream_t st) {
+  if (B == 1) gemv_tiled<NB, 1, CH>(B, packed, scales, zeros, N, K, x, ldx, out, st);
+  else if (B == 2) gemv_tiled<NB, 2, CH>(B, packed, scales, zeros, N, K, x, ldx, out, st);
+  else if (B <= 4) gemv_tiled<NB, 4, CH>(B, packed, scales, zeros, N, K, x, ldx, out, st);
+  else gemv_tiled<NB, 8, CH>(B, packed, scales, zeros, N, K, x, ldx, out, st);
 }
 
 template <int NB>
 static void gemv_nb(int B, const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K,
-                    const void* x, int64_t ldx, float* part, hipStream_t st) {
-  if (K % 2048 == 0) gemv_ch<NB, 4>(B, packed, scales, zeros, N, K, x, ldx, part, st);
-  else gemv_ch<NB, 1>(B, packed, scales, zeros, N, K, x, ldx, part, st);
+                    const void* x, int64_t ldx, GemvOut out, hipStream_t st) {
+  if (K % 2048 == 0) gemv_ch<NB, 4>(B, packed, scales, zeros, N, K, x, ldx, out, st);
+  else gemv_ch<NB, 1>(B, packed, scales, zeros, N, K, x, ldx, out, st);
 }
 
 int uintx_gemv_splits(int64_t K) { return (int)(K % 2048 == 0 ? K / 2048 : K / 512); }
@@ -222,15 +236,18 @@ bool uintx_gemv_supported(int64_t N, int64_t K) { return N % 8 == 0 && K % 512 =
 void launch_uintx_gemv(int nbits, int B, const void* packed, const void* scales, const void* zeros, int64_t N,
                        int64_t K, const void* x, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, float* part,
                        hipStream_t st) {
+  // one split: each row's sum is complete in one wavefront and goes straight to y
+  const int S = uintx_gemv_splits(K);
+  GemvOut out{part, y, ldy, S > 1 ? GemvOut::kPart : (y_dtype == kBF16 ? GemvOut::kBF16 : GemvOut::kF32)};
   switch (nbits) {
-    case 2: gemv_nb<2>(B, packed, scales, zeros, N, K, x, ldx, part, st); break;
-    case 3: gemv_nb<3>(B, packed, scales, zeros, N, K, x, ldx, part, st); break;
-    case 4: gemv_nb<4>(B, packed, scales, zeros, N, K, x, ldx, part, st); break;
-    case 5: gemv_nb<5>(B, packed, scales, zeros, N, K, x, ldx, part, st); break;
-    case 6: gemv_nb<6>(B, packed, scales, zeros, N, K, x, ldx, part, st); break;
-    default: gemv_nb<7>(B, packed, scales, zeros, N, K, x, ldx, part, st); break;
+    case 2: gemv_nb<2>(B, packed, scales, zeros, N, K, x, ldx, out, st); break;
+    case 3: gemv_nb<3>(B, packed, scales, zeros, N, K, x, ldx, out, st); break;
+    case 4: gemv_nb<4>(B, packed, scales, zeros, N, K, x, ldx, out, st); break;
+    case 5: gemv_nb<5>(B, packed, scales, zeros, N, K, x, ldx, out, st); break;
+    case 6: gemv_nb<6>(B, packed, scales, zeros, N, K, x, ldx, out, st); break;
+    default: gemv_nb<7>(B, packed, scales, zeros, N, K, x, ldx, out, st); break;
   }
-  launch_gemv_finalize(part, uintx_gemv_splits(K), B, N, y, y_dtype, ldy, st);
+  if (S > 1) launch_gemv_finalize(part, S, B, N, y, y_dtype, ldy, st);
 }
 
 }  // namespace gwb

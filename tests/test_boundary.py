@@ -234,8 +234,9 @@ def test_gemv_sizes_and_validation():
         sp, b = gwb.make_spec(fmt, 4, group), ctypes.c_size_t()
         rc = lib.gwb_gemv_workspace(ctypes.byref(sp), N, K, B, ctypes.byref(b))
         return rc, b.value
-    assert ws("gptq_sym", 131072, 2048, 1) == (gwb.OK, 4 * 131072 * 4)      # 4 K-splits of 512
-    assert ws("gptq_asym", 256, 640, 3, 64) == (gwb.OK, 2 * 3 * 256 * 4)
+    assert ws("gptq_sym", 131072, 2048, 1) == (gwb.OK, 0)                  # 512 column tiles: one split
+    assert ws("gptq_sym", 65536, 2048, 1) == (gwb.OK, 2 * 65536 * 4)        # 256 tiles: two K splits
+    assert ws("gptq_asym", 256, 640, 3, 64) == (gwb.OK, 2 * 3 * 256 * 4)    # one tile: a split per 512 k
     assert ws("mxfp4", 4096, 2048, 8) == (gwb.OK, 0)
     assert ws("gptq_sym", 256, 512, 0)[0] == gwb.E_ARG
     assert ws("gptq_sym", 256, 512, 9)[0] == gwb.E_ARG
@@ -244,17 +245,19 @@ def test_gemv_sizes_and_validation():
     assert lib.gwb_gemv_workspace(ctypes.byref(sp_u), 12, 512, 1, ctypes.byref(ctypes.c_size_t())) == gwb.E_UNSUPPORTED
     assert ws("uintx", 3072, 12288, 2) == (gwb.OK, 6 * 2 * 3072 * 4)             # 2048-column splits
     assert ws("uintx", 64, 1536, 1) == (gwb.OK, 3 * 64 * 4)                      # 512-column splits
+    assert ws("uintx", 131072, 2048, 1) == (gwb.OK, 0)                           # one split: y directly
     for g, dt in [(32, gwb.BF16), (64, gwb.F16), (64, gwb.F32)]:                 # bf16 group 64 only
         su = gwb.make_spec("uintx", 4, g, dt)
         assert lib.gwb_gemv_workspace(ctypes.byref(su), 64, 1536, 1, ctypes.byref(ctypes.c_size_t())) \
             == gwb.E_UNSUPPORTED
     sp = gwb.make_spec("gptq_sym", 4, 128)
-    def go(x=fake, B=1, ldx=512, y=fake, ydt=gwb.F32, ldy=256, w=0, wsb=0):
-        return lib.gwb_gemv(ctypes.byref(sp), ctypes.byref(qt), 256, 512, P(x), B, ldx, P(y), ydt, ldy, P(w), wsb, None)
+    def go(x=fake, B=1, ldx=1024, y=fake, ydt=gwb.F32, ldy=256, w=0, wsb=0):
+        return lib.gwb_gemv(ctypes.byref(sp), ctypes.byref(qt), 256, 1024, P(x), B, ldx, P(y), ydt, ldy, P(w), wsb,
+                            None)
     assert go(ydt=7) == gwb.E_ARG
     assert go(x=None) == gwb.E_ARG
-    assert go(ldx=500) == gwb.E_ARG
-    assert go(ldx=516) == gwb.E_UNSUPPORTED
+    assert go(ldx=1000) == gwb.E_ARG
+    assert go(ldx=1028) == gwb.E_UNSUPPORTED
     assert go(x=fake + 4) == gwb.E_UNSUPPORTED
     assert go() == gwb.E_SIZE                                                 # K-split partials needed
     assert go(w=fake + 8, wsb=1 << 20) == gwb.E_UNSUPPORTED

@@ -519,6 +519,23 @@ def test_gemv_uintx_config_3072x12288():
     _gemv_check(gwb.gemv(q, x.to(DEV)), ogv.gemv(deq, xf), U32 * (24 + 40) * ogv.abs_gemv(deq, xf), torch.float32)
 
 
+def test_gemv_gptq_split_choice_sampled():
+    """65536 x 1024 GPTQ asym g64: 256 column tiles give two K splits (partials and the
+    second pass); sampled output rows against the oracle."""
+    N_, K_ = 65536, 1024
+    W = workloads.normal_weight(N_, K_, seed=523)
+    x = workloads.normal_weight(3, K_, std=1.0, seed=524)
+    q = gwb.quantize(W.to(DEV), "gptq_asym", group=64)
+    assert gwb.gemv_workspace_bytes(q, 3) == 2 * 3 * N_ * 4
+    y = _np(gwb.gemv(q, x.to(DEV))).astype(np.float64)
+    rows = np.sort(np.random.default_rng(525).choice(N_ // 8, 24, replace=False)) * 8
+    ns = (rows[:, None] + np.arange(8)[None, :]).reshape(-1)
+    xf = x.float().numpy()
+    o = ogq.quantize_asym(W[ns].float().numpy(), 64)
+    deq = ogv.dequantized("gptq_asym", o, len(ns), K_, group=64)
+    _gemv_check(torch.from_numpy(y[:, ns]), ogv.gemv(deq, xf), _gptq_bound(o, xf, 64, False, K_), torch.float32)
+
+
 def test_gemv_one_hot_reads_columns_exactly():
     """A one-hot activation makes every sum a single exact product: the GEMV returns
     dequantized weight columns bit for bit (float32 output)."""
