@@ -9,7 +9,9 @@
 // group reduced over its channels perm[gG .. gG + G - 1], giving the float32 scale and
 // zero point of every (row, group) in a workspace; (3) the codes in channel order, in the
 // tile layout of gptq.hip (32 rows x 512 k, qweight words transposed through LDS), each
-// channel with the parameters of its group, the IEEE quotient x / s as the page divides.
+// channel with the parameters of its group; the codes are those of the IEEE quotient
+// x / s the page divides, found through the reciprocal with exact division near
+// rounding boundaries.
 // Dequantization and the fused error use the same tile with each channel's group read
 // from g_idx. Both tile kernels keep every group of their 32-row band in LDS, so K / G is
 // limited to kActMaxGroups; quantization also holds one weight row in LDS (64 KB).

@@ -21,7 +21,8 @@ namespace gwb {
 // sums 64 * CH weights per row before one transposed reduction leaves lane j with row
 // j's sum. The weight pairs (the hardware bf16 pair conversion of the exact products)
 // meet the activation pairs in v_dot2c_f32_bf16; each wavefront writes one partial per
-// row, added over the K / (512 CH) wavefronts of a row in order afterwards.
+// row, added over the K / (512 CH) wavefronts of a row in order afterwards, or, when one
+// wavefront covers the whole row, the row's sum straight into y.
 template <int CTRL, int NV>
 __device__ __forceinline__ void ux_fold_half(float (&v)[8], bool up) {
 #pragma unroll
