@@ -46,12 +46,27 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ------------------------------------------------------------------ GPTQ
-constexpr int kGqLaneN = 4, kGqWaveN = 64 * kGqLaneN, kGqWaveK = 128, kGqBlockK = 4 * kGqWaveK;
+constexpr int kGqWaveK = 128, kGqBlockK = 4 * kGqWaveK;
 
-// B is the compiled width (1, 2, 4, 8); Bn <= B activation rows are real: the others
-// re-read row Bn - 1 and are not stored. kspan: the K range of one split (a multiple of
-// kGqBlockK); with one split the block writes y (TY), otherwise its partial sums.
-template <bool SYM, int G, int B, typename TY>
+// LN adjacent qweight words (columns) of one row, one load.
+template <int LN>
+__device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[LN]) {
+  if constexpr (LN == 4) {
+    const U4 v = ld16(p);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  } else if constexpr (LN == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    w[0] = *p;
+  }
+}
+
+// LN: outputs (qweight columns) per lane; a wavefront covers 64 LN of them. B is the
+// compiled width (1, 2, 4, 8); Bn <= B activation rows are real: the others re-read row
+// Bn - 1 and are not stored. kspan: the K range of one split (a multiple of kGqBlockK);
+// with one split the block writes y (TY), otherwise its partial sums.
+template <bool SYM, int G, int B, int LN, typename TY>
 __global__ __launch_bounds__(256) void gptq_gemv_kernel(const uint32_t* __restrict__ qweight,
                                                         const uint16_t* __restrict__ scale_bits,
                                                         const uint32_t* __restrict__ qzeros, int N, int K,
@@ -59,24 +74,25 @@ __global__ __launch_bounds__(256) void gptq_gemv_kernel(const uint32_t* __restri
                                                         int Bn, float* __restrict__ part, TY* __restrict__ y,
                                                         int64_t ldy) {
   static_assert(kGqWaveK % G == 0, "a wavefront covers whole groups");
-  __shared__ float red[4][B][kGqWaveN];
+  constexpr int WN = 64 * LN;                           // columns per wavefront
+  __shared__ float red[4][B][WN];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int n0 = blockIdx.x * kGqWaveN + lane * kGqLaneN;
-  const int nc = min(n0, N - kGqLaneN);                 // N % 8 == 0: lanes past N read a valid place
+  const int n0 = blockIdx.x * WN + lane * LN;
+  const int nc = min(n0, N - LN);                       // N % 8 == 0: lanes past N read a valid place
   const int kend = min(K, (int)(blockIdx.y + 1) * kspan);
-  float acc[B][kGqLaneN];
+  float acc[B][LN];
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
-    for (int j = 0; j < kGqLaneN; ++j) acc[b][j] = 0.0f;
+    for (int j = 0; j < LN; ++j) acc[b][j] = 0.0f;
   // wave-uniform steps; K % G == 0, so every step holds whole groups
   for (int kw = blockIdx.y * kspan + wave * kGqWaveK; kw < kend; kw += kGqBlockK) {
     const int nr = min(kGqWaveK, K - kw) / 8;           // qweight rows of this wavefront
-    U4 wv[kGqWaveK / 8];
+    uint32_t wv[kGqWaveK / 8][LN];
 #pragma unroll
     for (int r = 0; r < kGqWaveK / 8; ++r)
-      if (r < nr) wv[r] = ld16(qweight + (int64_t)(kw / 8 + r) * N + nc);
+      if (r < nr) load_words<LN>(qweight + (int64_t)(kw / 8 + r) * N + nc, wv[r]);
 #pragma unroll
     for (int gi = 0; gi < kGqWaveK / G; ++gi) {
       const int g0 = kw + gi * G;
@@ -93,15 +109,14 @@ __global__ __launch_bounds__(256) void gptq_gemv_kernel(const uint32_t* __restri
         }
         xs[b] = wave_sum(v);
       }
-      float cx[B][kGqLaneN];
+      float cx[B][LN];
 #pragma unroll
       for (int b = 0; b < B; ++b)
 #pragma unroll
-        for (int j = 0; j < kGqLaneN; ++j) cx[b][j] = 0.0f;
+        for (int j = 0; j < LN; ++j) cx[b][j] = 0.0f;
 #pragma unroll
       for (int rr = 0; rr < G / 8; ++rr) {
         const int r = gi * (G / 8) + rr;
-        const uint32_t w4[4] = {wv[r].x, wv[r].y, wv[r].z, wv[r].w};
         float xk[B][8];
 #pragma unroll
         for (int b = 0; b < B; ++b) {
@@ -110,8 +125,8 @@ __global__ __launch_bounds__(256) void gptq_gemv_kernel(const uint32_t* __restri
           xk[b][4] = bf16_lo(xv.z); xk[b][5] = bf16_hi(xv.z); xk[b][6] = bf16_lo(xv.w); xk[b][7] = bf16_hi(xv.w);
         }
 #pragma unroll
-        for (int j = 0; j < kGqLaneN; ++j) {
-          uint32_t ev = w4[j] & 0x0F0F0F0Fu, od = (w4[j] >> 4) & 0x0F0F0F0Fu;
+        for (int j = 0; j < LN; ++j) {
+          uint32_t ev = wv[r][j] & 0x0F0F0F0Fu, od = (wv[r][j] >> 4) & 0x0F0F0F0Fu;
           // opaque to the combiner, so each code converts straight from its byte
           // (v_cvt_f32_ubyte0..3) instead of a bit-field extract per code
           asm volatile("" : "+v"(ev), "+v"(od));
@@ -125,31 +140,31 @@ __global__ __launch_bounds__(256) void gptq_gemv_kernel(const uint32_t* __restri
         }
       }
       // s * (sum c x - z * sum x) for this group
-      const uint2 sb = *reinterpret_cast<const uint2*>(scale_bits + (int64_t)g * N + nc);
-      const float s[4] = {(float)__builtin_bit_cast(_Float16, (uint16_t)(sb.x & 0xFFFFu)),
-                          (float)__builtin_bit_cast(_Float16, (uint16_t)(sb.x >> 16)),
-                          (float)__builtin_bit_cast(_Float16, (uint16_t)(sb.y & 0xFFFFu)),
-                          (float)__builtin_bit_cast(_Float16, (uint16_t)(sb.y >> 16))};
-      float z[4] = {8.0f, 8.0f, 8.0f, 8.0f};
+      float s[LN], z[LN];
+#pragma unroll
+      for (int j = 0; j < LN; ++j) {
+        s[j] = (float)__builtin_bit_cast(_Float16, scale_bits[(int64_t)g * N + nc + j]);
+        z[j] = 8.0f;
+      }
       if constexpr (!SYM) {
         const uint32_t zw = qzeros[(int64_t)g * (N / 8) + nc / 8] >> (4 * (nc % 8));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) z[j] = (float)((zw >> (4 * j)) & 0xFu);
+        for (int j = 0; j < LN; ++j) z[j] = (float)((zw >> (4 * j)) & 0xFu);
       }
 #pragma unroll
       for (int b = 0; b < B; ++b)
 #pragma unroll
-        for (int j = 0; j < kGqLaneN; ++j) acc[b][j] = __builtin_fmaf(s[j], __builtin_fmaf(-z[j], xs[b], cx[b][j]), acc[b][j]);
+        for (int j = 0; j < LN; ++j) acc[b][j] = __builtin_fmaf(s[j], __builtin_fmaf(-z[j], xs[b], cx[b][j]), acc[b][j]);
     }
   }
   // the four wavefronts' k-ranges, added in order
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
-    for (int j = 0; j < kGqLaneN; ++j) red[wave][b][lane * kGqLaneN + j] = acc[b][j];
+    for (int j = 0; j < LN; ++j) red[wave][b][lane * LN + j] = acc[b][j];
   __syncthreads();
-  for (int e = t; e < B * kGqWaveN; e += 256) {
-    const int b = e / kGqWaveN, i = e % kGqWaveN, n = blockIdx.x * kGqWaveN + i;
+  for (int e = t; e < B * WN; e += 256) {
+    const int b = e / WN, i = e % WN, n = blockIdx.x * WN + i;
     if (n < N && b < Bn) {
       const float v = ((red[0][b][i] + red[1][b][i]) + red[2][b][i]) + red[3][b][i];
       if (gridDim.y == 1) store_y(y + (int64_t)b * ldy + n, v);
@@ -256,25 +271,34 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restri
 }
 
 // ------------------------------------------------------------------ launchers
+// Outputs per lane: 4 (one 16-byte load per qweight row). One and two measured the same
+// for one activation row and slower for four: the kernel is VALU-bound there.
+constexpr int kGqLaneN = 4;
 // K splits: one per kGqBlockK of K when N gives few blocks, fewer (down to one, which needs
-// no second pass) when N / 256 alone gives at least kGqMinBlocks.
+// no second pass) when N / (64 LN) alone gives at least kGqMinBlocks.
 constexpr int kGqMinBlocks = 512;
 int gptq_gemv_splits(int64_t N, int64_t K) {
-  const int64_t tiles = (N + kGqWaveN - 1) / kGqWaveN, kb = (K + kGqBlockK - 1) / kGqBlockK;
+  const int64_t wn = 64 * kGqLaneN;
+  const int64_t tiles = (N + wn - 1) / wn, kb = (K + kGqBlockK - 1) / kGqBlockK;
   const int64_t want = (kGqMinBlocks + tiles - 1) / tiles;
   return (int)(want < 1 ? 1 : (want > kb ? kb : want));
 }
 
-template <bool SYM, int G, int B, typename TY>
-static void gptq_gemv_b(int Bn, const void* qw, const void* sc, const void* qz, int64_t N, int64_t K, const void* x,
-                        int64_t ldx, float* part, void* y, int64_t ldy, hipStream_t st) {
+template <bool SYM, int G, int B, int LN, typename TY>
+static void gptq_gemv_ln(int Bn, const void* qw, const void* sc, const void* qz, int64_t N, int64_t K, const void* x,
+                         int64_t ldx, float* part, void* y, int64_t ldy, hipStream_t st) {
   const int S = gptq_gemv_splits(N, K);
   const int64_t kb = (K + kGqBlockK - 1) / kGqBlockK;
   const int kspan = (int)((kb + S - 1) / S) * kGqBlockK;
-  const dim3 grid((unsigned)((N + kGqWaveN - 1) / kGqWaveN), (unsigned)S);
-  hipLaunchKernelGGL((gptq_gemv_kernel<SYM, G, B, TY>), grid, dim3(256), 0, st, (const uint32_t*)qw,
+  const dim3 grid((unsigned)((N + 64 * LN - 1) / (64 * LN)), (unsigned)S);
+  hipLaunchKernelGGL((gptq_gemv_kernel<SYM, G, B, LN, TY>), grid, dim3(256), 0, st, (const uint32_t*)qw,
                      (const uint16_t*)sc, (const uint32_t*)qz, (int)N, (int)K, kspan, (const uint16_t*)x, ldx, Bn,
                      part, (TY*)y, ldy);
+}
+template <bool SYM, int G, int B, typename TY>
+static void gptq_gemv_b(int Bn, const void* qw, const void* sc, const void* qz, int64_t N, int64_t K, const void* x,
+                        int64_t ldx, float* part, void* y, int64_t ldy, hipStream_t st) {
+  gptq_gemv_ln<SYM, G, B, kGqLaneN, TY>(Bn, qw, sc, qz, N, K, x, ldx, part, y, ldy, st);
 }
 
 template <bool SYM, int G, typename TY>
