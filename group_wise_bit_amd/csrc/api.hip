@@ -398,8 +398,6 @@ static int check_gemv(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
   if (int rc = check_spec(sp, N, K)) return rc;
   if (is_act(sp->format))
     return fail(GWB_E_UNSUPPORTED, "the GEMV reads contiguous GPTQ groups; act-order weights are not provided");
-  if (sp->format == GWB_UINTX && (sp->w_dtype != GWB_BF16 || sp->group != 64))
-    return fail(GWB_E_UNSUPPORTED, "the uintx GEMV takes bf16 weights in groups of 64");
   if (sp->format == GWB_UINTX && !gwb::uintx_gemv_supported(N, K))
     return fail(GWB_E_UNSUPPORTED, "the uintx GEMV needs N %% 8 == 0 and K %% 512 == 0, got N=%lld K=%lld",
                 (long long)N, (long long)K);
@@ -433,8 +431,8 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
   if (is_mxfp4(spec->format))
     gwb::launch_mxfp4_gemv((int)B, w->codes, w->scales, N, K, x, ldx, y, y_dtype, ldy, st);
   else if (spec->format == GWB_UINTX)
-    gwb::launch_uintx_gemv(spec->nbits, (int)B, w->codes, w->scales, w->zeros, N, K, x, ldx, y, y_dtype, ldy,
-                           (float*)workspace, st);
+    gwb::launch_uintx_gemv(spec->nbits, spec->w_dtype, spec->group, (int)B, w->codes, w->scales, w->zeros, N, K, x,
+                           ldx, y, y_dtype, ldy, (float*)workspace, st);
   else
     gwb::launch_gptq_gemv(spec->format == GWB_GPTQ_SYM, spec->group, (int)B, w->codes, w->scales, w->zeros, N, K, x,
                           ldx, y, y_dtype, ldy, (float*)workspace, st);

@@ -87,13 +87,23 @@ void launch_uintx_dequant_flat(int nbits, int32_t dt, int group, const void* pac
                                const void* zeros, int64_t N, int64_t K, void* out, int32_t out_dtype, int64_t ldo,
                                hipStream_t st);
 unsigned uintx_flat_err_blocks(int64_t N, int64_t K);
+// Where a GEMV's row sums go: K-split partials, or y itself (float32 or bf16, RNE).
+struct GemvOut {
+  enum { kPart = 0, kF32 = 1, kBF16 = 2 };
+  float* part;
+  void* y;
+  int64_t ldy;
+  int mode;
+};
 #define GWB_UINTX_TILED_DT(SUF)                                                                                     \
   void uintx_tiled_quant_##SUF(int nbits, int group, const void* W, int64_t N, int64_t K, int64_t ldw,              \
                                void* packed, void* scales, void* zeros, hipStream_t st);                             \
   void uintx_tiled_dequant_##SUF(int nbits, int group, const void* packed, const void* scales, const void* zeros,   \
                                  int64_t N, int64_t K, void* out, int32_t out_dtype, int64_t ldo, hipStream_t st);  \
   void uintx_tiled_err_##SUF(int nbits, int group, const void* W, int64_t N, int64_t K, int64_t ldw,                \
-                             const void* packed, const void* scales, const void* zeros, double* part, hipStream_t st);
+                             const void* packed, const void* scales, const void* zeros, double* part, hipStream_t st); \
+  void uintx_tiled_gemv_##SUF(int nbits, int group, int B, const void* packed, const void* scales, const void* zeros, \
+                              int64_t N, int64_t K, const void* x, int64_t ldx, GemvOut out, hipStream_t st);
 GWB_UINTX_TILED_DT(bf16)
 GWB_UINTX_TILED_DT(f16)
 GWB_UINTX_TILED_DT(f32)
@@ -131,9 +141,9 @@ void launch_mxfp4_gemv(int B, const void* packed, const void* e8m0, int64_t N, i
 // splits * B * N floats
 bool uintx_gemv_supported(int64_t N, int64_t K);
 int uintx_gemv_splits(int64_t K);
-void launch_uintx_gemv(int nbits, int B, const void* packed, const void* scales, const void* zeros, int64_t N,
-                       int64_t K, const void* x, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, float* part,
-                       hipStream_t st);
+void launch_uintx_gemv(int nbits, int32_t dt, int group, int B, const void* packed, const void* scales,
+                       const void* zeros, int64_t N, int64_t K, const void* x, int64_t ldx, void* y, int32_t y_dtype,
+                       int64_t ldy, float* part, hipStream_t st);
 // y[b, n] = sum over s < S of part[(s * B + b) * N + n], in order
 void launch_gemv_finalize(const float* part, int S, int B, int64_t N, void* y, int32_t y_dtype, int64_t ldy,
                           hipStream_t st);

@@ -26,4 +26,11 @@ void uintx_tiled_err_f32(int nbits, int group, const void* W, int64_t N, int64_t
   else ux_tiled_err_entry<kF32, 128>(nbits, W, N, K, ldw, packed, scales, zeros, part, st);
 }
 
+void uintx_tiled_gemv_f32(int nbits, int group, int B, const void* packed, const void* scales, const void* zeros,
+                          int64_t N, int64_t K, const void* x, int64_t ldx, GemvOut out, hipStream_t st) {
+  if (group == 32) ux_tiled_gemv_entry<kF32, 32>(nbits, B, packed, scales, zeros, N, K, x, ldx, out, st);
+  else if (group == 64) ux_tiled_gemv_entry<kF32, 64>(nbits, B, packed, scales, zeros, N, K, x, ldx, out, st);
+  else ux_tiled_gemv_entry<kF32, 128>(nbits, B, packed, scales, zeros, N, K, x, ldx, out, st);
+}
+
 }  // namespace gwb

@@ -313,6 +313,148 @@ __global__ __launch_bounds__(256) void uintx_dequant_tiled(const uint8_t* __rest
   if constexpr (SINK == kErr) block_sum2_store<256>(sw, se, part);
 }
 
+// ------------------------------------------------------------- decode GEMV
+// y[b, n] = sum_k x[b, k] * w[n, k] with w the weight page uintx_quant.py's forward
+// multiplies: r((q - zp) * s) in the weight dtype, converted to the bf16 of the
+// activations (one RNE rounding for bf16 weights, the page's two for fp16 and fp32).
+// With N % 8 == 0 and K % 512 == 0, position p of segment j is row j * N/8 + p / K,
+// column p % K: a lane's 8 positions of the 8 segments share 8 activation columns and feed
+// 8 output rows. A wavefront takes CH consecutive 512-position chunks of one row (CH = 4
+// when K % 2048 == 0), so each lane sums 64 * CH weights per row before one transposed
+// reduction leaves lane j with row j's sum. The weight pairs meet the activation pairs in
+// v_dot2c_f32_bf16; each wavefront writes one partial per row, added over the
+// K / (512 CH) wavefronts of a row in order afterwards, or, when one wavefront covers the
+// whole row, the row's sum straight into y.
+template <int CTRL, int NV>
+__device__ __forceinline__ void ux_fold_half(float (&v)[8], bool up) {
+#pragma unroll
+  for (int i = 0; i < NV / 2; ++i) {
+    const float keep = up ? v[i + NV / 2] : v[i], send = up ? v[i] : v[i + NV / 2];
+    v[i] = keep + dpp_read<CTRL>(send);
+  }
+}
+// 8 values per lane -> lane l holds the wavefront sum of value (l & 7). The half-mirror
+// partner of lane i is 7 - i (differs in bit 2), the quad steps pair bits 1 and 0; then
+// the eight 8-lane groups, which hold the same value index, are added.
+__device__ __forceinline__ float ux_transposed_sum(float (&v)[8], int lane) {
+  ux_fold_half<kDppHalfMirror, 8>(v, lane & 4);
+  ux_fold_half<kDppXor2, 4>(v, lane & 2);
+  ux_fold_half<kDppXor1, 2>(v, lane & 1);
+  float r = v[0];
+  r += dpp_read<kDppRor8>(r);
+  r += __shfl_xor(r, 16);
+  r += __shfl_xor(r, 32);
+  return r;
+}
+
+template <int NB, int DT, int G, int B, int CH>
+__global__ __launch_bounds__(256) void uintx_gemv_tiled(const uint8_t* __restrict__ packed,
+                                                        const typename UxDt<DT>::T* __restrict__ scales,
+                                                        const uint8_t* __restrict__ zeros, FastDiv kdiv, uint32_t L1,
+                                                        Shards sh, int N, const uint16_t* __restrict__ x,
+                                                        int64_t ldx, int Bn, GemvOut out) {
+  using SB = ShardBits<NB>;
+  using D = UxDt<DT>;
+  constexpr int LG = G / 8;                    // lanes per group
+  constexpr int PER = LG >= 8 ? 1 : 8 / LG;    // groups whose parameters one lane loads
+  __shared__ typename D::Lds qp_lds[CH][256 / LG * 8];
+  const int lane = threadIdx.x & 63;
+  const uint32_t p0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * (uint32_t)(kWavePos * CH) + lane * kLanePos;
+  const bool active = p0 < L1;               // whole wavefronts: L1 % (512 CH) == 0
+  const uint32_t pa = active ? p0 : 0;
+  const uint32_t row = fdiv(pa, kdiv), col0 = pa - row * kdiv.d;   // the CH chunks stay in this row
+  const int set = threadIdx.x / LG;
+  uint2 s4[CH][4], s2[CH][2], s1[CH];
+  U4 xv[CH][B];
+  if (active) {
+    const int i = lane % LG;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const uint32_t p = p0 + c * kWavePos, ps = p - i * kLanePos;   // ps: the set's first position
+#pragma unroll
+      for (int m = 0; m < PER; ++m) {
+        const int jj = (i + m * LG) & 7;
+        const uint32_t g = (jj * L1 + ps) / G;
+        const typename D::T sc = scales[g];
+        const uint32_t zz = zeros[g];
+        if (LG <= 8 || i < 8) qp_lds[c][set * 8 + jj] = D::pack(sc, zz);
+      }
+      if constexpr (SB::has4) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) s4[c][m] = ld8(packed + sh.base4 + (int64_t)m * L1 + p);
+      }
+      if constexpr (SB::has2) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) s2[c][m] = ld8(packed + sh.base2 + (int64_t)m * L1 + p);
+      }
+      if constexpr (SB::has1) s1[c] = ld8(packed + sh.base1 + p);
+#pragma unroll
+      for (int b = 0; b < B; ++b) xv[c][b] = ld16(x + (int64_t)min(b, Bn - 1) * ldx + col0 + c * kWavePos);
+    }
+  }
+  __syncthreads();
+  if (!active) return;                       // wave-uniform, after the only barrier
+  float acc[B][8];
+#pragma unroll
+  for (int b = 0; b < B; ++b)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[b][j] = 0.0f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const typename D::Lds* qpo = &qp_lds[c][set * 8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const typename D::Lds w = qpo[j];
+      const float s = D::lds_value(w), zp = D::lds_zp(w);
+      uint32_t cd[2] = {0u, 0u};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (SB::has4) cd[h] |= ((h ? s4[c][j & 3].y : s4[c][j & 3].x) >> (4 * (j >> 2))) & 0x0F0F0F0Fu;
+        if constexpr (SB::has2)
+          cd[h] |= (((h ? s2[c][j & 1].y : s2[c][j & 1].x) >> (2 * (j >> 1))) & 0x03030303u) << SB::off2;
+        if constexpr (SB::has1) cd[h] |= (((h ? s1[c].y : s1[c].x) >> j) & 0x01010101u) << SB::off1;
+      }
+      float d[8];
+      if constexpr (DT == kF32) {
+        // (q - zp) exact, times s: the page's one float32 rounding
+#pragma unroll
+        for (int q = 0; q < 8; ++q) d[q] = ((float)((cd[q >> 2] >> (8 * (q & 3))) & 0xFFu) - zp) * s;
+      } else {
+        // exact in float32 for the 2-byte dtypes: c * s - zp * s as one fma
+        const float nzs = -(zp * s);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) d[q] = __builtin_fmaf((float)((cd[q >> 2] >> (8 * (q & 3))) & 0xFFu), s, nzs);
+        if constexpr (DT == kF16) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) d[q] = D::rnd(d[q]);      // the fp16 weight, then its bf16
+        }
+      }
+      ux_bf16x2_t wp[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wp[q] = __builtin_convertvector(ux_f32x2_t{d[2 * q], d[2 * q + 1]}, ux_bf16x2_t);
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const uint32_t xw[4] = {xv[c][b].x, xv[c][b].y, xv[c][b].z, xv[c][b].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[b][j] = __builtin_amdgcn_fdot2_f32_bf16(wp[q], __builtin_bit_cast(ux_bf16x2_t, xw[q]), acc[b][j], false);
+      }
+    }
+  }
+  const int j = lane & 7;
+  const uint32_t chunk = col0 / (kWavePos * CH);
+#pragma unroll
+  for (int b = 0; b < B; ++b) {
+    const float v = ux_transposed_sum(acc[b], lane);
+    if (lane < 8 && b < Bn) {
+      const int64_t n = (int64_t)j * (N / 8) + row;
+      if (out.mode == GemvOut::kPart) out.part[((int64_t)chunk * Bn + b) * N + n] = v;
+      else if (out.mode == GemvOut::kF32) static_cast<float*>(out.y)[b * out.ldy + n] = v;
+      else static_cast<uint16_t*>(out.y)[b * out.ldy + n] = (uint16_t)f32_to_bf16_rne(v);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 // Contiguous rows (ld == K) index elements directly; otherwise through a fast division.
 template <int DT, int G, int NB>
@@ -381,6 +523,43 @@ template <int DT, int G>
 void ux_tiled_err_entry(int nbits, const void* W, int64_t N, int64_t K, int64_t ldw, const void* packed,
                         const void* scales, const void* zeros, double* part, hipStream_t st) {
   ux_deq_tiled<DT, G, kErr, kF32>(nbits, packed, scales, zeros, N, K, nullptr, 0, W, ldw, part, st);
+}
+
+template <int DT, int G, int NB, int B, int CH>
+void ux_gemv_launch(int Bn, const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K,
+                    const void* x, int64_t ldx, GemvOut out, hipStream_t st) {
+  const uint32_t numel = (uint32_t)(N * K);
+  const unsigned blocks = (unsigned)(((uint64_t)numel / 8 / (kWavePos * CH) + 3) / 4);
+  hipLaunchKernelGGL((uintx_gemv_tiled<NB, DT, G, B, CH>), dim3(blocks), dim3(256), 0, st, (const uint8_t*)packed,
+                     (const typename UxDt<DT>::T*)scales, (const uint8_t*)zeros, make_fastdiv((uint32_t)K),
+                     numel / 8, shards_of(NB, numel), (int)N, (const uint16_t*)x, ldx, Bn, out);
+}
+template <int DT, int G, int NB, int CH>
+void ux_gemv_b(int B, const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K, const void* x,
+               int64_t ldx, GemvOut out, hipStream_t st) {
+  if (B == 1) ux_gemv_launch<DT, G, NB, 1, CH>(B, packed, scales, zeros, N, K, x, ldx, out, st);
+  else if (B == 2) ux_gemv_launch<DT, G, NB, 2, CH>(B, packed, scales, zeros, N, K, x, ldx, out, st);
+  else if (B <= 4) ux_gemv_launch<DT, G, NB, 4, CH>(B, packed, scales, zeros, N, K, x, ldx, out, st);
+  else ux_gemv_launch<DT, G, NB, 8, CH>(B, packed, scales, zeros, N, K, x, ldx, out, st);
+}
+template <int DT, int G, int NB>
+void ux_gemv_nb(int B, const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K, const void* x,
+                int64_t ldx, GemvOut out, hipStream_t st) {
+  if (K % 2048 == 0) ux_gemv_b<DT, G, NB, 4>(B, packed, scales, zeros, N, K, x, ldx, out, st);
+  else ux_gemv_b<DT, G, NB, 1>(B, packed, scales, zeros, N, K, x, ldx, out, st);
+}
+// The decode GEMV of one (dtype, group): N % 8 == 0, K % 512 == 0, B <= 8.
+template <int DT, int G>
+void ux_tiled_gemv_entry(int nbits, int B, const void* packed, const void* scales, const void* zeros, int64_t N,
+                         int64_t K, const void* x, int64_t ldx, GemvOut out, hipStream_t st) {
+  switch (nbits) {
+    case 2: ux_gemv_nb<DT, G, 2>(B, packed, scales, zeros, N, K, x, ldx, out, st); break;
+    case 3: ux_gemv_nb<DT, G, 3>(B, packed, scales, zeros, N, K, x, ldx, out, st); break;
+    case 4: ux_gemv_nb<DT, G, 4>(B, packed, scales, zeros, N, K, x, ldx, out, st); break;
+    case 5: ux_gemv_nb<DT, G, 5>(B, packed, scales, zeros, N, K, x, ldx, out, st); break;
+    case 6: ux_gemv_nb<DT, G, 6>(B, packed, scales, zeros, N, K, x, ldx, out, st); break;
+    default: ux_gemv_nb<DT, G, 7>(B, packed, scales, zeros, N, K, x, ldx, out, st); break;
+  }
 }
 
 }  // namespace gwb

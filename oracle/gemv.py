@@ -17,17 +17,24 @@ from __future__ import annotations
 import numpy as np
 
 from . import gptq, mxfp4, uintx
-from ._fp import f32
+from ._fp import bf16_round, f32
 
 
-def dequantized(fmt: str, q: dict, N: int, K: int, group: int = 128, nbits: int = 4) -> np.ndarray:
-    """Stored tensors of one format -> float32 [N, K] (exact values)."""
+def dequantized(fmt: str, q: dict, N: int, K: int, group=None, nbits: int = 4,
+                dtype: str = "bf16") -> np.ndarray:
+    """Stored tensors of one format -> the float32 [N, K] weight the consumer multiplies
+    (group: the format's default, GPTQ 128 and uintx 64, when None).
+    uintx (page uintx_quant.py, forward): the dequantized weight of the weight dtype,
+    converted to the activations' bf16 when it is not bf16 already (`w.to(x.dtype)`)."""
     if fmt == "gptq_sym" or fmt == "gptq_asym":
-        return gptq.dequantize(q["qweight"], q["scales"], q["qzeros"], group, fmt == "gptq_sym")
+        return gptq.dequantize(q["qweight"], q["scales"], q["qzeros"], 128 if group is None else group,
+                               fmt == "gptq_sym")
     if fmt == "mxfp4":
         return mxfp4.dequantize(q["packed"], q["e8m0"], K)
     if fmt == "uintx":
-        return uintx.dequantize(q["packed"], q["scale_bytes"], q["zero_point"], nbits, N, K)
+        w = uintx.dequantize(q["packed"], q["scale_bytes"], q["zero_point"], nbits, N, K,
+                             64 if group is None else group, dtype)
+        return w if dtype == "bf16" else bf16_round(w)
     raise ValueError(fmt)
 
 

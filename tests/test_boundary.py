@@ -246,10 +246,10 @@ def test_gemv_sizes_and_validation():
     assert ws("uintx", 3072, 12288, 2) == (gwb.OK, 6 * 2 * 3072 * 4)             # 2048-column splits
     assert ws("uintx", 64, 1536, 1) == (gwb.OK, 3 * 64 * 4)                      # 512-column splits
     assert ws("uintx", 131072, 2048, 1) == (gwb.OK, 0)                           # one split: y directly
-    for g, dt in [(32, gwb.BF16), (64, gwb.F16), (64, gwb.F32)]:                 # bf16 group 64 only
-        su = gwb.make_spec("uintx", 4, g, dt)
-        assert lib.gwb_gemv_workspace(ctypes.byref(su), 64, 1536, 1, ctypes.byref(ctypes.c_size_t())) \
-            == gwb.E_UNSUPPORTED
+    for g, dt in [(32, gwb.BF16), (64, gwb.F16), (128, gwb.F32)]:                # every dtype and group
+        su, b = gwb.make_spec("uintx", 4, g, dt), ctypes.c_size_t()
+        assert lib.gwb_gemv_workspace(ctypes.byref(su), 64, 1536, 1, ctypes.byref(b)) == gwb.OK
+        assert b.value == 3 * 64 * 4
     sp = gwb.make_spec("gptq_sym", 4, 128)
     def go(x=fake, B=1, ldx=1024, y=fake, ydt=gwb.F32, ldy=256, w=0, wsb=0):
         return lib.gwb_gemv(ctypes.byref(sp), ctypes.byref(qt), 256, 1024, P(x), B, ldx, P(y), ydt, ldy, P(w), wsb,

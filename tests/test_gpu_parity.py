@@ -509,6 +509,31 @@ def test_gemv_uintx_parity(nbits, n, k, B):
         _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ogv.gemv(deq, xf), bound, ydt)
 
 
+@pytest.mark.parametrize("dt,group", [("f16", 64), ("f32", 64), ("bf16", 32), ("bf16", 128), ("f16", 128),
+                                      ("f32", 32)])
+@pytest.mark.parametrize("nbits,n,k,B", [(4, 64, 512, 1), (3, 16, 2048, 3), (7, 136, 1536, 8), (2, 24, 4096, 2)])
+def test_gemv_uintx_variants_parity(dt, group, nbits, n, k, B):
+    """The page's forward on fp16 / fp32 weights and groups 32 / 128: x times the
+    weight-dtype dequantized weight converted to the activations' bf16."""
+    W = workloads.uintx_weight(n, k, seed=540 + n + group, outlier_frac=0.01, dtype=_TDT[dt])
+    x = workloads.normal_weight(B, k, std=1.0, seed=541 + B)
+    q = gwb.quantize(W.to(DEV), "uintx", nbits=nbits, group=group)
+    o = oux.quantize(W.float().numpy(), nbits, group, dt)
+    deq = ogv.dequantized("uintx", o, n, k, group=group, nbits=nbits, dtype=dt)
+    xf = x.float().numpy()
+    bound = U32 * (k // 512 + 40) * ogv.abs_gemv(deq, xf)
+    for ydt in (torch.float32, torch.bfloat16):
+        _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ogv.gemv(deq, xf), bound, ydt)
+    # one-hot activations return the multiplied weight's columns bit for bit
+    xo = torch.zeros(B, k, dtype=torch.bfloat16)
+    cols = [(b * 97 + 5) % k for b in range(B)]
+    for b, kk in enumerate(cols):
+        xo[b, kk] = 1.0
+    y = _np(gwb.gemv(q, xo.to(DEV)))
+    for b, kk in enumerate(cols):
+        assert np.array_equal(y[b], deq[:, kk]), (b, kk)
+
+
 def test_gemv_uintx_config_3072x12288():
     W = workloads.uintx_weight()
     x = workloads.normal_weight(2, 12288, std=1.0, seed=532)

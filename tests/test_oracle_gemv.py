@@ -57,3 +57,25 @@ def test_dequantized_matches_each_format_oracle():
     q = gq.quantize_sym(W, 128)
     assert np.array_equal(og.dequantized("gptq_sym", q, 16, 256),
                           gq.dequantize(q["qweight"], q["scales"], q["qzeros"], 128, True))
+
+
+def test_uintx_forward_weight_is_bf16_of_the_dtype_value():
+    """Page uintx_quant.py's forward casts the dequantized weight to the activations'
+    dtype: for fp16 / fp32 weights the GEMV multiplies bf16(w), a second rounding that
+    changes some values (and none for bf16 weights)."""
+    import oracle.uintx as ux
+    import torch
+    from _exact import rnbf16
+    for dt, tdt in (("f16", torch.float16), ("f32", torch.float32)):
+        W = workloads.uintx_weight(8, 256, seed=97, dtype=tdt).float().numpy()
+        q = ux.quantize(W, 5, 32, dt)
+        wd = ux.dequantize(q["packed"], q["scale_bytes"], q["zero_point"], 5, 8, 256, 32, dt)
+        got = og.dequantized("uintx", q, 8, 256, group=32, nbits=5, dtype=dt)
+        for r in range(0, 8, 3):
+            for k in range(0, 256, 5):
+                assert F(got[r, k]) == rnbf16(F(wd[r, k]))
+        assert np.any(got != wd)
+    Wb = workloads.uintx_weight(8, 256, seed=98).float().numpy()
+    qb = ux.quantize(Wb, 4)
+    assert np.array_equal(og.dequantized("uintx", qb, 8, 256, group=64, nbits=4),
+                          ux.dequantize(qb["packed"], qb["scale_bytes"], qb["zero_point"], 4, 8, 256))
