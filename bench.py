@@ -158,7 +158,8 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
     """Paths next to the hot path, timed on their own after the step (not part of
     value): the AWQ fold of the gate_up weight (columns * s) straight to MXFP4, the same
     fold also writing the folded bf16 weight, and the decode GEMV reading a packed
-    131072 x 2048 lm_head (GPTQ sym g128, MXFP4, uintx4 g64) for one activation row, and
+    131072 x 2048 lm_head (GPTQ sym g128, MXFP4, uintx4 g64, GPTQ sym g128 with act-order
+    groups in a seeded channel order) for one activation row, and
     the uintx variants (float16 / float32 weights, groups 32 / 128) at [3072, 12288], and
     GPTQ with act-order groups on the gate_up weight."""
     out = []
@@ -183,6 +184,8 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
     qg = [gwb.quantize(head, "gptq_sym", group=128) for _ in range(3)]
     qm = [gwb.quantize(head, "mxfp4") for _ in range(3)]
     qu = [gwb.quantize(head, "uintx", nbits=4) for _ in range(3)]
+    hperm = torch.from_numpy(np.random.default_rng(526).permutation(HK).astype(np.int32)).to(dev)
+    qa = [gwb.quantize(head, "gptq_sym_act", group=128, perm=hperm) for _ in range(3)]
     del head
     wsu = torch.empty(gwb.gemv_workspace_bytes(qu[0], 1), dtype=torch.uint8, device=dev)
     wsg = torch.empty(gwb.gemv_workspace_bytes(qg[0], 1), dtype=torch.uint8, device=dev)
@@ -202,6 +205,8 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
          cycle([gwb.prepare_gemv(q, xh, yh, None) for q in qm])),
         ("gemv.uintx4_g64.lm_head_b1", hk / 2 + hk / 64 * 3 + 2 * HK + 4 * HN,
          cycle([gwb.prepare_gemv(q, xh, yh, wsu) for q in qu])),
+        ("gemv.gptq_sym_act_g128.lm_head_b1", hk / 2 + hk / 128 * 2 + 4 * HK + 2 * HK + 4 * HN,
+         cycle([gwb.prepare_gemv(q, xh, yh, None) for q in qa])),
     ]
     # uintx variants at the uintx workload shape [3072, 12288], 4 bits: float16 and
     # float32 weights (group 64) and bf16 groups 32 and 128; enough copies cycled that

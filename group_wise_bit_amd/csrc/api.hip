@@ -390,14 +390,13 @@ static size_t gemv_workspace(const gwb_qspec* sp, int64_t N, int64_t K, int64_t 
   // the K-split partial sums (none with a single split)
   int S = 0;
   if (sp->format == GWB_GPTQ_SYM || sp->format == GWB_GPTQ_ASYM) S = gwb::gptq_gemv_splits(N, K);
+  if (is_act(sp->format)) S = gwb::gptq_act_gemv_splits(N, K);
   if (sp->format == GWB_UINTX) S = gwb::uintx_gemv_splits(K);
   return S > 1 ? (size_t)S * (size_t)B * (size_t)N * sizeof(float) : 0;
 }
 
 static int check_gemv(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
   if (int rc = check_spec(sp, N, K)) return rc;
-  if (is_act(sp->format))
-    return fail(GWB_E_UNSUPPORTED, "the GEMV reads contiguous GPTQ groups; act-order weights are not provided");
   if (sp->format == GWB_UINTX && !gwb::uintx_gemv_supported(N, K))
     return fail(GWB_E_UNSUPPORTED, "the uintx GEMV needs N %% 8 == 0 and K %% 512 == 0, got N=%lld K=%lld",
                 (long long)N, (long long)K);
@@ -430,6 +429,9 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
   hipStream_t st = (hipStream_t)stream;
   if (is_mxfp4(spec->format))
     gwb::launch_mxfp4_gemv((int)B, w->codes, w->scales, N, K, x, ldx, y, y_dtype, ldy, st);
+  else if (is_act(spec->format))
+    gwb::launch_gptq_act_gemv(is_gptq_sym(spec->format), spec->group, (int)B, w->codes, w->scales, w->zeros,
+                              (const int32_t*)w->g_idx, N, K, x, ldx, y, y_dtype, ldy, (float*)workspace, st);
   else if (spec->format == GWB_UINTX)
     gwb::launch_uintx_gemv(spec->nbits, spec->w_dtype, spec->group, (int)B, w->codes, w->scales, w->zeros, N, K, x,
                            ldx, y, y_dtype, ldy, (float*)workspace, st);

@@ -173,6 +173,91 @@ __global__ __launch_bounds__(256) void gptq_gemv_kernel(const uint32_t* __restri
   }
 }
 
+// ------------------------------------------------------------------ GPTQ act-order
+// Act-order GPTQ (channel k in group g_idx[k], gptq_act.hip): the per-group factoring
+// above does not apply, so each weight is formed: w = (c - z) s, exact in float32 as one
+// fma (5-bit code difference, fp16 scale). A block covers 64 columns, one qweight word
+// per lane, and its four wavefronts take 128-k steps of its K range in turn; for every
+// k the group g_idx[k] is the same across the wavefront and picks each column's scale and
+// zero point from LDS, which holds every group's for the block's columns. Products with
+// the bf16 activations are exact; sums are float32 in k order per wavefront.
+constexpr int kActGvCols = 64;
+
+template <bool SYM, int B, typename TY>
+__global__ __launch_bounds__(256) void gptq_act_gemv_kernel(const uint32_t* __restrict__ qweight,
+                                                            const uint16_t* __restrict__ scale_bits,
+                                                            const uint32_t* __restrict__ qzeros,
+                                                            const int32_t* __restrict__ g_idx, int N, int K, int NG,
+                                                            int kspan, const uint16_t* __restrict__ x, int64_t ldx,
+                                                            int Bn, float* __restrict__ part, TY* __restrict__ y,
+                                                            int64_t ldy) {
+  extern __shared__ uint32_t lds[];
+  uint16_t* sl = reinterpret_cast<uint16_t*>(lds);             // [NG][64] fp16 scale bits
+  uint32_t* zl = lds + NG * (kActGvCols / 2);                    // [NG][8] qzeros words
+  __shared__ float red[4][B][kActGvCols];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int n0 = blockIdx.x * kActGvCols;
+  const int nc = min(n0 + lane, N - 1);                         // lanes past N read a valid place
+  for (int e = t; e < NG * kActGvCols; e += 256) {
+    const int g = e / kActGvCols, c = e - g * kActGvCols;
+    sl[e] = n0 + c < N ? scale_bits[(int64_t)g * N + n0 + c] : (uint16_t)0;
+  }
+  if constexpr (!SYM) {
+    for (int e = t; e < NG * (kActGvCols / 8); e += 256) {
+      const int g = e / (kActGvCols / 8), q = e - g * (kActGvCols / 8);
+      zl[e] = n0 + 8 * q < N ? qzeros[(int64_t)g * (N / 8) + n0 / 8 + q] : 0u;
+    }
+  }
+  __syncthreads();
+  const int kend = min(K, (int)(blockIdx.y + 1) * kspan);
+  float acc[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+  for (int kw = blockIdx.y * kspan + wave * 128; kw < kend; kw += 512) {   // wave-uniform
+    const int nr = min(128, K - kw) / 8;
+    uint32_t wv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (r < nr) wv[r] = qweight[(int64_t)(kw / 8 + r) * N + nc];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (r >= nr) continue;                                    // wave-uniform
+      const int k = kw + 8 * r;
+      const U4 ga = ld16(g_idx + k), gb = ld16(g_idx + k + 4);
+      const uint32_t g8[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+      float xk[B][8];
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        const U4 xv = *reinterpret_cast<const U4*>(x + (int64_t)min(b, Bn - 1) * ldx + k);
+        xk[b][0] = bf16_lo(xv.x); xk[b][1] = bf16_hi(xv.x); xk[b][2] = bf16_lo(xv.y); xk[b][3] = bf16_hi(xv.y);
+        xk[b][4] = bf16_lo(xv.z); xk[b][5] = bf16_hi(xv.z); xk[b][6] = bf16_lo(xv.w); xk[b][7] = bf16_hi(xv.w);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t g = g8[i] < (uint32_t)NG ? g8[i] : (uint32_t)(NG - 1);   // clamped into range
+        const float sc = (float)__builtin_bit_cast(_Float16, sl[g * kActGvCols + lane]);
+        float z = 8.0f;
+        if constexpr (!SYM) z = (float)((zl[g * (kActGvCols / 8) + lane / 8] >> (4 * (lane % 8))) & 0xFu);
+        const float w = __builtin_fmaf((float)((wv[r] >> (4 * i)) & 0xFu), sc, -(z * sc));
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] = __builtin_fmaf(w, xk[b][i], acc[b]);
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < B; ++b) red[wave][b][lane] = acc[b];
+  __syncthreads();
+  for (int e = t; e < B * kActGvCols; e += 256) {
+    const int b = e / kActGvCols, i = e - b * kActGvCols, n = n0 + i;
+    if (n < N && b < Bn) {
+      const float v = ((red[0][b][i] + red[1][b][i]) + red[2][b][i]) + red[3][b][i];
+      if (gridDim.y == 1) store_y(y + (int64_t)b * ldy + n, v);
+      else part[((int64_t)blockIdx.y * Bn + b) * N + n] = v;
+    }
+  }
+}
+
 // y[b, n] = sum over the K splits of part[s][b][n], in order.
 template <typename TY>
 __global__ __launch_bounds__(256) void gemv_finalize_kernel(const float* __restrict__ part, int S, int B, int N,
@@ -329,6 +414,49 @@ void launch_gptq_gemv(bool sym, int group, int B, const void* qweight, const voi
     else gptq_gemv_s<false, float>(group, B, qweight, scales, qzeros, N, K, x, ldx, part, y, ldy, st);
   }
   const int S = gptq_gemv_splits(N, K);
+  if (S > 1) launch_gemv_finalize(part, S, B, N, y, y_dtype, ldy, st);
+}
+
+int gptq_act_gemv_splits(int64_t N, int64_t K) {
+  const int64_t tiles = (N + kActGvCols - 1) / kActGvCols, kb = (K + 511) / 512;
+  const int64_t want = (kGqMinBlocks + tiles - 1) / tiles;
+  return (int)(want < 1 ? 1 : (want > kb ? kb : want));
+}
+
+template <bool SYM, int B, typename TY>
+static void act_gemv_b(int Bn, int group, const void* qw, const void* sc, const void* qz, const int32_t* g_idx,
+                       int64_t N, int64_t K, const void* x, int64_t ldx, float* part, void* y, int64_t ldy,
+                       hipStream_t st) {
+  const int S = gptq_act_gemv_splits(N, K), NG = (int)(K / group);
+  const int64_t kb = (K + 511) / 512;
+  const int kspan = (int)((kb + S - 1) / S) * 512;
+  const size_t lds = (size_t)NG * (kActGvCols * 2 + (SYM ? 0 : (kActGvCols / 8) * 4));
+  const dim3 grid((unsigned)((N + kActGvCols - 1) / kActGvCols), (unsigned)S);
+  hipLaunchKernelGGL((gptq_act_gemv_kernel<SYM, B, TY>), grid, dim3(256), lds, st, (const uint32_t*)qw,
+                     (const uint16_t*)sc, (const uint32_t*)qz, g_idx, (int)N, (int)K, NG, kspan, (const uint16_t*)x,
+                     ldx, Bn, part, (TY*)y, ldy);
+}
+template <bool SYM, typename TY>
+static void act_gemv_s(int B, int group, const void* qw, const void* sc, const void* qz, const int32_t* g_idx,
+                       int64_t N, int64_t K, const void* x, int64_t ldx, float* part, void* y, int64_t ldy,
+                       hipStream_t st) {
+  if (B == 1) act_gemv_b<SYM, 1, TY>(B, group, qw, sc, qz, g_idx, N, K, x, ldx, part, y, ldy, st);
+  else if (B == 2) act_gemv_b<SYM, 2, TY>(B, group, qw, sc, qz, g_idx, N, K, x, ldx, part, y, ldy, st);
+  else if (B <= 4) act_gemv_b<SYM, 4, TY>(B, group, qw, sc, qz, g_idx, N, K, x, ldx, part, y, ldy, st);
+  else act_gemv_b<SYM, 8, TY>(B, group, qw, sc, qz, g_idx, N, K, x, ldx, part, y, ldy, st);
+}
+
+void launch_gptq_act_gemv(bool sym, int group, int B, const void* qweight, const void* scales, const void* qzeros,
+                          const int32_t* g_idx, int64_t N, int64_t K, const void* x, int64_t ldx, void* y,
+                          int32_t y_dtype, int64_t ldy, float* part, hipStream_t st) {
+  if (y_dtype == kBF16) {
+    if (sym) act_gemv_s<true, uint16_t>(B, group, qweight, scales, qzeros, g_idx, N, K, x, ldx, part, y, ldy, st);
+    else act_gemv_s<false, uint16_t>(B, group, qweight, scales, qzeros, g_idx, N, K, x, ldx, part, y, ldy, st);
+  } else {
+    if (sym) act_gemv_s<true, float>(B, group, qweight, scales, qzeros, g_idx, N, K, x, ldx, part, y, ldy, st);
+    else act_gemv_s<false, float>(B, group, qweight, scales, qzeros, g_idx, N, K, x, ldx, part, y, ldy, st);
+  }
+  const int S = gptq_act_gemv_splits(N, K);
   if (S > 1) launch_gemv_finalize(part, S, B, N, y, y_dtype, ldy, st);
 }
 

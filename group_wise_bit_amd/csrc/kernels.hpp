@@ -135,6 +135,11 @@ int gptq_gemv_splits(int64_t N, int64_t K);   // K splits; with more than one, p
 void launch_gptq_gemv(bool sym, int group, int B, const void* qweight, const void* scales, const void* qzeros,
                       int64_t N, int64_t K, const void* x, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
                       float* part, hipStream_t st);
+// act-order GPTQ (group of channel k = g_idx[k]; K/G <= kActMaxGroups)
+int gptq_act_gemv_splits(int64_t N, int64_t K);
+void launch_gptq_act_gemv(bool sym, int group, int B, const void* qweight, const void* scales, const void* qzeros,
+                          const int32_t* g_idx, int64_t N, int64_t K, const void* x, int64_t ldx, void* y,
+                          int32_t y_dtype, int64_t ldy, float* part, hipStream_t st);
 void launch_mxfp4_gemv(int B, const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x,
                        int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, hipStream_t st);
 // uintx (uintx.hip): N % 8 == 0 and K % 512 == 0; with more than one split, part holds

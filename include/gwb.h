@@ -229,8 +229,8 @@ int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t
  *   spec, w  a GPTQ (sym or asym), MXFP4 or uintx weight as gwb_quantize wrote it, [N, K];
  *            uintx (page uintx_quant.py, forward: x times the dequantized weight of the
  *            weight dtype, r((q - zp) * s), converted to bf16 when it is not bf16) needs
- *            N % 8 == 0 and K % 512 == 0; act-order GPTQ is not provided; both refuse
- *            with GWB_E_UNSUPPORTED
+ *            N % 8 == 0 and K % 512 == 0 (else GWB_E_UNSUPPORTED); act-order GPTQ reads
+ *            w->g_idx (required)
  *   x        device bf16 [B, K], row stride ldx (multiple of 8), 16-byte aligned; 1 <= B <= 8
  *   y        device [B, N] of y_dtype (GWB_F32 or GWB_BF16, RNE), row stride ldy
  *   workspace at least gwb_gemv_workspace bytes (GPTQ and uintx: K-split partial sums;

@@ -297,9 +297,12 @@ def test_act_order_gptq_validates():
     assert act(wsb=100) == gwb.E_SIZE
     assert act(ws=fake + 8) == gwb.E_UNSUPPORTED
     assert act(perm=fake + 4) == gwb.E_UNSUPPORTED
-    # dequantization and SNR need g_idx; the GEMV does not take act-order weights
+    # dequantization and SNR need g_idx; the GEMV takes act-order weights
     assert lib.gwb_dequantize(ctypes.byref(sp), ctypes.byref(qn), 8, 256, P(fake), gwb.F32, 256, None, 0, None) \
         == gwb.E_ARG
     assert lib.gwb_snr(ctypes.byref(sp), P(fake), 8, 256, 256, ctypes.byref(qn), P(fake), P(fake), 1 << 20, None) \
         == gwb.E_ARG
-    assert lib.gwb_gemv_workspace(ctypes.byref(sp), 8, 256, 1, ctypes.byref(ctypes.c_size_t())) == gwb.E_UNSUPPORTED
+    b = ctypes.c_size_t()
+    assert lib.gwb_gemv_workspace(ctypes.byref(sp), 8, 256, 1, ctypes.byref(b)) == gwb.OK and b.value == 0
+    assert lib.gwb_gemv_workspace(ctypes.byref(sp), 64, 2048, 2, ctypes.byref(b)) == gwb.OK
+    assert b.value == 4 * 2 * 64 * 4                                # one column tile: a split per 512 k

@@ -534,6 +534,31 @@ def test_gemv_uintx_variants_parity(dt, group, nbits, n, k, B):
         assert np.array_equal(y[b], deq[:, kk]), (b, kk)
 
 
+@pytest.mark.parametrize("sym", [True, False])
+@pytest.mark.parametrize("group,n,k,B", [(128, 64, 512, 1), (32, 136, 1024, 3), (64, 1024, 4096, 8),
+                                          (128, 4096, 2048, 2)])
+def test_gemv_gptq_act_order_parity(sym, group, n, k, B):
+    """GEMV on act-order GPTQ weights: each channel dequantized with its group g_idx[k]."""
+    W = workloads.mxfp4_weight(n, k, seed=550 + n + group)
+    x = workloads.normal_weight(B, k, std=1.0, seed=551 + B)
+    perm = np.random.default_rng(552 + k).permutation(k)
+    q = gwb.quantize(W.to(DEV), "gptq_sym_act" if sym else "gptq_asym_act", group=group,
+                     perm=torch.from_numpy(perm.astype(np.int32)).to(DEV))
+    o = ogq.quantize_act_order(W.float().numpy(), group, sym, perm)
+    deq = ogq.dequantize(o["qweight"], o["scales"], o["qzeros"], group, sym, g_idx=o["g_idx"])
+    xf = x.float().numpy()
+    bound = U32 * (k // 4 + 48) * ogv.abs_gemv(deq, xf)      # float32 sums in k order per wavefront
+    for ydt in (torch.float32, torch.bfloat16):
+        _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ogv.gemv(deq, xf), bound, ydt)
+    xo = torch.zeros(B, k, dtype=torch.bfloat16)
+    cols = [(b * 131 + 7) % k for b in range(B)]
+    for b, kk in enumerate(cols):
+        xo[b, kk] = 1.0
+    y = _np(gwb.gemv(q, xo.to(DEV)))
+    for b, kk in enumerate(cols):
+        assert np.array_equal(y[b], deq[:, kk]), (b, kk)
+
+
 def test_gemv_uintx_config_3072x12288():
     W = workloads.uintx_weight()
     x = workloads.normal_weight(2, 12288, std=1.0, seed=532)
