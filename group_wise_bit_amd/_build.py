@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgwb.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["api.hip", "common.hip", "mxfp4.hip", "gptq.hip", "gptq_act.hip", "uintx.hip", "uintx_bf16.hip", "uintx_f16.hip", "uintx_f32.hip",
-           "uintx_flat.hip", "awq.hip", "fold.hip", "gemv.hip"]
+           "uintx_flat.hip", "awq.hip", "fold.hip", "gemv.hip", "gemm.hip"]
 # The uintx, GPTQ and AWQ arithmetic feeds no NaN to a float op whose result is kept
 # (the one NaN uintx can make, a float16 zero weight times an infinite reciprocal, is
 # decided on the reciprocal's bits first), and non-finite inputs are outside the method;

@@ -73,6 +73,9 @@ _SIGS = {
     "gwb_gemv_workspace": [ctypes.POINTER(QSpec), _I64, _I64, _I64, ctypes.POINTER(_SZ)],
     "gwb_gemv": [ctypes.POINTER(QSpec), ctypes.POINTER(QTensors), _I64, _I64, _P, _I64, _I64, _P, _I32, _I64, _P,
                  _SZ, _P],
+    "gwb_gemm_workspace": [ctypes.POINTER(QSpec), _I64, _I64, _I64, ctypes.POINTER(_SZ)],
+    "gwb_gemm": [ctypes.POINTER(QSpec), ctypes.POINTER(QTensors), _I64, _I64, _P, _I64, _I64, _P, _I32, _I64, _P,
+                 _SZ, _P],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(lib, _name)
@@ -355,6 +358,43 @@ def gemv(q: Quantized, x: torch.Tensor, y_dtype=torch.float32, out: Optional[tor
 def prepare_gemv(q: Quantized, x: torch.Tensor, y: torch.Tensor, workspace: Optional[torch.Tensor]) -> Prepared:
     args, keep = _gemv_args(q, x, y, workspace)
     return Prepared(lib.gwb_gemv, args, (keep, q, x, y, workspace))
+
+
+def gemm_workspace_bytes(q: Quantized, M: int) -> int:
+    sp, b = q.spec(), ctypes.c_size_t()
+    _check(lib.gwb_gemm_workspace(ctypes.byref(sp), q.N, q.K, M, ctypes.byref(b)))
+    return b.value
+
+
+def _gemm_args(q, x, y, workspace):
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != q.K or x.stride(1) != 1 or not x.is_cuda:
+        raise ValueError("x must be a bf16 CUDA tensor [M, K] with unit stride along K")
+    M = x.shape[0]
+    if y.dtype not in _DT or tuple(y.shape) != (M, q.N) or y.stride(1) != 1:
+        raise ValueError("y must be float32 or bf16 [M, N] with unit stride along N")
+    sp, qt = q.spec(), q.qtensors()
+    ws_b = 0 if workspace is None else workspace.numel()
+    return (ctypes.byref(sp), ctypes.byref(qt), q.N, q.K, _ptr(x), M, x.stride(0), _ptr(y), _DT[y.dtype], y.stride(0),
+            _ptr(workspace), ws_b, _stream()), (sp, qt)
+
+
+def gemm(q: Quantized, x: torch.Tensor, y_dtype=torch.float32, out: Optional[torch.Tensor] = None,
+         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x @ dequantize(W)^T on the matrix cores (GPTQ sym/asym or MXFP4); x bf16
+    [M, K]; returns y [M, N] of y_dtype."""
+    if out is None:
+        out = torch.empty(x.shape[0], q.N, dtype=y_dtype, device=x.device)
+    if workspace is None:
+        nb = gemm_workspace_bytes(q, x.shape[0])
+        workspace = _alloc(nb, x.device) if nb else None
+    args, _keep = _gemm_args(q, x, out, workspace)
+    _check(lib.gwb_gemm(*args))
+    return out
+
+
+def prepare_gemm(q: Quantized, x: torch.Tensor, y: torch.Tensor, workspace: Optional[torch.Tensor]) -> Prepared:
+    args, keep = _gemm_args(q, x, y, workspace)
+    return Prepared(lib.gwb_gemm, args, (keep, q, x, y, workspace))
 
 
 def stream_copy(dst: torch.Tensor, src: torch.Tensor) -> None:

@@ -441,6 +441,52 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
   return hip_check("gemv launch");
 }
 
+static int check_gemm(const gwb_qspec* sp, int64_t N, int64_t K, int64_t M) {
+  if (int rc = check_spec(sp, N, K)) return rc;
+  if (sp->format != GWB_GPTQ_SYM && sp->format != GWB_GPTQ_ASYM && !is_mxfp4(sp->format))
+    return fail(GWB_E_UNSUPPORTED, "the GEMM takes GPTQ (sym, asym, groups in index order) and MXFP4 weights");
+  if (N % 8 || K % 128)
+    return fail(GWB_E_UNSUPPORTED, "the GEMM needs N %% 8 == 0 and K %% 128 == 0, got N=%lld K=%lld", (long long)N,
+                (long long)K);
+  if (M < 0 || M > gwb::kGemmMaxRows) return fail(GWB_E_ARG, "M must be 0..%d, got %lld", gwb::kGemmMaxRows, (long long)M);
+  if (M * K >= kMaxElems) return fail(GWB_E_UNSUPPORTED, "M*K = %lld exceeds 2^31 elements", (long long)(M * K));
+  return GWB_OK;
+}
+
+int gwb_gemm_workspace(const gwb_qspec* spec, int64_t N, int64_t K, int64_t M, size_t* bytes) {
+  if (!bytes) return fail(GWB_E_ARG, "bytes is NULL");
+  if (int rc = check_gemm(spec, N, K, M)) return rc;
+  *bytes = gwb::gemm_workspace_bytes(!is_mxfp4(spec->format), spec->group, M, K);
+  return ok();
+}
+
+int gwb_gemm(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K, const void* x, int64_t M,
+             int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  if (int rc = check_gemm(spec, N, K, M)) return rc;
+  if (y_dtype != GWB_F32 && y_dtype != GWB_BF16) return fail(GWB_E_ARG, "unknown y_dtype %d", y_dtype);
+  if (N == 0 || M == 0) return ok();
+  if (K == 0) return fail(GWB_E_SHAPE, "K must be positive");
+  if (!x || !y) return fail(GWB_E_ARG, "x and y are required");
+  if (ldx < K || ldy < N) return fail(GWB_E_ARG, "ldx must be >= K and ldy >= N");
+  if (!aligned16(x) || ldx % 8) return fail(GWB_E_UNSUPPORTED, "x and its row stride must be 16-byte aligned");
+  if (!aligned16(y) || ldy % 8) return fail(GWB_E_UNSUPPORTED, "y must be 16-byte aligned with ldy %% 8 == 0");
+  if (int rc = check_tensors(spec, w)) return rc;
+  if (!aligned16(w->codes) || !aligned16(w->scales))
+    return fail(GWB_E_UNSUPPORTED, "the GEMM needs 16-byte aligned codes and scales");
+  const size_t need = gwb::gemm_workspace_bytes(!is_mxfp4(spec->format), spec->group, M, K);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (need && !aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  if (is_mxfp4(spec->format))
+    gwb::launch_mxfp4_gemm(w->codes, w->scales, N, K, x, M, ldx, y, y_dtype, ldy, st);
+  else
+    gwb::launch_gptq_gemm(spec->format == GWB_GPTQ_SYM, spec->group, w->codes, w->scales, w->zeros, N, K, x, M, ldx,
+                          y, y_dtype, ldy, (float*)workspace, st);
+  return hip_check("gemm launch");
+}
+
 // Host computation of the AWQ scaling table, the same steps and precision as the device
 // table kernels: a' = max(a, 1e-8) in float32, then float64 for an = a' / mean(a'),
 // p = clamp(an**alpha, 1e-2, 1e2) (exact 1, an and sqrt(an) for alpha 0, 1 and 0.5) and

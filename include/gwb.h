@@ -243,6 +243,32 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
              int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
              void* stream);
 
+/* Prefill GEMM on quantized weights: y[m, n] = sum_k x[m, k] * dequant(W)[n, k] for M
+ * rows of activations, the consumer of the stored tensors at prefill and batch sizes
+ * (page export_gptq_cpu.py: vLLM's W4A16 kernels read the GPTQ tensors as written;
+ * page quantize_dflash_mxfp4.py serves its linears as MXFP4). The weights are
+ * dequantized on chip and multiplied on the matrix cores (bf16 operands, float32
+ * accumulation).
+ *   spec, w  GPTQ sym or asym (groups 32, 64, 128 in index order; not act-order) or
+ *            MXFP4, as gwb_quantize wrote it, [N, K]; N % 8 == 0 and K % 128 == 0
+ *            (else GWB_E_UNSUPPORTED); codes and scales 16-byte aligned
+ *   x        device bf16 [M, K], row stride ldx (multiple of 8), 16-byte aligned;
+ *            0 <= M <= 2^24 and M * K < 2^31
+ *   y        device [M, N] of y_dtype (GWB_F32 or GWB_BF16, RNE), row stride ldy
+ *            (multiple of 8), 16-byte aligned
+ *   workspace at least gwb_gemm_workspace bytes: GPTQ the float32 group sums of x
+ *            (K/G x M rounded up to 128), MXFP4 0
+ * MXFP4 weights are exact bf16 operands, so every product is exact and only the
+ * float32 sums round. GPTQ feeds the exact integers 128 + c and applies each group's
+ * scale and zero point to the group's float32 sum: s * (sum x (128 + c) - (128 + z) *
+ * sum x), the group sum of x taken in float64 and rounded once; the offset costs about
+ * log2(143 / |c - z|) bits of the float32 sums relative to a direct sum. Deterministic
+ * for a given shape. Returns GWB_OK without launching when M or N is 0.            */
+int gwb_gemm_workspace(const gwb_qspec* spec, int64_t N, int64_t K, int64_t M, size_t* bytes);
+int gwb_gemm(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K, const void* x, int64_t M,
+             int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+             void* stream);
+
 /* The AWQ scaling table on the host (page quantize_dflash_mxfp4.py, search_scale: the
  * per-alpha s of the search). a: HOST float32 [K] per-channel mean |x|; alphas: HOST
  * array of n_alpha doubles (1..16); s_out: HOST float32 [n_alpha, K]. Steps as in

@@ -263,6 +263,45 @@ def test_gemv_sizes_and_validation():
     assert go(w=fake + 8, wsb=1 << 20) == gwb.E_UNSUPPORTED
 
 
+def test_gemm_sizes_and_validation():
+    P = ctypes.c_void_p
+    fake = 1 << 20
+    qt = gwb.QTensors(fake, fake, fake, None)
+    def ws(fmt, N, K, M, group=None):
+        sp, b = gwb.make_spec(fmt, 4, group), ctypes.c_size_t()
+        rc = lib.gwb_gemm_workspace(ctypes.byref(sp), N, K, M, ctypes.byref(b))
+        return rc, b.value
+    assert ws("gptq_sym", 34816, 5120, 2048) == (gwb.OK, 40 * 2048 * 4)       # group sums, rows padded to 128
+    assert ws("gptq_asym", 4096, 4096, 100, 32) == (gwb.OK, 128 * 128 * 4)
+    assert ws("mxfp4", 34816, 5120, 2048) == (gwb.OK, 0)
+    assert ws("mxfp4_page_ties", 256, 128, 1) == (gwb.OK, 0)
+    assert ws("gptq_sym", 256, 1024, 0) == (gwb.OK, 0)
+    assert ws("gptq_sym", 256, 576, 16, 64)[0] == gwb.E_UNSUPPORTED           # K % 128
+    assert ws("mxfp4", 100, 1024, 16)[0] == gwb.E_UNSUPPORTED                 # N % 8
+    assert ws("uintx", 256, 1024, 16, 64)[0] == gwb.E_UNSUPPORTED
+    assert ws("gptq_sym_act", 256, 1024, 16, 128)[0] == gwb.E_UNSUPPORTED
+    assert ws("gptq_sym", 256, 1024, -1)[0] == gwb.E_ARG
+    assert ws("gptq_sym", 256, 1024, (1 << 24) + 1)[0] == gwb.E_ARG
+    assert ws("gptq_sym", 256, 1 << 20, 1 << 11)[0] == gwb.E_UNSUPPORTED       # M*K = 2^31
+    sp = gwb.make_spec("gptq_sym", 4, 128)
+    def go(x=fake, M=16, ldx=1024, y=fake, ydt=gwb.F32, ldy=256, w=fake, wsb=1 << 20, q=qt):
+        return lib.gwb_gemm(ctypes.byref(sp), ctypes.byref(q), 256, 1024, P(x), M, ldx, P(y), ydt, ldy, P(w), wsb,
+                            None)
+    assert go(ydt=7) == gwb.E_ARG
+    assert go(x=None) == gwb.E_ARG
+    assert go(ldx=1000) == gwb.E_ARG
+    assert go(ldy=200) == gwb.E_ARG
+    assert go(ldx=1028) == gwb.E_UNSUPPORTED
+    assert go(x=fake + 4) == gwb.E_UNSUPPORTED
+    assert go(y=fake + 8) == gwb.E_UNSUPPORTED
+    assert go(ldy=260) == gwb.E_UNSUPPORTED
+    assert go(q=gwb.QTensors(fake + 4, fake, fake, None)) == gwb.E_UNSUPPORTED
+    assert go(w=None, wsb=0) == gwb.E_SIZE                                      # group sums needed
+    assert go(wsb=100) == gwb.E_SIZE
+    assert go(w=fake + 8) == gwb.E_UNSUPPORTED
+    assert go(M=0, x=None, y=None) == gwb.OK                                    # empty: nothing to do
+
+
 def test_page_ties_format_shares_mxfp4_sizes():
     for N, K in ((34816, 5120), (3, 96)):
         a = gwb.query_sizes("mxfp4", N, K, 4, 32)

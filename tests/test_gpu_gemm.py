@@ -1,0 +1,149 @@
+"""GPU parity of the prefill GEMM on quantized weights (gwb_gemm) against the oracle:
+y = x @ dequantize(W)^T with the stored tensors dequantized by the format oracles and the
+product taken in float64 (oracle/gemv.py; the consumer definition of pages
+export_gptq_cpu.py and quantize_dflash_mxfp4.py).
+
+Bounds follow the kernel's arithmetic (u = 2^-24; any summation order inside the matrix
+cores is allowed):
+  MXFP4  every product is exact (bf16 weights and activations), the float32 sum of K
+         products errs by at most u (K + 8) sum_k |x w|;
+  GPTQ   per group T = sum x (128 + c) (exact products, G terms), v = T - (128 + z) Sx
+         with Sx the float64 group sum rounded once, y = sum_g s v; the error is at most
+         u (G + K/G + 8) E with E = 143 sum_k s_g(k) |x_k| (|x (128 + c)| <= 143 |x|).
+A bf16 output adds half an ulp of bf16 (2^-8 relative, generous). One-hot activations
+make every sum a single exact product, so those cases compare bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.gemv as ogv
+import oracle.gptq as ogq
+import oracle.mxfp4 as omx
+from group_wise_bit_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from group_wise_bit_amd import binding as gwb      # must load: no fallback on a GPU machine
+else:  # collected on CPU only to be skipped
+    gwb = None
+
+DEV = "cuda"
+U32 = 2.0 ** -24
+
+
+def _np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def _check(y, ref, bound, ydt):
+    got = _np(y.float()).astype(np.float64)
+    err = np.abs(got - ref)
+    tol = bound + (np.abs(ref) * 2.0 ** -8 if ydt == torch.bfloat16 else 0.0)
+    assert np.all(err <= tol), float(np.max(err / np.maximum(tol, 1e-300)))
+
+
+def _gptq_bound(o, x, group, K):
+    s = np.abs(np.asarray(o["scales"], np.float16).astype(np.float64))      # [K/G, N]
+    sk = np.repeat(s, group, axis=0)                                        # [K, N]
+    return U32 * (group + K // group + 8) * 143.0 * (np.abs(x.astype(np.float64)) @ sk)
+
+
+def _gptq_case(fmt, group, M, n, k, seed):
+    W = workloads.mxfp4_weight(n, k, seed=seed)
+    x = workloads.normal_weight(M, k, std=1.0, seed=seed + 1)
+    q = gwb.quantize(W.to(DEV), fmt, group=group)
+    o = (ogq.quantize_sym if fmt == "gptq_sym" else ogq.quantize_asym)(W.float().numpy(), group)
+    return W, x, q, o
+
+
+@pytest.mark.parametrize("fmt", ["gptq_sym", "gptq_asym"])
+@pytest.mark.parametrize("group", [32, 64, 128])
+@pytest.mark.parametrize("M,n,k", [(1, 256, 128), (37, 264, 640), (130, 520, 1024), (64, 8, 256), (200, 776, 384)])
+def test_gemm_gptq_parity(fmt, group, M, n, k):
+    W, x, q, o = _gptq_case(fmt, group, M, n, k, 600 + M + n + group)
+    xf = x.float().numpy()
+    ref = ogv.gemv(ogv.dequantized(fmt, o, n, k, group=group), xf)
+    bound = _gptq_bound(o, xf, group, k)
+    for ydt in (torch.float32, torch.bfloat16):
+        _check(gwb.gemm(q, x.to(DEV), ydt), ref, bound, ydt)
+
+
+@pytest.mark.parametrize("M,n,k", [(1, 256, 128), (37, 264, 640), (130, 520, 1024), (64, 8, 256), (200, 776, 384),
+                                   (129, 1032, 2048)])
+def test_gemm_mxfp4_parity(M, n, k):
+    W = workloads.mxfp4_weight(n, k, seed=610 + M + n)
+    x = workloads.normal_weight(M, k, std=1.0, seed=611 + M)
+    q = gwb.quantize(W.to(DEV), "mxfp4")
+    packed, e8 = omx.quantize(W.float().numpy())
+    deq = omx.dequantize(packed, e8, k)
+    xf = x.float().numpy()
+    ref = ogv.gemv(deq, xf)
+    bound = U32 * (k + 8) * ogv.abs_gemv(deq, xf)
+    for ydt in (torch.float32, torch.bfloat16):
+        _check(gwb.gemm(q, x.to(DEV), ydt), ref, bound, ydt)
+
+
+@pytest.mark.parametrize("fmt,group", [("gptq_sym", 128), ("gptq_asym", 32), ("gptq_asym", 128), ("mxfp4", None)])
+def test_gemm_one_hot_reads_weights_exactly(fmt, group):
+    """x = 2^p times the identity (K rows, over several row tiles): every output is one
+    exact product, so y^T is the dequantized weight times 2^p, bit for bit."""
+    n, k = 264, 640
+    W = workloads.mxfp4_weight(n, k, seed=620)
+    q = gwb.quantize(W.to(DEV), fmt, group=group)
+    d = _np(gwb.dequantize(q, torch.float32))
+    for p, M in ((0, k), (-3, 100)):
+        x = torch.zeros(M, k, dtype=torch.bfloat16)
+        cols = np.arange(M) * 7 % k                   # distinct columns, not in order
+        x[np.arange(M), cols] = 2.0 ** p
+        y = _np(gwb.gemm(q, x.to(DEV)))
+        assert np.array_equal(y, (d[:, cols] * np.float32(2.0 ** p)).T), (fmt, p, M)
+
+
+def test_gemm_row_strides_and_bf16_output():
+    """x and y as column slices of wider tensors (ldx > K, ldy > N)."""
+    M, n, k = 70, 264, 512
+    W, x, q, o = _gptq_case("gptq_asym", 64, M, n, k, 630)
+    xw = torch.zeros(M, k + 64, dtype=torch.bfloat16, device=DEV)
+    xw[:, 8:8 + k] = x.to(DEV)
+    yw = torch.full((M, n + 24), 7.0, dtype=torch.float32, device=DEV)
+    gwb.gemm(q, xw[:, 8:8 + k], out=yw[:, 8:8 + n])
+    xf = x.float().numpy()
+    ref = ogv.gemv(ogv.dequantized("gptq_asym", o, n, k, group=64), xf)
+    _check(yw[:, 8:8 + n], ref, _gptq_bound(o, xf, 64, k), torch.float32)
+    assert torch.all(yw[:, :8] == 7.0) and torch.all(yw[:, 8 + n:] == 7.0)
+
+
+def test_gemm_empty_rows():
+    W = workloads.mxfp4_weight(64, 256, seed=640)
+    for fmt in ("gptq_sym", "mxfp4"):
+        q = gwb.quantize(W.to(DEV), fmt)
+        y = gwb.gemm(q, torch.zeros(0, 256, dtype=torch.bfloat16, device=DEV))
+        assert tuple(y.shape) == (0, 64)
+
+
+def test_full_gemm_34816x5120_m2048_sampled():
+    """The metric weight [34816, 5120] times 2048 activation rows (GPTQ sym g128, GPTQ
+    asym g128, MXFP4), checked on sampled whole qzeros words of columns for every row."""
+    N_, K_, M_ = 34816, 5120, 2048
+    W = workloads.mxfp4_weight()
+    x = workloads.normal_weight(M_, K_, std=1.0, seed=650)
+    Wd, xd = W.to(DEV), x.to(DEV)
+    cols = np.sort(np.random.default_rng(651).choice(N_ // 8, 6, replace=False)) * 8
+    ns = (cols[:, None] + np.arange(8)[None, :]).reshape(-1)
+    xf = x.float().numpy()
+    for fmt in ("gptq_sym", "gptq_asym"):
+        q = gwb.quantize(Wd, fmt, group=128)
+        y = _np(gwb.gemm(q, xd)).astype(np.float64)
+        o = (ogq.quantize_sym if fmt == "gptq_sym" else ogq.quantize_asym)(W[ns].float().numpy(), 128)
+        deq = ogv.dequantized(fmt, o, len(ns), K_, group=128)
+        _check(torch.from_numpy(y[:, ns]), ogv.gemv(deq, xf), _gptq_bound(o, xf, 128, K_), torch.float32)
+        del q, y
+    qm = gwb.quantize(Wd, "mxfp4")
+    ym = _np(gwb.gemm(qm, xd)).astype(np.float64)
+    packed, e8 = omx.quantize(W[ns].float().numpy())
+    dm = omx.dequantize(packed, e8, K_)
+    _check(torch.from_numpy(ym[:, ns]), ogv.gemv(dm, xf), U32 * (K_ + 8) * ogv.abs_gemv(dm, xf), torch.float32)
