@@ -12,17 +12,23 @@
 // accumulators hold rows 16mt + 4q + r (r < 4) of the 4 adjacent columns nb + 4j .. +3.
 // K runs in stages of 128 through a double-buffered LDS tile of activations.
 //
-// GPTQ: codes c are integers and bf16(128 + c) is exact; (w >> 4i) & 0x000F000F |
-// 0x43004300 gives codes i and i + 4 of a word as such a pair. Per group the matrix
-// cores sum T = sum_k x (128 + c) (exact products); the group adds
-// s * (T - (128 + z) * sum_k x) to the output, with the group sums of x from a pre-pass
-// (float64 sums, rounded once). The activations sit in LDS in the pairs' within-8 order
-// (k = 0, 4, 1, 5, 2, 6, 3, 7). A step covers 32 consecutive k, so a group ends on a
-// step boundary for every group size.
+// GPTQ: codes c are integers and bf16(128 + c) is exact: a byte select and a mask turn
+// codes 2i and 2i+1 of a word into such a pair. Per group the matrix cores sum
+// T = sum_k x (128 + c) (exact products); the group adds s * (T - (128 + z) * sum_k x)
+// to the output, with the group sums of x from a pre-pass (float64 sums, rounded once).
+// A step covers 32 consecutive k, so a group ends on a step boundary for every group
+// size.
 // MXFP4: the scaled FP4 conversion gives the exact bf16 weights (E2M1 times
 // 2^(e8m0 - 127)). A lane's 8-k slot in step s is k0 + 32q + 8s, so over a stage it
 // covers one 32-block of each of its columns: one 16-byte load of codes and one scale
-// byte per column and stage.
+// byte per column and stage. A scale byte of 255 (no E8M0 value; the page's products
+// are inf or NaN) is flagged in the loop and its columns recomputed after it.
+//
+// Activations go from memory straight to LDS (global_load_lds_dwordx4, no registers).
+// The tile holds BM rows of 16 chunks (8 bf16 each) without padding; chunk kc of row r
+// sits at slot 16r + (kc ^ (r & 15)), so the 16 rows one MFMA operand read touches fall
+// in 16 different bank groups. Rows past M and columns past N load clamped (valid)
+// data whose results are not stored.
 #include "kernels.hpp"
 #include "mxfp4_math.hpp"
 
@@ -33,7 +39,6 @@ typedef float gm_f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGmBN = 256;            // columns per block
 constexpr int kGmBK = 128;            // k per stage
-constexpr int kGmLd = kGmBK + 8;      // LDS row stride of the activation tile (bf16)
 constexpr int kGmSumMax = 4 * 128;    // group sums of one stage: up to 4 groups x BM rows
 
 __device__ __forceinline__ gm_f32x4_t mfma_bf16(U4 a, U4 b, gm_f32x4_t c) {
@@ -53,29 +58,29 @@ __device__ __forceinline__ void gemm_tile(int gx, int gy, int& bx, int& by) {
   by = r / rows;
 }
 
-// Block-cooperative copy of the activation tile rows m0 .. m0+BM-1, k0 .. k0+127:
-// chunk c = thread + 256 i is row c / 16, 8-k slot c % 16 (rows past M read as 0).
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Block-cooperative fetch of the activation tile rows m0 .. m0+BM-1, k0 .. k0+127 into
+// LDS: wavefront w's i-th instruction fills slots (4i + w) * 64 .. +63, one per lane.
 template <int MT>
-__device__ __forceinline__ void a_load(const uint16_t* __restrict__ x, int64_t ldx, int M, int m0, int k0,
-                                       U4 (&v)[MT]) {
+__device__ __forceinline__ void a_fetch(const uint16_t* __restrict__ x, int64_t ldx, int M, int m0, int k0,
+                                        uint16_t* lds) {
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    const int c = (int)threadIdx.x + 256 * i, m = m0 + (c >> 4);
-    v[i] = m < M ? ld16(x + (int64_t)m * ldx + k0 + 8 * (c & 15)) : U4{0u, 0u, 0u, 0u};
+    const int p = (4 * i + wv) * 64 + lane, r = p >> 4, kc = (p & 15) ^ (r & 15);
+    const uint16_t* src = x + (int64_t)min(m0 + r, M - 1) * ldx + k0 + 8 * kc;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds + (4 * i + wv) * 512), 16, 0, 0);
   }
 }
-// PAIRS: store each 8-k slot as (x0, x4), (x1, x5), (x2, x6), (x3, x7).
-template <int MT, bool PAIRS>
-__device__ __forceinline__ void a_store(uint16_t* lds, const U4 (&v)[MT]) {
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int c = (int)threadIdx.x + 256 * i;
-    U4 u = v[i];
-    if constexpr (PAIRS)
-      u = U4{__builtin_amdgcn_perm(u.z, u.x, 0x05040100u), __builtin_amdgcn_perm(u.z, u.x, 0x07060302u),
-             __builtin_amdgcn_perm(u.w, u.y, 0x05040100u), __builtin_amdgcn_perm(u.w, u.y, 0x07060302u)};
-    st16(lds + (c >> 4) * kGmLd + 8 * (c & 15), u);
-  }
+// Element offset of the lane's operand chunk kc in rows j, 16 + j, ... (row j of each tile).
+__device__ __forceinline__ int a_slot(int j, int kc) { return (16 * j + (kc ^ j)) * 8; }
+
+// Wait for this wavefront's outstanding memory loads (the LDS fills included), then
+// for the whole block.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  __syncthreads();
 }
 
 // Rows 16mt + 4q + r of the lane's 4 columns nl .. nl+3.
@@ -125,48 +130,57 @@ __global__ __launch_bounds__(256) void gemm_group_sums_kernel(const uint16_t* __
 }
 
 // ------------------------------------------------------------------ GPTQ
+// Codes 2i and 2i+1 of a word as bf16(128 + c) values of one dword: byte i of w and of
+// w >> 4 into bytes 0 and 2, low nibbles kept, exponent bits of 128 added.
+__device__ __forceinline__ U4 gptq_pairs(uint32_t w) {
+  const uint32_t h = w >> 4, m = 0x000F000Fu, e = 0x43004300u;
+  return U4{(__builtin_amdgcn_perm(h, w, 0x0C040C00u) & m) | e, (__builtin_amdgcn_perm(h, w, 0x0C050C01u) & m) | e,
+            (__builtin_amdgcn_perm(h, w, 0x0C060C02u) & m) | e, (__builtin_amdgcn_perm(h, w, 0x0C070C03u) & m) | e};
+}
+
 template <bool SYM, int G, int MT, typename TY>
 __global__ __launch_bounds__(256, 1) void gptq_gemm_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int M, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ sc, const uint32_t* __restrict__ qz, int N, int K, const float* __restrict__ gsum,
     int Mp, TY* __restrict__ y, int64_t ldy, int gx, int gy) {
   constexpr int BM = 16 * MT, SPG = G / 32, NGS = kGmBK / G;   // steps per group, groups per stage
-  constexpr int SUMS = BM * NGS / 4;                            // float4 chunks of group sums per stage
+  constexpr int SUMS = BM * NGS / 4;                            // 16-byte chunks of group sums per stage
   static_assert(SUMS <= 256 && BM * NGS <= kGmSumMax, "group sums of a stage fit one chunk per thread");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kGmLd];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 128];
   __shared__ __attribute__((aligned(16))) float Ss[2][NGS * BM];
 
   int bx, by;
   gemm_tile(gx, gy, bx, by);
   const int lane = threadIdx.x & 63, j = lane & 15, q = lane >> 4;
-  const int m0 = bx * BM, nl = by * kGmBN + (int)(threadIdx.x >> 6) * 64 + 4 * j;
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int m0 = bx * BM, nl = by * kGmBN + wv * 64 + 4 * j;
   const bool nok = nl < N;
-  const int tid = threadIdx.x;
+  const int nc = min(nl, N - 4);                     // clamped column for loads
+  const int zsh = 4 * (nc & 7);
+  const uint32_t* qp = qw + (int64_t)q * N + nc;     // + (k0/8 + 4s) N per step
+  int aoff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aoff[s] = a_slot(j, 4 * s + q);
 
-  // stage prefetch: activations, group sums, code words, scales and zero points
-  U4 av[MT], wv[4];
-  float4 sv = float4{0.f, 0.f, 0.f, 0.f};
+  U4 wv4[4];
   uint2 scv[NGS];
   uint32_t zv[NGS];
-  auto fetch = [&](int k0) {
-    a_load<MT>(x, ldx, M, m0, k0, av);
-    if (tid < SUMS) {
-      const int gi = tid / (BM / 4), rr = 4 * (tid % (BM / 4));
-      sv = *reinterpret_cast<const float4*>(gsum + (int64_t)(k0 / G + gi) * Mp + m0 + rr);
+  auto fetch = [&](int k0, int buf) {
+    a_fetch<MT>(x, ldx, M, m0, k0, As[buf]);
+    const int p = wv * 64 + lane;
+    if (p < SUMS) {
+      const int gi = p / (BM / 4), rr = 4 * (p % (BM / 4));
+      __builtin_amdgcn_global_load_lds(gsum + (int64_t)(k0 / G + gi) * Mp + m0 + rr,
+                                       (lds_void_t*)(&Ss[buf][0] + wv * 256), 16, 0, 0);
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      wv[s] = nok ? ld16(qw + (int64_t)(k0 / 8 + 4 * s + q) * N + nl) : U4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < 4; ++s) wv4[s] = ld16(qp + (int64_t)(k0 / 8 + 4 * s) * N);
 #pragma unroll
     for (int gi = 0; gi < NGS; ++gi) {
       const int g = k0 / G + gi;
-      scv[gi] = nok ? *reinterpret_cast<const uint2*>(sc + (int64_t)g * N + nl) : uint2{0u, 0u};
-      if constexpr (!SYM) zv[gi] = nok ? qz[(int64_t)g * (N / 8) + nl / 8] : 0u;
+      scv[gi] = *reinterpret_cast<const uint2*>(sc + (int64_t)g * N + nc);
+      if constexpr (!SYM) zv[gi] = qz[(int64_t)g * (N / 8) + nc / 8];
     }
-  };
-  auto commit = [&](int buf) {
-    a_store<MT, true>(As[buf], av);
-    if (tid < SUMS) *reinterpret_cast<float4*>(&Ss[buf][4 * tid]) = sv;
   };
 
   gm_f32x4_t acc[MT][4], tmp[MT][4];
@@ -175,33 +189,27 @@ __global__ __launch_bounds__(256, 1) void gptq_gemm_kernel(
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[mt][t] = gm_f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  fetch(0);
-  commit(0);
-  __syncthreads();
+  fetch(0, 0);
+  stage_barrier();
   const int nst = K / kGmBK;
   for (int st = 0; st < nst; ++st) {
     const int buf = st & 1;
-    const uint16_t* A = As[buf] + j * kGmLd + 8 * q;
+    const uint16_t* A = As[buf];
     U4 w[4];
     uint2 scl[NGS];
     uint32_t zl[NGS];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) w[s] = wv[s];
+    for (int s = 0; s < 4; ++s) w[s] = wv4[s];
 #pragma unroll
     for (int gi = 0; gi < NGS; ++gi) {
       scl[gi] = scv[gi];
       if constexpr (!SYM) zl[gi] = zv[gi];
     }
-    if (st + 1 < nst) fetch((st + 1) * kGmBK);
+    if (st + 1 < nst) fetch((st + 1) * kGmBK, buf ^ 1);
 
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint32_t wd[4] = {w[s].x, w[s].y, w[s].z, w[s].w};
-      U4 b[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        b[t] = U4{(wd[t] & 0x000F000Fu) | 0x43004300u, ((wd[t] >> 4) & 0x000F000Fu) | 0x43004300u,
-                  ((wd[t] >> 8) & 0x000F000Fu) | 0x43004300u, ((wd[t] >> 12) & 0x000F000Fu) | 0x43004300u};
+      const U4 b[4] = {gptq_pairs(w[s].x), gptq_pairs(w[s].y), gptq_pairs(w[s].z), gptq_pairs(w[s].w)};
       if (s % SPG == 0) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(256, 1) void gptq_gemm_kernel(
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const U4 a = *reinterpret_cast<const U4*>(A + 16 * mt * kGmLd + 32 * s);
+        const U4 a = *reinterpret_cast<const U4*>(A + aoff[s] + 16 * mt * 128);
 #pragma unroll
         for (int t = 0; t < 4; ++t) tmp[mt][t] = mfma_bf16(a, b[t], tmp[mt][t]);
       }
@@ -222,7 +230,7 @@ __global__ __launch_bounds__(256, 1) void gptq_gemm_kernel(
         for (int t = 0; t < 4; ++t) {
           sf[t] = (float)__builtin_bit_cast(_Float16, (uint16_t)sb[t]);
           if constexpr (SYM) cz[t] = -136.0f;
-          else cz[t] = -(float)(128u + ((zl[gi] >> (4 * ((nl & 7) + t))) & 0xFu));
+          else cz[t] = -(float)(128u + ((zl[gi] >> (zsh + 4 * t)) & 0xFu));
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -236,8 +244,7 @@ __global__ __launch_bounds__(256, 1) void gptq_gemm_kernel(
         }
       }
     }
-    if (st + 1 < nst) commit(buf ^ 1);
-    __syncthreads();
+    stage_barrier();
   }
   gemm_store<MT, TY>(acc, y, ldy, M, m0, q, nl, nok);
 }
@@ -249,23 +256,30 @@ __global__ __launch_bounds__(256, 1) void mxfp4_gemm_kernel(const uint16_t* __re
                                                            const uint8_t* __restrict__ e8m0, int N, int K,
                                                            TY* __restrict__ y, int64_t ldy, int gx, int gy) {
   constexpr int BM = 16 * MT;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kGmLd];
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 128];
 
   int bx, by;
   gemm_tile(gx, gy, bx, by);
   const int lane = threadIdx.x & 63, j = lane & 15, q = lane >> 4;
-  const int m0 = bx * BM, nl = by * kGmBN + (int)(threadIdx.x >> 6) * 64 + 4 * j;
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int m0 = bx * BM, nl = by * kGmBN + wv * 64 + 4 * j;
   const bool nok = nl < N;
-  const int64_t rowb = K / 2, rows = K / 32;
+  const int nc = min(nl, N - 4);
+  const int64_t rowb = K / 2, rowe = K / 32;
+  const uint8_t* cp = codes + (int64_t)nc * rowb + 16 * q;   // + k0/2 per stage, + t rowb per column
+  const uint8_t* ep = e8m0 + (int64_t)nc * rowe + q;          // + k0/32 per stage, + t rowe per column
+  int aoff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aoff[s] = a_slot(j, 4 * q + s);
 
-  U4 av[MT], wv[4];
+  U4 wv4[4];
   uint32_t ev[4];
-  auto fetch = [&](int k0) {
-    a_load<MT>(x, ldx, M, m0, k0, av);
+  auto fetch = [&](int k0, int buf) {
+    a_fetch<MT>(x, ldx, M, m0, k0, As[buf]);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      wv[t] = nok ? ld16(codes + (int64_t)(nl + t) * rowb + k0 / 2 + 16 * q) : U4{0u, 0u, 0u, 0u};
-      ev[t] = nok ? (uint32_t)e8m0[(int64_t)(nl + t) * rows + k0 / 32 + q] : 127u;
+      wv4[t] = ld16(cp + t * rowb + k0 / 2);
+      ev[t] = ep[t * rowe + k0 / 32];
     }
   };
 
@@ -275,37 +289,73 @@ __global__ __launch_bounds__(256, 1) void mxfp4_gemm_kernel(const uint16_t* __re
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[mt][t] = gm_f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  fetch(0);
-  a_store<MT, false>(As[0], av);
-  __syncthreads();
+  fetch(0, 0);
+  stage_barrier();
   const int nst = K / kGmBK;
+  uint32_t nanc = 0;   // bit t: column nc + t has a block with scale byte 255
   for (int st = 0; st < nst; ++st) {
-    const uint16_t* A = As[st & 1] + j * kGmLd + 32 * q;
+    const int buf = st & 1;
     U4 w[4];
     uint32_t e[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      w[t] = wv[t];
+      w[t] = wv4[t];
       e[t] = ev[t];
     }
-    if (st + 1 < nst) fetch((st + 1) * kGmBK);
+    if (st + 1 < nst) fetch((st + 1) * kGmBK, buf ^ 1);
+    float scl[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      scl[t] = mx_scale_operand(e[t]);
+      nanc |= (uint32_t)(e[t] == 255u) << t;
+    }
+    const uint16_t* A = As[buf];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       U4 b[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const uint32_t wd = s == 0 ? w[t].x : s == 1 ? w[t].y : s == 2 ? w[t].z : w[t].w;
-        b[t] = mx_unpack8_bf16(wd, e[t]);
+        b[t] = U4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl[t], 0)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl[t], 1)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl[t], 2)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl[t], 3))};
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const U4 a = *reinterpret_cast<const U4*>(A + 16 * mt * kGmLd + 8 * s);
+        const U4 a = *reinterpret_cast<const U4*>(A + aoff[s] + 16 * mt * 128);
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[mt][t] = mfma_bf16(a, b[t], acc[mt][t]);
       }
     }
-    if (st + 1 < nst) a_store<MT, false>(As[(st & 1) ^ 1], av);
-    __syncthreads();
+    stage_barrier();
+  }
+  // Columns with a scale byte of 255 (no E8M0 value): the loop's products there are
+  // meaningless, and the page's weights +-E2M1 * 2^128 are inf or NaN, so the output is
+  // the float32 sum over those blocks alone (inf or NaN; adding the finite rest cannot
+  // change it). Wave-uniform and rare; a plain loop over K.
+  if (__any(nanc != 0u)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (!((nanc >> t) & 1u)) continue;
+      const uint8_t* crow = codes + (int64_t)(nc + t) * rowb;
+      const uint8_t* erow = e8m0 + (int64_t)(nc + t) * rowe;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint16_t* xr = x + (int64_t)min(m0 + 16 * mt + 4 * q + r, M - 1) * ldx;
+          float sum = 0.f;
+          for (int blk = 0; blk < K / 32; ++blk) {
+            if (erow[blk] != 255u) continue;
+            for (int k = 32 * blk; k < 32 * blk + 32; ++k) {
+              const uint32_t c = (crow[k >> 1] >> (4 * (k & 1))) & 0xFu;
+              sum += bf16_to_f32(xr[k]) * mx_value_nan_scale(c);
+            }
+          }
+          acc[mt][t][r] = sum;
+        }
+    }
   }
   gemm_store<MT, TY>(acc, y, ldy, M, m0, q, nl, nok);
 }

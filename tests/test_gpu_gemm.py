@@ -103,6 +103,31 @@ def test_gemm_one_hot_reads_weights_exactly(fmt, group):
         assert np.array_equal(y, (d[:, cols] * np.float32(2.0 ** p)).T), (fmt, p, M)
 
 
+def test_gemm_mxfp4_scale_byte_255_columns():
+    """Scale byte 255 has no E8M0 value: the page's weights +-E2M1 * 2^128 are inf (NaN
+    for a zero code), so those columns' outputs are inf or NaN as in the float64
+    product; every other column keeps the ordinary bound."""
+    M, n, k = 70, 264, 640
+    W = workloads.mxfp4_weight(n, k, seed=660)
+    x = workloads.normal_weight(M, k, std=1.0, seed=661)
+    q = gwb.quantize(W.to(DEV), "mxfp4")
+    for row, blk in ((5, 3), (100, 0), (263, 19), (64, 7)):
+        q["e8m0"][row, blk] = 255
+    packed, e8 = _np(q["packed"]), _np(q["e8m0"])
+    deq = omx.dequantize(packed, e8, k)
+    xf = x.float().numpy()
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = ogv.gemv(deq, xf)
+    y = _np(gwb.gemm(q, x.to(DEV))).astype(np.float64)
+    bad = ~np.isfinite(ref)
+    assert bad[:, [5, 100, 263, 64]].all() and not bad[:, [0, 6, 99, 262]].any()
+    assert np.array_equal(np.isnan(y), np.isnan(ref))
+    assert np.array_equal(np.isposinf(y), np.isposinf(ref)) and np.array_equal(np.isneginf(y), np.isneginf(ref))
+    fin = np.isfinite(deq).all(axis=1)
+    bound = U32 * (k + 8) * ogv.abs_gemv(deq[fin], xf)
+    _check(torch.from_numpy(y[:, fin]), ref[:, fin], bound, torch.float32)
+
+
 def test_gemm_row_strides_and_bf16_output():
     """x and y as column slices of wider tensors (ldx > K, ldy > N)."""
     M, n, k = 70, 264, 512
