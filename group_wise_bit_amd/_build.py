@@ -65,7 +65,9 @@ def build(verbose: bool = True) -> str:
     if failed:
         raise RuntimeError("hipcc failed for " + ", ".join(r[0] for r in failed))
     tmp = LIB + ".tmp"
-    rc, out = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[r[1] for r in results]])
+    # --no-undefined: a kernel whose host-side launch stub went missing fails here, not at load
+    rc, out = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp,
+                    *[r[1] for r in results]])
     if rc:
         raise RuntimeError("link failed:\n" + out)
     os.replace(tmp, LIB)

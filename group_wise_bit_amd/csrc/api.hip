@@ -471,6 +471,7 @@ int gwb_gemm(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
   if (ldx < K || ldy < N) return fail(GWB_E_ARG, "ldx must be >= K and ldy >= N");
   if (!aligned16(x) || ldx % 8) return fail(GWB_E_UNSUPPORTED, "x and its row stride must be 16-byte aligned");
   if (!aligned16(y) || ldy % 8) return fail(GWB_E_UNSUPPORTED, "y must be 16-byte aligned with ldy %% 8 == 0");
+  if (M * ldx >= kMaxElems) return fail(GWB_E_UNSUPPORTED, "M*ldx = %lld exceeds 2^31 elements", (long long)(M * ldx));
   if (int rc = check_tensors(spec, w)) return rc;
   if (!aligned16(w->codes) || !aligned16(w->scales))
     return fail(GWB_E_UNSUPPORTED, "the GEMM needs 16-byte aligned codes and scales");

@@ -26,9 +26,11 @@
 //
 // Activations go from memory straight to LDS (global_load_lds_dwordx4, no registers).
 // The tile holds BM rows of 16 chunks (8 bf16 each) without padding; chunk kc of row r
-// sits at slot 16r + (kc ^ (r & 15)), so the 16 rows one MFMA operand read touches fall
-// in 16 different bank groups. Rows past M and columns past N load clamped (valid)
-// data whose results are not stored.
+// sits at slot 16r + (kc ^ swz(r & 15)). An operand read has 16 rows per 8-k chunk
+// index and, across lane groups, chunk indices 4 apart (MXFP4) or 1 apart (GPTQ); the
+// swizzle keeps the 32 lanes a read serves per pass on distinct banks in both cases
+// (the plain r & 15 left MXFP4 reads 2-way conflicted). Rows past M and columns past N
+// load clamped (valid) data whose results are not stored.
 #include "kernels.hpp"
 #include "mxfp4_math.hpp"
 
@@ -60,21 +62,34 @@ __device__ __forceinline__ void gemm_tile(int gx, int gy, int& bx, int& by) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Block-cooperative fetch of the activation tile rows m0 .. m0+BM-1, k0 .. k0+127 into
-// LDS: wavefront w's i-th instruction fills slots (4i + w) * 64 .. +63, one per lane.
+// XOR applied to the chunk index of tile row r (r & 15 = j): a permutation of 0..15 in
+// which rows of equal parity never differ by 1 or 4.
+__device__ __forceinline__ int swz(int j) {
+  const int i = j >> 1;
+  return (((i & 4) << 1) | (i & 2) | ((i & 1) * 5)) ^ (j & 1);
+}
+
+// The activation tile's source offsets for this lane (elements from x + k0): wavefront
+// w's i-th fill instruction writes slots (4i + w) * 64 .. +63, one per lane, i.e. row
+// 16i + 4w + lane/16 at swizzled slot lane % 16.
 template <int MT>
-__device__ __forceinline__ void a_fetch(const uint16_t* __restrict__ x, int64_t ldx, int M, int m0, int k0,
-                                        uint16_t* lds) {
-  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
+__device__ __forceinline__ void a_offsets(int64_t ldx, int M, int m0, int wv, int lane, uint32_t (&off)[MT]) {
+  const int rr = 4 * wv + (lane >> 4), kc = (lane & 15) ^ swz(rr);
+#pragma unroll
+  for (int i = 0; i < MT; ++i) off[i] = (uint32_t)((int64_t)min(m0 + 16 * i + rr, M - 1) * ldx + 8 * kc);
+}
+template <int MT>
+__device__ __forceinline__ void a_fetch(const uint32_t (&off)[MT], const uint16_t* xk, uint16_t* lds, int wv) {
 #pragma unroll
   for (int i = 0; i < MT; ++i) {
-    const int p = (4 * i + wv) * 64 + lane, r = p >> 4, kc = (p & 15) ^ (r & 15);
-    const uint16_t* src = x + (int64_t)min(m0 + r, M - 1) * ldx + k0 + 8 * kc;
+    // (a named pointer: the builtin given the sum directly fails to instantiate in
+    // clang's host pass, which then silently drops the kernel's launch stub)
+    const uint16_t* src = xk + off[i];
     __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds + (4 * i + wv) * 512), 16, 0, 0);
   }
 }
-// Element offset of the lane's operand chunk kc in rows j, 16 + j, ... (row j of each tile).
-__device__ __forceinline__ int a_slot(int j, int kc) { return (16 * j + (kc ^ j)) * 8; }
+// Element offset of the lane's operand chunk kc in row j of the first 16-row tile.
+__device__ __forceinline__ int a_slot(int j, int kc) { return (16 * j + (kc ^ swz(j))) * 8; }
 
 // Wait for this wavefront's outstanding memory loads (the LDS fills included), then
 // for the whole block.
@@ -132,8 +147,10 @@ __global__ __launch_bounds__(256) void gemm_group_sums_kernel(const uint16_t* __
 // ------------------------------------------------------------------ GPTQ
 // Codes 2i and 2i+1 of a word as bf16(128 + c) values of one dword: byte i of w and of
 // w >> 4 into bytes 0 and 2, low nibbles kept, exponent bits of 128 added.
-__device__ __forceinline__ U4 gptq_pairs(uint32_t w) {
-  const uint32_t h = w >> 4, m = 0x000F000Fu, e = 0x43004300u;
+// e is held in a register by the caller: with both constants as operands the compiler
+// cannot form one v_and_or_b32 (one scalar operand per instruction) and splits it.
+__device__ __forceinline__ U4 gptq_pairs(uint32_t w, uint32_t e) {
+  const uint32_t h = w >> 4, m = 0x000F000Fu;
   return U4{(__builtin_amdgcn_perm(h, w, 0x0C040C00u) & m) | e, (__builtin_amdgcn_perm(h, w, 0x0C050C01u) & m) | e,
             (__builtin_amdgcn_perm(h, w, 0x0C060C02u) & m) | e, (__builtin_amdgcn_perm(h, w, 0x0C070C03u) & m) | e};
 }
@@ -146,8 +163,11 @@ __global__ __launch_bounds__(256, 1) void gptq_gemm_kernel(
   constexpr int BM = 16 * MT, SPG = G / 32, NGS = kGmBK / G;   // steps per group, groups per stage
   constexpr int SUMS = BM * NGS / 4;                            // 16-byte chunks of group sums per stage
   static_assert(SUMS <= 256 && BM * NGS <= kGmSumMax, "group sums of a stage fit one chunk per thread");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 128];
-  __shared__ __attribute__((aligned(16))) float Ss[2][NGS * BM];
+  // one LDS object: activation tiles, then group sums (with two objects the compiler
+  // waits for every outstanding load before the stage's first LDS read)
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BM * 128 + 2 * 2 * NGS * BM];
+  uint16_t(*As)[BM * 128] = reinterpret_cast<uint16_t(*)[BM * 128]>(smem);
+  float(*Ss)[NGS * BM] = reinterpret_cast<float(*)[NGS * BM]>(smem + 2 * BM * 128);
 
   int bx, by;
   gemm_tile(gx, gy, bx, by);
@@ -157,29 +177,37 @@ __global__ __launch_bounds__(256, 1) void gptq_gemm_kernel(
   const bool nok = nl < N;
   const int nc = min(nl, N - 4);                     // clamped column for loads
   const int zsh = 4 * (nc & 7);
-  const uint32_t* qp = qw + (int64_t)q * N + nc;     // + (k0/8 + 4s) N per step
+  const uint32_t qoff = (uint32_t)(q * N + nc);      // qweight words from row k0/8 + 4s
+  const int p = wv * 64 + lane;                      // group-sum chunk of this thread (p < SUMS)
+  const uint32_t soff = (uint32_t)((p / (BM / 4)) * Mp + m0 + 4 * (p % (BM / 4)));   // from row k0/G
   int aoff[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) aoff[s] = a_slot(j, 4 * s + q);
+  uint32_t aof[MT];
+  a_offsets<MT>(ldx, M, m0, wv, lane, aof);
+  uint32_t pe = 0x43004300u;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(pe));   // keep the constant in a vector register
+#endif
 
   U4 wv4[4];
   uint2 scv[NGS];
   uint32_t zv[NGS];
+  // Each stage reads its group sums from LDS before it issues the next fills: an LDS
+  // access behind a pending fill makes the compiler wait for all outstanding loads.
   auto fetch = [&](int k0, int buf) {
-    a_fetch<MT>(x, ldx, M, m0, k0, As[buf]);
-    const int p = wv * 64 + lane;
+    a_fetch<MT>(aof, x + k0, As[buf], wv);
     if (p < SUMS) {
-      const int gi = p / (BM / 4), rr = 4 * (p % (BM / 4));
-      __builtin_amdgcn_global_load_lds(gsum + (int64_t)(k0 / G + gi) * Mp + m0 + rr,
-                                       (lds_void_t*)(&Ss[buf][0] + wv * 256), 16, 0, 0);
+      const float* src = gsum + (int64_t)(k0 / G) * Mp + soff;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(&Ss[buf][0] + wv * 256), 16, 0, 0);
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) wv4[s] = ld16(qp + (int64_t)(k0 / 8 + 4 * s) * N);
+    for (int s = 0; s < 4; ++s) wv4[s] = ld16(qw + (int64_t)(k0 / 8 + 4 * s) * N + qoff);
 #pragma unroll
     for (int gi = 0; gi < NGS; ++gi) {
-      const int g = k0 / G + gi;
-      scv[gi] = *reinterpret_cast<const uint2*>(sc + (int64_t)g * N + nc);
-      if constexpr (!SYM) zv[gi] = qz[(int64_t)g * (N / 8) + nc / 8];
+      const int64_t g = k0 / G + gi;
+      scv[gi] = *reinterpret_cast<const uint2*>(sc + g * N + nc);
+      if constexpr (!SYM) zv[gi] = qz[g * (N / 8) + nc / 8];
     }
   };
 
@@ -195,6 +223,11 @@ __global__ __launch_bounds__(256, 1) void gptq_gemm_kernel(
   for (int st = 0; st < nst; ++st) {
     const int buf = st & 1;
     const uint16_t* A = As[buf];
+    float4 sx[NGS][MT];
+#pragma unroll
+    for (int gi = 0; gi < NGS; ++gi)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) sx[gi][mt] = *reinterpret_cast<const float4*>(&Ss[buf][gi * BM + 16 * mt + 4 * q]);
     U4 w[4];
     uint2 scl[NGS];
     uint32_t zl[NGS];
@@ -209,7 +242,8 @@ __global__ __launch_bounds__(256, 1) void gptq_gemm_kernel(
 
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const U4 b[4] = {gptq_pairs(w[s].x), gptq_pairs(w[s].y), gptq_pairs(w[s].z), gptq_pairs(w[s].w)};
+      const U4 b[4] = {gptq_pairs(w[s].x, pe), gptq_pairs(w[s].y, pe), gptq_pairs(w[s].z, pe),
+                       gptq_pairs(w[s].w, pe)};
       if (s % SPG == 0) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
@@ -234,8 +268,7 @@ __global__ __launch_bounds__(256, 1) void gptq_gemm_kernel(
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const float4 sx = *reinterpret_cast<const float4*>(&Ss[buf][gi * BM + 16 * mt + 4 * q]);
-          const float sxa[4] = {sx.x, sx.y, sx.z, sx.w};
+          const float sxa[4] = {sx[gi][mt].x, sx[gi][mt].y, sx[gi][mt].z, sx[gi][mt].w};
 #pragma unroll
           for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -266,20 +299,22 @@ __global__ __launch_bounds__(256, 1) void mxfp4_gemm_kernel(const uint16_t* __re
   const bool nok = nl < N;
   const int nc = min(nl, N - 4);
   const int64_t rowb = K / 2, rowe = K / 32;
-  const uint8_t* cp = codes + (int64_t)nc * rowb + 16 * q;   // + k0/2 per stage, + t rowb per column
-  const uint8_t* ep = e8m0 + (int64_t)nc * rowe + q;          // + k0/32 per stage, + t rowe per column
+  const uint32_t coff = (uint32_t)(nc * rowb + 16 * q);   // codes of column nc from byte k0/2 (+ t rowb)
+  const uint32_t eoff = (uint32_t)(nc * rowe + q);        // scale bytes from k0/32 (+ t rowe)
   int aoff[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) aoff[s] = a_slot(j, 4 * q + s);
+  uint32_t aof[MT];
+  a_offsets<MT>(ldx, M, m0, wv, lane, aof);
 
   U4 wv4[4];
   uint32_t ev[4];
   auto fetch = [&](int k0, int buf) {
-    a_fetch<MT>(x, ldx, M, m0, k0, As[buf]);
+    a_fetch<MT>(aof, x + k0, As[buf], wv);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      wv4[t] = ld16(cp + t * rowb + k0 / 2);
-      ev[t] = ep[t * rowe + k0 / 32];
+      wv4[t] = ld16(codes + (k0 / 2 + t * rowb) + coff);
+      ev[t] = e8m0[(k0 / 32 + t * rowe) + eoff];
     }
   };
 

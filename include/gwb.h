@@ -253,7 +253,7 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
  *            MXFP4, as gwb_quantize wrote it, [N, K]; N % 8 == 0 and K % 128 == 0
  *            (else GWB_E_UNSUPPORTED); codes and scales 16-byte aligned
  *   x        device bf16 [M, K], row stride ldx (multiple of 8), 16-byte aligned;
- *            0 <= M <= 2^24 and M * K < 2^31
+ *            0 <= M <= 2^24 and M * ldx < 2^31
  *   y        device [M, N] of y_dtype (GWB_F32 or GWB_BF16, RNE), row stride ldy
  *            (multiple of 8), 16-byte aligned
  *   workspace at least gwb_gemm_workspace bytes: GPTQ the float32 group sums of x
