@@ -156,7 +156,7 @@ __device__ __forceinline__ U4 gptq_pairs(uint32_t w, uint32_t e) {
 }
 
 template <bool SYM, int G, int MT, typename TY>
-__global__ __launch_bounds__(256, 1) void gptq_gemm_kernel(
+__global__ __launch_bounds__(256, MT == 4 && G == 128 ? 2 : 1) void gptq_gemm_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int M, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ sc, const uint32_t* __restrict__ qz, int N, int K, const float* __restrict__ gsum,
     int Mp, TY* __restrict__ y, int64_t ldy, int gx, int gy) {
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256, 1) void gptq_gemm_kernel(
 
 // ------------------------------------------------------------------ MXFP4
 template <int MT, typename TY>
-__global__ __launch_bounds__(256, 1) void mxfp4_gemm_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
+__global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
                                                            const uint8_t* __restrict__ codes,
                                                            const uint8_t* __restrict__ e8m0, int N, int K,
                                                            TY* __restrict__ y, int64_t ldy, int gx, int gy) {
@@ -396,7 +396,11 @@ __global__ __launch_bounds__(256, 1) void mxfp4_gemm_kernel(const uint16_t* __re
 }
 
 // ------------------------------------------------------------------ launchers
-static int gemm_mt(int64_t M) { return M <= 64 ? 4 : 8; }
+// Block rows: two wavefronts per SIMD (at most 256 registers each) hide each other's
+// waits and GPTQ's per-group VALU work; that holds for 128-row MXFP4 blocks and 64-row
+// GPTQ blocks with 128-groups (measured at M = 2048: MXFP4 1150 vs 920 TFLOP/s for one
+// wavefront per SIMD, GPTQ 930-970 vs 640). Smaller GPTQ groups keep 64 rows at one
+// wavefront per SIMD (their per-group state does not fit 256 registers).
 
 size_t gemm_workspace_bytes(bool gptq, int group, int64_t M, int64_t K) {
   if (!gptq) return 0;
@@ -412,22 +416,11 @@ static void gptq_gemm_go(const void* x, int64_t ldx, int M, const void* qw, cons
                      M, (const uint32_t*)qw, (const uint16_t*)sc, (const uint32_t*)qz, N, K, gs, Mp, (TY*)y, ldy,
                      gx, gy);
 }
-// 128-row blocks only with one group per stage: with more, the per-group work of
-// 128 rows no longer fits the register file.
-template <bool SYM, int G, typename TY>
-static void gptq_gemm_mt(int mt, const void* x, int64_t ldx, int M, const void* qw, const void* sc, const void* qz,
-                         int N, int K, const float* gs, int Mp, void* y, int64_t ldy, hipStream_t st) {
-  if constexpr (G == 128) {
-    if (mt == 8) return gptq_gemm_go<SYM, G, 8, TY>(x, ldx, M, qw, sc, qz, N, K, gs, Mp, y, ldy, st);
-  }
-  gptq_gemm_go<SYM, G, 4, TY>(x, ldx, M, qw, sc, qz, N, K, gs, Mp, y, ldy, st);
-}
 template <bool SYM, int G>
-static void gptq_gemm_ty(int ty, int mt, const void* x, int64_t ldx, int M, const void* qw, const void* sc,
-                         const void* qz, int N, int K, const float* gs, int Mp, void* y, int64_t ldy,
-                         hipStream_t st) {
-  if (ty == GemvOut::kBF16) gptq_gemm_mt<SYM, G, uint16_t>(mt, x, ldx, M, qw, sc, qz, N, K, gs, Mp, y, ldy, st);
-  else gptq_gemm_mt<SYM, G, float>(mt, x, ldx, M, qw, sc, qz, N, K, gs, Mp, y, ldy, st);
+static void gptq_gemm_ty(int ty, const void* x, int64_t ldx, int M, const void* qw, const void* sc, const void* qz,
+                         int N, int K, const float* gs, int Mp, void* y, int64_t ldy, hipStream_t st) {
+  if (ty == GemvOut::kBF16) gptq_gemm_go<SYM, G, 4, uint16_t>(x, ldx, M, qw, sc, qz, N, K, gs, Mp, y, ldy, st);
+  else gptq_gemm_go<SYM, G, 4, float>(x, ldx, M, qw, sc, qz, N, K, gs, Mp, y, ldy, st);
 }
 template <int G>
 static void group_sums_go(const void* x, int64_t ldx, int M, int K, int Mp, float* sums, hipStream_t st) {
@@ -439,15 +432,13 @@ static void group_sums_go(const void* x, int64_t ldx, int M, int K, int Mp, floa
 void launch_gptq_gemm(bool sym, int group, const void* qweight, const void* scales, const void* qzeros, int64_t N,
                       int64_t K, const void* x, int64_t M, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
                       float* sums, hipStream_t st) {
-  const int Mp = (int)((M + 127) / 128 * 128), mt = gemm_mt(M);
+  const int Mp = (int)((M + 127) / 128 * 128);
   const int ty = y_dtype == kF32 ? GemvOut::kF32 : GemvOut::kBF16;
 #define GWB_GEMM_G(G)                                                                                               \
   do {                                                                                                              \
     group_sums_go<G>(x, ldx, (int)M, (int)K, Mp, sums, st);                                                         \
-    if (sym) gptq_gemm_ty<true, G>(ty, mt, x, ldx, (int)M, qweight, scales, qzeros, (int)N, (int)K, sums, Mp, y,    \
-                                   ldy, st);                                                                        \
-    else gptq_gemm_ty<false, G>(ty, mt, x, ldx, (int)M, qweight, scales, qzeros, (int)N, (int)K, sums, Mp, y, ldy,  \
-                                st);                                                                                \
+    if (sym) gptq_gemm_ty<true, G>(ty, x, ldx, (int)M, qweight, scales, qzeros, (int)N, (int)K, sums, Mp, y, ldy, st); \
+    else gptq_gemm_ty<false, G>(ty, x, ldx, (int)M, qweight, scales, qzeros, (int)N, (int)K, sums, Mp, y, ldy, st);    \
   } while (0)
   if (group == 32) GWB_GEMM_G(32);
   else if (group == 64) GWB_GEMM_G(64);
@@ -465,7 +456,7 @@ static void mxfp4_gemm_go(const void* x, int64_t ldx, int M, const void* codes, 
 
 void launch_mxfp4_gemm(const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x, int64_t M,
                        int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, hipStream_t st) {
-  const int mt = gemm_mt(M);
+  const int mt = M <= 64 ? 4 : 8;
   if (y_dtype == kF32) {
     if (mt == 4) mxfp4_gemm_go<4, float>(x, ldx, (int)M, packed, e8m0, (int)N, (int)K, y, ldy, st);
     else mxfp4_gemm_go<8, float>(x, ldx, (int)M, packed, e8m0, (int)N, (int)K, y, ldy, st);
