@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 N, K = 34816, 5120
 PEAK_HBM_GBPS = 8000.0
+PEAK_MFMA_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 FORMATS = [("mxfp4", 4, 32), ("gptq_sym", 4, 128), ("gptq_asym", 4, 128)] + \
           [("uintx", b, 64) for b in range(2, 8)]
 ALPHAS = tuple(i / 10 for i in range(11))
@@ -251,6 +252,34 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
         out.append({"op": name, "shape": shape, "us": round(us, 2),
                     "hbm_GBps": round(abytes / (us * 1e-6) / 1e9, 1),
                     "frac_hbm_peak": round(abytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)})
+    out += measure_gemm(gwb, workloads, Wd, dev)
+    return out
+
+
+def measure_gemm(gwb, workloads, Wd, dev):
+    """The prefill GEMM y = x @ dequant(W)^T on the packed gate_up weight for M
+    activation rows (bf16 in, bf16 out, matrix cores), against the dense bf16 MFMA peak;
+    beside it torch's bf16 matmul of the same shape on an unquantized weight (hipBLASLt),
+    for context."""
+    out = []
+    Wt = Wd.t().contiguous()            # [K, N]: a plain (untransposed) right operand
+    for M in (2048, 256):
+        x = workloads.normal_weight(M, K, std=1.0, seed=650).to(dev)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        flops = 2.0 * M * N * K
+        calls = []
+        for fmt in ("gptq_sym", "gptq_asym", "mxfp4"):
+            q = gwb.quantize(Wd, fmt, group=128 if fmt != "mxfp4" else None)
+            nb = gwb.gemm_workspace_bytes(q, M)
+            ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+            tag = f"{fmt}_g128" if fmt != "mxfp4" else fmt
+            calls.append((f"gemm.{tag}.m{M}", gwb.prepare_gemm(q, x, y, ws), q, ws))
+        calls.append((f"gemm.bf16_torch_matmul_reference.m{M}", lambda: torch.matmul(x, Wt, out=y), None, None))
+        for name, fn, _q, _ws in calls:
+            us = _time_op(fn)
+            tf = flops / (us * 1e-6) / 1e12
+            out.append({"op": name, "shape": [M, N, K], "us": round(us, 2), "TFLOPs": round(tf, 1),
+                        "frac_mfma_bf16_peak": round(tf / PEAK_MFMA_BF16_TFLOPS, 4)})
     return out
 
 

@@ -1,4 +1,5 @@
-"""Dequantize-and-multiply reference for the decode GEMV (test infrastructure only).
+"""Dequantize-and-multiply reference for the decode GEMV and the prefill GEMM (test
+infrastructure only; both consumers compute the same product, for B <= 8 or M rows).
 
 Page export_gptq_cpu.py gives the reason for the 4-bit formats: in a decode step the
 weight read dominates (its lm_head note: the 131072 x 2048 head is the single largest
