@@ -35,6 +35,9 @@ sys.path.insert(0, ROOT)
 N, K = 34816, 5120
 PEAK_HBM_GBPS = 8000.0
 PEAK_MFMA_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak
+# kernels launched by one library call of each step op (quantize, dequantize: one; SNR: the
+# error pass and its finalize; AWQ: table pow, table scale, search, finalize)
+OP_KERNELS = {"quant": 1, "dequant": 1, "snr": 2, "search": 4}
 FORMATS = [("mxfp4", 4, 32), ("gptq_sym", 4, 128), ("gptq_asym", 4, 128)] + \
           [("uintx", b, 64) for b in range(2, 8)]
 ALPHAS = tuple(i / 10 for i in range(11))
@@ -435,6 +438,9 @@ def main():
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
             "algorithmic_bytes_per_launch": int(dbytes), "avg_launch_us": round(dom_ms * 1e3, 2),
+            # kernels one library call of this op launches (all inside its event pair): an SNR
+            # pass is its error kernel plus the in-order float64 finalize of the block sums
+            "kernels_in_event_pair": OP_KERNELS[dname.split(".")[1] if "." in dname else dname],
         },
         "cpu_baseline": cpu,
         "copy_ceiling_GBps": round(copy_gbps, 1),
