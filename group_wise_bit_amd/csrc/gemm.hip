@@ -6,10 +6,10 @@
 // accumulation) in registers, and the activations are staged through LDS, shared by
 // the block's four wavefronts.
 //
-// Block: 4 wavefronts, BM = 16*MT rows x 256 columns; wavefront w owns columns
-// n0 + 64w .. +63 and all BM rows (MT x 4 MFMA tiles of 16 x 16). Lane l (j = l % 16,
-// q = l / 16) feeds B column j of tile t with the weights of column nb + 4j + t, so its
-// accumulators hold rows 16mt + 4q + r (r < 4) of the 4 adjacent columns nb + 4j .. +3.
+// Block: 4 wavefronts, BM = 16*MT rows x 256 columns; wavefront w owns the 64 columns
+// from nw = n0 + 64w and all BM rows (MT x 4 MFMA tiles of 16 x 16). Lane l (j = l % 16,
+// q = l / 16) feeds B column j of tile t with the weights of column nw + 4j + t, so its
+// accumulators hold rows 16mt + 4q + r (r < 4) of the 4 adjacent columns nw + 4j .. +3.
 // K runs in stages of 128 through a double-buffered LDS tile of activations.
 //
 // GPTQ: codes c are integers and bf16(128 + c) is exact: a byte select and a mask turn
