@@ -186,9 +186,7 @@ __global__ __launch_bounds__(256, MT == 4 && G == 128 ? 2 : 1) void gptq_gemm_ke
   uint32_t aof[MT];
   a_offsets<MT>(ldx, M, m0, wv, lane, aof);
   uint32_t pe = 0x43004300u;
-#if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("" : "+v"(pe));   // keep the constant in a vector register
-#endif
 
   U4 wv4[4];
   uint2 scv[NGS];
