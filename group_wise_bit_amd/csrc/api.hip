@@ -456,7 +456,7 @@ static int check_gemm(const gwb_qspec* sp, int64_t N, int64_t K, int64_t M) {
 int gwb_gemm_workspace(const gwb_qspec* spec, int64_t N, int64_t K, int64_t M, size_t* bytes) {
   if (!bytes) return fail(GWB_E_ARG, "bytes is NULL");
   if (int rc = check_gemm(spec, N, K, M)) return rc;
-  *bytes = gwb::gemm_workspace_bytes(!is_mxfp4(spec->format), spec->group, M, K);
+  *bytes = gwb::gemm_workspace_bytes(!is_mxfp4(spec->format), spec->group, M, N, K);
   return ok();
 }
 
@@ -475,16 +475,16 @@ int gwb_gemm(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
   if (int rc = check_tensors(spec, w)) return rc;
   if (!aligned16(w->codes) || !aligned16(w->scales))
     return fail(GWB_E_UNSUPPORTED, "the GEMM needs 16-byte aligned codes and scales");
-  const size_t need = gwb::gemm_workspace_bytes(!is_mxfp4(spec->format), spec->group, M, K);
+  const size_t need = gwb::gemm_workspace_bytes(!is_mxfp4(spec->format), spec->group, M, N, K);
   if (need && (!workspace || workspace_bytes < need))
     return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (need && !aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   if (is_mxfp4(spec->format))
-    gwb::launch_mxfp4_gemm(w->codes, w->scales, N, K, x, M, ldx, y, y_dtype, ldy, st);
+    gwb::launch_mxfp4_gemm(w->codes, w->scales, N, K, x, M, ldx, y, y_dtype, ldy, workspace, st);
   else
     gwb::launch_gptq_gemm(spec->format == GWB_GPTQ_SYM, spec->group, w->codes, w->scales, w->zeros, N, K, x, M, ldx,
-                          y, y_dtype, ldy, (float*)workspace, st);
+                          y, y_dtype, ldy, workspace, st);
   return hip_check("gemm launch");
 }
 

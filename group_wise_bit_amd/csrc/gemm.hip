@@ -51,8 +51,8 @@ __device__ __forceinline__ gm_f32x4_t mfma_bf16(U4 a, U4 b, gm_f32x4_t c) {
 // Workgroups go round-robin over the 8 XCDs, each with its own L2. Each XCD gets a
 // contiguous range of tiles; tiles run in bands of up to 4 row tiles across all column
 // tiles, so the blocks an XCD holds at one time share activation rows and weights.
-__device__ __forceinline__ void gemm_tile(int gx, int gy, int& bx, int& by) {
-  const int T = gx * gy, id = blockIdx.x, xcd = id & 7, rem = T & 7;
+__device__ __forceinline__ void gemm_tile(int id, int gx, int gy, int& bx, int& by) {
+  const int T = gx * gy, xcd = id & 7, rem = T & 7;
   const int t = xcd * (T >> 3) + min(xcd, rem) + (id >> 3);
   const int band = t / (4 * gy), first = band * 4, rows = min(4, gx - first);
   const int r = t - first * gy;
@@ -156,10 +156,10 @@ __device__ __forceinline__ U4 gptq_pairs(uint32_t w, uint32_t e) {
 }
 
 template <bool SYM, int G, int MT, typename TY>
-__global__ __launch_bounds__(256, MT == 4 && G == 128 ? 2 : 1) void gptq_gemm_kernel(
+__global__ __launch_bounds__(256, MT <= 2 || (MT == 4 && G == 128) ? 2 : 1) void gptq_gemm_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, int M, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ sc, const uint32_t* __restrict__ qz, int N, int K, const float* __restrict__ gsum,
-    int Mp, TY* __restrict__ y, int64_t ldy, int gx, int gy) {
+    int Mp, TY* __restrict__ y, int64_t ldy, int gx, int gy, int S) {
   constexpr int BM = 16 * MT, SPG = G / 32, NGS = kGmBK / G;   // steps per group, groups per stage
   constexpr int SUMS = BM * NGS / 4;                            // 16-byte chunks of group sums per stage
   static_assert(SUMS <= 256 && BM * NGS <= kGmSumMax, "group sums of a stage fit one chunk per thread");
@@ -169,8 +169,13 @@ __global__ __launch_bounds__(256, MT == 4 && G == 128 ? 2 : 1) void gptq_gemm_ke
   uint16_t(*As)[BM * 128] = reinterpret_cast<uint16_t(*)[BM * 128]>(smem);
   float(*Ss)[NGS * BM] = reinterpret_cast<float(*)[NGS * BM]>(smem + 2 * BM * 128);
 
+  // K split (small grids): block = split * tiles + tile; split s takes stages
+  // [s * nst / S, (s + 1) * nst / S) and stores float32 partials at y + s * M * ldy
+  const int T = gx * gy, split = (int)blockIdx.x / T, nst = K / kGmBK;
+  const int st0 = split * nst / S, st1 = (split + 1) * nst / S;
+  y += (int64_t)split * M * ldy;
   int bx, by;
-  gemm_tile(gx, gy, bx, by);
+  gemm_tile((int)blockIdx.x - split * T, gx, gy, bx, by);
   const int lane = threadIdx.x & 63, j = lane & 15, q = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int m0 = bx * BM, nl = by * kGmBN + wv * 64 + 4 * j;
@@ -215,11 +220,10 @@ __global__ __launch_bounds__(256, MT == 4 && G == 128 ? 2 : 1) void gptq_gemm_ke
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[mt][t] = gm_f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  fetch(0, 0);
+  fetch(st0 * kGmBK, 0);
   stage_barrier();
-  const int nst = K / kGmBK;
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
+  for (int st = st0; st < st1; ++st) {
+    const int buf = (st - st0) & 1;
     const uint16_t* A = As[buf];
     float4 sx[NGS][MT];
 #pragma unroll
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(256, MT == 4 && G == 128 ? 2 : 1) void gptq_gemm_ke
       scl[gi] = scv[gi];
       if constexpr (!SYM) zl[gi] = zv[gi];
     }
-    if (st + 1 < nst) fetch((st + 1) * kGmBK, buf ^ 1);
+    if (st + 1 < st1) fetch((st + 1) * kGmBK, buf ^ 1);
 
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -285,12 +289,18 @@ template <int MT, typename TY>
 __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
                                                            const uint8_t* __restrict__ codes,
                                                            const uint8_t* __restrict__ e8m0, int N, int K,
-                                                           TY* __restrict__ y, int64_t ldy, int gx, int gy) {
+                                                           TY* __restrict__ y, int64_t ldy, int gx, int gy,
+                                                           int S) {
   constexpr int BM = 16 * MT;
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * 128];
 
+  // K split (small grids): block = split * tiles + tile; split s takes stages
+  // [s * nst / S, (s + 1) * nst / S) and stores float32 partials at y + s * M * ldy
+  const int T = gx * gy, split = (int)blockIdx.x / T, nst = K / kGmBK;
+  const int st0 = split * nst / S, st1 = (split + 1) * nst / S;
+  y += (int64_t)split * M * ldy;
   int bx, by;
-  gemm_tile(gx, gy, bx, by);
+  gemm_tile((int)blockIdx.x - split * T, gx, gy, bx, by);
   const int lane = threadIdx.x & 63, j = lane & 15, q = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int m0 = bx * BM, nl = by * kGmBN + wv * 64 + 4 * j;
@@ -322,12 +332,11 @@ __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(const uint16_t* __re
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[mt][t] = gm_f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  fetch(0, 0);
+  fetch(st0 * kGmBK, 0);
   stage_barrier();
-  const int nst = K / kGmBK;
   uint32_t nanc = 0;   // bit t: column nc + t has a block with scale byte 255
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
+  for (int st = st0; st < st1; ++st) {
+    const int buf = (st - st0) & 1;
     U4 w[4];
     uint32_t e[4];
 #pragma unroll
@@ -335,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(const uint16_t* __re
       w[t] = wv4[t];
       e[t] = ev[t];
     }
-    if (st + 1 < nst) fetch((st + 1) * kGmBK, buf ^ 1);
+    if (st + 1 < st1) fetch((st + 1) * kGmBK, buf ^ 1);
     float scl[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -400,25 +409,70 @@ __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(const uint16_t* __re
 // wavefront per SIMD, GPTQ 930-970 vs 640). Smaller GPTQ groups keep 64 rows at one
 // wavefront per SIMD (their per-group state does not fit 256 registers).
 
-size_t gemm_workspace_bytes(bool gptq, int group, int64_t M, int64_t K) {
+// K splits: small-M grids (one row tile over N / 256 column tiles) leave most CUs idle;
+// up to 4 splits, each of at least 2 stages, bring the grid to about 512 blocks. Their
+// float32 partials (M x N each) are summed in split order by a second kernel. Only for
+// M <= 64, where the partials stay small next to the packed weight.
+// 16-row granularity of the matrix-core tiles: small M takes 16- or 32-row blocks
+// rather than computing padding rows.
+static int gemm_small_mt(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+static int gemm_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t rows = 16 * gemm_small_mt(M);
+  const int64_t T = ((M + rows - 1) / rows) * ((N + kGmBN - 1) / kGmBN), nst = K / kGmBK;
+  if (M > 64 || T == 0) return 1;
+  int64_t S = (512 + T - 1) / T;
+  if (S > 4) S = 4;
+  if (S > nst / 2) S = nst / 2;
+  return S < 1 ? 1 : (int)S;
+}
+static size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+static size_t sums_bytes(bool gptq, int group, int64_t M, int64_t K) {
   if (!gptq) return 0;
   const int64_t Mp = (M + 127) / 128 * 128;
-  return (size_t)(K / group) * (size_t)Mp * sizeof(float);
+  return align256((size_t)(K / group) * (size_t)Mp * sizeof(float));
+}
+
+size_t gemm_workspace_bytes(bool gptq, int group, int64_t M, int64_t N, int64_t K) {
+  const int S = gemm_splits(M, N, K);
+  return sums_bytes(gptq, group, M, K) + (S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0);
+}
+
+// y[m, n] = sum over splits of part[s][m][n], in split order; 4 outputs per thread.
+template <typename TY>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, int S, int M, int N,
+                                                         TY* __restrict__ y, int64_t ldy) {
+  const int64_t MN = (int64_t)M * N, i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= MN) return;
+  float4 v = *reinterpret_cast<const float4*>(part + i);
+  for (int s = 1; s < S; ++s) {
+    const float4 u = *reinterpret_cast<const float4*>(part + s * MN + i);
+    v.x += u.x;
+    v.y += u.y;
+    v.z += u.z;
+    v.w += u.w;
+  }
+  const int64_t m = i / N, n = i - m * N;
+  TY* p = y + m * ldy + n;
+  if constexpr (sizeof(TY) == 4) *reinterpret_cast<float4*>(p) = v;
+  else *reinterpret_cast<uint2*>(p) = uint2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+}
+static void gemm_reduce(const float* part, int S, int M, int N, void* y, int32_t y_dtype, int64_t ldy,
+                        hipStream_t st) {
+  const int64_t threads = (int64_t)M * N / 4;
+  const dim3 grid((unsigned)((threads + 255) / 256));
+  if (y_dtype == kF32)
+    hipLaunchKernelGGL(gemm_reduce_kernel<float>, grid, dim3(256), 0, st, part, S, M, N, (float*)y, ldy);
+  else
+    hipLaunchKernelGGL(gemm_reduce_kernel<uint16_t>, grid, dim3(256), 0, st, part, S, M, N, (uint16_t*)y, ldy);
 }
 
 template <bool SYM, int G, int MT, typename TY>
 static void gptq_gemm_go(const void* x, int64_t ldx, int M, const void* qw, const void* sc, const void* qz, int N,
-                         int K, const float* gs, int Mp, void* y, int64_t ldy, hipStream_t st) {
+                         int K, const float* gs, int Mp, void* y, int64_t ldy, int S, hipStream_t st) {
   const int gx = (M + 16 * MT - 1) / (16 * MT), gy = (N + kGmBN - 1) / kGmBN;
-  hipLaunchKernelGGL((gptq_gemm_kernel<SYM, G, MT, TY>), dim3(gx * gy), dim3(256), 0, st, (const uint16_t*)x, ldx,
-                     M, (const uint32_t*)qw, (const uint16_t*)sc, (const uint32_t*)qz, N, K, gs, Mp, (TY*)y, ldy,
-                     gx, gy);
-}
-template <bool SYM, int G>
-static void gptq_gemm_ty(int ty, const void* x, int64_t ldx, int M, const void* qw, const void* sc, const void* qz,
-                         int N, int K, const float* gs, int Mp, void* y, int64_t ldy, hipStream_t st) {
-  if (ty == GemvOut::kBF16) gptq_gemm_go<SYM, G, 4, uint16_t>(x, ldx, M, qw, sc, qz, N, K, gs, Mp, y, ldy, st);
-  else gptq_gemm_go<SYM, G, 4, float>(x, ldx, M, qw, sc, qz, N, K, gs, Mp, y, ldy, st);
+  hipLaunchKernelGGL((gptq_gemm_kernel<SYM, G, MT, TY>), dim3(gx * gy * S), dim3(256), 0, st, (const uint16_t*)x,
+                     ldx, M, (const uint32_t*)qw, (const uint16_t*)sc, (const uint32_t*)qz, N, K, gs, Mp, (TY*)y, ldy,
+                     gx, gy, S);
 }
 template <int G>
 static void group_sums_go(const void* x, int64_t ldx, int M, int K, int Mp, float* sums, hipStream_t st) {
@@ -426,17 +480,45 @@ static void group_sums_go(const void* x, int64_t ldx, int M, int K, int Mp, floa
   hipLaunchKernelGGL((gemm_group_sums_kernel<G>), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, st,
                      (const uint16_t*)x, ldx, M, K, Mp, sums);
 }
+// GPTQ blocks are 64 rows (two wavefronts per SIMD with 128-groups); with K splits the
+// kernel writes float32 partials and the reduction writes y.
+template <bool SYM, int G, int MT>
+static void gptq_gemm_mt(const void* x, int64_t ldx, int M, const void* qw, const void* sc, const void* qz, int N,
+                         int K, float* sums, int Mp, void* y, int32_t y_dtype, int64_t ldy, float* part,
+                         hipStream_t st) {
+  const int S = gemm_splits(M, N, K);
+  if (S > 1) {
+    gptq_gemm_go<SYM, G, MT, float>(x, ldx, M, qw, sc, qz, N, K, sums, Mp, part, N, S, st);
+    gemm_reduce(part, S, M, N, y, y_dtype, ldy, st);
+  } else if (y_dtype == kBF16) {
+    gptq_gemm_go<SYM, G, MT, uint16_t>(x, ldx, M, qw, sc, qz, N, K, sums, Mp, y, ldy, 1, st);
+  } else {
+    gptq_gemm_go<SYM, G, MT, float>(x, ldx, M, qw, sc, qz, N, K, sums, Mp, y, ldy, 1, st);
+  }
+}
+template <bool SYM, int G>
+static void gptq_gemm_run(const void* x, int64_t ldx, int M, const void* qw, const void* sc, const void* qz, int N,
+                          int K, float* sums, int Mp, void* y, int32_t y_dtype, int64_t ldy, float* part,
+                          hipStream_t st) {
+  const int mt = gemm_small_mt(M);
+  if (mt == 1) gptq_gemm_mt<SYM, G, 1>(x, ldx, M, qw, sc, qz, N, K, sums, Mp, y, y_dtype, ldy, part, st);
+  else if (mt == 2) gptq_gemm_mt<SYM, G, 2>(x, ldx, M, qw, sc, qz, N, K, sums, Mp, y, y_dtype, ldy, part, st);
+  else gptq_gemm_mt<SYM, G, 4>(x, ldx, M, qw, sc, qz, N, K, sums, Mp, y, y_dtype, ldy, part, st);
+}
 
 void launch_gptq_gemm(bool sym, int group, const void* qweight, const void* scales, const void* qzeros, int64_t N,
                       int64_t K, const void* x, int64_t M, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
-                      float* sums, hipStream_t st) {
+                      void* workspace, hipStream_t st) {
   const int Mp = (int)((M + 127) / 128 * 128);
-  const int ty = y_dtype == kF32 ? GemvOut::kF32 : GemvOut::kBF16;
+  float* sums = (float*)workspace;
+  float* part = (float*)((char*)workspace + sums_bytes(true, group, M, K));
 #define GWB_GEMM_G(G)                                                                                               \
   do {                                                                                                              \
     group_sums_go<G>(x, ldx, (int)M, (int)K, Mp, sums, st);                                                         \
-    if (sym) gptq_gemm_ty<true, G>(ty, x, ldx, (int)M, qweight, scales, qzeros, (int)N, (int)K, sums, Mp, y, ldy, st); \
-    else gptq_gemm_ty<false, G>(ty, x, ldx, (int)M, qweight, scales, qzeros, (int)N, (int)K, sums, Mp, y, ldy, st);    \
+    if (sym) gptq_gemm_run<true, G>(x, ldx, (int)M, qweight, scales, qzeros, (int)N, (int)K, sums, Mp, y, y_dtype,  \
+                                    ldy, part, st);                                                                 \
+    else gptq_gemm_run<false, G>(x, ldx, (int)M, qweight, scales, qzeros, (int)N, (int)K, sums, Mp, y, y_dtype,     \
+                                 ldy, part, st);                                                                    \
   } while (0)
   if (group == 32) GWB_GEMM_G(32);
   else if (group == 64) GWB_GEMM_G(64);
@@ -446,22 +528,33 @@ void launch_gptq_gemm(bool sym, int group, const void* qweight, const void* scal
 
 template <int MT, typename TY>
 static void mxfp4_gemm_go(const void* x, int64_t ldx, int M, const void* codes, const void* e8, int N, int K,
-                          void* y, int64_t ldy, hipStream_t st) {
+                          void* y, int64_t ldy, int S, hipStream_t st) {
   const int gx = (M + 16 * MT - 1) / (16 * MT), gy = (N + kGmBN - 1) / kGmBN;
-  hipLaunchKernelGGL((mxfp4_gemm_kernel<MT, TY>), dim3(gx * gy), dim3(256), 0, st, (const uint16_t*)x, ldx, M,
-                     (const uint8_t*)codes, (const uint8_t*)e8, N, K, (TY*)y, ldy, gx, gy);
+  hipLaunchKernelGGL((mxfp4_gemm_kernel<MT, TY>), dim3(gx * gy * S), dim3(256), 0, st, (const uint16_t*)x, ldx, M,
+                     (const uint8_t*)codes, (const uint8_t*)e8, N, K, (TY*)y, ldy, gx, gy, S);
 }
 
-void launch_mxfp4_gemm(const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x, int64_t M,
-                       int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, hipStream_t st) {
-  const int mt = M <= 64 ? 4 : 8;
-  if (y_dtype == kF32) {
-    if (mt == 4) mxfp4_gemm_go<4, float>(x, ldx, (int)M, packed, e8m0, (int)N, (int)K, y, ldy, st);
-    else mxfp4_gemm_go<8, float>(x, ldx, (int)M, packed, e8m0, (int)N, (int)K, y, ldy, st);
+template <int MT>
+static void mxfp4_gemm_mt(const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x, int64_t M,
+                          int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, hipStream_t st) {
+  const int S = gemm_splits(M, N, K);
+  if (S > 1) {
+    mxfp4_gemm_go<MT, float>(x, ldx, (int)M, packed, e8m0, (int)N, (int)K, workspace, N, S, st);
+    gemm_reduce((const float*)workspace, S, (int)M, (int)N, y, y_dtype, ldy, st);
+  } else if (y_dtype == kF32) {
+    mxfp4_gemm_go<MT, float>(x, ldx, (int)M, packed, e8m0, (int)N, (int)K, y, ldy, 1, st);
   } else {
-    if (mt == 4) mxfp4_gemm_go<4, uint16_t>(x, ldx, (int)M, packed, e8m0, (int)N, (int)K, y, ldy, st);
-    else mxfp4_gemm_go<8, uint16_t>(x, ldx, (int)M, packed, e8m0, (int)N, (int)K, y, ldy, st);
+    mxfp4_gemm_go<MT, uint16_t>(x, ldx, (int)M, packed, e8m0, (int)N, (int)K, y, ldy, 1, st);
   }
+}
+// MXFP4 blocks are 128 rows above M = 64 (two wavefronts per SIMD either way).
+void launch_mxfp4_gemm(const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x, int64_t M,
+                       int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, hipStream_t st) {
+  const int mt = M > 64 ? 8 : gemm_small_mt(M);
+  if (mt == 1) mxfp4_gemm_mt<1>(packed, e8m0, N, K, x, M, ldx, y, y_dtype, ldy, workspace, st);
+  else if (mt == 2) mxfp4_gemm_mt<2>(packed, e8m0, N, K, x, M, ldx, y, y_dtype, ldy, workspace, st);
+  else if (mt == 4) mxfp4_gemm_mt<4>(packed, e8m0, N, K, x, M, ldx, y, y_dtype, ldy, workspace, st);
+  else mxfp4_gemm_mt<8>(packed, e8m0, N, K, x, M, ldx, y, y_dtype, ldy, workspace, st);
 }
 
 }  // namespace gwb

@@ -143,14 +143,15 @@ void launch_gptq_act_gemv(bool sym, int group, int B, const void* qweight, const
 void launch_mxfp4_gemv(int B, const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x,
                        int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, hipStream_t st);
 // ---- prefill GEMM on quantized weights (gemm.hip): M activation rows (bf16), matrix
-// cores; N % 8 == 0, K % 128 == 0. GPTQ needs gemm_workspace_bytes for the group sums.
+// cores; N % 8 == 0, K % 128 == 0. Workspace: GPTQ's group sums of x, then (small M)
+// the K-split partial sums.
 constexpr int kGemmMaxRows = 1 << 24;
-size_t gemm_workspace_bytes(bool gptq, int group, int64_t M, int64_t K);
+size_t gemm_workspace_bytes(bool gptq, int group, int64_t M, int64_t N, int64_t K);
 void launch_gptq_gemm(bool sym, int group, const void* qweight, const void* scales, const void* qzeros, int64_t N,
                       int64_t K, const void* x, int64_t M, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
-                      float* sums, hipStream_t st);
+                      void* workspace, hipStream_t st);
 void launch_mxfp4_gemm(const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x, int64_t M,
-                       int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, hipStream_t st);
+                       int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, hipStream_t st);
 // uintx (uintx.hip): N % 8 == 0 and K % 512 == 0; with more than one split, part holds
 // splits * B * N floats
 bool uintx_gemv_supported(int64_t N, int64_t K);

@@ -257,7 +257,9 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
  *   y        device [M, N] of y_dtype (GWB_F32 or GWB_BF16, RNE), row stride ldy
  *            (multiple of 8), 16-byte aligned
  *   workspace at least gwb_gemm_workspace bytes: GPTQ the float32 group sums of x
- *            (K/G x M rounded up to 128), MXFP4 0
+ *            (K/G x M rounded up to 128, padded to 256 bytes); for M <= 64 with few
+ *            column tiles also the float32 partial sums of a K split (splits x M x N),
+ *            which a second kernel adds in split order; MXFP4 only the latter
  * MXFP4 weights are exact bf16 operands, so every product is exact and only the
  * float32 sums round. GPTQ feeds the exact integers 128 + c and applies each group's
  * scale and zero point to the group's float32 sum: s * (sum x (128 + c) - (128 + z) *

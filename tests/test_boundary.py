@@ -276,6 +276,10 @@ def test_gemm_sizes_and_validation():
     assert ws("mxfp4", 34816, 5120, 2048) == (gwb.OK, 0)
     assert ws("mxfp4_page_ties", 256, 128, 1) == (gwb.OK, 0)
     assert ws("gptq_sym", 256, 1024, 0) == (gwb.OK, 0)
+    assert ws("mxfp4", 264, 2048, 16) == (gwb.OK, 4 * 16 * 264 * 4)            # small M: 4 K splits
+    assert ws("gptq_sym", 264, 2048, 16, 128) == (gwb.OK, 16 * 128 * 4 + 4 * 16 * 264 * 4)
+    assert ws("mxfp4", 34816, 640, 64) == (gwb.OK, 2 * 64 * 34816 * 4)         # 5 stages: 2 splits
+    assert ws("mxfp4", 131072, 2048, 64) == (gwb.OK, 0)                        # 512 tiles: no split
     assert ws("gptq_sym", 256, 576, 16, 64)[0] == gwb.E_UNSUPPORTED           # K % 128
     assert ws("mxfp4", 100, 1024, 16)[0] == gwb.E_UNSUPPORTED                 # N % 8
     assert ws("uintx", 256, 1024, 16, 64)[0] == gwb.E_UNSUPPORTED

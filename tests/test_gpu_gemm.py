@@ -103,11 +103,41 @@ def test_gemm_one_hot_reads_weights_exactly(fmt, group):
         assert np.array_equal(y, (d[:, cols] * np.float32(2.0 ** p)).T), (fmt, p, M)
 
 
-def test_gemm_mxfp4_scale_byte_255_columns():
+@pytest.mark.parametrize("fmt,group", [("gptq_sym", 128), ("gptq_asym", 32), ("mxfp4", None)])
+@pytest.mark.parametrize("M,k", [(8, 2048), (48, 640), (16, 768)])
+def test_gemm_k_split_parity(fmt, group, M, k):
+    """Small M splits K (2 to 4 splits, also uneven ones: 5 stages over 2 splits); the
+    float32 partials are summed in split order. Same bounds; one-hot rows stay exact."""
+    n = 264
+    W = workloads.mxfp4_weight(n, k, seed=670 + M)
+    x = workloads.normal_weight(M, k, std=1.0, seed=671 + M)
+    q = gwb.quantize(W.to(DEV), fmt, group=group)
+    xf = x.float().numpy()
+    if fmt == "mxfp4":
+        packed, e8 = omx.quantize(W.float().numpy())
+        deq = omx.dequantize(packed, e8, k)
+        bound = U32 * (k + 8) * ogv.abs_gemv(deq, xf)
+    else:
+        o = (ogq.quantize_sym if fmt == "gptq_sym" else ogq.quantize_asym)(W.float().numpy(), group)
+        deq = ogv.dequantized(fmt, o, n, k, group=group)
+        bound = _gptq_bound(o, xf, group, k)
+    ref = ogv.gemv(deq, xf)
+    for ydt in (torch.float32, torch.bfloat16):
+        _check(gwb.gemm(q, x.to(DEV), ydt), ref, bound, ydt)
+    d = _np(gwb.dequantize(q, torch.float32))
+    oh = torch.zeros(M, k, dtype=torch.bfloat16)
+    cols = (np.arange(M) * 37 + 5) % k
+    oh[np.arange(M), cols] = 0.5
+    y = _np(gwb.gemm(q, oh.to(DEV)))
+    assert np.array_equal(y, (d[:, cols] * np.float32(0.5)).T)
+
+
+@pytest.mark.parametrize("M", [70, 12])
+def test_gemm_mxfp4_scale_byte_255_columns(M):
     """Scale byte 255 has no E8M0 value: the page's weights +-E2M1 * 2^128 are inf (NaN
     for a zero code), so those columns' outputs are inf or NaN as in the float64
-    product; every other column keeps the ordinary bound."""
-    M, n, k = 70, 264, 640
+    product; every other column keeps the ordinary bound (M = 12 also splits K)."""
+    n, k = 264, 640
     W = workloads.mxfp4_weight(n, k, seed=660)
     x = workloads.normal_weight(M, k, std=1.0, seed=661)
     q = gwb.quantize(W.to(DEV), "mxfp4")
