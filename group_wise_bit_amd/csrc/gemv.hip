@@ -181,9 +181,13 @@ __global__ __launch_bounds__(256) void gptq_gemv_kernel(const uint32_t* __restri
 // k the group g_idx[k] is the same across the wavefront and picks each column's scale and
 // zero point from LDS, which holds every group's for the block's columns. Products with
 // the bf16 activations are exact; sums are float32 in k order per wavefront.
+// TAB (up to kActTabGroups groups): LDS holds each (group, column)'s float32 pair
+// (s, -z s), both exact, so a weight is one 8-byte LDS read and one fma; otherwise the
+// fp16 scale bits and the qzeros words (a fifth of the bytes), widened per weight.
 constexpr int kActGvCols = 64;
+constexpr int kActTabGroups = 96;   // 48 KB of (s, -z s) pairs per block
 
-template <bool SYM, int B, typename TY>
+template <bool SYM, int B, typename TY, bool TAB>
 __global__ __launch_bounds__(256) void gptq_act_gemv_kernel(const uint32_t* __restrict__ qweight,
                                                             const uint16_t* __restrict__ scale_bits,
                                                             const uint32_t* __restrict__ qzeros,
@@ -194,19 +198,32 @@ __global__ __launch_bounds__(256) void gptq_act_gemv_kernel(const uint32_t* __re
   extern __shared__ uint32_t lds[];
   uint16_t* sl = reinterpret_cast<uint16_t*>(lds);             // [NG][64] fp16 scale bits
   uint32_t* zl = lds + NG * (kActGvCols / 2);                    // [NG][8] qzeros words
+  float2* tz = reinterpret_cast<float2*>(lds);                   // TAB: [NG][64] (s, -z s)
   __shared__ float red[4][B][kActGvCols];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int n0 = blockIdx.x * kActGvCols;
   const int nc = min(n0 + lane, N - 1);                         // lanes past N read a valid place
-  for (int e = t; e < NG * kActGvCols; e += 256) {
-    const int g = e / kActGvCols, c = e - g * kActGvCols;
-    sl[e] = n0 + c < N ? scale_bits[(int64_t)g * N + n0 + c] : (uint16_t)0;
-  }
-  if constexpr (!SYM) {
-    for (int e = t; e < NG * (kActGvCols / 8); e += 256) {
-      const int g = e / (kActGvCols / 8), q = e - g * (kActGvCols / 8);
-      zl[e] = n0 + 8 * q < N ? qzeros[(int64_t)g * (N / 8) + n0 / 8 + q] : 0u;
+  if constexpr (TAB) {
+    for (int e = t; e < NG * kActGvCols; e += 256) {
+      const int g = e / kActGvCols, c = e - g * kActGvCols, n = n0 + c;
+      float sc = 0.0f, z = 8.0f;
+      if (n < N) {
+        sc = (float)__builtin_bit_cast(_Float16, scale_bits[(int64_t)g * N + n]);
+        if constexpr (!SYM) z = (float)((qzeros[(int64_t)g * (N / 8) + n / 8] >> (4 * (n % 8))) & 0xFu);
+      }
+      tz[e] = float2{sc, -(z * sc)};
+    }
+  } else {
+    for (int e = t; e < NG * kActGvCols; e += 256) {
+      const int g = e / kActGvCols, c = e - g * kActGvCols;
+      sl[e] = n0 + c < N ? scale_bits[(int64_t)g * N + n0 + c] : (uint16_t)0;
+    }
+    if constexpr (!SYM) {
+      for (int e = t; e < NG * (kActGvCols / 8); e += 256) {
+        const int g = e / (kActGvCols / 8), q = e - g * (kActGvCols / 8);
+        zl[e] = n0 + 8 * q < N ? qzeros[(int64_t)g * (N / 8) + n0 / 8 + q] : 0u;
+      }
     }
   }
   __syncthreads();
@@ -233,13 +250,24 @@ __global__ __launch_bounds__(256) void gptq_act_gemv_kernel(const uint32_t* __re
         xk[b][0] = bf16_lo(xv.x); xk[b][1] = bf16_hi(xv.x); xk[b][2] = bf16_lo(xv.y); xk[b][3] = bf16_hi(xv.y);
         xk[b][4] = bf16_lo(xv.z); xk[b][5] = bf16_hi(xv.z); xk[b][6] = bf16_lo(xv.w); xk[b][7] = bf16_hi(xv.w);
       }
+      uint32_t ev = wv[r] & 0x0F0F0F0Fu, od = (wv[r] >> 4) & 0x0F0F0F0Fu;
+      asm volatile("" : "+v"(ev), "+v"(od));   // codes convert from their bytes (v_cvt_f32_ubyte)
+      const float cf[8] = {(float)(ev & 0xFFu), (float)(od & 0xFFu), (float)((ev >> 8) & 0xFFu),
+                           (float)((od >> 8) & 0xFFu), (float)((ev >> 16) & 0xFFu), (float)((od >> 16) & 0xFFu),
+                           (float)(ev >> 24), (float)(od >> 24)};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t g = g8[i] < (uint32_t)NG ? g8[i] : (uint32_t)(NG - 1);   // clamped into range
-        const float sc = (float)__builtin_bit_cast(_Float16, sl[g * kActGvCols + lane]);
-        float z = 8.0f;
-        if constexpr (!SYM) z = (float)((zl[g * (kActGvCols / 8) + lane / 8] >> (4 * (lane % 8))) & 0xFu);
-        const float w = __builtin_fmaf((float)((wv[r] >> (4 * i)) & 0xFu), sc, -(z * sc));
+        float w;
+        if constexpr (TAB) {
+          const float2 sz = tz[g * kActGvCols + lane];
+          w = __builtin_fmaf(cf[i], sz.x, sz.y);
+        } else {
+          const float sc = (float)__builtin_bit_cast(_Float16, sl[g * kActGvCols + lane]);
+          float z = 8.0f;
+          if constexpr (!SYM) z = (float)((zl[g * (kActGvCols / 8) + lane / 8] >> (4 * (lane % 8))) & 0xFu);
+          w = __builtin_fmaf(cf[i], sc, -(z * sc));
+        }
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[b] = __builtin_fmaf(w, xk[b][i], acc[b]);
       }
@@ -430,11 +458,18 @@ static void act_gemv_b(int Bn, int group, const void* qw, const void* sc, const 
   const int S = gptq_act_gemv_splits(N, K), NG = (int)(K / group);
   const int64_t kb = (K + 511) / 512;
   const int kspan = (int)((kb + S - 1) / S) * 512;
-  const size_t lds = (size_t)NG * (kActGvCols * 2 + (SYM ? 0 : (kActGvCols / 8) * 4));
   const dim3 grid((unsigned)((N + kActGvCols - 1) / kActGvCols), (unsigned)S);
-  hipLaunchKernelGGL((gptq_act_gemv_kernel<SYM, B, TY>), grid, dim3(256), lds, st, (const uint32_t*)qw,
-                     (const uint16_t*)sc, (const uint32_t*)qz, g_idx, (int)N, (int)K, NG, kspan, (const uint16_t*)x,
-                     ldx, Bn, part, (TY*)y, ldy);
+  if (NG <= kActTabGroups) {
+    const size_t lds = (size_t)NG * kActGvCols * sizeof(float2);
+    hipLaunchKernelGGL((gptq_act_gemv_kernel<SYM, B, TY, true>), grid, dim3(256), lds, st, (const uint32_t*)qw,
+                       (const uint16_t*)sc, (const uint32_t*)qz, g_idx, (int)N, (int)K, NG, kspan,
+                       (const uint16_t*)x, ldx, Bn, part, (TY*)y, ldy);
+  } else {
+    const size_t lds = (size_t)NG * (kActGvCols * 2 + (SYM ? 0 : (kActGvCols / 8) * 4));
+    hipLaunchKernelGGL((gptq_act_gemv_kernel<SYM, B, TY, false>), grid, dim3(256), lds, st, (const uint32_t*)qw,
+                       (const uint16_t*)sc, (const uint32_t*)qz, g_idx, (int)N, (int)K, NG, kspan,
+                       (const uint16_t*)x, ldx, Bn, part, (TY*)y, ldy);
+  }
 }
 template <bool SYM, typename TY>
 static void act_gemv_s(int B, int group, const void* qw, const void* sc, const void* qz, const int32_t* g_idx,

@@ -536,9 +536,11 @@ def test_gemv_uintx_variants_parity(dt, group, nbits, n, k, B):
 
 @pytest.mark.parametrize("sym", [True, False])
 @pytest.mark.parametrize("group,n,k,B", [(128, 64, 512, 1), (32, 136, 1024, 3), (64, 1024, 4096, 8),
-                                          (128, 4096, 2048, 2)])
+                                          (128, 4096, 2048, 2), (32, 72, 4096, 2)])
 def test_gemv_gptq_act_order_parity(sym, group, n, k, B):
-    """GEMV on act-order GPTQ weights: each channel dequantized with its group g_idx[k]."""
+    """GEMV on act-order GPTQ weights: each channel dequantized with its group g_idx[k]
+    (up to 96 groups per row from a float32 (s, -z s) table, 128 groups from the packed
+    scales and zero points)."""
     W = workloads.mxfp4_weight(n, k, seed=550 + n + group)
     x = workloads.normal_weight(B, k, std=1.0, seed=551 + B)
     perm = np.random.default_rng(552 + k).permutation(k)
