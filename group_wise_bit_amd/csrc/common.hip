@@ -39,39 +39,47 @@ unsigned stream_blocks(uint64_t units) {
 // part[2*i], part[2*i+1] for i < nblocks -> out[0] = sum w^2, out[1] = sum (w-d)^2,
 // out[2] = 10 log10(out[0] / max(out[1], 1e-24)) (page export_gptq_cpu.py's
 // 20 log10(||w|| / max(||w - deq||, 1e-12)), squared inside the log). One block of
-// 1024 threads; each thread sums a fixed strided subset with four independent chains,
-// then a fixed tree: deterministic for a given partial count.
+// 1024 threads. The partials were just written by every XCD, so each load waits on the
+// Infinity Cache: a thread issues kFinBatch independent loads per round (one round for
+// up to 16384 partials) and sums them in index order, then the wavefronts reduce by a
+// fixed butterfly and wavefront 0 adds the 16 wavefront sums in order: deterministic for
+// a given partial count.
 constexpr int kFinThreads = 1024;
+constexpr int kFinBatch = 16;
 __global__ __launch_bounds__(kFinThreads) void err_finalize_kernel(const double2* __restrict__ part,
                                                                    unsigned nblocks, double* __restrict__ out) {
-  __shared__ double sa[kFinThreads], sb[kFinThreads];
-  double a[4] = {0.0, 0.0, 0.0, 0.0}, b[4] = {0.0, 0.0, 0.0, 0.0};
-  unsigned i = threadIdx.x;
-  for (; i + 3 * kFinThreads < nblocks; i += 4 * kFinThreads) {
+  __shared__ double sa[kFinThreads / 64], sb[kFinThreads / 64];
+  double a = 0.0, b = 0.0;
+  for (unsigned base = 0; base < nblocks; base += kFinBatch * kFinThreads) {
+    double2 v[kFinBatch];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const double2 v = part[i + j * kFinThreads];
-      a[j] += v.x;
-      b[j] += v.y;
+    for (int j = 0; j < kFinBatch; ++j) {
+      const unsigned k = base + j * kFinThreads + threadIdx.x;
+      v[j] = k < nblocks ? part[k] : double2{0.0, 0.0};
+    }
+#pragma unroll
+    for (int j = 0; j < kFinBatch; ++j) {
+      a += v[j].x;
+      b += v[j].y;
     }
   }
-  for (; i < nblocks; i += kFinThreads) {
-    const double2 v = part[i];
-    a[0] += v.x;
-    b[0] += v.y;
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) {
+    a += __shfl_xor(a, m);
+    b += __shfl_xor(b, m);
   }
-  sa[threadIdx.x] = (a[0] + a[1]) + (a[2] + a[3]);
-  sb[threadIdx.x] = (b[0] + b[1]) + (b[2] + b[3]);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sa[w] = a;
+    sb[w] = b;
+  }
   __syncthreads();
-  for (int s = kFinThreads / 2; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) {
-      sa[threadIdx.x] += sa[threadIdx.x + s];
-      sb[threadIdx.x] += sb[threadIdx.x + s];
-    }
-    __syncthreads();
-  }
   if (threadIdx.x == 0) {
-    const double w2 = sa[0], e2 = sb[0];
+    double w2 = 0.0, e2 = 0.0;
+    for (int i = 0; i < kFinThreads / 64; ++i) {
+      w2 += sa[i];
+      e2 += sb[i];
+    }
     out[0] = w2;
     out[1] = e2;
     out[2] = w2 == 0.0 ? -__builtin_inf() : 10.0 * log10(w2 / fmax(e2, 1e-24));

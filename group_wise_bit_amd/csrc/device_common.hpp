@@ -167,25 +167,32 @@ __device__ __forceinline__ void acc_err8(const float* x, const float* d, double&
 }
 
 // ---------------------------------------------------------------- error sums
-// Block-wide sum of two doubles; thread 0 writes them to part[2*blockIdx.x].
-// Fixed tree order, so the result is deterministic for a given launch shape.
+// Block-wide sum of two doubles; thread 0 writes them to part[2*blockIdx.x]. A fixed
+// butterfly inside each wavefront, then thread 0 adds the wavefront sums in order, so
+// the result is deterministic for a given launch shape.
 template <int THREADS>
 __device__ __forceinline__ void block_sum2_store(double a, double b, double* part) {
-  __shared__ double sa[THREADS], sb[THREADS];
-  sa[threadIdx.x] = a;
-  sb[threadIdx.x] = b;
-  __syncthreads();
+  static_assert(THREADS % 64 == 0 && THREADS <= 1024, "whole wavefronts");
+  __shared__ double sa[THREADS / 64], sb[THREADS / 64];
 #pragma unroll
-  for (int s = THREADS / 2; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) {
-      sa[threadIdx.x] += sa[threadIdx.x + s];
-      sb[threadIdx.x] += sb[threadIdx.x + s];
-    }
-    __syncthreads();
+  for (int m = 32; m > 0; m >>= 1) {
+    a += __shfl_xor(a, m);
+    b += __shfl_xor(b, m);
   }
+  if ((threadIdx.x & 63) == 0) {
+    sa[threadIdx.x >> 6] = a;
+    sb[threadIdx.x >> 6] = b;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    part[2 * blockIdx.x] = sa[0];
-    part[2 * blockIdx.x + 1] = sb[0];
+    double ta = sa[0], tb = sb[0];
+#pragma unroll
+    for (int i = 1; i < THREADS / 64; ++i) {
+      ta += sa[i];
+      tb += sb[i];
+    }
+    part[2 * blockIdx.x] = ta;
+    part[2 * blockIdx.x + 1] = tb;
   }
 }
 
