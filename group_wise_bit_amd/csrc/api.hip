@@ -386,13 +386,31 @@ int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t
   return hip_check("fold launch");
 }
 
-static size_t gemv_workspace(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
-  // the K-split partial sums (none with a single split)
+// Batches that the matrix-core tile kernels of gwb_gemm take faster than the GEMV
+// kernels: GPTQ with groups in index order from 2 rows, MXFP4 from 5 (where the GEMV
+// runs its 8-row instance), when the shape fits the tile (N % 8 == 0, K % 128 == 0).
+static bool gemv_shape_via_gemm(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
+  if (N % 8 || K % 128 || B * K >= kMaxElems) return false;
+  if (sp->format == GWB_GPTQ_SYM || sp->format == GWB_GPTQ_ASYM) return B >= 2;
+  return is_mxfp4(sp->format) && B >= 5;
+}
+
+// The GEMV kernels' K-split partial sums (none with a single split).
+static size_t gemv_kernel_workspace(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
   int S = 0;
   if (sp->format == GWB_GPTQ_SYM || sp->format == GWB_GPTQ_ASYM) S = gwb::gptq_gemv_splits(N, K);
   if (is_act(sp->format)) S = gwb::gptq_act_gemv_splits(N, K);
   if (sp->format == GWB_UINTX) S = gwb::uintx_gemv_splits(K);
   return S > 1 ? (size_t)S * (size_t)B * (size_t)N * sizeof(float) : 0;
+}
+
+// Enough for either path: the tile path is taken only when the buffers' alignment
+// allows it, which the size query cannot know.
+static size_t gemv_workspace(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
+  const size_t a = gemv_kernel_workspace(sp, N, K, B);
+  if (!gemv_shape_via_gemm(sp, N, K, B)) return a;
+  const size_t b = gwb::gemm_workspace_bytes(!is_mxfp4(sp->format), sp->group, B, N, K);
+  return a > b ? a : b;
 }
 
 static int check_gemv(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
@@ -427,7 +445,14 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
     return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (need && !aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
-  if (is_mxfp4(spec->format))
+  const bool tiles = gemv_shape_via_gemm(spec, N, K, B) && aligned16(y) && ldy % 8 == 0 && B * ldx < kMaxElems &&
+                     aligned16(w->codes) && aligned16(w->scales);
+  if (tiles && is_mxfp4(spec->format))
+    gwb::launch_mxfp4_gemm(w->codes, w->scales, N, K, x, B, ldx, y, y_dtype, ldy, workspace, st);
+  else if (tiles)
+    gwb::launch_gptq_gemm(spec->format == GWB_GPTQ_SYM, spec->group, w->codes, w->scales, w->zeros, N, K, x, B, ldx,
+                          y, y_dtype, ldy, workspace, st);
+  else if (is_mxfp4(spec->format))
     gwb::launch_mxfp4_gemv((int)B, w->codes, w->scales, N, K, x, ldx, y, y_dtype, ldy, st);
   else if (is_act(spec->format))
     gwb::launch_gptq_act_gemv(is_gptq_sym(spec->format), spec->group, (int)B, w->codes, w->scales, w->zeros,

@@ -416,12 +416,18 @@ __global__ __launch_bounds__(256, 2) void mxfp4_gemm_kernel(const uint16_t* __re
 // 16-row granularity of the matrix-core tiles: small M takes 16- or 32-row blocks
 // rather than computing padding rows.
 static int gemm_small_mt(int64_t M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+// K splits for M <= 64: enough workgroups for two per compute unit (512 with T tiles),
+// each split at least 2 stages; up to 4 splits always, up to 16 while the partials
+// (S M N float32, written and read back) stay within a quarter of the packed weight
+// (N K / 2 bytes), i.e. S <= K / (32 M).
 static int gemm_splits(int64_t M, int64_t N, int64_t K) {
   const int64_t rows = 16 * gemm_small_mt(M);
   const int64_t T = ((M + rows - 1) / rows) * ((N + kGmBN - 1) / kGmBN), nst = K / kGmBK;
   if (M > 64 || T == 0) return 1;
   int64_t S = (512 + T - 1) / T;
-  if (S > 4) S = 4;
+  const int64_t cap = K / (32 * M) > 4 ? K / (32 * M) : 4;
+  if (S > cap) S = cap;
+  if (S > 16) S = 16;
   if (S > nst / 2) S = nst / 2;
   return S < 1 ? 1 : (int)S;
 }

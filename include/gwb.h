@@ -233,11 +233,14 @@ int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t
  *            w->g_idx (required)
  *   x        device bf16 [B, K], row stride ldx (multiple of 8), 16-byte aligned; 1 <= B <= 8
  *   y        device [B, N] of y_dtype (GWB_F32 or GWB_BF16, RNE), row stride ldy
- *   workspace at least gwb_gemv_workspace bytes (GPTQ and uintx: K-split partial sums;
- *            MXFP4: 0)
- * Products of dequantized values and activations are exact in float32; sums are float32
- * in a fixed order (deterministic for a given shape; error bounded by the float32
- * accumulation).                                                                    */
+ *   workspace at least gwb_gemv_workspace bytes (K-split partial sums of either path,
+ *            the tile path's group sums; none for MXFP4 below 5 rows)
+ * Paths: GPTQ with groups in index order at B >= 2 and MXFP4 at B >= 5 run gwb_gemm's
+ * matrix-core tiles (and its numerics) when N % 8 == 0, K % 128 == 0, y and its rows
+ * are 16-byte aligned (ldy % 8 == 0) and codes and scales are 16-byte aligned; every
+ * other call runs the GEMV kernels: products of dequantized values and activations
+ * exact in float32, float32 sums in a fixed order. Both are deterministic for a given
+ * shape and path; the error is bounded by the float32 accumulation.                */
 int gwb_gemv_workspace(const gwb_qspec* spec, int64_t N, int64_t K, int64_t B, size_t* bytes);
 int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K, const void* x, int64_t B,
              int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,

@@ -104,10 +104,11 @@ def test_gemm_one_hot_reads_weights_exactly(fmt, group):
 
 
 @pytest.mark.parametrize("fmt,group", [("gptq_sym", 128), ("gptq_asym", 32), ("mxfp4", None)])
-@pytest.mark.parametrize("M,k", [(8, 2048), (48, 640), (16, 768)])
+@pytest.mark.parametrize("M,k", [(8, 2048), (48, 640), (16, 768), (8, 4096)])
 def test_gemm_k_split_parity(fmt, group, M, k):
-    """Small M splits K (2 to 4 splits, also uneven ones: 5 stages over 2 splits); the
-    float32 partials are summed in split order. Same bounds; one-hot rows stay exact."""
+    """Small M splits K (264 columns: 2, 3, 8 and 16 splits, also uneven ones: 5 stages
+    over 2 splits); the float32 partials are summed in split order. Same bounds; one-hot
+    rows stay exact."""
     n = 264
     W = workloads.mxfp4_weight(n, k, seed=670 + M)
     x = workloads.normal_weight(M, k, std=1.0, seed=671 + M)

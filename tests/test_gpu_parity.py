@@ -465,22 +465,52 @@ def _gptq_bound(o, x, group, sym, K):
     return U32 * (group + K // group + 40) * (np.abs(x.astype(np.float64)) @ w.reshape(K, -1))
 
 
+def _gemv_tiles(fmt, n, k, B):
+    """gwb_gemv hands GPTQ (index-order groups) batches of 2+ rows and MXFP4 batches of
+    5+ to the GEMM tile kernels when N % 8 == 0 and K % 128 == 0 and y's rows are
+    16-byte aligned (every output here with ldy = N)."""
+    if n % 8 or k % 128:
+        return False
+    return B >= 2 if fmt in ("gptq_sym", "gptq_asym") else (fmt == "mxfp4" and B >= 5)
+
+
+def _gemm_gptq_bound(o, x, group, K):
+    """The tile kernels' bound (per group T = sum x (128 + c), v = T - (128 + z) Sx with
+    the float64 group sum Sx rounded once): u (G + K/G + 8) 143 sum_k s |x|."""
+    s = np.abs(np.asarray(o["scales"], np.float16).astype(np.float64))
+    return U32 * (group + K // group + 8) * 143.0 * (np.abs(x.astype(np.float64)) @ np.repeat(s, group, axis=0))
+
+
+def _strided_out(B, n, ydt):
+    """y as a [B, n] view with row stride n + 4: rows not 16-byte aligned, so gwb_gemv
+    keeps its own kernels at every batch."""
+    return torch.zeros(B, n + 4, dtype=ydt, device=DEV)[:, :n]
+
+
 @pytest.mark.parametrize("fmt", ["gptq_sym", "gptq_asym"])
 @pytest.mark.parametrize("group", [32, 64, 128])
-@pytest.mark.parametrize("n,k,B", [(256, 512, 1), (72, 384, 3), (520, 1664, 8), (264, 640, 2)])
+@pytest.mark.parametrize("n,k,B", [(256, 512, 1), (72, 384, 3), (520, 1664, 8), (264, 640, 2), (136, 576, 4)])
 def test_gemv_gptq_parity(fmt, group, n, k, B):
+    """Both paths: the GEMV kernels (B = 1, K % 128 != 0, or unaligned y rows) within the
+    GEMV bound, the GEMM tiles (B >= 2) within theirs."""
+    if k % group:
+        pytest.skip("group does not divide K")
     W = workloads.mxfp4_weight(n, k, seed=500 + n + group)
     x = workloads.normal_weight(B, k, std=1.0, seed=501 + B)
     q = gwb.quantize(W.to(DEV), fmt, group=group)
     o = (ogq.quantize_sym if fmt == "gptq_sym" else ogq.quantize_asym)(W.float().numpy(), group)
     deq = ogv.dequantized(fmt, o, n, k, group=group)
-    ref = ogv.gemv(deq, x.float().numpy())
-    bound = _gptq_bound(o, x.float().numpy(), group, fmt == "gptq_sym", k)
+    xf = x.float().numpy()
+    ref = ogv.gemv(deq, xf)
+    gemv_bound = _gptq_bound(o, xf, group, fmt == "gptq_sym", k)
+    bound = _gemm_gptq_bound(o, xf, group, k) if _gemv_tiles(fmt, n, k, B) else gemv_bound
     for ydt in (torch.float32, torch.bfloat16):
         _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ref, bound, ydt)
+        _gemv_check(gwb.gemv(q, x.to(DEV), out=_strided_out(B, n, ydt)), ref, gemv_bound, ydt)
 
 
-@pytest.mark.parametrize("n,k,B", [(64, 512, 1), (33, 96, 3), (40, 4096, 2), (17, 2080, 8), (300, 2048, 5)])
+@pytest.mark.parametrize("n,k,B", [(64, 512, 1), (33, 96, 3), (40, 4096, 2), (17, 2080, 8), (300, 2048, 5),
+                                   (264, 2048, 8), (72, 640, 6)])
 def test_gemv_mxfp4_parity(n, k, B):
     W = workloads.mxfp4_weight(n, k, seed=510 + n)
     x = workloads.normal_weight(B, k, std=1.0, seed=511 + B)
@@ -489,9 +519,12 @@ def test_gemv_mxfp4_parity(n, k, B):
     deq = omx.dequantize(packed, e8, k)
     xf = x.float().numpy()
     ref = ogv.gemv(deq, xf)
-    bound = U32 * (32 + k // 2048 + 40) * ogv.abs_gemv(deq, xf)
+    gemv_bound = U32 * (32 + k // 2048 + 40) * ogv.abs_gemv(deq, xf)
+    # the tiles' products are exact too; the matrix cores' float32 sums: u (K + 8) sum |w x|
+    bound = U32 * (k + 8) * ogv.abs_gemv(deq, xf) if _gemv_tiles("mxfp4", n, k, B) else gemv_bound
     for ydt in (torch.float32, torch.bfloat16):
         _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ref, bound, ydt)
+        _gemv_check(gwb.gemv(q, x.to(DEV), out=_strided_out(B, n, ydt)), ref, gemv_bound, ydt)
 
 
 @pytest.mark.parametrize("nbits", [2, 3, 4, 5, 6, 7])
@@ -573,13 +606,14 @@ def test_gemv_uintx_config_3072x12288():
 
 def test_gemv_gptq_split_choice_sampled():
     """65536 x 1024 GPTQ asym g64: 256 column tiles give two K splits (partials and the
-    second pass); sampled output rows against the oracle."""
+    second pass) in the GEMV kernel (kept by unaligned y rows); sampled output rows
+    against the oracle."""
     N_, K_ = 65536, 1024
     W = workloads.normal_weight(N_, K_, seed=523)
     x = workloads.normal_weight(3, K_, std=1.0, seed=524)
     q = gwb.quantize(W.to(DEV), "gptq_asym", group=64)
-    assert gwb.gemv_workspace_bytes(q, 3) == 2 * 3 * N_ * 4
-    y = _np(gwb.gemv(q, x.to(DEV))).astype(np.float64)
+    assert gwb.gemv_workspace_bytes(q, 3) >= 2 * 3 * N_ * 4
+    y = _np(gwb.gemv(q, x.to(DEV), out=_strided_out(3, N_, torch.float32))).astype(np.float64)
     rows = np.sort(np.random.default_rng(525).choice(N_ // 8, 24, replace=False)) * 8
     ns = (rows[:, None] + np.arange(8)[None, :]).reshape(-1)
     xf = x.float().numpy()
