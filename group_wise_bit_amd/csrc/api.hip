@@ -400,7 +400,7 @@ static size_t gemv_kernel_workspace(const gwb_qspec* sp, int64_t N, int64_t K, i
   int S = 0;
   if (sp->format == GWB_GPTQ_SYM || sp->format == GWB_GPTQ_ASYM) S = gwb::gptq_gemv_splits(N, K);
   if (is_act(sp->format)) S = gwb::gptq_act_gemv_splits(N, K);
-  if (sp->format == GWB_UINTX) S = gwb::uintx_gemv_splits(K);
+  if (sp->format == GWB_UINTX) S = gwb::uintx_gemv_splits(K, (int)B);
   return S > 1 ? (size_t)S * (size_t)B * (size_t)N * sizeof(float) : 0;
 }
 

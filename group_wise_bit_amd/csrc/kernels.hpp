@@ -155,7 +155,7 @@ void launch_mxfp4_gemm(const void* packed, const void* e8m0, int64_t N, int64_t 
 // uintx (uintx.hip): N % 8 == 0 and K % 512 == 0; with more than one split, part holds
 // splits * B * N floats
 bool uintx_gemv_supported(int64_t N, int64_t K);
-int uintx_gemv_splits(int64_t K);
+int uintx_gemv_splits(int64_t K, int B);
 void launch_uintx_gemv(int nbits, int32_t dt, int group, int B, const void* packed, const void* scales,
                        const void* zeros, int64_t N, int64_t K, const void* x, int64_t ldx, void* y, int32_t y_dtype,
                        int64_t ldy, float* part, hipStream_t st);

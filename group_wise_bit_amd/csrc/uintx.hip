@@ -71,7 +71,7 @@ void launch_uintx_err(int nbits, int32_t dt, int group, const void* W, int64_t N
 }
 
 // ------------------------------------------------------------------ decode GEMV
-int uintx_gemv_splits(int64_t K) { return (int)(K % 2048 == 0 ? K / 2048 : K / 512); }
+int uintx_gemv_splits(int64_t K, int B) { return (int)(K / (512 * ux_gemv_chunks(K, B))); }
 
 bool uintx_gemv_supported(int64_t N, int64_t K) { return N % 8 == 0 && K % 512 == 0; }
 
@@ -79,7 +79,7 @@ void launch_uintx_gemv(int nbits, int32_t dt, int group, int B, const void* pack
                        const void* zeros, int64_t N, int64_t K, const void* x, int64_t ldx, void* y, int32_t y_dtype,
                        int64_t ldy, float* part, hipStream_t st) {
   // one split: each row's sum is complete in one wavefront and goes straight to y
-  const int S = uintx_gemv_splits(K);
+  const int S = uintx_gemv_splits(K, B);
   const GemvOut out{part, y, ldy, S > 1 ? GemvOut::kPart : (y_dtype == kBF16 ? GemvOut::kBF16 : GemvOut::kF32)};
   if (dt == kBF16 && group == 64) ux_tiled_gemv_entry<kBF16, 64>(nbits, B, packed, scales, zeros, N, K, x, ldx, out, st);
   else if (dt == kBF16) uintx_tiled_gemv_bf16(nbits, group, B, packed, scales, zeros, N, K, x, ldx, out, st);

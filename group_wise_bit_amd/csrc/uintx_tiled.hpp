@@ -320,7 +320,9 @@ __global__ __launch_bounds__(256) void uintx_dequant_tiled(const uint8_t* __rest
 // With N % 8 == 0 and K % 512 == 0, position p of segment j is row j * N/8 + p / K,
 // column p % K: a lane's 8 positions of the 8 segments share 8 activation columns and feed
 // 8 output rows. A wavefront takes CH consecutive 512-position chunks of one row (CH = 4
-// when K % 2048 == 0), so each lane sums 64 * CH weights per row before one transposed
+// when K % 2048 == 0 for up to 4 activation rows, 2 when K % 1024 == 0 for more, else 1:
+// the chunks' activations stay in registers, B x CH x 16 bytes per lane, and 8 rows of 4
+// chunks left one wavefront per SIMD), so each lane sums 64 * CH weights per row before one transposed
 // reduction leaves lane j with row j's sum. The weight pairs meet the activation pairs in
 // v_dot2c_f32_bf16; each wavefront writes one partial per row, added over the
 // K / (512 CH) wavefronts of a row in order afterwards, or, when one wavefront covers the
@@ -345,6 +347,12 @@ __device__ __forceinline__ float ux_transposed_sum(float (&v)[8], int lane) {
   r += __shfl_xor(r, 16);
   r += __shfl_xor(r, 32);
   return r;
+}
+
+// 512-position chunks per wavefront (CH above) for B activation rows.
+inline int ux_gemv_chunks(int64_t K, int B) {
+  if (B <= 4) return K % 2048 == 0 ? 4 : 1;
+  return K % 1024 == 0 ? 2 : 1;
 }
 
 template <int NB, int DT, int G, int B, int CH>
@@ -545,7 +553,11 @@ void ux_gemv_b(int B, const void* packed, const void* scales, const void* zeros,
 template <int DT, int G, int NB>
 void ux_gemv_nb(int B, const void* packed, const void* scales, const void* zeros, int64_t N, int64_t K, const void* x,
                 int64_t ldx, GemvOut out, hipStream_t st) {
-  if (K % 2048 == 0) ux_gemv_b<DT, G, NB, 4>(B, packed, scales, zeros, N, K, x, ldx, out, st);
+  const int ch = ux_gemv_chunks(K, B);
+  if (ch == 4 && B == 1) ux_gemv_launch<DT, G, NB, 1, 4>(B, packed, scales, zeros, N, K, x, ldx, out, st);
+  else if (ch == 4 && B == 2) ux_gemv_launch<DT, G, NB, 2, 4>(B, packed, scales, zeros, N, K, x, ldx, out, st);
+  else if (ch == 4) ux_gemv_launch<DT, G, NB, 4, 4>(B, packed, scales, zeros, N, K, x, ldx, out, st);
+  else if (ch == 2) ux_gemv_launch<DT, G, NB, 8, 2>(B, packed, scales, zeros, N, K, x, ldx, out, st);
   else ux_gemv_b<DT, G, NB, 1>(B, packed, scales, zeros, N, K, x, ldx, out, st);
 }
 // The decode GEMV of one (dtype, group): N % 8 == 0, K % 512 == 0, B <= 8.

@@ -250,6 +250,10 @@ def test_gemv_sizes_and_validation():
     assert lib.gwb_gemv_workspace(ctypes.byref(sp_u), 64, 128, 1, ctypes.byref(ctypes.c_size_t())) == gwb.E_UNSUPPORTED
     assert lib.gwb_gemv_workspace(ctypes.byref(sp_u), 12, 512, 1, ctypes.byref(ctypes.c_size_t())) == gwb.E_UNSUPPORTED
     assert ws("uintx", 3072, 12288, 2) == (gwb.OK, 6 * 2 * 3072 * 4)             # 2048-column splits
+    assert ws("uintx", 3072, 12288, 4) == (gwb.OK, 6 * 4 * 3072 * 4)
+    assert ws("uintx", 3072, 12288, 8) == (gwb.OK, 12 * 8 * 3072 * 4)            # 1024 columns from 5 rows
+    assert ws("uintx", 3072, 11264, 8) == (gwb.OK, 11 * 8 * 3072 * 4)
+    assert ws("uintx", 3072, 11776, 8) == (gwb.OK, 23 * 8 * 3072 * 4)            # K % 1024 != 0: 512
     assert ws("uintx", 64, 1536, 1) == (gwb.OK, 3 * 64 * 4)                      # 512-column splits
     assert ws("uintx", 131072, 2048, 1) == (gwb.OK, 0)                           # one split: y directly
     for g, dt in [(32, gwb.BF16), (64, gwb.F16), (128, gwb.F32)]:                # every dtype and group
