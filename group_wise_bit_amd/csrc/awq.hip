@@ -31,6 +31,10 @@ constexpr int kRB = 4;                      // subsample rows a lane keeps
 constexpr int kTaskCols = 512;              // columns of a wavefront task (64 lanes x 8)
 constexpr int kTasksPerBlock = 4;           // one per wavefront
 constexpr unsigned kSearchGridCap = 4096;
+// Loads a thread issues before summing them in order: the table and partial reads come
+// from the previous kernel's output in the Infinity Cache, and one round of loads instead
+// of one per value keeps these small kernels from waiting on each load in turn.
+constexpr int kLoadBatch = 32;
 
 struct Alphas {
   double v[kMaxAlpha];
@@ -61,7 +65,17 @@ __global__ __launch_bounds__(kChunk) void awq_pow_kernel(const float* __restrict
                                                          double* __restrict__ pw, double* __restrict__ logs) {
   const int ai = blockIdx.y;
   double acc = 0.0;
-  for (int k = threadIdx.x; k < K; k += kChunk) acc += (double)fmaxf(a[k], 1e-8f);
+  for (int base = 0; base < K; base += kChunk * kLoadBatch) {   // k = t, t + 256, ... in order
+    float v[kLoadBatch];
+#pragma unroll
+    for (int j = 0; j < kLoadBatch; ++j) {
+      const int k = base + j * kChunk + threadIdx.x;
+      v[j] = a[min(k, K - 1)];                                    // loads without branches
+    }
+#pragma unroll
+    for (int j = 0; j < kLoadBatch; ++j)
+      if (base + j * kChunk + (int)threadIdx.x < K) acc += (double)fmaxf(v[j], 1e-8f);
+  }
   const double mean = block_sum<kChunk>(acc) / (double)K;
   const int k = blockIdx.x * kChunk + threadIdx.x;
   double lg = 0.0;
@@ -84,7 +98,14 @@ __global__ __launch_bounds__(kChunk) void awq_scale_kernel(const double* __restr
   float s;
   if (pw) {
     double lg = 0.0;
-    for (unsigned c = 0; c < gridDim.x; ++c) lg += logs[(int64_t)ai * gridDim.x + c];
+    for (unsigned c0 = 0; c0 < gridDim.x; c0 += kLoadBatch) {   // chunk order
+      double v[kLoadBatch];
+#pragma unroll
+      for (int j = 0; j < kLoadBatch; ++j) v[j] = logs[(int64_t)ai * gridDim.x + min(c0 + j, gridDim.x - 1)];
+#pragma unroll
+      for (int j = 0; j < kLoadBatch; ++j)
+        if (c0 + j < gridDim.x) lg += v[j];
+    }
     s = (float)(pw[(int64_t)ai * K + k] / exp(lg / (double)K));
     s_table[(int64_t)ai * K + k] = s;
   } else {
@@ -195,7 +216,18 @@ __global__ __launch_bounds__(1024) void awq_finalize_kernel(const double* __rest
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   if (wave < n_alpha) {
     double acc = 0.0;
-    for (unsigned b = lane; b < nblocks; b += 64) acc += part[(int64_t)b * n_alpha + wave];
+    // b = lane, lane + 64, ... in order; half batches (1024 threads leave 128 registers)
+    for (unsigned b0 = lane; b0 < nblocks; b0 += 64 * (kLoadBatch / 2)) {
+      double v[kLoadBatch / 2];
+#pragma unroll
+      for (int j = 0; j < kLoadBatch / 2; ++j) {
+        const unsigned b = b0 + 64 * j;
+        v[j] = part[(int64_t)min(b, nblocks - 1) * n_alpha + wave];
+      }
+#pragma unroll
+      for (int j = 0; j < kLoadBatch / 2; ++j)
+        if (b0 + 64 * j < nblocks) acc += v[j];
+    }
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (lane == 0) {
       e[wave] = acc;
