@@ -767,26 +767,40 @@ def test_full_fold_34816x5120_sampled():
     assert np.array_equal(_np(r["mxfp4"]["e8m0"][rows]), e8)
 
 
-def test_full_gemv_lm_head_131072x2048_sampled():
-    """The page's lm_head decode read: GPTQ sym g128 and MXFP4 of a 131072 x 2048
-    weight, one activation row; checked on sampled output rows against the oracle."""
+@pytest.mark.parametrize("fmt,B", [("gptq_sym", 1), ("gptq_sym", 8), ("mxfp4", 1), ("mxfp4", 8), ("uintx", 1),
+                                   ("gptq_sym_act", 1)])
+def test_full_gemv_lm_head_131072x2048_sampled(fmt, B):
+    """The page's lm_head decode read, 131072 x 2048, in the launch shapes the benchmark
+    times (B = 1: the GEMV kernels; B = 8: GPTQ and MXFP4 on the GEMM tiles); checked on
+    sampled output rows (whole qzeros words) against the oracle."""
     N_, K_ = 131072, 2048
     W = workloads.normal_weight(N_, K_, seed=520)
-    x = workloads.normal_weight(1, K_, std=1.0, seed=521)
+    x = workloads.normal_weight(B, K_, std=1.0, seed=521)
     Wd, xd = W.to(DEV), x.to(DEV)
     rows = np.sort(np.random.default_rng(522).choice(N_ // 8, 32, replace=False)) * 8
-    ns = (rows[:, None] + np.arange(8)[None, :]).reshape(-1)            # whole qzeros words
-    xf = x.float().numpy()
-    q = gwb.quantize(Wd, "gptq_sym", group=128)
+    ns = (rows[:, None] + np.arange(8)[None, :]).reshape(-1)
+    Ws, xf = W[ns].float().numpy(), x.float().numpy()
+    if fmt == "gptq_sym":
+        q = gwb.quantize(Wd, fmt, group=128)
+        o = ogq.quantize_sym(Ws, 128)
+        deq = ogv.dequantized(fmt, o, len(ns), K_, group=128)
+        bound = _gemm_gptq_bound(o, xf, 128, K_) if B > 1 else _gptq_bound(o, xf, 128, True, K_)
+    elif fmt == "mxfp4":
+        q = gwb.quantize(Wd, fmt)
+        deq = omx.dequantize(*omx.quantize(Ws), K_)
+        bound = U32 * ((K_ + 8) if B > 1 else (32 + K_ // 2048 + 40)) * ogv.abs_gemv(deq, xf)
+    elif fmt == "uintx":
+        q = gwb.quantize(Wd, fmt, nbits=4)
+        deq = ogv.dequantized("uintx", oux.quantize(Ws, 4), len(ns), K_, nbits=4)
+        bound = U32 * (K_ // 512 + 40) * ogv.abs_gemv(deq, xf)
+    else:
+        perm = np.random.default_rng(526).permutation(K_)
+        q = gwb.quantize(Wd, fmt, group=128, perm=torch.from_numpy(perm.astype(np.int32)).to(DEV))
+        o = ogq.quantize_act_order(Ws, 128, True, perm)
+        deq = ogq.dequantize(o["qweight"], o["scales"], o["qzeros"], 128, True, g_idx=o["g_idx"])
+        bound = U32 * (K_ // 4 + 48) * ogv.abs_gemv(deq, xf)
     y = _np(gwb.gemv(q, xd)).astype(np.float64)
-    o = ogq.quantize_sym(W[ns].float().numpy(), 128)
-    deq = ogv.dequantized("gptq_sym", o, len(ns), K_, group=128)
-    _gemv_check(torch.from_numpy(y[:, ns]), ogv.gemv(deq, xf), _gptq_bound(o, xf, 128, True, K_), torch.float32)
-    qm = gwb.quantize(Wd, "mxfp4")
-    ym = _np(gwb.gemv(qm, xd)).astype(np.float64)
-    packed, e8 = omx.quantize(W[ns].float().numpy())
-    dm = omx.dequantize(packed, e8, K_)
-    _gemv_check(torch.from_numpy(ym[:, ns]), ogv.gemv(dm, xf), U32 * 73 * ogv.abs_gemv(dm, xf), torch.float32)
+    _gemv_check(torch.from_numpy(y[:, ns]), ogv.gemv(deq, xf), bound, torch.float32)
 
 
 # ------------------------------------------------------------------ empty shapes
