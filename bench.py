@@ -212,6 +212,15 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
         ("gemv.gptq_sym_act_g128.lm_head_b1", hk / 2 + hk / 128 * 2 + 4 * HK + 2 * HK + 4 * HN,
          cycle([gwb.prepare_gemv(q, xh, yh, None) for q in qa])),
     ]
+    # a decode batch of 8 rows (GPTQ and MXFP4 run on the GEMM tiles there)
+    x8 = workloads.normal_weight(8, HK, std=1.0, seed=527).to(dev)
+    y8 = torch.empty(8, HN, dtype=torch.float32, device=dev)
+    for tag, qs, per_w in (("gptq_sym_g128", qg, 0.5 + 2 / 128), ("mxfp4", qm, 0.5 + 1 / 32),
+                           ("uintx4_g64", qu, 0.5 + 3 / 64)):
+        nb = gwb.gemv_workspace_bytes(qs[0], 8)
+        ws8 = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+        gemv_cases.append((f"gemv.{tag}.lm_head_b8", hk * per_w + 8 * 2 * HK + 8 * 4 * HN,
+                           cycle([gwb.prepare_gemv(q, x8, y8, ws8) for q in qs])))
     # uintx variants at the uintx workload shape [3072, 12288], 4 bits: float16 and
     # float32 weights (group 64) and bf16 groups 32 and 128; enough copies cycled that
     # the weights exceed the Infinity Cache

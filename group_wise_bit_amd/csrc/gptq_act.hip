@@ -37,17 +37,21 @@ __device__ __forceinline__ uint32_t clamp_idx(int32_t v, uint32_t n) {
 // Staging loops issue their loads in batches of kBatch before storing any of them, so a
 // thread waits for one memory round trip per batch rather than one per element.
 constexpr int kBatch = 8;
+template <int NT = 256>
 __device__ __forceinline__ void stage16(U4* __restrict__ dst, const U4* __restrict__ src, int n) {
-  for (int c0 = threadIdx.x; c0 < n; c0 += 256 * kBatch) {
+  for (int c0 = threadIdx.x; c0 < n; c0 += NT * kBatch) {
     U4 v[kBatch];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q)
-      if (c0 + 256 * q < n) v[q] = ld16(src + c0 + 256 * q);
+      if (c0 + NT * q < n) v[q] = ld16(src + c0 + NT * q);
 #pragma unroll
     for (int q = 0; q < kBatch; ++q)
-      if (c0 + 256 * q < n) dst[c0 + 256 * q] = v[q];
+      if (c0 + NT * q < n) dst[c0 + NT * q] = v[q];
   }
 }
+// Threads of a parameters block: one weight row each, so 128 threads let a CU hold 16
+// rows in LDS (160 KB at 10 KB a row) and keep more of them loading while others reduce.
+constexpr int kParamThreads = 128;
 }  // namespace
 
 // g_idx[perm[j]] = j / G
@@ -68,7 +72,7 @@ template <> __device__ __forceinline__ float act_widen<float>(float v) { return 
 // the row, so LDS bank conflicts bound this kernel. Sym: s = max(amax / 8, 1e-9); asym:
 // s = max(max - min, 1e-9) / 15, zp = clamp(rint(-min / s), 0, 15).
 template <bool SYM, int G, typename TW>
-__global__ __launch_bounds__(256) void act_order_params_kernel(const TW* __restrict__ W, int64_t ldw,
+__global__ __launch_bounds__(kParamThreads) void act_order_params_kernel(const TW* __restrict__ W, int64_t ldw,
                                                                const int32_t* __restrict__ perm, int N, int K,
                                                                float* __restrict__ ps, uint8_t* __restrict__ pz) {
   constexpr int LG = G / 8;                     // lanes per group
@@ -76,9 +80,9 @@ __global__ __launch_bounds__(256) void act_order_params_kernel(const TW* __restr
   extern __shared__ uint32_t lds[];
   TW* row = reinterpret_cast<TW*>(lds);         // [K]
   const int t = threadIdx.x, NG = K / G, i = t % LG, n = blockIdx.x;
-  stage16(reinterpret_cast<U4*>(row), reinterpret_cast<const U4*>(W + (int64_t)n * ldw), K / E16);
+  stage16<kParamThreads>(reinterpret_cast<U4*>(row), reinterpret_cast<const U4*>(W + (int64_t)n * ldw), K / E16);
   __syncthreads();
-  for (int g = t / LG; g < NG; g += 256 / LG) {     // the same for the LG lanes of a group
+  for (int g = t / LG; g < NG; g += kParamThreads / LG) {     // the same for the LG lanes of a group
     const int j = g * G + 8 * i;
     const U4 pa = ld16(perm + j), pb = ld16(perm + j + 4);
     const uint32_t pj[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
@@ -323,7 +327,7 @@ size_t gptq_act_workspace_bytes(int64_t N, int64_t K, int group) {
 template <bool SYM, int G, typename TW>
 static void act_params_launch(const void* W, int64_t N, int64_t K, int64_t ldw, const int32_t* perm, float* ps,
                               uint8_t* pz, hipStream_t st) {
-  hipLaunchKernelGGL((act_order_params_kernel<SYM, G, TW>), dim3((unsigned)N), dim3(256), (size_t)K * sizeof(TW), st,
+  hipLaunchKernelGGL((act_order_params_kernel<SYM, G, TW>), dim3((unsigned)N), dim3(kParamThreads), (size_t)K * sizeof(TW), st,
                      (const TW*)W, ldw, perm, (int)N, (int)K, ps, pz);
 }
 template <bool SYM, typename TW>
