@@ -394,6 +394,15 @@ static bool gemv_shape_via_gemm(const gwb_qspec* sp, int64_t N, int64_t K, int64
   if (sp->format == GWB_GPTQ_SYM || sp->format == GWB_GPTQ_ASYM) return B >= 2;
   return is_mxfp4(sp->format) && B >= 5;
 }
+// bf16-weight uintx batches of 5+ rows on weights of 65536+ rows take gwb_gemm's uintx
+// tiles (measured: lm_head 131072 x 2048 at B = 8 105 -> 62 us; on narrower weights the
+// tiles' grid is too small and the GEMV stays faster).
+static bool gemm_uintx_shape(const gwb_qspec* sp, int64_t N, int64_t K) {
+  return sp->format == GWB_UINTX && sp->w_dtype == GWB_BF16 && N % 8 == 0 && K % 512 == 0;
+}
+static bool gemv_uintx_via_tiles(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
+  return gemm_uintx_shape(sp, N, K) && B >= 5 && N >= 65536 && B * K < kMaxElems;
+}
 
 // The GEMV kernels' K-split partial sums (none with a single split).
 static size_t gemv_kernel_workspace(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
@@ -408,6 +417,10 @@ static size_t gemv_kernel_workspace(const gwb_qspec* sp, int64_t N, int64_t K, i
 // allows it, which the size query cannot know.
 static size_t gemv_workspace(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
   const size_t a = gemv_kernel_workspace(sp, N, K, B);
+  if (gemv_uintx_via_tiles(sp, N, K, B)) {
+    const size_t b = gwb::uintx_gemm_workspace_bytes(B, N, K);
+    return a > b ? a : b;
+  }
   if (!gemv_shape_via_gemm(sp, N, K, B)) return a;
   const size_t b = gwb::gemm_workspace_bytes(!is_mxfp4(sp->format), sp->group, B, N, K);
   return a > b ? a : b;
@@ -447,7 +460,10 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
   hipStream_t st = (hipStream_t)stream;
   const bool tiles = gemv_shape_via_gemm(spec, N, K, B) && aligned16(y) && ldy % 8 == 0 && B * ldx < kMaxElems &&
                      aligned16(w->codes) && aligned16(w->scales);
-  if (tiles && is_mxfp4(spec->format))
+  if (gemv_uintx_via_tiles(spec, N, K, B) && aligned16(w->codes))
+    gwb::launch_uintx_gemm(spec->nbits, spec->group, w->codes, w->scales, w->zeros, N, K, x, B, ldx, y, y_dtype, ldy,
+                           workspace, st);
+  else if (tiles && is_mxfp4(spec->format))
     gwb::launch_mxfp4_gemm(w->codes, w->scales, N, K, x, B, ldx, y, y_dtype, ldy, workspace, st);
   else if (tiles)
     gwb::launch_gptq_gemm(spec->format == GWB_GPTQ_SYM, spec->group, w->codes, w->scales, w->zeros, N, K, x, B, ldx,
@@ -468,8 +484,10 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
 
 static int check_gemm(const gwb_qspec* sp, int64_t N, int64_t K, int64_t M) {
   if (int rc = check_spec(sp, N, K)) return rc;
-  if (sp->format != GWB_GPTQ_SYM && sp->format != GWB_GPTQ_ASYM && !is_mxfp4(sp->format))
-    return fail(GWB_E_UNSUPPORTED, "the GEMM takes GPTQ (sym, asym, groups in index order) and MXFP4 weights");
+  if (sp->format == GWB_UINTX && !gemm_uintx_shape(sp, N, K))
+    return fail(GWB_E_UNSUPPORTED, "the uintx GEMM takes bf16 weights with N %% 8 == 0 and K %% 512 == 0");
+  if (sp->format != GWB_GPTQ_SYM && sp->format != GWB_GPTQ_ASYM && !is_mxfp4(sp->format) && sp->format != GWB_UINTX)
+    return fail(GWB_E_UNSUPPORTED, "the GEMM takes GPTQ (sym, asym, groups in index order), MXFP4 and uintx weights");
   if (N % 8 || K % 128)
     return fail(GWB_E_UNSUPPORTED, "the GEMM needs N %% 8 == 0 and K %% 128 == 0, got N=%lld K=%lld", (long long)N,
                 (long long)K);
@@ -478,10 +496,15 @@ static int check_gemm(const gwb_qspec* sp, int64_t N, int64_t K, int64_t M) {
   return GWB_OK;
 }
 
+static size_t gemm_workspace(const gwb_qspec* sp, int64_t M, int64_t N, int64_t K) {
+  if (sp->format == GWB_UINTX) return gwb::uintx_gemm_workspace_bytes(M, N, K);
+  return gwb::gemm_workspace_bytes(!is_mxfp4(sp->format), sp->group, M, N, K);
+}
+
 int gwb_gemm_workspace(const gwb_qspec* spec, int64_t N, int64_t K, int64_t M, size_t* bytes) {
   if (!bytes) return fail(GWB_E_ARG, "bytes is NULL");
   if (int rc = check_gemm(spec, N, K, M)) return rc;
-  *bytes = gwb::gemm_workspace_bytes(!is_mxfp4(spec->format), spec->group, M, N, K);
+  *bytes = gemm_workspace(spec, M, N, K);
   return ok();
 }
 
@@ -500,12 +523,15 @@ int gwb_gemm(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
   if (int rc = check_tensors(spec, w)) return rc;
   if (!aligned16(w->codes) || !aligned16(w->scales))
     return fail(GWB_E_UNSUPPORTED, "the GEMM needs 16-byte aligned codes and scales");
-  const size_t need = gwb::gemm_workspace_bytes(!is_mxfp4(spec->format), spec->group, M, N, K);
+  const size_t need = gemm_workspace(spec, M, N, K);
   if (need && (!workspace || workspace_bytes < need))
     return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (need && !aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
-  if (is_mxfp4(spec->format))
+  if (spec->format == GWB_UINTX)
+    gwb::launch_uintx_gemm(spec->nbits, spec->group, w->codes, w->scales, w->zeros, N, K, x, M, ldx, y, y_dtype, ldy,
+                           workspace, st);
+  else if (is_mxfp4(spec->format))
     gwb::launch_mxfp4_gemm(w->codes, w->scales, N, K, x, M, ldx, y, y_dtype, ldy, workspace, st);
   else
     gwb::launch_gptq_gemm(spec->format == GWB_GPTQ_SYM, spec->group, w->codes, w->scales, w->zeros, N, K, x, M, ldx,

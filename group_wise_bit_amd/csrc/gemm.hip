@@ -33,6 +33,7 @@
 // load clamped (valid) data whose results are not stored.
 #include "kernels.hpp"
 #include "mxfp4_math.hpp"
+#include "uintx_layout.hpp"
 
 namespace gwb {
 
@@ -561,6 +562,194 @@ void launch_mxfp4_gemm(const void* packed, const void* e8m0, int64_t N, int64_t 
   else if (mt == 2) mxfp4_gemm_mt<2>(packed, e8m0, N, K, x, M, ldx, y, y_dtype, ldy, workspace, st);
   else if (mt == 4) mxfp4_gemm_mt<4>(packed, e8m0, N, K, x, M, ldx, y, y_dtype, ldy, workspace, st);
   else mxfp4_gemm_mt<8>(packed, e8m0, N, K, x, M, ldx, y, y_dtype, ldy, workspace, st);
+}
+
+// ------------------------------------------------------------------ uintx, bf16 weights
+// Decode batches on the tiled uintx layout (page uintx_quant.py, forward). The flattened
+// [N, K] weight is 8 segments of L1 = N K / 8 positions (segment t = rows t N/8 ..
+// (t+1) N/8 - 1, position p = (row - t N/8) K + k); a shard byte holds position p of
+// several segments (4-bit planes t & 3, nibble t >> 2; 2-bit planes t & 1, field t >> 1;
+// 1-bit: bit t), so a lane takes the same positions of all 8 segments and every byte it
+// loads serves all of them. Block: 16 activation rows x 64 positions-rows of each
+// segment; wavefront w owns position-rows r = r0 + 16w .. +15, and lane l (j = l % 16,
+// q = l / 16) feeds B column j of tile t (segment t) with row t N/8 + r0 + 16w + j over
+// k0 + 32q .. +31: the MXFP4 kernel's k assignment, so the activation tile and its
+// operand reads are shared with it. The B operands are the forward weights
+// bf16((q - zp) s): c s - zp s is exact in float32 and one conversion rounds it, so every
+// product with the bf16 activations is exact and the sums are float32. One 16-row tile
+// converts each weight once per 16 activation rows: a decode kernel.
+typedef __bf16 gm_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float gm_f32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kUxRows = 64;           // position-rows of each segment per block
+
+__device__ __forceinline__ uint32_t ux_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(gm_f32x2_t{a, b}, gm_bf16x2_t));
+}
+__device__ __forceinline__ uint32_t u4_word(const U4 (&v)[2], int i) {
+  const U4& u = v[i >> 2];
+  return (i & 3) == 0 ? u.x : (i & 3) == 1 ? u.y : (i & 3) == 2 ? u.z : u.w;
+}
+
+template <int NB, typename TY>
+__global__ __launch_bounds__(256, 2) void uintx_gemm_kernel(const uint16_t* __restrict__ x, int64_t ldx, int M,
+                                                           const uint8_t* __restrict__ packed,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const uint8_t* __restrict__ zeros, Shards sh, int R8,
+                                                           int K, int lg, TY* __restrict__ y, int64_t ldy, int gx,
+                                                           int gy, int S) {
+  using SB = ShardBits<NB>;
+  constexpr int P4 = SB::has4 ? 4 : 0, P2 = SB::has2 ? 2 : 0, P1 = SB::has1 ? 1 : 0, NP = P4 + P2 + P1;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][16 * 128];
+
+  const int T = gx * gy, split = (int)blockIdx.x / T, nst = K / kGmBK;
+  const int st0 = split * nst / S, st1 = (split + 1) * nst / S;
+  y += (int64_t)split * M * ldy;
+  int bx, by;
+  gemm_tile((int)blockIdx.x - split * T, gx, gy, bx, by);
+  const int lane = threadIdx.x & 63, j = lane & 15, q = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int m0 = bx * 16, r = by * kUxRows + wv * 16 + j;
+  const uint32_t L1 = (uint32_t)R8 * (uint32_t)K;
+  const uint32_t pos = (uint32_t)min(r, R8 - 1) * (uint32_t)K + 32 * q;   // + k0: this lane's 32 positions
+  uint32_t plane[NP];                    // byte offset of each shard plane in packed
+#pragma unroll
+  for (int i = 0; i < P4; ++i) plane[i] = (uint32_t)sh.base4 + i * L1;
+#pragma unroll
+  for (int i = 0; i < P2; ++i) plane[P4 + i] = (uint32_t)sh.base2 + i * L1;
+  if constexpr (P1 != 0) plane[P4 + P2] = (uint32_t)sh.base1;
+  int aoff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) aoff[s] = a_slot(j, 4 * q + s);
+  uint32_t aof[1];
+  a_offsets<1>(ldx, M, m0, wv, lane, aof);
+
+  U4 pb[NP][2];
+  uint32_t pq[8];                        // segment t's group: scale bits << 16 | zero point
+  auto fetch = [&](int k0, int buf) {
+    a_fetch<1>(aof, x + k0, As[buf], wv);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      pb[i][0] = ld16(packed + plane[i] + pos + k0);
+      pb[i][1] = ld16(packed + plane[i] + pos + k0 + 16);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t g = (t * L1 + pos + k0) >> lg;
+      pq[t] = ((uint32_t)scales[g] << 16) | zeros[g];
+    }
+  };
+
+  gm_f32x4_t acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = gm_f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  fetch(st0 * kGmBK, 0);
+  stage_barrier();
+  for (int st = st0; st < st1; ++st) {
+    const int buf = (st - st0) & 1;
+    U4 b8[NP][2];
+    uint32_t qp[8];
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      b8[i][0] = pb[i][0];
+      b8[i][1] = pb[i][1];
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qp[t] = pq[t];
+    if (st + 1 < st1) fetch((st + 1) * kGmBK, buf ^ 1);
+    const uint16_t* A = As[buf];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const U4 a = *reinterpret_cast<const U4*>(A + aoff[s]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float sc = __uint_as_float(qp[t] & 0xFFFF0000u), nzs = -((float)(qp[t] & 0xFFu) * sc);
+        uint32_t c[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int wi = 2 * s + h;                    // word of the lane's 32 bytes: k0 + 32q + 4 wi ..
+          uint32_t v = 0u;
+          if constexpr (SB::has4) v |= (u4_word(b8[t & 3], wi) >> (4 * (t >> 2))) & 0x0F0F0F0Fu;
+          if constexpr (SB::has2) v |= ((u4_word(b8[P4 + (t & 1)], wi) >> (2 * (t >> 1))) & 0x03030303u) << SB::off2;
+          if constexpr (SB::has1) v |= ((u4_word(b8[P4 + P2], wi) >> t) & 0x01010101u) << SB::off1;
+          c[h] = v;
+        }
+        asm volatile("" : "+v"(c[0]), "+v"(c[1]));   // codes convert from their bytes (v_cvt_f32_ubyte0..3)
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = __builtin_fmaf((float)((c[e >> 2] >> (8 * (e & 3))) & 0xFFu), sc, nzs);
+        const U4 b = U4{ux_pair(f[0], f[1]), ux_pair(f[2], f[3]), ux_pair(f[4], f[5]), ux_pair(f[6], f[7])};
+        acc[t] = mfma_bf16(a, b, acc[t]);
+      }
+    }
+    stage_barrier();
+  }
+  if (r >= R8) return;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 4 * q + i;
+      if (m >= M) continue;
+      TY* p = y + (int64_t)m * ldy + (int64_t)t * R8 + r;
+      if constexpr (sizeof(TY) == 4) *p = acc[t][i];
+      else *p = (TY)(__float_as_uint(round_bf16(acc[t][i])) >> 16);
+    }
+}
+
+// K splits toward 512 blocks (at most 32, each at least 2 stages, partials within a
+// quarter of the packed weight as for the GEMM).
+static int uintx_gemm_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t T = ((M + 15) / 16) * ((N / 8 + kUxRows - 1) / kUxRows), nst = K / kGmBK;
+  if (T == 0) return 1;
+  int64_t S = (512 + T - 1) / T;
+  const int64_t cap = K / (32 * M) > 4 ? K / (32 * M) : 4;
+  if (S > cap) S = cap;
+  if (S > 32) S = 32;
+  if (S > nst / 2) S = nst / 2;
+  return S < 1 ? 1 : (int)S;
+}
+size_t uintx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const int S = uintx_gemm_splits(M, N, K);
+  return S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+template <int NB, typename TY>
+static void uintx_gemm_go(const void* x, int64_t ldx, int M, const void* packed, const void* scales,
+                          const void* zeros, int64_t N, int64_t K, int lg, void* y, int64_t ldy, int S,
+                          hipStream_t st) {
+  const int R8 = (int)(N / 8);
+  const int gx = (M + 15) / 16, gy = (R8 + kUxRows - 1) / kUxRows;
+  hipLaunchKernelGGL((uintx_gemm_kernel<NB, TY>), dim3(gx * gy * S), dim3(256), 0, st, (const uint16_t*)x, ldx, M,
+                     (const uint8_t*)packed, (const uint16_t*)scales, (const uint8_t*)zeros, shards_of(NB, N * K),
+                     R8, (int)K, lg, (TY*)y, ldy, gx, gy, S);
+}
+template <int NB>
+static void uintx_gemm_nb(const void* x, int64_t ldx, int64_t M, const void* packed, const void* scales,
+                          const void* zeros, int64_t N, int64_t K, int lg, void* y, int32_t y_dtype, int64_t ldy,
+                          void* workspace, hipStream_t st) {
+  const int S = uintx_gemm_splits(M, N, K);
+  if (S > 1) {
+    uintx_gemm_go<NB, float>(x, ldx, (int)M, packed, scales, zeros, N, K, lg, workspace, N, S, st);
+    gemm_reduce((const float*)workspace, S, (int)M, (int)N, y, y_dtype, ldy, st);
+  } else if (y_dtype == kF32) {
+    uintx_gemm_go<NB, float>(x, ldx, (int)M, packed, scales, zeros, N, K, lg, y, ldy, 1, st);
+  } else {
+    uintx_gemm_go<NB, uint16_t>(x, ldx, (int)M, packed, scales, zeros, N, K, lg, y, ldy, 1, st);
+  }
+}
+void launch_uintx_gemm(int nbits, int group, const void* packed, const void* scales, const void* zeros, int64_t N,
+                       int64_t K, const void* x, int64_t M, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
+                       void* workspace, hipStream_t st) {
+  const int lg = group == 32 ? 5 : (group == 64 ? 6 : 7);
+  switch (nbits) {
+    case 2: uintx_gemm_nb<2>(x, ldx, M, packed, scales, zeros, N, K, lg, y, y_dtype, ldy, workspace, st); break;
+    case 3: uintx_gemm_nb<3>(x, ldx, M, packed, scales, zeros, N, K, lg, y, y_dtype, ldy, workspace, st); break;
+    case 4: uintx_gemm_nb<4>(x, ldx, M, packed, scales, zeros, N, K, lg, y, y_dtype, ldy, workspace, st); break;
+    case 5: uintx_gemm_nb<5>(x, ldx, M, packed, scales, zeros, N, K, lg, y, y_dtype, ldy, workspace, st); break;
+    case 6: uintx_gemm_nb<6>(x, ldx, M, packed, scales, zeros, N, K, lg, y, y_dtype, ldy, workspace, st); break;
+    default: uintx_gemm_nb<7>(x, ldx, M, packed, scales, zeros, N, K, lg, y, y_dtype, ldy, workspace, st); break;
+  }
 }
 
 }  // namespace gwb

@@ -146,6 +146,12 @@ void launch_mxfp4_gemv(int B, const void* packed, const void* e8m0, int64_t N, i
 // cores; N % 8 == 0, K % 128 == 0. Workspace: GPTQ's group sums of x, then (small M)
 // the K-split partial sums.
 constexpr int kGemmMaxRows = 1 << 24;
+// Decode batches on bf16-weight uintx in the tiled layout (N % 8 == 0, K % 512 == 0):
+// the matrix-core path of gwb_gemv; float32 K-split partials in the workspace.
+size_t uintx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+void launch_uintx_gemm(int nbits, int group, const void* packed, const void* scales, const void* zeros, int64_t N,
+                       int64_t K, const void* x, int64_t M, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
+                       void* workspace, hipStream_t st);
 size_t gemm_workspace_bytes(bool gptq, int group, int64_t M, int64_t N, int64_t K);
 void launch_gptq_gemm(bool sym, int group, const void* qweight, const void* scales, const void* qzeros, int64_t N,
                       int64_t K, const void* x, int64_t M, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,

@@ -237,8 +237,9 @@ int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t
  *            the tile path's group sums; none for MXFP4 below 5 rows)
  * Paths: GPTQ with groups in index order at B >= 2 and MXFP4 at B >= 5 run gwb_gemm's
  * matrix-core tiles (and its numerics) when N % 8 == 0, K % 128 == 0, y and its rows
- * are 16-byte aligned (ldy % 8 == 0) and codes and scales are 16-byte aligned; every
- * other call runs the GEMV kernels: products of dequantized values and activations
+ * are 16-byte aligned (ldy % 8 == 0) and codes and scales are 16-byte aligned, as does
+ * bf16-weight uintx at B >= 5 on weights of N >= 65536 rows (16-byte aligned codes);
+ * every other call runs the GEMV kernels: products of dequantized values and activations
  * exact in float32, float32 sums in a fixed order. Both are deterministic for a given
  * shape and path; the error is bounded by the float32 accumulation.                */
 int gwb_gemv_workspace(const gwb_qspec* spec, int64_t N, int64_t K, int64_t B, size_t* bytes);
@@ -252,9 +253,10 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
  * page quantize_dflash_mxfp4.py serves its linears as MXFP4). The weights are
  * dequantized on chip and multiplied on the matrix cores (bf16 operands, float32
  * accumulation).
- *   spec, w  GPTQ sym or asym (groups 32, 64, 128 in index order; not act-order) or
- *            MXFP4, as gwb_quantize wrote it, [N, K]; N % 8 == 0 and K % 128 == 0
- *            (else GWB_E_UNSUPPORTED); codes and scales 16-byte aligned
+ *   spec, w  GPTQ sym or asym (groups 32, 64, 128 in index order; not act-order),
+ *            MXFP4, or uintx of bf16 weights (page uintx_quant.py, forward; K % 512 ==
+ *            0), as gwb_quantize wrote it, [N, K]; N % 8 == 0 and K % 128 == 0 (else
+ *            GWB_E_UNSUPPORTED); codes and scales 16-byte aligned
  *   x        device bf16 [M, K], row stride ldx (multiple of 8), 16-byte aligned;
  *            0 <= M <= 2^24 and M * ldx < 2^31
  *   y        device [M, N] of y_dtype (GWB_F32 or GWB_BF16, RNE), row stride ldy
@@ -262,9 +264,11 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
  *   workspace at least gwb_gemm_workspace bytes: GPTQ the float32 group sums of x
  *            (K/G x M rounded up to 128, padded to 256 bytes); for M <= 64 with few
  *            column tiles also the float32 partial sums of a K split (splits x M x N),
- *            which a second kernel adds in split order; MXFP4 only the latter
+ *            which a second kernel adds in split order; MXFP4 and uintx only the latter
  * MXFP4 weights are exact bf16 operands, so every product is exact and only the
- * float32 sums round. GPTQ feeds the exact integers 128 + c and applies each group's
+ * float32 sums round; so are uintx's forward weights bf16((q - zp) * s) (one rounding
+ * of an exact product). uintx runs 16-row tiles that convert each weight once per 16
+ * rows of x: a decode-batch kernel, slow for large M. GPTQ feeds the exact integers 128 + c and applies each group's
  * scale and zero point to the group's float32 sum: s * (sum x (128 + c) - (128 + z) *
  * sum x), the group sum of x taken in float64 and rounded once; the offset costs about
  * log2(143 / |c - z|) bits of the float32 sums relative to a direct sum. Deterministic

@@ -230,8 +230,8 @@ def test_gemv_sizes_and_validation():
     P = ctypes.c_void_p
     fake = 1 << 20
     qt = gwb.QTensors(fake, fake, fake, None)
-    def ws(fmt, N, K, B, group=None):
-        sp, b = gwb.make_spec(fmt, 4, group), ctypes.c_size_t()
+    def ws(fmt, N, K, B, group=None, dt=gwb.BF16):
+        sp, b = gwb.make_spec(fmt, 4, group, dt), ctypes.c_size_t()
         rc = lib.gwb_gemv_workspace(ctypes.byref(sp), N, K, B, ctypes.byref(b))
         return rc, b.value
     assert ws("gptq_sym", 131072, 2048, 1) == (gwb.OK, 0)                  # 512 column tiles: one split
@@ -250,10 +250,16 @@ def test_gemv_sizes_and_validation():
     assert lib.gwb_gemv_workspace(ctypes.byref(sp_u), 64, 128, 1, ctypes.byref(ctypes.c_size_t())) == gwb.E_UNSUPPORTED
     assert lib.gwb_gemv_workspace(ctypes.byref(sp_u), 12, 512, 1, ctypes.byref(ctypes.c_size_t())) == gwb.E_UNSUPPORTED
     assert ws("uintx", 3072, 12288, 2) == (gwb.OK, 6 * 2 * 3072 * 4)             # 2048-column splits
-    assert ws("uintx", 3072, 12288, 4) == (gwb.OK, 6 * 4 * 3072 * 4)
-    assert ws("uintx", 3072, 12288, 8) == (gwb.OK, 12 * 8 * 3072 * 4)            # 1024 columns from 5 rows
-    assert ws("uintx", 3072, 11264, 8) == (gwb.OK, 11 * 8 * 3072 * 4)
-    assert ws("uintx", 3072, 11776, 8) == (gwb.OK, 23 * 8 * 3072 * 4)            # K % 1024 != 0: 512
+    # the GEMV kernels (fp16 weights): 2048 columns per wavefront up to 4 rows, 1024 or 512 beyond
+    assert ws("uintx", 3072, 12288, 4, 64, gwb.F16) == (gwb.OK, 6 * 4 * 3072 * 4)
+    assert ws("uintx", 3072, 12288, 8, 64, gwb.F16) == (gwb.OK, 12 * 8 * 3072 * 4)
+    assert ws("uintx", 3072, 11776, 8, 64, gwb.F16) == (gwb.OK, 23 * 8 * 3072 * 4)   # K % 1024 != 0
+    assert ws("uintx", 3072, 12288, 8) == (gwb.OK, 12 * 8 * 3072 * 4)             # bf16 too: narrow
+    # bf16 weights of 65536+ rows from 5 activation rows: gwb_gemm's uintx tiles,
+    # 256 blocks of 64 x 8 rows -> 2 K splits (the GEMV needs as much here)
+    assert ws("uintx", 131072, 2048, 8) == (gwb.OK, 2 * 8 * 131072 * 4)
+    assert ws("uintx", 131072, 4096, 8) == (gwb.OK, 4 * 8 * 131072 * 4)           # GEMV: 4 splits
+    assert ws("uintx", 131072, 2048, 4) == (gwb.OK, 0)                            # 4 rows: the GEMV
     assert ws("uintx", 64, 1536, 1) == (gwb.OK, 3 * 64 * 4)                      # 512-column splits
     assert ws("uintx", 131072, 2048, 1) == (gwb.OK, 0)                           # one split: y directly
     for g, dt in [(32, gwb.BF16), (64, gwb.F16), (128, gwb.F32)]:                # every dtype and group
@@ -277,8 +283,8 @@ def test_gemm_sizes_and_validation():
     P = ctypes.c_void_p
     fake = 1 << 20
     qt = gwb.QTensors(fake, fake, fake, None)
-    def ws(fmt, N, K, M, group=None):
-        sp, b = gwb.make_spec(fmt, 4, group), ctypes.c_size_t()
+    def ws(fmt, N, K, M, group=None, dt=gwb.BF16):
+        sp, b = gwb.make_spec(fmt, 4, group, dt), ctypes.c_size_t()
         rc = lib.gwb_gemm_workspace(ctypes.byref(sp), N, K, M, ctypes.byref(b))
         return rc, b.value
     assert ws("gptq_sym", 34816, 5120, 2048) == (gwb.OK, 40 * 2048 * 4)       # group sums, rows padded to 128
@@ -292,7 +298,13 @@ def test_gemm_sizes_and_validation():
     assert ws("mxfp4", 131072, 2048, 64) == (gwb.OK, 0)                        # 512 tiles: no split
     assert ws("gptq_sym", 256, 576, 16, 64)[0] == gwb.E_UNSUPPORTED           # K % 128
     assert ws("mxfp4", 100, 1024, 16)[0] == gwb.E_UNSUPPORTED                 # N % 8
-    assert ws("uintx", 256, 1024, 16, 64)[0] == gwb.E_UNSUPPORTED
+    # uintx: bf16 weights, N % 8 == 0, K % 512 == 0; 16-row tiles of 64 x 8 weight rows
+    assert ws("uintx", 256, 1024, 16, 64) == (gwb.OK, 4 * 16 * 256 * 4)       # 1 block: 4 = 8 stages / 2
+    assert ws("uintx", 3072, 12288, 8, 64) == (gwb.OK, 32 * 8 * 3072 * 4)     # 6 blocks: 32 splits
+    assert ws("uintx", 131072, 2048, 8, 64) == (gwb.OK, 2 * 8 * 131072 * 4)   # 256 blocks: 2 splits
+    assert ws("uintx", 131072, 2048, 64, 64) == (gwb.OK, 0)                   # 1024 blocks
+    assert ws("uintx", 256, 1152, 16, 64)[0] == gwb.E_UNSUPPORTED             # K % 512
+    assert ws("uintx", 256, 1024, 16, 64, gwb.F16)[0] == gwb.E_UNSUPPORTED    # fp16 weights
     assert ws("gptq_sym_act", 256, 1024, 16, 128)[0] == gwb.E_UNSUPPORTED
     assert ws("gptq_sym", 256, 1024, -1)[0] == gwb.E_ARG
     assert ws("gptq_sym", 256, 1024, (1 << 24) + 1)[0] == gwb.E_ARG

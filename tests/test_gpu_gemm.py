@@ -1,12 +1,13 @@
-"""GPU parity of the prefill GEMM on quantized weights (gwb_gemm) against the oracle:
+"""GPU parity of the GEMM on quantized weights (gwb_gemm) against the oracle:
 y = x @ dequantize(W)^T with the stored tensors dequantized by the format oracles and the
 product taken in float64 (oracle/gemv.py; the consumer definition of pages
-export_gptq_cpu.py and quantize_dflash_mxfp4.py).
+export_gptq_cpu.py, quantize_dflash_mxfp4.py and uintx_quant.py).
 
 Bounds follow the kernel's arithmetic (u = 2^-24; any summation order inside the matrix
 cores is allowed):
   MXFP4  every product is exact (bf16 weights and activations), the float32 sum of K
          products errs by at most u (K + 8) sum_k |x w|;
+  uintx  the same, with w the forward weight bf16((q - zp) s) (page uintx_quant.py);
   GPTQ   per group T = sum x (128 + c) (exact products, G terms), v = T - (128 + z) Sx
          with Sx the float64 group sum rounded once, y = sum_g s v; the error is at most
          u (G + K/G + 8) E with E = 143 sum_k s_g(k) |x_k| (|x (128 + c)| <= 143 |x|).
@@ -22,6 +23,7 @@ import torch
 import oracle.gemv as ogv
 import oracle.gptq as ogq
 import oracle.mxfp4 as omx
+import oracle.uintx as oux
 from group_wise_bit_amd import workloads
 
 pytestmark = pytest.mark.gpu
@@ -157,6 +159,31 @@ def test_gemm_mxfp4_scale_byte_255_columns(M):
     fin = np.isfinite(deq).all(axis=1)
     bound = U32 * (k + 8) * ogv.abs_gemv(deq[fin], xf)
     _check(torch.from_numpy(y[:, fin]), ref[:, fin], bound, torch.float32)
+
+
+@pytest.mark.parametrize("nbits", [2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("M,n,k,group", [(1, 64, 512, 64), (5, 1040, 1024, 64), (16, 264, 2048, 32),
+                                         (37, 136, 1536, 128), (8, 8, 4096, 64)])
+def test_gemm_uintx_parity(nbits, M, n, k, group):
+    """uintx (bf16 weights, the tiled layout) on its 16-row tiles: the B operands are the
+    forward weights bf16((q - zp) s), so every product is exact and the float32 sums obey
+    u (K + 8) sum |x w|. Ragged position-rows (1040 / 8 = 130 of 64-row blocks), several
+    16-row activation tiles (M = 37) and 2 to 32 K splits."""
+    W = workloads.uintx_weight(n, k, seed=700 + n + nbits, outlier_frac=0.01)
+    x = workloads.normal_weight(M, k, std=1.0, seed=701 + M)
+    q = gwb.quantize(W.to(DEV), "uintx", nbits=nbits, group=group)
+    o = oux.quantize(W.float().numpy(), nbits, group)
+    deq = ogv.dequantized("uintx", o, n, k, group=group, nbits=nbits)
+    xf = x.float().numpy()
+    ref = ogv.gemv(deq, xf)
+    bound = U32 * (k + 8) * ogv.abs_gemv(deq, xf)
+    for ydt in (torch.float32, torch.bfloat16):
+        _check(gwb.gemm(q, x.to(DEV), ydt), ref, bound, ydt)
+    oh = torch.zeros(M, k, dtype=torch.bfloat16)
+    cols = (np.arange(M) * 53 + 11) % k
+    oh[np.arange(M), cols] = 2.0
+    y = _np(gwb.gemm(q, oh.to(DEV)))
+    assert np.array_equal(y, (deq[:, cols] * 2.0).T.astype(np.float32))
 
 
 def test_gemm_row_strides_and_bf16_output():

@@ -474,6 +474,13 @@ def _gemv_tiles(fmt, n, k, B):
     return B >= 2 if fmt in ("gptq_sym", "gptq_asym") else (fmt == "mxfp4" and B >= 5)
 
 
+def _uintx_tiles(dt, n, k, B):
+    """gwb_gemv hands bf16-weight uintx batches of 5+ rows on weights of 65536+ rows to
+    gwb_gemm's uintx tiles; their float32 sums run in the matrix cores' order:
+    u (K + 8) sum |w x|."""
+    return dt == "bf16" and B >= 5 and n >= 65536 and n % 8 == 0 and k % 512 == 0
+
+
 def _gemm_gptq_bound(o, x, group, K):
     """The tile kernels' bound (per group T = sum x (128 + c), v = T - (128 + z) Sx with
     the float64 group sum Sx rounded once): u (G + K/G + 8) 143 sum_k s |x|."""
@@ -530,7 +537,8 @@ def test_gemv_mxfp4_parity(n, k, B):
 
 
 @pytest.mark.parametrize("nbits", [2, 3, 4, 5, 6, 7])
-@pytest.mark.parametrize("n,k,B", [(64, 512, 1), (16, 1024, 3), (8, 2048, 8), (136, 1536, 2)])
+@pytest.mark.parametrize("n,k,B", [(64, 512, 1), (16, 1024, 3), (8, 2048, 8), (136, 1536, 2), (1040, 1024, 4),
+                                   (264, 2048, 8)])
 def test_gemv_uintx_parity(nbits, n, k, B):
     """The page's forward: x times the bf16 weight bf16((q - zp) * s)."""
     W = workloads.uintx_weight(n, k, seed=530 + n + nbits, outlier_frac=0.01)
@@ -539,9 +547,16 @@ def test_gemv_uintx_parity(nbits, n, k, B):
     o = oux.quantize(W.float().numpy(), nbits)
     deq = ogv.dequantized("uintx", o, n, k, nbits=nbits)
     xf = x.float().numpy()
-    bound = U32 * (k // 512 + 40) * ogv.abs_gemv(deq, xf)
+    bound = U32 * ((k + 8) if _uintx_tiles("bf16", n, k, B) else (k // 512 + 40)) * ogv.abs_gemv(deq, xf)
     for ydt in (torch.float32, torch.bfloat16):
         _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ogv.gemv(deq, xf), bound, ydt)
+    # one-hot activations: every output is one exact product, on either path
+    xo = torch.zeros(B, k, dtype=torch.bfloat16)
+    cols = [(b * 89 + 3) % k for b in range(B)]
+    for b, kk in enumerate(cols):
+        xo[b, kk] = 1.0
+    yo = _np(gwb.gemv(q, xo.to(DEV)))
+    assert np.array_equal(yo, deq[:, cols].T.astype(np.float32))
 
 
 @pytest.mark.parametrize("dt,group", [("f16", 64), ("f32", 64), ("bf16", 32), ("bf16", 128), ("f16", 128),
@@ -556,7 +571,7 @@ def test_gemv_uintx_variants_parity(dt, group, nbits, n, k, B):
     o = oux.quantize(W.float().numpy(), nbits, group, dt)
     deq = ogv.dequantized("uintx", o, n, k, group=group, nbits=nbits, dtype=dt)
     xf = x.float().numpy()
-    bound = U32 * (k // 512 + 40) * ogv.abs_gemv(deq, xf)
+    bound = U32 * ((k + 8) if _uintx_tiles(dt, n, k, B) else (k // 512 + 40)) * ogv.abs_gemv(deq, xf)
     for ydt in (torch.float32, torch.bfloat16):
         _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ogv.gemv(deq, xf), bound, ydt)
     # one-hot activations return the multiplied weight's columns bit for bit
@@ -768,10 +783,10 @@ def test_full_fold_34816x5120_sampled():
 
 
 @pytest.mark.parametrize("fmt,B", [("gptq_sym", 1), ("gptq_sym", 8), ("mxfp4", 1), ("mxfp4", 8), ("uintx", 1),
-                                   ("gptq_sym_act", 1)])
+                                   ("uintx", 8), ("gptq_sym_act", 1)])
 def test_full_gemv_lm_head_131072x2048_sampled(fmt, B):
     """The page's lm_head decode read, 131072 x 2048, in the launch shapes the benchmark
-    times (B = 1: the GEMV kernels; B = 8: GPTQ and MXFP4 on the GEMM tiles); checked on
+    times (B = 1: the GEMV kernels; B = 8: the matrix-core tiles); checked on
     sampled output rows (whole qzeros words) against the oracle."""
     N_, K_ = 131072, 2048
     W = workloads.normal_weight(N_, K_, seed=520)
@@ -792,7 +807,7 @@ def test_full_gemv_lm_head_131072x2048_sampled(fmt, B):
     elif fmt == "uintx":
         q = gwb.quantize(Wd, fmt, nbits=4)
         deq = ogv.dequantized("uintx", oux.quantize(Ws, 4), len(ns), K_, nbits=4)
-        bound = U32 * (K_ // 512 + 40) * ogv.abs_gemv(deq, xf)
+        bound = U32 * ((K_ + 8) if B > 1 else (K_ // 512 + 40)) * ogv.abs_gemv(deq, xf)
     else:
         perm = np.random.default_rng(526).permutation(K_)
         q = gwb.quantize(Wd, fmt, group=128, perm=torch.from_numpy(perm.astype(np.int32)).to(DEV))
