@@ -625,17 +625,22 @@ __global__ __launch_bounds__(256, 2) void uintx_gemm_kernel(const uint16_t* __re
 
   U4 pb[NP][2];
   uint32_t pq[8];                        // segment t's group: scale bits << 16 | zero point
+  // uniform 64-bit bases plus 32-bit lane offsets (the scalar-base load form: no 64-bit
+  // address arithmetic per load)
+  const char* sbase = reinterpret_cast<const char*>(scales);
   auto fetch = [&](int k0, int buf) {
     a_fetch<1>(aof, x + k0, As[buf], wv);
+    const uint8_t* pk = packed + k0;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
-      pb[i][0] = ld16(packed + plane[i] + pos + k0);
-      pb[i][1] = ld16(packed + plane[i] + pos + k0 + 16);
+      const uint32_t o = plane[i] + pos;
+      pb[i][0] = ld16(pk + o);
+      pb[i][1] = ld16(pk + (o + 16u));
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const uint32_t g = (t * L1 + pos + k0) >> lg;
-      pq[t] = ((uint32_t)scales[g] << 16) | zeros[g];
+      const uint32_t g = (t * L1 + pos + (uint32_t)k0) >> lg;
+      pq[t] = ((uint32_t)*reinterpret_cast<const uint16_t*>(sbase + (g << 1)) << 16) | zeros[g];
     }
   };
 
@@ -658,12 +663,17 @@ __global__ __launch_bounds__(256, 2) void uintx_gemm_kernel(const uint16_t* __re
     for (int t = 0; t < 8; ++t) qp[t] = pq[t];
     if (st + 1 < st1) fetch((st + 1) * kGmBK, buf ^ 1);
     const uint16_t* A = As[buf];
+    float sc[8], nzs[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      sc[t] = __uint_as_float(qp[t] & 0xFFFF0000u);
+      nzs[t] = -((float)(qp[t] & 0xFFu) * sc[t]);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const U4 a = *reinterpret_cast<const U4*>(A + aoff[s]);
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float sc = __uint_as_float(qp[t] & 0xFFFF0000u), nzs = -((float)(qp[t] & 0xFFu) * sc);
         uint32_t c[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -677,7 +687,7 @@ __global__ __launch_bounds__(256, 2) void uintx_gemm_kernel(const uint16_t* __re
         asm volatile("" : "+v"(c[0]), "+v"(c[1]));   // codes convert from their bytes (v_cvt_f32_ubyte0..3)
         float f[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = __builtin_fmaf((float)((c[e >> 2] >> (8 * (e & 3))) & 0xFFu), sc, nzs);
+        for (int e = 0; e < 8; ++e) f[e] = __builtin_fmaf((float)((c[e >> 2] >> (8 * (e & 3))) & 0xFFu), sc[t], nzs[t]);
         const U4 b = U4{ux_pair(f[0], f[1]), ux_pair(f[2], f[3]), ux_pair(f[4], f[5]), ux_pair(f[6], f[7])};
         acc[t] = mfma_bf16(a, b, acc[t]);
       }
