@@ -86,10 +86,12 @@ def quantize_sym(w, group: int = 128):
     codes = np.clip(np.rint(blocks / scale[:, None, :]) + np.float32(8.0), 0, 15)
     deq = ((codes - np.float32(8.0)) * scale[:, None, :]).reshape(k, n)
     codes = codes.reshape(k, n).astype(np.uint8)
+    with np.errstate(over="ignore"):                    # scales past fp16's range round to inf
+        scales16 = scale.astype(np.float16)
     return dict(
         qweight=pack_int32(codes, 0),
         qzeros=pack_int32(np.full((g, n), 7, np.uint8), 1),
-        scales=scale.astype(np.float16),
+        scales=scales16,
         g_idx=(np.arange(k, dtype=np.int32) // group).astype(np.int32),
         codes=codes, scale_f32=scale,
         snr_db_f32=_snr_page(wt, deq),
@@ -108,10 +110,12 @@ def quantize_asym(w, group: int = 128):
     deq = ((codes - zp[:, None, :]) * scale[:, None, :]).reshape(k, n)
     codes = codes.reshape(k, n).astype(np.uint8)
     zp = zp.astype(np.uint8)
+    with np.errstate(over="ignore"):                    # scales past fp16's range round to inf
+        scales16 = scale.astype(np.float16)
     return dict(
         qweight=pack_int32(codes, 0),
         qzeros=pack_int32(zp, 1),
-        scales=scale.astype(np.float16),
+        scales=scales16,
         g_idx=(np.arange(k, dtype=np.int32) // group).astype(np.int32),
         codes=codes, zp=zp, scale_f32=scale,
         snr_db_f32=_snr_page(wt, deq),
@@ -157,7 +161,8 @@ def dequantize(qweight, scales, qzeros, group: int, sym: bool, g_idx=None) -> np
     else:
         zp = unpack_int32(qzeros, 1).astype(np.float32)             # [G, N]
     gi = np.arange(k) // group if g_idx is None else np.asarray(g_idx, np.int64)
-    d = (codes - zp[gi, :]) * s[gi, :]                              # row k uses group gi[k]
+    with np.errstate(invalid="ignore"):                 # an inf scale times code - zp = 0: NaN
+        d = (codes - zp[gi, :]) * s[gi, :]                          # row k uses group gi[k]
     return np.ascontiguousarray(d.T)
 
 

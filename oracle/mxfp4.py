@@ -101,6 +101,6 @@ def dequantize(packed, e8m0, k: int) -> np.ndarray:
     val = np.where((code & 8) > 0, -mag, mag)
     with np.errstate(over="ignore"):
         scale = np.ldexp(np.float32(1.0), np.asarray(e8m0, np.int32) - 127).astype(np.float32)
-    with np.errstate(invalid="ignore"):
+    with np.errstate(invalid="ignore", over="ignore"):   # 2^128 (byte 255) times E2M1: inf, 0 * inf: NaN
         out = val.reshape(n, k // GROUP, GROUP) * scale[..., None]
     return out.reshape(n, k).astype(np.float32)
