@@ -45,6 +45,33 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// VP values per lane (VP = 8 or 16) -> lane l holds the wavefront sum of value l & (VP - 1).
+// Each fold halves the values a lane keeps: the half whose index has the lane's bit set
+// stays, the other half goes to the DPP partner, which differs in that bit (ror 8 within
+// a 16-lane row: bit 3; half mirror 7 - i: bit 2; then bits 1 and 0); lanes 16 and 32
+// apart, which hold the same value, are added last. 2 VP - 2 adds instead of 12 VP.
+template <int CTRL, int NV, int VP>
+__device__ __forceinline__ void gv_fold(float (&v)[VP], bool up) {
+#pragma unroll
+  for (int i = 0; i < NV / 2; ++i) {
+    const float keep = up ? v[i + NV / 2] : v[i], send = up ? v[i] : v[i + NV / 2];
+    v[i] = keep + dpp_read<CTRL>(send);
+  }
+}
+template <int VP>
+__device__ __forceinline__ float gv_transposed_sum(float (&v)[VP], int lane) {
+  static_assert(VP == 8 || VP == 16, "8 or 16 values");
+  if constexpr (VP == 16) gv_fold<kDppRor8, 16>(v, lane & 8);
+  gv_fold<kDppHalfMirror, 8>(v, lane & 4);
+  gv_fold<kDppXor2, 4>(v, lane & 2);
+  gv_fold<kDppXor1, 2>(v, lane & 1);
+  float r = v[0];
+  if constexpr (VP == 8) r += dpp_read<kDppRor8>(r);
+  r += __shfl_xor(r, 16);
+  r += __shfl_xor(r, 32);
+  return r;
+}
+
 // ------------------------------------------------------------------ GPTQ
 constexpr int kGqWaveK = 128, kGqBlockK = 4 * kGqWaveK;
 
@@ -372,14 +399,14 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restri
         for (int b = 0; b < B; ++b) acc[i][b] += ok ? ldexpf(d[b], ex) : 0.0f;
       }
     }
+    // value i B + b (row i, activation row b), padded with zeros to VP
+    constexpr int V = R * B, VP = V <= 8 ? 8 : 16;
+    float v[VP];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const float v = wave_sum(acc[i][b]);
-        if (lane == 0 && row0 + i < N) store_y(y + (int64_t)b * ldy + row0 + i, v);
-      }
-    }
+    for (int e = 0; e < VP; ++e) v[e] = e < V ? acc[e / B][e % B] : 0.0f;
+    const float sum = gv_transposed_sum<VP>(v, lane);
+    const int e = lane & (VP - 1), i = e / B, b = e - i * B;
+    if (lane < V && row0 + i < N) store_y(y + (int64_t)b * ldy + row0 + i, sum);
   }
 }
 
