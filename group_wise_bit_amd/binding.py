@@ -65,6 +65,7 @@ _SIGS = {
                                _P],
     "gwb_dequantize": [ctypes.POINTER(QSpec), ctypes.POINTER(QTensors), _I64, _I64, _P, _I32, _I64, _P, _SZ, _P],
     "gwb_snr": [ctypes.POINTER(QSpec), _P, _I64, _I64, _I64, ctypes.POINTER(QTensors), _P, _P, _SZ, _P],
+    "gwb_quantize_snr": [ctypes.POINTER(QSpec), _P, _I64, _I64, _I64, ctypes.POINTER(QTensors), _P, _P, _SZ, _P],
     "gwb_awq_workspace": [_I64, _I64, _I32, _I64, ctypes.POINTER(_SZ)],
     "gwb_awq_search_mxfp4": [_P, _I32, _I64, _I64, _I64, _P, _P, _I32, _I64, _P, _P, _P, _P, _SZ, _P],
     "gwb_stream_copy": [_P, _P, _SZ, _P],
@@ -232,6 +233,40 @@ def snr(W: torch.Tensor, q: Quantized, workspace: Optional[torch.Tensor] = None,
     _check(lib.gwb_snr(ctypes.byref(sp), _ptr(W), N, K, ldw, ctypes.byref(qt), _ptr(out), _ptr(workspace),
                        workspace.numel(), _stream()))
     return out
+
+
+def quantize_snr(W: torch.Tensor, fmt: str, nbits: int = 4, group: Optional[int] = None,
+                 out: Optional[Quantized] = None, snr_out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None):
+    """quantize and snr in one call (gwb_quantize_snr): returns (Quantized, device float64
+    [sum w^2, sum (w - d)^2, SNR dB])."""
+    N, K, ldw = _weight_args(W)
+    group = DEFAULT_GROUP[fmt] if group is None else group
+    if out is None:
+        sz = query_sizes(fmt, N, K, nbits, group, W.dtype)
+        dev = W.device
+        gidx = _alloc(sz["g_idx"], dev) if fmt.startswith("gptq") else None
+        zeros = _alloc(sz["zeros"], dev) if not fmt.startswith("mxfp4") else None
+        out = Quantized(fmt, nbits, group, W.dtype, N, K, _alloc(sz["codes"], dev), _alloc(sz["scales"], dev),
+                        zeros, gidx, sz)
+    if snr_out is None:
+        snr_out = torch.empty(3, dtype=torch.float64, device=W.device)
+    if workspace is None:
+        workspace = _alloc(max(out.sizes["workspace"], 16), W.device)
+    sp, qt = out.spec(), out.qtensors()
+    _check(lib.gwb_quantize_snr(ctypes.byref(sp), _ptr(W), N, K, ldw, ctypes.byref(qt), _ptr(snr_out),
+                                _ptr(workspace), workspace.numel(), _stream()))
+    return out, snr_out
+
+
+def prepare_quantize_snr(W: torch.Tensor, q: Quantized, snr_out: torch.Tensor, workspace: torch.Tensor) -> Prepared:
+    N, K, ldw = _weight_args(W)
+    if (N, K, W.dtype) != (q.N, q.K, q.w_dtype):
+        raise ValueError("W does not match the Quantized buffers")
+    sp, qt = q.spec(), q.qtensors()
+    return Prepared(lib.gwb_quantize_snr, (ctypes.byref(sp), _ptr(W), N, K, ldw, ctypes.byref(qt), _ptr(snr_out),
+                                           _ptr(workspace), workspace.numel(), _stream()),
+                    (sp, qt, W, q, snr_out, workspace))
 
 
 DEFAULT_ALPHAS = tuple(i / 10 for i in range(11))

@@ -213,13 +213,53 @@ int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int
     case GWB_MXFP4:
     case GWB_MXFP4_PAGE_TIES:
       gwb::launch_mxfp4_quant(spec->format == GWB_MXFP4_PAGE_TIES, W, spec->w_dtype, N, K, ldw, out->codes,
-                              out->scales, st);
+                              out->scales, nullptr, st);
       break;
     default:
       gwb::launch_uintx_quant(spec->nbits, spec->w_dtype, spec->group, W, N, K, ldw, out->codes, out->scales,
-                              out->zeros, workspace, st);
+                              out->zeros, workspace, nullptr, st);
   }
   return hip_check("quantize launch");
+}
+
+// Quantize and the reconstruction SNR of what was stored, in one pass over W where the
+// quantize kernel can form the sums itself (MXFP4, GPTQ in index order while its tiles
+// fit the partials, uintx in the tiled layout); otherwise the two calls in turn.
+int gwb_quantize_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
+                     const gwb_qtensors* out, double* d_out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = check_spec(spec, N, K)) return rc;
+  if (is_act(spec->format)) return fail(GWB_E_ARG, "act-order GPTQ quantizes with gwb_quantize_act_order");
+  if (!d_out) return fail(GWB_E_ARG, "d_out is NULL");
+  if (N == 0 || K == 0) return fail(GWB_E_SHAPE, "SNR of an empty matrix is undefined");
+  if (int rc = check_weight(spec, W, K, ldw)) return rc;
+  if (int rc = check_tensors(spec, out)) return rc;
+  bool fused = true;
+  if (spec->format == GWB_GPTQ_SYM || spec->format == GWB_GPTQ_ASYM)
+    fused = gwb::gptq_quant_snr_fits(spec->group, N, K);
+  else if (spec->format == GWB_UINTX)
+    fused = gwb::uintx_tiled(spec->w_dtype, spec->group, N, K);
+  if (!fused) {
+    if (int rc = gwb_quantize(spec, W, N, K, ldw, out, workspace, workspace_bytes, stream)) return rc;
+    return gwb_snr(spec, W, N, K, ldw, out, d_out, workspace, workspace_bytes, stream);
+  }
+  const unsigned nb = err_blocks(spec, N, K);
+  const size_t need = (size_t)nb * 2 * sizeof(double);
+  if (!workspace || workspace_bytes < need)
+    return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  double* part = (double*)workspace;
+  if (spec->format == GWB_GPTQ_SYM || spec->format == GWB_GPTQ_ASYM)
+    gwb::launch_gptq_quant_snr(spec->format == GWB_GPTQ_SYM, spec->group, W, spec->w_dtype, N, K, ldw, out->codes,
+                               out->scales, out->zeros, out->g_idx, part, st);
+  else if (is_mxfp4(spec->format))
+    gwb::launch_mxfp4_quant(spec->format == GWB_MXFP4_PAGE_TIES, W, spec->w_dtype, N, K, ldw, out->codes,
+                            out->scales, part, st);
+  else
+    gwb::launch_uintx_quant(spec->nbits, spec->w_dtype, spec->group, W, N, K, ldw, out->codes, out->scales,
+                            out->zeros, nullptr, part, st);
+  gwb::launch_err_finalize(part, nb, d_out, st);
+  return hip_check("quantize_snr launch");
 }
 
 int gwb_dequantize(const gwb_qspec* spec, const gwb_qtensors* in, int64_t N, int64_t K, void* out,

@@ -94,13 +94,16 @@ struct TileG {
 // rint(u) = rint(fl(x / s)) + zp. Otherwise (the exact and near ties, a few weights in
 // a thousand for bf16 data, or every weight of a group whose A / s reaches 2^18) the
 // weight is divided exactly.
-template <bool SYM, int G, typename TIn>
+// SNR: also the reconstruction sums of the stored values, (c - z) times the fp16 scale
+// as the dequantize kernel forms them, over the tile's valid weights; one partial pair
+// per block (block = tile).
+template <bool SYM, int G, typename TIn, bool SNR>
 __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__ W, int64_t ldw,
                                                          int N, int K, int ntk,
                                                          uint32_t* __restrict__ qweight,
                                                          _Float16* __restrict__ scales,
                                                          uint32_t* __restrict__ qzeros,
-                                                         int32_t* __restrict__ g_idx) {
+                                                         int32_t* __restrict__ g_idx, double* __restrict__ part) {
   using T = TileG<G>;
   constexpr int L = T::L, LL = L < 8 ? L : 8, R = 8 / LL;
   __shared__ uint32_t qtile[kTR * kQS];
@@ -165,6 +168,7 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
   }
   __syncthreads();
   const int gl = lane / L;
+  double sw = 0.0, se = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float4 p = qp[wave * 8 + i][gl];
@@ -190,7 +194,17 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
       od = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_fmed3f(c[2 * j + 1], 0.0f, 15.0f), j, od);
     }
     qtile[lane * kQS + wave * 8 + i] = ev | (od << 4);
+    if constexpr (SNR) {
+      if (n0 + wave * 8 + i < N && k0 + lane * 8 < K) {
+        const float s16 = (float)(_Float16)p.w;
+        float d[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d[j] = (__builtin_amdgcn_fmed3f(c[j], 0.0f, 15.0f) - p.y) * s16;
+        acc_err8(x, d, sw, se);
+      }
+    }
   }
+  if constexpr (SNR) block_sum2_store<256>(sw, se, part);   // synchronizes the block too
   __syncthreads();
   {  // qweight [K/8, N]: 64 r-rows x 32 words, 8 words (32 bytes) per thread
     const int r = t >> 2, c8 = (t & 3) * 8;
@@ -334,31 +348,42 @@ __global__ __launch_bounds__(256) void gptq_dequant_kernel(const uint32_t* __res
 static int ntk_of(int64_t K) { return (int)((K + kTK - 1) / kTK); }
 static unsigned tiles_of(int64_t N, int64_t K) { return (unsigned)(((N + kTN - 1) / kTN) * ntk_of(K)); }
 
-template <bool SYM, int G>
+template <bool SYM, int G, bool SNR>
 static void quant_g(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw, void* qw,
-                    void* sc, void* qz, void* gi, hipStream_t st) {
+                    void* sc, void* qz, void* gi, double* part, hipStream_t st) {
   const dim3 grid(tiles_of(N, K));
   if (w_dtype == kBF16)
-    hipLaunchKernelGGL((gptq_quant_kernel<SYM, G, uint16_t>), grid, dim3(256), 0, st, (const uint16_t*)W,
-                       ldw, (int)N, (int)K, ntk_of(K), (uint32_t*)qw, (_Float16*)sc, (uint32_t*)qz, (int32_t*)gi);
+    hipLaunchKernelGGL((gptq_quant_kernel<SYM, G, uint16_t, SNR>), grid, dim3(256), 0, st, (const uint16_t*)W,
+                       ldw, (int)N, (int)K, ntk_of(K), (uint32_t*)qw, (_Float16*)sc, (uint32_t*)qz, (int32_t*)gi,
+                       part);
   else
-    hipLaunchKernelGGL((gptq_quant_kernel<SYM, G, float>), grid, dim3(256), 0, st, (const float*)W, ldw,
-                       (int)N, (int)K, ntk_of(K), (uint32_t*)qw, (_Float16*)sc, (uint32_t*)qz, (int32_t*)gi);
+    hipLaunchKernelGGL((gptq_quant_kernel<SYM, G, float, SNR>), grid, dim3(256), 0, st, (const float*)W, ldw,
+                       (int)N, (int)K, ntk_of(K), (uint32_t*)qw, (_Float16*)sc, (uint32_t*)qz, (int32_t*)gi,
+                       part);
 }
 
-template <bool SYM>
+template <bool SYM, bool SNR>
 static void quant_s(int group, const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
-                    void* qw, void* sc, void* qz, void* gi, hipStream_t st) {
-  if (group == 32) quant_g<SYM, 32>(W, w_dtype, N, K, ldw, qw, sc, qz, gi, st);
-  else if (group == 64) quant_g<SYM, 64>(W, w_dtype, N, K, ldw, qw, sc, qz, gi, st);
-  else quant_g<SYM, 128>(W, w_dtype, N, K, ldw, qw, sc, qz, gi, st);
+                    void* qw, void* sc, void* qz, void* gi, double* part, hipStream_t st) {
+  if (group == 32) quant_g<SYM, 32, SNR>(W, w_dtype, N, K, ldw, qw, sc, qz, gi, part, st);
+  else if (group == 64) quant_g<SYM, 64, SNR>(W, w_dtype, N, K, ldw, qw, sc, qz, gi, part, st);
+  else quant_g<SYM, 128, SNR>(W, w_dtype, N, K, ldw, qw, sc, qz, gi, part, st);
 }
 
 void launch_gptq_quant(bool sym, int group, const void* W, int32_t w_dtype, int64_t N, int64_t K,
                        int64_t ldw, void* qweight, void* scales, void* qzeros, void* g_idx,
                        hipStream_t st) {
-  if (sym) quant_s<true>(group, W, w_dtype, N, K, ldw, qweight, scales, qzeros, g_idx, st);
-  else quant_s<false>(group, W, w_dtype, N, K, ldw, qweight, scales, qzeros, g_idx, st);
+  if (sym) quant_s<true, false>(group, W, w_dtype, N, K, ldw, qweight, scales, qzeros, g_idx, nullptr, st);
+  else quant_s<false, false>(group, W, w_dtype, N, K, ldw, qweight, scales, qzeros, g_idx, nullptr, st);
+}
+
+// One partial pair per tile: only while the tiles fit the error kernel's partials.
+bool gptq_quant_snr_fits(int group, int64_t N, int64_t K) { return tiles_of(N, K) == gptq_err_blocks(group, N, K); }
+void launch_gptq_quant_snr(bool sym, int group, const void* W, int32_t w_dtype, int64_t N, int64_t K,
+                           int64_t ldw, void* qweight, void* scales, void* qzeros, void* g_idx, double* part,
+                           hipStream_t st) {
+  if (sym) quant_s<true, true>(group, W, w_dtype, N, K, ldw, qweight, scales, qzeros, g_idx, part, st);
+  else quant_s<false, true>(group, W, w_dtype, N, K, ldw, qweight, scales, qzeros, g_idx, part, st);
 }
 
 template <int SINK, bool SYM, int G, typename TOut, typename TW>

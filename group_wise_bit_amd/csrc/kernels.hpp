@@ -30,8 +30,9 @@ inline unsigned err_blocks_for(uint64_t units) {
 }
 
 // ---- MXFP4 (mxfp4.hip)
+// part != NULL: also the reconstruction sums' per-block partials (mxfp4_err_blocks of them)
 void launch_mxfp4_quant(bool page_ties, const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
-                        void* packed, void* e8m0, hipStream_t st);
+                        void* packed, void* e8m0, double* part, hipStream_t st);
 void launch_mxfp4_dequant(const void* packed, const void* e8m0, int64_t N, int64_t K, void* out,
                           int32_t out_dtype, int64_t ldo, hipStream_t st);
 unsigned mxfp4_err_blocks(int64_t N, int64_t K);
@@ -46,6 +47,12 @@ void launch_gptq_dequant(bool sym, int group, const void* qweight, const void* s
                          const void* qzeros, int64_t N, int64_t K, void* out, int32_t out_dtype,
                          int64_t ldo, hipStream_t st);
 unsigned gptq_err_blocks(int group, int64_t N, int64_t K);
+// quantize and the reconstruction sums in one pass (gptq_err_blocks partials), when
+// gptq_quant_snr_fits: one partial per tile
+bool gptq_quant_snr_fits(int group, int64_t N, int64_t K);
+void launch_gptq_quant_snr(bool sym, int group, const void* W, int32_t w_dtype, int64_t N, int64_t K,
+                           int64_t ldw, void* qweight, void* scales, void* qzeros, void* g_idx, double* part,
+                           hipStream_t st);
 void launch_gptq_err(bool sym, int group, const void* W, int32_t w_dtype, int64_t N, int64_t K,
                      int64_t ldw, const void* qweight, const void* scales, const void* qzeros,
                      double* part, hipStream_t st);
@@ -73,8 +80,10 @@ void launch_gptq_act_err(bool sym, int group, const void* W, int32_t w_dtype, in
 // dtype (kBF16, kF16, kF32); group 32, 64 or 128.
 bool uintx_tiled(int32_t dt, int group, int64_t N, int64_t K);
 size_t uintx_code_workspace(int32_t dt, int group, int64_t N, int64_t K);
+// part != NULL (tiled layout only: uintx_tiled): also the reconstruction sums' per-block
+// partials, uintx_err_blocks of them
 void launch_uintx_quant(int nbits, int32_t dt, int group, const void* W, int64_t N, int64_t K, int64_t ldw,
-                        void* packed, void* scales, void* zeros, void* workspace, hipStream_t st);
+                        void* packed, void* scales, void* zeros, void* workspace, double* part, hipStream_t st);
 void launch_uintx_dequant(int nbits, int32_t dt, int group, const void* packed, const void* scales,
                           const void* zeros, int64_t N, int64_t K, void* out, int32_t out_dtype, int64_t ldo,
                           hipStream_t st);
@@ -97,7 +106,7 @@ struct GemvOut {
 };
 #define GWB_UINTX_TILED_DT(SUF)                                                                                     \
   void uintx_tiled_quant_##SUF(int nbits, int group, const void* W, int64_t N, int64_t K, int64_t ldw,              \
-                               void* packed, void* scales, void* zeros, hipStream_t st);                             \
+                               void* packed, void* scales, void* zeros, double* part, hipStream_t st);               \
   void uintx_tiled_dequant_##SUF(int nbits, int group, const void* packed, const void* scales, const void* zeros,   \
                                  int64_t N, int64_t K, void* out, int32_t out_dtype, int64_t ldo, hipStream_t st);  \
   void uintx_tiled_err_##SUF(int nbits, int group, const void* W, int64_t N, int64_t K, int64_t ldw,                \

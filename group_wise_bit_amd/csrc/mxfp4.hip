@@ -54,36 +54,48 @@ __device__ __forceinline__ uint32_t page_tie_fix(const Raw8<TIn>& r, uint32_t e8
   return corr;
 }
 
-template <bool LIT, typename TIn>
+// SNR: also the reconstruction sums of the stored values (the dequantize kernel's
+// arithmetic on the word and scale just written), in the error kernel's per-thread
+// order when launched on its grid.
+template <bool LIT, bool SNR, typename TIn>
 __device__ __forceinline__ void quant_unit(const Raw8<TIn>& r, uint32_t u, uint32_t* __restrict__ packed,
-                                           uint8_t* __restrict__ e8m0) {
+                                           uint8_t* __restrict__ e8m0, double& sw, double& se) {
   const uint32_t e8 = mx_e8m0_bits(quad_max_u(absmax_bits(r)));
   uint32_t w = pack_unit(r, mx_scale_operand(e8));
   if constexpr (LIT) w -= page_tie_fix(r, e8);
   packed[u] = w;
   if ((u & 3u) == 0) e8m0[u >> 2] = (uint8_t)e8;
+  if constexpr (SNR) {
+    float d[8], x[8];
+    mx_unpack8(w, e8, d);
+    to_f32(r, x);
+    acc_err8(x, d, sw, se);
+  }
 }
 
 // units = N*K/8 is a multiple of 4 and every stride is too, so the four lanes of a
 // block always take the same branch of each loop (the DPP step needs all four).
-template <bool CONTIG, bool LIT, typename TIn>
+template <bool CONTIG, bool LIT, typename TIn, bool SNR>
 __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const TIn* __restrict__ W, int64_t ldw,
                                                           uint32_t units, FastDiv upr,
                                                           uint32_t* __restrict__ packed,
-                                                          uint8_t* __restrict__ e8m0) {
+                                                          uint8_t* __restrict__ e8m0, double* __restrict__ part) {
   const uint32_t stride = gridDim.x * blockDim.x;
+  double sw = 0.0, se = 0.0;
   uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
   for (; u + 3 * stride < units; u += 4 * stride) {
     const Raw8<TIn> r0 = load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr));
     const Raw8<TIn> r1 = load_raw8(unit_ptr<CONTIG>(W, ldw, u + stride, upr));
     const Raw8<TIn> r2 = load_raw8(unit_ptr<CONTIG>(W, ldw, u + 2 * stride, upr));
     const Raw8<TIn> r3 = load_raw8(unit_ptr<CONTIG>(W, ldw, u + 3 * stride, upr));
-    quant_unit<LIT>(r0, u, packed, e8m0);
-    quant_unit<LIT>(r1, u + stride, packed, e8m0);
-    quant_unit<LIT>(r2, u + 2 * stride, packed, e8m0);
-    quant_unit<LIT>(r3, u + 3 * stride, packed, e8m0);
+    quant_unit<LIT, SNR>(r0, u, packed, e8m0, sw, se);
+    quant_unit<LIT, SNR>(r1, u + stride, packed, e8m0, sw, se);
+    quant_unit<LIT, SNR>(r2, u + 2 * stride, packed, e8m0, sw, se);
+    quant_unit<LIT, SNR>(r3, u + 3 * stride, packed, e8m0, sw, se);
   }
-  for (; u < units; u += stride) quant_unit<LIT>(load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr)), u, packed, e8m0);
+  for (; u < units; u += stride)
+    quant_unit<LIT, SNR>(load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr)), u, packed, e8m0, sw, se);
+  if constexpr (SNR) block_sum2_store<256>(sw, se, part);
 }
 
 // Unpack + dequantize. SINK == kStore writes out[n, k]; SINK == kErr takes W at the
@@ -139,27 +151,34 @@ __global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint32_t* __re
 }
 
 // ------------------------------------------------------------------ launchers
-template <bool LIT>
+template <bool LIT, bool SNR>
 static void quant_lit(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw, void* packed, void* e8m0,
-                      hipStream_t st) {
+                      double* part, hipStream_t st) {
   const uint32_t units = (uint32_t)(N * K / 8);
   const FastDiv upr = make_fastdiv((uint32_t)(K / 8));
-  const unsigned grid = stream_blocks(units);
+  // with the sums: the error kernel's grid, whose partials the workspace holds
+  const unsigned grid = SNR ? mxfp4_err_blocks(N, K) : stream_blocks(units);
   const bool contig = ldw == K;
   if (w_dtype == kBF16)
-    hipLaunchKernelGGL((contig ? mxfp4_quant_kernel<true, LIT, uint16_t> : mxfp4_quant_kernel<false, LIT, uint16_t>),
+    hipLaunchKernelGGL((contig ? mxfp4_quant_kernel<true, LIT, uint16_t, SNR>
+                               : mxfp4_quant_kernel<false, LIT, uint16_t, SNR>),
                        dim3(grid), dim3(256), 0, st, (const uint16_t*)W, ldw, units, upr, (uint32_t*)packed,
-                       (uint8_t*)e8m0);
+                       (uint8_t*)e8m0, part);
   else
-    hipLaunchKernelGGL((contig ? mxfp4_quant_kernel<true, LIT, float> : mxfp4_quant_kernel<false, LIT, float>),
+    hipLaunchKernelGGL((contig ? mxfp4_quant_kernel<true, LIT, float, SNR> : mxfp4_quant_kernel<false, LIT, float, SNR>),
                        dim3(grid), dim3(256), 0, st, (const float*)W, ldw, units, upr, (uint32_t*)packed,
-                       (uint8_t*)e8m0);
+                       (uint8_t*)e8m0, part);
 }
 
 void launch_mxfp4_quant(bool page_ties, const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
-                        void* packed, void* e8m0, hipStream_t st) {
-  if (page_ties) quant_lit<true>(W, w_dtype, N, K, ldw, packed, e8m0, st);
-  else quant_lit<false>(W, w_dtype, N, K, ldw, packed, e8m0, st);
+                        void* packed, void* e8m0, double* part, hipStream_t st) {
+  if (page_ties) {
+    if (part) quant_lit<true, true>(W, w_dtype, N, K, ldw, packed, e8m0, part, st);
+    else quant_lit<true, false>(W, w_dtype, N, K, ldw, packed, e8m0, nullptr, st);
+  } else {
+    if (part) quant_lit<false, true>(W, w_dtype, N, K, ldw, packed, e8m0, part, st);
+    else quant_lit<false, false>(W, w_dtype, N, K, ldw, packed, e8m0, nullptr, st);
+  }
 }
 
 void launch_mxfp4_dequant(const void* packed, const void* e8m0, int64_t N, int64_t K, void* out,

@@ -22,17 +22,17 @@ size_t uintx_code_workspace(int32_t dt, int group, int64_t N, int64_t K) {
 }
 
 void launch_uintx_quant(int nbits, int32_t dt, int group, const void* W, int64_t N, int64_t K, int64_t ldw,
-                        void* packed, void* scales, void* zeros, void* workspace, hipStream_t st) {
+                        void* packed, void* scales, void* zeros, void* workspace, double* part, hipStream_t st) {
   if (!uintx_tiled(dt, group, N, K))
     launch_uintx_quant_flat(nbits, dt, group, W, N, K, ldw, packed, scales, zeros, workspace, st);
   else if (dt == kBF16 && group == 64)
-    ux_tiled_quant_entry<kBF16, 64>(nbits, W, N, K, ldw, packed, scales, zeros, st);
+    ux_tiled_quant_entry<kBF16, 64>(nbits, W, N, K, ldw, packed, scales, zeros, part, st);
   else if (dt == kBF16)
-    uintx_tiled_quant_bf16(nbits, group, W, N, K, ldw, packed, scales, zeros, st);
+    uintx_tiled_quant_bf16(nbits, group, W, N, K, ldw, packed, scales, zeros, part, st);
   else if (dt == kF16)
-    uintx_tiled_quant_f16(nbits, group, W, N, K, ldw, packed, scales, zeros, st);
+    uintx_tiled_quant_f16(nbits, group, W, N, K, ldw, packed, scales, zeros, part, st);
   else
-    uintx_tiled_quant_f32(nbits, group, W, N, K, ldw, packed, scales, zeros, st);
+    uintx_tiled_quant_f32(nbits, group, W, N, K, ldw, packed, scales, zeros, part, st);
 }
 
 void launch_uintx_dequant(int nbits, int32_t dt, int group, const void* packed, const void* scales,

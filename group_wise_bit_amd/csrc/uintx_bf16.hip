@@ -6,9 +6,9 @@
 namespace gwb {
 
 void uintx_tiled_quant_bf16(int nbits, int group, const void* W, int64_t N, int64_t K, int64_t ldw, void* packed,
-                            void* scales, void* zeros, hipStream_t st) {
-  if (group == 32) ux_tiled_quant_entry<kBF16, 32>(nbits, W, N, K, ldw, packed, scales, zeros, st);
-  else ux_tiled_quant_entry<kBF16, 128>(nbits, W, N, K, ldw, packed, scales, zeros, st);
+                            void* scales, void* zeros, double* part, hipStream_t st) {
+  if (group == 32) ux_tiled_quant_entry<kBF16, 32>(nbits, W, N, K, ldw, packed, scales, zeros, part, st);
+  else ux_tiled_quant_entry<kBF16, 128>(nbits, W, N, K, ldw, packed, scales, zeros, part, st);
 }
 
 void uintx_tiled_dequant_bf16(int nbits, int group, const void* packed, const void* scales, const void* zeros,

@@ -123,17 +123,21 @@ __device__ __forceinline__ void ux_codes8(const Raw8<typename UxDt<DT>::T>& r, f
 // the qparams of 8/(G/8) of the set's 8 groups (G = 128: lanes 8..15 repeat lanes 0..7)
 // and the set exchanges (1/scale, zp) through LDS; codes are assembled into shard bytes
 // in registers.
-template <int NB, int DT, int G, bool CONTIG>
+// SNR: also the reconstruction sums of the stored values (the dequantize kernel's
+// arithmetic on the codes and scale just written, in its per-thread order), one partial
+// pair per block.
+template <int NB, int DT, int G, bool CONTIG, bool SNR>
 __global__ __launch_bounds__(256) void uintx_quant_tiled(const typename UxDt<DT>::T* __restrict__ W, int64_t ldw,
                                                          FastDiv kdiv, uint32_t L1, Shards sh,
                                                          uint8_t* __restrict__ packed,
                                                          typename UxDt<DT>::T* __restrict__ scales,
-                                                         uint8_t* __restrict__ zeros) {
+                                                         uint8_t* __restrict__ zeros, double* __restrict__ part) {
   using SB = ShardBits<NB>;
   using D = UxDt<DT>;
   constexpr int LG = G / 8;                    // lanes per group
   constexpr int PER = LG >= 8 ? 1 : 8 / LG;    // groups whose qparams one lane computes
   __shared__ typename D::Lds qp_lds[256 / LG * 8];
+  __shared__ typename D::Lds qs_lds[SNR ? 256 / LG * 8 : 1];   // (s, zp) as the dequantize kernel reads them
   const float qmax = (float)((1 << NB) - 1);
   const int lane = threadIdx.x & 63;
   const uint32_t p = blockIdx.x * kBlockPos + (threadIdx.x >> 6) * kWavePos + lane * kLanePos;
@@ -168,11 +172,13 @@ __global__ __launch_bounds__(256) void uintx_quant_tiled(const typename UxDt<DT>
         scales[g] = D::word(q.s);
         zeros[g] = (uint8_t)q.zp;
         set_qp[jj] = D::pack(D::word(q.inv), (uint32_t)q.zp);
+        if constexpr (SNR) qs_lds[(threadIdx.x / LG) * 8 + jj] = D::pack(D::word(q.s), (uint32_t)q.zp);
       }
     }
   }
   __syncthreads();
-  if (!active) return;
+  double sw = 0.0, se = 0.0;
+  if (active) {
   uint32_t clo[8], chi[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -206,6 +212,29 @@ __global__ __launch_bounds__(256) void uintx_quant_tiled(const typename UxDt<DT>
     }
     st8(packed + sh.base1 + p, lo, hi);
   }
+  if constexpr (SNR) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const typename D::Lds w = qs_lds[(threadIdx.x / LG) * 8 + j];
+      const float s = D::lds_value(w), zp = D::lds_zp(w);
+      const uint32_t c[2] = {clo[j], chi[j]};
+      float d[8];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) d[b] = ((float)((c[b >> 2] >> (8 * (b & 3))) & 0xFFu) - zp) * s;
+      if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int b = 0; b < 8; b += 2) round_bf16_pair(d[b], d[b + 1]);
+      } else if constexpr (DT == kF16) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) d[b] = D::rnd(d[b]);
+      }
+      float x[8];
+      ux_widen8<DT>(raw[j], x);
+      acc_err8(x, d, sw, se);
+    }
+  }
+  }
+  if constexpr (SNR) block_sum2_store<256>(sw, se, part);
 }
 
 // ------------------------------------------------------------- tiled dequantize
@@ -467,23 +496,28 @@ __global__ __launch_bounds__(256) void uintx_gemv_tiled(const uint8_t* __restric
 // Contiguous rows (ld == K) index elements directly; otherwise through a fast division.
 template <int DT, int G, int NB>
 void ux_quant_tiled_nb(const void* W, int64_t N, int64_t K, int64_t ldw, void* packed, void* scales, void* zeros,
-                       hipStream_t st) {
+                       double* part, hipStream_t st) {
   using T = typename UxDt<DT>::T;
   const uint32_t numel = (uint32_t)(N * K);
-  hipLaunchKernelGGL((ldw == K ? uintx_quant_tiled<NB, DT, G, true> : uintx_quant_tiled<NB, DT, G, false>),
-                     dim3(uintx_tiles(numel)), dim3(256), 0, st, (const T*)W, ldw, make_fastdiv((uint32_t)K),
-                     numel / 8, shards_of(NB, numel), (uint8_t*)packed, (T*)scales, (uint8_t*)zeros);
+  if (part)
+    hipLaunchKernelGGL((ldw == K ? uintx_quant_tiled<NB, DT, G, true, true> : uintx_quant_tiled<NB, DT, G, false, true>),
+                       dim3(uintx_tiles(numel)), dim3(256), 0, st, (const T*)W, ldw, make_fastdiv((uint32_t)K),
+                       numel / 8, shards_of(NB, numel), (uint8_t*)packed, (T*)scales, (uint8_t*)zeros, part);
+  else
+    hipLaunchKernelGGL((ldw == K ? uintx_quant_tiled<NB, DT, G, true, false> : uintx_quant_tiled<NB, DT, G, false, false>),
+                       dim3(uintx_tiles(numel)), dim3(256), 0, st, (const T*)W, ldw, make_fastdiv((uint32_t)K),
+                       numel / 8, shards_of(NB, numel), (uint8_t*)packed, (T*)scales, (uint8_t*)zeros, part);
 }
 template <int DT, int G>
 void ux_quant_tiled(int nbits, const void* W, int64_t N, int64_t K, int64_t ldw, void* packed, void* scales,
-                    void* zeros, hipStream_t st) {
+                    void* zeros, double* part, hipStream_t st) {
   switch (nbits) {
-    case 2: ux_quant_tiled_nb<DT, G, 2>(W, N, K, ldw, packed, scales, zeros, st); break;
-    case 3: ux_quant_tiled_nb<DT, G, 3>(W, N, K, ldw, packed, scales, zeros, st); break;
-    case 4: ux_quant_tiled_nb<DT, G, 4>(W, N, K, ldw, packed, scales, zeros, st); break;
-    case 5: ux_quant_tiled_nb<DT, G, 5>(W, N, K, ldw, packed, scales, zeros, st); break;
-    case 6: ux_quant_tiled_nb<DT, G, 6>(W, N, K, ldw, packed, scales, zeros, st); break;
-    default: ux_quant_tiled_nb<DT, G, 7>(W, N, K, ldw, packed, scales, zeros, st); break;
+    case 2: ux_quant_tiled_nb<DT, G, 2>(W, N, K, ldw, packed, scales, zeros, part, st); break;
+    case 3: ux_quant_tiled_nb<DT, G, 3>(W, N, K, ldw, packed, scales, zeros, part, st); break;
+    case 4: ux_quant_tiled_nb<DT, G, 4>(W, N, K, ldw, packed, scales, zeros, part, st); break;
+    case 5: ux_quant_tiled_nb<DT, G, 5>(W, N, K, ldw, packed, scales, zeros, part, st); break;
+    case 6: ux_quant_tiled_nb<DT, G, 6>(W, N, K, ldw, packed, scales, zeros, part, st); break;
+    default: ux_quant_tiled_nb<DT, G, 7>(W, N, K, ldw, packed, scales, zeros, part, st); break;
   }
 }
 
@@ -516,8 +550,8 @@ void ux_deq_tiled(int nbits, const void* packed, const void* scales, const void*
 // float32, and the error sink. Instantiated per (dtype, group) in its own source file.
 template <int DT, int G>
 void ux_tiled_quant_entry(int nbits, const void* W, int64_t N, int64_t K, int64_t ldw, void* packed, void* scales,
-                          void* zeros, hipStream_t st) {
-  ux_quant_tiled<DT, G>(nbits, W, N, K, ldw, packed, scales, zeros, st);
+                          void* zeros, double* part, hipStream_t st) {
+  ux_quant_tiled<DT, G>(nbits, W, N, K, ldw, packed, scales, zeros, part, st);
 }
 template <int DT, int G>
 void ux_tiled_dequant_entry(int nbits, const void* packed, const void* scales, const void* zeros, int64_t N,

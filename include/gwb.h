@@ -176,6 +176,21 @@ int gwb_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t 
             const gwb_qtensors* in, double* d_out, void* workspace, size_t workspace_bytes,
             void* stream);
 
+/* Quantize and SNR in one call: what gwb_quantize followed by gwb_snr on the stored
+ * tensors computes (page export_gptq_cpu.py computes its SNR inside its quantize
+ * functions; here it is the SNR of the stored values, as gwb_snr defines it), with the
+ * sums formed by the quantize kernel from the weights it has loaded and the values it
+ * stores, so W is read once: MXFP4 (both tie modes), GPTQ sym / asym (groups in index
+ * order; up to 16384 tiles of 32 rows x 512 k, larger matrices take the two passes) and
+ * uintx in the tiled layout. Other shapes run the two calls in turn. Act-order formats:
+ * GWB_E_ARG (they quantize with gwb_quantize_act_order). Arguments as gwb_quantize plus
+ * d_out (device, 3 doubles, as gwb_snr); workspace at least gwb_sizes.workspace bytes,
+ * 16-byte aligned. The sums match gwb_snr's up to the float64 summation order (the
+ * MXFP4 pass runs the error kernel's order). N or K of 0: GWB_E_SHAPE.              */
+int gwb_quantize_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
+                     const gwb_qtensors* out, double* d_out, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
 /* Workspace bytes for gwb_awq_search_mxfp4 on an [N, K] weight. Host only. */
 int gwb_awq_workspace(int64_t N, int64_t K, int32_t n_alpha, int64_t max_rows, size_t* bytes);
 

@@ -226,6 +226,20 @@ def test_fold_validates_before_launch():
     assert go(N=1 << 20, K=1 << 12, ldw=1 << 12, ldo=1 << 12) == gwb.E_UNSUPPORTED
 
 
+def test_quantize_snr_validation():
+    P = ctypes.c_void_p
+    fake = 1 << 20
+    qt = gwb.QTensors(fake, fake, fake, None)
+    sp = gwb.make_spec("mxfp4", 4, 32)
+    def go(spec=sp, N=64, K=256, W=fake, d=fake, ws=fake, wsb=1 << 20):
+        return lib.gwb_quantize_snr(ctypes.byref(spec), P(W), N, K, K, ctypes.byref(qt), P(d), P(ws), wsb, None)
+    assert go(d=None) == gwb.E_ARG
+    assert go(N=0) == gwb.E_SHAPE and go(K=0) == gwb.E_SHAPE
+    assert go(wsb=16) == gwb.E_SIZE
+    assert go(ws=fake + 8) == gwb.E_UNSUPPORTED
+    assert go(spec=gwb.make_spec("gptq_sym_act", 4, 128)) == gwb.E_ARG
+
+
 def test_gemv_sizes_and_validation():
     P = ctypes.c_void_p
     fake = 1 << 20
