@@ -3,12 +3,12 @@
 
 One step = the whole hot path over the gate_up-shaped bf16 weight [34816, 5120]:
 for each of MXFP4 (block 32), GPTQ symmetric and asymmetric (group 128) and affine
-uintx 2..7 bits (group 64): quantize+pack, unpack+dequantize to bf16, fused
-reconstruction SNR; then the AWQ alpha search (11 alphas) on the 2048-row strided
-subsample. Inputs are resident in HBM before timing starts.
+uintx 2..7 bits (group 64): quantize+pack with the reconstruction SNR of the stored
+values formed in the same pass over W, then unpack+dequantize to bf16; then the AWQ
+alpha search (11 alphas) on the 2048-row strided subsample. Inputs are resident in HBM before timing starts.
 
 value = weight GB/s = (2 bytes * N * K) * (quantize + dequantize passes) / step time.
-The timed steps carry no per-op markers (an event pair around each of the 40 launches
+The timed steps carry no per-op markers (an event pair around each of the 31 launches
 costs about 0.2 ms of the step): an untimed pass with an event pair per op gives the
 breakdown and names the op with the largest share, and in the timed steps one event
 pair brackets that op alone. The roofline object is for that kernel: its algorithmic
@@ -36,8 +36,9 @@ N, K = 34816, 5120
 PEAK_HBM_GBPS = 8000.0
 PEAK_MFMA_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 # kernels launched by one library call of each step op (quantize, dequantize: one; SNR: the
-# error pass and its finalize; AWQ: table pow, table scale, search, finalize)
-OP_KERNELS = {"quant": 1, "dequant": 1, "snr": 2, "search": 4}
+# error pass and its finalize; quantize with the SNR fused: the quantize pass and the same
+# finalize; AWQ: table pow, table scale, search, finalize)
+OP_KERNELS = {"quant": 1, "dequant": 1, "snr": 2, "quant_snr": 2, "search": 4}
 FORMATS = [("mxfp4", 4, 32), ("gptq_sym", 4, 128), ("gptq_asym", 4, 128)] + \
           [("uintx", b, 64) for b in range(2, 8)]
 ALPHAS = tuple(i / 10 for i in range(11))
@@ -59,7 +60,7 @@ def algo_bytes(op: str, fmt: str, nbits: int, n: int, k: int) -> float:
             packed += nk / 128 / 2                     # qzeros (sym dequant ignores them)
     else:
         packed = nk * nbits / 8 + nk / 64 * 3          # shards + bf16 scale + uint8 zp
-    if op == "quant":
+    if op in ("quant", "quant_snr"):              # the fused SNR reads nothing more
         return 2 * nk + packed
     if op == "dequant":
         return packed + 2 * nk
@@ -336,13 +337,10 @@ def main():
     for f, b, g in FORMATS:
         key = label(f, b)
         q = qs[key]
-        ops.append((f"{key}.quant", f"{f}.quant", algo_bytes("quant", f, b, N, K), 2 * N * K,
-                    gwb.prepare_quantize(Wd, q, workspace=ws)))
-        # the SNR pass before dequantization: the quantizer's packed output (written back from
-        # the Infinity Cache after it ends) then drains during a read-heavy pass (2.211 -> 2.200
-        # ms per step measured)
-        ops.append((f"{key}.snr", f"{f}.snr", algo_bytes("snr", f, b, N, K), 0,
-                    gwb.prepare_snr(Wd, q, snr_out[key], ws)))
+        # quantize+pack with the reconstruction SNR of the stored values formed in the same
+        # pass (gwb_quantize_snr: W is read once for both)
+        ops.append((f"{key}.quant_snr", f"{f}.quant_snr", algo_bytes("quant_snr", f, b, N, K), 2 * N * K,
+                    gwb.prepare_quantize_snr(Wd, q, snr_out[key], ws)))
         ops.append((f"{key}.dequant", f"{f}.dequant", algo_bytes("dequant", f, b, N, K), 2 * N * K,
                     gwb.prepare_dequantize(q, deq)))
     awq_err = torch.empty(len(ALPHAS), dtype=torch.float64, device=dev)
@@ -436,8 +434,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "bf16 [34816, 5120] (N(0, 0.015) x row gain lognormal(0, 0.5), seed 3): "
-                        "mxfp4 b32, gptq_sym g128, gptq_asym g128, uintx2..7 g64 -> quantize+pack, "
-                        "unpack+dequant to bf16, fused SNR; AWQ alpha search (11 alphas) on the 2048 "
+                        "mxfp4 b32, gptq_sym g128, gptq_asym g128, uintx2..7 g64 -> quantize+pack with "
+                        "the stored values' SNR in the same pass, unpack+dequant to bf16; AWQ alpha "
+                        "search (11 alphas) on the 2048 "
                         "strided rows with a[5120] lognormal(0, 1) seed 5",
             "N": N, "K": K, "passes_per_step": sum(1 for op in ops if op[3]),
         },
