@@ -310,8 +310,8 @@ def main():
     ap.add_argument("--cpu-awq-rows", type=int, default=384)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the quantization of "
-              "one weight is sharded by rows only in design; see the sharding notes). Run with --gpus 1.",
+        print("bench.py measures one GPU: the library has no multi-GPU path (the quantization of "
+              "one weight would shard by rows, one row range per GPU; nothing here runs it). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
