@@ -10,6 +10,7 @@ from golden.golden import floats, load
 from group_wise_bit_amd import workloads
 
 G = load("gptq_worked_group8.txt")
+PS = load("gptq_page_snr.txt")
 
 
 def _hexwords(s):
@@ -234,3 +235,22 @@ def test_dequant_g_idx_exact(sym):
             assert F(d[col, k]) == want
     # without g_idx the same tensors would be read as contiguous groups: a different weight
     assert not np.array_equal(d, gq.dequantize(q["qweight"], q["scales"], q["qzeros"], 64, sym))
+
+
+def _page_snr_weights():
+    t = np.float32(float(PS["t_f32"]))
+    assert float(t) == 1 + 2 ** -11 + 2 ** -20
+    ws = np.zeros((8, 8), np.float32)
+    ws[0, 0], ws[1, 0], ws[1, 1] = 8 * t, 4 * t, 2 * t
+    wa = np.zeros((8, 8), np.float32)
+    wa[0, 0], wa[0, 1] = 15 * t, 7.5 * t
+    return ws, wa
+
+
+def test_page_in_function_snr_closed_form():
+    """quantize_sym / quantize_asym's snr_db_f32 is the page's in-function SNR with the
+    float32 scale: closed forms 10 log10(67.2) and 10 log10(1125) (tests/golden)."""
+    import math
+    ws, wa = _page_snr_weights()
+    assert abs(gq.quantize_sym(ws, 8)["snr_db_f32"] - 10 * math.log10(float(PS["sym_snr_ratio"]))) < 1e-9
+    assert abs(gq.quantize_asym(wa, 8)["snr_db_f32"] - 10 * math.log10(float(PS["asym_snr_ratio"]))) < 1e-9

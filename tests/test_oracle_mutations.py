@@ -151,3 +151,28 @@ def test_gemv_transposed_weight_caught(monkeypatch):
                         @ np.asarray(deq, np.float64) if np.shape(x)[-1] == np.shape(deq)[0]
                         else np.zeros((np.atleast_2d(x).shape[0], np.shape(deq)[0])))
     _fails(tgv.test_orientation_and_linearity)
+
+
+def test_gptq_page_snr_with_fp16_scale_caught(monkeypatch):
+    """The page's in-function SNR formed with the stored fp16 scale instead of the
+    float32 one must fail the closed-form pin."""
+    for name, sym in (("quantize_sym", True), ("quantize_asym", False)):
+        orig = getattr(gq, name)
+        def fp16_snr(w, group=128, _orig=orig, _sym=sym):
+            q = _orig(w, group)
+            d = gq.dequantize(q["qweight"], q["scales"], q["qzeros"], group, _sym)
+            q["snr_db_f32"] = snr.snr_db(w, d)
+            return q
+        monkeypatch.setattr(gq, name, fp16_snr)
+    _fails(tg.test_page_in_function_snr_closed_form)
+
+
+def test_gptq_page_snr_per_column_caught(monkeypatch):
+    """Norms taken per output column (SNRs averaged) instead of over the whole tensor."""
+    def per_column(wt, deq):
+        num = np.sqrt(np.sum(wt.astype(np.float64) ** 2, axis=0))
+        den = np.maximum(np.sqrt(np.sum((wt - deq).astype(np.float64) ** 2, axis=0)), 1e-12)
+        live = num > 0
+        return float(np.mean(20.0 * np.log10(num[live] / den[live])))
+    monkeypatch.setattr(gq, "_snr_page", per_column)
+    _fails(tg.test_page_in_function_snr_closed_form)
