@@ -4,15 +4,23 @@
 One step = the whole hot path over the gate_up-shaped bf16 weight [34816, 5120]:
 for each of MXFP4 (block 32), GPTQ symmetric and asymmetric (group 128) and affine
 uintx 2..7 bits (group 64): quantize+pack with the reconstruction SNR of the stored
-values formed in the same pass over W, then unpack+dequantize to bf16; then the AWQ
-alpha search (11 alphas) on the 2048-row strided subsample. Inputs are resident in HBM before timing starts.
+values formed in the same pass over W; then for each format unpack+dequantize to bf16;
+then the AWQ alpha search (11 alphas) on the 2048-row strided subsample. Inputs are
+resident in HBM before timing starts.
+
+Cold caches: the weight and the dequantized output exist in three copies, and
+consecutive ops use different copies; a dequantize reads packed tensors written eight or
+more passes earlier. No op finds its input in the 256 MB Infinity Cache. Warm figures
+(each op back to back on the same buffers) are reported beside the cold ones, as are
+cold figures of plain quantize+pack (no SNR), which is not part of the step.
 
 value = weight GB/s = (2 bytes * N * K) * (quantize + dequantize passes) / step time.
-The timed steps carry no per-op markers (an event pair around each of the 31 launches
-costs about 0.2 ms of the step): an untimed pass with an event pair per op gives the
-breakdown and names the op with the largest share, and in the timed steps one event
-pair brackets that op alone. The roofline object is for that kernel: its algorithmic
-bytes per launch / its average HIP-event duration in the timed steps, against 8 TB/s.
+The timed steps carry no per-op markers (an event pair around each launch costs about
+0.2 ms of the step): an untimed pass with an event pair per op gives the breakdown and
+names the op with the largest share, and in the timed steps one event pair brackets that
+op alone. The roofline object is for that kernel: its algorithmic bytes per launch / its
+average HIP-event duration in the timed steps, against 8 TB/s; beside it the same-run
+streaming ceilings of gwb_stream_bench.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--breakdown-steps 10]
                     [--no-cpu-baseline] [--no-extras]
@@ -39,6 +47,7 @@ PEAK_MFMA_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 # error pass and its finalize; quantize with the SNR fused: the quantize pass and the same
 # finalize; AWQ: table pow, table scale, search, finalize)
 OP_KERNELS = {"quant": 1, "dequant": 1, "snr": 2, "quant_snr": 2, "search": 4}
+COPIES = 3                       # weight / output copies in rotation (3 x 356 MB > the Infinity Cache)
 FORMATS = [("mxfp4", 4, 32), ("gptq_sym", 4, 128), ("gptq_asym", 4, 128)] + \
           [("uintx", b, 64) for b in range(2, 8)]
 ALPHAS = tuple(i / 10 for i in range(11))
@@ -91,58 +100,77 @@ def family_of(op: str) -> str:
     return "gptq" if head.startswith("gptq") else ("uintx" if head.startswith("uintx") else head)
 
 
-def measured_traffic(op: str):
-    """HBM bytes per launch of op's main kernel from the committed rocprofv3 --pmc
-    summary (profiles/traffic.json), if it was taken on the current kernel source;
-    else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def measured_counters(op: str) -> dict:
+    """Counters of op's main kernel from the committed rocprofv3 --pmc summary
+    (profiles/counters.json): HBM-side bytes per launch (calibrated FETCH_SIZE +
+    WRITE_SIZE), VALU instructions per launch and the kernel's duration in that run, if
+    they were taken on the current kernel source; else {}."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
-        return None
+        return {}
     try:
         rec = json.load(open(path))["ops"].get(op)
     except (OSError, ValueError, KeyError):
-        return None
+        return {}
     if not rec or rec.get("source_sha") != source_digest(family_of(op)):
-        return None
-    return rec.get("bytes_per_launch")
+        return {}
+    return rec
 
 
 def cpu_baseline(W_cpu: torch.Tensor, a_cpu: torch.Tensor, rows: int, awq_rows: int):
     """The oracle, as it stands, on the first `rows` rows (all formats: quantize,
-    dequantize, SNR) plus the AWQ search on `awq_rows` rows of the subsample."""
+    dequantize, SNR) plus the AWQ search on `awq_rows` rows of the subsample. Row chunks
+    of 544 run on host threads (numpy releases the interpreter lock in its array ops);
+    each AWQ alpha is one task."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle.awq as oawq
     import oracle.gptq as ogq
     import oracle.mxfp4 as omx
     import oracle.snr as osnr
     import oracle.uintx as oux
 
+    host_cores = os.cpu_count() or 1
+    threads = max(1, min(16, host_cores))
     w = W_cpu[:rows].float().numpy()
     wa = W_cpu[0:AWQ_ROWS * (N // AWQ_ROWS):N // AWQ_ROWS][:awq_rows].float().numpy()
-    t0 = time.perf_counter()
-    passes = 0
-    for fmt, nbits, g in FORMATS:
+    an = a_cpu.numpy()
+    chunk = 544
+
+    def one(task):
+        fmt, nbits, g, r0 = task
+        x = w[r0:r0 + chunk]
         if fmt == "mxfp4":
-            p, e = omx.quantize(w)
+            p, e = omx.quantize(x)
             d = omx.dequantize(p, e, K)
         elif fmt.startswith("gptq"):
-            o = (ogq.quantize_sym if fmt == "gptq_sym" else ogq.quantize_asym)(w, g)
+            o = (ogq.quantize_sym if fmt == "gptq_sym" else ogq.quantize_asym)(x, g)
             d = ogq.dequantize(o["qweight"], o["scales"], o["qzeros"], g, fmt == "gptq_sym")
         else:
-            o = oux.quantize(w, nbits, g)
-            d = oux.dequantize(o["packed"], o["scale_bytes"], o["zero_point"], nbits, rows, K, g)
-        osnr.snr_db(w, d)
-        passes += 2
-    oawq.search(wa, a_cpu.numpy(), ALPHAS, max_rows=awq_rows)
-    dt = time.perf_counter() - t0
+            o = oux.quantize(x, nbits, g)
+            d = oux.dequantize(o["packed"], o["scale_bytes"], o["zero_point"], nbits, x.shape[0], K, g)
+        return osnr.sums(x, d)
+
+    tasks = [(f, b, g, r0) for f, b, g in FORMATS for r0 in range(0, rows, chunk)]
+    table = oawq.scale_table(an, ALPHAS)
+    t0, c0 = time.perf_counter(), time.process_time()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, tasks))
+        list(ex.map(lambda i: oawq.weighted_error(wa, an, table[i]), range(len(ALPHAS))))
+    dt, cpu_s = time.perf_counter() - t0, time.process_time() - c0
+    passes = 2 * len(FORMATS)
     return {
         "value": round(2.0 * rows * K * passes / dt / 1e9, 6),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": threads,
+        "host_cores": host_cores,
         "kind": "oracle",
         "sample": f"first {rows} rows of the 34816x5120 weight through all 9 format variants "
                   f"(quantize, dequantize, SNR) + AWQ search on {awq_rows} of the 2048 strided rows; "
-                  f"{dt:.1f} s single-threaded numpy; value uses the same weight-bytes formula as the GPU",
+                  f"{dt:.1f} s wall, {cpu_s:.1f} s CPU on {threads} threads (544-row chunks and one task per "
+                  f"alpha) of a {host_cores}-core host; value uses the same weight-bytes formula as the GPU",
         "seconds": round(dt, 2),
+        "cpu_seconds": round(cpu_s, 2),
     }
 
 
@@ -159,24 +187,33 @@ def _time_op(fn, reps: int = 21, warm: int = 3) -> float:
     return e0.elapsed_time(e1) * 1e3 / reps
 
 
-def measure_extras(gwb, workloads, Wd, ad, dev):
+def measure_extras(gwb, workloads, Ws, deqs, ad, dev):
     """Paths next to the hot path, timed on their own after the step (not part of
     value): the AWQ fold of the gate_up weight (columns * s) straight to MXFP4, the same
     fold also writing the folded bf16 weight, and the decode GEMV reading a packed
     131072 x 2048 lm_head (GPTQ sym g128, MXFP4, uintx4 g64, GPTQ sym g128 with act-order
     groups in a seeded channel order) for one activation row, and
     the uintx variants (float16 / float32 weights, groups 32 / 128) at [3072, 12288], and
-    GPTQ with act-order groups on the gate_up weight."""
+    GPTQ with act-order groups on the gate_up weight. Launches cycle over copies of
+    their inputs and outputs, so each starts cold."""
     out = []
+    Wd = Ws[0]
     s = torch.from_numpy(gwb.awq_scales_host(ad.cpu(), (0.5,))[0].numpy()).to(dev)
-    mx = gwb.fold_mxfp4(Wd, s, "mul", want_folded=False)["mxfp4"]
-    folded = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+    mxs = [gwb.fold_mxfp4(Wd, s, "mul", want_folded=False)["mxfp4"] for _ in Ws]
     nk = N * K
+
+    def cycle(calls):
+        it = {"i": 0}
+
+        def fn():
+            calls[it["i"] % len(calls)]()
+            it["i"] += 1
+        return fn
     cases = [
         ("fold_mxfp4.columns_to_mxfp4", 2 * nk + nk / 2 + nk / 32 + 4 * K,
-         gwb.prepare_fold_mxfp4(Wd, s, "mul", None, "none", None, mx)),
+         cycle([gwb.prepare_fold_mxfp4(w, s, "mul", None, "none", None, m) for w, m in zip(Ws, mxs)])),
         ("fold_mxfp4.columns_to_bf16_and_mxfp4", 4 * nk + nk / 2 + nk / 32 + 4 * K,
-         gwb.prepare_fold_mxfp4(Wd, s, "mul", None, "none", folded, mx)),
+         cycle([gwb.prepare_fold_mxfp4(w, s, "mul", None, "none", o, m) for w, o, m in zip(Ws, deqs, mxs)])),
     ]
     # decode GEMV on the 131072 x 2048 lm_head (one activation row), weights packed
     HN, HK = 131072, 2048
@@ -195,14 +232,6 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
     wsu = torch.empty(gwb.gemv_workspace_bytes(qu[0], 1), dtype=torch.uint8, device=dev)
     wsg = torch.empty(gwb.gemv_workspace_bytes(qg[0], 1), dtype=torch.uint8, device=dev)
     hk = HN * HK
-
-    def cycle(calls):
-        it = {"i": 0}
-
-        def fn():
-            calls[it["i"] % len(calls)]()
-            it["i"] += 1
-        return fn
     gemv_cases = [
         ("gemv.gptq_sym_g128.lm_head_b1", hk / 2 + hk / 128 * 2 + 2 * HK + 4 * HN,
          cycle([gwb.prepare_gemv(q, xh, yh, wsg) for q in qg])),
@@ -232,32 +261,32 @@ def measure_extras(gwb, workloads, Wd, ad, dev):
                            ("bf16", torch.bfloat16, 32), ("bf16", torch.bfloat16, 128)):
         esz = torch.tensor([], dtype=tdt).element_size()
         copies = -(-320 * 2 ** 20 // (esz * unk))
-        Ws = [workloads.uintx_weight(UN, UK, dtype=tdt).to(dev) for _ in range(copies)]
-        qs = [gwb.quantize(w, "uintx", nbits=4, group=group) for w in Ws]
+        Vs = [workloads.uintx_weight(UN, UK, dtype=tdt).to(dev) for _ in range(copies)]
+        qs = [gwb.quantize(w, "uintx", nbits=4, group=group) for w in Vs]
         ws = torch.empty(max(qs[0].sizes["workspace"], 16), dtype=torch.uint8, device=dev)
         outs = [torch.empty(UN, UK, dtype=tdt, device=dev) for _ in range(copies)]
         res = torch.empty(3, dtype=torch.float64, device=dev)
         packed = unk / 2 + unk / group * (esz + 1)
         tag = f"uintx4_{dt}_g{group}"
         var_cases += [
-            (f"{tag}.quant", esz * unk + packed, cycle([gwb.prepare_quantize(w, q, ws) for w, q in zip(Ws, qs)])),
+            (f"{tag}.quant", esz * unk + packed, cycle([gwb.prepare_quantize(w, q, ws) for w, q in zip(Vs, qs)])),
             (f"{tag}.dequant", packed + esz * unk, cycle([gwb.prepare_dequantize(q, o) for q, o in zip(qs, outs)])),
-            (f"{tag}.snr", esz * unk + packed, cycle([gwb.prepare_snr(w, q, res, ws) for w, q in zip(Ws, qs)])),
+            (f"{tag}.snr", esz * unk + packed, cycle([gwb.prepare_snr(w, q, res, ws) for w, q in zip(Vs, qs)])),
         ]
     # GPTQ with act-order groups (sym and asym, g128) on the gate_up weight, channels in
     # the order of decreasing activation statistic (the AWQ stat a)
     perm = torch.argsort(ad, descending=True).to(torch.int32).contiguous()
     act_cases = []
     for fmt in ("gptq_sym_act", "gptq_asym_act"):
-        qa = gwb.quantize(Wd, fmt, group=128, perm=perm)
-        wsa = torch.empty(qa.sizes["workspace"], dtype=torch.uint8, device=dev)
+        qa = [gwb.quantize(w, fmt, group=128, perm=perm) for w in Ws]
+        wsa = torch.empty(qa[0].sizes["workspace"], dtype=torch.uint8, device=dev)
         res = torch.empty(3, dtype=torch.float64, device=dev)
         packed = nk / 2 + nk / 128 * 2 + (nk / 128 / 2 if fmt == "gptq_asym_act" else 0) + 4 * K
         act_cases += [
             (f"{fmt}_g128.quant", 2 * nk + packed + nk / 128 / 2 * (fmt == "gptq_sym_act"),
-             gwb.prepare_quantize(Wd, qa, wsa, perm=perm)),
-            (f"{fmt}_g128.dequant", packed + 2 * nk, gwb.prepare_dequantize(qa, folded)),
-            (f"{fmt}_g128.snr", 2 * nk + packed, gwb.prepare_snr(Wd, qa, res, wsa)),
+             cycle([gwb.prepare_quantize(w, q, wsa, perm=perm) for w, q in zip(Ws, qa)])),
+            (f"{fmt}_g128.dequant", packed + 2 * nk, cycle([gwb.prepare_dequantize(q, o) for q, o in zip(qa, deqs)])),
+            (f"{fmt}_g128.snr", 2 * nk + packed, cycle([gwb.prepare_snr(w, q, res, wsa) for w, q in zip(Ws, qa)])),
         ]
     for name, abytes, fn in cases + gemv_cases + var_cases + act_cases:
         us = _time_op(fn)
@@ -296,6 +325,39 @@ def measure_gemm(gwb, workloads, Wd, dev):
     return out
 
 
+def _avg_us(pairs) -> float:
+    return float(np.mean([e0.elapsed_time(e1) for e0, e1 in pairs])) * 1e3
+
+
+def stream_ceilings(gwb, dev):
+    """Same-run streaming ceilings (gwb_stream_bench, 1 GiB, best of a few grid sizes and
+    both work assignments):
+    copy, read only, quantize-shaped (4 bytes read per byte written) and
+    dequantize-shaped (1 byte read per 4 written), GB/s of both sides together."""
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    moved = {"copy": 2.0 * nb, "read": 1.0 * nb, "read4_write1": 1.25 * nb, "read1_write4": 1.25 * nb}
+    out = {}
+    for pat, b in moved.items():
+        best = 0.0
+        for strided in (False, True):
+            for blocks in (256, 512, 768, 1024, 2048):
+                for _ in range(2):
+                    gwb.stream_bench(pat, dst, src, blocks, strided)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(8):
+                    gwb.stream_bench(pat, dst, src, blocks, strided)
+                e1.record()
+                torch.cuda.synchronize()
+                best = max(best, b * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        out[pat] = round(best, 1)
+    del src, dst
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,8 +368,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the paths timed beside the step (keeps a profile to the step's kernels)")
-    ap.add_argument("--cpu-rows", type=int, default=6528)          # 17 x 384: the step's 17:1 ratio
-    ap.add_argument("--cpu-awq-rows", type=int, default=384)
+    ap.add_argument("--cpu-rows", type=int, default=4352)          # 17 x 256: the step's 17:1 ratio
+    ap.add_argument("--cpu-awq-rows", type=int, default=256)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (the quantization of "
@@ -321,47 +383,42 @@ def main():
     torch.cuda.set_device(dev)
     W_cpu = workloads.mxfp4_weight(N, K, seed=3)
     a_cpu = workloads.awq_activation_stat(K, seed=5)
-    Wd = W_cpu.to(dev)
+    # COPIES copies of the weight at different addresses (same values): consecutive ops
+    # read different copies, so no op finds its input in the 256 MB Infinity Cache
+    Ws = [W_cpu.to(dev) for _ in range(COPIES)]
+    Wd = Ws[0]
     ad = a_cpu.to(dev)
 
     # every buffer allocated up front: nothing is allocated in the timed region
     qs = {label(f, b): gwb.quantize(Wd, f, nbits=b, group=g) for f, b, g in FORMATS}
-    deq = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
+    deqs = [torch.empty(N, K, dtype=torch.bfloat16, device=dev) for _ in range(COPIES)]
     ws = torch.empty(max(q.sizes["workspace"] for q in qs.values()) + 16, dtype=torch.uint8, device=dev)
     snr_out = {k: torch.empty(3, dtype=torch.float64, device=dev) for k in qs}
     awq_ws = torch.empty(gwb.awq_workspace_bytes(N, K, len(ALPHAS), AWQ_ROWS), dtype=torch.uint8, device=dev)
     s_table = torch.empty(len(ALPHAS), K, dtype=torch.float32, device=dev)
-
-    # calls marshalled once: one C call per launch inside the timed region
-    ops = []   # (name, kernel key, algorithmic bytes, weight bytes, fn)
-    for f, b, g in FORMATS:
-        key = label(f, b)
-        q = qs[key]
-        # quantize+pack with the reconstruction SNR of the stored values formed in the same
-        # pass (gwb_quantize_snr: W is read once for both)
-        ops.append((f"{key}.quant_snr", f"{f}.quant_snr", algo_bytes("quant_snr", f, b, N, K), 2 * N * K,
-                    gwb.prepare_quantize_snr(Wd, q, snr_out[key], ws)))
-        ops.append((f"{key}.dequant", f"{f}.dequant", algo_bytes("dequant", f, b, N, K), 2 * N * K,
-                    gwb.prepare_dequantize(q, deq)))
     awq_err = torch.empty(len(ALPHAS), dtype=torch.float64, device=dev)
     awq_best = torch.empty(1, dtype=torch.int32, device=dev)
+
+    # The step, calls marshalled once (one C call per launch in the timed region): every
+    # format's quantize+pack with the SNR of its stored values formed in the same pass
+    # (gwb_quantize_snr: W read once for both), then every format's unpack+dequantize to
+    # bf16, then the AWQ search. Op i reads weight copy i % COPIES and dequantize i writes
+    # output copy i % COPIES; a dequantize reads packed tensors written eight or more
+    # passes (> 2 GB of traffic) earlier. Every op therefore starts cold.
+    ops = []   # (name, algorithmic bytes, weight bytes, fn)
+    for i, (f, b, g) in enumerate(FORMATS):
+        key = label(f, b)
+        ops.append((f"{key}.quant_snr", algo_bytes("quant_snr", f, b, N, K), 2 * N * K,
+                    gwb.prepare_quantize_snr(Ws[i % COPIES], qs[key], snr_out[key], ws)))
+    for i, (f, b, g) in enumerate(FORMATS):
+        key = label(f, b)
+        ops.append((f"{key}.dequant", algo_bytes("dequant", f, b, N, K), 2 * N * K,
+                    gwb.prepare_dequantize(qs[key], deqs[i % COPIES])))
     awq_bytes = AWQ_ROWS * K * 2 + len(ALPHAS) * K * 4 + K * 4
-    ops.append(("awq.search", "awq", awq_bytes, 0,
+    ops.append(("awq.search", awq_bytes, 0,
                 gwb.prepare_awq_search(Wd, ad, ALPHAS, AWQ_ROWS, s_table, awq_err, awq_best, awq_ws)))
 
-    # same-run bandwidth ceiling: 1 GiB device-to-device with the library's copy kernel
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        gwb.stream_copy(dst, src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(10):
-        gwb.stream_copy(dst, src)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_gbps = 2 * (1 << 30) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del src, dst
+    ceil = stream_ceilings(gwb, dev)
 
     # event pairs created before anything is timed
     bd_steps = max(args.breakdown_steps, 1)
@@ -375,13 +432,13 @@ def main():
             ev = pairs[i] if pairs is not None else (mark_pair if i == mark else None)
             if ev is not None:
                 ev[0].record()
-            op[4]()
+            op[3]()
             if ev is not None:
                 ev[1].record()
 
     for _ in range(args.warmup):
         step()
-    # untimed breakdown pass: one event pair per op
+    # untimed breakdown pass: one event pair per op, in the step's own order (cold)
     for s in range(bd_steps):
         step(pairs=evs[s])
     torch.cuda.synchronize()
@@ -397,28 +454,74 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    dom_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in dom_evs]))
+    dom_us = _avg_us(dom_evs)
+
+    # warm figures for comparison (not graded): each op launched back to back on the same
+    # buffers, so its small inputs (packed tensors, scales) stay in the Infinity Cache
+    warm = {name: _time_op(fn) for name, _, _, fn in ops}
+    # plain quantize+pack (no SNR), cold: launches cycle over the weight copies
+    plain = []
+    for f, b, g in FORMATS:
+        key = label(f, b)
+        calls = [gwb.prepare_quantize(Ws[c], qs[key], ws) for c in range(COPIES)]
+        for c in calls:
+            c()
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(12)]
+        for r, (e0, e1) in enumerate(pairs):
+            e0.record()
+            calls[r % COPIES]()
+            e1.record()
+        torch.cuda.synchronize()
+        plain.append((f"{key}.quant", algo_bytes("quant", f, b, N, K), _avg_us(pairs)))
+
+    def shape_ceiling(name):
+        return ceil["read1_write4"] if name.endswith(".dequant") else ceil["read4_write1"]
 
     breakdown = []
-    for i, (name, key, abytes, wbytes, _) in enumerate(ops):
-        breakdown.append({
-            "op": name, "us": round(avg[i] * 1e3, 2),
-            "hbm_GBps": round(abytes / (avg[i] * 1e-3) / 1e9, 1),
-            "frac_hbm_peak": round(abytes / (avg[i] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-            "weight_GBps": round(wbytes / (avg[i] * 1e-3) / 1e9, 1) if wbytes else None,
-        })
-    dname, dkey, dbytes = ops[dom][0], ops[dom][1], ops[dom][2]
-    achieved = dbytes / (dom_ms * 1e-3) / 1e9
-    traffic = measured_traffic(dname)
-    weight_bytes_step = sum(op[3] for op in ops)
+    for i, (name, abytes, wbytes, _) in enumerate(ops):
+        us = avg[i] * 1e3
+        gbps = abytes / (us * 1e-6) / 1e9
+        rec = {"op": name, "us": round(us, 2), "hbm_GBps": round(gbps, 1),
+               "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+               "weight_GBps": round(wbytes / (us * 1e-6) / 1e9, 1) if wbytes else None,
+               "us_warm": round(warm[name], 2)}
+        if wbytes:
+            rec["frac_stream_ceiling"] = round(gbps / shape_ceiling(name), 4)
+        breakdown.append(rec)
+    for name, abytes, us in plain:
+        gbps = abytes / (us * 1e-6) / 1e9
+        breakdown.append({"op": name, "in_step": False, "us": round(us, 2), "hbm_GBps": round(gbps, 1),
+                          "frac_hbm_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                          "weight_GBps": round(2 * N * K / (us * 1e-6) / 1e9, 1),
+                          "frac_stream_ceiling": round(gbps / ceil["read4_write1"], 4)})
+    dname, dbytes = ops[dom][0], ops[dom][1]
+    achieved = dbytes / (dom_us * 1e-6) / 1e9
+    counters = measured_counters(dname)
+    weight_bytes_step = sum(op[2] for op in ops)
     value = weight_bytes_step / (ms_per_step * 1e-3) / 1e9
 
-    extras = None if args.no_extras else measure_extras(gwb, workloads, Wd, ad, dev)
+    extras = None if args.no_extras else measure_extras(gwb, workloads, Ws, deqs, ad, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(W_cpu, a_cpu, args.cpu_rows, args.cpu_awq_rows)
 
+    roof = {
+        "bound": "hbm", "kernel": dname,
+        "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+        "frac": round(achieved / PEAK_HBM_GBPS, 4),
+        "traffic": counters.get("bytes_per_launch"),
+        "algorithmic_bytes_per_launch": int(dbytes), "avg_launch_us": round(dom_us, 2),
+        # kernels one library call of this op launches (all inside its event pair): a
+        # fused quantize+SNR is the quantize kernel plus the in-order float64 finalize
+        "kernels_in_event_pair": OP_KERNELS[dname.split(".")[1] if "." in dname else dname],
+        "frac_stream_ceiling": round(achieved / shape_ceiling(dname), 4),
+    }
+    if counters.get("valu_insts_per_launch") is not None and counters.get("kernel_us"):
+        # VALU issue load of the dominant kernel: wavefront VALU instructions x 4 cycles
+        # (a wave64 instruction on a 16-lane SIMD) over 1024 SIMDs x 2.4 GHz x its duration
+        roof["valu_frac"] = round(counters["valu_insts_per_launch"] * 4 /
+                                  (1024 * 2.4e9 * counters["kernel_us"] * 1e-6), 4)
     line = {
         "metric": "weight GB/s quantize+pack and unpack+dequant; % of HBM peak (34816x5120)",
         "value": round(value, 2),
@@ -430,28 +533,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
             "workload": "bf16 [34816, 5120] (N(0, 0.015) x row gain lognormal(0, 0.5), seed 3): "
                         "mxfp4 b32, gptq_sym g128, gptq_asym g128, uintx2..7 g64 -> quantize+pack with "
-                        "the stored values' SNR in the same pass, unpack+dequant to bf16; AWQ alpha "
-                        "search (11 alphas) on the 2048 "
-                        "strided rows with a[5120] lognormal(0, 1) seed 5",
-            "N": N, "K": K, "passes_per_step": sum(1 for op in ops if op[3]),
+                        "the stored values' SNR in the same pass, then unpack+dequant to bf16; AWQ alpha "
+                        "search (11 alphas) on the 2048 strided rows with a[5120] lognormal(0, 1) seed 5; "
+                        f"every op cold ({COPIES} weight and output copies in rotation)",
+            "N": N, "K": K, "passes_per_step": sum(1 for op in ops if op[2]),
         },
-        "roofline": {
-            "bound": "hbm", "kernel": dname,
-            "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": int(dbytes), "avg_launch_us": round(dom_ms * 1e3, 2),
-            # kernels one library call of this op launches (all inside its event pair): an SNR
-            # pass is its error kernel plus the in-order float64 finalize of the block sums
-            "kernels_in_event_pair": OP_KERNELS[dname.split(".")[1] if "." in dname else dname],
-        },
+        "roofline": roof,
         "cpu_baseline": cpu,
-        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "stream_ceilings_GBps": ceil,
         "breakdown_steps": bd_steps,
         "breakdown": breakdown,
         "extras": extras,

@@ -68,7 +68,7 @@ _SIGS = {
     "gwb_quantize_snr": [ctypes.POINTER(QSpec), _P, _I64, _I64, _I64, ctypes.POINTER(QTensors), _P, _P, _SZ, _P],
     "gwb_awq_workspace": [_I64, _I64, _I32, _I64, ctypes.POINTER(_SZ)],
     "gwb_awq_search_mxfp4": [_P, _I32, _I64, _I64, _I64, _P, _P, _I32, _I64, _P, _P, _P, _P, _SZ, _P],
-    "gwb_stream_copy": [_P, _P, _SZ, _P],
+    "gwb_stream_bench": [_I32, _I32, _P, _P, _SZ, _P],
     "gwb_awq_scales_host": [_P, _I64, _P, _I32, _P],
     "gwb_fold_mxfp4": [_P, _I32, _I64, _I64, _I64, ctypes.POINTER(Fold), _P, _I64, ctypes.POINTER(QTensors), _P],
     "gwb_gemv_workspace": [ctypes.POINTER(QSpec), _I64, _I64, _I64, ctypes.POINTER(_SZ)],
@@ -432,9 +432,19 @@ def prepare_gemm(q: Quantized, x: torch.Tensor, y: torch.Tensor, workspace: Opti
     return Prepared(lib.gwb_gemm, args, (keep, q, x, y, workspace))
 
 
-def stream_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
-    n = src.numel() * src.element_size()
-    _check(lib.gwb_stream_copy(_ptr(dst), _ptr(src), n, _stream()))
+STREAM_PATTERNS = {"copy": 0, "read": 1, "read4_write1": 2, "read1_write4": 3}
+
+
+STREAM_STRIDED = 4
+
+
+def stream_bench(pattern: str, dst: torch.Tensor, src: torch.Tensor, blocks: int = 1024,
+                 strided: bool = False) -> None:
+    """One launch of the streaming ceiling (gwb_stream_bench); both tensors hold the
+    larger side's bytes."""
+    n = min(src.numel() * src.element_size(), dst.numel() * dst.element_size())
+    pat = STREAM_PATTERNS[pattern] | (STREAM_STRIDED if strided else 0)
+    _check(lib.gwb_stream_bench(pat, blocks, _ptr(dst), _ptr(src), n, _stream()))
 
 
 class Prepared:

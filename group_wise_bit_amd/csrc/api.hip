@@ -238,15 +238,20 @@ int gwb_quantize_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K,
     fused = gwb::gptq_quant_snr_fits(spec->group, N, K);
   else if (spec->format == GWB_UINTX)
     fused = gwb::uintx_tiled(spec->w_dtype, spec->group, N, K);
+  const unsigned nb = err_blocks(spec, N, K);
+  size_t need = (size_t)nb * 2 * sizeof(double);
+  if (!fused && spec->format == GWB_UINTX) {   // the two-pass quantize's code buffer shares the workspace
+    const size_t c = gwb::uintx_code_workspace(spec->w_dtype, spec->group, N, K);
+    need = c > need ? c : need;
+  }
+  // checked before anything is enqueued, the unfused pair of calls included
+  if (!workspace || workspace_bytes < need)
+    return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
   if (!fused) {
     if (int rc = gwb_quantize(spec, W, N, K, ldw, out, workspace, workspace_bytes, stream)) return rc;
     return gwb_snr(spec, W, N, K, ldw, out, d_out, workspace, workspace_bytes, stream);
   }
-  const unsigned nb = err_blocks(spec, N, K);
-  const size_t need = (size_t)nb * 2 * sizeof(double);
-  if (!workspace || workspace_bytes < need)
-    return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
-  if (!aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
   double* part = (double*)workspace;
   if (spec->format == GWB_GPTQ_SYM || spec->format == GWB_GPTQ_ASYM)
@@ -610,13 +615,19 @@ int gwb_awq_scales_host(const float* a, int64_t K, const double* alphas, int32_t
   return ok();
 }
 
-int gwb_stream_copy(void* d_dst, const void* d_src, size_t bytes, void* stream) {
+int gwb_stream_bench(int32_t pattern, int32_t blocks, void* d_dst, const void* d_src, size_t bytes, void* stream) {
   if (!d_dst || !d_src) return fail(GWB_E_ARG, "NULL pointer");
-  if (bytes % 16 || !aligned16(d_dst) || !aligned16(d_src))
-    return fail(GWB_E_UNSUPPORTED, "copy needs 16-byte aligned pointers and a multiple of 16 bytes");
+  const int kind = pattern & 3;
+  if (pattern < 0 || pattern > (GWB_STREAM_STRIDED | 3)) return fail(GWB_E_ARG, "unknown stream pattern %d", pattern);
+  if (blocks < 1 || blocks > 65536) return fail(GWB_E_ARG, "blocks must be 1..65536, got %d", blocks);
+  if (bytes % 64 || !aligned16(d_dst) || !aligned16(d_src))
+    return fail(GWB_E_UNSUPPORTED, "stream needs 16-byte aligned pointers and a multiple of 64 bytes");
+  if (kind == 1 && (size_t)blocks * 1024 > bytes)
+    return fail(GWB_E_SIZE, "the read pattern writes blocks * 1024 bytes; %zu given", bytes);
   if (bytes == 0) return ok();
-  gwb::launch_stream_copy(d_dst, d_src, bytes, (hipStream_t)stream);
-  return hip_check("copy launch");
+  gwb::launch_stream_bench(kind, (pattern & GWB_STREAM_STRIDED) != 0, (unsigned)blocks, d_dst, d_src, bytes / 16,
+                           (hipStream_t)stream);
+  return hip_check("stream launch");
 }
 
 }  // extern "C"

@@ -1,5 +1,5 @@
-// Reduction of the fused error kernels' per-block partial sums, and the bandwidth
-// reference copy used by the benchmark.
+// Reduction of the fused error kernels' per-block partial sums, and the streaming
+// bandwidth ceilings the benchmark reports beside them.
 #include <atomic>
 #include <cstdlib>
 
@@ -90,18 +90,79 @@ void launch_err_finalize(const double* part, unsigned nblocks, double* out, hipS
   hipLaunchKernelGGL(err_finalize_kernel, dim3(1), dim3(kFinThreads), 0, st, (const double2*)part, nblocks, out);
 }
 
-__global__ __launch_bounds__(256) void stream_copy_kernel(U4* __restrict__ dst, const U4* __restrict__ src,
-                                                          uint64_t n16) {
-  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
-    dst[i] = src[i];
+// Streaming ceilings for the benchmark (not part of the method): eight 16-byte units per
+// lane in flight, non-temporal loads of the large side, non-temporal 16-byte stores.
+// Pattern: 0 copy (read `units` 16-byte units, write as many), 1 read only (one word per
+// thread out), 2 quantize-shaped (read a 16-byte unit, write 4 bytes), 3 dequantize-shaped
+// (read 4 bytes, write a 16-byte unit). STRIDED: grid-stride over the units; otherwise
+// each block streams one contiguous range.
+template <int PAT, bool STRIDED>
+__global__ __launch_bounds__(256) void stream_bench_kernel(void* __restrict__ dst, const void* __restrict__ src,
+                                                           uint64_t units) {
+  constexpr int U = 8;
+  uint64_t i, end, step;
+  if constexpr (STRIDED) {
+    i = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    end = units;
+    step = (uint64_t)gridDim.x * 256;
+  } else {
+    uint64_t per = (units + gridDim.x - 1) / gridDim.x;
+    per = (per + 256 * U - 1) / (256 * U) * (256 * U);
+    const uint64_t b0 = (uint64_t)blockIdx.x * per;
+    i = b0 + threadIdx.x;
+    end = b0 + per < units ? b0 + per : units;
+    step = 256;
+  }
+  const U4* s16 = (const U4*)src;
+  const uint32_t* s4 = (const uint32_t*)src;
+  U4* d16 = (U4*)dst;
+  uint32_t* d4 = (uint32_t*)dst;
+  uint32_t acc = 0;
+  for (; i + (U - 1) * step < end; i += U * step) {
+    if constexpr (PAT == 3) {
+      uint32_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = s4[i + u * step];
+#pragma unroll
+      for (int u = 0; u < U; ++u) st16_nt(d16 + i + u * step, U4{v[u], v[u] + 1, v[u] + 2, v[u] + 3});
+    } else {
+      U4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = ld16_nt(s16 + i + u * step);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if constexpr (PAT == 0) st16_nt(d16 + i + u * step, v[u]);
+        else if constexpr (PAT == 1) acc ^= v[u].x ^ v[u].w;
+        else d4[i + u * step] = v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+      }
+    }
+  }
+  for (; i < end; i += step) {
+    if constexpr (PAT == 3) {
+      const uint32_t v = s4[i];
+      st16_nt(d16 + i, U4{v, v + 1, v + 2, v + 3});
+    } else {
+      const U4 v = ld16_nt(s16 + i);
+      if constexpr (PAT == 0) st16_nt(d16 + i, v);
+      else if constexpr (PAT == 1) acc ^= v.x ^ v.w;
+      else d4[i] = v.x ^ v.y ^ v.z ^ v.w;
+    }
+  }
+  if constexpr (PAT == 1) d4[(uint64_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
-void launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t st) {
-  uint64_t n16 = bytes / 16;
-  uint64_t g = (n16 + 255) / 256;
-  unsigned grid = (unsigned)(g < kStreamGridCap ? (g ? g : 1) : kStreamGridCap);
-  hipLaunchKernelGGL(stream_copy_kernel, dim3(grid), dim3(256), 0, st, (U4*)dst, (const U4*)src, n16);
+template <bool STRIDED>
+static void stream_bench_launch(int pattern, unsigned blocks, void* d, const void* s, uint64_t units, hipStream_t st) {
+  if (pattern == 0) hipLaunchKernelGGL((stream_bench_kernel<0, STRIDED>), dim3(blocks), dim3(256), 0, st, d, s, units);
+  else if (pattern == 1) hipLaunchKernelGGL((stream_bench_kernel<1, STRIDED>), dim3(blocks), dim3(256), 0, st, d, s, units);
+  else if (pattern == 2) hipLaunchKernelGGL((stream_bench_kernel<2, STRIDED>), dim3(blocks), dim3(256), 0, st, d, s, units);
+  else hipLaunchKernelGGL((stream_bench_kernel<3, STRIDED>), dim3(blocks), dim3(256), 0, st, d, s, units);
+}
+
+void launch_stream_bench(int pattern, bool strided, unsigned blocks, void* dst, const void* src, uint64_t units,
+                         hipStream_t st) {
+  if (strided) stream_bench_launch<true>(pattern, blocks, dst, src, units, st);
+  else stream_bench_launch<false>(pattern, blocks, dst, src, units, st);
 }
 
 }  // namespace gwb

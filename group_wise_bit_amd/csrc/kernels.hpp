@@ -179,6 +179,7 @@ void launch_gemv_finalize(const float* part, int S, int B, int64_t N, void* y, i
                           hipStream_t st);
 
 // ---- measurement copy (common.hip)
-void launch_stream_copy(void* dst, const void* src, size_t bytes, hipStream_t st);
+void launch_stream_bench(int pattern, bool strided, unsigned blocks, void* dst, const void* src, uint64_t units,
+                         hipStream_t st);
 
 }  // namespace gwb

@@ -300,10 +300,20 @@ int gwb_gemm(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
  * within one float32 ulp (float64 summation order). Touches no device memory.      */
 int gwb_awq_scales_host(const float* a, int64_t K, const double* alphas, int32_t n_alpha, float* s_out);
 
-/* Measurement helper, not part of the method: copy `bytes` (a multiple of 16, both
- * pointers 16-byte aligned) from d_src to d_dst with the same 128-bit load/store
- * idiom the quantization kernels use; a same-run bandwidth ceiling. */
-int gwb_stream_copy(void* d_dst, const void* d_src, size_t bytes, void* stream);
+/* Measurement helper, not part of the method: a same-run streaming ceiling. Eight
+ * 16-byte units in flight per lane, non-temporal loads of the larger side and non-temporal
+ * 16-byte stores, in one of four patterns (`bytes` is the larger side):
+ *   0 copy: read `bytes` from d_src, write `bytes` to d_dst;
+ *   1 read: read `bytes` from d_src, write blocks * 1024 bytes (one word per thread) to d_dst;
+ *   2 quantize-shaped: read `bytes` from d_src in 16-byte units, write 4 bytes per unit;
+ *   3 dequantize-shaped: read 4 bytes per 16-byte unit written, `bytes` written.
+ * OR-ing GWB_STREAM_STRIDED into the pattern makes the grid stride over the data; without
+ * it each block streams one contiguous range. Both buffers must hold `bytes` (a multiple
+ * of 64), 16-byte aligned; blocks in 1..65536 (pattern 1: blocks * 1024 <= bytes).
+ * Asynchronous on `stream`. Returns GWB_E_ARG, GWB_E_UNSUPPORTED or GWB_E_SIZE (nothing
+ * launched) on bad arguments. */
+#define GWB_STREAM_STRIDED 4
+int gwb_stream_bench(int32_t pattern, int32_t blocks, void* d_dst, const void* d_src, size_t bytes, void* stream);
 
 /* Message for the last non-zero return on this thread ("" if none). */
 const char* gwb_last_error(void);

@@ -158,7 +158,10 @@ def test_dequantize_snr_awq_validate():
     assert awq(a=None) == gwb.E_ARG
     b = ctypes.c_size_t()
     assert lib.gwb_awq_workspace(34816, 5120, 11, 2048, ctypes.byref(b)) == 0 and b.value > 0
-    assert lib.gwb_stream_copy(fake, fake, 24, None) == gwb.E_UNSUPPORTED
+    assert lib.gwb_stream_bench(0, 64, fake, fake, 24, None) == gwb.E_UNSUPPORTED
+    assert lib.gwb_stream_bench(8, 64, fake, fake, 1 << 20, None) == gwb.E_ARG
+    assert lib.gwb_stream_bench(0, 0, fake, fake, 1 << 20, None) == gwb.E_ARG
+    assert lib.gwb_stream_bench(1, 2048, fake, fake, 1 << 20, None) == gwb.E_SIZE
 
 
 def test_error_message_is_thread_local_and_cleared():
@@ -238,6 +241,13 @@ def test_quantize_snr_validation():
     assert go(wsb=16) == gwb.E_SIZE
     assert go(ws=fake + 8) == gwb.E_UNSUPPORTED
     assert go(spec=gwb.make_spec("gptq_sym_act", 4, 128)) == gwb.E_ARG
+    # shapes the fused kernels do not cover run quantize and SNR as two calls; the
+    # workspace of both is checked before the first launch (fake pointers: a launch here
+    # would fail, a short workspace must be refused first)
+    big = gwb.make_spec("gptq_sym", 4, 128)
+    assert go(spec=big, N=131072, K=4096, wsb=64) == gwb.E_SIZE
+    ux = gwb.make_spec("uintx", 5, 64)
+    assert go(spec=ux, N=10, K=128, wsb=256) == gwb.E_SIZE       # two-pass codes need N*K bytes
 
 
 def test_gemv_sizes_and_validation():
