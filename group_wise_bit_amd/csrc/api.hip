@@ -5,6 +5,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 #include <cmath>
@@ -613,6 +614,52 @@ int gwb_awq_scales_host(const float* a, int64_t K, const double* alphas, int32_t
     for (int64_t k = 0; k < K; ++k) s_out[(int64_t)i * K + k] = (float)(p[k] / g);
   }
   return ok();
+}
+
+// ------------------------------------------------------------ allocation-free SNR
+// gwb_quantize_snr_static keeps the per-block partial sums of the fused pass (and the
+// code buffer of the two-call fallback, where it fits) in this file-scope device array
+// instead of a caller workspace. Each device the library runs on holds its own copy
+// until the process ends. The array's name is a host-side stand-in: host code never
+// passes it to a kernel; it passes the device address hipGetSymbolAddress returns,
+// looked up once per device on that device's first call (with the device current) and
+// kept per device. Every call on one device shares that copy, so calls that overlap on
+// one GPU race. Nothing in it needs to start at zero: each launch writes every partial
+// (or code) that it later reads.
+static __device__ __align__(256) unsigned char scratch[GWB_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int device_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(GWB_E_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(GWB_E_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(GWB_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return GWB_OK;
+}
+}  // namespace
+
+int gwb_quantize_snr_static(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
+                            const gwb_qtensors* out, double* d_out, void* stream) {
+  if (int rc = check_spec(spec, N, K)) return rc;
+  const gwb_sizes sz = sizes_of(spec, N, K);
+  if (sz.workspace > (size_t)GWB_STATIC_SCRATCH_BYTES)
+    return fail(GWB_E_SIZE, "this shape needs %zu bytes of scratch; the static array holds %d", sz.workspace,
+                GWB_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (int rc = device_scratch(&ws)) return rc;
+  return gwb_quantize_snr(spec, W, N, K, ldw, out, d_out, ws, (size_t)GWB_STATIC_SCRATCH_BYTES, stream);
 }
 
 int gwb_stream_bench(int32_t pattern, int32_t blocks, void* d_dst, const void* d_src, size_t bytes, void* stream) {

@@ -300,6 +300,19 @@ int gwb_gemm(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
  * within one float32 ulp (float64 summation order). Touches no device memory.      */
 int gwb_awq_scales_host(const float* a, int64_t K, const double* alphas, int32_t n_alpha, float* s_out);
 
+/* gwb_quantize_snr for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. It takes no
+ * workspace: the scratch it needs (the fused pass's per-block partial sums, or the
+ * two-call fallback's code buffer) lives in a static device array of
+ * GWB_STATIC_SCRATCH_BYTES that each device holds until the process ends. Arguments,
+ * results and errors as gwb_quantize_snr; a shape whose gwb_sizes.workspace exceeds
+ * GWB_STATIC_SCRATCH_BYTES returns GWB_E_SIZE (nothing enqueued). It allocates nothing.
+ * All calls on one device share that device's array: calls that overlap on one GPU
+ * (concurrent streams, other host threads) race and must be serialized by the caller. */
+#define GWB_STATIC_SCRATCH_BYTES 262144
+int gwb_quantize_snr_static(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
+                            const gwb_qtensors* out, double* d_out, void* stream);
+
 /* Measurement helper, not part of the method: a same-run streaming ceiling. Eight
  * 16-byte units in flight per lane, non-temporal loads of the larger side and non-temporal
  * 16-byte stores, in one of four patterns (`bytes` is the larger side):

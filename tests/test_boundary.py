@@ -395,3 +395,19 @@ def test_act_order_gptq_validates():
     assert lib.gwb_gemv_workspace(ctypes.byref(sp), 8, 256, 1, ctypes.byref(b)) == gwb.OK and b.value == 0
     assert lib.gwb_gemv_workspace(ctypes.byref(sp), 64, 2048, 2, ctypes.byref(b)) == gwb.OK
     assert b.value == 4 * 2 * 64 * 4                                # one column tile: a split per 512 k
+
+
+def test_static_quantize_snr_rejects_beyond_its_scratch():
+    """gwb_quantize_snr_static validates before touching the device: a shape whose
+    partials exceed the static array is GWB_E_SIZE, a bad spec keeps its own code."""
+    P = ctypes.c_void_p
+    fake = 1 << 20
+    qt = gwb.QTensors(fake, fake, fake, None)
+    ux = gwb.make_spec("uintx", 4, 64)
+    # 16384 x 17408 bf16: 17408 tiles of 16384 weights, 16 bytes of partials each > 256 KiB
+    assert lib.gwb_quantize_snr_static(ctypes.byref(ux), P(fake), 16384, 17408, 17408, ctypes.byref(qt), P(fake),
+                                       None) == gwb.E_SIZE
+    assert "static" in lib.gwb_last_error().decode()
+    bad = gwb.make_spec("uintx", 8, 64)
+    assert lib.gwb_quantize_snr_static(ctypes.byref(bad), P(fake), 64, 512, 512, ctypes.byref(qt), P(fake),
+                                       None) == gwb.E_UNSUPPORTED

@@ -1,0 +1,65 @@
+"""The allocation-free entry point gwb_quantize_snr_static against gwb_quantize_snr,
+through the C ABI: the same stored tensors and the same three SNR values, bit for bit
+(the same kernels on the same grid, only the scratch memory differs), on two calls in a
+row on one device, the second with a smaller input, for every fused format and for a
+shape that takes the two-call fallback."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from group_wise_bit_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from group_wise_bit_amd import binding as gwb      # must load: no fallback on a GPU machine
+else:  # collected on CPU only to be skipped
+    gwb = None
+
+DEV = "cuda"
+
+
+def _call(fn, W, fmt, nbits, group, with_ws):
+    q = gwb.quantize(W, fmt, nbits=nbits, group=group)
+    for t in (q.codes, q.scales, q.zeros, q.gidx):
+        if t is not None:
+            t.fill_(0x5A)
+    d = torch.full((3,), float("nan"), dtype=torch.float64, device=DEV)
+    N, K = W.shape
+    sp, qt = q.spec(), q.qtensors()
+    if with_ws:
+        ws = torch.empty(max(q.sizes["workspace"], 16), dtype=torch.uint8, device=DEV)
+        rc = fn(ctypes.byref(sp), W.data_ptr(), N, K, W.stride(0), ctypes.byref(qt), d.data_ptr(), ws.data_ptr(),
+                ws.numel(), torch.cuda.current_stream().cuda_stream)
+    else:
+        rc = fn(ctypes.byref(sp), W.data_ptr(), N, K, W.stride(0), ctypes.byref(qt), d.data_ptr(),
+                torch.cuda.current_stream().cuda_stream)
+    assert rc == 0, gwb.lib.gwb_last_error()
+    torch.cuda.synchronize()
+    return q, d.cpu().numpy()
+
+
+def _same(a, b):
+    qa, da = a
+    qb, db = b
+    for x, y in ((qa.codes, qb.codes), (qa.scales, qb.scales), (qa.zeros, qb.zeros), (qa.gidx, qb.gidx)):
+        if x is not None:
+            assert torch.equal(x, y)
+    assert np.array_equal(da.view(np.uint64), db.view(np.uint64))
+
+
+@pytest.mark.parametrize("fmt,nbits,group,big,small", [
+    ("mxfp4", 4, 32, (34816, 5120), (256, 1024)),
+    ("gptq_sym", 4, 128, (4096, 4096), (256, 1024)),
+    ("gptq_asym", 4, 128, (4096, 4096), (72, 640)),
+    ("uintx", 3, 64, (3072, 12288), (64, 512)),
+    ("uintx", 6, 64, (34816, 5120), (10, 128)),          # the second takes the two-call fallback
+])
+def test_static_matches_workspace_call(fmt, nbits, group, big, small):
+    for shape, seed in ((big, 900), (small, 901)):
+        W = workloads.mxfp4_weight(*shape, seed=seed).to(DEV)
+        a = _call(gwb.lib.gwb_quantize_snr, W, fmt, nbits, group, True)
+        b = _call(gwb.lib.gwb_quantize_snr_static, W, fmt, nbits, group, False)
+        _same(a, b)
