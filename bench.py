@@ -330,31 +330,33 @@ def _avg_us(pairs) -> float:
 
 
 def stream_ceilings(gwb, dev):
-    """Same-run streaming ceilings (gwb_stream_bench, 1 GiB, best of a few grid sizes and
-    both work assignments):
-    copy, read only, quantize-shaped (4 bytes read per byte written) and
-    dequantize-shaped (1 byte read per 4 written), GB/s of both sides together."""
+    """Same-run streaming ceilings (gwb_stream_bench): copy, read only, quantize-shaped
+    (4 bytes read per byte written) and dequantize-shaped (1 byte read per 4 written), GB/s
+    of both sides together, best of a few grid sizes and both work assignments. The
+    launches cycle over four 1 GiB source and destination pairs, so each one streams from
+    and to HBM (a 256 MB side would otherwise stay in the Infinity Cache)."""
     nb = 1 << 30
-    src = torch.empty(nb, dtype=torch.uint8, device=dev)
-    dst = torch.empty(nb, dtype=torch.uint8, device=dev)
-    src.fill_(1)
+    pairs = [(torch.empty(nb, dtype=torch.uint8, device=dev), torch.empty(nb, dtype=torch.uint8, device=dev))
+             for _ in range(4)]
+    for src, _ in pairs:
+        src.fill_(1)
     moved = {"copy": 2.0 * nb, "read": 1.0 * nb, "read4_write1": 1.25 * nb, "read1_write4": 1.25 * nb}
     out = {}
     for pat, b in moved.items():
         best = 0.0
         for strided in (False, True):
             for blocks in (256, 512, 768, 1024, 2048):
-                for _ in range(2):
-                    gwb.stream_bench(pat, dst, src, blocks, strided)
+                for r in range(4):
+                    gwb.stream_bench(pat, pairs[r][1], pairs[r][0], blocks, strided)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
-                for _ in range(8):
-                    gwb.stream_bench(pat, dst, src, blocks, strided)
+                for r in range(8):
+                    gwb.stream_bench(pat, pairs[r % 4][1], pairs[r % 4][0], blocks, strided)
                 e1.record()
                 torch.cuda.synchronize()
                 best = max(best, b * 8 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
         out[pat] = round(best, 1)
-    del src, dst
+    del pairs
     return out
 
 

@@ -20,19 +20,24 @@ static int compute_units_of_current_device() {
   return n;
 }
 
-static int blocks_per_cu() {
+// GWB_BLOCKS_PER_CU (1..64), when set, replaces every streaming kernel's own choice of
+// resident blocks per compute unit (a measurement knob; unset in normal use).
+static int blocks_per_cu_override() {
   static const int v = [] {
     const char* s = std::getenv("GWB_BLOCKS_PER_CU");
     int x = s ? std::atoi(s) : 0;
-    return x > 0 && x <= 64 ? x : 8;
+    return x > 0 && x <= 64 ? x : 0;
   }();
   return v;
 }
 
-unsigned stream_blocks(uint64_t units) {
+unsigned stream_blocks(uint64_t units) { return stream_grid(units, 0); }
+
+unsigned stream_grid(uint64_t units, int per_cu) {
   uint64_t need = (units + 255) / 256;
   if (need == 0) need = 1;
-  const uint64_t cap = (uint64_t)compute_units_of_current_device() * (uint64_t)blocks_per_cu();
+  const int bpc = blocks_per_cu_override() > 0 ? blocks_per_cu_override() : (per_cu > 0 ? per_cu : 8);
+  const uint64_t cap = (uint64_t)compute_units_of_current_device() * (uint64_t)bpc;
   return (unsigned)(need < cap ? need : cap);
 }
 

@@ -166,6 +166,48 @@ __device__ __forceinline__ void acc_err8(const float* x, const float* d, double&
   }
 }
 
+// Sums of w^2 and (w - d)^2 over the 8 weights of a unit for the fused quantize+SNR
+// kernels: the squares and the seven additions of each sum in float32 (one rounding
+// each, fused multiply-adds), then one float64 addition per sum and unit, where acc_err8
+// squares and adds every weight in float64. The terms are non-negative, so each unit's
+// float32 sums are within 8 * 2^-24 of their exact values, relative; values below
+// float32's normal range add at most 2^-126 absolute per operation. No float32 value
+// overflows while |w| < 2^60 and |w - d| < 2^62: callers take acc_err8 for any group
+// whose largest magnitude reaches 2^60 (kSafeSqMax).
+constexpr float kSafeSqMax = 0x1p60f;
+__device__ __forceinline__ void acc_err8_f32(const float* x, const float* d, double& sw, double& se) {
+  float a = x[0] * x[0];
+  float e = x[0] - d[0];
+  float b = e * e;
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    a = __builtin_fmaf(x[i], x[i], a);
+    e = x[i] - d[i];
+    b = __builtin_fmaf(e, e, b);
+  }
+  sw += (double)a;
+  se += (double)b;
+}
+
+// The same for bf16 weights given as their raw words: each pair's squares in one
+// v_dot2_f32_bf16 (both products exact, one accumulation).
+__device__ __forceinline__ void acc_err8_f32_bf16(U4 v, const float* x, const float* d, double& sw, double& se) {
+  float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dc_bf16x2_t, v.x), __builtin_bit_cast(dc_bf16x2_t, v.x),
+                                            0.0f, false);
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dc_bf16x2_t, v.y), __builtin_bit_cast(dc_bf16x2_t, v.y), a, false);
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dc_bf16x2_t, v.z), __builtin_bit_cast(dc_bf16x2_t, v.z), a, false);
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dc_bf16x2_t, v.w), __builtin_bit_cast(dc_bf16x2_t, v.w), a, false);
+  float e = x[0] - d[0];
+  float b = e * e;
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    e = x[i] - d[i];
+    b = __builtin_fmaf(e, e, b);
+  }
+  sw += (double)a;
+  se += (double)b;
+}
+
 // ---------------------------------------------------------------- error sums
 // Block-wide sum of two doubles; thread 0 writes them to part[2*blockIdx.x]. A fixed
 // butterfly inside each wavefront, then thread 0 adds the wavefront sums in order, so

@@ -142,6 +142,7 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
   }
   if constexpr (!SYM) xreduce<L, false>(lo, lane);
   xreduce<L, true>(hi, lane);
+  int big = 0;
   if (L < 16 || (lane & 8) == 0) {                  // for 16 lanes, lanes 8-15 repeat 0-7
 #pragma unroll
     for (int j = 0; j < R; ++j) {
@@ -164,9 +165,22 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
         margin = -1.0f;
       }
       qp[wave * 8 + row][lane / L] = make_float4(y, zp, margin, s);
+      if constexpr (SNR) {
+        const float s16 = (float)(_Float16)s;
+        big |= !(a < kSafeSqMax) || !__builtin_isfinite(s16) || s16 == 0.0f;
+      }
     }
   }
-  __syncthreads();
+  // one flag per tile: a group too large for the float32 squares of the fused
+  // reconstruction sums, or whose fp16 scale overflowed or underflowed, sends the whole
+  // tile through the float64 squares and the plain (c - z) * s
+  bool tile_big = false;
+  if constexpr (SNR) {
+    tile_big = __syncthreads_or(big) != 0;
+  } else {
+    (void)big;
+    __syncthreads();
+  }
   const int gl = lane / L;
   double sw = 0.0, se = 0.0;
 #pragma unroll
@@ -198,21 +212,34 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
       if (n0 + wave * 8 + i < N && k0 + lane * 8 < K) {
         const float s16 = (float)(_Float16)p.w;
         float d[8];
+        if (!tile_big) {
+          // (c - z) * s is exact in float32 for a finite non-zero fp16 scale, so
+          // c*s - z*s as one fma rounds it exactly
+          const float nzs = -(p.y * s16);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) d[j] = (__builtin_amdgcn_fmed3f(c[j], 0.0f, 15.0f) - p.y) * s16;
-        acc_err8(x, d, sw, se);
+          for (int j = 0; j < 8; ++j) d[j] = __builtin_fmaf(__builtin_amdgcn_fmed3f(c[j], 0.0f, 15.0f), s16, nzs);
+          if constexpr (sizeof(TIn) == 2) acc_err8_f32_bf16(raw[i].v, x, d, sw, se);
+          else acc_err8_f32(x, d, sw, se);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) d[j] = (__builtin_amdgcn_fmed3f(c[j], 0.0f, 15.0f) - p.y) * s16;
+          acc_err8(x, d, sw, se);
+        }
       }
     }
   }
   if constexpr (SNR) block_sum2_store<256>(sw, se, part);   // synchronizes the block too
   __syncthreads();
-  {  // qweight [K/8, N]: 64 r-rows x 32 words, 8 words (32 bytes) per thread
-    const int r = t >> 2, c8 = (t & 3) * 8;
-    if (k0 / 8 + r < K / 8 && n0 + c8 < N) {
-      const uint32_t* src = &qtile[r * kQS + c8];
-      uint32_t* dst = qweight + (int64_t)(k0 / 8 + r) * N + n0 + c8;
-      st16(dst, U4{src[0], src[1], src[2], src[3]});
-      st16(dst + 4, U4{src[4], src[5], src[6], src[7]});
+  // qweight [K/8, N]: 64 r-rows x 32 words. Each store instruction of a wavefront writes
+  // eight whole 128-byte rows (16 bytes per lane): non-temporal stores reach memory as
+  // full lines (the packed tensors are read back much later, if at all, and ordinary
+  // stores would leave them as dirty lines for the next kernel to write back).
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = wave * 16 + h * 8 + (lane >> 3), c4 = (lane & 7) * 4;
+    if (k0 / 8 + r < K / 8 && n0 + c4 < N) {    // N % 8 == 0: a run that starts inside N ends inside it
+      const uint32_t* src = &qtile[r * kQS + c4];
+      st16_nt(qweight + (int64_t)(k0 / 8 + r) * N + n0 + c4, U4{src[0], src[1], src[2], src[3]});
     }
   }
   for (int e = t; e < T::NG * kTN; e += 256) {   // scales [K/G, N]
@@ -263,13 +290,14 @@ __global__ __launch_bounds__(256) void gptq_dequant_kernel(const uint32_t* __res
     // Staging loads first, then the error sink's weights: the LDS stores below wait only
     // for the staging data, and the weights stay in flight across the barrier. (Rows
     // past N or k past K read clamped in-bounds places; those values are not used.)
-    const int r = t >> 2, c8 = (t & 3) * 8;
-    const bool qok = k0 / 8 + r < K / 8 && n0 + c8 < N;
-    U4 qa{}, qb{};
-    if (qok) {
-      const uint32_t* src = qweight + (int64_t)(k0 / 8 + r) * N + n0 + c8;
-      qa = ld16(src);
-      qb = ld16(src + 4);
+    // each load instruction of a wavefront reads eight whole 128-byte qweight rows
+    U4 qv[2];
+    bool qok[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = wave * 16 + h * 8 + (lane >> 3), c4 = (lane & 7) * 4;
+      qok[h] = k0 / 8 + r < K / 8 && n0 + c4 < N;    // N % 8 == 0: whole 16-byte runs
+      qv[h] = qok[h] ? ld16(qweight + (int64_t)(k0 / 8 + r) * N + n0 + c4) : U4{};
     }
     constexpr int kSPer = (T::NG * kTN + 255) / 256;   // scales per thread
     uint16_t sv[kSPer];
@@ -290,10 +318,12 @@ __global__ __launch_bounds__(256) void gptq_dequant_kernel(const uint32_t* __res
 #pragma unroll
       for (int i = 0; i < 8; ++i) wr[i] = load_raw8(W + (int64_t)min(n0 + wave * 8 + i, N - 1) * ldw + kc);
     }
-    if (qok) {
-      uint32_t* dst = &qtile[r * kQS + c8];
-      dst[0] = qa.x; dst[1] = qa.y; dst[2] = qa.z; dst[3] = qa.w;
-      dst[4] = qb.x; dst[5] = qb.y; dst[6] = qb.z; dst[7] = qb.w;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (qok[h]) {
+        uint32_t* dst = &qtile[(wave * 16 + h * 8 + (lane >> 3)) * kQS + (lane & 7) * 4];
+        dst[0] = qv[h].x; dst[1] = qv[h].y; dst[2] = qv[h].z; dst[3] = qv[h].w;
+      }
     }
 #pragma unroll
     for (int q = 0; q < kSPer; ++q)

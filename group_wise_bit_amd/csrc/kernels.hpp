@@ -24,6 +24,8 @@ constexpr unsigned kErrGridCap = 1024;
 // one unit per thread at most, and at most GWB_BLOCKS_PER_CU (default 8) blocks per
 // compute unit of the current device. Launch time only (queries the device).
 unsigned stream_blocks(uint64_t units);
+// The same with per_cu blocks per compute unit (0: the default 8).
+unsigned stream_grid(uint64_t units, int per_cu);
 inline unsigned err_blocks_for(uint64_t units) {
   uint64_t g = (units + 255) / 256;
   return (unsigned)(g < kErrGridCap ? (g ? g : 1) : kErrGridCap);

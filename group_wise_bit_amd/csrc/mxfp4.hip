@@ -12,6 +12,15 @@
 
 namespace gwb {
 
+// Launch shape of the streaming MXFP4 kernels (measured at the metric shape with inputs
+// cold): units in flight per lane, resident blocks per compute unit of the quantize and
+// dequantize passes, and the fixed block count of the error passes (whose partial sums
+// the workspace holds, so it depends on the shape only).
+constexpr int kMxUnits = 8;
+constexpr int kMxQuantPerCU = 2;
+constexpr int kMxDequantPerCU = 1;
+constexpr unsigned kMxErrBlocks = 512;
+
 __device__ __forceinline__ uint32_t absmax_bits(const Raw8<uint16_t>& r) { return absmax8_bits(r.v); }
 __device__ __forceinline__ uint32_t absmax_bits(const Raw8<float>& r) {
   float x[8];
@@ -63,18 +72,24 @@ __device__ __forceinline__ void quant_unit(const Raw8<TIn>& r, uint32_t u, uint3
   const uint32_t e8 = mx_e8m0_bits(quad_max_u(absmax_bits(r)));
   uint32_t w = pack_unit(r, mx_scale_operand(e8));
   if constexpr (LIT) w -= page_tie_fix(r, e8);
-  packed[u] = w;
+  // non-temporal: the packed codes are read back much later, if at all, and ordinary
+  // stores would leave them as dirty lines for the next kernel to write back (the small
+  // E8M0 bytes stay ordinary stores, which L2 merges into lines)
+  __builtin_nontemporal_store(w, packed + u);
   if ((u & 3u) == 0) e8m0[u >> 2] = (uint8_t)e8;
   if constexpr (SNR) {
     float d[8], x[8];
     mx_unpack8(w, e8, d);
     to_f32(r, x);
-    acc_err8(x, d, sw, se);
+    // blocks whose maximum reaches 2^60 (E8M0 byte 185 or more) square in float64
+    if (e8 < 127u + 58u) acc_err8_f32(x, d, sw, se);
+    else acc_err8(x, d, sw, se);
   }
 }
 
 // units = N*K/8 is a multiple of 4 and every stride is too, so the four lanes of a
-// block always take the same branch of each loop (the DPP step needs all four).
+// block always take the same branch of each loop (the DPP step needs all four). Each
+// lane has kMxUnits units' loads in flight before converting them.
 template <bool CONTIG, bool LIT, typename TIn, bool SNR>
 __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const TIn* __restrict__ W, int64_t ldw,
                                                           uint32_t units, FastDiv upr,
@@ -83,15 +98,12 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(const TIn* __restrict_
   const uint32_t stride = gridDim.x * blockDim.x;
   double sw = 0.0, se = 0.0;
   uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
-  for (; u + 3 * stride < units; u += 4 * stride) {
-    const Raw8<TIn> r0 = load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr));
-    const Raw8<TIn> r1 = load_raw8(unit_ptr<CONTIG>(W, ldw, u + stride, upr));
-    const Raw8<TIn> r2 = load_raw8(unit_ptr<CONTIG>(W, ldw, u + 2 * stride, upr));
-    const Raw8<TIn> r3 = load_raw8(unit_ptr<CONTIG>(W, ldw, u + 3 * stride, upr));
-    quant_unit<LIT, SNR>(r0, u, packed, e8m0, sw, se);
-    quant_unit<LIT, SNR>(r1, u + stride, packed, e8m0, sw, se);
-    quant_unit<LIT, SNR>(r2, u + 2 * stride, packed, e8m0, sw, se);
-    quant_unit<LIT, SNR>(r3, u + 3 * stride, packed, e8m0, sw, se);
+  for (; u + (kMxUnits - 1) * stride < units; u += kMxUnits * stride) {
+    Raw8<TIn> r[kMxUnits];
+#pragma unroll
+    for (int i = 0; i < kMxUnits; ++i) r[i] = load_raw8(unit_ptr<CONTIG>(W, ldw, u + i * stride, upr));
+#pragma unroll
+    for (int i = 0; i < kMxUnits; ++i) quant_unit<LIT, SNR>(r[i], u + i * stride, packed, e8m0, sw, se);
   }
   for (; u < units; u += stride)
     quant_unit<LIT, SNR>(load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr)), u, packed, e8m0, sw, se);
@@ -131,17 +143,18 @@ __global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint32_t* __re
   const uint32_t stride = gridDim.x * blockDim.x;
   double sw = 0.0, se = 0.0;
   uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
-  Raw8<TW> x[4] = {};
-  for (; u + 3 * stride < units; u += 4 * stride) {
-    uint32_t w[4], e[4];
+  Raw8<TW> x[kMxUnits] = {};
+  for (; u + (kMxUnits - 1) * stride < units; u += kMxUnits * stride) {
+    uint32_t w[kMxUnits], e[kMxUnits];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kMxUnits; ++i) {
       w[i] = packed[u + i * stride];
       e[i] = e8m0[(u + i * stride) >> 2];
       if constexpr (SINK == kErr) x[i] = load_raw8(unit_ptr<CONTIG>(W, ldw, u + i * stride, upr));
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dequant_unit<SINK, CONTIG>(w[i], e[i], u + i * stride, upr, out, ldo, x[i], sw, se);
+    for (int i = 0; i < kMxUnits; ++i)
+      dequant_unit<SINK, CONTIG>(w[i], e[i], u + i * stride, upr, out, ldo, x[i], sw, se);
   }
   for (; u < units; u += stride) {
     if constexpr (SINK == kErr) x[0] = load_raw8(unit_ptr<CONTIG>(W, ldw, u, upr));
@@ -157,7 +170,7 @@ static void quant_lit(const void* W, int32_t w_dtype, int64_t N, int64_t K, int6
   const uint32_t units = (uint32_t)(N * K / 8);
   const FastDiv upr = make_fastdiv((uint32_t)(K / 8));
   // with the sums: the error kernel's grid, whose partials the workspace holds
-  const unsigned grid = SNR ? mxfp4_err_blocks(N, K) : stream_blocks(units);
+  const unsigned grid = SNR ? mxfp4_err_blocks(N, K) : stream_grid(units, kMxQuantPerCU);
   const bool contig = ldw == K;
   if (w_dtype == kBF16)
     hipLaunchKernelGGL((contig ? mxfp4_quant_kernel<true, LIT, uint16_t, SNR>
@@ -185,7 +198,7 @@ void launch_mxfp4_dequant(const void* packed, const void* e8m0, int64_t N, int64
                           int32_t out_dtype, int64_t ldo, hipStream_t st) {
   const uint32_t units = (uint32_t)(N * K / 8);
   const FastDiv upr = make_fastdiv((uint32_t)(K / 8));
-  const unsigned grid = stream_blocks(units);
+  const unsigned grid = stream_grid(units, kMxDequantPerCU);
   const bool contig = ldo == K;
   if (out_dtype == kBF16)
     hipLaunchKernelGGL((contig ? mxfp4_dequant_kernel<kStore, true, uint16_t, uint16_t> : mxfp4_dequant_kernel<kStore, false, uint16_t, uint16_t>),
@@ -197,7 +210,10 @@ void launch_mxfp4_dequant(const void* packed, const void* e8m0, int64_t N, int64
                        (float*)out, ldo, (const uint16_t*)nullptr, (int64_t)0, (double*)nullptr);
 }
 
-unsigned mxfp4_err_blocks(int64_t N, int64_t K) { return err_blocks_for((uint64_t)(N * K / 8)); }
+unsigned mxfp4_err_blocks(int64_t N, int64_t K) {
+  const uint64_t g = ((uint64_t)(N * K / 8) + 255) / 256;
+  return (unsigned)(g < kMxErrBlocks ? (g ? g : 1) : kMxErrBlocks);
+}
 
 void launch_mxfp4_err(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
                       const void* packed, const void* e8m0, double* part, hipStream_t st) {

@@ -37,8 +37,11 @@ __device__ __forceinline__ T* elem_ptr(T* base, int64_t ld, uint32_t e, FastDiv 
   return base + (int64_t)n * ld + (e - n * kdiv.d);
 }
 
+// Shard bytes are stored non-temporally: the packed tensors are read back much later, if
+// at all, and ordinary stores would leave them as dirty lines for the next kernel.
+typedef uint32_t ux_u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void st8(uint8_t* p, uint32_t lo, uint32_t hi) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+  __builtin_nontemporal_store(ux_u32x2_t{lo, hi}, reinterpret_cast<ux_u32x2_t*>(p));
 }
 __device__ __forceinline__ uint2 ld8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
 
@@ -86,16 +89,22 @@ __device__ __forceinline__ void round_bf16_pair(float& a, float& b) {
   b = __uint_as_float(r & 0xFFFF0000u);
 }
 
-// Codes of 8 weights as bytes: lo = positions 0..3, hi = 4..7.
+// Codes of 8 weights as bytes: lo = positions 0..3, hi = 4..7; also the weights x and
+// q - zp as floats (what the fused reconstruction sums start from). clamp(rint(t) + zp,
+// 0, qmax) is formed as clamp(rint(t), -zp, qmax - zp) + zp: the same integer, with
+// q - zp on the way.
 template <int DT>
 __device__ __forceinline__ void ux_codes8(const Raw8<typename UxDt<DT>::T>& r, float inv, float zp, float qmax,
-                                          uint32_t& lo, uint32_t& hi) {
-  float x[8];
+                                          uint32_t& lo, uint32_t& hi, float* x, float* qz) {
   ux_widen8<DT>(r, x);
   uint32_t w[2] = {0u, 0u};
   if (ux_inv_is_inf<DT>(inv)) {              // float16 only; see ux_inv_is_inf
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i >> 2] |= (x[i] > 0.0f ? (uint32_t)qmax : 0u) << (8 * (i & 3));
+    for (int i = 0; i < 8; ++i) {
+      const float c = x[i] > 0.0f ? qmax : 0.0f;
+      qz[i] = c - zp;
+      w[i >> 2] |= (uint32_t)c << (8 * (i & 3));
+    }
   } else {
     float t[8];
 #pragma unroll
@@ -107,10 +116,11 @@ __device__ __forceinline__ void ux_codes8(const Raw8<typename UxDt<DT>::T>& r, f
 #pragma unroll
       for (int i = 0; i < 8; ++i) t[i] = UxDt<DT>::rnd(t[i]);
     }
+    const float lo_q = -zp, hi_q = qmax - zp;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float c = __builtin_amdgcn_fmed3f(rintf(t[i]) + zp, 0.0f, qmax);
-      w[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(c, i & 3, w[i >> 2]);
+      qz[i] = __builtin_amdgcn_fmed3f(rintf(t[i]), lo_q, hi_q);
+      w[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(qz[i] + zp, i & 3, w[i >> 2]);
     }
   }
   lo = w[0];
@@ -144,6 +154,7 @@ __global__ __launch_bounds__(256) void uintx_quant_tiled(const typename UxDt<DT>
   const bool active = p < L1;                // whole sets: L1 % G == 0
   typename D::Lds* const set_qp = &qp_lds[(threadIdx.x / LG) * 8];
   Raw8<typename D::T> raw[8];
+  bool safe[8];                              // group small enough for float32 squares
   if (active) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) raw[j] = ux_load_raw8(elem_ptr<CONTIG>(W, ldw, j * L1 + p, kdiv));
@@ -154,6 +165,8 @@ __global__ __launch_bounds__(256) void uintx_quant_tiled(const typename UxDt<DT>
       ux_extremes8<DT>(raw[j], a, b);
       mn[j] = lanes_min<LG>(a);
       mx[j] = lanes_max<LG>(b);
+      // a 2-byte key orders like, and is below 2^60 exactly when, the weight it holds
+      safe[j] = DT == kF16 || fmaxf(fabsf(mn[j]), fabsf(mx[j])) < kSafeSqMax;
     }
     const int i = lane % LG;
     const uint32_t p0 = p - i * kLanePos;    // the set's first position
@@ -183,7 +196,26 @@ __global__ __launch_bounds__(256) void uintx_quant_tiled(const typename UxDt<DT>
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const typename D::Lds w = set_qp[j];
-    ux_codes8<DT>(raw[j], D::lds_value(w), D::lds_zp(w), qmax, clo[j], chi[j]);
+    float x[8], qz[8];
+    ux_codes8<DT>(raw[j], D::lds_value(w), D::lds_zp(w), qmax, clo[j], chi[j], x, qz);
+    if constexpr (SNR) {
+      // the reconstruction sums of the stored values: r(r(q - zp) * s) as the dequantize
+      // kernel forms it (q - zp exact), from the codes just formed
+      const float sc = D::lds_value(qs_lds[(threadIdx.x / LG) * 8 + j]);
+      float d[8];
+#pragma unroll
+      for (int b = 0; b < 8; ++b) d[b] = qz[b] * sc;
+      if constexpr (DT == kBF16) {
+#pragma unroll
+        for (int b = 0; b < 8; b += 2) round_bf16_pair(d[b], d[b + 1]);
+      } else if constexpr (DT == kF16) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) d[b] = D::rnd(d[b]);
+      }
+      if (!safe[j]) acc_err8(x, d, sw, se);
+      else if constexpr (DT == kBF16) acc_err8_f32_bf16(raw[j].v, x, d, sw, se);
+      else acc_err8_f32(x, d, sw, se);
+    }
   }
   if constexpr (SB::has4) {
 #pragma unroll
@@ -212,36 +244,17 @@ __global__ __launch_bounds__(256) void uintx_quant_tiled(const typename UxDt<DT>
     }
     st8(packed + sh.base1 + p, lo, hi);
   }
-  if constexpr (SNR) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const typename D::Lds w = qs_lds[(threadIdx.x / LG) * 8 + j];
-      const float s = D::lds_value(w), zp = D::lds_zp(w);
-      const uint32_t c[2] = {clo[j], chi[j]};
-      float d[8];
-#pragma unroll
-      for (int b = 0; b < 8; ++b) d[b] = ((float)((c[b >> 2] >> (8 * (b & 3))) & 0xFFu) - zp) * s;
-      if constexpr (DT == kBF16) {
-#pragma unroll
-        for (int b = 0; b < 8; b += 2) round_bf16_pair(d[b], d[b + 1]);
-      } else if constexpr (DT == kF16) {
-#pragma unroll
-        for (int b = 0; b < 8; ++b) d[b] = D::rnd(d[b]);
-      }
-      float x[8];
-      ux_widen8<DT>(raw[j], x);
-      acc_err8(x, d, sw, se);
-    }
-  }
   }
   if constexpr (SNR) block_sum2_store<256>(sw, se, part);
 }
 
 // ------------------------------------------------------------- tiled dequantize
 // SINK kStore writes out (OUT = the weight dtype or kF32), SINK kErr accumulates the
-// reconstruction error against W. The set's scales and zero points go first: the LDS
-// exchange waits only for them, while the shard bytes and the weights stay in flight
-// across the barrier.
+// reconstruction error against W. Each lane loads the scale and zero point of its own
+// group in each segment (the eight lanes of a set read the same ones; a wavefront's load
+// covers eight consecutive groups), so no lane waits at a barrier for another's loads:
+// the shard bytes, the group parameters and the error sink's weights all go out first,
+// then each segment's values are formed and stored.
 template <int NB, int DT, int G, int SINK, int OUT, bool CONTIG>
 __global__ __launch_bounds__(256) void uintx_dequant_tiled(const uint8_t* __restrict__ packed,
                                                            const typename UxDt<DT>::T* __restrict__ scales,
@@ -251,26 +264,14 @@ __global__ __launch_bounds__(256) void uintx_dequant_tiled(const uint8_t* __rest
                                                            int64_t ldw, double* __restrict__ part) {
   using SB = ShardBits<NB>;
   using D = UxDt<DT>;
-  constexpr int LG = G / 8;
-  constexpr int PER = LG >= 8 ? 1 : 8 / LG;
-  __shared__ typename D::Lds qp_lds[256 / LG * 8];
   const int lane = threadIdx.x & 63;
   const uint32_t p = blockIdx.x * kBlockPos + (threadIdx.x >> 6) * kWavePos + lane * kLanePos;
-  const bool active = p < L1;
-  typename D::Lds* const set_qp = &qp_lds[(threadIdx.x / LG) * 8];
-  uint2 s4[4], s2[2], s1;
-  Raw8<typename D::T> wr[8];                 // the error sink's weights
-  if (active) {
-    const int i = lane % LG;
-    const uint32_t p0 = p - i * kLanePos;
-    typename D::T sc[PER];
-    uint32_t zz[PER];
-#pragma unroll
-    for (int m = 0; m < PER; ++m) {
-      const uint32_t g = (((i + m * LG) & 7) * L1 + p0) / G;
-      sc[m] = scales[g];
-      zz[m] = zeros[g];
-    }
+  double sw = 0.0, se = 0.0;
+  if (p < L1) {
+    uint2 s4[4], s2[2], s1;
+    typename D::T sc[8];
+    uint32_t zz[8];
+    Raw8<typename D::T> wr[8];               // the error sink's weights
     if constexpr (SB::has4) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) s4[m] = ld8(packed + sh.base4 + (int64_t)m * L1 + p);
@@ -280,20 +281,19 @@ __global__ __launch_bounds__(256) void uintx_dequant_tiled(const uint8_t* __rest
       for (int m = 0; m < 2; ++m) s2[m] = ld8(packed + sh.base2 + (int64_t)m * L1 + p);
     }
     if constexpr (SB::has1) s1 = ld8(packed + sh.base1 + p);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t g = (j * L1 + p) / G;   // L1 % G == 0: a lane's 8 positions share a group
+      sc[j] = scales[g];
+      zz[j] = zeros[g];
+    }
     if constexpr (SINK == kErr) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) wr[j] = ux_load_raw8(elem_ptr<CONTIG>(W, ldw, j * L1 + p, kdiv));
     }
 #pragma unroll
-    for (int m = 0; m < PER; ++m)
-      if (LG <= 8 || i < 8) set_qp[(i + m * LG) & 7] = D::pack(sc[m], zz[m]);
-  }
-  __syncthreads();
-  double sw = 0.0, se = 0.0;
-  if (active) {
-#pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const typename D::Lds w = set_qp[j];
+      const typename D::Lds w = D::pack(sc[j], zz[j]);
       const float s = D::lds_value(w), zp = D::lds_zp(w);
       uint32_t c[2] = {0u, 0u};
 #pragma unroll
@@ -321,10 +321,10 @@ __global__ __launch_bounds__(256) void uintx_dequant_tiled(const uint8_t* __rest
         for (int b = 0; b < 8; b += 2) round_bf16_pair(d[b], d[b + 1]);
       } else if constexpr (DT == kF16) {
         if constexpr (SINK == kStore && OUT == kF16) {
-          uint32_t h[4];
+          uint32_t hh[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) h[q] = (uint32_t)D::word(d[2 * q]) | ((uint32_t)D::word(d[2 * q + 1]) << 16);
-          st16_nt(elem_ptr<CONTIG>((uint16_t*)out, ldo, e, kdiv), U4{h[0], h[1], h[2], h[3]});
+          for (int q = 0; q < 4; ++q) hh[q] = (uint32_t)D::word(d[2 * q]) | ((uint32_t)D::word(d[2 * q + 1]) << 16);
+          st16_nt(elem_ptr<CONTIG>((uint16_t*)out, ldo, e, kdiv), U4{hh[0], hh[1], hh[2], hh[3]});
           continue;
         }
 #pragma unroll

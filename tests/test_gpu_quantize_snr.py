@@ -1,8 +1,10 @@
 """GPU checks of gwb_quantize_snr, quantization and SNR in one pass over W: the stored
-tensors equal gwb_quantize's bit for bit, and the three SNR values equal gwb_snr's (the
-fused sums differ only in float64 summation order) and the float64 sums over the
-dequantized matrix on the host (page export_gptq_cpu.py's 20 log10(||w|| / ||w - deq||)
-of the stored values, as gwb_snr defines it)."""
+tensors equal gwb_quantize's bit for bit, and the sums equal gwb_snr's and the float64
+sums over the dequantized matrix on the host (page export_gptq_cpu.py's
+20 log10(||w|| / ||w - deq||) of the stored values, as gwb_snr defines it) within the
+fused pass's bound: it adds each unit of 8 weights' squares in float32 before the
+float64 accumulation (gwb_snr squares every weight in float64), which is within
+16 * 2^-24 of the exact sums, relative (non-negative terms), i.e. within 1e-5 dB."""
 from __future__ import annotations
 
 import numpy as np
@@ -19,6 +21,7 @@ else:  # collected on CPU only to be skipped
     gwb = None
 
 DEV = "cuda"
+FUSED_REL = 16 * 2.0 ** -24 + 1e-12     # the fused pass's float32 unit sums, relative
 _TDT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
@@ -38,30 +41,44 @@ def _check(W, fmt, nbits=4, group=None):
     assert torch.equal(q1.codes, q2.codes) and torch.equal(q1.scales, q2.scales)
     if q1.zeros is not None:
         assert torch.equal(q1.zeros, q2.zeros)
-    assert s2[0] == pytest.approx(s1[0], rel=1e-12) and s2[1] == pytest.approx(s1[1], rel=1e-12, abs=1e-300)
-    assert s2[2] == pytest.approx(s1[2], rel=1e-10, abs=1e-9)
+    if not np.all(np.isfinite(s1[:2])):            # fp16 GPTQ scales past their range: inf / NaN sums
+        assert np.array_equal(np.isnan(s1), np.isnan(s2)) and np.array_equal(np.isinf(s1), np.isinf(s2))
+        return s1, s2
+    assert s2[0] == pytest.approx(s1[0], rel=FUSED_REL) and s2[1] == pytest.approx(s1[1], rel=FUSED_REL, abs=1e-30)
+    assert abs(s2[2] - s1[2]) < 1e-5 or (np.isinf(s1[2]) and s1[2] == s2[2])
     w2, e2 = _host_sums(W, q2)
-    assert s2[0] == pytest.approx(w2, rel=1e-9) and s2[1] == pytest.approx(e2, rel=1e-9, abs=1e-300)
+    assert s2[0] == pytest.approx(w2, rel=FUSED_REL) and s2[1] == pytest.approx(e2, rel=FUSED_REL, abs=1e-30)
     return s1, s2
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp4_page_ties"])
 @pytest.mark.parametrize("n,k,ld", [(64, 512, 512), (37, 96, 96), (130, 2048, 2080)])
-def test_quantize_snr_mxfp4(fmt, n, k, ld):
-    """MXFP4 runs the error kernel's grid and per-thread order: the sums are bit-identical
-    to gwb_snr's (row strides too)."""
-    Wf = workloads.mxfp4_weight(n, ld, seed=800 + n)
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_quantize_snr_mxfp4(fmt, n, k, ld, dt):
+    """MXFP4 on bf16 and float32 weights (row strides too)."""
+    Wf = workloads.mxfp4_weight(n, ld, seed=800 + n, dtype=_TDT[dt])
     W = Wf[:, :k]
-    s1, s2 = _check(W, fmt)
-    assert np.array_equal(s1[:2], s2[:2])
+    _check(W, fmt)
 
 
 @pytest.mark.parametrize("fmt", ["gptq_sym", "gptq_asym"])
 @pytest.mark.parametrize("group", [32, 64, 128])
 @pytest.mark.parametrize("n,k", [(64, 512), (72, 640), (264, 1536)])
-def test_quantize_snr_gptq(fmt, group, n, k):
-    W = workloads.mxfp4_weight(n, k, seed=810 + n + group)
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_quantize_snr_gptq(fmt, group, n, k, dt):
+    W = workloads.mxfp4_weight(n, k, seed=810 + n + group, dtype=_TDT[dt])
     _check(W, fmt, group=group)
+
+
+@pytest.mark.parametrize("fmt,nbits,group", [("mxfp4", 4, None), ("gptq_sym", 4, 128), ("gptq_asym", 4, 64),
+                                             ("uintx", 3, 64), ("uintx", 6, 32)])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_quantize_snr_adversarial(fmt, nbits, group, dt):
+    """Spans of 2^100-scale values (groups the fused pass squares in float64, past the
+    float32 range), 2^-126-scale and subnormal values, exact ties, zeros and constants,
+    mixed in one matrix: the fused sums still within the bound of gwb_snr's."""
+    W = workloads.adversarial_weight(64, 2048, seed=830 + (nbits or 0), dtype=_TDT[dt])
+    _check(W, fmt, nbits=nbits, group=group)
 
 
 @pytest.mark.parametrize("nbits", [2, 3, 4, 5, 6, 7])
@@ -85,5 +102,5 @@ def test_quantize_snr_full_34816x5120():
         q2, s2 = gwb.quantize_snr(Wd, fmt, nbits=nb, group=g)
         s2 = s2.cpu().numpy()
         assert torch.equal(q1.codes, q2.codes) and torch.equal(q1.scales, q2.scales), fmt
-        assert s2[0] == pytest.approx(s1[0], rel=1e-12) and s2[1] == pytest.approx(s1[1], rel=1e-12), fmt
+        assert s2[0] == pytest.approx(s1[0], rel=FUSED_REL) and s2[1] == pytest.approx(s1[1], rel=FUSED_REL), fmt
         del q1, q2
