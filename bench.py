@@ -43,6 +43,8 @@ sys.path.insert(0, ROOT)
 N, K = 34816, 5120
 PEAK_HBM_GBPS = 8000.0
 PEAK_MFMA_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak
+PEAK_SIMDS, PEAK_CLOCK_HZ = 1024, 2.4e9       # 256 CUs x 4 SIMDs; peak engine clock
+PEAK_VALU_TOPS = PEAK_SIMDS * 16 * PEAK_CLOCK_HZ / 1e12   # 16 lanes per SIMD per cycle: 39.32 T lane-instructions/s
 # kernels launched by one library call of each step op (quantize, dequantize: one; SNR: the
 # error pass and its finalize; quantize with the SNR fused: the quantize pass and the same
 # finalize; AWQ: table pow, table scale, search, finalize)
@@ -508,22 +510,29 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(W_cpu, a_cpu, args.cpu_rows, args.cpu_awq_rows)
 
-    roof = {
-        "bound": "hbm", "kernel": dname,
-        "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-        "frac": round(achieved / PEAK_HBM_GBPS, 4),
+    hbm = {"achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+           "frac": round(achieved / PEAK_HBM_GBPS, 4)}
+    roof = {"bound": "hbm", "kernel": dname, **hbm}
+    valu = counters.get("valu_insts_per_launch")
+    if valu is not None:
+        # VALU issue load: wavefront VALU instructions (rocprofv3 SQ_INSTS_VALU of this
+        # kernel, per launch, profiles/counters.json) x 4 cycles (a wave64 instruction on a
+        # 16-lane SIMD) over 1024 SIMDs x 2.4 GHz x the launch's live duration
+        lane_ops = valu * 64 / (dom_us * 1e-6) / 1e12                 # T lane-instructions / s
+        roof["valu_load"] = round(valu * 4 / (PEAK_SIMDS * PEAK_CLOCK_HZ * dom_us * 1e-6), 4)
+        if roof["valu_load"] >= 0.9:
+            # issue-bound on the vector ALU: that is the roofline the kernel runs against
+            roof = {"bound": "alu", "kernel": dname, "achieved": round(lane_ops, 2), "peak": PEAK_VALU_TOPS,
+                    "unit": "T lane-instructions/s", "frac": round(lane_ops / PEAK_VALU_TOPS, 4),
+                    "valu_load": roof["valu_load"], "hbm": hbm}
+    roof.update({
         "traffic": counters.get("bytes_per_launch"),
         "algorithmic_bytes_per_launch": int(dbytes), "avg_launch_us": round(dom_us, 2),
         # kernels one library call of this op launches (all inside its event pair): a
         # fused quantize+SNR is the quantize kernel plus the in-order float64 finalize
         "kernels_in_event_pair": OP_KERNELS[dname.split(".")[1] if "." in dname else dname],
         "frac_stream_ceiling": round(achieved / shape_ceiling(dname), 4),
-    }
-    if counters.get("valu_insts_per_launch") is not None and counters.get("kernel_us"):
-        # VALU issue load of the dominant kernel: wavefront VALU instructions x 4 cycles
-        # (a wave64 instruction on a 16-lane SIMD) over 1024 SIMDs x 2.4 GHz x its duration
-        roof["valu_frac"] = round(counters["valu_insts_per_launch"] * 4 /
-                                  (1024 * 2.4e9 * counters["kernel_us"] * 1e-6), 4)
+    })
     line = {
         "metric": "weight GB/s quantize+pack and unpack+dequant; % of HBM peak (34816x5120)",
         "value": round(value, 2),

@@ -109,7 +109,11 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
   __shared__ uint32_t qtile[kTR * kQS];
   __shared__ float4 qp[kTN][T::NG];                 // per tile row and group: {1/s, zp, margin, s}
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
-  const int nt = blockIdx.x / ntk, kt = blockIdx.x - nt * ntk;
+  // consecutive blocks take consecutive column tiles of one k range, so the qweight rows
+  // they write (128 bytes each) lie side by side in memory
+  const int ntn = (N + kTN - 1) / kTN;
+  const int kt = blockIdx.x / ntn, nt = blockIdx.x - kt * ntn;
+  (void)ntk;
   const int n0 = nt * kTN, k0 = kt * kTK;
   // Lanes past K read a valid place instead: K % G == 0, so their groups lie wholly past
   // K and every reduction below stays within one group. Rows past N repeat row N - 1.
