@@ -10,7 +10,7 @@
 //
 // GPTQ ([K/8, N] words, n contiguous): a lane owns 4 adjacent outputs (one 16-byte load
 // per qweight row r), a wavefront 256 outputs x 128 k per step (16 loads in flight); a
-// block's four wavefronts take the steps of its K range in turn and are combined through
+// block's four wavefronts take contiguous bands of its K range and are combined through
 // LDS. With (c - z) * s per group, sum_k (c - z) s x = s (sum_k c x - z sum_k x): codes
 // become floats with v_cvt_f32_ubyte, the group sum of x is a wavefront reduction. When
 // N alone gives enough blocks, one block covers all of K and writes y; otherwise K is
@@ -73,13 +73,15 @@ __device__ __forceinline__ float gv_transposed_sum(float (&v)[VP], int lane) {
 }
 
 // ------------------------------------------------------------------ GPTQ
-constexpr int kGqWaveK = 128, kGqBlockK = 4 * kGqWaveK;
+constexpr int kGqWaveK = 128;
 
-// LN adjacent qweight words (columns) of one row, one load.
+// LN adjacent qweight words (columns) of one row, one load. The 4-word load is
+// non-temporal: each packed word is read once per call and should not displace the
+// activations and scales from the caches.
 template <int LN>
 __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[LN]) {
   if constexpr (LN == 4) {
-    const U4 v = ld16(p);
+    const U4 v = ld16_nt(p);
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   } else if constexpr (LN == 2) {
     const uint2 v = *reinterpret_cast<const uint2*>(p);
@@ -89,12 +91,149 @@ __device__ __forceinline__ void load_words(const uint32_t* p, uint32_t (&w)[LN])
   }
 }
 
-// LN: outputs (qweight columns) per lane; a wavefront covers 64 LN of them. B is the
-// compiled width (1, 2, 4, 8); Bn <= B activation rows are real: the others re-read row
-// Bn - 1 and are not stored. kspan: the K range of one split (a multiple of kGqBlockK);
-// with one split the block writes y (TY), otherwise its partial sums.
+// One qweight row (8 k) of a lane's LN columns: cx += c x for the group's rows; its
+// first row clears cx, its last adds s (sum c x - z sum x) to acc. A 4-bit code c, read
+// as an OCP e4m3 byte, is c * 2^-9 exactly (subnormals and the first binade share one
+// spacing), so the scaled FP8 conversion at scale 2^9 turns two code bytes into an
+// exact bf16 pair; v_dot2_f32_bf16 multiplies it with the matching activation pair
+// (products exact, one float32 accumulation each).
+template <bool SYM, int B, int LN, int RG>
+__device__ __forceinline__ void gq_row(int r, const uint32_t (&w)[LN], const U4 (&xv)[B], const float (&s)[LN],
+                                       const float (&z)[LN], const float (&xs)[B], float (&cx)[B][LN],
+                                       float (&acc)[B][LN]) {
+  if (r % RG == 0) {
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int j = 0; j < LN; ++j) cx[b][j] = 0.0f;
+  }
+  if constexpr (B > 2) {
+    // wider batches: each code widened on its own (v_cvt_f32_ubyte0..3) and one fma per
+    // product, so that the activations stay in the order they were loaded (rearranging
+    // them costs more scalar registers than a wavefront has)
+    float xk[B][8];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const U4 v = xv[b];
+      xk[b][0] = bf16_lo(v.x); xk[b][1] = bf16_hi(v.x); xk[b][2] = bf16_lo(v.y); xk[b][3] = bf16_hi(v.y);
+      xk[b][4] = bf16_lo(v.z); xk[b][5] = bf16_hi(v.z); xk[b][6] = bf16_lo(v.w); xk[b][7] = bf16_hi(v.w);
+    }
+#pragma unroll
+    for (int j = 0; j < LN; ++j) {
+      uint32_t ev = w[j] & 0x0F0F0F0Fu, od = (w[j] >> 4) & 0x0F0F0F0Fu;
+      // opaque to the combiner, so each code converts straight from its byte
+      asm volatile("" : "+v"(ev), "+v"(od));
+      const float c[8] = {(float)(ev & 0xFFu), (float)(od & 0xFFu), (float)((ev >> 8) & 0xFFu),
+                          (float)((od >> 8) & 0xFFu), (float)((ev >> 16) & 0xFFu), (float)((od >> 16) & 0xFFu),
+                          (float)(ev >> 24), (float)(od >> 24)};
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) cx[b][j] = __builtin_fmaf(c[q], xk[b][q], cx[b][j]);
+    }
+  } else {
+    // activation pairs in the order the code pairs come out: (k0, k2), (k4, k6), (k1, k3), (k5, k7)
+    gv_bf16x2_t xq[B][4];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const U4 v = xv[b];
+      xq[b][0] = __builtin_bit_cast(gv_bf16x2_t, (v.x & 0xFFFFu) | (v.y << 16));
+      xq[b][1] = __builtin_bit_cast(gv_bf16x2_t, (v.z & 0xFFFFu) | (v.w << 16));
+      xq[b][2] = __builtin_bit_cast(gv_bf16x2_t, (v.x >> 16) | (v.y & 0xFFFF0000u));
+      xq[b][3] = __builtin_bit_cast(gv_bf16x2_t, (v.z >> 16) | (v.w & 0xFFFF0000u));
+    }
+    const float two9 = 512.0f;
+#pragma unroll
+    for (int j = 0; j < LN; ++j) {
+      const uint32_t ev = w[j] & 0x0F0F0F0Fu, od = (w[j] >> 4) & 0x0F0F0F0Fu;   // codes k0 k2 k4 k6 / k1 k3 k5 k7
+      const gv_bf16x2_t c[4] = {__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, two9, false),
+                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ev, two9, true),
+                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, two9, false),
+                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(od, two9, true)};
+#pragma unroll
+      for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cx[b][j] = __builtin_amdgcn_fdot2_f32_bf16(c[q], xq[b][q], cx[b][j], false);
+    }
+  }
+  if (r % RG == RG - 1) {
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int j = 0; j < LN; ++j) acc[b][j] = __builtin_fmaf(s[j], __builtin_fmaf(-z[j], xs[b], cx[b][j]), acc[b][j]);
+  }
+}
+
+// One 128-k step of a wavefront: nr qweight rows (FULL: all 16, known at compile time, so
+// no row needs a branch and every load can be issued ahead of the arithmetic).
+template <bool SYM, int G, int B, int LN, bool FULL>
+__device__ __forceinline__ void gq_step(const uint32_t* __restrict__ qweight, const uint16_t* __restrict__ scale_bits,
+                                        const uint32_t* __restrict__ qzeros, int N, int K,
+                                        const uint16_t* __restrict__ x, int64_t ldx, int Bn, int nc, int lane, int kw,
+                                        int nr_, float (&acc)[B][LN]) {
+  constexpr int NGS = kGqWaveK / G, RG = G / 8;       // groups per step, qweight rows per group
+  constexpr int XR = B == 1 ? 16 : 1;                   // rows of activations fetched together
+  const int nr = FULL ? kGqWaveK / 8 : nr_;
+  // every load of the step is issued before the first use, the small ones first: the
+  // step's scales (and zero points), two activations per lane of each group, then the
+  // qweight rows
+  uint32_t sb[NGS][LN], zw[NGS], xp[NGS][B];
+#pragma unroll
+  for (int gi = 0; gi < NGS; ++gi) {
+    const int g = min(kw + gi * G, K - G) / G;        // groups past K are not used
+#pragma unroll
+    for (int j = 0; j < LN; ++j) sb[gi][j] = scale_bits[(int64_t)g * N + nc + j];
+    zw[gi] = 0u;
+    if constexpr (!SYM) zw[gi] = qzeros[(int64_t)g * (N / 8) + nc / 8] >> (4 * (nc % 8));
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+      xp[gi][b] = 2 * lane < G ? *reinterpret_cast<const uint32_t*>(x + (int64_t)min(b, Bn - 1) * ldx + g * G + 2 * lane)
+                               : 0u;
+  }
+  uint32_t wv[kGqWaveK / 8][LN];                      // rows past nr re-read row nr - 1, unused
+#pragma unroll
+  for (int r = 0; r < kGqWaveK / 8; ++r) load_words<LN>(qweight + (int64_t)(kw / 8 + min(r, nr - 1)) * N + nc, wv[r]);
+  __builtin_amdgcn_sched_barrier(0);                 // keep the loads ahead of the arithmetic
+  float s[NGS][LN], z[NGS][LN], xs[NGS][B];
+#pragma unroll
+  for (int gi = 0; gi < NGS; ++gi) {
+#pragma unroll
+    for (int j = 0; j < LN; ++j) {
+      s[gi][j] = (float)__builtin_bit_cast(_Float16, (uint16_t)sb[gi][j]);
+      z[gi][j] = SYM ? 8.0f : (float)((zw[gi] >> (4 * j)) & 0xFu);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) xs[gi][b] = wave_sum(bf16_lo(xp[gi][b]) + bf16_hi(xp[gi][b]));
+  }
+  // rows past nr (a multiple of RG) are skipped by wave-uniform branches, not loop exits:
+  // the loops unroll fully and wv stays in registers
+  float cx[B][LN];
+#pragma unroll
+  for (int rc = 0; rc < kGqWaveK / 8; rc += XR) {
+    if (rc < nr) {
+      U4 xv[XR][B];                                   // the same for every lane
+#pragma unroll
+      for (int i = 0; i < XR; ++i)
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+          xv[i][b] = *reinterpret_cast<const U4*>(x + (int64_t)min(b, Bn - 1) * ldx + kw + 8 * min(rc + i, nr - 1));
+#pragma unroll
+      for (int i = 0; i < XR; ++i) {
+        const int r = rc + i, gi = r / RG;
+        if (r < nr) gq_row<SYM, B, LN, RG>(r, wv[r], xv[i], s[gi], z[gi], xs[gi], cx, acc);
+      }
+    }
+  }
+}
+
+// LN: outputs (qweight columns) per lane; a wavefront covers 64 LN of them, and the four
+// wavefronts of a block split its K range into contiguous bands of whole 128-k steps,
+// combined through LDS in k order. B is the compiled width
+// (1, 2, 4, 8); Bn <= B activation rows are real: the others re-read row Bn - 1 and are not
+// stored. kspan: the K range of one split (a multiple of kGqWaveK); with one split the
+// block writes y (TY), otherwise its partial sums.
 template <bool SYM, int G, int B, int LN, typename TY>
-__global__ __launch_bounds__(256) void gptq_gemv_kernel(const uint32_t* __restrict__ qweight,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 4))) void gptq_gemv_kernel(const uint32_t* __restrict__ qweight,
                                                         const uint16_t* __restrict__ scale_bits,
                                                         const uint32_t* __restrict__ qzeros, int N, int K,
                                                         int kspan, const uint16_t* __restrict__ x, int64_t ldx,
@@ -107,84 +246,26 @@ __global__ __launch_bounds__(256) void gptq_gemv_kernel(const uint32_t* __restri
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int n0 = blockIdx.x * WN + lane * LN;
   const int nc = min(n0, N - LN);                       // N % 8 == 0: lanes past N read a valid place
-  const int kend = min(K, (int)(blockIdx.y + 1) * kspan);
+  const int ks = blockIdx.y * kspan, ke = min(K, ks + kspan);
+  const int per = ((ke - ks + kGqWaveK - 1) / kGqWaveK + 3) / 4;   // steps per band
+  const int kbeg = ks + wave * per * kGqWaveK, kend = min(ke, kbeg + per * kGqWaveK);
   float acc[B][LN];
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
     for (int j = 0; j < LN; ++j) acc[b][j] = 0.0f;
-  // wave-uniform steps; K % G == 0, so every step holds whole groups
-  for (int kw = blockIdx.y * kspan + wave * kGqWaveK; kw < kend; kw += kGqBlockK) {
+  // wave-uniform steps; K % G == 0, so every step holds whole groups, and all but the
+  // last of a band cover kGqWaveK k
+  for (int kw = kbeg; kw < kend; kw += kGqWaveK) {
     const int nr = min(kGqWaveK, K - kw) / 8;           // qweight rows of this wavefront
-    uint32_t wv[kGqWaveK / 8][LN];
-#pragma unroll
-    for (int r = 0; r < kGqWaveK / 8; ++r)
-      if (r < nr) load_words<LN>(qweight + (int64_t)(kw / 8 + r) * N + nc, wv[r]);
-#pragma unroll
-    for (int gi = 0; gi < kGqWaveK / G; ++gi) {
-      const int g0 = kw + gi * G;
-      if (g0 >= K) break;
-      const int g = g0 / G;
-      // group sum of each activation row: two activations per lane, then the wavefront
-      float xs[B];
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        float v = 0.0f;
-        if (2 * lane < G) {
-          const uint32_t p = *reinterpret_cast<const uint32_t*>(x + (int64_t)min(b, Bn - 1) * ldx + g0 + 2 * lane);
-          v = bf16_lo(p) + bf16_hi(p);
-        }
-        xs[b] = wave_sum(v);
-      }
-      float cx[B][LN];
-#pragma unroll
-      for (int b = 0; b < B; ++b)
-#pragma unroll
-        for (int j = 0; j < LN; ++j) cx[b][j] = 0.0f;
-#pragma unroll
-      for (int rr = 0; rr < G / 8; ++rr) {
-        const int r = gi * (G / 8) + rr;
-        float xk[B][8];
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-          const U4 xv = *reinterpret_cast<const U4*>(x + (int64_t)min(b, Bn - 1) * ldx + kw + 8 * r);
-          xk[b][0] = bf16_lo(xv.x); xk[b][1] = bf16_hi(xv.x); xk[b][2] = bf16_lo(xv.y); xk[b][3] = bf16_hi(xv.y);
-          xk[b][4] = bf16_lo(xv.z); xk[b][5] = bf16_hi(xv.z); xk[b][6] = bf16_lo(xv.w); xk[b][7] = bf16_hi(xv.w);
-        }
-#pragma unroll
-        for (int j = 0; j < LN; ++j) {
-          uint32_t ev = wv[r][j] & 0x0F0F0F0Fu, od = (wv[r][j] >> 4) & 0x0F0F0F0Fu;
-          // opaque to the combiner, so each code converts straight from its byte
-          // (v_cvt_f32_ubyte0..3) instead of a bit-field extract per code
-          asm volatile("" : "+v"(ev), "+v"(od));
-          const float c[8] = {(float)(ev & 0xFFu), (float)(od & 0xFFu), (float)((ev >> 8) & 0xFFu),
-                              (float)((od >> 8) & 0xFFu), (float)((ev >> 16) & 0xFFu), (float)((od >> 16) & 0xFFu),
-                              (float)(ev >> 24), (float)(od >> 24)};
-#pragma unroll
-          for (int b = 0; b < B; ++b)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) cx[b][j] = __builtin_fmaf(c[i], xk[b][i], cx[b][j]);
-        }
-      }
-      // s * (sum c x - z * sum x) for this group
-      float s[LN], z[LN];
-#pragma unroll
-      for (int j = 0; j < LN; ++j) {
-        s[j] = (float)__builtin_bit_cast(_Float16, scale_bits[(int64_t)g * N + nc + j]);
-        z[j] = 8.0f;
-      }
-      if constexpr (!SYM) {
-        const uint32_t zw = qzeros[(int64_t)g * (N / 8) + nc / 8] >> (4 * (nc % 8));
-#pragma unroll
-        for (int j = 0; j < LN; ++j) z[j] = (float)((zw >> (4 * j)) & 0xFu);
-      }
-#pragma unroll
-      for (int b = 0; b < B; ++b)
-#pragma unroll
-        for (int j = 0; j < LN; ++j) acc[b][j] = __builtin_fmaf(s[j], __builtin_fmaf(-z[j], xs[b], cx[b][j]), acc[b][j]);
-    }
+    // batches of more than one row keep the per-row branches: without them the scalar
+    // loads of later rows' activations are merged and hoisted past the registers there are
+    if (B == 1 && nr == kGqWaveK / 8)
+      gq_step<SYM, G, B, LN, true>(qweight, scale_bits, qzeros, N, K, x, ldx, Bn, nc, lane, kw, nr, acc);
+    else
+      gq_step<SYM, G, B, LN, false>(qweight, scale_bits, qzeros, N, K, x, ldx, Bn, nc, lane, kw, nr, acc);
   }
-  // the four wavefronts' k-ranges, added in order
+  // the four bands, added in k order
 #pragma unroll
   for (int b = 0; b < B; ++b)
 #pragma unroll
@@ -263,7 +344,7 @@ __global__ __launch_bounds__(256) void gptq_act_gemv_kernel(const uint32_t* __re
     uint32_t wv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (r < nr) wv[r] = qweight[(int64_t)(kw / 8 + r) * N + nc];
+      if (r < nr) wv[r] = ld4_nt(qweight + (int64_t)(kw / 8 + r) * N + nc);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       if (r >= nr) continue;                                    // wave-uniform
@@ -414,22 +495,28 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restri
 // Outputs per lane: 4 (one 16-byte load per qweight row). One and two measured the same
 // for one activation row and slower for four: the kernel is VALU-bound there.
 constexpr int kGqLaneN = 4;
-// K splits: one per kGqBlockK of K when N gives few blocks, fewer (down to one, which needs
-// no second pass) when N / (64 LN) alone gives at least kGqMinBlocks.
-constexpr int kGqMinBlocks = 512;
+// K splits: none when the column chunks alone give kGqMinBlocks blocks (a second pass
+// costs more than it gains there); otherwise enough for about kGqSplitBlocks blocks, at
+// most one per four wavefront steps of K. Measured on MI355X: contiguous K bands per
+// wavefront read faster than wavefronts on interleaved 128-k steps, and one 1 KB column
+// chunk per block faster than two or four neighbouring chunks.
+constexpr int kGqMinBlocks = 512, kGqSplitBlocks = 1024;
+constexpr int kGqBandK = 4 * kGqWaveK;                   // one step of each of a block's bands
 int gptq_gemv_splits(int64_t N, int64_t K) {
   const int64_t wn = 64 * kGqLaneN;
-  const int64_t tiles = (N + wn - 1) / wn, kb = (K + kGqBlockK - 1) / kGqBlockK;
-  const int64_t want = (kGqMinBlocks + tiles - 1) / tiles;
-  return (int)(want < 1 ? 1 : (want > kb ? kb : want));
+  const int64_t tiles = (N + wn - 1) / wn, kb = (K + kGqBandK - 1) / kGqBandK;
+  if (tiles >= kGqMinBlocks) return 1;
+  const int64_t want = (kGqSplitBlocks + tiles - 1) / tiles;
+  const int64_t per = (kb + (want > kb ? kb : want) - 1) / (want > kb ? kb : want);   // units per split
+  return (int)((kb + per - 1) / per);                   // every split holds some of K
 }
 
 template <bool SYM, int G, int B, int LN, typename TY>
 static void gptq_gemv_ln(int Bn, const void* qw, const void* sc, const void* qz, int64_t N, int64_t K, const void* x,
                          int64_t ldx, float* part, void* y, int64_t ldy, hipStream_t st) {
   const int S = gptq_gemv_splits(N, K);
-  const int64_t kb = (K + kGqBlockK - 1) / kGqBlockK;
-  const int kspan = (int)((kb + S - 1) / S) * kGqBlockK;
+  const int64_t kb = (K + kGqBandK - 1) / kGqBandK;
+  const int kspan = (int)((kb + S - 1) / S) * kGqBandK;
   const dim3 grid((unsigned)((N + 64 * LN - 1) / (64 * LN)), (unsigned)S);
   hipLaunchKernelGGL((gptq_gemv_kernel<SYM, G, B, LN, TY>), grid, dim3(256), 0, st, (const uint32_t*)qw,
                      (const uint16_t*)sc, (const uint32_t*)qz, (int)N, (int)K, kspan, (const uint16_t*)x, ldx, Bn,
@@ -472,9 +559,10 @@ void launch_gptq_gemv(bool sym, int group, int B, const void* qweight, const voi
   if (S > 1) launch_gemv_finalize(part, S, B, N, y, y_dtype, ldy, st);
 }
 
+constexpr int kActMinBlocks = 512;
 int gptq_act_gemv_splits(int64_t N, int64_t K) {
   const int64_t tiles = (N + kActGvCols - 1) / kActGvCols, kb = (K + 511) / 512;
-  const int64_t want = (kGqMinBlocks + tiles - 1) / tiles;
+  const int64_t want = (kActMinBlocks + tiles - 1) / tiles;
   return (int)(want < 1 ? 1 : (want > kb ? kb : want));
 }
 

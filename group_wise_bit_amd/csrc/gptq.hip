@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) void gptq_dequant_kernel(const uint32_t* __res
     for (int h = 0; h < 2; ++h) {
       const int r = wave * 16 + h * 8 + (lane >> 3), c4 = (lane & 7) * 4;
       qok[h] = k0 / 8 + r < K / 8 && n0 + c4 < N;    // N % 8 == 0: whole 16-byte runs
-      qv[h] = qok[h] ? ld16(qweight + (int64_t)(k0 / 8 + r) * N + n0 + c4) : U4{};
+      qv[h] = qok[h] ? ld16_nt(qweight + (int64_t)(k0 / 8 + r) * N + n0 + c4) : U4{};
     }
     constexpr int kSPer = (T::NG * kTN + 255) / 256;   // scales per thread
     uint16_t sv[kSPer];

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void mxfp4_dequant_kernel(const uint32_t* __re
     uint32_t w[kMxUnits], e[kMxUnits];
 #pragma unroll
     for (int i = 0; i < kMxUnits; ++i) {
-      w[i] = packed[u + i * stride];
+      w[i] = ld4_nt(packed + u + i * stride);
       e[i] = e8m0[(u + i * stride) >> 2];
       if constexpr (SINK == kErr) x[i] = load_raw8(unit_ptr<CONTIG>(W, ldw, u + i * stride, upr));
     }

@@ -44,6 +44,10 @@ __device__ __forceinline__ void st8(uint8_t* p, uint32_t lo, uint32_t hi) {
   __builtin_nontemporal_store(ux_u32x2_t{lo, hi}, reinterpret_cast<ux_u32x2_t*>(p));
 }
 __device__ __forceinline__ uint2 ld8(const uint8_t* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ uint2 ld8_nt(const uint8_t* p) {
+  const ux_u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const ux_u32x2_t*>(p));
+  return make_uint2(v[0], v[1]);
+}
 
 template <typename T>
 __device__ __forceinline__ Raw8<T> ux_load_raw8(const T* p) { return load_raw8(p); }
@@ -274,13 +278,13 @@ __global__ __launch_bounds__(256) void uintx_dequant_tiled(const uint8_t* __rest
     Raw8<typename D::T> wr[8];               // the error sink's weights
     if constexpr (SB::has4) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) s4[m] = ld8(packed + sh.base4 + (int64_t)m * L1 + p);
+      for (int m = 0; m < 4; ++m) s4[m] = ld8_nt(packed + sh.base4 + (int64_t)m * L1 + p);
     }
     if constexpr (SB::has2) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) s2[m] = ld8(packed + sh.base2 + (int64_t)m * L1 + p);
+      for (int m = 0; m < 2; ++m) s2[m] = ld8_nt(packed + sh.base2 + (int64_t)m * L1 + p);
     }
-    if constexpr (SB::has1) s1 = ld8(packed + sh.base1 + p);
+    if constexpr (SB::has1) s1 = ld8_nt(packed + sh.base1 + p);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const uint32_t g = (j * L1 + p) / G;   // L1 % G == 0: a lane's 8 positions share a group
