@@ -433,12 +433,12 @@ int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t
 }
 
 // Batches that the matrix-core tile kernels of gwb_gemm take faster than the GEMV
-// kernels: GPTQ with groups in index order from 2 rows, MXFP4 from 5 (where the GEMV
-// runs its 8-row instance), when the shape fits the tile (N % 8 == 0, K % 128 == 0).
+// kernels: GPTQ with groups in index order from 2 rows, when the shape fits the tile
+// (N % 8 == 0, K % 128 == 0). MXFP4 batches stay with the GEMV, whose own matrix-core
+// kernel takes 5 to 8 rows.
 static bool gemv_shape_via_gemm(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
   if (N % 8 || K % 128 || B * K >= kMaxElems) return false;
-  if (sp->format == GWB_GPTQ_SYM || sp->format == GWB_GPTQ_ASYM) return B >= 2;
-  return is_mxfp4(sp->format) && B >= 5;
+  return (sp->format == GWB_GPTQ_SYM || sp->format == GWB_GPTQ_ASYM) && B >= 2;
 }
 // bf16-weight uintx batches of 5+ rows on weights of 65536+ rows take gwb_gemm's uintx
 // tiles (measured: lm_head 131072 x 2048 at B = 8 105 -> 62 us; on narrower weights the
@@ -456,6 +456,7 @@ static size_t gemv_kernel_workspace(const gwb_qspec* sp, int64_t N, int64_t K, i
   if (sp->format == GWB_GPTQ_SYM || sp->format == GWB_GPTQ_ASYM) S = gwb::gptq_gemv_splits(N, K);
   if (is_act(sp->format)) S = gwb::gptq_act_gemv_splits(N, K);
   if (sp->format == GWB_UINTX) S = gwb::uintx_gemv_splits(K, (int)B);
+  if (is_mxfp4(sp->format)) S = gwb::mxfp4_gemv_splits(K, (int)B);
   return S > 1 ? (size_t)S * (size_t)B * (size_t)N * sizeof(float) : 0;
 }
 
@@ -515,7 +516,7 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
     gwb::launch_gptq_gemm(spec->format == GWB_GPTQ_SYM, spec->group, w->codes, w->scales, w->zeros, N, K, x, B, ldx,
                           y, y_dtype, ldy, workspace, st);
   else if (is_mxfp4(spec->format))
-    gwb::launch_mxfp4_gemv((int)B, w->codes, w->scales, N, K, x, ldx, y, y_dtype, ldy, st);
+    gwb::launch_mxfp4_gemv((int)B, w->codes, w->scales, N, K, x, ldx, y, y_dtype, ldy, (float*)workspace, st);
   else if (is_act(spec->format))
     gwb::launch_gptq_act_gemv(is_gptq_sym(spec->format), spec->group, (int)B, w->codes, w->scales, w->zeros,
                               (const int32_t*)w->g_idx, N, K, x, ldx, y, y_dtype, ldy, (float*)workspace, st);

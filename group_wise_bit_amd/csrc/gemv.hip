@@ -21,6 +21,8 @@
 // scale 1 (exact), v_dot2c_f32_bf16 multiplies them with the activation pairs, and the
 // block sum is scaled by 2^(e8m0 - 127) (exact). A wavefront takes 8 rows at a time and
 // reduces each across its lanes.
+#include <atomic>
+
 #include "kernels.hpp"
 #include "mxfp4_math.hpp"
 
@@ -422,6 +424,24 @@ __device__ __forceinline__ void load_x_block(const uint16_t* __restrict__ x, int
   }
 }
 
+// Sum over the 32-blocks lane, lane + 64, ... of row n that have a scale byte of 255, of
+// the activations xr times the page's weights there (+-E2M1 * 2^128: inf, or NaN for a
+// zero code), in float32. Out of line: the rare path keeps its registers out of the
+// main loop.
+__device__ __attribute__((noinline)) float mx_nan_lane_sum(const uint8_t* __restrict__ packed,
+                                                           const uint8_t* __restrict__ e8m0, int K, int n,
+                                                           const uint16_t* __restrict__ xr, int lane) {
+  const int nblk = K / 32;
+  const uint8_t* crow = packed + (int64_t)n * (K / 2);
+  float sum = 0.0f;
+  for (int blk = lane; blk < nblk; blk += 64) {
+    if (e8m0[(int64_t)n * nblk + blk] != 255u) continue;
+    for (int k = 32 * blk; k < 32 * blk + 32; ++k)
+      sum += bf16_to_f32(xr[k]) * mx_value_nan_scale((crow[k >> 1] >> (4 * (k & 1))) & 0xFu);
+  }
+  return sum;
+}
+
 template <int B, typename TY>
 __global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restrict__ packed,
                                                          const uint8_t* __restrict__ e8m0, int N, int K,
@@ -442,6 +462,7 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restri
     for (int i = 0; i < R; ++i)
 #pragma unroll
       for (int b = 0; b < B; ++b) acc[i][b] = 0.0f;
+    uint32_t nanm = 0;                                  // bit i: this lane has a block of row i with scale byte 255
     for (int st = 0; st < steps; ++st) {
       const int blk = st * 64 + lane;
       const bool ok = blk < nblk;
@@ -476,8 +497,21 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restri
                                                      false);
         }
         const int ex = (int)ev[i] - 127;
+        nanm |= (uint32_t)(ok && ev[i] == 255u) << i;
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[i][b] += ok ? ldexpf(d[b], ex) : 0.0f;
+      }
+    }
+    // Blocks with a scale byte of 255 (no E8M0 value): the page's weights +-E2M1 * 2^128
+    // are inf or NaN (NaN for a zero code), so such a lane's sum for that row becomes the
+    // float32 sum over its 255 blocks alone, which adding the finite rest cannot change.
+    if (__any(nanm != 0u)) {                                    // wave-uniform, rare
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        if (!((nanm >> i) & 1u)) continue;
+        const int n = min(row0 + i, N - 1);
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[i][b] = mx_nan_lane_sum(packed, e8m0, K, n, x + (int64_t)b * ldx, lane);
       }
     }
     // value i B + b (row i, activation row b), padded with zeros to VP
@@ -488,6 +522,216 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_kernel(const uint8_t* __restri
     const float sum = gv_transposed_sum<VP>(v, lane);
     const int e = lane & (VP - 1), i = e / B, b = e - i * B;
     if (lane < V && row0 + i < N) store_y(y + (int64_t)b * ldy + row0 + i, sum);
+  }
+}
+
+// ------------------------------------------------------------------ MXFP4, batches on the matrix cores
+// Five to eight activation rows: v_mfma_f32_16x16x32_bf16 with the weights as A (16 rows
+// x 32 k) and the activations as B (32 k x 16 columns, one per activation row; columns
+// past the batch repeat the last row and are not stored). A wavefront takes tiles of 16
+// weight rows. Per 128 k, lane (j = l % 16, q = l / 16) loads the 16 bytes of 32-block
+// k0 + 32q of row j; their scaled FP4 conversion gives the exact bf16 weights of four A
+// fragments, slot q of MFMA s holding k0 + 32q + 8s .. +7, and the B fragment of that slot
+// is x[j][k0 + 32q + 8s .. +7] (the same relabelling of k on both sides). Lane (j, q)
+// ends with weight rows 4q .. 4q + 3 for activation row j. Products are exact; the sums
+// are the matrix cores' float32 sums.
+// K splits of at most mxm_chunk(B) k (blockIdx.y) keep a block's activations in LDS,
+// staged once; with more than one split each writes float32 partials, added in split
+// order afterwards. The blocks are persistent, and a wavefront's loads run one batch
+// (kMxmNS steps of 128 k) ahead of its products, across tile boundaries, from two
+// register buffers.
+constexpr int kMxmNS = 8;
+constexpr int kMxmLds = 8 * 2056 * 2;               // activation bytes staged per block: 8 rows of 2048 k
+// From 5 activation rows (measured on the 131072 x 2048 lm_head: B = 8 37 us against 45
+// for the GEMM tiles and 75 for the 32-block GEMV kernel; B <= 4 the GEMV kernel is as
+// fast or faster: each of its loads reads 1 KB of one row, the matrix-core order 64 bytes
+// of each of 16 rows).
+constexpr int kMxmMinRows = 5;
+
+// K per split for B activation rows: B (kc + 8) bf16 within kMxmLds bytes, a multiple
+// of the 1024 k of a batch.
+__host__ __device__ constexpr int mxm_chunk(int B) { return (kMxmLds / (2 * B) - 8) / 1024 * 1024; }
+int mxfp4_gemv_splits(int64_t K, int B) {
+  if (B < kMxmMinRows) return 1;
+  const int64_t kc = mxm_chunk(B);
+  return (int)((K + kc - 1) / kc);
+}
+
+typedef __bf16 gv_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float gv_f32x4_t __attribute__((ext_vector_type(4)));
+
+struct MxmBuf {
+  U4 w[kMxmNS];
+  uint32_t e[kMxmNS];   // AL: the batch's 32 scale bytes of the row (step i's block q in byte q of e[i]); else step i's byte
+};
+
+// The loads of one batch: steps k0 + 128 i. AL (K % 1024 == 0: every batch lies inside
+// its split, and rows of scale bytes are 16-byte aligned): the row's 32 scale bytes of
+// the batch in two 16-byte loads; otherwise one byte per step, and slots past the split
+// end re-read its last block. live == false points every lane at the row's first bytes
+// (a prefetch past the wavefront's last tile), so the instruction count never depends on
+// data.
+template <bool AL>
+__device__ __forceinline__ void mxm_load(MxmBuf& bf, const uint8_t* __restrict__ wr, const uint8_t* __restrict__ er,
+                                         int k0, int kend, int q, bool live) {
+#pragma unroll
+  for (int i = 0; i < kMxmNS; ++i) {
+    const int kk = !live ? 0 : AL ? k0 + 128 * i + 32 * q : min(k0 + 128 * i + 32 * q, kend - 32);
+    bf.w[i] = ld16_nt(wr + kk / 2);
+    if constexpr (!AL) bf.e[i] = er[kk / 32];
+  }
+  if constexpr (AL) {
+    const uint8_t* ep = er + (live ? k0 / 32 : 0);
+    const U4 lo = ld16(ep), hi = ld16(ep + 16);
+    bf.e[0] = lo.x; bf.e[1] = lo.y; bf.e[2] = lo.z; bf.e[3] = lo.w;
+    bf.e[4] = hi.x; bf.e[5] = hi.y; bf.e[6] = hi.z; bf.e[7] = hi.w;
+  }
+}
+
+// The products of one batch; xb: this lane's activation row in LDS, from the split start.
+// FULL: the whole batch lies inside the split.
+template <bool AL, bool FULL>
+__device__ __forceinline__ void mxm_mma(const MxmBuf& bf, const uint16_t* xb, int k0, int ks, int kend, int q,
+                                        gv_f32x4_t& acc, uint32_t& nan) {
+  static_assert(kMxmNS == 8, "a batch's scale bytes are two 16-byte loads");
+#pragma unroll
+  for (int i = 0; i < kMxmNS; ++i) {
+    const int k = k0 + 128 * i;
+    if (FULL || k < kend) {                                     // wave-uniform
+      const bool ok = FULL || k + 32 * q < kend;                // this lane's 32-block is inside the split
+      const uint32_t e8 = AL ? (bf.e[i] >> (8 * q)) & 0xFFu : bf.e[i];
+      const float scl = mx_scale_operand(e8);
+      nan |= (uint32_t)(ok && e8 == 255u);
+      U4 b[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        b[s] = *reinterpret_cast<const U4*>(xb + (ok ? (k - ks) + 32 * q + 8 * s : 0));   // inside the staged row
+        if (!ok) b[s] = U4{0u, 0u, 0u, 0u};
+      }
+      const U4 w = bf.w[i];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t wd = s == 0 ? w.x : s == 1 ? w.y : s == 2 ? w.z : w.w;
+        U4 a{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 0)),
+             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 1)),
+             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 2)),
+             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, scl, 3))};
+        if (!ok) a = U4{0u, 0u, 0u, 0u};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(gv_bf16x8_t, a),
+                                                      __builtin_bit_cast(gv_bf16x8_t, b[s]), acc, 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Rows of a tile with a scale byte of 255 in the split [ks, kend): lane (j, q)'s outputs
+// 4q + r of those rows become the float32 sum of x[j] times the page's inf or NaN weights
+// over the split's such blocks. Out of line: the common path keeps its load bookkeeping.
+__device__ __attribute__((noinline)) gv_f32x4_t mxm_nan_rows(const uint8_t* __restrict__ packed,
+                                                             const uint8_t* __restrict__ e8m0, int N, int K,
+                                                             const uint16_t* __restrict__ x, int64_t ldx, int ks,
+                                                             int kend, int n0, int j, int q, bool bcol, uint32_t rows,
+                                                             gv_f32x4_t acc) {
+  const int64_t rowb = K / 2, rowe = K / 32;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (!((rows >> (4 * q + r)) & 1u) || !bcol) continue;
+    const int n = min(n0 + 4 * q + r, N - 1);
+    const uint8_t* crow = packed + n * rowb;
+    const uint8_t* erow = e8m0 + n * rowe;
+    const uint16_t* xr = x + (int64_t)j * ldx;
+    float sum = 0.f;
+    for (int blk = ks / 32; blk < kend / 32; ++blk) {
+      if (erow[blk] != 255u) continue;
+      for (int k = 32 * blk; k < 32 * blk + 32; ++k)
+        sum += bf16_to_f32(xr[k]) * mx_value_nan_scale((crow[k >> 1] >> (4 * (k & 1))) & 0xFu);
+    }
+    acc[r] = sum;
+  }
+  return acc;
+}
+
+template <typename TY, bool AL>
+__global__ __launch_bounds__(256) void mxfp4_gemv_mfma_kernel(const uint8_t* __restrict__ packed,
+                                                              const uint8_t* __restrict__ e8m0, int N, int K,
+                                                              const uint16_t* __restrict__ x, int64_t ldx, int Bn,
+                                                              TY* __restrict__ y, int64_t ldy,
+                                                              float* __restrict__ part) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [Bn][kc + 8]
+  const int t = threadIdx.x, lane = t & 63, j = lane & 15, q = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t rowb = K / 2, rowe = K / 32;
+  const int kc = mxm_chunk(Bn), xp = kc + 8;
+  const int ks = (int)blockIdx.y * kc, kend = min(K, ks + kc);   // this split: [ks, kend), a multiple of 32
+  const int nb = (kend - ks + 128 * kMxmNS - 1) / (128 * kMxmNS);   // batches per tile
+  const int nbt = (N + 63) / 64;                                // 64-row block tiles
+  // the split's activations, staged once (rows in LDS padded by 16 bytes: no bank conflicts)
+  const int cpr = (kend - ks) / 8;
+  for (int v = t; v < Bn * cpr; v += 256) {
+    const int b = v / cpr, c = v - b * cpr;
+    *reinterpret_cast<U4*>(xs + b * xp + 8 * c) = ld16(x + (int64_t)b * ldx + ks + 8 * c);
+  }
+  __syncthreads();
+  const uint16_t* xb = xs + min(j, Bn - 1) * xp;                // rows past the batch repeat the last
+  const bool bcol = j < Bn;
+  auto rows_of = [&](int bt, const uint8_t*& wr, const uint8_t*& er) {
+    const int nl = min((bt * 4 + wave) * 16 + j, N - 1);        // rows past N read a valid row, not stored
+    wr = packed + nl * rowb;
+    er = e8m0 + nl * rowe;
+  };
+  // finish a tile: rows with a scale byte of 255 (no E8M0 value; the page's weights
+  // +-E2M1 * 2^128 are inf or NaN) get the float32 sum over the split's such blocks alone,
+  // which adding the finite rest cannot change; then the rows are stored
+  auto finish = [&](int bt, gv_f32x4_t& acc, uint32_t& nan) {
+    const int n0 = (bt * 4 + wave) * 16;
+    const uint64_t m = __ballot(nan != 0u);
+    const uint32_t rows = (uint32_t)((m | (m >> 16) | (m >> 32) | (m >> 48)) & 0xFFFFu);
+    if (rows != 0u) acc = mxm_nan_rows(packed, e8m0, N, K, x, ldx, ks, kend, n0, j, q, bcol, rows, acc);   // rare
+    if (bcol) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = n0 + 4 * q + r;
+        if (n >= N) continue;
+        if (gridDim.y == 1) store_y(y + (int64_t)j * ldy + n, acc[r]);
+        else part[((int64_t)blockIdx.y * Bn + j) * N + n] = acc[r];
+      }
+    }
+    acc = gv_f32x4_t{0.f, 0.f, 0.f, 0.f};
+    nan = 0u;
+  };
+  int bt = blockIdx.x, h = 0;                                   // block-uniform
+  if (bt >= nbt) return;                                        // after the only barrier
+  gv_f32x4_t acc = gv_f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint32_t nan = 0u;
+  const uint8_t *wr, *er;
+  rows_of(bt, wr, er);
+  MxmBuf b0, b1;
+  mxm_load<AL>(b0, wr, er, ks, kend, q, true);
+  // two items per trip, one per buffer: load the next item, then multiply the current
+  for (;;) {
+    int bt2 = bt, h2 = h + 1;
+    if (h2 == nb) { h2 = 0; bt2 += gridDim.x; }
+    bool more = bt2 < nbt;
+    const uint8_t *wr2 = wr, *er2 = er;
+    if (bt2 != bt && more) rows_of(bt2, wr2, er2);
+    mxm_load<AL>(b1, wr2, er2, ks + h2 * 128 * kMxmNS, kend, q, more);
+    if (AL || ks + (h + 1) * 128 * kMxmNS <= kend) mxm_mma<AL, true>(b0, xb, ks + h * 128 * kMxmNS, ks, kend, q, acc, nan);
+    else mxm_mma<AL, false>(b0, xb, ks + h * 128 * kMxmNS, ks, kend, q, acc, nan);
+    if (h == nb - 1) finish(bt, acc, nan);
+    if (!more) break;
+    bt = bt2; h = h2; wr = wr2; er = er2;
+
+    bt2 = bt; h2 = h + 1;
+    if (h2 == nb) { h2 = 0; bt2 += gridDim.x; }
+    more = bt2 < nbt;
+    wr2 = wr; er2 = er;
+    if (bt2 != bt && more) rows_of(bt2, wr2, er2);
+    mxm_load<AL>(b0, wr2, er2, ks + h2 * 128 * kMxmNS, kend, q, more);
+    if (AL || ks + (h + 1) * 128 * kMxmNS <= kend) mxm_mma<AL, true>(b1, xb, ks + h * 128 * kMxmNS, ks, kend, q, acc, nan);
+    else mxm_mma<AL, false>(b1, xb, ks + h * 128 * kMxmNS, ks, kend, q, acc, nan);
+    if (h == nb - 1) finish(bt, acc, nan);
+    if (!more) break;
+    bt = bt2; h = h2; wr = wr2; er = er2;
   }
 }
 
@@ -630,25 +874,65 @@ static void mxfp4_gemv_b(const void* packed, const void* e8m0, int64_t N, int64_
                      (const uint8_t*)e8m0, (int)N, (int)K, (const uint16_t*)x, ldx, (TY*)y, ldy);
 }
 
+// Blocks of the matrix-core MXFP4 GEMV that are resident at once (its registers and
+// the LDS of B activation rows), times the compute units: the kernel loops over its tiles
+// with that many blocks, so none waits for a second round. Cached per device, B, output
+// type and variant.
+static unsigned mxm_resident_blocks(const void* kern, size_t lds, int B, bool f32, bool al) {
+  constexpr int kDev = 64;
+  static std::atomic<unsigned> cache[kDev][9][2][2];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDev) dev = -1;
+  if (dev >= 0) {
+    const unsigned c = cache[dev][B][f32][al].load(std::memory_order_relaxed);
+    if (c) return c;
+  }
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess || cus < 1)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, 256, lds) != hipSuccess || per < 1) per = 1;
+  const unsigned r = (unsigned)per * (unsigned)cus;
+  if (dev >= 0) cache[dev][B][f32][al].store(r, std::memory_order_relaxed);
+  return r;
+}
+
 template <typename TY>
 static void mxfp4_gemv_t(int B, const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x,
-                         int64_t ldx, void* y, int64_t ldy, hipStream_t st) {
+                         int64_t ldx, void* y, int64_t ldy, float* part, hipStream_t st) {
+  if (B >= kMxmMinRows) {
+    const int S = mxfp4_gemv_splits(K, B);
+    const size_t lds = (size_t)B * (mxm_chunk(B) + 8) * sizeof(uint16_t);   // at most kMxmLds
+    const int64_t tiles = (N + 63) / 64;
+    const bool al = K % 1024 == 0;
+    const void* kern = al ? reinterpret_cast<const void*>(&mxfp4_gemv_mfma_kernel<TY, true>)
+                          : reinterpret_cast<const void*>(&mxfp4_gemv_mfma_kernel<TY, false>);
+    const unsigned res = mxm_resident_blocks(kern, lds, B, sizeof(TY) == 4, al);
+    const int64_t per = ((int64_t)res + S - 1) / S;             // blocks per split
+    const unsigned gx = (unsigned)(tiles < per ? tiles : per);
+    if (al)
+      hipLaunchKernelGGL((mxfp4_gemv_mfma_kernel<TY, true>), dim3(gx, (unsigned)S), dim3(256), lds, st,
+                         (const uint8_t*)packed, (const uint8_t*)e8m0, (int)N, (int)K, (const uint16_t*)x, ldx, B,
+                         (TY*)y, ldy, part);
+    else
+      hipLaunchKernelGGL((mxfp4_gemv_mfma_kernel<TY, false>), dim3(gx, (unsigned)S), dim3(256), lds, st,
+                         (const uint8_t*)packed, (const uint8_t*)e8m0, (int)N, (int)K, (const uint16_t*)x, ldx, B,
+                         (TY*)y, ldy, part);
+    return;
+  }
   switch (B) {
     case 1: mxfp4_gemv_b<1, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
     case 2: mxfp4_gemv_b<2, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
     case 3: mxfp4_gemv_b<3, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
-    case 4: mxfp4_gemv_b<4, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
-    case 5: mxfp4_gemv_b<5, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
-    case 6: mxfp4_gemv_b<6, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
-    case 7: mxfp4_gemv_b<7, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
-    default: mxfp4_gemv_b<8, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
+    default: mxfp4_gemv_b<4, TY>(packed, e8m0, N, K, x, ldx, y, ldy, st); break;
   }
 }
 
 void launch_mxfp4_gemv(int B, const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x,
-                       int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, hipStream_t st) {
-  if (y_dtype == kBF16) mxfp4_gemv_t<uint16_t>(B, packed, e8m0, N, K, x, ldx, y, ldy, st);
-  else mxfp4_gemv_t<float>(B, packed, e8m0, N, K, x, ldx, y, ldy, st);
+                       int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, float* part, hipStream_t st) {
+  if (y_dtype == kBF16) mxfp4_gemv_t<uint16_t>(B, packed, e8m0, N, K, x, ldx, y, ldy, part, st);
+  else mxfp4_gemv_t<float>(B, packed, e8m0, N, K, x, ldx, y, ldy, part, st);
+  const int S = mxfp4_gemv_splits(K, B);
+  if (S > 1) launch_gemv_finalize(part, S, B, N, y, y_dtype, ldy, st);
 }
 
 }  // namespace gwb

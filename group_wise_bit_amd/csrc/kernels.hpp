@@ -151,8 +151,9 @@ int gptq_act_gemv_splits(int64_t N, int64_t K);
 void launch_gptq_act_gemv(bool sym, int group, int B, const void* qweight, const void* scales, const void* qzeros,
                           const int32_t* g_idx, int64_t N, int64_t K, const void* x, int64_t ldx, void* y,
                           int32_t y_dtype, int64_t ldy, float* part, hipStream_t st);
+int mxfp4_gemv_splits(int64_t K, int B);      // K splits of the matrix-core GEMV (B >= 2); part as for GPTQ
 void launch_mxfp4_gemv(int B, const void* packed, const void* e8m0, int64_t N, int64_t K, const void* x,
-                       int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, hipStream_t st);
+                       int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, float* part, hipStream_t st);
 // ---- prefill GEMM on quantized weights (gemm.hip): M activation rows (bf16), matrix
 // cores; N % 8 == 0, K % 128 == 0. Workspace: GPTQ's group sums of x, then (small M)
 // the K-split partial sums.

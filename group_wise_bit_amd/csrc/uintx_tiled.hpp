@@ -388,6 +388,22 @@ inline int ux_gemv_chunks(int64_t K, int B) {
   return K % 1024 == 0 ? 2 : 1;
 }
 
+// The 4 code bytes of a dword as floats. A code below 16 (NB <= 4) read as an OCP e4m3
+// byte is c * 2^-9 exactly (subnormals and the first binade share one spacing), so the
+// scaled FP8 conversion at 2^9 gives two per instruction; wider codes convert byte by
+// byte.
+template <int NB>
+__device__ __forceinline__ void ux_code_floats(uint32_t cd, float (&c)[4]) {
+  if constexpr (NB <= 4) {
+    const ux_f32x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cd, 512.0f, false);
+    const ux_f32x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cd, 512.0f, true);
+    c[0] = lo[0]; c[1] = lo[1]; c[2] = hi[0]; c[3] = hi[1];
+  } else {
+    c[0] = (float)(cd & 0xFFu); c[1] = (float)((cd >> 8) & 0xFFu);
+    c[2] = (float)((cd >> 16) & 0xFFu); c[3] = (float)(cd >> 24);
+  }
+}
+
 template <int NB, int DT, int G, int B, int CH>
 __global__ __launch_bounds__(256) void uintx_gemv_tiled(const uint8_t* __restrict__ packed,
                                                         const typename UxDt<DT>::T* __restrict__ scales,
@@ -455,16 +471,18 @@ __global__ __launch_bounds__(256) void uintx_gemv_tiled(const uint8_t* __restric
           cd[h] |= (((h ? s2[c][j & 1].y : s2[c][j & 1].x) >> (2 * (j >> 1))) & 0x03030303u) << SB::off2;
         if constexpr (SB::has1) cd[h] |= (((h ? s1[c].y : s1[c].x) >> j) & 0x01010101u) << SB::off1;
       }
-      float d[8];
+      float cf[8], d[8];
+      ux_code_floats<NB>(cd[0], reinterpret_cast<float(&)[4]>(cf[0]));
+      ux_code_floats<NB>(cd[1], reinterpret_cast<float(&)[4]>(cf[4]));
       if constexpr (DT == kF32) {
         // (q - zp) exact, times s: the page's one float32 rounding
 #pragma unroll
-        for (int q = 0; q < 8; ++q) d[q] = ((float)((cd[q >> 2] >> (8 * (q & 3))) & 0xFFu) - zp) * s;
+        for (int q = 0; q < 8; ++q) d[q] = (cf[q] - zp) * s;
       } else {
         // exact in float32 for the 2-byte dtypes: c * s - zp * s as one fma
         const float nzs = -(zp * s);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) d[q] = __builtin_fmaf((float)((cd[q >> 2] >> (8 * (q & 3))) & 0xFFu), s, nzs);
+        for (int q = 0; q < 8; ++q) d[q] = __builtin_fmaf(cf[q], s, nzs);
         if constexpr (DT == kF16) {
 #pragma unroll
           for (int q = 0; q < 8; ++q) d[q] = D::rnd(d[q]);      // the fp16 weight, then its bf16

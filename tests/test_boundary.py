@@ -259,15 +259,19 @@ def test_gemv_sizes_and_validation():
         rc = lib.gwb_gemv_workspace(ctypes.byref(sp), N, K, B, ctypes.byref(b))
         return rc, b.value
     assert ws("gptq_sym", 131072, 2048, 1) == (gwb.OK, 0)                  # 512 column tiles: one split
-    assert ws("gptq_sym", 65536, 2048, 1) == (gwb.OK, 2 * 65536 * 4)        # 256 tiles: two K splits
-    # B >= 2 GPTQ and B >= 5 MXFP4 may take the GEMM tiles: the larger of the two needs.
+    assert ws("gptq_sym", 65536, 2048, 1) == (gwb.OK, 4 * 65536 * 4)        # 256 tiles: four K splits (~1024 blocks)
+    assert ws("gptq_sym", 34816, 5120, 1) == (gwb.OK, 5 * 34816 * 4)        # 136 tiles: 1024 k per split, 5 splits
+    # B >= 2 GPTQ may take the GEMM tiles: the larger of the two needs.
     # GPTQ asym g64 256 x 640, B = 3: GEMV 2 splits x 3 x 256 floats; tiles: the group
     # sums (10 groups x 128 padded rows floats) + 2 K splits x 3 x 256 floats
     assert ws("gptq_asym", 256, 640, 3, 64) == (gwb.OK, 10 * 128 * 4 + 2 * 3 * 256 * 4)
     assert ws("gptq_sym", 131072, 2048, 2) == (gwb.OK, 16 * 128 * 4)            # 512 tiles: no split
     assert ws("gptq_asym", 256, 576, 3, 64) == (gwb.OK, 2 * 3 * 256 * 4)      # K % 128 != 0: GEMV only
     assert ws("mxfp4", 4096, 2048, 4) == (gwb.OK, 0)                          # the GEMV: no workspace
-    assert ws("mxfp4", 4096, 2048, 8) == (gwb.OK, 8 * 8 * 4096 * 4)           # 16 tiles: 8 K splits
+    # 5 to 8 rows: the matrix-core GEMV, K splits of at most 2048 k (8 rows) or 3072 (5)
+    assert ws("mxfp4", 4096, 2048, 8) == (gwb.OK, 0)
+    assert ws("mxfp4", 34816, 5120, 8) == (gwb.OK, 3 * 8 * 34816 * 4)
+    assert ws("mxfp4", 34816, 5120, 5) == (gwb.OK, 2 * 5 * 34816 * 4)
     assert ws("gptq_sym", 256, 512, 0)[0] == gwb.E_ARG
     assert ws("gptq_sym", 256, 512, 9)[0] == gwb.E_ARG
     sp_u = gwb.make_spec("uintx", 4, 64)

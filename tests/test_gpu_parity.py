@@ -466,12 +466,12 @@ def _gptq_bound(o, x, group, sym, K):
 
 
 def _gemv_tiles(fmt, n, k, B):
-    """gwb_gemv hands GPTQ (index-order groups) batches of 2+ rows and MXFP4 batches of
-    5+ to the GEMM tile kernels when N % 8 == 0 and K % 128 == 0 and y's rows are
-    16-byte aligned (every output here with ldy = N)."""
+    """gwb_gemv hands GPTQ (index-order groups) batches of 2+ rows to the GEMM tile
+    kernels when N % 8 == 0 and K % 128 == 0 and y's rows are 16-byte aligned (every
+    output here with ldy = N)."""
     if n % 8 or k % 128:
         return False
-    return B >= 2 if fmt in ("gptq_sym", "gptq_asym") else (fmt == "mxfp4" and B >= 5)
+    return B >= 2 and fmt in ("gptq_sym", "gptq_asym")
 
 
 def _uintx_tiles(dt, n, k, B):
@@ -518,6 +518,13 @@ def test_gemv_gptq_parity(fmt, group, n, k, B):
         _gemv_check(gwb.gemv(q, x.to(DEV), out=_strided_out(B, n, ydt)), ref, gemv_bound, ydt)
 
 
+def _mx_gemv_bound(deq, xf, k, B):
+    """Products exact. Up to 4 rows: 32-block sums in float32, scaled exactly, then added
+    over K; 5 to 8 rows (the matrix-core GEMV, any y layout): the matrix cores' float32
+    sums, u (K + 8) sum |w x|."""
+    return U32 * ((k + 8) if B >= 5 else (32 + k // 2048 + 40)) * ogv.abs_gemv(deq, xf)
+
+
 @pytest.mark.parametrize("n,k,B", [(64, 512, 1), (33, 96, 3), (40, 4096, 2), (17, 2080, 8), (300, 2048, 5),
                                    (264, 2048, 8), (72, 640, 6)])
 def test_gemv_mxfp4_parity(n, k, B):
@@ -528,12 +535,42 @@ def test_gemv_mxfp4_parity(n, k, B):
     deq = omx.dequantize(packed, e8, k)
     xf = x.float().numpy()
     ref = ogv.gemv(deq, xf)
-    gemv_bound = U32 * (32 + k // 2048 + 40) * ogv.abs_gemv(deq, xf)
-    # the tiles' products are exact too; the matrix cores' float32 sums: u (K + 8) sum |w x|
-    bound = U32 * (k + 8) * ogv.abs_gemv(deq, xf) if _gemv_tiles("mxfp4", n, k, B) else gemv_bound
+    bound = _mx_gemv_bound(deq, xf, k, B)
     for ydt in (torch.float32, torch.bfloat16):
         _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ref, bound, ydt)
-        _gemv_check(gwb.gemv(q, x.to(DEV), out=_strided_out(B, n, ydt)), ref, gemv_bound, ydt)
+        _gemv_check(gwb.gemv(q, x.to(DEV), out=_strided_out(B, n, ydt)), ref, bound, ydt)
+
+
+@pytest.mark.parametrize("B,k", [(1, 1280), (3, 1280), (6, 1280), (8, 1280), (8, 2048), (1, 4096)])
+def test_gemv_mxfp4_scale_byte_255_rows(B, k):
+    """Scale byte 255 has no E8M0 value: the page's weights +-E2M1 * 2^128 are inf (NaN
+    for a zero code), so those rows' outputs are inf or NaN exactly where the float64
+    product is, with its sign; every other row keeps its bound. Blocks of all-zero
+    codes (0 * inf = NaN however the activations cancel) and of nonzero codes both.
+    K = 2048 at B = 8 takes the matrix-core kernel's whole-batch path; K = 4096 at B = 1
+    gives a lane two blocks of a row."""
+    n = 72
+    W = workloads.mxfp4_weight(n, k, seed=662)
+    x = workloads.normal_weight(B, k, std=1.0, seed=663)
+    q = gwb.quantize(W.to(DEV), "mxfp4")
+    for row, blk in ((5, 3), (33, 0), (71, 39), (40, 20)):
+        q["e8m0"][row, blk] = 255
+    q["packed"][33, 0:16] = 0                                  # block 0 of row 33: every code +0
+    q["packed"][40, 320:336] = 0x11                            # block 20 of row 40: every code +0.5
+    packed, e8 = _np(q["packed"]), _np(q["e8m0"])
+    deq = omx.dequantize(packed, e8, k)
+    xf = x.float().numpy()
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = ogv.gemv(deq, xf)
+    for out in (None, _strided_out(B, n, torch.float32)):
+        y = _np(gwb.gemv(q, x.to(DEV), out=out)).astype(np.float64)
+        bad = ~np.isfinite(ref)
+        assert bad[:, [5, 33, 71, 40]].all() and not bad[:, [0, 6, 34, 70]].any()
+        assert np.array_equal(np.isnan(y), np.isnan(ref))
+        assert np.array_equal(np.isposinf(y), np.isposinf(ref)) and np.array_equal(np.isneginf(y), np.isneginf(ref))
+        fin = np.isfinite(deq).all(axis=1)
+        bound = _mx_gemv_bound(deq[fin], xf, k, B)
+        _gemv_check(torch.from_numpy(y[:, fin]), ref[:, fin], bound, torch.float32)
 
 
 @pytest.mark.parametrize("nbits", [2, 3, 4, 5, 6, 7])
@@ -786,8 +823,8 @@ def test_full_fold_34816x5120_sampled():
                                    ("uintx", 8), ("gptq_sym_act", 1)])
 def test_full_gemv_lm_head_131072x2048_sampled(fmt, B):
     """The page's lm_head decode read, 131072 x 2048, in the launch shapes the benchmark
-    times (B = 1: the GEMV kernels; B = 8: the matrix-core tiles); checked on
-    sampled output rows (whole qzeros words) against the oracle."""
+    times (B = 1: the GEMV kernels; B = 8: the matrix-core GEMV (MXFP4) or tiles (GPTQ,
+    uintx)); checked on sampled output rows (whole qzeros words) against the oracle."""
     N_, K_ = 131072, 2048
     W = workloads.normal_weight(N_, K_, seed=520)
     x = workloads.normal_weight(B, K_, std=1.0, seed=521)
