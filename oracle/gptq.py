@@ -140,6 +140,25 @@ def quantize_act_order(w, group: int, sym: bool, perm):
     return q
 
 
+def group_order(qweight, g_idx, group: int):
+    """Act-order tensors rearranged into group order: the channels taken group by group,
+    ascending channel index within a group (a stable sort by g_idx), so that group g's
+    channels sit at positions g*G .. g*G + G - 1 and the index-order GPTQ layout (group
+    k // G) applies once the activations are gathered the same way: x @ dequant^T is
+    unchanged when column j of the rearranged weight meets x[perm[j]].
+    Returns (qweight [K/8, N] with nibble i of word (r, n) = code of channel perm[8r + i],
+    perm int32 [K] = the channel at each position). Every group must hold exactly G
+    channels (as quantize_act_order makes them)."""
+    codes = unpack_int32(qweight, 0)                                # [K, N]
+    k = codes.shape[0]
+    gi = np.asarray(g_idx, np.int64)
+    assert gi.shape == (k,) and k % group == 0
+    assert gi.min(initial=0) >= 0 and gi.max(initial=0) < k // group, "g_idx out of range"
+    assert np.all(np.bincount(gi, minlength=k // group) == group), "every group needs exactly G channels"
+    perm = np.argsort(gi, kind="stable")
+    return pack_int32(codes[perm], 0), perm.astype(np.int32)
+
+
 def _snr_page(wt, deq) -> float:
     """20 log10(||w|| / max(||w - deq||, 1e-12)) with float64 norms of float32 data."""
     num = np.sqrt(np.sum(wt.astype(np.float64) ** 2))

@@ -237,6 +237,45 @@ def test_dequant_g_idx_exact(sym):
     assert not np.array_equal(d, gq.dequantize(q["qweight"], q["scales"], q["qzeros"], 64, sym))
 
 
+@pytest.mark.parametrize("sym", [True, False])
+def test_group_order_bruteforce(sym):
+    """Group order by hand: positions taken group by group, channels ascending inside a
+    group; position j's codes are channel perm[j]'s, nibble j % 8 of word j // 8; the
+    index-order dequantization of the result is the act-order weight with its columns
+    in that order, so the GEMV of the gathered activations is unchanged."""
+    w = workloads.gptq_asym_weight(24, 256, seed=35).float().numpy()
+    perm_q = _perm(256, 36)
+    q = gq.quantize_act_order(w, 32, sym, perm_q)
+    qw, perm = gq.group_order(q["qweight"], q["g_idx"], 32)
+    want = [k for g in range(8) for k in range(256) if q["g_idx"][k] == g]
+    assert perm.dtype == np.int32 and perm.tolist() == want
+    for j in range(256):
+        for n in range(0, 24, 5):
+            assert (int(np.uint32(qw[j // 8, n]) >> np.uint32(4 * (j % 8))) & 15) == q["codes"][perm[j], n]
+    d_act = gq.dequantize(q["qweight"], q["scales"], q["qzeros"], 32, sym, g_idx=q["g_idx"])
+    d_grp = gq.dequantize(qw, q["scales"], q["qzeros"], 32, sym)          # index order: group j // G
+    assert np.array_equal(d_grp, d_act[:, perm])
+    x = np.random.default_rng(37).standard_normal((3, 256))
+    assert np.allclose(x @ d_act.T.astype(np.float64), x[:, perm] @ d_grp.T.astype(np.float64), rtol=1e-12, atol=1e-12)
+
+
+def test_group_order_identity_and_refusals():
+    """Index-order groups are already in group order; a group of the wrong size or a
+    group index past K/G is refused."""
+    w = workloads.gptq_asym_weight(8, 128, seed=38).float().numpy()
+    q = gq.quantize_sym(w, 32)
+    qw, perm = gq.group_order(q["qweight"], q["g_idx"], 32)
+    assert np.array_equal(qw, q["qweight"]) and np.array_equal(perm, np.arange(128))
+    bad = q["g_idx"].copy()
+    bad[0] = 1
+    with pytest.raises(AssertionError):
+        gq.group_order(q["qweight"], bad, 32)
+    bad = q["g_idx"].copy()
+    bad[5], bad[40] = 4, 0
+    with pytest.raises(AssertionError):
+        gq.group_order(q["qweight"], bad, 32)
+
+
 def _page_snr_weights():
     t = np.float32(float(PS["t_f32"]))
     assert float(t) == 1 + 2 ** -11 + 2 ** -20

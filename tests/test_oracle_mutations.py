@@ -176,3 +176,27 @@ def test_gptq_page_snr_per_column_caught(monkeypatch):
         return float(np.mean(20.0 * np.log10(num[live] / den[live])))
     monkeypatch.setattr(gq, "_snr_page", per_column)
     _fails(tg.test_page_in_function_snr_closed_form)
+
+
+def test_gptq_group_order_unstable_caught(monkeypatch):
+    """Group order with the channels of a group reversed (an unstable sort)."""
+    orig = gq.group_order
+    def reversed_within(qweight, g_idx, group):
+        qw, perm = orig(qweight, g_idx, group)
+        perm = perm.reshape(-1, group)[:, ::-1].reshape(-1).copy()
+        codes = gq.unpack_int32(qweight, 0)
+        return gq.pack_int32(codes[perm], 0), perm
+    monkeypatch.setattr(gq, "group_order", reversed_within)
+    _fails(tg.test_group_order_bruteforce, True)
+
+
+def test_gptq_group_order_inverse_perm_caught(monkeypatch):
+    """Group order that gathers the codes by the inverse permutation."""
+    orig = gq.group_order
+    def inverse(qweight, g_idx, group):
+        qw, perm = orig(qweight, g_idx, group)
+        inv = np.argsort(perm).astype(np.int32)
+        codes = gq.unpack_int32(qweight, 0)
+        return gq.pack_int32(codes[inv], 0), perm
+    monkeypatch.setattr(gq, "group_order", inverse)
+    _fails(tg.test_group_order_bruteforce, False)
