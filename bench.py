@@ -194,7 +194,7 @@ def measure_extras(gwb, workloads, Ws, deqs, ad, dev):
     value): the AWQ fold of the gate_up weight (columns * s) straight to MXFP4, the same
     fold also writing the folded bf16 weight, and the decode GEMV reading a packed
     131072 x 2048 lm_head (GPTQ sym g128, MXFP4, uintx4 g64, GPTQ sym g128 with act-order
-    groups in a seeded channel order) for one activation row, and
+    groups in a seeded channel order, as stored and in group order) for one activation row, and
     the uintx variants (float16 / float32 weights, groups 32 / 128) at [3072, 12288], and
     GPTQ with act-order groups on the gate_up weight. Launches cycle over copies of
     their inputs and outputs, so each starts cold."""
@@ -230,6 +230,8 @@ def measure_extras(gwb, workloads, Ws, deqs, ad, dev):
     qu = [gwb.quantize(head, "uintx", nbits=4) for _ in range(3)]
     hperm = torch.from_numpy(np.random.default_rng(526).permutation(HK).astype(np.int32)).to(dev)
     qa = [gwb.quantize(head, "gptq_sym_act", group=128, perm=hperm) for _ in range(3)]
+    qo = [gwb.group_order(q) for q in qa]                        # the same weights in group order
+    wso = torch.empty(gwb.gemv_workspace_bytes(qo[0], 1), dtype=torch.uint8, device=dev)
     del head
     wsu = torch.empty(gwb.gemv_workspace_bytes(qu[0], 1), dtype=torch.uint8, device=dev)
     wsg = torch.empty(gwb.gemv_workspace_bytes(qg[0], 1), dtype=torch.uint8, device=dev)
@@ -243,6 +245,8 @@ def measure_extras(gwb, workloads, Ws, deqs, ad, dev):
          cycle([gwb.prepare_gemv(q, xh, yh, wsu) for q in qu])),
         ("gemv.gptq_sym_act_g128.lm_head_b1", hk / 2 + hk / 128 * 2 + 4 * HK + 2 * HK + 4 * HN,
          cycle([gwb.prepare_gemv(q, xh, yh, None) for q in qa])),
+        ("gemv.gptq_sym_act_g128_grouped.lm_head_b1", hk / 2 + hk / 128 * 2 + 4 * HK + 2 * HK + 4 * HN,
+         cycle([gwb.prepare_gemv(q, xh, yh, wso) for q in qo])),
     ]
     # a decode batch of 8 rows (GPTQ and MXFP4 run on the GEMM tiles there)
     x8 = workloads.normal_weight(8, HK, std=1.0, seed=527).to(dev)

@@ -7,7 +7,9 @@ the library is missing, importing this package raises.
 
 Formats ("fmt"): "gptq_sym", "gptq_asym", "mxfp4", "uintx", "mxfp4_page_ties" (MXFP4 with the
 page code's own tie rule; same stored layout), "gptq_sym_act" / "gptq_asym_act" (GPTQ with
-act-order groups: quantize takes the channel order `perm`, g_idx names each channel's group).
+act-order groups: quantize takes the channel order `perm`, g_idx names each channel's group),
+"gptq_sym_grouped" / "gptq_asym_grouped" (the same weight in group order, made by group_order()
+for the decode GEMV; g_idx holds the channel permutation).
 """
 from __future__ import annotations
 
@@ -27,9 +29,9 @@ lib = ctypes.CDLL(LIB_PATH)
 
 OK, E_ARG, E_SHAPE, E_UNSUPPORTED, E_SIZE, E_HIP = 0, -1, -2, -3, -4, -5
 FORMATS = {"gptq_sym": 1, "gptq_asym": 2, "mxfp4": 3, "uintx": 4, "mxfp4_page_ties": 5,
-           "gptq_sym_act": 6, "gptq_asym_act": 7}
+           "gptq_sym_act": 6, "gptq_asym_act": 7, "gptq_sym_grouped": 8, "gptq_asym_grouped": 9}
 DEFAULT_GROUP = {"gptq_sym": 128, "gptq_asym": 128, "mxfp4": 32, "uintx": 64, "mxfp4_page_ties": 32,
-                 "gptq_sym_act": 128, "gptq_asym_act": 128}
+                 "gptq_sym_act": 128, "gptq_asym_act": 128, "gptq_sym_grouped": 128, "gptq_asym_grouped": 128}
 F32, BF16, F16 = 0, 1, 2
 _DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
 
@@ -63,6 +65,7 @@ _SIGS = {
     "gwb_quantize": [ctypes.POINTER(QSpec), _P, _I64, _I64, _I64, ctypes.POINTER(QTensors), _P, _SZ, _P],
     "gwb_quantize_act_order": [ctypes.POINTER(QSpec), _P, _I64, _I64, _I64, _P, ctypes.POINTER(QTensors), _P, _SZ,
                                _P],
+    "gwb_gptq_group_order": [ctypes.POINTER(QSpec), ctypes.POINTER(QTensors), _I64, _I64, _P, _P, _P, _P],
     "gwb_dequantize": [ctypes.POINTER(QSpec), ctypes.POINTER(QTensors), _I64, _I64, _P, _I32, _I64, _P, _SZ, _P],
     "gwb_snr": [ctypes.POINTER(QSpec), _P, _I64, _I64, _I64, ctypes.POINTER(QTensors), _P, _P, _SZ, _P],
     "gwb_quantize_snr": [ctypes.POINTER(QSpec), _P, _I64, _I64, _I64, ctypes.POINTER(QTensors), _P, _P, _SZ, _P],
@@ -204,6 +207,28 @@ def quantize(W: torch.Tensor, fmt: str, nbits: int = 4, group: Optional[int] = N
         _check(lib.gwb_quantize(ctypes.byref(sp), _ptr(W), N, K, ldw, ctypes.byref(qt), _ptr(workspace), ws_b,
                                 _stream()))
     return out
+
+
+def group_order(q: Quantized) -> Quantized:
+    """Act-order GPTQ into group order for the decode GEMV (gwb_gptq_group_order): a new
+    Quantized of format gptq_{sym,asym}_grouped sharing q's scales and qzeros, with the
+    rearranged qweight and the permutation in g_idx. Synchronizes to read the kernels'
+    status; raises GwbError (E_SHAPE) when a group does not hold exactly G channels or a
+    g_idx entry lies outside [0, K/G)."""
+    if not q.fmt.endswith("_act"):
+        raise ValueError("group_order takes act-order GPTQ (gptq_sym_act / gptq_asym_act)")
+    dev = q.codes.device
+    codes, perm = _alloc(q.sizes["codes"], dev), _alloc(q.sizes["g_idx"], dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    sp, qt = q.spec(), q.qtensors()
+    _check(lib.gwb_gptq_group_order(ctypes.byref(sp), ctypes.byref(qt), q.N, q.K, _ptr(codes), _ptr(perm),
+                                    _ptr(status), _stream()))
+    st = int(status.item())
+    if st:
+        raise GwbError(E_SHAPE, "g_idx: a group without exactly G channels" if st == 1 else
+                       "g_idx: an entry outside [0, K/G)")
+    return Quantized(q.fmt.replace("_act", "_grouped"), q.nbits, q.group, q.w_dtype, q.N, q.K, codes, q.scales,
+                     q.zeros, perm, q.sizes)
 
 
 def dequantize(q: Quantized, out_dtype=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:

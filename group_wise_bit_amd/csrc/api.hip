@@ -47,7 +47,15 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool is_mxfp4(int32_t f) { return f == GWB_MXFP4 || f == GWB_MXFP4_PAGE_TIES; }
 // act-order GPTQ shares GPTQ's stored layout; its groups come from g_idx
 bool is_act(int32_t f) { return f == GWB_GPTQ_SYM_ACT || f == GWB_GPTQ_ASYM_ACT; }
-bool is_gptq_sym(int32_t f) { return f == GWB_GPTQ_SYM || f == GWB_GPTQ_SYM_ACT; }
+// act-order GPTQ in group order (gwb_gptq_group_order): GPTQ's index-order layout, whose
+// column j is channel g_idx[j] (there the channel permutation) of the layer
+bool is_grouped(int32_t f) { return f == GWB_GPTQ_SYM_GROUPED || f == GWB_GPTQ_ASYM_GROUPED; }
+bool is_gptq_sym(int32_t f) { return f == GWB_GPTQ_SYM || f == GWB_GPTQ_SYM_ACT || f == GWB_GPTQ_SYM_GROUPED; }
+int refuse_grouped(const gwb_qspec* sp) {
+  return is_grouped(sp->format)
+             ? fail(GWB_E_UNSUPPORTED, "group-ordered GPTQ is made by gwb_gptq_group_order and read by gwb_gemv")
+             : GWB_OK;
+}
 
 size_t elem_size(int32_t dt) { return dt == GWB_F32 ? 4 : 2; }
 
@@ -65,6 +73,8 @@ int check_spec(const gwb_qspec* sp, int64_t N, int64_t K) {
     case GWB_GPTQ_ASYM:
     case GWB_GPTQ_SYM_ACT:
     case GWB_GPTQ_ASYM_ACT:
+    case GWB_GPTQ_SYM_GROUPED:
+    case GWB_GPTQ_ASYM_GROUPED:
       if (sp->nbits != 4) return fail(GWB_E_ARG, "GPTQ is 4-bit, got nbits=%d", sp->nbits);
       if (sp->group <= 0) return fail(GWB_E_ARG, "group must be positive, got %d", sp->group);
       if (sp->group != 32 && sp->group != 64 && sp->group != 128)
@@ -126,6 +136,8 @@ gwb_sizes sizes_of(const gwb_qspec* sp, int64_t N, int64_t K) {
     case GWB_GPTQ_ASYM:
     case GWB_GPTQ_SYM_ACT:
     case GWB_GPTQ_ASYM_ACT:
+    case GWB_GPTQ_SYM_GROUPED:
+    case GWB_GPTQ_ASYM_GROUPED:
       s.codes = (size_t)(K / 8 * N * 4);
       s.scales = (size_t)(K / G * N * 2);
       s.zeros = (size_t)(K / G * (N / 8) * 4);
@@ -143,7 +155,7 @@ gwb_sizes sizes_of(const gwb_qspec* sp, int64_t N, int64_t K) {
       break;
   }
   size_t ws = 0;
-  if (N > 0 && K > 0) {
+  if (N > 0 && K > 0 && !is_grouped(sp->format)) {
     ws = (size_t)err_blocks(sp, N, K) * 2 * sizeof(double);
     if (sp->format == GWB_UINTX) {
       size_t c = gwb::uintx_code_workspace(sp->w_dtype, sp->group, N, K);
@@ -171,8 +183,9 @@ int check_tensors(const gwb_qspec* sp, const gwb_qtensors* q) {
   if (!q->codes || !q->scales) return fail(GWB_E_ARG, "codes and scales are required");
   if (!is_mxfp4(sp->format) && !q->zeros) return fail(GWB_E_ARG, "zeros is required for this format");
   if (is_act(sp->format) && !q->g_idx) return fail(GWB_E_ARG, "act-order GPTQ needs g_idx");
+  if (is_grouped(sp->format) && !q->g_idx) return fail(GWB_E_ARG, "group-ordered GPTQ needs its permutation in g_idx");
   if (!aligned16(q->codes) || !aligned16(q->scales) || (q->zeros && !aligned16(q->zeros)) ||
-      (is_act(sp->format) && !aligned16(q->g_idx)))
+      ((is_act(sp->format) || is_grouped(sp->format)) && !aligned16(q->g_idx)))
     return fail(GWB_E_UNSUPPORTED, "quantized tensors must be 16-byte aligned");
   return GWB_OK;
 }
@@ -195,6 +208,7 @@ int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int
   if (int rc = check_spec(spec, N, K)) return rc;
   if (is_act(spec->format))
     return fail(GWB_E_ARG, "act-order GPTQ takes the channel order: use gwb_quantize_act_order");
+  if (int rc = refuse_grouped(spec)) return rc;
   if (N == 0 || K == 0) return ok();          // empty: valid, nothing to enqueue
   if (int rc = check_weight(spec, W, K, ldw)) return rc;
   if (int rc = check_tensors(spec, out)) return rc;
@@ -230,6 +244,7 @@ int gwb_quantize_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K,
                      const gwb_qtensors* out, double* d_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (int rc = check_spec(spec, N, K)) return rc;
   if (is_act(spec->format)) return fail(GWB_E_ARG, "act-order GPTQ quantizes with gwb_quantize_act_order");
+  if (int rc = refuse_grouped(spec)) return rc;
   if (!d_out) return fail(GWB_E_ARG, "d_out is NULL");
   if (N == 0 || K == 0) return fail(GWB_E_SHAPE, "SNR of an empty matrix is undefined");
   if (int rc = check_weight(spec, W, K, ldw)) return rc;
@@ -273,6 +288,7 @@ int gwb_dequantize(const gwb_qspec* spec, const gwb_qtensors* in, int64_t N, int
   (void)workspace;
   (void)workspace_bytes;
   if (int rc = check_spec(spec, N, K)) return rc;
+  if (int rc = refuse_grouped(spec)) return rc;
   if (out_dtype != GWB_F32 && out_dtype != GWB_BF16 && out_dtype != GWB_F16)
     return fail(GWB_E_ARG, "unknown out_dtype %d", out_dtype);
   // UINTX values are of the weight dtype (float32 holds them exactly); the other
@@ -311,6 +327,7 @@ int gwb_dequantize(const gwb_qspec* spec, const gwb_qtensors* in, int64_t N, int
 int gwb_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw, const gwb_qtensors* in,
             double* d_out, void* workspace, size_t workspace_bytes, void* stream) {
   if (int rc = check_spec(spec, N, K)) return rc;
+  if (int rc = refuse_grouped(spec)) return rc;
   if (int rc = check_weight(spec, W, K, ldw)) return rc;
   if (int rc = check_tensors(spec, in)) return rc;
   if (!d_out) return fail(GWB_E_ARG, "d_out is NULL");
@@ -362,6 +379,21 @@ int gwb_quantize_act_order(const gwb_qspec* spec, const void* W, int64_t N, int6
   gwb::launch_gptq_act_quant(is_gptq_sym(spec->format), spec->group, W, spec->w_dtype, N, K, ldw, perm, out->codes,
                              out->scales, out->zeros, (int32_t*)out->g_idx, workspace, (hipStream_t)stream);
   return hip_check("act-order quantize launch");
+}
+
+int gwb_gptq_group_order(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K, void* codes_out,
+                         int32_t* perm_out, int32_t* d_status, void* stream) {
+  if (int rc = check_spec(spec, N, K)) return rc;
+  if (!is_act(spec->format)) return fail(GWB_E_ARG, "format must be GWB_GPTQ_SYM_ACT or GWB_GPTQ_ASYM_ACT");
+  if (!w || !w->codes || !w->g_idx) return fail(GWB_E_ARG, "the act-order codes and g_idx are required");
+  if (!codes_out || !perm_out || !d_status) return fail(GWB_E_ARG, "codes_out, perm_out and d_status are required");
+  if (!aligned16(w->codes) || !aligned16(w->g_idx) || !aligned16(codes_out) || !aligned16(perm_out))
+    return fail(GWB_E_UNSUPPORTED, "tensors must be 16-byte aligned");
+  if (codes_out == w->codes) return fail(GWB_E_ARG, "codes_out must not be the input codes");
+  if (N == 0 || K == 0) return ok();          // empty: valid, nothing to enqueue
+  gwb::launch_gptq_group_order(spec->group, w->codes, (const int32_t*)w->g_idx, N, K, codes_out, perm_out, d_status,
+                               (hipStream_t)stream);
+  return hip_check("group order launch");
 }
 
 static int awq_rows(int64_t N, int64_t max_rows, int64_t* rows, int64_t* step) {
@@ -462,7 +494,20 @@ static size_t gemv_kernel_workspace(const gwb_qspec* sp, int64_t N, int64_t K, i
 
 // Enough for either path: the tile path is taken only when the buffers' alignment
 // allows it, which the size query cannot know.
+// The index-order GPTQ spec that group-ordered GPTQ is read as once its activations are
+// gathered, and the workspace bytes of those gathered activations (bf16 [B, K]).
+static gwb_qspec index_twin(const gwb_qspec* sp) {
+  gwb_qspec t = *sp;
+  t.format = sp->format == GWB_GPTQ_SYM_GROUPED ? GWB_GPTQ_SYM : GWB_GPTQ_ASYM;
+  return t;
+}
+static size_t gathered_x_bytes(int64_t B, int64_t K) { return ((size_t)(B * K * 2) + 255) / 256 * 256; }
+
 static size_t gemv_workspace(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
+  if (is_grouped(sp->format)) {
+    const gwb_qspec t = index_twin(sp);
+    return gathered_x_bytes(B, K) + gemv_workspace(&t, N, K, B);
+  }
   const size_t a = gemv_kernel_workspace(sp, N, K, B);
   if (gemv_uintx_via_tiles(sp, N, K, B)) {
     const size_t b = gwb::uintx_gemm_workspace_bytes(B, N, K);
@@ -489,22 +534,9 @@ int gwb_gemv_workspace(const gwb_qspec* spec, int64_t N, int64_t K, int64_t B, s
   return ok();
 }
 
-int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K, const void* x, int64_t B,
-             int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
-             void* stream) {
-  if (int rc = check_gemv(spec, N, K, B)) return rc;
-  if (y_dtype != GWB_F32 && y_dtype != GWB_BF16) return fail(GWB_E_ARG, "unknown y_dtype %d", y_dtype);
-  if (N == 0) return ok();
-  if (!x || !y) return fail(GWB_E_ARG, "x and y are required");
-  if (ldx < K || ldy < N) return fail(GWB_E_ARG, "ldx must be >= K and ldy >= N");
-  if (!aligned16(x) || ldx % 8) return fail(GWB_E_UNSUPPORTED, "x and its row stride must be 16-byte aligned");
-  if (K == 0) return fail(GWB_E_SHAPE, "K must be positive");
-  if (int rc = check_tensors(spec, w)) return rc;
-  const size_t need = gemv_workspace(spec, N, K, B);
-  if (need && (!workspace || workspace_bytes < need))
-    return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
-  if (need && !aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
-  hipStream_t st = (hipStream_t)stream;
+// gwb_gemv's kernels for validated arguments (x 16-byte aligned, workspace as needed).
+static int gemv_dispatch(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K, const void* x, int64_t B,
+                         int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, hipStream_t st) {
   const bool tiles = gemv_shape_via_gemm(spec, N, K, B) && aligned16(y) && ldy % 8 == 0 && B * ldx < kMaxElems &&
                      aligned16(w->codes) && aligned16(w->scales);
   if (gemv_uintx_via_tiles(spec, N, K, B) && aligned16(w->codes))
@@ -527,6 +559,32 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
     gwb::launch_gptq_gemv(spec->format == GWB_GPTQ_SYM, spec->group, (int)B, w->codes, w->scales, w->zeros, N, K, x,
                           ldx, y, y_dtype, ldy, (float*)workspace, st);
   return hip_check("gemv launch");
+}
+
+int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K, const void* x, int64_t B,
+             int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  if (int rc = check_gemv(spec, N, K, B)) return rc;
+  if (y_dtype != GWB_F32 && y_dtype != GWB_BF16) return fail(GWB_E_ARG, "unknown y_dtype %d", y_dtype);
+  if (N == 0) return ok();
+  if (!x || !y) return fail(GWB_E_ARG, "x and y are required");
+  if (ldx < K || ldy < N) return fail(GWB_E_ARG, "ldx must be >= K and ldy >= N");
+  if (!aligned16(x) || ldx % 8) return fail(GWB_E_UNSUPPORTED, "x and its row stride must be 16-byte aligned");
+  if (K == 0) return fail(GWB_E_SHAPE, "K must be positive");
+  if (int rc = check_tensors(spec, w)) return rc;
+  const size_t need = gemv_workspace(spec, N, K, B);
+  if (need && (!workspace || workspace_bytes < need))
+    return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (need && !aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  if (is_grouped(spec->format)) {
+    // group order: the activations gathered by the permutation, then index-order GPTQ
+    gwb::launch_gather_columns(x, ldx, B, K, (const int32_t*)w->g_idx, workspace, st);
+    const gwb_qspec t = index_twin(spec);
+    return gemv_dispatch(&t, w, N, K, workspace, B, K, y, y_dtype, ldy,
+                         (char*)workspace + gathered_x_bytes(B, K), st);
+  }
+  return gemv_dispatch(spec, w, N, K, x, B, ldx, y, y_dtype, ldy, workspace, st);
 }
 
 static int check_gemm(const gwb_qspec* sp, int64_t N, int64_t K, int64_t M) {

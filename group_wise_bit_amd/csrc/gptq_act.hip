@@ -417,4 +417,78 @@ void launch_gptq_act_err(bool sym, int group, const void* W, int32_t w_dtype, in
   }
 }
 
+// ------------------------------------------------------------- group order
+// Act-order tensors rearranged for the decode GEMV, once per weight: the channels taken
+// group by group, ascending inside a group, so group g's channels sit at positions
+// g*G .. g*G + G - 1 and the index-order GPTQ kernels apply to the gathered activations.
+// perm: thread g scans g_idx in channel order and places its group's channels; a group
+// of another size, or a group index outside [0, K/G), sets the status word (1: a group
+// does not hold exactly G channels, 2: g_idx out of range; 0: none).
+__global__ __launch_bounds__(256) void gptq_group_perm_kernel(const int32_t* __restrict__ g_idx, int K, int G, int NG,
+                                                              int32_t* __restrict__ perm, int32_t* __restrict__ status) {
+  const int g = threadIdx.x;
+  int sizes_bad = 0, range_bad = 0;
+  if (g < NG) {
+    int cnt = 0;
+    for (int k = 0; k < K; ++k) {
+      if (g_idx[k] == g) {
+        if (cnt < G) perm[g * G + cnt] = k;
+        ++cnt;
+      }
+    }
+    sizes_bad = cnt != G;
+  }
+  for (int k = threadIdx.x; k < K; k += 256) {
+    const int gk = g_idx[k];
+    range_bad |= gk < 0 || gk >= NG;
+  }
+  const int rb = __syncthreads_or(range_bad), sb = __syncthreads_or(sizes_bad);
+  if (threadIdx.x == 0) *status = rb ? 2 : (sb ? 1 : 0);
+}
+
+// Word (r, n) of the rearranged qweight: nibble i = code of channel perm[8r + i]. perm
+// entries are clamped into [0, K): a refused g_idx leaves unwritten slots, whose reads
+// stay in bounds (the status word reports the refusal).
+__global__ __launch_bounds__(256) void gptq_group_repack_kernel(const uint32_t* __restrict__ qweight, int N, int K,
+                                                                const int32_t* __restrict__ perm,
+                                                                uint32_t* __restrict__ out) {
+  const int n = blockIdx.x * 256 + threadIdx.x, r = blockIdx.y;
+  if (n >= N) return;
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k = min(max(perm[8 * r + i], 0), K - 1);
+    const uint32_t src = qweight[(int64_t)(k >> 3) * N + n];
+    w |= ((src >> (4 * (k & 7))) & 0xFu) << (4 * i);
+  }
+  out[(int64_t)r * N + n] = w;
+}
+
+void launch_gptq_group_order(int group, const void* qweight, const int32_t* g_idx, int64_t N, int64_t K,
+                             void* qweight_out, int32_t* perm, int32_t* status, hipStream_t st) {
+  const int NG = (int)(K / group);                               // <= kActMaxGroups: one thread per group
+  hipLaunchKernelGGL(gptq_group_perm_kernel, dim3(1), dim3(256), 0, st, g_idx, (int)K, group, NG, perm, status);
+  hipLaunchKernelGGL(gptq_group_repack_kernel, dim3((unsigned)((N + 255) / 256), (unsigned)(K / 8)), dim3(256), 0, st,
+                     (const uint32_t*)qweight, (int)N, (int)K, perm, (uint32_t*)qweight_out);
+}
+
+// The activations gathered into group order: xo[b][j] = x[b][perm[j]] (perm clamped into
+// [0, K)), rows of K contiguous.
+__global__ __launch_bounds__(256) void gather_columns_kernel(const uint16_t* __restrict__ x, int64_t ldx, int B, int K,
+                                                             const int32_t* __restrict__ perm,
+                                                             uint16_t* __restrict__ xo) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)B * K) return;
+  const int b = (int)(e / K), j = (int)(e - (int64_t)b * K);
+  const int k = min(max(perm[j], 0), K - 1);
+  xo[e] = x[(int64_t)b * ldx + k];
+}
+
+void launch_gather_columns(const void* x, int64_t ldx, int64_t B, int64_t K, const int32_t* perm, void* xo,
+                           hipStream_t st) {
+  const int64_t total = B * K;
+  hipLaunchKernelGGL(gather_columns_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     (const uint16_t*)x, ldx, (int)B, (int)K, perm, (uint16_t*)xo);
+}
+
 }  // namespace gwb

@@ -75,6 +75,13 @@ unsigned gptq_act_err_blocks(int64_t N, int64_t K);
 void launch_gptq_act_err(bool sym, int group, const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t ldw,
                          const void* qweight, const void* scales, const void* qzeros, const int32_t* g_idx,
                          double* part, hipStream_t st);
+// act-order tensors into group order (perm: the channel at each position; status 0 ok,
+// 1 a group without exactly G channels, 2 g_idx out of range), and the activation gather
+// that the GEMV on group-ordered tensors starts with
+void launch_gptq_group_order(int group, const void* qweight, const int32_t* g_idx, int64_t N, int64_t K,
+                             void* qweight_out, int32_t* perm, int32_t* status, hipStream_t st);
+void launch_gather_columns(const void* x, int64_t ldx, int64_t B, int64_t K, const int32_t* perm, void* xo,
+                           hipStream_t st);
 
 // ---- UINTX: tiled kernels (uintx_tiled.hpp) when N*K % (8 group) == 0, instantiated
 // for bf16 group 64 in uintx.hip and for the other (dtype, group) pairs in uintx_bf16.hip,

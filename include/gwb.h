@@ -23,6 +23,11 @@
  *                  stays in channel order and g_idx[k] names channel k's group. Per-group
  *                  formulas as GWB_GPTQ_SYM / _ASYM; stored layout as GPTQ plus g_idx,
  *                  which gwb_quantize_act_order writes and dequantization and SNR read.
+ *   GWB_GPTQ_SYM_GROUPED / GWB_GPTQ_ASYM_GROUPED  the same weight in group order, for the
+ *                  decode GEMV (gwb_gptq_group_order makes it once): the channels taken
+ *                  group by group, ascending inside a group, so group g sits at positions
+ *                  g*G .. g*G + G - 1 and GPTQ's index-order layout applies; g_idx holds the
+ *                  permutation (the channel at each position). Read by gwb_gemv only.
  *
  * Conventions for every entry point:
  *   - Pointers named d_* and every tensor pointer are DEVICE pointers owned by the
@@ -55,7 +60,7 @@ typedef enum {
 
 typedef enum {
   GWB_GPTQ_SYM = 1, GWB_GPTQ_ASYM = 2, GWB_MXFP4 = 3, GWB_UINTX = 4, GWB_MXFP4_PAGE_TIES = 5,
-  GWB_GPTQ_SYM_ACT = 6, GWB_GPTQ_ASYM_ACT = 7
+  GWB_GPTQ_SYM_ACT = 6, GWB_GPTQ_ASYM_ACT = 7, GWB_GPTQ_SYM_GROUPED = 8, GWB_GPTQ_ASYM_GROUPED = 9
 } gwb_format;
 typedef enum { GWB_F32 = 0, GWB_BF16 = 1, GWB_F16 = 2 } gwb_dtype;
 
@@ -86,7 +91,8 @@ typedef struct {
  *                 column 8q+i; symmetric: every nibble 7; asymmetric: zp itself
  *          g_idx  int32 [K] = k / G; optional on output (NULL skips), unused on input;
  *                 act-order GPTQ: the group of channel k, required (input to
- *                 dequantization and SNR, output of gwb_quantize_act_order)
+ *                 dequantization and SNR, output of gwb_quantize_act_order);
+ *                 group-ordered GPTQ: perm, the channel at position k (required)
  *   MXFP4  codes  uint8 [N, K/2]: byte = code(2i) | code(2i+1) << 4, code = e2m1
  *                 magnitude index | sign << 3
  *          scales uint8 e8m0 [N, K/32] = exponent + 127;  zeros, g_idx unused (NULL)
@@ -147,6 +153,25 @@ int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int
 int gwb_quantize_act_order(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
                            const int32_t* perm, const gwb_qtensors* out, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* Act-order GPTQ into group order, once per weight, for the decode GEMV (GPTQ runtimes
+ * reorder act-order weights at load time for the same reason): page export_gptq_cpu.py's
+ * g_idx names each channel's group, so taking the channels group by group (ascending
+ * inside a group) puts group g at positions g*G .. g*G + G - 1, where the index-order
+ * GPTQ kernels read it with the activations gathered the same way.
+ *   spec      GWB_GPTQ_SYM_ACT or GWB_GPTQ_ASYM_ACT (group 32, 64, 128; K/G <= 256)
+ *   w         act-order tensors: codes (qweight [K/8, N], channel order) and g_idx [K]
+ *             are read; scales and zeros are not touched (they stay valid as they are)
+ *   codes_out int32 [K/8, N]: nibble i of word (r, n) = code of channel perm[8r + i]
+ *   perm_out  int32 [K]: the channel at each position
+ *   d_status  one device int32, written by the kernels: 0, or 1 when a group does not hold
+ *             exactly G channels, 2 when a g_idx entry lies outside [0, K/G); on 1 or 2
+ *             codes_out and perm_out are unspecified (every access stayed in bounds)
+ * With spec->format changed to GWB_GPTQ_SYM_GROUPED / _ASYM_GROUPED, {codes_out, scales,
+ * zeros, perm_out} is a valid gwb_qtensors for gwb_gemv. codes_out must not alias
+ * w->codes. Empty shapes enqueue nothing (d_status is not written). */
+int gwb_gptq_group_order(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K, void* codes_out,
+                         int32_t* perm_out, int32_t* d_status, void* stream);
 
 /* Unpack and dequantize into out [N, K] (row stride ldo >= K) of out_dtype, in the
  * weight's own [N, K] layout for every format (the GPTQ transpose is undone).
@@ -245,18 +270,23 @@ int gwb_fold_mxfp4(const void* W, int32_t w_dtype, int64_t N, int64_t K, int64_t
  *            uintx (page uintx_quant.py, forward: x times the dequantized weight of the
  *            weight dtype, r((q - zp) * s), converted to bf16 when it is not bf16) needs
  *            N % 8 == 0 and K % 512 == 0 (else GWB_E_UNSUPPORTED); act-order GPTQ reads
- *            w->g_idx (required)
+ *            w->g_idx (required); group-ordered GPTQ (gwb_gptq_group_order) reads its
+ *            permutation in w->g_idx and runs as index-order GPTQ on the activations
+ *            gathered into the workspace
  *   x        device bf16 [B, K], row stride ldx (multiple of 8), 16-byte aligned; 1 <= B <= 8
  *   y        device [B, N] of y_dtype (GWB_F32 or GWB_BF16, RNE), row stride ldy
  *   workspace at least gwb_gemv_workspace bytes (K-split partial sums of either path,
- *            the tile path's group sums; none for MXFP4 below 5 rows)
- * Paths: GPTQ with groups in index order at B >= 2 and MXFP4 at B >= 5 run gwb_gemm's
+ *            the tile path's group sums, group order's gathered activations; none for
+ *            MXFP4 below 5 rows of K <= 8192)
+ * Paths: GPTQ with groups in index order (or group order) at B >= 2 runs gwb_gemm's
  * matrix-core tiles (and its numerics) when N % 8 == 0, K % 128 == 0, y and its rows
  * are 16-byte aligned (ldy % 8 == 0) and codes and scales are 16-byte aligned, as does
  * bf16-weight uintx at B >= 5 on weights of N >= 65536 rows (16-byte aligned codes);
- * every other call runs the GEMV kernels: products of dequantized values and activations
- * exact in float32, float32 sums in a fixed order. Both are deterministic for a given
- * shape and path; the error is bounded by the float32 accumulation.                */
+ * MXFP4 at B >= 5 runs the GEMV's own matrix-core kernel (v_mfma_f32_16x16x32_bf16,
+ * exact bf16 weights, the matrix cores' float32 sums); every other call runs the GEMV
+ * kernels: products of dequantized values and activations exact in float32, float32
+ * sums in a fixed order. All are deterministic for a given shape and path; the error is
+ * bounded by the float32 accumulation.                                             */
 int gwb_gemv_workspace(const gwb_qspec* spec, int64_t N, int64_t K, int64_t B, size_t* bytes);
 int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K, const void* x, int64_t B,
              int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes,

@@ -100,7 +100,8 @@ def test_query_rejects(fmt, N, K, nbits, group, dt, code):
 
 def test_unknown_format_and_dtype():
     s = gwb.Sizes()
-    assert lib.gwb_query_sizes(ctypes.byref(gwb.QSpec(9, 4, 32, 1)), 8, 64, ctypes.byref(s)) == gwb.E_ARG
+    assert lib.gwb_query_sizes(ctypes.byref(gwb.QSpec(10, 4, 32, 1)), 8, 64, ctypes.byref(s)) == gwb.E_ARG
+    assert lib.gwb_query_sizes(ctypes.byref(gwb.QSpec(0, 4, 32, 1)), 8, 64, ctypes.byref(s)) == gwb.E_ARG
     assert lib.gwb_query_sizes(ctypes.byref(gwb.QSpec(3, 4, 32, 7)), 8, 64, ctypes.byref(s)) == gwb.E_ARG
     assert lib.gwb_query_sizes(None, 8, 64, ctypes.byref(s)) == gwb.E_ARG
 
@@ -399,6 +400,52 @@ def test_act_order_gptq_validates():
     assert lib.gwb_gemv_workspace(ctypes.byref(sp), 8, 256, 1, ctypes.byref(b)) == gwb.OK and b.value == 0
     assert lib.gwb_gemv_workspace(ctypes.byref(sp), 64, 2048, 2, ctypes.byref(b)) == gwb.OK
     assert b.value == 4 * 2 * 64 * 4                                # one column tile: a split per 512 k
+
+
+def test_group_order_validates():
+    """gwb_gptq_group_order takes act-order tensors and validates before enqueueing; the
+    group-ordered formats have GPTQ's sizes, are refused by every entry point but
+    gwb_gemv, and need their permutation there."""
+    fake = 1 << 20
+    P = ctypes.c_void_p
+    rc, s = _sizes("gptq_sym_grouped", 256, 1024, group=32)
+    rc2, s2 = _sizes("gptq_sym", 256, 1024, group=32)
+    assert rc == 0 and (s.codes, s.scales, s.zeros, s.g_idx, s.workspace) == (s2.codes, s2.scales, s2.zeros, s2.g_idx, 0)
+    act = gwb.make_spec("gptq_sym_act", 4, 128, gwb.BF16)
+    qt = gwb.QTensors(fake, fake, fake, fake)
+    def go(spec=act, q=qt, out=fake + 4096, perm=fake + 8192, status=fake + 16384, N=64, K=256):
+        return lib.gwb_gptq_group_order(ctypes.byref(spec), None if q is None else ctypes.byref(q), N, K, P(out),
+                                        P(perm), P(status), None)
+    assert go(spec=gwb.make_spec("gptq_sym", 4, 128, gwb.BF16)) == gwb.E_ARG
+    assert go(q=None) == gwb.E_ARG
+    assert go(q=gwb.QTensors(fake, fake, fake, None)) == gwb.E_ARG      # g_idx is the input
+    assert go(out=None) == gwb.E_ARG and go(perm=None) == gwb.E_ARG and go(status=None) == gwb.E_ARG
+    assert go(out=fake) == gwb.E_ARG                                    # no in-place rearrangement
+    assert go(out=fake + 4100) == gwb.E_UNSUPPORTED
+    assert go(K=200) == gwb.E_SHAPE
+    assert go(N=0) == gwb.OK and go(K=0) == gwb.OK                      # empty: nothing enqueued
+    grp = gwb.make_spec("gptq_asym_grouped", 4, 128, gwb.BF16)
+    qn = gwb.QTensors(fake, fake, fake, None)
+    assert lib.gwb_quantize(ctypes.byref(grp), fake, 8, 256, 256, ctypes.byref(qt), fake, 1 << 30, None) \
+        == gwb.E_UNSUPPORTED
+    assert lib.gwb_dequantize(ctypes.byref(grp), ctypes.byref(qt), 8, 256, P(fake), gwb.F32, 256, None, 0, None) \
+        == gwb.E_UNSUPPORTED
+    assert lib.gwb_snr(ctypes.byref(grp), P(fake), 8, 256, 256, ctypes.byref(qt), P(fake), P(fake), 1 << 20,
+                       None) == gwb.E_UNSUPPORTED
+    assert lib.gwb_quantize_snr(ctypes.byref(grp), P(fake), 8, 256, 256, ctypes.byref(qt), P(fake), P(fake),
+                                1 << 20, None) == gwb.E_UNSUPPORTED
+    b = ctypes.c_size_t()
+    # the GEMV: gathered activations (256-byte aligned) before index-order GPTQ's own needs
+    assert lib.gwb_gemv_workspace(ctypes.byref(grp), 131072, 2048, 1, ctypes.byref(b)) == gwb.OK
+    assert b.value == 2048 * 2
+    assert lib.gwb_gemv_workspace(ctypes.byref(grp), 64, 2048, 3, ctypes.byref(b)) == gwb.OK
+    twin = ctypes.c_size_t()
+    assert lib.gwb_gemv_workspace(ctypes.byref(gwb.make_spec("gptq_asym", 4, 128, gwb.BF16)), 64, 2048, 3,
+                                  ctypes.byref(twin)) == gwb.OK
+    assert b.value == (3 * 2048 * 2 + 255) // 256 * 256 + twin.value
+    y = P(fake + (1 << 16))
+    assert lib.gwb_gemv(ctypes.byref(grp), ctypes.byref(qn), 64, 2048, P(fake), 1, 2048, y, gwb.F32, 64, P(fake),
+                        1 << 20, None) == gwb.E_ARG                     # the permutation is required
 
 
 def test_static_quantize_snr_rejects_beyond_its_scratch():

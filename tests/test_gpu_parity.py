@@ -648,6 +648,77 @@ def test_gemv_gptq_act_order_parity(sym, group, n, k, B):
         assert np.array_equal(y[b], deq[:, kk]), (b, kk)
 
 
+@pytest.mark.parametrize("sym", [True, False])
+@pytest.mark.parametrize("group,n,k", [(128, 64, 512), (32, 136, 1024), (64, 264, 4096), (128, 4096, 2048)])
+def test_group_order_parity(sym, group, n, k):
+    """gwb_gptq_group_order against the oracle: the rearranged qweight bit for bit and the
+    permutation (page export_gptq_cpu.py's g_idx taken group by group); scales and
+    qzeros are shared, untouched."""
+    W = workloads.mxfp4_weight(n, k, seed=560 + n + group)
+    perm_q = np.random.default_rng(561 + k).permutation(k)
+    q = gwb.quantize(W.to(DEV), "gptq_sym_act" if sym else "gptq_asym_act", group=group,
+                     perm=torch.from_numpy(perm_q.astype(np.int32)).to(DEV))
+    o = ogq.quantize_act_order(W.float().numpy(), group, sym, perm_q)
+    qw_ref, perm_ref = ogq.group_order(o["qweight"], o["g_idx"], group)
+    qg = gwb.group_order(q)
+    assert qg.fmt == ("gptq_sym_grouped" if sym else "gptq_asym_grouped")
+    assert np.array_equal(_np(qg["g_idx"]), perm_ref)
+    assert np.array_equal(_np(qg["qweight"]).view(np.uint32), qw_ref.view(np.uint32))
+    assert qg.scales.data_ptr() == q.scales.data_ptr() and qg.zeros.data_ptr() == q.zeros.data_ptr()
+
+
+@pytest.mark.parametrize("sym", [True, False])
+@pytest.mark.parametrize("group,n,k,B", [(128, 64, 512, 1), (32, 136, 1024, 3), (64, 1024, 4096, 8),
+                                          (128, 4096, 2048, 1), (128, 4096, 2048, 2), (32, 72, 4096, 2)])
+def test_gemv_group_order_parity(sym, group, n, k, B):
+    """GEMV on group-ordered act-order weights: the activations gathered by the
+    permutation, then index-order GPTQ (the GEMV kernels at one row or with unaligned y
+    rows, the GEMM tiles otherwise) against the oracle's act-order product, within that
+    path's bound for the rearranged tensors; one-hot activations read channels exactly."""
+    W = workloads.mxfp4_weight(n, k, seed=562 + n + group)
+    x = workloads.normal_weight(B, k, std=1.0, seed=563 + B)
+    perm_q = np.random.default_rng(564 + k).permutation(k)
+    q = gwb.quantize(W.to(DEV), "gptq_sym_act" if sym else "gptq_asym_act", group=group,
+                     perm=torch.from_numpy(perm_q.astype(np.int32)).to(DEV))
+    qg = gwb.group_order(q)
+    o = ogq.quantize_act_order(W.float().numpy(), group, sym, perm_q)
+    deq = ogq.dequantize(o["qweight"], o["scales"], o["qzeros"], group, sym, g_idx=o["g_idx"])
+    qw_g, perm = ogq.group_order(o["qweight"], o["g_idx"], group)
+    og = dict(o, qweight=qw_g, codes=ogq.unpack_int32(qw_g, 0))   # index-order view of the rearranged weight
+    xf = x.float().numpy()
+    ref = ogv.gemv(deq, xf)
+    fmt = "gptq_sym" if sym else "gptq_asym"
+    gemv_bound = _gptq_bound(og, xf[:, perm], group, sym, k)
+    bound = _gemm_gptq_bound(og, xf[:, perm], group, k) if _gemv_tiles(fmt, n, k, B) else gemv_bound
+    for ydt in (torch.float32, torch.bfloat16):
+        _gemv_check(gwb.gemv(qg, x.to(DEV), ydt), ref, bound, ydt)
+        _gemv_check(gwb.gemv(qg, x.to(DEV), out=_strided_out(B, n, ydt)), ref, gemv_bound, ydt)
+    xo = torch.zeros(B, k, dtype=torch.bfloat16)
+    cols = [(b * 131 + 7) % k for b in range(B)]
+    for b, kk in enumerate(cols):
+        xo[b, kk] = 1.0
+    y = _np(gwb.gemv(qg, xo.to(DEV), out=_strided_out(B, n, torch.float32)))
+    for b, kk in enumerate(cols):
+        assert np.array_equal(y[b], deq[:, kk]), (b, kk)
+
+
+def test_group_order_refuses_bad_g_idx():
+    """A g_idx whose groups do not hold exactly G channels, or with an entry past K/G, is
+    reported by the kernels' status word (every access stays in bounds)."""
+    W = workloads.mxfp4_weight(64, 256, seed=565)
+    q = gwb.quantize(W.to(DEV), "gptq_sym_act", group=64,
+                     perm=torch.arange(256, dtype=torch.int32, device=DEV))
+    gi = q["g_idx"]
+    gi[3] = 1                                                   # group 0: 63 channels, group 1: 65
+    with pytest.raises(gwb.GwbError):
+        gwb.group_order(q)
+    gi[3] = 7                                                   # K/G = 4 groups
+    with pytest.raises(gwb.GwbError):
+        gwb.group_order(q)
+    gi[3] = 0
+    assert np.array_equal(_np(gwb.group_order(q)["g_idx"]), np.arange(256))
+
+
 def test_gemv_uintx_config_3072x12288():
     W = workloads.uintx_weight()
     x = workloads.normal_weight(2, 12288, std=1.0, seed=532)
@@ -820,7 +891,7 @@ def test_full_fold_34816x5120_sampled():
 
 
 @pytest.mark.parametrize("fmt,B", [("gptq_sym", 1), ("gptq_sym", 8), ("mxfp4", 1), ("mxfp4", 8), ("uintx", 1),
-                                   ("uintx", 8), ("gptq_sym_act", 1)])
+                                   ("uintx", 8), ("gptq_sym_act", 1), ("gptq_sym_grouped", 1)])
 def test_full_gemv_lm_head_131072x2048_sampled(fmt, B):
     """The page's lm_head decode read, 131072 x 2048, in the launch shapes the benchmark
     times (B = 1: the GEMV kernels; B = 8: the matrix-core GEMV (MXFP4) or tiles (GPTQ,
@@ -847,10 +918,15 @@ def test_full_gemv_lm_head_131072x2048_sampled(fmt, B):
         bound = U32 * ((K_ + 8) if B > 1 else (K_ // 512 + 40)) * ogv.abs_gemv(deq, xf)
     else:
         perm = np.random.default_rng(526).permutation(K_)
-        q = gwb.quantize(Wd, fmt, group=128, perm=torch.from_numpy(perm.astype(np.int32)).to(DEV))
+        q = gwb.quantize(Wd, "gptq_sym_act", group=128, perm=torch.from_numpy(perm.astype(np.int32)).to(DEV))
         o = ogq.quantize_act_order(Ws, 128, True, perm)
         deq = ogq.dequantize(o["qweight"], o["scales"], o["qzeros"], 128, True, g_idx=o["g_idx"])
-        bound = U32 * (K_ // 4 + 48) * ogv.abs_gemv(deq, xf)
+        if fmt == "gptq_sym_act":
+            bound = U32 * (K_ // 4 + 48) * ogv.abs_gemv(deq, xf)
+        else:                                   # group order: index-order GPTQ on the gathered x
+            q = gwb.group_order(q)
+            qw_g, pg = ogq.group_order(o["qweight"], o["g_idx"], 128)
+            bound = _gptq_bound(dict(o, codes=ogq.unpack_int32(qw_g, 0)), xf[:, pg], 128, True, K_)
     y = _np(gwb.gemv(q, xd)).astype(np.float64)
     _gemv_check(torch.from_numpy(y[:, ns]), ogv.gemv(deq, xf), bound, torch.float32)
 
