@@ -591,8 +591,10 @@ static int check_gemm(const gwb_qspec* sp, int64_t N, int64_t K, int64_t M) {
   if (int rc = check_spec(sp, N, K)) return rc;
   if (sp->format == GWB_UINTX && !gemm_uintx_shape(sp, N, K))
     return fail(GWB_E_UNSUPPORTED, "the uintx GEMM takes bf16 weights with N %% 8 == 0 and K %% 512 == 0");
-  if (sp->format != GWB_GPTQ_SYM && sp->format != GWB_GPTQ_ASYM && !is_mxfp4(sp->format) && sp->format != GWB_UINTX)
-    return fail(GWB_E_UNSUPPORTED, "the GEMM takes GPTQ (sym, asym, groups in index order), MXFP4 and uintx weights");
+  if (sp->format != GWB_GPTQ_SYM && sp->format != GWB_GPTQ_ASYM && !is_grouped(sp->format) && !is_mxfp4(sp->format) &&
+      sp->format != GWB_UINTX)
+    return fail(GWB_E_UNSUPPORTED,
+                "the GEMM takes GPTQ (sym, asym, groups in index order or group order), MXFP4 and uintx weights");
   if (N % 8 || K % 128)
     return fail(GWB_E_UNSUPPORTED, "the GEMM needs N %% 8 == 0 and K %% 128 == 0, got N=%lld K=%lld", (long long)N,
                 (long long)K);
@@ -602,6 +604,10 @@ static int check_gemm(const gwb_qspec* sp, int64_t N, int64_t K, int64_t M) {
 }
 
 static size_t gemm_workspace(const gwb_qspec* sp, int64_t M, int64_t N, int64_t K) {
+  if (is_grouped(sp->format)) {
+    const gwb_qspec t = index_twin(sp);
+    return gathered_x_bytes(M, K) + gemm_workspace(&t, M, N, K);
+  }
   if (sp->format == GWB_UINTX) return gwb::uintx_gemm_workspace_bytes(M, N, K);
   return gwb::gemm_workspace_bytes(!is_mxfp4(sp->format), sp->group, M, N, K);
 }
@@ -633,14 +639,21 @@ int gwb_gemm(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
     return fail(GWB_E_SIZE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if (need && !aligned16(workspace)) return fail(GWB_E_UNSUPPORTED, "workspace must be 16-byte aligned");
   hipStream_t st = (hipStream_t)stream;
+  if (is_grouped(spec->format)) {
+    // group order: the activation rows gathered by the permutation, then index-order GPTQ
+    gwb::launch_gather_columns(x, ldx, M, K, (const int32_t*)w->g_idx, workspace, st);
+    x = workspace;
+    ldx = K;
+    workspace = (char*)workspace + gathered_x_bytes(M, K);
+  }
   if (spec->format == GWB_UINTX)
     gwb::launch_uintx_gemm(spec->nbits, spec->group, w->codes, w->scales, w->zeros, N, K, x, M, ldx, y, y_dtype, ldy,
                            workspace, st);
   else if (is_mxfp4(spec->format))
     gwb::launch_mxfp4_gemm(w->codes, w->scales, N, K, x, M, ldx, y, y_dtype, ldy, workspace, st);
   else
-    gwb::launch_gptq_gemm(spec->format == GWB_GPTQ_SYM, spec->group, w->codes, w->scales, w->zeros, N, K, x, M, ldx,
-                          y, y_dtype, ldy, workspace, st);
+    gwb::launch_gptq_gemm(is_gptq_sym(spec->format), spec->group, w->codes, w->scales, w->zeros, N, K, x, M, ldx, y,
+                          y_dtype, ldy, workspace, st);
   return hip_check("gemm launch");
 }
 

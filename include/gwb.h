@@ -298,10 +298,12 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
  * page quantize_dflash_mxfp4.py serves its linears as MXFP4). The weights are
  * dequantized on chip and multiplied on the matrix cores (bf16 operands, float32
  * accumulation).
- *   spec, w  GPTQ sym or asym (groups 32, 64, 128 in index order; not act-order),
- *            MXFP4, or uintx of bf16 weights (page uintx_quant.py, forward; K % 512 ==
- *            0), as gwb_quantize wrote it, [N, K]; N % 8 == 0 and K % 128 == 0 (else
- *            GWB_E_UNSUPPORTED); codes and scales 16-byte aligned
+ *   spec, w  GPTQ sym or asym (groups 32, 64, 128 in index order, or act-order groups
+ *            in group order from gwb_gptq_group_order: the rows of x are gathered by its
+ *            permutation into the workspace first), MXFP4, or uintx of bf16 weights
+ *            (page uintx_quant.py, forward; K % 512 == 0), as gwb_quantize wrote it,
+ *            [N, K]; N % 8 == 0 and K % 128 == 0 (else GWB_E_UNSUPPORTED); codes and
+ *            scales 16-byte aligned
  *   x        device bf16 [M, K], row stride ldx (multiple of 8), 16-byte aligned;
  *            0 <= M <= 2^24 and M * ldx < 2^31
  *   y        device [M, N] of y_dtype (GWB_F32 or GWB_BF16, RNE), row stride ldy
@@ -309,7 +311,8 @@ int gwb_gemv(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N, int64_t K,
  *   workspace at least gwb_gemm_workspace bytes: GPTQ the float32 group sums of x
  *            (K/G x M rounded up to 128, padded to 256 bytes); for M <= 64 with few
  *            column tiles also the float32 partial sums of a K split (splits x M x N),
- *            which a second kernel adds in split order; MXFP4 and uintx only the latter
+ *            which a second kernel adds in split order; MXFP4 and uintx only the latter;
+ *            group order first the gathered x (M x K bf16, padded to 256 bytes)
  * MXFP4 weights are exact bf16 operands, so every product is exact and only the
  * float32 sums round; so are uintx's forward weights bf16((q - zp) * s) (one rounding
  * of an exact product). uintx runs 16-row tiles that convert each weight once per 16

@@ -74,6 +74,28 @@ def test_gemm_gptq_parity(fmt, group, M, n, k):
         _check(gwb.gemm(q, x.to(DEV), ydt), ref, bound, ydt)
 
 
+@pytest.mark.parametrize("sym", [True, False])
+@pytest.mark.parametrize("group,M,n,k", [(128, 37, 264, 640), (32, 130, 520, 1024), (64, 8, 136, 2048)])
+def test_gemm_group_order_parity(sym, group, M, n, k):
+    """Act-order GPTQ in group order (gwb_gptq_group_order): x's rows gathered by the
+    permutation, then the index-order tiles; against the oracle's act-order product,
+    within the tiles' bound for the rearranged tensors."""
+    W = workloads.mxfp4_weight(n, k, seed=640 + n + group)
+    x = workloads.normal_weight(M, k, std=1.0, seed=641 + M)
+    perm_q = np.random.default_rng(642 + k).permutation(k)
+    q = gwb.quantize(W.to(DEV), "gptq_sym_act" if sym else "gptq_asym_act", group=group,
+                     perm=torch.from_numpy(perm_q.astype(np.int32)).to(DEV))
+    qg = gwb.group_order(q)
+    o = ogq.quantize_act_order(W.float().numpy(), group, sym, perm_q)
+    deq = ogq.dequantize(o["qweight"], o["scales"], o["qzeros"], group, sym, g_idx=o["g_idx"])
+    _, perm = ogq.group_order(o["qweight"], o["g_idx"], group)
+    xf = x.float().numpy()
+    ref = ogv.gemv(deq, xf)
+    bound = _gptq_bound(o, xf[:, perm], group, k)
+    for ydt in (torch.float32, torch.bfloat16):
+        _check(gwb.gemm(qg, x.to(DEV), ydt), ref, bound, ydt)
+
+
 @pytest.mark.parametrize("M,n,k", [(1, 256, 128), (37, 264, 640), (130, 520, 1024), (64, 8, 256), (200, 776, 384),
                                    (129, 1032, 2048)])
 def test_gemm_mxfp4_parity(M, n, k):
