@@ -82,8 +82,9 @@ __device__ __forceinline__ void quant_unit(const Raw8<TIn>& r, uint32_t u, uint3
     mx_unpack8(w, e8, d);
     to_f32(r, x);
     // blocks whose maximum reaches 2^60 (E8M0 byte 185 or more) square in float64
-    if (e8 < 127u + 58u) acc_err8_f32(x, d, sw, se);
-    else acc_err8(x, d, sw, se);
+    if (e8 >= 127u + 58u) acc_err8(x, d, sw, se);
+    else if constexpr (sizeof(TIn) == 2) acc_err8_f32_bf16(r.v, x, d, sw, se);
+    else acc_err8_f32(x, d, sw, se);
   }
 }
 

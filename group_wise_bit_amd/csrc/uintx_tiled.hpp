@@ -131,6 +131,24 @@ __device__ __forceinline__ void ux_codes8(const Raw8<typename UxDt<DT>::T>& r, f
   hi = w[1];
 }
 
+// bfloat16 weights: t = x * inv is exact in float32 (two 8-bit significands), and
+// bf16(v) as a float32 is one pair conversion of (0, v), whose low half is the zero's.
+__device__ __forceinline__ float ux_round_bf16(float v) {
+  return __builtin_bit_cast(float, __builtin_convertvector(ux_f32x2_t{0.0f, v}, ux_bf16x2_t));
+}
+__device__ __forceinline__ void ux_codes8_bf16(const float* x, float inv, float zp, float qmax, uint32_t& lo,
+                                               uint32_t& hi, float* qz) {
+  uint32_t w[2] = {0u, 0u};
+  const float lo_q = -zp, hi_q = qmax - zp;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    qz[i] = __builtin_amdgcn_fmed3f(rintf(ux_round_bf16(x[i] * inv)), lo_q, hi_q);
+    w[i >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(qz[i] + zp, i & 3, w[i >> 2]);
+  }
+  lo = w[0];
+  hi = w[1];
+}
+
 // ------------------------------------------------------------- tiled quantize
 // One block per 2048 positions. Per lane: 8 loads (one per segment) in flight; per
 // segment a DPP min/max over the G/8 lanes of a set; each lane of the set then computes
@@ -201,6 +219,22 @@ __global__ __launch_bounds__(256) void uintx_quant_tiled(const typename UxDt<DT>
   for (int j = 0; j < 8; ++j) {
     const typename D::Lds w = set_qp[j];
     float x[8], qz[8];
+    if constexpr (DT == kBF16) {
+      to_f32(raw[j], x);
+      ux_codes8_bf16(x, D::lds_value(w), D::lds_zp(w), qmax, clo[j], chi[j], qz);
+      // the code words are formed here: left to itself the compiler defers their
+      // conversions to the shard packing and keeps all 64 q - zp values live
+      asm volatile("" : "+v"(clo[j]), "+v"(chi[j]));
+      if constexpr (SNR) {
+        const float sc = D::lds_value(qs_lds[(threadIdx.x / LG) * 8 + j]);
+        float d[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) d[b] = ux_round_bf16(qz[b] * sc);
+        if (safe[j]) acc_err8_f32_bf16(raw[j].v, x, d, sw, se);
+        else acc_err8(x, d, sw, se);
+      }
+      continue;
+    }
     ux_codes8<DT>(raw[j], D::lds_value(w), D::lds_zp(w), qmax, clo[j], chi[j], x, qz);
     if constexpr (SNR) {
       // the reconstruction sums of the stored values: r(r(q - zp) * s) as the dequantize
