@@ -199,11 +199,19 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
       dev = fmaxf(dev, fabsf(u[j] - c[j]));
     }
     // Bf16 weights make exact and near ties x / s = k + 1/2 common (a few per thousand):
-    // only the weights that fail the margin divide, each under its own mask.
+    // only the weights that fail the margin divide, each under its own mask. Symmetric
+    // groups of bf16 weights with s = amax / 8 (exact) need no division: x / s = 8x / amax
+    // is a ratio of 8-bit significands, which lies either exactly on a half step or at
+    // least 1/510 away from every half step, far outside the margin band; so a weight
+    // that fails the margin is an exact tie, x / s + 8 = u's nearest half step h, and the
+    // page's rint(x / s) + 8 is rint(h) (8 is even).
     if (dev >= p.z) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (fabsf(u[j] - c[j]) >= p.z) c[j] = rintf(x[j] / p.w) + p.y;
+        if (fabsf(u[j] - c[j]) >= p.z) {
+          if (SYM && sizeof(TIn) == 2 && p.w != 1e-9f) c[j] = rintf(c[j] + copysignf(0.5f, u[j] - c[j]));
+          else c[j] = rintf(x[j] / p.w) + p.y;
+        }
     }
     uint32_t ev = 0, od = 0;
 #pragma unroll
@@ -216,19 +224,24 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
       if (n0 + wave * 8 + i < N && k0 + lane * 8 < K) {
         const float s16 = (float)(_Float16)p.w;
         float d[8];
+        // the unit's two sums, added to the running ones after both branches (one pair
+        // of accumulators, no copies where the branches meet)
+        double uw = 0.0, ue = 0.0;
         if (!tile_big) {
           // (c - z) * s is exact in float32 for a finite non-zero fp16 scale, so
           // c*s - z*s as one fma rounds it exactly
           const float nzs = -(p.y * s16);
 #pragma unroll
           for (int j = 0; j < 8; ++j) d[j] = __builtin_fmaf(__builtin_amdgcn_fmed3f(c[j], 0.0f, 15.0f), s16, nzs);
-          if constexpr (sizeof(TIn) == 2) acc_err8_f32_bf16(raw[i].v, x, d, sw, se);
-          else acc_err8_f32(x, d, sw, se);
+          if constexpr (sizeof(TIn) == 2) acc_err8_f32_bf16(raw[i].v, x, d, uw, ue);
+          else acc_err8_f32(x, d, uw, ue);
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) d[j] = (__builtin_amdgcn_fmed3f(c[j], 0.0f, 15.0f) - p.y) * s16;
-          acc_err8(x, d, sw, se);
+          acc_err8(x, d, uw, ue);
         }
+        sw += uw;
+        se += ue;
       }
     }
   }

@@ -158,3 +158,69 @@ def test_fma32_emulation_is_one_rounding():
     got = _fma32(a, b, c)
     for i in range(3000):
         assert F(got[i]) == rn32(F(a[i]) * F(b[i]) + F(c[i])), i
+
+
+def _sym_tie_rule(x, amax, recips_all=True, rule=np.rint):
+    """The kernel's symmetric bf16 path for weights that fail the margin: h = rint(u) +-
+    1/2 towards u, code rint(h). Returns (rejected count, mismatches, non-ties among the
+    rejected) against the page's rint(fl(x / s)) + 8."""
+    s = F32(amax * F32(0.125))
+    exact = np.rint((x / s).astype(F32)) + F32(8.0)
+    rej, bad, nontie = 0, 0, 0
+    ys = _recips(np.array([s], F32)) if recips_all else [np.array([(F64(1.0) / F64(s))], F32)]
+    for y in ys:
+        u = _fma32(x, np.full_like(x, y[0]), np.full_like(x, F32(8.0)))
+        c = np.rint(u)
+        t = _fma32(np.array([amax], F32), y, np.array([16.0], F32))[0]
+        margin = F32(0.5) - F32(t * F32(2.0 ** -19))
+        fail = ~(np.abs(u - c) < margin)
+        if not fail.any():
+            continue
+        xf = x[fail].astype(F64)
+        m = np.rint(16.0 * xf / F64(amax))                      # 2 x / s, an odd integer at a tie
+        nontie += int(((16.0 * xf != m * F64(amax)) | (m % 2 == 0)).sum())
+        h = c[fail] + np.copysign(F32(0.5), u[fail] - c[fail])
+        code = rule(h).astype(F32)
+        rej += int(fail.sum())
+        bad += int((code != exact[fail]).sum())
+    return rej, bad, nontie
+
+
+def test_sym_bf16_margin_failures_are_exact_ties():
+    """Symmetric groups of bf16 weights (s = amax / 8, exact): every weight that fails the
+    margin is an exact tie x / s = k + 1/2, and the kernel's rint(h) equals the page's
+    rint(fl(x / s)) + 8 - over every bf16 weight of 240 groups, every reciprocal within
+    one ulp, and every significand pair of an amax and a weight."""
+    rng = np.random.default_rng(17)
+    xs = _all_bf16()
+    rej_total = 0
+    for amax in _groups(rng, 240):
+        if amax * F32(0.125) < F32(1e-9):
+            continue
+        x = xs[np.abs(xs) <= amax]
+        rej, bad, nontie = _sym_tie_rule(x, amax)
+        assert bad == 0 and nontie == 0, (amax, bad, nontie)
+        rej_total += rej
+    assert rej_total > 0
+    # every pair of significands (the quotient depends on them and the exponent gap)
+    mx = np.arange(128, 256, dtype=F64)
+    for ma in range(128, 256):
+        amax = F32(ma)
+        for gap in range(0, 12):
+            x = np.concatenate([mx, -mx]) * 2.0 ** (-gap - 1)
+            x = x.astype(F32)
+            x = x[np.abs(x) <= amax]
+            rej, bad, nontie = _sym_tie_rule(x, amax, recips_all=False)
+            assert bad == 0 and nontie == 0, (ma, gap)
+
+
+def test_sym_tie_rule_needs_round_half_even():
+    """Planted mistake: rounding the half step away from zero instead of to even."""
+    rng = np.random.default_rng(18)
+    xs = _all_bf16()
+    away = lambda h: np.sign(h) * np.floor(np.abs(h) + 0.5)
+    bad_total = 0
+    for amax in _groups(rng, 60):
+        x = xs[np.abs(xs) <= amax]
+        bad_total += _sym_tie_rule(x, amax, rule=away)[1]
+    assert bad_total > 0
