@@ -19,8 +19,10 @@ The timed steps carry no per-op markers (an event pair around each launch costs 
 0.2 ms of the step): an untimed pass with an event pair per op gives the breakdown and
 names the op with the largest share, and in the timed steps one event pair brackets that
 op alone. The roofline object is for that kernel: its algorithmic bytes per launch / its
-average HIP-event duration in the timed steps, against 8 TB/s; beside it the same-run
-streaming ceilings of gwb_stream_bench.
+average HIP-event duration in the timed steps, against 8 TB/s, and its VALU issue slots
+per launch (from the committed rocprofv3 counters) over the same duration, against the
+SIMDs' slot rate; the bound is the one of the two it uses the larger share of. Beside it
+the same-run streaming ceilings of gwb_stream_bench.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--breakdown-steps 10]
                     [--no-cpu-baseline] [--no-extras]
@@ -44,7 +46,9 @@ N, K = 34816, 5120
 PEAK_HBM_GBPS = 8000.0
 PEAK_MFMA_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 PEAK_SIMDS, PEAK_CLOCK_HZ = 1024, 2.4e9       # 256 CUs x 4 SIMDs; peak engine clock
-PEAK_VALU_TOPS = PEAK_SIMDS * 16 * PEAK_CLOCK_HZ / 1e12   # 16 lanes per SIMD per cycle: 39.32 T lane-instructions/s
+# one wave64 VALU issue slot per SIMD every 4 cycles (a slot issues one instruction or a
+# pair), counted per lane: 1024 x 2.4 GHz / 4 x 64 = 39.32 T lane-slots/s
+PEAK_VALU_TOPS = PEAK_SIMDS * 16 * PEAK_CLOCK_HZ / 1e12
 # kernels launched by one library call of each step op (quantize, dequantize: one; SNR: the
 # error pass and its finalize; quantize with the SNR fused: the quantize pass and the same
 # finalize; AWQ: table pow, table scale, search, finalize)
@@ -518,17 +522,21 @@ def main():
            "frac": round(achieved / PEAK_HBM_GBPS, 4)}
     roof = {"bound": "hbm", "kernel": dname, **hbm}
     valu = counters.get("valu_insts_per_launch")
-    if valu is not None:
-        # VALU issue load: wavefront VALU instructions (rocprofv3 SQ_INSTS_VALU of this
-        # kernel, per launch, profiles/counters.json) x 4 cycles (a wave64 instruction on a
-        # 16-lane SIMD) over 1024 SIMDs x 2.4 GHz x the launch's live duration
-        lane_ops = valu * 64 / (dom_us * 1e-6) / 1e12                 # T lane-instructions / s
-        roof["valu_load"] = round(valu * 4 / (PEAK_SIMDS * PEAK_CLOCK_HZ * dom_us * 1e-6), 4)
-        if roof["valu_load"] >= 0.9:
-            # issue-bound on the vector ALU: that is the roofline the kernel runs against
-            roof = {"bound": "alu", "kernel": dname, "achieved": round(lane_ops, 2), "peak": PEAK_VALU_TOPS,
-                    "unit": "T lane-instructions/s", "frac": round(lane_ops / PEAK_VALU_TOPS, 4),
-                    "valu_load": roof["valu_load"], "hbm": hbm}
+    pairs = counters.get("valu_pair_quads_per_launch")
+    if valu is not None and pairs is not None:
+        # VALU issue slots (rocprofv3 of this kernel, per launch, profiles/counters.json):
+        # a SIMD issues one wave64 VALU instruction per 4-cycle slot, or two when it pairs
+        # them (SQ_ACTIVE_INST_VALU2 counts those slots), so slots = SQ_INSTS_VALU - pairs.
+        # Peak: 1024 SIMDs x 2.4 GHz / 4 cycles slots/s, x 64 lanes = 39.32 T lane-slots/s.
+        # The roofline is the resource the kernel uses the larger share of.
+        slots = (valu - pairs) * 64 / (dom_us * 1e-6) / 1e12
+        alu = {"achieved": round(slots, 2), "peak": PEAK_VALU_TOPS, "unit": "T lane-issue-slots/s",
+               "frac": round(slots / PEAK_VALU_TOPS, 4), "valu_insts_per_launch": int(valu),
+               "paired_share": round(2 * pairs / valu, 4)}
+        if alu["frac"] > hbm["frac"]:
+            roof = {"bound": "alu", "kernel": dname, **alu, "hbm": hbm}
+        else:
+            roof["alu"] = alu
     roof.update({
         "traffic": counters.get("bytes_per_launch"),
         "algorithmic_bytes_per_launch": int(dbytes), "avg_launch_us": round(dom_us, 2),
