@@ -888,6 +888,18 @@ def test_full_fold_34816x5120_sampled():
     assert np.array_equal(_gpu_bf16bits(r["folded"][rows]), _ref_bf16bits(x))
     assert np.array_equal(_np(r["mxfp4"]["packed"][rows]), packed)
     assert np.array_equal(_np(r["mxfp4"]["e8m0"][rows]), e8)
+    # MXFP4 alone (the benchmark's launch shape: the column-fixed kernel at 8 blocks per
+    # compute unit, every row of the output), and the row step beside the column step
+    mx = gwb.fold_mxfp4(W.to(DEV), torch.from_numpy(s).to(DEV), "mul", want_folded=False)["mxfp4"]
+    assert np.array_equal(_np(mx["packed"][rows]), packed)
+    assert np.array_equal(_np(mx["e8m0"][rows]), e8)
+    assert torch.equal(mx["packed"], r["mxfp4"]["packed"]) and torch.equal(mx["e8m0"], r["mxfp4"]["e8m0"])
+    rv = _fold_vec(34816, 409)
+    mr = gwb.fold_mxfp4(W.to(DEV), torch.from_numpy(s).to(DEV), "mul", torch.from_numpy(rv).to(DEV), "div",
+                        want_folded=False)["mxfp4"]
+    x2, packed2, e82 = ofold.fold_quantize(W[rows].float().numpy(), s, "mul", rv[rows], "div")
+    assert np.array_equal(_np(mr["packed"][rows]), packed2)
+    assert np.array_equal(_np(mr["e8m0"][rows]), e82)
 
 
 @pytest.mark.parametrize("fmt,B", [("gptq_sym", 1), ("gptq_sym", 8), ("mxfp4", 1), ("mxfp4", 8), ("uintx", 1),
