@@ -46,9 +46,9 @@ unsigned stream_grid(uint64_t units, int per_cu) {
 // 20 log10(||w|| / max(||w - deq||, 1e-12)), squared inside the log). One block of
 // 1024 threads. The partials were just written by every XCD, so each load waits on the
 // Infinity Cache: a thread issues kFinBatch independent loads per round (one round for
-// up to 16384 partials) and sums them in index order, then the wavefronts reduce by a
-// fixed butterfly and wavefront 0 adds the 16 wavefront sums in order: deterministic for
-// a given partial count.
+// up to 16384 partials) and sums them in index order, then each wavefront sums its lanes
+// (wave_sum_f64) and thread 0 adds the 16 wavefront sums in order: deterministic for a
+// given partial count.
 constexpr int kFinThreads = 1024;
 constexpr int kFinBatch = 16;
 __global__ __launch_bounds__(kFinThreads) void err_finalize_kernel(const double2* __restrict__ part,
@@ -68,11 +68,8 @@ __global__ __launch_bounds__(kFinThreads) void err_finalize_kernel(const double2
       b += v[j].y;
     }
   }
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) {
-    a += __shfl_xor(a, m);
-    b += __shfl_xor(b, m);
-  }
+  a = wave_sum_f64(a);
+  b = wave_sum_f64(b);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
     sa[w] = a;

@@ -209,18 +209,42 @@ __device__ __forceinline__ void acc_err8_f32_bf16(U4 v, const float* x, const fl
 }
 
 // ---------------------------------------------------------------- error sums
-// Block-wide sum of two doubles; thread 0 writes them to part[2*blockIdx.x]. A fixed
-// butterfly inside each wavefront, then thread 0 adds the wavefront sums in order, so
+// Sum of a double over the 64 lanes of a wavefront, the same value in every lane: DPP
+// steps inside each 16-lane row (quad xor 1 and 2, half mirror, mirror: after each step
+// the lanes being joined hold equal values, and a + b == b + a, so every lane of a row
+// ends with the same sum), then the four row sums read from lanes 0, 16, 32 and 48 and
+// added in that order. Fixed order: deterministic. No LDS traffic (a butterfly of
+// cross-lane shuffles costs an LDS round trip per step).
+template <int CTRL>
+__device__ __forceinline__ double dpp_read_f64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, true);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v += dpp_read_f64<kDppXor1>(v);
+  v += dpp_read_f64<kDppXor2>(v);
+  v += dpp_read_f64<kDppHalfMirror>(v);
+  v += dpp_read_f64<kDppMirror>(v);
+  return ((readlane_f64(v, 0) + readlane_f64(v, 16)) + readlane_f64(v, 32)) + readlane_f64(v, 48);
+}
+
+// Block-wide sum of two doubles; thread 0 writes them to part[2*blockIdx.x]. Each
+// wavefront's sum (wave_sum_f64), then thread 0 adds the wavefront sums in order, so
 // the result is deterministic for a given launch shape.
 template <int THREADS>
 __device__ __forceinline__ void block_sum2_store(double a, double b, double* part) {
   static_assert(THREADS % 64 == 0 && THREADS <= 1024, "whole wavefronts");
   __shared__ double sa[THREADS / 64], sb[THREADS / 64];
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) {
-    a += __shfl_xor(a, m);
-    b += __shfl_xor(b, m);
-  }
+  a = wave_sum_f64(a);
+  b = wave_sum_f64(b);
   if ((threadIdx.x & 63) == 0) {
     sa[threadIdx.x >> 6] = a;
     sb[threadIdx.x >> 6] = b;
