@@ -204,31 +204,30 @@ __global__ __launch_bounds__(256) void awq_search_kernel(const TIn* __restrict__
   }
   __syncthreads();
   const int t = threadIdx.x;
-  if (t < n_alpha) part[(int64_t)blockIdx.x * n_alpha + t] = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
+  if (t < n_alpha) part[(int64_t)t * gridDim.x + blockIdx.x] = (red[0][t] + red[1][t]) + (red[2][t] + red[3][t]);
 }
 
-// One wavefront per alpha sums that alpha's partials (lane-strided, then a fixed
-// butterfly), then thread 0 takes the first strict minimum.
+// One wavefront per alpha sums that alpha's partials (a contiguous row of the [alpha,
+// block] layout: lane-strided in block order, then wave_sum_f64), then thread 0 takes the
+// first strict minimum.
 __global__ __launch_bounds__(1024) void awq_finalize_kernel(const double* __restrict__ part, unsigned nblocks,
                                                             int n_alpha, double* __restrict__ err,
                                                             int32_t* __restrict__ best) {
   __shared__ double e[kMaxAlpha];
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   if (wave < n_alpha) {
+    const double* row = part + (int64_t)wave * nblocks;
     double acc = 0.0;
     // b = lane, lane + 64, ... in order; half batches (1024 threads leave 128 registers)
     for (unsigned b0 = lane; b0 < nblocks; b0 += 64 * (kLoadBatch / 2)) {
       double v[kLoadBatch / 2];
 #pragma unroll
-      for (int j = 0; j < kLoadBatch / 2; ++j) {
-        const unsigned b = b0 + 64 * j;
-        v[j] = part[(int64_t)min(b, nblocks - 1) * n_alpha + wave];
-      }
+      for (int j = 0; j < kLoadBatch / 2; ++j) v[j] = row[min(b0 + 64 * j, nblocks - 1)];
 #pragma unroll
       for (int j = 0; j < kLoadBatch / 2; ++j)
         if (b0 + 64 * j < nblocks) acc += v[j];
     }
-    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    acc = wave_sum_f64(acc);
     if (lane == 0) {
       e[wave] = acc;
       err[wave] = acc;
@@ -258,7 +257,7 @@ static AwqShape awq_shape(int64_t rows, int64_t K) {
 }
 
 // Workspace: powers p [n_alpha, K] f64 | log sums [n_alpha, chunks] f64 |
-// quotients [n_alpha, 2, K] f32 | search partials [grid, n_alpha] f64, each 16-byte aligned.
+// quotients [n_alpha, 2, K] f32 | search partials [n_alpha, grid] f64, each 16-byte aligned.
 struct AwqLayout {
   size_t pw, logs, rc, part, total;
 };
