@@ -40,17 +40,19 @@ struct Alphas {
   double v[kMaxAlpha];
 };
 
+// Sum over the block, the same value in every thread: each wavefront's sum
+// (wave_sum_f64), then the wavefront sums in order through LDS.
 template <int THREADS>
 __device__ double block_sum(double v) {
-  __shared__ double sh[THREADS];
+  __shared__ double sh[THREADS / 64];
+  v = wave_sum_f64(v);
   __syncthreads();
-  sh[threadIdx.x] = v;
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
   __syncthreads();
-  for (int s = THREADS / 2; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
-    __syncthreads();
-  }
-  return sh[0];
+  double t = sh[0];
+#pragma unroll
+  for (int i = 1; i < THREADS / 64; ++i) t += sh[i];
+  return t;
 }
 
 __device__ __forceinline__ double awq_p(double an, double alpha) {
