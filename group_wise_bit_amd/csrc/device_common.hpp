@@ -208,6 +208,25 @@ __device__ __forceinline__ void acc_err8_f32_bf16(U4 v, const float* x, const fl
   se += (double)b;
 }
 
+// The bf16 sums of up to 8 units (64 weights) kept in one lane's float32 running sums,
+// fa and fb, before one float64 addition each at the end of the lane's work: every step
+// is one float32 rounding of a sum of non-negative terms, so for n terms the result is
+// within (n + 2) * 2^-24 of the exact sum, relative (66 * 2^-24, about 4e-6 or 2e-5 dB,
+// for 64). No float32 value overflows while |w| < 2^56 and |w - d| < 2^58: callers take
+// acc_err8 for any group whose largest magnitude reaches 2^56 (kSafeSqMax64).
+constexpr float kSafeSqMax64 = 0x1p56f;
+__device__ __forceinline__ void acc_err8_f32_bf16_into(U4 v, const float* x, const float* d, float& fa, float& fb) {
+  fa = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dc_bf16x2_t, v.x), __builtin_bit_cast(dc_bf16x2_t, v.x), fa, false);
+  fa = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dc_bf16x2_t, v.y), __builtin_bit_cast(dc_bf16x2_t, v.y), fa, false);
+  fa = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dc_bf16x2_t, v.z), __builtin_bit_cast(dc_bf16x2_t, v.z), fa, false);
+  fa = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(dc_bf16x2_t, v.w), __builtin_bit_cast(dc_bf16x2_t, v.w), fa, false);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float e = x[i] - d[i];
+    fb = __builtin_fmaf(e, e, fb);
+  }
+}
+
 // ---------------------------------------------------------------- error sums
 // Sum of a double over the 64 lanes of a wavefront, the same value in every lane: DPP
 // steps inside each 16-lane row (quad xor 1 and 2, half mirror, mirror: after each step

@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
       qp[wave * 8 + row][lane / L] = make_float4(y, zp, margin, s);
       if constexpr (SNR) {
         const float s16 = (float)(_Float16)s;
-        big |= !(a < kSafeSqMax) || !__builtin_isfinite(s16) || s16 == 0.0f;
+        big |= !(a < (sizeof(TIn) == 2 ? kSafeSqMax64 : kSafeSqMax)) || !__builtin_isfinite(s16) || s16 == 0.0f;
       }
     }
   }
@@ -187,6 +187,7 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
   }
   const int gl = lane / L;
   double sw = 0.0, se = 0.0;
+  float fa = 0.0f, fb = 0.0f;                  // bf16 weights: the lane's float32 sums over its 8 rows
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float4 p = qp[wave * 8 + i][gl];
@@ -224,28 +225,23 @@ __global__ __launch_bounds__(256) void gptq_quant_kernel(const TIn* __restrict__
       if (n0 + wave * 8 + i < N && k0 + lane * 8 < K) {
         const float s16 = (float)(_Float16)p.w;
         float d[8];
-        // the unit's two sums, added to the running ones after both branches (one pair
-        // of accumulators, no copies where the branches meet)
-        double uw = 0.0, ue = 0.0;
         if (!tile_big) {
           // (c - z) * s is exact in float32 for a finite non-zero fp16 scale, so
           // c*s - z*s as one fma rounds it exactly
           const float nzs = -(p.y * s16);
 #pragma unroll
           for (int j = 0; j < 8; ++j) d[j] = __builtin_fmaf(__builtin_amdgcn_fmed3f(c[j], 0.0f, 15.0f), s16, nzs);
-          if constexpr (sizeof(TIn) == 2) acc_err8_f32_bf16(raw[i].v, x, d, uw, ue);
-          else acc_err8_f32(x, d, uw, ue);
+          if constexpr (sizeof(TIn) == 2) acc_err8_f32_bf16_into(raw[i].v, x, d, fa, fb);
+          else acc_err8_f32(x, d, sw, se);
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) d[j] = (__builtin_amdgcn_fmed3f(c[j], 0.0f, 15.0f) - p.y) * s16;
-          acc_err8(x, d, uw, ue);
+          acc_err8(x, d, sw, se);
         }
-        sw += uw;
-        se += ue;
       }
     }
   }
-  if constexpr (SNR) block_sum2_store<256>(sw, se, part);   // synchronizes the block too
+  if constexpr (SNR) block_sum2_store<256>(sw + (double)fa, se + (double)fb, part);   // synchronizes the block too
   __syncthreads();
   // qweight [K/8, N]: 64 r-rows x 32 words. Each store instruction of a wavefront writes
   // eight whole 128-byte rows (16 bytes per lane): non-temporal stores reach memory as

@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void uintx_quant_tiled(const typename UxDt<DT>
       mn[j] = lanes_min<LG>(a);
       mx[j] = lanes_max<LG>(b);
       // a 2-byte key orders like, and is below 2^60 exactly when, the weight it holds
-      safe[j] = DT == kF16 || fmaxf(fabsf(mn[j]), fabsf(mx[j])) < kSafeSqMax;
+      safe[j] = DT == kF16 || fmaxf(fabsf(mn[j]), fabsf(mx[j])) < (DT == kBF16 ? kSafeSqMax64 : kSafeSqMax);
     }
     const int i = lane % LG;
     const uint32_t p0 = p - i * kLanePos;    // the set's first position
@@ -213,6 +213,7 @@ __global__ __launch_bounds__(256) void uintx_quant_tiled(const typename UxDt<DT>
   }
   __syncthreads();
   double sw = 0.0, se = 0.0;
+  float fa = 0.0f, fb = 0.0f;                // bf16 weights: the lane's float32 sums over its safe segments
   if (active) {
   uint32_t clo[8], chi[8];
 #pragma unroll
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(256) void uintx_quant_tiled(const typename UxDt<DT>
         float d[8];
 #pragma unroll
         for (int b = 0; b < 8; ++b) d[b] = ux_round_bf16(qz[b] * sc);
-        if (safe[j]) acc_err8_f32_bf16(raw[j].v, x, d, sw, se);
+        if (safe[j]) acc_err8_f32_bf16_into(raw[j].v, x, d, fa, fb);
         else acc_err8(x, d, sw, se);
       }
       continue;
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(256) void uintx_quant_tiled(const typename UxDt<DT>
     st8(packed + sh.base1 + p, lo, hi);
   }
   }
-  if constexpr (SNR) block_sum2_store<256>(sw, se, part);
+  if constexpr (SNR) block_sum2_store<256>(sw + (double)fa, se + (double)fb, part);
 }
 
 // ------------------------------------------------------------- tiled dequantize

@@ -21,7 +21,7 @@ else:  # collected on CPU only to be skipped
     gwb = None
 
 DEV = "cuda"
-FUSED_REL = 16 * 2.0 ** -24 + 1e-12     # the fused pass's float32 unit sums, relative
+FUSED_REL = 72 * 2.0 ** -24 + 1e-12     # the fused pass's float32 sums of up to 64 terms per lane, relative
 _TDT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
@@ -104,3 +104,19 @@ def test_quantize_snr_full_34816x5120():
         assert torch.equal(q1.codes, q2.codes) and torch.equal(q1.scales, q2.scales), fmt
         assert s2[0] == pytest.approx(s1[0], rel=FUSED_REL) and s2[1] == pytest.approx(s1[1], rel=FUSED_REL), fmt
         del q1, q2
+
+
+@pytest.mark.parametrize("fmt,nbits,group", [("uintx", 2, 64), ("uintx", 7, 64), ("uintx", 4, 32),
+                                             ("gptq_sym", 4, 128), ("mxfp4", 4, None)])
+def test_quantize_snr_bf16_large_groups(fmt, nbits, group):
+    """bf16 groups scaled by 2^50 .. 2^63 beside ordinary ones: those at 2^56 and above
+    take float64 squares, those below keep a lane's float32 sums, which must neither
+    overflow nor lose the bound next to them."""
+    n, k = 64, 1024
+    W = workloads.uintx_weight(n, k, seed=840 + nbits, dtype=torch.float32)
+    g = group or 32
+    gain = 2.0 ** np.random.default_rng(841).integers(50, 64, (n, k // g))
+    gain[::3] = 1.0                                 # every third row ordinary
+    W = (W * torch.from_numpy(np.repeat(gain, g, 1)).float()).to(torch.bfloat16)
+    assert torch.isfinite(W.float()).all()
+    _check(W, fmt, nbits=nbits, group=group)
