@@ -762,4 +762,269 @@ void launch_uintx_gemm(int nbits, int group, const void* packed, const void* sca
   }
 }
 
+// ------------------------------------------------------------------ uintx decode
+// Decode (B <= 8 activation rows) on the same layout, spread for memory parallelism
+// rather than operand reuse: a wavefront takes 16 position-rows (lanes j) and one class
+// of segments, those sharing their 4-bit plane (t & 3: segments t and t + 4) or, without
+// a 4-bit shard, their 2-bit plane (t & 1: four segments), so it loads one plane of each
+// shard present and keeps 2 or 4 accumulator tiles; the four wavefronts of a block cover
+// all classes of 16 (or 32) position-rows. The block's activations for its K range sit
+// in LDS for the whole kernel (one barrier, at the start), so wavefronts never wait for
+// one another.
+// A batch is 4 RUN positions of each of the 16 rows, lane q holding the contiguous run
+// q RUN .. q RUN + RUN - 1 of each plane (RUN = 128 bytes with one plane per wavefront,
+// 64 with two or three), and matrix-core step m takes positions q RUN + 8m .. + 7 from
+// lane q (any split of K into 32-k slices serves, with the activations read to match).
+// Long runs per row matter: 16 rows of 32 bytes per lane and batch, K bytes apart, left
+// the memory system at 4 TB/s on the 131072 x 2048 head; whole 128-byte runs read it at
+// the rate of contiguous reads. Each wavefront keeps the next batch's codes, scales and
+// zero points in flight while it converts and multiplies the current one.
+template <int NB> struct UdShape {
+  static constexpr int kSegs = (NB & 4) ? 2 : 4;   // segments per wavefront
+  static constexpr int kClasses = 8 / kSegs;         // wavefronts per 16 position-rows
+  static constexpr int kRowGroups = 4 / kClasses;    // 16-row groups per block
+  static constexpr int kPlanes = ((NB & 4) != 0) + ((NB & 2) != 0) + ((NB & 1) != 0);
+  static constexpr int kRun = 64;                         // bytes per lane, plane and batch
+  static constexpr int kBatch = 4 * kRun;                // positions of a row per batch
+};
+
+template <int NB, int NGR>
+struct UdBuf {
+  static constexpr int W = UdShape<NB>::kRun / 16;   // 16-byte loads per plane
+  U4 w4[W], w2[W], w1[W];                            // the lane's run of each plane
+  uint32_t sb[UdShape<NB>::kSegs][NGR], zb[UdShape<NB>::kSegs][NGR];   // scale bits, zero points
+};
+
+template <int NB, int G, typename TY>
+__global__ __launch_bounds__(256) void uintx_decode_kernel(const uint16_t* __restrict__ x, int64_t ldx, int Bn,
+                                                           const uint8_t* __restrict__ packed,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const uint8_t* __restrict__ zeros, Shards sh, int R8, int K,
+                                                           int kspan, TY* __restrict__ y, int64_t ldy,
+                                                           float* __restrict__ part) {
+  using SB = ShardBits<NB>;
+  using SH = UdShape<NB>;
+  constexpr int SEGS = SH::kSegs, RUN = SH::kRun, BP = SH::kBatch;
+  constexpr int NGR = RUN >= G ? RUN / G : 1;        // groups in a lane's run
+  constexpr int W = RUN / 16;
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [Bn][kspan + 8]
+  const int t = threadIdx.x, lane = t & 63, j = lane & 15, q = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int cls = wv % SH::kClasses, rg = wv / SH::kClasses;
+  const int ks = (int)blockIdx.y * kspan, kend = min(K, ks + kspan);   // multiples of BP
+  const int xp = kspan + 8;                      // LDS row pitch: 16 bytes of padding per row
+  const int cpr = (kend - ks) / 8;
+  for (int v = t; v < Bn * cpr; v += 256) {
+    const int b = v / cpr, c = v - b * cpr;
+    *reinterpret_cast<U4*>(xs + b * xp + 8 * c) = ld16(x + (int64_t)b * ldx + ks + 8 * c);
+  }
+  __syncthreads();
+  const uint16_t* xb = xs + min(j, Bn - 1) * xp + RUN * q - ks;   // rows past the batch repeat the last
+  const int r = ((int)blockIdx.x * SH::kRowGroups + rg) * 16 + j;
+  const uint32_t L1 = (uint32_t)R8 * (uint32_t)K;
+  const uint32_t pos = (uint32_t)min(r, R8 - 1) * (uint32_t)K + RUN * q;   // rows past R8 read a valid row
+  const uint32_t p4 = (uint32_t)sh.base4 + (uint32_t)(cls & 3) * L1 + pos;
+  const uint32_t p2 = (uint32_t)sh.base2 + (uint32_t)(cls & 1) * L1 + pos;
+  const uint32_t p1 = (uint32_t)sh.base1 + pos;
+  auto seg = [&](int i) { return SB::has4 ? cls + 4 * i : cls + 2 * i; };
+  const char* sbase = reinterpret_cast<const char*>(scales);
+  auto load = [&](UdBuf<NB, NGR>& b, int k0) {
+    const uint8_t* pk = packed + k0;
+#pragma unroll
+    for (int u = 0; u < W; ++u) {
+      if constexpr (SB::has4) b.w4[u] = ld16(pk + (p4 + 16u * u));
+      if constexpr (SB::has2) b.w2[u] = ld16(pk + (p2 + 16u * u));
+      if constexpr (SB::has1) b.w1[u] = ld16(pk + (p1 + 16u * u));
+    }
+    // scale and zero point stay apart until the batch is converted: combining them here
+    // would wait for both loads at once
+#pragma unroll
+    for (int i = 0; i < SEGS; ++i)
+#pragma unroll
+      for (int u = 0; u < NGR; ++u) {
+        const uint32_t g = ((uint32_t)seg(i) * L1 + pos + (uint32_t)(k0 + u * G)) / (uint32_t)G;
+        b.sb[i][u] = *reinterpret_cast<const uint16_t*>(sbase + (g << 1));
+        b.zb[i][u] = zeros[g];
+      }
+  };
+  gm_f32x4_t acc[SEGS];
+#pragma unroll
+  for (int i = 0; i < SEGS; ++i) acc[i] = gm_f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto word = [](const U4 (&v)[W], int wi) {
+    const U4& u = v[wi >> 2];
+    return (wi & 3) == 0 ? u.x : (wi & 3) == 1 ? u.y : (wi & 3) == 2 ? u.z : u.w;
+  };
+  auto compute = [&](const UdBuf<NB, NGR>& b, int k0) {
+    float sc[SEGS][NGR], nzs[SEGS][NGR];
+#pragma unroll
+    for (int i = 0; i < SEGS; ++i)
+#pragma unroll
+      for (int u = 0; u < NGR; ++u) {
+        sc[i][u] = __uint_as_float(b.sb[i][u] << 16);
+        nzs[i][u] = -((float)b.zb[i][u] * sc[i][u]);
+      }
+#pragma unroll
+    for (int m = 0; m < RUN / 8; ++m) {
+      const U4 a = *reinterpret_cast<const U4*>(xb + k0 + 8 * m);
+      const int u = RUN >= G ? (8 * m) / G : 0;       // the group of positions q RUN + 8m ..
+#pragma unroll
+      for (int i = 0; i < SEGS; ++i) {
+        const int tt = seg(i);
+        uint32_t c[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int wi = 2 * m + h;
+          uint32_t v = 0u;
+          if constexpr (SB::has4) v |= (word(b.w4, wi) >> (4 * (tt >> 2))) & 0x0F0F0F0Fu;
+          if constexpr (SB::has2) v |= ((word(b.w2, wi) >> (2 * (tt >> 1))) & 0x03030303u) << SB::off2;
+          if constexpr (SB::has1) v |= ((word(b.w1, wi) >> tt) & 0x01010101u) << SB::off1;
+          c[h] = v;
+        }
+        float f[8];
+        if constexpr (NB <= 4) {
+          // a code below 16 read as an OCP e4m3 byte is c * 2^-9 exactly: the scaled FP8
+          // conversion at 2^9 gives two codes as floats per instruction
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const gm_f32x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[h], 512.0f, false);
+            const gm_f32x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(c[h], 512.0f, true);
+            f[4 * h] = lo[0]; f[4 * h + 1] = lo[1]; f[4 * h + 2] = hi[0]; f[4 * h + 3] = hi[1];
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = __builtin_fmaf(f[e], sc[i][u], nzs[i][u]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            f[e] = __builtin_fmaf((float)((c[e >> 2] >> (8 * (e & 3))) & 0xFFu), sc[i][u], nzs[i][u]);
+        }
+        const U4 bw = U4{ux_pair(f[0], f[1]), ux_pair(f[2], f[3]), ux_pair(f[4], f[5]), ux_pair(f[6], f[7])};
+        acc[i] = mfma_bf16(a, bw, acc[i]);
+      }
+      // one step at a time: left free, the scheduler converts many steps ahead of their
+      // products and doubles the registers a wavefront needs
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Two batches per trip, one per buffer: load the next batch, then convert the current.
+  // The loads are unconditional (past the last batch they re-read it), so the compiler
+  // waits for exactly the current batch's loads and leaves the next batch's in flight;
+  // after each group of loads, an empty asm with a memory clobber and a scheduling
+  // barrier keep it from sinking the loads to their first use or hoisting the current
+  // batch's arithmetic above them (either would wait for the loads at once).
+  const int nbt = (kend - ks) / BP;
+  UdBuf<NB, NGR> b0, b1;
+  load(b0, ks);
+  int bt = 0;
+  for (; bt + 1 < nbt; bt += 2) {
+    load(b1, ks + (bt + 1) * BP);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b0, ks + bt * BP);
+    load(b0, ks + min(bt + 2, nbt - 1) * BP);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b1, ks + (bt + 1) * BP);
+  }
+  if (bt < nbt) compute(b0, ks + bt * BP);
+  if (r >= R8) return;
+  const int64_t N = 8 * (int64_t)R8;
+#pragma unroll
+  for (int i = 0; i < SEGS; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int b = 4 * q + e;
+      if (b >= Bn) continue;
+      const int64_t n = (int64_t)seg(i) * R8 + r;
+      if (gridDim.y > 1) {
+        part[((int64_t)blockIdx.y * Bn + b) * N + n] = acc[i][e];
+      } else {
+        TY* p = y + (int64_t)b * ldy + n;
+        if constexpr (sizeof(TY) == 4) *p = acc[i][e];
+        else *p = (TY)(__float_as_uint(round_bf16(acc[i][e])) >> 16);
+      }
+    }
+}
+
+// K splits: toward 1024 blocks (four wavefronts per SIMD), each split at least 2 batches,
+// and the split's activations within kUdLds bytes of LDS.
+constexpr int kUdLds = 64 * 1024;
+template <int NB>
+static int uintx_decode_blocks(int64_t N) {
+  return (int)((N / 8 + 16 * UdShape<NB>::kRowGroups - 1) / (16 * UdShape<NB>::kRowGroups));
+}
+template <int NB>
+static int uintx_decode_splits_nb(int64_t B, int64_t N, int64_t K) {
+  constexpr int BP = UdShape<NB>::kBatch;
+  const int blocks = uintx_decode_blocks<NB>(N);
+  const int64_t nbt = K / BP;
+  int64_t S = (1024 + blocks - 1) / blocks;
+  if (S > nbt / 2) S = nbt / 2;
+  if (S < 1) S = 1;
+  while (S < nbt && (int64_t)B * ((nbt + S - 1) / S * BP + 8) * 2 > kUdLds) ++S;   // LDS bound
+  const int64_t per = (nbt + S - 1) / S;                 // batches per split
+  return (int)((nbt + per - 1) / per);                   // no split left empty
+}
+int uintx_decode_splits(int nbits, int64_t B, int64_t N, int64_t K) {
+  switch (nbits) {
+    case 2: return uintx_decode_splits_nb<2>(B, N, K);
+    case 3: return uintx_decode_splits_nb<3>(B, N, K);
+    case 4: return uintx_decode_splits_nb<4>(B, N, K);
+    case 5: return uintx_decode_splits_nb<5>(B, N, K);
+    case 6: return uintx_decode_splits_nb<6>(B, N, K);
+    default: return uintx_decode_splits_nb<7>(B, N, K);
+  }
+}
+size_t uintx_decode_workspace_bytes(int nbits, int64_t B, int64_t N, int64_t K) {
+  const int S = uintx_decode_splits(nbits, B, N, K);
+  return S > 1 ? (size_t)S * (size_t)B * (size_t)N * sizeof(float) : 0;
+}
+
+template <int NB, int G>
+static void uintx_decode_nb(const void* x, int64_t ldx, int B, const void* packed, const void* scales,
+                            const void* zeros, int64_t N, int64_t K, void* y, int32_t y_dtype, int64_t ldy,
+                            void* workspace, hipStream_t st) {
+  constexpr int BP = UdShape<NB>::kBatch;
+  const int blocks = uintx_decode_blocks<NB>(N);
+  const int S = uintx_decode_splits_nb<NB>(B, N, K);
+  const int nbt = (int)(K / BP), kspan = (nbt + S - 1) / S * BP;
+  const size_t lds = (size_t)B * (kspan + 8) * sizeof(uint16_t);
+  const dim3 grid((unsigned)blocks, (unsigned)S);
+  const Shards sh = shards_of(NB, N * K);
+  if (S > 1) {
+    hipLaunchKernelGGL((uintx_decode_kernel<NB, G, float>), grid, dim3(256), lds, st, (const uint16_t*)x, ldx, B,
+                       (const uint8_t*)packed, (const uint16_t*)scales, (const uint8_t*)zeros, sh, (int)(N / 8),
+                       (int)K, kspan, (float*)nullptr, (int64_t)0, (float*)workspace);
+    gemm_reduce((const float*)workspace, S, B, (int)N, y, y_dtype, ldy, st);
+  } else if (y_dtype == kF32) {
+    hipLaunchKernelGGL((uintx_decode_kernel<NB, G, float>), grid, dim3(256), lds, st, (const uint16_t*)x, ldx, B,
+                       (const uint8_t*)packed, (const uint16_t*)scales, (const uint8_t*)zeros, sh, (int)(N / 8),
+                       (int)K, kspan, (float*)y, ldy, (float*)nullptr);
+  } else {
+    hipLaunchKernelGGL((uintx_decode_kernel<NB, G, uint16_t>), grid, dim3(256), lds, st, (const uint16_t*)x, ldx,
+                       B, (const uint8_t*)packed, (const uint16_t*)scales, (const uint8_t*)zeros, sh, (int)(N / 8),
+                       (int)K, kspan, (uint16_t*)y, ldy, (float*)nullptr);
+  }
+}
+template <int NB>
+static void uintx_decode_g(int group, const void* x, int64_t ldx, int B, const void* packed, const void* scales,
+                           const void* zeros, int64_t N, int64_t K, void* y, int32_t y_dtype, int64_t ldy,
+                           void* workspace, hipStream_t st) {
+  if (group == 32) uintx_decode_nb<NB, 32>(x, ldx, B, packed, scales, zeros, N, K, y, y_dtype, ldy, workspace, st);
+  else if (group == 64) uintx_decode_nb<NB, 64>(x, ldx, B, packed, scales, zeros, N, K, y, y_dtype, ldy, workspace, st);
+  else uintx_decode_nb<NB, 128>(x, ldx, B, packed, scales, zeros, N, K, y, y_dtype, ldy, workspace, st);
+}
+void launch_uintx_decode(int nbits, int group, const void* packed, const void* scales, const void* zeros, int64_t N,
+                         int64_t K, const void* x, int64_t B, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
+                         void* workspace, hipStream_t st) {
+  const int b = (int)B;
+  switch (nbits) {
+    case 2: uintx_decode_g<2>(group, x, ldx, b, packed, scales, zeros, N, K, y, y_dtype, ldy, workspace, st); break;
+    case 3: uintx_decode_g<3>(group, x, ldx, b, packed, scales, zeros, N, K, y, y_dtype, ldy, workspace, st); break;
+    case 4: uintx_decode_g<4>(group, x, ldx, b, packed, scales, zeros, N, K, y, y_dtype, ldy, workspace, st); break;
+    case 5: uintx_decode_g<5>(group, x, ldx, b, packed, scales, zeros, N, K, y, y_dtype, ldy, workspace, st); break;
+    case 6: uintx_decode_g<6>(group, x, ldx, b, packed, scales, zeros, N, K, y, y_dtype, ldy, workspace, st); break;
+    default: uintx_decode_g<7>(group, x, ldx, b, packed, scales, zeros, N, K, y, y_dtype, ldy, workspace, st); break;
+  }
+}
+
 }  // namespace gwb

@@ -168,6 +168,11 @@ constexpr int kGemmMaxRows = 1 << 24;
 // Decode batches on bf16-weight uintx in the tiled layout (N % 8 == 0, K % 512 == 0):
 // the matrix-core path of gwb_gemv; float32 K-split partials in the workspace.
 size_t uintx_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int uintx_decode_splits(int nbits, int64_t B, int64_t N, int64_t K);
+size_t uintx_decode_workspace_bytes(int nbits, int64_t B, int64_t N, int64_t K);
+void launch_uintx_decode(int nbits, int group, const void* packed, const void* scales, const void* zeros, int64_t N,
+                         int64_t K, const void* x, int64_t B, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
+                         void* workspace, hipStream_t st);
 void launch_uintx_gemm(int nbits, int group, const void* packed, const void* scales, const void* zeros, int64_t N,
                        int64_t K, const void* x, int64_t M, int64_t ldx, void* y, int32_t y_dtype, int64_t ldy,
                        void* workspace, hipStream_t st);

@@ -474,11 +474,18 @@ def _gemv_tiles(fmt, n, k, B):
     return B >= 2 and fmt in ("gptq_sym", "gptq_asym")
 
 
-def _uintx_tiles(dt, n, k, B):
-    """gwb_gemv hands bf16-weight uintx batches of 5+ rows on weights of 65536+ rows to
-    gwb_gemm's uintx tiles; their float32 sums run in the matrix cores' order:
+def _uintx_mfma(dt, n, k, B, nbits):
+    """Whether gwb_gemv runs a bf16-weight uintx batch on the matrix cores (the decode
+    kernel: 2 and 4 bits from 2 rows, 3, 5 and 6 bits from 4 rows; 7 bits on gwb_gemm's
+    tiles from 5 rows on weights of 65536+ rows), whose float32 sums have no stated order:
     u (K + 8) sum |w x|."""
-    return dt == "bf16" and B >= 5 and n >= 65536 and n % 8 == 0 and k % 512 == 0
+    if dt != "bf16" or n % 8 or k % 512:
+        return False
+    if nbits in (2, 4):
+        return B >= 2
+    if nbits == 7:
+        return B >= 5 and n >= 65536
+    return B >= 4
 
 
 def _gemm_gptq_bound(o, x, group, K):
@@ -584,7 +591,7 @@ def test_gemv_uintx_parity(nbits, n, k, B):
     o = oux.quantize(W.float().numpy(), nbits)
     deq = ogv.dequantized("uintx", o, n, k, nbits=nbits)
     xf = x.float().numpy()
-    bound = U32 * ((k + 8) if _uintx_tiles("bf16", n, k, B) else (k // 512 + 40)) * ogv.abs_gemv(deq, xf)
+    bound = U32 * ((k + 8) if _uintx_mfma("bf16", n, k, B, nbits) else (k // 512 + 40)) * ogv.abs_gemv(deq, xf)
     for ydt in (torch.float32, torch.bfloat16):
         _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ogv.gemv(deq, xf), bound, ydt)
     # one-hot activations: every output is one exact product, on either path
@@ -594,6 +601,50 @@ def test_gemv_uintx_parity(nbits, n, k, B):
         xo[b, kk] = 1.0
     yo = _np(gwb.gemv(q, xo.to(DEV)))
     assert np.array_equal(yo, deq[:, cols].T.astype(np.float32))
+
+
+@pytest.mark.parametrize("nbits", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("group", [32, 64, 128])
+@pytest.mark.parametrize("n,k,B", [(264, 2048, 8), (1040, 1536, 4), (8, 512, 5), (136, 4096, 6)])
+def test_gemv_uintx_decode_parity(nbits, group, n, k, B):
+    """The matrix-core decode kernel (bf16 weights, 4+ activation rows): every width it
+    takes, every group size, ragged 16-row groups (1040 / 8 = 130 position-rows), one
+    position-row (n = 8), K splits summed afterwards, and odd batch counts. The page's
+    forward, x times bf16((q - zp) s), within u (K + 8) sum |w x|; one-hot activations
+    bit for bit."""
+    assert _uintx_mfma("bf16", n, k, B, nbits)
+    W = workloads.uintx_weight(n, k, seed=560 + n + nbits + group, outlier_frac=0.01)
+    x = workloads.normal_weight(B, k, std=1.0, seed=561 + B)
+    q = gwb.quantize(W.to(DEV), "uintx", nbits=nbits, group=group)
+    o = oux.quantize(W.float().numpy(), nbits, group)
+    deq = ogv.dequantized("uintx", o, n, k, group=group, nbits=nbits)
+    xf = x.float().numpy()
+    bound = U32 * (k + 8) * ogv.abs_gemv(deq, xf)
+    for ydt in (torch.float32, torch.bfloat16):
+        _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ogv.gemv(deq, xf), bound, ydt)
+    xo = torch.zeros(B, k, dtype=torch.bfloat16)
+    cols = [(b * 131 + 7) % k for b in range(B)]
+    for b, kk in enumerate(cols):
+        xo[b, kk] = 1.0
+    yo = _np(gwb.gemv(q, xo.to(DEV)))
+    assert np.array_equal(yo, deq[:, cols].T.astype(np.float32))
+
+
+def test_gemv_uintx_decode_uneven_splits_sampled():
+    """22528 x 3584, uintx4, 8 rows: 176 decode blocks ask for 6 K splits of 14 batches,
+    which the launcher turns into 5 of 3 batches (the last with 2), so no split is left
+    empty; sampled output rows against the oracle."""
+    n, k, B = 22528, 3584, 8
+    W = workloads.uintx_weight(n, k, seed=570, outlier_frac=0.01)
+    x = workloads.normal_weight(B, k, std=1.0, seed=571)
+    q = gwb.quantize(W.to(DEV), "uintx", nbits=4)
+    y = _np(gwb.gemv(q, x.to(DEV)))
+    rows = np.unique(np.concatenate([np.random.default_rng(572).choice(n, 96, replace=False), [0, n - 1]]))
+    o = oux.quantize(W[rows].float().numpy(), 4)
+    deq = ogv.dequantized("uintx", o, len(rows), k, nbits=4)
+    xf = x.float().numpy()
+    _gemv_check(torch.from_numpy(y[:, rows]), ogv.gemv(deq, xf), U32 * (k + 8) * ogv.abs_gemv(deq, xf),
+                torch.float32)
 
 
 @pytest.mark.parametrize("dt,group", [("f16", 64), ("f32", 64), ("bf16", 32), ("bf16", 128), ("f16", 128),
@@ -608,7 +659,7 @@ def test_gemv_uintx_variants_parity(dt, group, nbits, n, k, B):
     o = oux.quantize(W.float().numpy(), nbits, group, dt)
     deq = ogv.dequantized("uintx", o, n, k, group=group, nbits=nbits, dtype=dt)
     xf = x.float().numpy()
-    bound = U32 * ((k + 8) if _uintx_tiles(dt, n, k, B) else (k // 512 + 40)) * ogv.abs_gemv(deq, xf)
+    bound = U32 * ((k + 8) if _uintx_mfma(dt, n, k, B, nbits) else (k // 512 + 40)) * ogv.abs_gemv(deq, xf)
     for ydt in (torch.float32, torch.bfloat16):
         _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ogv.gemv(deq, xf), bound, ydt)
     # one-hot activations return the multiplied weight's columns bit for bit
