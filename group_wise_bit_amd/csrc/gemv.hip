@@ -598,14 +598,15 @@ __device__ __forceinline__ void mxm_mma(const MxmBuf& bf, const uint16_t* xb, in
   for (int i = 0; i < kMxmNS; ++i) {
     const int k = k0 + 128 * i;
     if (FULL || k < kend) {                                     // wave-uniform
-      const bool ok = FULL || k + 32 * q < kend;                // this lane's 32-block is inside the split
+      const int kl = k + 32 * q;                                // this lane's 32-block
+      const bool ok = FULL || kl < kend;                        // inside the split
       const uint32_t e8 = AL ? (bf.e[i] >> (8 * q)) & 0xFFu : bf.e[i];
       const float scl = mx_scale_operand(e8);
       nan |= (uint32_t)(ok && e8 == 255u);
       U4 b[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        b[s] = *reinterpret_cast<const U4*>(xb + (ok ? (k - ks) + 32 * q + 8 * s : 0));   // inside the staged row
+        b[s] = *reinterpret_cast<const U4*>(xb + (ok ? (kl - ks) + 8 * s : 0));   // inside the staged row
         if (!ok) b[s] = U4{0u, 0u, 0u, 0u};
       }
       const U4 w = bf.w[i];
@@ -715,6 +716,8 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_mfma_kernel(const uint8_t* __r
     const uint8_t *wr2 = wr, *er2 = er;
     if (bt2 != bt && more) rows_of(bt2, wr2, er2);
     mxm_load<AL>(b1, wr2, er2, ks + h2 * 128 * kMxmNS, kend, q, more);
+    asm volatile("" ::: "memory");       // keep the loads here, ahead of the products
+    __builtin_amdgcn_sched_barrier(0);
     if (AL || ks + (h + 1) * 128 * kMxmNS <= kend) mxm_mma<AL, true>(b0, xb, ks + h * 128 * kMxmNS, ks, kend, q, acc, nan);
     else mxm_mma<AL, false>(b0, xb, ks + h * 128 * kMxmNS, ks, kend, q, acc, nan);
     if (h == nb - 1) finish(bt, acc, nan);
@@ -727,6 +730,8 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_mfma_kernel(const uint8_t* __r
     wr2 = wr; er2 = er;
     if (bt2 != bt && more) rows_of(bt2, wr2, er2);
     mxm_load<AL>(b0, wr2, er2, ks + h2 * 128 * kMxmNS, kend, q, more);
+    asm volatile("" ::: "memory");       // keep the loads here, ahead of the products
+    __builtin_amdgcn_sched_barrier(0);
     if (AL || ks + (h + 1) * 128 * kMxmNS <= kend) mxm_mma<AL, true>(b1, xb, ks + h * 128 * kMxmNS, ks, kend, q, acc, nan);
     else mxm_mma<AL, false>(b1, xb, ks + h * 128 * kMxmNS, ks, kend, q, acc, nan);
     if (h == nb - 1) finish(bt, acc, nan);
