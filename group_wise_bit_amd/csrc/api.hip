@@ -556,7 +556,7 @@ static int gemv_dispatch(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N
   if (gemv_uintx_via_decode(spec, N, K, B) && aligned16(w->codes))
     gwb::launch_uintx_decode(spec->nbits, spec->group, w->codes, w->scales, w->zeros, N, K, x, B, ldx, y, y_dtype,
                              ldy, workspace, st);
-  else if (gemv_uintx_via_tiles(spec, N, K, B) && aligned16(w->codes))
+  else if (gemv_uintx_via_tiles(spec, N, K, B) && aligned16(w->codes) && aligned16(y) && ldy % 8 == 0)
     gwb::launch_uintx_gemm(spec->nbits, spec->group, w->codes, w->scales, w->zeros, N, K, x, B, ldx, y, y_dtype, ldy,
                            workspace, st);
   else if (tiles && is_mxfp4(spec->format))

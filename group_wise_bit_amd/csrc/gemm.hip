@@ -994,7 +994,7 @@ static void uintx_decode_nb(const void* x, int64_t ldx, int B, const void* packe
     hipLaunchKernelGGL((uintx_decode_kernel<NB, G, float>), grid, dim3(256), lds, st, (const uint16_t*)x, ldx, B,
                        (const uint8_t*)packed, (const uint16_t*)scales, (const uint8_t*)zeros, sh, (int)(N / 8),
                        (int)K, kspan, (float*)nullptr, (int64_t)0, (float*)workspace);
-    gemm_reduce((const float*)workspace, S, B, (int)N, y, y_dtype, ldy, st);
+    launch_gemv_finalize((const float*)workspace, S, B, N, y, y_dtype, ldy, st);   // any y alignment
   } else if (y_dtype == kF32) {
     hipLaunchKernelGGL((uintx_decode_kernel<NB, G, float>), grid, dim3(256), lds, st, (const uint16_t*)x, ldx, B,
                        (const uint8_t*)packed, (const uint16_t*)scales, (const uint8_t*)zeros, sh, (int)(N / 8),

@@ -622,6 +622,11 @@ def test_gemv_uintx_decode_parity(nbits, group, n, k, B):
     bound = U32 * (k + 8) * ogv.abs_gemv(deq, xf)
     for ydt in (torch.float32, torch.bfloat16):
         _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ogv.gemv(deq, xf), bound, ydt)
+    # activations with a row stride past K (64 more elements) and a strided y
+    xw = torch.zeros(B, k + 64, dtype=torch.bfloat16, device=DEV)
+    xw[:, :k] = x.to(DEV)
+    _gemv_check(gwb.gemv(q, xw[:, :k], out=_strided_out(B, n, torch.float32)), ogv.gemv(deq, xf), bound,
+                torch.float32)
     xo = torch.zeros(B, k, dtype=torch.bfloat16)
     cols = [(b * 131 + 7) % k for b in range(B)]
     for b, kk in enumerate(cols):
