@@ -473,23 +473,19 @@ static bool gemv_shape_via_gemm(const gwb_qspec* sp, int64_t N, int64_t K, int64
   return (sp->format == GWB_GPTQ_SYM || sp->format == GWB_GPTQ_ASYM) && B >= 2;
 }
 // bf16-weight uintx batches go to the matrix-core decode kernel where it is faster than
-// the GEMV: from 2 rows for 2 and 4 bits (one plane per wavefront), from 4 rows for 3, 5
-// and 6 bits (two planes); 7 bits (three planes: half the wavefronts per SIMD) keep the
-// GEMV, or gwb_gemm's uintx tiles for 5+ rows on weights of 65536+ rows. Measured on the
-// 131072 x 2048 head, cold: B = 8, uintx4 62.5 -> 47.3 us, uintx2 53.1 -> 44.1, uintx3
-// 72.5 -> 60.2, uintx5 82.1 -> 67.4, uintx6 82.7 -> 72.2, uintx7 85.5 (tiles) against
-// 92.8; B = 2, uintx4 47.5 -> 43.7, uintx3 46.1 against 54.9; B = 1, uintx4 36.0 against
-// 42.8.
+// the GEMV kernels: from 2 rows for 2 and 4 bits (one plane per wavefront), from 3 rows
+// for 3, 5 and 6 bits (two planes), from 5 rows for 7 bits (three planes: fewer
+// wavefronts per SIMD). Measured on the 131072 x 2048 head, cold, decode against GEMV:
+// B = 8, uintx4 42.5 against 62.5 us (the GEMM tiles), uintx7 78.5 against 88.6 (tiles);
+// B = 3, uintx3 49.3 against 56.8; B = 2, uintx3 48.1 against 45.6, uintx7 74.6 against
+// 61.6; B = 1, uintx4 38.6 against 34.8.
 static bool gemm_uintx_shape(const gwb_qspec* sp, int64_t N, int64_t K) {
   return sp->format == GWB_UINTX && sp->w_dtype == GWB_BF16 && N % 8 == 0 && K % 512 == 0;
 }
 static bool gemv_uintx_via_decode(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
   if (!gemm_uintx_shape(sp, N, K) || B * K >= kMaxElems) return false;
   if (sp->nbits == 2 || sp->nbits == 4) return B >= 2;
-  return sp->nbits != 7 && B >= 4;
-}
-static bool gemv_uintx_via_tiles(const gwb_qspec* sp, int64_t N, int64_t K, int64_t B) {
-  return gemm_uintx_shape(sp, N, K) && sp->nbits == 7 && B >= 5 && N >= 65536 && B * K < kMaxElems;
+  return B >= (sp->nbits == 7 ? 5 : 3);
 }
 
 // The GEMV kernels' K-split partial sums (none with a single split).
@@ -523,10 +519,6 @@ static size_t gemv_workspace(const gwb_qspec* sp, int64_t N, int64_t K, int64_t 
     const size_t b = gwb::uintx_decode_workspace_bytes(sp->nbits, B, N, K);
     return a > b ? a : b;
   }
-  if (gemv_uintx_via_tiles(sp, N, K, B)) {
-    const size_t b = gwb::uintx_gemm_workspace_bytes(B, N, K);
-    return a > b ? a : b;
-  }
   if (!gemv_shape_via_gemm(sp, N, K, B)) return a;
   const size_t b = gwb::gemm_workspace_bytes(!is_mxfp4(sp->format), sp->group, B, N, K);
   return a > b ? a : b;
@@ -553,12 +545,9 @@ static int gemv_dispatch(const gwb_qspec* spec, const gwb_qtensors* w, int64_t N
                          int64_t ldx, void* y, int32_t y_dtype, int64_t ldy, void* workspace, hipStream_t st) {
   const bool tiles = gemv_shape_via_gemm(spec, N, K, B) && aligned16(y) && ldy % 8 == 0 && B * ldx < kMaxElems &&
                      aligned16(w->codes) && aligned16(w->scales);
-  if (gemv_uintx_via_decode(spec, N, K, B) && aligned16(w->codes))
+  if (gemv_uintx_via_decode(spec, N, K, B) && aligned16(w->codes) && aligned16(w->scales) && aligned16(w->zeros))
     gwb::launch_uintx_decode(spec->nbits, spec->group, w->codes, w->scales, w->zeros, N, K, x, B, ldx, y, y_dtype,
                              ldy, workspace, st);
-  else if (gemv_uintx_via_tiles(spec, N, K, B) && aligned16(w->codes) && aligned16(y) && ldy % 8 == 0)
-    gwb::launch_uintx_gemm(spec->nbits, spec->group, w->codes, w->scales, w->zeros, N, K, x, B, ldx, y, y_dtype, ldy,
-                           workspace, st);
   else if (tiles && is_mxfp4(spec->format))
     gwb::launch_mxfp4_gemm(w->codes, w->scales, N, K, x, B, ldx, y, y_dtype, ldy, workspace, st);
   else if (tiles)

@@ -771,28 +771,29 @@ void launch_uintx_gemm(int nbits, int group, const void* packed, const void* sca
 // all classes of 16 (or 32) position-rows. The block's activations for its K range sit
 // in LDS for the whole kernel (one barrier, at the start), so wavefronts never wait for
 // one another.
-// A batch is 4 RUN positions of each of the 16 rows, lane q holding the contiguous run
-// q RUN .. q RUN + RUN - 1 of each plane (RUN = 128 bytes with one plane per wavefront,
-// 64 with two or three), and matrix-core step m takes positions q RUN + 8m .. + 7 from
-// lane q (any split of K into 32-k slices serves, with the activations read to match).
-// Long runs per row matter: 16 rows of 32 bytes per lane and batch, K bytes apart, left
-// the memory system at 4 TB/s on the 131072 x 2048 head; whole 128-byte runs read it at
-// the rate of contiguous reads. Each wavefront keeps the next batch's codes, scales and
-// zero points in flight while it converts and multiplies the current one.
+// A batch is 256 positions of each of the 16 rows: lane q holds the 16-byte pieces at
+// 64u + 16q (u < 4) of each plane, so every load instruction reads 64 contiguous bytes of
+// each row, and matrix-core step m takes positions 64 (m >> 1) + 16q + 8 (m & 1) .. + 7
+// from lane q (any split of K into 32-k slices serves, with the activations read to
+// match); the row's scales and zero points of the batch (256 / G groups) are one load
+// each. Measured on the 131072 x 2048 head, 8 rows, 4 bits: 16 rows of 32 bytes per lane
+// and batch, K bytes apart, 57 us; a contiguous 64-byte run per lane (each instruction
+// reading 16 bytes every 64 of each row) 47 us; these pieces 42 us. Each wavefront keeps
+// the next batch's codes, scales and zero points in flight while it converts and
+// multiplies the current one.
 template <int NB> struct UdShape {
   static constexpr int kSegs = (NB & 4) ? 2 : 4;   // segments per wavefront
   static constexpr int kClasses = 8 / kSegs;         // wavefronts per 16 position-rows
   static constexpr int kRowGroups = 4 / kClasses;    // 16-row groups per block
-  static constexpr int kPlanes = ((NB & 4) != 0) + ((NB & 2) != 0) + ((NB & 1) != 0);
-  static constexpr int kRun = 64;                         // bytes per lane, plane and batch
+  static constexpr int kRun = 64;                    // bytes per lane, plane and batch
   static constexpr int kBatch = 4 * kRun;                // positions of a row per batch
 };
 
 template <int NB, int NGR>
 struct UdBuf {
   static constexpr int W = UdShape<NB>::kRun / 16;   // 16-byte loads per plane
-  U4 w4[W], w2[W], w1[W];                            // the lane's run of each plane
-  uint32_t sb[UdShape<NB>::kSegs][NGR], zb[UdShape<NB>::kSegs][NGR];   // scale bits, zero points
+  U4 w4[W], w2[W], w1[W];                            // the lane's pieces of each plane
+  uint32_t sb[UdShape<NB>::kSegs][(NGR + 1) / 2], zb[UdShape<NB>::kSegs][(NGR + 3) / 4];   // the row's scales, zero points
 };
 
 template <int NB, int G, typename TY>
@@ -805,7 +806,7 @@ __global__ __launch_bounds__(256) void uintx_decode_kernel(const uint16_t* __res
   using SB = ShardBits<NB>;
   using SH = UdShape<NB>;
   constexpr int SEGS = SH::kSegs, RUN = SH::kRun, BP = SH::kBatch;
-  constexpr int NGR = RUN >= G ? RUN / G : 1;        // groups in a lane's run
+  constexpr int NGR = BP / G;                        // groups of a row in a batch
   constexpr int W = RUN / 16;
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];   // [Bn][kspan + 8]
   const int t = threadIdx.x, lane = t & 63, j = lane & 15, q = lane >> 4;
@@ -819,10 +820,11 @@ __global__ __launch_bounds__(256) void uintx_decode_kernel(const uint16_t* __res
     *reinterpret_cast<U4*>(xs + b * xp + 8 * c) = ld16(x + (int64_t)b * ldx + ks + 8 * c);
   }
   __syncthreads();
-  const uint16_t* xb = xs + min(j, Bn - 1) * xp + RUN * q - ks;   // rows past the batch repeat the last
+  const uint16_t* xb = xs + min(j, Bn - 1) * xp + 16 * q - ks;   // rows past the batch repeat the last
   const int r = ((int)blockIdx.x * SH::kRowGroups + rg) * 16 + j;
   const uint32_t L1 = (uint32_t)R8 * (uint32_t)K;
-  const uint32_t pos = (uint32_t)min(r, R8 - 1) * (uint32_t)K + RUN * q;   // rows past R8 read a valid row
+  const uint32_t rowp = (uint32_t)min(r, R8 - 1) * (uint32_t)K;
+  const uint32_t pos = rowp + 16 * q;   // rows past R8 read a valid row
   const uint32_t p4 = (uint32_t)sh.base4 + (uint32_t)(cls & 3) * L1 + pos;
   const uint32_t p2 = (uint32_t)sh.base2 + (uint32_t)(cls & 1) * L1 + pos;
   const uint32_t p1 = (uint32_t)sh.base1 + pos;
@@ -832,20 +834,29 @@ __global__ __launch_bounds__(256) void uintx_decode_kernel(const uint16_t* __res
     const uint8_t* pk = packed + k0;
 #pragma unroll
     for (int u = 0; u < W; ++u) {
-      if constexpr (SB::has4) b.w4[u] = ld16(pk + (p4 + 16u * u));
-      if constexpr (SB::has2) b.w2[u] = ld16(pk + (p2 + 16u * u));
-      if constexpr (SB::has1) b.w1[u] = ld16(pk + (p1 + 16u * u));
+      if constexpr (SB::has4) b.w4[u] = ld16(pk + (p4 + 64u * u));
+      if constexpr (SB::has2) b.w2[u] = ld16(pk + (p2 + 64u * u));
+      if constexpr (SB::has1) b.w1[u] = ld16(pk + (p1 + 64u * u));
     }
     // scale and zero point stay apart until the batch is converted: combining them here
     // would wait for both loads at once
 #pragma unroll
-    for (int i = 0; i < SEGS; ++i)
-#pragma unroll
-      for (int u = 0; u < NGR; ++u) {
-        const uint32_t g = ((uint32_t)seg(i) * L1 + pos + (uint32_t)(k0 + u * G)) / (uint32_t)G;
-        b.sb[i][u] = *reinterpret_cast<const uint16_t*>(sbase + (g << 1));
-        b.zb[i][u] = zeros[g];
+    for (int i = 0; i < SEGS; ++i) {
+      const uint32_t g = ((uint32_t)seg(i) * L1 + rowp + (uint32_t)k0) / (uint32_t)G;   // a multiple of NGR
+      if constexpr (NGR == 8) {
+        const U4 v = *reinterpret_cast<const U4*>(sbase + (g << 1));
+        b.sb[i][0] = v.x; b.sb[i][1] = v.y; b.sb[i][2] = v.z; b.sb[i][3] = v.w;
+        const uint2 z = *reinterpret_cast<const uint2*>(zeros + g);
+        b.zb[i][0] = z.x; b.zb[i][1] = z.y;
+      } else if constexpr (NGR == 4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(sbase + (g << 1));
+        b.sb[i][0] = v.x; b.sb[i][1] = v.y;
+        b.zb[i][0] = *reinterpret_cast<const uint32_t*>(zeros + g);
+      } else {
+        b.sb[i][0] = *reinterpret_cast<const uint32_t*>(sbase + (g << 1));
+        b.zb[i][0] = *reinterpret_cast<const uint16_t*>(zeros + g);
       }
+    }
   };
   gm_f32x4_t acc[SEGS];
 #pragma unroll
@@ -854,22 +865,32 @@ __global__ __launch_bounds__(256) void uintx_decode_kernel(const uint16_t* __res
     const U4& u = v[wi >> 2];
     return (wi & 3) == 0 ? u.x : (wi & 3) == 1 ? u.y : (wi & 3) == 2 ? u.z : u.w;
   };
+  const bool qhi = (q & 2) != 0;
   auto compute = [&](const UdBuf<NB, NGR>& b, int k0) {
-    float sc[SEGS][NGR], nzs[SEGS][NGR];
-#pragma unroll
-    for (int i = 0; i < SEGS; ++i)
-#pragma unroll
-      for (int u = 0; u < NGR; ++u) {
-        sc[i][u] = __uint_as_float(b.sb[i][u] << 16);
-        nzs[i][u] = -((float)b.zb[i][u] * sc[i][u]);
-      }
 #pragma unroll
     for (int m = 0; m < RUN / 8; ++m) {
-      const U4 a = *reinterpret_cast<const U4*>(xb + k0 + 8 * m);
-      const int u = RUN >= G ? (8 * m) / G : 0;       // the group of positions q RUN + 8m ..
+      const U4 a = *reinterpret_cast<const U4*>(xb + k0 + 64 * (m >> 1) + 8 * (m & 1));
 #pragma unroll
       for (int i = 0; i < SEGS; ++i) {
         const int tt = seg(i);
+        // the group of positions 64 (m >> 1) + 16 q + 8 (m & 1) .. of the batch
+        uint32_t swd, zwd;
+        int hs, hz;
+        if constexpr (G == 32) {
+          const int g0 = 2 * (m >> 1);
+          swd = b.sb[i][g0 >> 1];                      // groups g0, g0 + 1 in one word
+          zwd = b.zb[i][g0 >> 2];
+          hs = qhi ? 1 : 0;
+          hz = (g0 & 3) + (qhi ? 1 : 0);
+        } else {
+          const int gi = G == 64 ? (m >> 1) : (m >> 2);
+          swd = b.sb[i][gi >> 1];
+          zwd = b.zb[i][gi >> 2];
+          hs = gi & 1;
+          hz = gi & 3;
+        }
+        const float scv = __uint_as_float(hs ? (swd & 0xFFFF0000u) : (swd << 16));
+        const float nzv = -((float)((zwd >> (8 * hz)) & 0xFFu) * scv);
         uint32_t c[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -891,11 +912,11 @@ __global__ __launch_bounds__(256) void uintx_decode_kernel(const uint16_t* __res
             f[4 * h] = lo[0]; f[4 * h + 1] = lo[1]; f[4 * h + 2] = hi[0]; f[4 * h + 3] = hi[1];
           }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = __builtin_fmaf(f[e], sc[i][u], nzs[i][u]);
+          for (int e = 0; e < 8; ++e) f[e] = __builtin_fmaf(f[e], scv, nzv);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            f[e] = __builtin_fmaf((float)((c[e >> 2] >> (8 * (e & 3))) & 0xFFu), sc[i][u], nzs[i][u]);
+            f[e] = __builtin_fmaf((float)((c[e >> 2] >> (8 * (e & 3))) & 0xFFu), scv, nzv);
         }
         const U4 bw = U4{ux_pair(f[0], f[1]), ux_pair(f[2], f[3]), ux_pair(f[4], f[5]), ux_pair(f[6], f[7])};
         acc[i] = mfma_bf16(a, bw, acc[i]);

@@ -278,22 +278,22 @@ def test_gemv_sizes_and_validation():
     sp_u = gwb.make_spec("uintx", 4, 64)
     assert lib.gwb_gemv_workspace(ctypes.byref(sp_u), 64, 128, 1, ctypes.byref(ctypes.c_size_t())) == gwb.E_UNSUPPORTED
     assert lib.gwb_gemv_workspace(ctypes.byref(sp_u), 12, 512, 1, ctypes.byref(ctypes.c_size_t())) == gwb.E_UNSUPPORTED
-    # bf16 uintx2/4 from 2 rows (3, 5, 6 bits from 4): the matrix-core decode kernel,
-    # 24 blocks of 16 x 8 rows -> K splits toward 1024 blocks, at least 2 batches of 256 k
+    # bf16 uintx2/4 from 2 rows (3, 5, 6 bits from 3, 7 bits from 5): the matrix-core decode
+    # kernel, 24 blocks of 16 x 8 rows -> K splits toward 1024 blocks, at least 2 batches of 256 k
     assert ws("uintx", 3072, 12288, 2) == (gwb.OK, 24 * 2 * 3072 * 4)
     # the GEMV kernels (fp16 weights): 2048 columns per wavefront up to 4 rows, 1024 or 512 beyond
     assert ws("uintx", 3072, 12288, 4, 64, gwb.F16) == (gwb.OK, 6 * 4 * 3072 * 4)
     assert ws("uintx", 3072, 12288, 8, 64, gwb.F16) == (gwb.OK, 12 * 8 * 3072 * 4)
     assert ws("uintx", 3072, 11776, 8, 64, gwb.F16) == (gwb.OK, 23 * 8 * 3072 * 4)   # K % 1024 != 0
     assert ws("uintx", 3072, 12288, 8) == (gwb.OK, 24 * 8 * 3072 * 4)             # bf16: the decode kernel
-    assert ws("uintx", 3072, 12288, 8, 64, gwb.BF16, 7) == (gwb.OK, 12 * 8 * 3072 * 4)   # 7 bits: the GEMV
+    assert ws("uintx", 3072, 12288, 8, 64, gwb.BF16, 7) == (gwb.OK, 24 * 8 * 3072 * 4)
+    assert ws("uintx", 3072, 12288, 4, 64, gwb.BF16, 7) == (gwb.OK, 6 * 4 * 3072 * 4)    # 7 bits, 4 rows: the GEMV
     # bf16 uintx4 on the 131072 x 2048 head: 1024 decode blocks, no split; the size still
     # covers the GEMV's (2 splits), which takes the call when the packed codes are not
     # 16-byte aligned
     assert ws("uintx", 131072, 2048, 8) == (gwb.OK, 2 * 8 * 131072 * 4)
     assert ws("uintx", 131072, 4096, 8) == (gwb.OK, 4 * 8 * 131072 * 4)           # GEMV: 4 splits
     assert ws("uintx", 131072, 2048, 4) == (gwb.OK, 0)
-    # 7 bits from 5 rows on 65536+ rows: gwb_gemm's uintx tiles, 256 blocks -> 2 K splits
     assert ws("uintx", 131072, 2048, 8, 64, gwb.BF16, 7) == (gwb.OK, 2 * 8 * 131072 * 4)
     assert ws("uintx", 64, 1536, 1) == (gwb.OK, 3 * 64 * 4)                      # 512-column splits
     assert ws("uintx", 131072, 2048, 1) == (gwb.OK, 0)                           # one split: y directly

@@ -475,17 +475,14 @@ def _gemv_tiles(fmt, n, k, B):
 
 
 def _uintx_mfma(dt, n, k, B, nbits):
-    """Whether gwb_gemv runs a bf16-weight uintx batch on the matrix cores (the decode
-    kernel: 2 and 4 bits from 2 rows, 3, 5 and 6 bits from 4 rows; 7 bits on gwb_gemm's
-    tiles from 5 rows on weights of 65536+ rows), whose float32 sums have no stated order:
-    u (K + 8) sum |w x|."""
+    """Whether gwb_gemv runs a bf16-weight uintx batch on the matrix-core decode kernel
+    (2 and 4 bits from 2 rows, 3, 5 and 6 bits from 3, 7 bits from 5), whose float32 sums
+    have no stated order: u (K + 8) sum |w x|."""
     if dt != "bf16" or n % 8 or k % 512:
         return False
     if nbits in (2, 4):
         return B >= 2
-    if nbits == 7:
-        return B >= 5 and n >= 65536
-    return B >= 4
+    return B >= (5 if nbits == 7 else 3)
 
 
 def _gemm_gptq_bound(o, x, group, K):
@@ -603,12 +600,12 @@ def test_gemv_uintx_parity(nbits, n, k, B):
     assert np.array_equal(yo, deq[:, cols].T.astype(np.float32))
 
 
-@pytest.mark.parametrize("nbits", [2, 3, 4, 5, 6])
+@pytest.mark.parametrize("nbits", [2, 3, 4, 5, 6, 7])
 @pytest.mark.parametrize("group", [32, 64, 128])
-@pytest.mark.parametrize("n,k,B", [(264, 2048, 8), (1040, 1536, 4), (8, 512, 5), (136, 4096, 6)])
+@pytest.mark.parametrize("n,k,B", [(264, 2048, 8), (1040, 1536, 5), (8, 512, 5), (136, 4096, 6)])
 def test_gemv_uintx_decode_parity(nbits, group, n, k, B):
-    """The matrix-core decode kernel (bf16 weights, 4+ activation rows): every width it
-    takes, every group size, ragged 16-row groups (1040 / 8 = 130 position-rows), one
+    """The matrix-core decode kernel (bf16 weights, 5+ activation rows): every width,
+    every group size, ragged 16-row groups (1040 / 8 = 130 position-rows), one
     position-row (n = 8), K splits summed afterwards, and odd batch counts. The page's
     forward, x times bf16((q - zp) s), within u (K + 8) sum |w x|; one-hot activations
     bit for bit."""
