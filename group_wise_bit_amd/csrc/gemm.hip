@@ -775,8 +775,9 @@ void launch_uintx_gemm(int nbits, int group, const void* packed, const void* sca
 // 64u + 16q (u < 4) of each plane, so every load instruction reads 64 contiguous bytes of
 // each row, and matrix-core step m takes positions 64 (m >> 1) + 16q + 8 (m & 1) .. + 7
 // from lane q (any split of K into 32-k slices serves, with the activations read to
-// match); the row's scales and zero points of the batch (256 / G groups) are one load
-// each. Measured on the 131072 x 2048 head, 8 rows, 4 bits: 16 rows of 32 bytes per lane
+// match); the row's scales and zero points of the batch (256 / G groups, starting at a
+// multiple of 256 / G) are one load each, so gwb_gemv takes this kernel only with the packed codes,
+// scales and zero points 16-byte aligned. Measured on the 131072 x 2048 head, 8 rows, 4 bits: 16 rows of 32 bytes per lane
 // and batch, K bytes apart, 57 us; a contiguous 64-byte run per lane (each instruction
 // reading 16 bytes every 64 of each row) 47 us; these pieces 42 us. Each wavefront keeps
 // the next batch's codes, scales and zero points in flight while it converts and
@@ -786,7 +787,7 @@ template <int NB> struct UdShape {
   static constexpr int kClasses = 8 / kSegs;         // wavefronts per 16 position-rows
   static constexpr int kRowGroups = 4 / kClasses;    // 16-row groups per block
   static constexpr int kRun = 64;                    // bytes per lane, plane and batch
-  static constexpr int kBatch = 4 * kRun;                // positions of a row per batch
+  static constexpr int kBatch = 4 * kRun;            // positions of a row per batch
 };
 
 template <int NB, int NGR>
