@@ -772,16 +772,16 @@ void launch_uintx_gemm(int nbits, int group, const void* packed, const void* sca
 // in LDS for the whole kernel (one barrier, at the start), so wavefronts never wait for
 // one another.
 // A batch is 256 positions of each of the 16 rows: lane q holds the 16-byte pieces at
-// 64u + 16q (u < 4) of each plane, so every load instruction reads 64 contiguous bytes of
-// each row, and matrix-core step m takes positions 64 (m >> 1) + 16q + 8 (m & 1) .. + 7
-// from lane q (any split of K into 32-k slices serves, with the activations read to
+// 64u + 16q (u < 4) of each plane, so every load instruction reads 64 contiguous bytes
+// of each row, and matrix-core step m takes positions 64 (m >> 1) + 16q + 8 (m & 1) to
+// + 7 from lane q (any split of K into 32-k slices serves, with the activations read to
 // match); the row's scales and zero points of the batch (256 / G groups, starting at a
-// multiple of 256 / G) are one load each, so gwb_gemv takes this kernel only with the packed codes,
-// scales and zero points 16-byte aligned. Measured on the 131072 x 2048 head, 8 rows, 4 bits: 16 rows of 32 bytes per lane
-// and batch, K bytes apart, 57 us; a contiguous 64-byte run per lane (each instruction
-// reading 16 bytes every 64 of each row) 47 us; these pieces 42 us. Each wavefront keeps
-// the next batch's codes, scales and zero points in flight while it converts and
-// multiplies the current one.
+// multiple of 256 / G) are one load each, so gwb_gemv takes this kernel only with the
+// packed codes, scales and zero points 16-byte aligned. Measured on the 131072 x 2048
+// head, 8 rows, 4 bits: 16 rows of 32 bytes per lane and batch, K bytes apart, 57 us; a
+// contiguous 64-byte run per lane (each instruction reading 16 bytes every 64 of each
+// row) 47 us; these pieces 42 us. Each wavefront keeps the next batch's codes, scales
+// and zero points in flight while it converts and multiplies the current one.
 template <int NB> struct UdShape {
   static constexpr int kSegs = (NB & 4) ? 2 : 4;   // segments per wavefront
   static constexpr int kClasses = 8 / kSegs;         // wavefronts per 16 position-rows
