@@ -91,6 +91,27 @@ __device__ __forceinline__ U4 ld16(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, U4 v) { *reinterpret_cast<U4*>(p) = v; }
 
+// Rows [ks, kend) of the bf16 activations x (Bn rows, row stride ldx) into LDS rows of
+// pitch xp elements, by a 256-thread block: each thread issues up to eight 16-byte loads
+// before it writes any (a load-then-write loop waits a full round trip per load).
+__device__ __forceinline__ void stage_rows(uint16_t* xs, int xp, const uint16_t* __restrict__ x, int64_t ldx, int Bn,
+                                           int ks, int kend) {
+  const int cpr = (kend - ks) / 8, total = Bn * cpr;
+  for (int v0 = (int)threadIdx.x; v0 < total; v0 += 8 * 256) {
+    U4 tmp[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int v = min(v0 + 256 * u, total - 1), b = v / cpr, c = v - b * cpr;   // past the end: re-read the last
+      tmp[u] = ld16(x + (int64_t)b * ldx + ks + 8 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int v = v0 + 256 * u, b = v / cpr, c = v - b * cpr;
+      if (v < total) *reinterpret_cast<U4*>(xs + b * xp + 8 * c) = tmp[u];
+    }
+  }
+}
+
 // Non-temporal (streaming) variants: data read or written exactly once.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ U4 ld16_nt(const void* p) {

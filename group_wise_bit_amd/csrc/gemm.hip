@@ -815,12 +815,6 @@ __global__ __launch_bounds__(256) void uintx_decode_kernel(const uint16_t* __res
   const int cls = wv % SH::kClasses, rg = wv / SH::kClasses;
   const int ks = (int)blockIdx.y * kspan, kend = min(K, ks + kspan);   // multiples of BP
   const int xp = kspan + 8;                      // LDS row pitch: 16 bytes of padding per row
-  const int cpr = (kend - ks) / 8;
-  for (int v = t; v < Bn * cpr; v += 256) {
-    const int b = v / cpr, c = v - b * cpr;
-    *reinterpret_cast<U4*>(xs + b * xp + 8 * c) = ld16(x + (int64_t)b * ldx + ks + 8 * c);
-  }
-  __syncthreads();
   const uint16_t* xb = xs + min(j, Bn - 1) * xp + 16 * q - ks;   // rows past the batch repeat the last
   const int r = ((int)blockIdx.x * SH::kRowGroups + rg) * 16 + j;
   const uint32_t L1 = (uint32_t)R8 * (uint32_t)K;
@@ -935,7 +929,10 @@ __global__ __launch_bounds__(256) void uintx_decode_kernel(const uint16_t* __res
   // batch's arithmetic above them (either would wait for the loads at once).
   const int nbt = (kend - ks) / BP;
   UdBuf<NB, NGR> b0, b1;
-  load(b0, ks);
+  load(b0, ks);                                  // the weight stream starts before the staging
+  asm volatile("" ::: "memory");
+  stage_rows(xs, xp, x, ldx, Bn, ks, kend);
+  __syncthreads();
   int bt = 0;
   for (; bt + 1 < nbt; bt += 2) {
     load(b1, ks + (bt + 1) * BP);

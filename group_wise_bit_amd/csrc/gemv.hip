@@ -666,13 +666,6 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_mfma_kernel(const uint8_t* __r
   const int ks = (int)blockIdx.y * kc, kend = min(K, ks + kc);   // this split: [ks, kend), a multiple of 32
   const int nb = (kend - ks + 128 * kMxmNS - 1) / (128 * kMxmNS);   // batches per tile
   const int nbt = (N + 63) / 64;                                // 64-row block tiles
-  // the split's activations, staged once (rows in LDS padded by 16 bytes: no bank conflicts)
-  const int cpr = (kend - ks) / 8;
-  for (int v = t; v < Bn * cpr; v += 256) {
-    const int b = v / cpr, c = v - b * cpr;
-    *reinterpret_cast<U4*>(xs + b * xp + 8 * c) = ld16(x + (int64_t)b * ldx + ks + 8 * c);
-  }
-  __syncthreads();
   const uint16_t* xb = xs + min(j, Bn - 1) * xp;                // rows past the batch repeat the last
   const bool bcol = j < Bn;
   auto rows_of = [&](int bt, const uint8_t*& wr, const uint8_t*& er) {
@@ -700,14 +693,17 @@ __global__ __launch_bounds__(256) void mxfp4_gemv_mfma_kernel(const uint8_t* __r
     acc = gv_f32x4_t{0.f, 0.f, 0.f, 0.f};
     nan = 0u;
   };
-  int bt = blockIdx.x, h = 0;                                   // block-uniform
-  if (bt >= nbt) return;                                        // after the only barrier
+  int bt = blockIdx.x, h = 0;                                   // block-uniform, below nbt (the grid is capped)
   gv_f32x4_t acc = gv_f32x4_t{0.f, 0.f, 0.f, 0.f};
   uint32_t nan = 0u;
   const uint8_t *wr, *er;
   rows_of(bt, wr, er);
   MxmBuf b0, b1;
-  mxm_load<AL>(b0, wr, er, ks, kend, q, true);
+  mxm_load<AL>(b0, wr, er, ks, kend, q, true);                  // the weight stream starts before the staging
+  asm volatile("" ::: "memory");
+  // the split's activations, staged once (rows in LDS padded by 16 bytes: no bank conflicts)
+  stage_rows(xs, xp, x, ldx, Bn, ks, kend);
+  __syncthreads();
   // two items per trip, one per buffer: load the next item, then multiply the current
   for (;;) {
     int bt2 = bt, h2 = h + 1;

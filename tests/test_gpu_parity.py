@@ -465,13 +465,13 @@ def _gptq_bound(o, x, group, sym, K):
     return U32 * (group + K // group + 40) * (np.abs(x.astype(np.float64)) @ w.reshape(K, -1))
 
 
-def _gemv_tiles(fmt, n, k, B):
+def _gemv_tiles(fmt, n, k, B, y_aligned=True):
     """gwb_gemv hands GPTQ (index-order groups) batches of 2+ rows to the GEMM tile
-    kernels when N % 8 == 0 and K % 128 == 0 and y's rows are 16-byte aligned (every
-    output here with ldy = N)."""
-    if n % 8 or k % 128:
+    kernels when N % 8 == 0, K % 128 == 0 and y's rows are 16-byte aligned (with ldy = N
+    here); otherwise the GEMV kernels run."""
+    if B < 2 or fmt not in ("gptq_sym", "gptq_asym") or n % 8:
         return False
-    return B >= 2 and fmt in ("gptq_sym", "gptq_asym")
+    return k % 128 == 0 and y_aligned
 
 
 def _uintx_mfma(dt, n, k, B, nbits):
@@ -499,7 +499,8 @@ def _strided_out(B, n, ydt):
 
 
 _GEMV_GPTQ_CASES = [(g, n, k, B) for g in (32, 64, 128)
-                    for n, k, B in ((256, 512, 1), (72, 384, 3), (520, 1664, 8), (264, 640, 2), (136, 576, 4))
+                    for n, k, B in ((256, 512, 1), (72, 384, 3), (520, 1664, 8), (264, 640, 2), (136, 576, 4),
+                                    (264, 2048, 8), (8, 512, 3), (1048, 1536, 5), (136, 4608, 2))
                     if k % g == 0]
 
 
@@ -517,9 +518,10 @@ def test_gemv_gptq_parity(fmt, group, n, k, B):
     ref = ogv.gemv(deq, xf)
     gemv_bound = _gptq_bound(o, xf, group, fmt == "gptq_sym", k)
     bound = _gemm_gptq_bound(o, xf, group, k) if _gemv_tiles(fmt, n, k, B) else gemv_bound
+    sbound = _gemm_gptq_bound(o, xf, group, k) if _gemv_tiles(fmt, n, k, B, False) else gemv_bound
     for ydt in (torch.float32, torch.bfloat16):
         _gemv_check(gwb.gemv(q, x.to(DEV), ydt), ref, bound, ydt)
-        _gemv_check(gwb.gemv(q, x.to(DEV), out=_strided_out(B, n, ydt)), ref, gemv_bound, ydt)
+        _gemv_check(gwb.gemv(q, x.to(DEV), out=_strided_out(B, n, ydt)), ref, sbound, ydt)
 
 
 def _mx_gemv_bound(deq, xf, k, B):
@@ -743,9 +745,10 @@ def test_gemv_group_order_parity(sym, group, n, k, B):
     fmt = "gptq_sym" if sym else "gptq_asym"
     gemv_bound = _gptq_bound(og, xf[:, perm], group, sym, k)
     bound = _gemm_gptq_bound(og, xf[:, perm], group, k) if _gemv_tiles(fmt, n, k, B) else gemv_bound
+    sbound = _gemm_gptq_bound(og, xf[:, perm], group, k) if _gemv_tiles(fmt, n, k, B, False) else gemv_bound
     for ydt in (torch.float32, torch.bfloat16):
         _gemv_check(gwb.gemv(qg, x.to(DEV), ydt), ref, bound, ydt)
-        _gemv_check(gwb.gemv(qg, x.to(DEV), out=_strided_out(B, n, ydt)), ref, gemv_bound, ydt)
+        _gemv_check(gwb.gemv(qg, x.to(DEV), out=_strided_out(B, n, ydt)), ref, sbound, ydt)
     xo = torch.zeros(B, k, dtype=torch.bfloat16)
     cols = [(b * 131 + 7) % k for b in range(B)]
     for b, kk in enumerate(cols):
