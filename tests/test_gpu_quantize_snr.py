@@ -16,7 +16,7 @@ from group_wise_bit_amd import workloads
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
-    from group_wise_bit_amd import binding as gwb      # must load: no fallback on a GPU machine
+    from group_wise_bit_amd import binding as gwb      # must load: no fallback where a GPU is present
 else:  # collected on CPU only to be skipped
     gwb = None
 
