@@ -40,6 +40,11 @@ int hip_check(const char* what) {
 
 // Kernels index elements with 32-bit unsigned integers.
 constexpr int64_t kMaxElems = (int64_t)1 << 31;
+// MXFP4 rows are independent, so gwb_query_sizes, gwb_quantize, gwb_quantize_snr,
+// gwb_dequantize and gwb_snr take MXFP4 shapes of up to kMaxBandedElems elements and run
+// them as row bands of fewer than kMaxElems, each on offset pointers (the SNR partials of
+// every band go to one finalize).
+constexpr int64_t kMaxBandedElems = (int64_t)1 << 37;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -59,15 +64,17 @@ int refuse_grouped(const gwb_qspec* sp) {
 
 size_t elem_size(int32_t dt) { return dt == GWB_F32 ? 4 : 2; }
 
-int check_spec(const gwb_qspec* sp, int64_t N, int64_t K) {
+// banded: the call runs MXFP4 in row bands (see kMaxBandedElems).
+int check_spec(const gwb_qspec* sp, int64_t N, int64_t K, bool banded = false) {
   if (!sp) return fail(GWB_E_ARG, "spec is NULL");
   if (N < 0 || K < 0) return fail(GWB_E_ARG, "negative shape N=%lld K=%lld", (long long)N, (long long)K);
   if (sp->w_dtype != GWB_F32 && sp->w_dtype != GWB_BF16 && sp->w_dtype != GWB_F16)
     return fail(GWB_E_ARG, "unknown w_dtype %d", sp->w_dtype);
   if (sp->w_dtype == GWB_F16 && sp->format != GWB_UINTX)
     return fail(GWB_E_UNSUPPORTED, "float16 weights are provided for UINTX only");
-  if (N > 0 && K > 0 && (N >= kMaxElems || K >= kMaxElems || N * K >= kMaxElems))
-    return fail(GWB_E_UNSUPPORTED, "N*K = %lld exceeds 2^31 elements", (long long)(N * K));
+  const bool bands = banded && is_mxfp4(sp->format);
+  if (N > 0 && K > 0 && (N >= kMaxElems || K >= kMaxElems || N * K >= (bands ? kMaxBandedElems : kMaxElems)))
+    return fail(GWB_E_UNSUPPORTED, "N*K = %lld exceeds %s elements", (long long)(N * K), bands ? "2^37" : "2^31");
   switch (sp->format) {
     case GWB_GPTQ_SYM:
     case GWB_GPTQ_ASYM:
@@ -117,10 +124,27 @@ size_t uintx_packed_bytes(int nbits, int64_t numel) {
   return b;
 }
 
+// Rows of an MXFP4 band: fewer than kMaxElems elements (all N when the shape is below).
+int64_t mx_band_rows(int64_t N, int64_t K) {
+  const int64_t r = (kMaxElems - 1) / (K > 0 ? K : 1);
+  return r < N ? r : N;
+}
+// f(r0, n) for each band of rows [r0, r0 + n), in order.
+template <typename F>
+void mx_bands(int64_t N, int64_t K, F&& f) {
+  const int64_t R = mx_band_rows(N, K);
+  for (int64_t r0 = 0; r0 < N; r0 += R) f(r0, N - r0 < R ? N - r0 : R);
+}
+unsigned mx_err_blocks(int64_t N, int64_t K) {
+  unsigned nb = 0;
+  mx_bands(N, K, [&](int64_t, int64_t n) { nb += gwb::mxfp4_err_blocks(n, K); });
+  return nb;
+}
+
 unsigned err_blocks(const gwb_qspec* sp, int64_t N, int64_t K) {
   switch (sp->format) {
     case GWB_MXFP4:
-    case GWB_MXFP4_PAGE_TIES: return gwb::mxfp4_err_blocks(N, K);
+    case GWB_MXFP4_PAGE_TIES: return mx_err_blocks(N, K);
     case GWB_UINTX: return gwb::uintx_err_blocks(sp->w_dtype, sp->group, N, K);
     case GWB_GPTQ_SYM_ACT:
     case GWB_GPTQ_ASYM_ACT: return gwb::gptq_act_err_blocks(N, K);
@@ -197,7 +221,7 @@ extern "C" {
 const char* gwb_last_error(void) { return g_err.c_str(); }
 
 int gwb_query_sizes(const gwb_qspec* spec, int64_t N, int64_t K, gwb_sizes* out) {
-  if (int rc = check_spec(spec, N, K)) return rc;
+  if (int rc = check_spec(spec, N, K, true)) return rc;
   if (!out) return fail(GWB_E_ARG, "out is NULL");
   *out = sizes_of(spec, N, K);
   return ok();
@@ -205,7 +229,7 @@ int gwb_query_sizes(const gwb_qspec* spec, int64_t N, int64_t K, gwb_sizes* out)
 
 int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
                  const gwb_qtensors* out, void* workspace, size_t workspace_bytes, void* stream) {
-  if (int rc = check_spec(spec, N, K)) return rc;
+  if (int rc = check_spec(spec, N, K, true)) return rc;
   if (is_act(spec->format))
     return fail(GWB_E_ARG, "act-order GPTQ takes the channel order: use gwb_quantize_act_order");
   if (int rc = refuse_grouped(spec)) return rc;
@@ -227,8 +251,12 @@ int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int
       break;
     case GWB_MXFP4:
     case GWB_MXFP4_PAGE_TIES:
-      gwb::launch_mxfp4_quant(spec->format == GWB_MXFP4_PAGE_TIES, W, spec->w_dtype, N, K, ldw, out->codes,
-                              out->scales, nullptr, st);
+      mx_bands(N, K, [&](int64_t r0, int64_t n) {
+        gwb::launch_mxfp4_quant(spec->format == GWB_MXFP4_PAGE_TIES,
+                                (const char*)W + r0 * ldw * (int64_t)elem_size(spec->w_dtype), spec->w_dtype, n, K,
+                                ldw, (uint8_t*)out->codes + r0 * (K / 2), (uint8_t*)out->scales + r0 * (K / 32),
+                                nullptr, st);
+      });
       break;
     default:
       gwb::launch_uintx_quant(spec->nbits, spec->w_dtype, spec->group, W, N, K, ldw, out->codes, out->scales,
@@ -242,7 +270,7 @@ int gwb_quantize(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int
 // fit the partials, uintx in the tiled layout); otherwise the two calls in turn.
 int gwb_quantize_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
                      const gwb_qtensors* out, double* d_out, void* workspace, size_t workspace_bytes, void* stream) {
-  if (int rc = check_spec(spec, N, K)) return rc;
+  if (int rc = check_spec(spec, N, K, true)) return rc;
   if (is_act(spec->format)) return fail(GWB_E_ARG, "act-order GPTQ quantizes with gwb_quantize_act_order");
   if (int rc = refuse_grouped(spec)) return rc;
   if (!d_out) return fail(GWB_E_ARG, "d_out is NULL");
@@ -273,10 +301,15 @@ int gwb_quantize_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K,
   if (spec->format == GWB_GPTQ_SYM || spec->format == GWB_GPTQ_ASYM)
     gwb::launch_gptq_quant_snr(spec->format == GWB_GPTQ_SYM, spec->group, W, spec->w_dtype, N, K, ldw, out->codes,
                                out->scales, out->zeros, out->g_idx, part, st);
-  else if (is_mxfp4(spec->format))
-    gwb::launch_mxfp4_quant(spec->format == GWB_MXFP4_PAGE_TIES, W, spec->w_dtype, N, K, ldw, out->codes,
-                            out->scales, part, st);
-  else
+  else if (is_mxfp4(spec->format)) {
+    double* p = part;
+    mx_bands(N, K, [&](int64_t r0, int64_t n) {
+      gwb::launch_mxfp4_quant(spec->format == GWB_MXFP4_PAGE_TIES,
+                              (const char*)W + r0 * ldw * (int64_t)elem_size(spec->w_dtype), spec->w_dtype, n, K, ldw,
+                              (uint8_t*)out->codes + r0 * (K / 2), (uint8_t*)out->scales + r0 * (K / 32), p, st);
+      p += 2 * (size_t)gwb::mxfp4_err_blocks(n, K);
+    });
+  } else
     gwb::launch_uintx_quant(spec->nbits, spec->w_dtype, spec->group, W, N, K, ldw, out->codes, out->scales,
                             out->zeros, nullptr, part, st);
   gwb::launch_err_finalize(part, nb, d_out, st);
@@ -287,7 +320,7 @@ int gwb_dequantize(const gwb_qspec* spec, const gwb_qtensors* in, int64_t N, int
                    int32_t out_dtype, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
-  if (int rc = check_spec(spec, N, K)) return rc;
+  if (int rc = check_spec(spec, N, K, true)) return rc;
   if (int rc = refuse_grouped(spec)) return rc;
   if (out_dtype != GWB_F32 && out_dtype != GWB_BF16 && out_dtype != GWB_F16)
     return fail(GWB_E_ARG, "unknown out_dtype %d", out_dtype);
@@ -315,7 +348,10 @@ int gwb_dequantize(const gwb_qspec* spec, const gwb_qtensors* in, int64_t N, int
       break;
     case GWB_MXFP4:
     case GWB_MXFP4_PAGE_TIES:
-      gwb::launch_mxfp4_dequant(in->codes, in->scales, N, K, out, out_dtype, ldo, st);
+      mx_bands(N, K, [&](int64_t r0, int64_t n) {
+        gwb::launch_mxfp4_dequant((const uint8_t*)in->codes + r0 * (K / 2), (const uint8_t*)in->scales + r0 * (K / 32),
+                                  n, K, (char*)out + r0 * ldo * (int64_t)elem_size(out_dtype), out_dtype, ldo, st);
+      });
       break;
     default:
       gwb::launch_uintx_dequant(spec->nbits, spec->w_dtype, spec->group, in->codes, in->scales, in->zeros, N, K,
@@ -326,7 +362,7 @@ int gwb_dequantize(const gwb_qspec* spec, const gwb_qtensors* in, int64_t N, int
 
 int gwb_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw, const gwb_qtensors* in,
             double* d_out, void* workspace, size_t workspace_bytes, void* stream) {
-  if (int rc = check_spec(spec, N, K)) return rc;
+  if (int rc = check_spec(spec, N, K, true)) return rc;
   if (int rc = refuse_grouped(spec)) return rc;
   if (int rc = check_weight(spec, W, K, ldw)) return rc;
   if (int rc = check_tensors(spec, in)) return rc;
@@ -351,9 +387,16 @@ int gwb_snr(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t 
                                in->scales, in->zeros, (const int32_t*)in->g_idx, part, st);
       break;
     case GWB_MXFP4:
-    case GWB_MXFP4_PAGE_TIES:
-      gwb::launch_mxfp4_err(W, spec->w_dtype, N, K, ldw, in->codes, in->scales, part, st);
+    case GWB_MXFP4_PAGE_TIES: {
+      double* p = part;
+      mx_bands(N, K, [&](int64_t r0, int64_t n) {
+        gwb::launch_mxfp4_err((const char*)W + r0 * ldw * (int64_t)elem_size(spec->w_dtype), spec->w_dtype, n, K, ldw,
+                              (const uint8_t*)in->codes + r0 * (K / 2), (const uint8_t*)in->scales + r0 * (K / 32), p,
+                              st);
+        p += 2 * (size_t)gwb::mxfp4_err_blocks(n, K);
+      });
       break;
+    }
     default:
       gwb::launch_uintx_err(spec->nbits, spec->w_dtype, spec->group, W, N, K, ldw, in->codes, in->scales,
                             in->zeros, part, st);
@@ -730,7 +773,7 @@ int device_scratch(void** ptr) {
 
 int gwb_quantize_snr_static(const gwb_qspec* spec, const void* W, int64_t N, int64_t K, int64_t ldw,
                             const gwb_qtensors* out, double* d_out, void* stream) {
-  if (int rc = check_spec(spec, N, K)) return rc;
+  if (int rc = check_spec(spec, N, K, true)) return rc;
   const gwb_sizes sz = sizes_of(spec, N, K);
   if (sz.workspace > (size_t)GWB_STATIC_SCRATCH_BYTES)
     return fail(GWB_E_SIZE, "this shape needs %zu bytes of scratch; the static array holds %d", sz.workspace,

@@ -125,7 +125,12 @@ typedef struct {
  *   GPTQ: K % group == 0, N % 8 == 0 (qzeros pack 8 columns per word); act-order
  *         GPTQ also K / group <= 256 and K * element size <= 64 KB (GWB_E_UNSUPPORTED);
  *   MXFP4: K % 32 == 0 (page quantize_mxfp4 asserts it);
- *   UINTX: K % group == 0 (can_quantize refuses otherwise).                      */
+ *   UINTX: K % group == 0 (can_quantize refuses otherwise).
+ * Size: N * K < 2^31 elements (GWB_E_UNSUPPORTED beyond). MXFP4 rows are independent:
+ * this query, gwb_quantize, gwb_quantize_snr (and its static variant), gwb_dequantize and
+ * gwb_snr take MXFP4 up to N * K < 2^37 and run row bands of fewer than 2^31 elements
+ * (the SNR partials of every band summed by one finalize); the GEMV, GEMM and fold keep
+ * 2^31.                                                                          */
 int gwb_query_sizes(const gwb_qspec* spec, int64_t N, int64_t K, gwb_sizes* out);
 
 /* Quantize and pack W [N, K] (row stride ldw >= K elements, of spec->w_dtype).

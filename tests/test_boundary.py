@@ -90,12 +90,31 @@ def test_bits_per_weight_from_sizes():
     ("mxfp4", 8, 128, 4, 32, gwb.F16, gwb.E_UNSUPPORTED),     # float16 weights: uintx only
     ("gptq_sym", 8, 128, 4, 128, gwb.F16, gwb.E_UNSUPPORTED),
     ("uintx", -1, 128, 4, 64, gwb.BF16, gwb.E_ARG),
-    ("mxfp4", 1 << 16, 1 << 16, 4, 32, gwb.BF16, gwb.E_UNSUPPORTED),   # beyond 2^31 elements
+    ("mxfp4", 1 << 21, 1 << 16, 4, 32, gwb.BF16, gwb.E_UNSUPPORTED),   # 2^37 elements: past MXFP4's row bands
+    ("gptq_sym", 1 << 16, 1 << 16, 4, 128, gwb.BF16, gwb.E_UNSUPPORTED),   # 2^32: GPTQ indexes below 2^31
+    ("uintx", 1 << 16, 1 << 16, 4, 64, gwb.BF16, gwb.E_UNSUPPORTED),
 ])
 def test_query_rejects(fmt, N, K, nbits, group, dt, code):
     rc, _ = _sizes(fmt, N, K, nbits, group, dt)
     assert rc == code
     assert lib.gwb_last_error().decode()
+
+
+def test_mxfp4_row_bands_past_2_31():
+    """MXFP4 shapes of 2^31 elements or more are accepted by the size query, quantize,
+    dequantize and SNR (row bands of fewer than 2^31 elements each); sizes are those of
+    the whole layout, and the workspace holds every band's partials. The GEMV, GEMM and
+    fold keep the 2^31 limit."""
+    N, K = 131080, 16384                      # 2^31 + 131072 elements: bands of 131071 and 9 rows
+    rc, sz = _sizes("mxfp4", N, K, 4, 32, gwb.BF16)
+    assert rc == gwb.OK
+    assert sz.codes == N * K // 2 and sz.scales == N * K // 32
+    rc1, sz1 = _sizes("mxfp4", 131071, K, 4, 32, gwb.BF16)
+    rc2, sz2 = _sizes("mxfp4", 9, K, 4, 32, gwb.BF16)
+    assert rc1 == rc2 == gwb.OK and sz.workspace == sz1.workspace + sz2.workspace
+    sp, b = gwb.make_spec("mxfp4", 4, 32, gwb.BF16), ctypes.c_size_t()
+    assert lib.gwb_gemv_workspace(ctypes.byref(sp), N, K, 1, ctypes.byref(b)) == gwb.E_UNSUPPORTED
+    assert lib.gwb_gemm_workspace(ctypes.byref(sp), N, K, 16, ctypes.byref(b)) == gwb.E_UNSUPPORTED
 
 
 def test_unknown_format_and_dtype():

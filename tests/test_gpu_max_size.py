@@ -48,17 +48,22 @@ def _ref_bf16bits(x) -> np.ndarray:
     return (np.asarray(bf16_round(x), np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
+def _draw(n, k, seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    W = torch.empty(n, k, dtype=torch.bfloat16, device=DEV)
+    gain = torch.exp(0.5 * torch.randn(n, generator=g, device=DEV))
+    for r0 in range(0, n, 8192):                   # float32 draws in row bands, rounded to bf16
+        r1 = min(n, r0 + 8192)
+        band = torch.randn(r1 - r0, k, generator=g, device=DEV) * 0.015 * gain[r0:r1, None]
+        W[r0:r1] = band.to(torch.bfloat16)
+    return W
+
+
 @pytest.fixture(scope="module")
 def big_weight():
     assert N * K < 2 ** 31 and (2 ** 31 - N * K) == 131072
-    g = torch.Generator(device=DEV)
-    g.manual_seed(2031)
-    W = torch.empty(N, K, dtype=torch.bfloat16, device=DEV)
-    gain = torch.exp(0.5 * torch.randn(N, generator=g, device=DEV))
-    for r0 in range(0, N, 8192):                   # float32 draws in row bands, rounded to bf16
-        r1 = min(N, r0 + 8192)
-        band = torch.randn(r1 - r0, K, generator=g, device=DEV) * 0.015 * gain[r0:r1, None]
-        W[r0:r1] = band.to(torch.bfloat16)
+    W = _draw(N, K, 2031)
     yield W
     del W
     torch.cuda.empty_cache()
@@ -72,7 +77,7 @@ def _rows(count, seed, mult=1):
 def _sums(W: torch.Tensor, D: torch.Tensor):
     """float64 sum of w^2 and of (w - d)^2 over the whole matrix, in row bands."""
     sw = se = 0.0
-    for r0 in range(0, N, 8192):
+    for r0 in range(0, W.shape[0], 8192):
         w = W[r0:r0 + 8192].double()
         sw += float((w * w).sum())
         e = w - D[r0:r0 + 8192].double()
@@ -157,4 +162,29 @@ def test_max_size_uintx4(big_weight):
     assert np.array_equal(_bf16bits(d[rows]), _ref_bf16bits(ref))
     _check_sums(snr, W, d)
     del q, d
+    torch.cuda.empty_cache()
+
+
+def test_max_size_mxfp4_row_bands():
+    """MXFP4 past 2^31 elements: 131080 x 16384 = 2^31 + 131072 runs as row bands of
+    131071 and 9 rows (each under the kernels' 32-bit indices). Rows on both sides of the
+    band edge and spread over the matrix bit for bit against the oracle; the fused sums
+    and gwb_snr's (every band's partials in one finalize) against float64 sums of the
+    whole matrix."""
+    n = 131080
+    assert n * K >= 2 ** 31 and (2 ** 31 - 1) // K == 131071
+    W = _draw(n, K, 2032)
+    q, snr = gwb.quantize_snr(W, "mxfp4")
+    d = gwb.dequantize(q, torch.bfloat16)
+    rows = np.unique(np.concatenate([np.random.default_rng(34).choice(n, 40, replace=False),
+                                     [0, 131069, 131070, 131071, 131072, n - 1]]))
+    w = W[rows].float().cpu().numpy()
+    p, e = omx.quantize(w)
+    assert np.array_equal(_np(q["packed"][rows]), p)
+    assert np.array_equal(_np(q["e8m0"][rows]), e)
+    assert np.array_equal(_bf16bits(d[rows]), _ref_bf16bits(omx.dequantize(p, e, K)))
+    _check_sums(snr, W, d)
+    s2 = gwb.snr(W, q)
+    _check_sums(s2, W, d)
+    del q, d, W
     torch.cuda.empty_cache()
