@@ -678,11 +678,13 @@ def test_gemv_uintx_variants_parity(dt, group, nbits, n, k, B):
 
 @pytest.mark.parametrize("sym", [True, False])
 @pytest.mark.parametrize("group,n,k,B", [(128, 64, 512, 1), (32, 136, 1024, 3), (64, 1024, 4096, 8),
-                                          (128, 4096, 2048, 2), (32, 72, 4096, 2)])
+                                          (128, 4096, 2048, 2), (32, 72, 4096, 2), (128, 136, 1024, 4),
+                                          (64, 520, 2048, 8), (128, 4096, 2048, 5), (128, 8, 512, 3)])
 def test_gemv_gptq_act_order_parity(sym, group, n, k, B):
     """GEMV on act-order GPTQ weights: each channel dequantized with its group g_idx[k]
     (up to 96 groups per row from a float32 (s, -z s) table, 128 groups from the packed
-    scales and zero points)."""
+    scales and zero points; from three rows and up to 48 groups, two columns per lane:
+    ragged 128-column blocks, K splits and the smallest N included)."""
     W = workloads.mxfp4_weight(n, k, seed=550 + n + group)
     x = workloads.normal_weight(B, k, std=1.0, seed=551 + B)
     perm = np.random.default_rng(552 + k).permutation(k)
