@@ -961,11 +961,12 @@ def test_full_fold_34816x5120_sampled():
 
 
 @pytest.mark.parametrize("fmt,B", [("gptq_sym", 1), ("gptq_sym", 8), ("mxfp4", 1), ("mxfp4", 8), ("uintx", 1),
-                                   ("uintx", 8), ("gptq_sym_act", 1), ("gptq_sym_grouped", 1)])
+                                   ("uintx", 8), ("gptq_sym_act", 1), ("gptq_sym_act", 8), ("gptq_sym_grouped", 1)])
 def test_full_gemv_lm_head_131072x2048_sampled(fmt, B):
     """The page's lm_head decode read, 131072 x 2048, in the launch shapes the benchmark
-    times (B = 1: the GEMV kernels; B = 8: the matrix-core GEMV (MXFP4) or tiles (GPTQ,
-    uintx)); checked on sampled output rows (whole qzeros words) against the oracle."""
+    times (B = 1: the GEMV kernels; B = 8: the matrix-core GEMV (MXFP4), the tiles (GPTQ),
+    the matrix-core decode kernel (uintx) and the two-column act-order kernel); checked on
+    sampled output rows (whole qzeros words) against the oracle."""
     N_, K_ = 131072, 2048
     W = workloads.normal_weight(N_, K_, seed=520)
     x = workloads.normal_weight(B, K_, std=1.0, seed=521)
